@@ -1,0 +1,320 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test pins one oracle function to a value the pages print (fixtures under
+tests/golden/), a closed form, brute force, an independent library routine, or central
+finite differences, chosen so that a dropped term, a wrong sign or index, or a
+transposed operand anywhere in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+from oracle import moe_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _ffn_torch(x, W13, W2):
+    """Dense bias-free SwiGLU FFN via torch's own silu and linear, in float64."""
+    x, W13, W2 = (torch.as_tensor(np.asarray(a, dtype=np.float64)) for a in (x, W13, W2))
+    F = W13.shape[0] // 2
+    h = torch.nn.functional.linear(x, W13)
+    return (torch.nn.functional.silu(h[:, :F]) * h[:, F:]) @ W2.T
+
+
+def _rand_layer(rng, T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux=0.0, bias=None):
+    x = rng.standard_normal((T, d))
+    Wg = rng.standard_normal((E, d)) / np.sqrt(d)
+    W13 = rng.standard_normal((E, 2 * F, d)) / np.sqrt(d)
+    W2 = rng.standard_normal((E, d, F)) / np.sqrt(F)
+    W13s = rng.standard_normal((2 * Fs, d)) / np.sqrt(d) if Fs else None
+    W2s = rng.standard_normal((d, Fs)) / np.sqrt(Fs) if Fs else None
+    bg = rng.standard_normal(E) * 0.3 if bias == "bg" else None
+    eb = rng.standard_normal(E) * 0.1 if bias == "expert_bias" else None
+    dy = rng.standard_normal((T, d))
+    spec = O.LayerSpec(E=E, k=k, score=score, scaling=scaling, aux_coeff=aux)
+    return dict(x=x, Wg=Wg, W13=W13, W2=W2, W13s=W13s, W2s=W2s, bg=bg, expert_bias=eb, dy=dy), spec
+
+
+# ------------------------------------------------------------------ worked examples
+
+def test_worked_mixture_075_025():
+    g = gold("worked_mixture.json")
+    wa, wb = g["weights"]
+    # a softmax over the two selected logits gives (0.75, 0.25) iff l_A - l_B = ln 3
+    logits = np.array([[math.log(3.0), 0.0]])
+    idx = O.topk(O.selection_keys(logits, "softmax"), 2)
+    assert idx.tolist() == [[0, 1]]
+    w = O.mixing_weights(logits, idx, "softmax")
+    assert abs(w[0, 0] - wa) < 1e-15 and abs(w[0, 1] - wb) < 1e-15
+    # whole layer: y = 0.75 * A(x) + 0.25 * B(x), coordinate by coordinate
+    rng = np.random.default_rng(0)
+    d, F = 2, 4
+    x = np.array([[1.0, 0.0]])
+    Wg = np.array([[math.log(3.0), 0.0], [0.0, 0.0]])
+    W13 = rng.standard_normal((2, 2 * F, d))
+    W2 = rng.standard_normal((2, d, F))
+    out = O.layer_forward(x, Wg, W13, W2, O.LayerSpec(E=2, k=2))
+    A = _ffn_torch(x, W13[0], W2[0]).numpy()
+    B = _ffn_torch(x, W13[1], W2[1]).numpy()
+    np.testing.assert_allclose(out["y"], wa * A + wb * B, rtol=1e-13, atol=1e-13)
+
+
+def test_four_gpu_scenario_counts_maxvio_buffer():
+    g = gold("four_gpu_loads.json")
+    T, k, E = g["tokens"], g["top_k"], g["experts"]
+    labels = np.repeat(np.arange(E), g["loads"])          # 8192 expert labels
+    assert labels.size == g["assignments"]
+    idx = np.stack([labels[:T], labels[T:]], axis=1)       # token t gets labels t and t+T
+    assert np.all(idx[:, 0] != idx[:, 1])
+    counts = O.expert_counts(idx, E)
+    assert counts.tolist() == g["loads"]
+    assert counts.sum() == T * k == g["assignments"]
+    assert O.max_violation(counts) == g["maxvio"]
+    assert counts.mean() == g["even_load_per_expert"]
+    perm = O.permutation(idx, E)
+    assert perm.token_of.size == g["assignments"]
+    assert O.permuted_buffer_bytes(T, k, g["values_per_vector"], g["bytes_per_value"]) == g["permuted_input_bytes"]
+    assert g["permuted_input_bytes"] == 32 * 2 ** 20
+
+
+def test_first_moe_shapes_and_extremes():
+    g = gold("first_moe.json")
+    d, F = g["d_model"], g["expert_ffn"]
+    assert O.expert_param_count(d, F) == g["params_per_expert"]
+    assert 8 * O.expert_param_count(d, F) == g["params_eight_experts"] == 3 * d * g["dense_ffn_width"]
+    # busiest expert receives every token: MaxVio = E/k - 1 = 7 at 64 experts, top-8
+    E, k, T = g["num_experts"], g["top_k"], 4096
+    idx = np.zeros((T, k), dtype=np.int64)
+    idx[:, 0] = 0
+    rest = np.arange(T * (k - 1)) % (E - 1) + 1
+    idx[:, 1:] = rest.reshape(T, k - 1)
+    idx[:, 1:] = (np.arange(T)[:, None] * (k - 1) + np.arange(k - 1)[None, :]) % (E - 1) + 1
+    assert all(len(set(r)) == k for r in idx.tolist())
+    assert O.max_violation(O.expert_counts(idx, E)) == g["most_biased_maxvio"]
+
+
+def test_single_expert_lb_loss_is_one_and_router_gets_no_gradient():
+    g = gold("first_moe.json")
+    rng = np.random.default_rng(1)
+    L, spec = _rand_layer(rng, T=32, d=8, E=1, k=1, F=6, aux=1e-3)
+    f = O.layer_forward(L["x"], L["Wg"], L["W13"], L["W2"], spec)
+    assert f["route"]["aux"] / spec.aux_coeff == pytest.approx(g["one_expert_load_balancing_loss"], abs=1e-15)
+    b = O.layer_backward(f, L["x"], L["Wg"], L["W13"], L["W2"], L["dy"], spec)
+    assert np.all(b["dlogits"] == 0.0) and np.all(b["dWg"] == 0.0)
+    # and the one-expert layer is the dense FFN (independent torch implementation)
+    np.testing.assert_allclose(f["y"], _ffn_torch(L["x"], L["W13"][0], L["W2"][0]).numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------------- router
+
+def test_topk_matches_brute_force_with_ties():
+    rng = np.random.default_rng(2)
+    for trial in range(300):
+        E = int(rng.integers(2, 8))
+        k = int(rng.integers(1, E + 1))
+        levels = int(rng.integers(1, 4)) if trial % 2 else 1000
+        keys = rng.integers(0, levels, size=(1, E)).astype(np.float64) + (0 if levels < 1000 else rng.random((1, E)))
+        got = O.topk(keys, k)[0].tolist()
+        assert got == O.brute_force_topk(keys[0], k), (keys, k)
+
+
+def test_constructed_ties_go_to_lower_index():
+    keys = np.array([[0.5, 1.0, 1.0, 0.2, 1.0]])
+    assert O.topk(keys, 2).tolist() == [[1, 2]]
+    assert O.topk(keys, 4).tolist() == [[1, 2, 4, 0]]
+    assert O.topk(np.zeros((1, 6)), 3).tolist() == [[0, 1, 2]]
+
+
+def test_weights_sum_to_one_or_scaling():
+    rng = np.random.default_rng(3)
+    l = rng.standard_normal((64, 16)) * 2
+    for score in ("softmax", "sigmoid"):
+        for c in (1.0, 2.5):
+            idx = O.topk(O.selection_keys(l, score), 4)
+            w = O.mixing_weights(l, idx, score, c)
+            np.testing.assert_allclose(w.sum(1), c, rtol=1e-14)
+            assert np.all(w > 0)
+
+
+def test_softmax_weights_equal_renormalised_full_softmax():
+    rng = np.random.default_rng(4)
+    l = rng.standard_normal((32, 12))
+    idx = O.topk(l, 3)
+    p = torch.softmax(torch.as_tensor(l), dim=1).numpy()     # library softmax over all E
+    pS = np.take_along_axis(p, idx, axis=1)
+    np.testing.assert_allclose(O.mixing_weights(l, idx, "softmax"), pS / pS.sum(1, keepdims=True), rtol=1e-13)
+
+
+def test_sigmoid_matches_library_and_bias_selects_only():
+    rng = np.random.default_rng(5)
+    l = rng.standard_normal((256, 16)) * 2
+    np.testing.assert_allclose(O.sigmoid(l), expit(l), rtol=1e-15)
+    bias = rng.standard_normal(16) * 0.3
+    idx_b = O.topk(O.selection_keys(l, "sigmoid", bias), 4)
+    idx_0 = O.topk(O.selection_keys(l, "sigmoid"), 4)
+    assert np.any(idx_b != idx_0)                 # the bias does change the selection ...
+    w = O.mixing_weights(l, idx_b, "sigmoid")
+    s = expit(np.take_along_axis(l, idx_b, axis=1))
+    np.testing.assert_allclose(w, s / s.sum(1, keepdims=True), rtol=1e-14)  # ... but not the weights
+    # k = 1 sigmoid: the raw score, no renormalisation
+    idx1 = O.topk(O.selection_keys(l, "sigmoid"), 1)
+    np.testing.assert_allclose(O.mixing_weights(l, idx1, "sigmoid"), expit(np.take_along_axis(l, idx1, 1)), rtol=1e-15)
+
+
+def test_shift_invariance():
+    rng = np.random.default_rng(6)
+    l = rng.standard_normal((128, 16))
+    idx = O.topk(l, 4)
+    assert np.array_equal(O.topk(l + 3.25, 4), idx)
+    np.testing.assert_allclose(O.mixing_weights(l + 3.25, idx, "softmax"), O.mixing_weights(l, idx, "softmax"), rtol=1e-13)
+    bias = rng.standard_normal(16) * 0.1
+    assert np.array_equal(O.topk(O.selection_keys(l, "sigmoid", bias + 0.5), 4),
+                          O.topk(O.selection_keys(l, "sigmoid", bias), 4))
+
+
+def test_top1_post_softmax_weight_one_and_no_router_gradient():
+    rng = np.random.default_rng(7)
+    L, spec = _rand_layer(rng, T=24, d=6, E=4, k=1, F=4)
+    f = O.layer_forward(L["x"], L["Wg"], L["W13"], L["W2"], spec)
+    assert np.all(f["route"]["w"] == 1.0)
+    b = O.layer_backward(f, L["x"], L["Wg"], L["W13"], L["W2"], L["dy"], spec)
+    assert np.all(b["dlogits"] == 0.0)
+    assert np.any(b["dw"] != 0.0)
+
+
+def test_aux_loss_closed_forms():
+    rng = np.random.default_rng(8)
+    T, E, k = 200, 8, 2
+    # flat router probabilities: aux / coeff = 1 whatever the load
+    for _ in range(5):
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+        counts = O.expert_counts(idx, E)
+        assert O.aux_loss(counts, np.full((T, E), 1.0 / E), k, 1.0) == pytest.approx(1.0, abs=1e-14)
+    # a one-hot router that sends every token's whole probability to expert 0, which
+    # is also in every token's top-k: f_0 = 1/k, P_0 = 1 -> aux / coeff = E / k
+    idx = np.stack([np.r_[0, rng.permutation(np.arange(1, E))[:k - 1]] for _ in range(T)])
+    p = np.zeros((T, E)); p[:, 0] = 1.0
+    assert O.aux_loss(O.expert_counts(idx, E), p, k, 1.0) == pytest.approx(E / k, rel=1e-15)
+    # counts always sum to T * k
+    l = rng.standard_normal((T, E))
+    assert O.expert_counts(O.topk(l, k), E).sum() == T * k
+
+
+def test_aux_loss_matches_printed_code_form():
+    # the handbook's code form: sum(probs.sum(0) * tokens_per_expert) * E * coeff / (k * T * T)
+    rng = np.random.default_rng(9)
+    T, E, k, c = 97, 10, 3, 0.013
+    l = rng.standard_normal((T, E))
+    idx = O.topk(l, k)
+    probs = torch.softmax(torch.as_tensor(l), dim=1)
+    tpe = torch.bincount(torch.as_tensor(idx).flatten(), minlength=E).double()
+    code = float(torch.sum(probs.sum(0) * tpe) * (E * c / (k * T * T)))
+    assert O.aux_loss(O.expert_counts(idx, E), O.softmax_full(l), k, c) == pytest.approx(code, rel=1e-13)
+
+
+# ------------------------------------------------------------------- permutation
+
+def test_permutation_is_valid_and_matches_counting_sort():
+    rng = np.random.default_rng(10)
+    for T, E, k in [(1, 1, 1), (7, 3, 2), (50, 9, 4), (300, 32, 8), (64, 64, 64)]:
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+        p = O.permutation(idx, E)
+        # independent construction: a pure-Python counting sort
+        buckets = [[] for _ in range(E)]
+        for t in range(T):
+            for j in range(k):
+                buckets[idx[t, j]].append((t, j))
+        flat = [tj for b in buckets for tj in b]
+        assert [t for t, _ in flat] == p.token_of.tolist()
+        for r, (t, j) in enumerate(flat):
+            assert p.row_of[t, j] == r
+        assert p.offsets[0] == 0 and p.offsets[-1] == T * k
+        assert np.all(np.diff(p.offsets) >= 0)
+        assert np.array_equal(p.token_of[p.row_of], np.repeat(np.arange(T)[:, None], k, 1))
+
+
+# ------------------------------------------------------------------------- experts
+
+def test_swiglu_matches_torch_and_silu_matches_library():
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((9, 6)); W13 = rng.standard_normal((10, 6)); W2 = rng.standard_normal((6, 5))
+    H, Act, Y = O.swiglu_forward(X, W13, W2)
+    np.testing.assert_allclose(Y, _ffn_torch(X, W13, W2).numpy(), rtol=1e-12, atol=1e-12)
+    g = rng.standard_normal(1000) * 5
+    np.testing.assert_allclose(O.silu(g), g * expit(g), rtol=1e-14, atol=1e-300)
+
+
+def test_identical_experts_make_routing_irrelevant():
+    rng = np.random.default_rng(12)
+    L, spec = _rand_layer(rng, T=40, d=8, E=6, k=3, F=5, Fs=4, score="sigmoid", scaling=2.5)
+    W13 = np.repeat(L["W13"][:1], 6, 0); W2 = np.repeat(L["W2"][:1], 6, 0)
+    f = O.layer_forward(L["x"], L["Wg"], W13, W2, spec, W13s=L["W13s"], W2s=L["W2s"])
+    ref = 2.5 * _ffn_torch(L["x"], W13[0], W2[0]).numpy() + _ffn_torch(L["x"], L["W13s"], L["W2s"]).numpy()
+    np.testing.assert_allclose(f["y"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_against_independent_token_loop():
+    """The vectorised layer equals a per-token loop over torch's dense FFNs."""
+    rng = np.random.default_rng(13)
+    L, spec = _rand_layer(rng, T=30, d=8, E=5, k=2, F=6, Fs=3, score="softmax", bias="bg")
+    f = O.layer_forward(L["x"], L["Wg"], L["W13"], L["W2"], spec, bg=L["bg"], W13s=L["W13s"], W2s=L["W2s"])
+    logits = torch.as_tensor(L["x"]) @ torch.as_tensor(L["Wg"]).T + torch.as_tensor(L["bg"])
+    for t in range(30):
+        vals, ids = torch.topk(logits[t], 2)
+        w = torch.softmax(vals, 0)
+        y = _ffn_torch(L["x"][t:t + 1], L["W13s"], L["W2s"])[0]
+        for j in range(2):
+            e = int(ids[j])
+            y = y + w[j] * _ffn_torch(L["x"][t:t + 1], L["W13"][e], L["W2"][e])[0]
+        np.testing.assert_allclose(f["y"][t], y.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------------ backward
+
+@pytest.mark.parametrize("case", [
+    dict(score="softmax", k=2, aux=0.7, Fs=0, scaling=1.0, bias="bg"),
+    dict(score="softmax", k=3, aux=0.0, Fs=4, scaling=2.5, bias=None),
+    dict(score="sigmoid", k=2, aux=0.0, Fs=4, scaling=1.0, bias="expert_bias"),
+    dict(score="sigmoid", k=1, aux=0.0, Fs=0, scaling=1.3, bias=None),
+])
+def test_backward_matches_central_differences(case):
+    rng = np.random.default_rng(14)
+    L, spec = _rand_layer(rng, T=16, d=8, E=4, k=case["k"], F=8, Fs=case["Fs"], score=case["score"],
+                          scaling=case["scaling"], aux=case["aux"], bias=case["bias"])
+    keys = O.selection_keys(O.gate_logits(L["x"], L["Wg"], L["bg"]), spec.score, L["expert_bias"])
+    assert O.margins(keys, spec.k).min() > 1e-4           # far from a routing flip
+    kw = dict(bg=L["bg"], expert_bias=L["expert_bias"], W13s=L["W13s"], W2s=L["W2s"])
+    f = O.layer_forward(L["x"], L["Wg"], L["W13"], L["W2"], spec, **kw)
+    b = O.layer_backward(f, L["x"], L["Wg"], L["W13"], L["W2"], L["dy"], spec,
+                         W13s=L["W13s"], W2s=L["W2s"], daux=1.0)
+    names = [("x", "dx"), ("Wg", "dWg"), ("W13", "dW13"), ("W2", "dW2")]
+    if L["bg"] is not None:
+        names.append(("bg", "dbg"))
+    if case["Fs"]:
+        names += [("W13s", "dW13s"), ("W2s", "dW2s")]
+    h = 1e-6
+    for pname, gname in names:
+        P = L[pname]
+        flat = P.reshape(-1)
+        picks = rng.choice(flat.size, size=min(flat.size, 40), replace=False)
+        for i in picks:
+            old = flat[i]
+            flat[i] = old + h
+            lp = O.layer_loss(L["x"], L["Wg"], L["W13"], L["W2"], L["dy"], spec, **kw)
+            flat[i] = old - h
+            lm = O.layer_loss(L["x"], L["Wg"], L["W13"], L["W2"], L["dy"], spec, **kw)
+            flat[i] = old
+            fd = (lp - lm) / (2 * h)
+            an = b[gname].reshape(-1)[i]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (pname, i, fd, an)
