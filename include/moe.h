@@ -1,0 +1,229 @@
+/*
+ * libmoe: one Mixture-of-Experts layer, forward and backward, on one AMD Instinct
+ * MI355X (gfx950).  Plain C ABI: every tensor argument is a DEVICE pointer that the
+ * caller allocated; sizes come from moe_config_t; `stream` is a hipStream_t (NULL =
+ * the default stream).  The library allocates nothing, keeps no state between calls
+ * and never synchronises the host: every call only enqueues kernels on `stream`.
+ *
+ * Sources, cited by page title and section:
+ *   [HB] "The Ultimate MoE Training Handbook" (Hugging Face).
+ *   [LC] LeCompute, "MoE training: cluster, routing, load balancing".
+ *
+ * Notation: T tokens, d model width, E routed experts, k experts per token, F expert
+ * FFN width, Fs shared-expert width (0 = none), A = T*k routed rows.
+ *
+ * Layouts (all row-major, contiguous):
+ *   x, y, dy, dx          [T, d]      activation dtype (act_dtype)
+ *   Wg                    [E, d]      fp32        router weight ([HB] §3.4 Count and size)
+ *   W13                   [E, 2F, d]  act dtype   fc1 of each expert, gate rows then up rows
+ *   W2                    [E, d, F]   act dtype   fc2 of each expert
+ *   W13s [2Fs, d], W2s [d, Fs]        act dtype   shared expert
+ *   logits, dlogits       [T, E]      fp32
+ *   idx [T, k] int32, w [T, k] fp32   slot j: j-th best expert (key descending, ties to the
+ *                                     lower expert index) and its mixing weight
+ *   counts [E] int32, offsets [E+1] int32, row_of [T, k] int32, token_of [A] int32
+ *   x_perm, Y_perm        [A, d]      act dtype, rows grouped by expert ascending, and by
+ *                                     token ascending inside an expert
+ *   H [A, 2F], Act [A, F]             act dtype
+ *
+ * Errors: every argument is checked on the host before anything is launched.  A call
+ * that fails a check launches nothing and returns MOE_ERR_INVALID_ARG,
+ * MOE_ERR_UNSUPPORTED or MOE_ERR_WORKSPACE; a failed launch returns MOE_ERR_HIP.
+ * moe_last_error() gives the text of the last failure on the calling thread.
+ * Numerical faults (non-finite inputs) are not detected.
+ *
+ * Determinism: no floating-point atomics; every reduction runs in a fixed order, so
+ * repeated calls on the same inputs give bit-identical outputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* [HB] §3.1 Router scoring, Gating function. */
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_t;
+
+#define MOE_NSTATS 4 /* stats[]: aux loss, MaxVio, number of empty experts, max count */
+
+/*
+ * The layer's settings, mirroring the flags of [HB] §2.5 Your first MoE (number of
+ * experts, expert FFN width, top-k), §3.1 (score function, routed scaling factor),
+ * §3.3 Aux loss (coefficient) and §3.4 Shared experts (shared width).
+ * Rules checked by moe_validate:
+ *   1 <= k <= min(E, 32), E <= 2048, T >= 1, T*k < 2^31, d % 64 == 0, F % 64 == 0,
+ *   Fs % 64 == 0; bf16: F % 128 == 0 and Fs % 128 == 0;
+ *   softmax with k == 1 needs pre-softmax, which is not provided: UNSUPPORTED
+ *   ([HB] §3.1 Output scale: a softmax over one logit has no gradient);
+ *   pre_softmax must be 0 (UNSUPPORTED otherwise);
+ *   aux_coeff != 0 only with softmax scores (UNSUPPORTED otherwise).
+ */
+typedef struct moe_config {
+  int32_t T, d, E, k, F, Fs;
+  int32_t score;          /* moe_score_t */
+  int32_t pre_softmax;    /* must be 0 */
+  float routed_scaling;   /* multiplies the renormalised weights ([HB] §3.1 Output scale) */
+  float aux_coeff;        /* Switch aux-loss coefficient ([HB] §3.3 Aux loss) */
+  int32_t act_dtype;      /* moe_dtype_t of activations and expert weights */
+  int32_t reserved;       /* must be 0 */
+} moe_config_t;
+
+typedef struct moe_weights {
+  const float* Wg;          /* [E, d] fp32 */
+  const float* bg;          /* [E] fp32 additive logit bias, or NULL */
+  const float* expert_bias; /* [E] fp32 selection-only bias (sigmoid only), or NULL */
+  const void* W13;          /* [E, 2F, d] */
+  const void* W2;           /* [E, d, F] */
+  const void* W13s;         /* [2Fs, d], NULL when Fs == 0 */
+  const void* W2s;          /* [d, Fs],  NULL when Fs == 0 */
+} moe_weights_t;
+
+/* Tensors the forward writes and the backward reads (all caller-owned). */
+typedef struct moe_saved {
+  float* logits;     /* [T, E] */
+  int32_t* idx;      /* [T, k] */
+  float* w;          /* [T, k] */
+  int32_t* counts;   /* [E] */
+  int32_t* offsets;  /* [E+1] */
+  int32_t* row_of;   /* [T, k] */
+  int32_t* token_of; /* [A] */
+  void* x_perm;      /* [A, d] */
+  void* H;           /* [A, 2F] */
+  void* Act;         /* [A, F] */
+  void* Y_perm;      /* [A, d] */
+  void* H_s;         /* [T, 2Fs] or NULL when Fs == 0 */
+  void* Act_s;       /* [T, Fs]  or NULL */
+  void* Y_s;         /* [T, d]   or NULL */
+} moe_saved_t;
+
+/* Gradients written by moe_layer_bwd (overwritten, not accumulated). */
+typedef struct moe_grads {
+  float* dWg;  /* [E, d] fp32 */
+  float* dbg;  /* [E] fp32, or NULL */
+  void* dW13;  /* [E, 2F, d] act dtype; experts with no rows get exact zeros */
+  void* dW2;   /* [E, d, F] act dtype */
+  void* dW13s; /* [2Fs, d] or NULL when Fs == 0 */
+  void* dW2s;  /* [d, Fs]  or NULL */
+} moe_grads_t;
+
+const char* moe_status_string(moe_status_t status);
+const char* moe_last_error(void);
+
+/* Checks the configuration rules listed at moe_config_t.  Host only. */
+moe_status_t moe_validate(const moe_config_t* cfg);
+
+/* Workspace bytes the forward (router, permute, layer forward) and backward calls need.
+ * Host only.  One workspace of max(fwd, bwd) bytes serves every call. */
+moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* fwd_bytes, size_t* bwd_bytes);
+
+/* Router logits = x Wg^T (+ bg), fp32 ([HB] §3.1 Router scoring, Precision: the router's
+ * linear layer runs in fp32).  x act dtype [T, d]; logits [T, E]. */
+moe_status_t moe_gate_logits(const moe_config_t* cfg, const void* x, const float* Wg, const float* bg,
+                             float* logits, void* stream);
+
+/* Top-k router ([HB] §3.1 Gating function and Output scale; §3.3 Aux loss):
+ *   keys: softmax -> the logits; sigmoid -> sigma(l) + expert_bias, evaluated in fp64;
+ *   idx: top-k of the keys, ties to the lower expert index;
+ *   w:   softmax over the k selected logits, or sigma(l_S) / (sum + 1e-20) (k > 1), times
+ *        routed_scaling;
+ *   counts[e]: tokens routed to e; prob_sum[e] = sum_t softmax(l_t)_e (softmax only, NULL ok);
+ *   stats[MOE_NSTATS] (NULL ok): aux = coeff * E * sum_e f_e P_e, MaxVio, empty experts,
+ *   max count.  expert_bias must be NULL for softmax. */
+moe_status_t moe_router_topk(const moe_config_t* cfg, const float* logits, const float* expert_bias,
+                             int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* stats,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Dropless permutation ([LC] "Read the timeline before blaming the network": tokens are
+ * grouped by expert before the expert matmuls): offsets = exclusive prefix of the
+ * per-expert counts; row_of[t, j] = row of (t, j); token_of[row] = t;
+ * x_perm[row_of[t, j]] = x[t]. */
+moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* idx, int32_t* offsets,
+                         int32_t* row_of, int32_t* token_of, void* x_perm, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Grouped SwiGLU experts ([HB] §3.4 Count and size, Activation): for each expert e, on its
+ * rows [offsets[e], offsets[e+1]):  H = X W13[e]^T, Act = silu(H[:, :F]) * H[:, F:],
+ * Y_perm = Act W2[e]^T.  When Fs > 0 the shared expert runs the same on x (all T rows)
+ * into H_s, Act_s, Y_s ([HB] §3.4 Shared experts). */
+moe_status_t moe_grouped_gemm_swiglu(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
+                                     const void* W13, const void* W2, const void* x, const void* W13s,
+                                     const void* W2s, void* H, void* Act, void* Y_perm, void* H_s,
+                                     void* Act_s, void* Y_s, void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine ([LC] "An expert transforms numbers inside the model": the weighted
+ * sum of the selected outputs, coordinate by coordinate; [HB] §3.4 Shared experts: the
+ * shared output is added at weight 1):
+ *   y[t] = sum_j w[t, j] * Y_perm[row_of[t, j]] (+ Y_s[t]), fp32 accumulation, slot order. */
+moe_status_t moe_unpermute_combine(const moe_config_t* cfg, const void* Y_perm, const int32_t* row_of,
+                                   const float* w, const void* Y_s, void* y, void* stream);
+
+/* Whole forward: gate logits, router, permute, grouped experts (+ shared), combine.
+ * Fills *saved for the backward.  stats as in moe_router_topk (NULL ok). */
+moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* weights, const void* x,
+                           const moe_saved_t* saved, void* y, float* stats, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* ---------------------------------------------------------------- backward pieces
+ * Derivatives of L = sum(dy * y) + daux * aux; mixing weights carry the gradient to
+ * the router, selection carries none ([LC] "How the router learns without an
+ * expert-selection answer key"). */
+
+/* dY_perm[row_of[t, j]] = w[t, j] * dy[t];  dw[t, j] = <dy[t], Y_perm[row_of[t, j]]>. */
+moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const void* dy, const void* Y_perm,
+                                       const int32_t* row_of, const float* w, void* dY_perm, float* dw,
+                                       void* stream);
+
+/* Expert backward, per expert e on its rows (and the shared expert on all T rows with
+ * upstream gradient dy, when Fs > 0):
+ *   dAct = dY W2[e];  dH = [dAct * up * silu'(gate), dAct * silu(gate)];
+ *   dW2[e] = dY^T Act;  dX = dH W13[e];  dW13[e] = dH^T X.
+ * dX_perm may alias dY_perm (dY_perm is consumed before dX_perm is written).
+ * dH [A, 2F] and dH_s [T, 2Fs] are outputs too.  dx_s [T, d] receives the shared
+ * expert's input gradient. */
+moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
+                                         const void* W13, const void* W2, const void* H, const void* Act,
+                                         const void* dY_perm, void* dH, void* dX_perm, void* dW13, void* dW2,
+                                         const void* x, const void* W13s, const void* W2s, const void* H_s,
+                                         const void* Act_s, const void* dy, void* dH_s, void* dx_s,
+                                         void* dW13s, void* dW2s, void* ws, size_t ws_bytes, void* stream);
+
+/* Unpermute-reduce: dx[t] = sum_j dX_perm[row_of[t, j]] (+ dx_s[t]) (+ dx_r[t]),
+ * fp32 accumulation in that order.  dx_s act dtype or NULL; dx_r fp32 or NULL. */
+moe_status_t moe_permute_bwd(const moe_config_t* cfg, const void* dX_perm, const int32_t* row_of,
+                             const void* dx_s, const float* dx_r, void* dx, void* stream);
+
+/* Router backward: dlogits [T, E] from dw [T, k] through the weights of the selected
+ * experts, plus daux times the aux-loss gradient through the full softmax (counts held
+ * constant).  counts may be NULL when aux_coeff == 0 or daux == 0. */
+moe_status_t moe_router_bwd(const moe_config_t* cfg, const float* logits, const int32_t* idx, const float* w,
+                            const float* dw, const int32_t* counts, float daux, float* dlogits, void* stream);
+
+/* Gate backward: dWg = dlogits^T x [E, d]; dbg = column sums of dlogits (NULL ok);
+ * dx_r = dlogits Wg [T, d] fp32 (NULL ok). */
+moe_status_t moe_gate_logits_bwd(const moe_config_t* cfg, const void* x, const float* Wg,
+                                 const float* dlogits, float* dWg, float* dbg, float* dx_r, void* stream);
+
+/* Whole backward from the saved forward tensors. */
+moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* weights, const moe_saved_t* saved,
+                           const void* x, const void* dy, float daux, void* dx, const moe_grads_t* grads,
+                           void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

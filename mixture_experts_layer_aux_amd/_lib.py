@@ -1,0 +1,312 @@
+"""ctypes binding of libmoe (include/moe.h): argument marshalling only.
+
+Each function takes torch tensors (device memory owned by the caller), checks their
+dtype, size and contiguity, and passes raw device pointers plus the current HIP stream
+to the C entry point of the same name.  All arithmetic runs in the HIP kernels; if
+libmoe.so is missing every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_NSTATS = 4
+
+EXPORTED = (
+    "moe_status_string", "moe_last_error", "moe_validate", "moe_workspace_size", "moe_gate_logits",
+    "moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu", "moe_unpermute_combine", "moe_layer_fwd",
+    "moe_unpermute_combine_bwd", "moe_grouped_gemm_swiglu_bwd", "moe_permute_bwd", "moe_router_bwd",
+    "moe_gate_logits_bwd", "moe_layer_bwd",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libmoe status {status}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("F", ctypes.c_int32), ("Fs", ctypes.c_int32), ("score", ctypes.c_int32),
+                ("pre_softmax", ctypes.c_int32), ("routed_scaling", ctypes.c_float), ("aux_coeff", ctypes.c_float),
+                ("act_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("Wg", _P), ("bg", _P), ("expert_bias", _P), ("W13", _P), ("W2", _P), ("W13s", _P), ("W2s", _P)]
+
+
+class Saved(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("logits", "idx", "w", "counts", "offsets", "row_of", "token_of", "x_perm", "H",
+                                  "Act", "Y_perm", "H_s", "Act_s", "Y_s")]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("dWg", "dbg", "dW13", "dW2", "dW13s", "dW2s")]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m mixture_experts_layer_aux_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.moe_status_string.restype = ctypes.c_char_p
+        lib.moe_status_string.argtypes = [ctypes.c_int]
+        lib.moe_last_error.restype = ctypes.c_char_p
+        lib.moe_last_error.argtypes = []
+        for name in EXPORTED[2:]:
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        lib = load()
+        raise MoeError(status, f"{lib.moe_status_string(status).decode()}: {lib.moe_last_error().decode()}")
+
+
+def make_config(T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux_coeff=0.0, act="bf16") -> Config:
+    return Config(T=T, d=d, E=E, k=k, F=F, Fs=Fs, score=MOE_SOFTMAX if score == "softmax" else MOE_SIGMOID,
+                  pre_softmax=0, routed_scaling=scaling, aux_coeff=aux_coeff,
+                  act_dtype=MOE_BF16 if act == "bf16" else MOE_F32, reserved=0)
+
+
+def config_from_shape(s) -> Config:
+    return make_config(s.T, s.d, s.E, s.k, s.F, s.Fs, s.score, s.scaling, s.aux_coeff, s.act)
+
+
+def act_dtype(cfg: Config) -> torch.dtype:
+    return torch.bfloat16 if cfg.act_dtype == MOE_BF16 else torch.float32
+
+
+def validate(cfg: Config) -> None:
+    _check(load().moe_validate(ctypes.byref(cfg)))
+
+
+def workspace_size(cfg: Config) -> Tuple[int, int]:
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(load().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
+
+
+# ----------------------------------------------------------------- marshalling helpers
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, numel=None, name="tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ws(ws: torch.Tensor) -> Tuple[int, int]:
+    return _ptr(ws, torch.uint8, name="ws"), ws.numel()
+
+
+# ----------------------------------------------------------------- entry points
+
+def gate_logits(cfg, x, Wg, bg, logits, stream=None):
+    ad = act_dtype(cfg)
+    _check(load().moe_gate_logits(ctypes.byref(cfg), _P(_ptr(x, ad, cfg.T * cfg.d, "x")),
+                                  _P(_ptr(Wg, torch.float32, cfg.E * cfg.d, "Wg")),
+                                  _P(_ptr(bg, torch.float32, cfg.E, "bg")),
+                                  _P(_ptr(logits, torch.float32, cfg.T * cfg.E, "logits")), _P(_stream(stream))))
+
+
+def router_topk(cfg, logits, expert_bias, idx, w, counts, prob_sum, stats, ws, stream=None):
+    wp, wn = _ws(ws)
+    TK = cfg.T * cfg.k
+    _check(load().moe_router_topk(ctypes.byref(cfg), _P(_ptr(logits, torch.float32, cfg.T * cfg.E, "logits")),
+                                  _P(_ptr(expert_bias, torch.float32, cfg.E, "expert_bias")),
+                                  _P(_ptr(idx, torch.int32, TK, "idx")), _P(_ptr(w, torch.float32, TK, "w")),
+                                  _P(_ptr(counts, torch.int32, cfg.E, "counts")),
+                                  _P(_ptr(prob_sum, torch.float32, cfg.E, "prob_sum")),
+                                  _P(_ptr(stats, torch.float32, MOE_NSTATS, "stats")), _P(wp), ctypes.c_size_t(wn),
+                                  _P(_stream(stream))))
+
+
+def permute(cfg, x, idx, offsets, row_of, token_of, x_perm, ws, stream=None):
+    ad, TK = act_dtype(cfg), cfg.T * cfg.k
+    wp, wn = _ws(ws)
+    _check(load().moe_permute(ctypes.byref(cfg), _P(_ptr(x, ad, cfg.T * cfg.d, "x")),
+                              _P(_ptr(idx, torch.int32, TK, "idx")), _P(_ptr(offsets, torch.int32, cfg.E + 1, "offsets")),
+                              _P(_ptr(row_of, torch.int32, TK, "row_of")), _P(_ptr(token_of, torch.int32, TK, "token_of")),
+                              _P(_ptr(x_perm, ad, TK * cfg.d, "x_perm")), _P(wp), ctypes.c_size_t(wn),
+                              _P(_stream(stream))))
+
+
+def grouped_gemm_swiglu(cfg, x_perm, offsets, W13, W2, x, W13s, W2s, H, Act, Y_perm, H_s, Act_s, Y_s, ws,
+                        stream=None):
+    ad, A, T, d, E, F, Fs = act_dtype(cfg), cfg.T * cfg.k, cfg.T, cfg.d, cfg.E, cfg.F, cfg.Fs
+    wp, wn = _ws(ws)
+    _check(load().moe_grouped_gemm_swiglu(
+        ctypes.byref(cfg), _P(_ptr(x_perm, ad, A * d, "x_perm")), _P(_ptr(offsets, torch.int32, E + 1, "offsets")),
+        _P(_ptr(W13, ad, E * 2 * F * d, "W13")), _P(_ptr(W2, ad, E * d * F, "W2")),
+        _P(_ptr(x, ad, T * d, "x")), _P(_ptr(W13s, ad, 2 * Fs * d, "W13s")), _P(_ptr(W2s, ad, d * Fs, "W2s")),
+        _P(_ptr(H, ad, A * 2 * F, "H")), _P(_ptr(Act, ad, A * F, "Act")), _P(_ptr(Y_perm, ad, A * d, "Y_perm")),
+        _P(_ptr(H_s, ad, T * 2 * Fs, "H_s")), _P(_ptr(Act_s, ad, T * Fs, "Act_s")), _P(_ptr(Y_s, ad, T * d, "Y_s")),
+        _P(wp), ctypes.c_size_t(wn), _P(_stream(stream))))
+
+
+def unpermute_combine(cfg, Y_perm, row_of, w, Y_s, y, stream=None):
+    ad, A = act_dtype(cfg), cfg.T * cfg.k
+    _check(load().moe_unpermute_combine(ctypes.byref(cfg), _P(_ptr(Y_perm, ad, A * cfg.d, "Y_perm")),
+                                        _P(_ptr(row_of, torch.int32, A, "row_of")), _P(_ptr(w, torch.float32, A, "w")),
+                                        _P(_ptr(Y_s, ad, cfg.T * cfg.d, "Y_s")), _P(_ptr(y, ad, cfg.T * cfg.d, "y")),
+                                        _P(_stream(stream))))
+
+
+def unpermute_combine_bwd(cfg, dy, Y_perm, row_of, w, dY_perm, dw, stream=None):
+    ad, A = act_dtype(cfg), cfg.T * cfg.k
+    _check(load().moe_unpermute_combine_bwd(ctypes.byref(cfg), _P(_ptr(dy, ad, cfg.T * cfg.d, "dy")),
+                                            _P(_ptr(Y_perm, ad, A * cfg.d, "Y_perm")),
+                                            _P(_ptr(row_of, torch.int32, A, "row_of")),
+                                            _P(_ptr(w, torch.float32, A, "w")),
+                                            _P(_ptr(dY_perm, ad, A * cfg.d, "dY_perm")),
+                                            _P(_ptr(dw, torch.float32, A, "dw")), _P(_stream(stream))))
+
+
+def grouped_gemm_swiglu_bwd(cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, dX_perm, dW13, dW2, x, W13s, W2s,
+                            H_s, Act_s, dy, dH_s, dx_s, dW13s, dW2s, ws, stream=None):
+    ad, A, T, d, E, F, Fs = act_dtype(cfg), cfg.T * cfg.k, cfg.T, cfg.d, cfg.E, cfg.F, cfg.Fs
+    wp, wn = _ws(ws)
+    _check(load().moe_grouped_gemm_swiglu_bwd(
+        ctypes.byref(cfg), _P(_ptr(x_perm, ad, A * d, "x_perm")), _P(_ptr(offsets, torch.int32, E + 1, "offsets")),
+        _P(_ptr(W13, ad, E * 2 * F * d, "W13")), _P(_ptr(W2, ad, E * d * F, "W2")), _P(_ptr(H, ad, A * 2 * F, "H")),
+        _P(_ptr(Act, ad, A * F, "Act")), _P(_ptr(dY_perm, ad, A * d, "dY_perm")), _P(_ptr(dH, ad, A * 2 * F, "dH")),
+        _P(_ptr(dX_perm, ad, A * d, "dX_perm")), _P(_ptr(dW13, ad, E * 2 * F * d, "dW13")),
+        _P(_ptr(dW2, ad, E * d * F, "dW2")), _P(_ptr(x, ad, T * d, "x")), _P(_ptr(W13s, ad, 2 * Fs * d, "W13s")),
+        _P(_ptr(W2s, ad, d * Fs, "W2s")), _P(_ptr(H_s, ad, T * 2 * Fs, "H_s")), _P(_ptr(Act_s, ad, T * Fs, "Act_s")),
+        _P(_ptr(dy, ad, T * d, "dy")), _P(_ptr(dH_s, ad, T * 2 * Fs, "dH_s")), _P(_ptr(dx_s, ad, T * d, "dx_s")),
+        _P(_ptr(dW13s, ad, 2 * Fs * d, "dW13s")), _P(_ptr(dW2s, ad, d * Fs, "dW2s")), _P(wp), ctypes.c_size_t(wn),
+        _P(_stream(stream))))
+
+
+def permute_bwd(cfg, dX_perm, row_of, dx_s, dx_r, dx, stream=None):
+    ad, A = act_dtype(cfg), cfg.T * cfg.k
+    _check(load().moe_permute_bwd(ctypes.byref(cfg), _P(_ptr(dX_perm, ad, A * cfg.d, "dX_perm")),
+                                  _P(_ptr(row_of, torch.int32, A, "row_of")), _P(_ptr(dx_s, ad, cfg.T * cfg.d, "dx_s")),
+                                  _P(_ptr(dx_r, torch.float32, cfg.T * cfg.d, "dx_r")),
+                                  _P(_ptr(dx, ad, cfg.T * cfg.d, "dx")), _P(_stream(stream))))
+
+
+def router_bwd(cfg, logits, idx, w, dw, counts, daux, dlogits, stream=None):
+    A = cfg.T * cfg.k
+    _check(load().moe_router_bwd(ctypes.byref(cfg), _P(_ptr(logits, torch.float32, cfg.T * cfg.E, "logits")),
+                                 _P(_ptr(idx, torch.int32, A, "idx")), _P(_ptr(w, torch.float32, A, "w")),
+                                 _P(_ptr(dw, torch.float32, A, "dw")), _P(_ptr(counts, torch.int32, cfg.E, "counts")),
+                                 ctypes.c_float(daux), _P(_ptr(dlogits, torch.float32, cfg.T * cfg.E, "dlogits")),
+                                 _P(_stream(stream))))
+
+
+def gate_logits_bwd(cfg, x, Wg, dlogits, dWg, dbg, dx_r, stream=None):
+    ad = act_dtype(cfg)
+    _check(load().moe_gate_logits_bwd(ctypes.byref(cfg), _P(_ptr(x, ad, cfg.T * cfg.d, "x")),
+                                      _P(_ptr(Wg, torch.float32, cfg.E * cfg.d, "Wg")),
+                                      _P(_ptr(dlogits, torch.float32, cfg.T * cfg.E, "dlogits")),
+                                      _P(_ptr(dWg, torch.float32, cfg.E * cfg.d, "dWg")),
+                                      _P(_ptr(dbg, torch.float32, cfg.E, "dbg")),
+                                      _P(_ptr(dx_r, torch.float32, cfg.T * cfg.d, "dx_r")), _P(_stream(stream))))
+
+
+def _weights_struct(cfg, W: Dict[str, torch.Tensor]) -> Weights:
+    ad, d, E, F, Fs = act_dtype(cfg), cfg.d, cfg.E, cfg.F, cfg.Fs
+    return Weights(Wg=_ptr(W["Wg"], torch.float32, E * d, "Wg"), bg=_ptr(W.get("bg"), torch.float32, E, "bg"),
+                   expert_bias=_ptr(W.get("expert_bias"), torch.float32, E, "expert_bias"),
+                   W13=_ptr(W["W13"], ad, E * 2 * F * d, "W13"), W2=_ptr(W["W2"], ad, E * d * F, "W2"),
+                   W13s=_ptr(W.get("W13s"), ad, 2 * Fs * d, "W13s"), W2s=_ptr(W.get("W2s"), ad, d * Fs, "W2s"))
+
+
+def _saved_struct(cfg, S: Dict[str, torch.Tensor]) -> Saved:
+    ad, T, d, E, F, Fs, A = act_dtype(cfg), cfg.T, cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.T * cfg.k
+    spec = dict(logits=(torch.float32, T * E), idx=(torch.int32, A), w=(torch.float32, A), counts=(torch.int32, E),
+                offsets=(torch.int32, E + 1), row_of=(torch.int32, A), token_of=(torch.int32, A),
+                x_perm=(ad, A * d), H=(ad, A * 2 * F), Act=(ad, A * F), Y_perm=(ad, A * d),
+                H_s=(ad, T * 2 * Fs), Act_s=(ad, T * Fs), Y_s=(ad, T * d))
+    return Saved(**{n: _ptr(S.get(n), dt, ne, n) for n, (dt, ne) in spec.items()})
+
+
+def layer_fwd(cfg, W, x, S, y, stats, ws, stream=None):
+    wp, wn = _ws(ws)
+    ad = act_dtype(cfg)
+    ws_ = _weights_struct(cfg, W)
+    ss = _saved_struct(cfg, S)
+    _check(load().moe_layer_fwd(ctypes.byref(cfg), ctypes.byref(ws_), _P(_ptr(x, ad, cfg.T * cfg.d, "x")),
+                                ctypes.byref(ss), _P(_ptr(y, ad, cfg.T * cfg.d, "y")),
+                                _P(_ptr(stats, torch.float32, MOE_NSTATS, "stats")), _P(wp), ctypes.c_size_t(wn),
+                                _P(_stream(stream))))
+
+
+def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None):
+    wp, wn = _ws(ws)
+    ad, d, E, F, Fs = act_dtype(cfg), cfg.d, cfg.E, cfg.F, cfg.Fs
+    ws_ = _weights_struct(cfg, W)
+    ss = _saved_struct(cfg, S)
+    gs = Grads(dWg=_ptr(G["dWg"], torch.float32, E * d, "dWg"), dbg=_ptr(G.get("dbg"), torch.float32, E, "dbg"),
+               dW13=_ptr(G["dW13"], ad, E * 2 * F * d, "dW13"), dW2=_ptr(G["dW2"], ad, E * d * F, "dW2"),
+               dW13s=_ptr(G.get("dW13s"), ad, 2 * Fs * d, "dW13s"), dW2s=_ptr(G.get("dW2s"), ad, d * Fs, "dW2s"))
+    _check(load().moe_layer_bwd(ctypes.byref(cfg), ctypes.byref(ws_), ctypes.byref(ss),
+                                _P(_ptr(x, ad, cfg.T * d, "x")), _P(_ptr(dy, ad, cfg.T * d, "dy")),
+                                ctypes.c_float(daux), _P(_ptr(dx, ad, cfg.T * d, "dx")), ctypes.byref(gs), _P(wp),
+                                ctypes.c_size_t(wn), _P(_stream(stream))))
+
+
+# ----------------------------------------------------------------- buffer helpers
+
+def alloc_saved(cfg: Config, device="cuda") -> Dict[str, torch.Tensor]:
+    ad, T, d, E, F, Fs, A = act_dtype(cfg), cfg.T, cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.T * cfg.k
+    e = lambda *s, dt=ad: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
+    S = dict(logits=e(T, E, dt=torch.float32), idx=e(T, cfg.k, dt=torch.int32), w=e(T, cfg.k, dt=torch.float32),
+             counts=e(E, dt=torch.int32), offsets=e(E + 1, dt=torch.int32), row_of=e(T, cfg.k, dt=torch.int32),
+             token_of=e(A, dt=torch.int32), x_perm=e(A, d), H=e(A, 2 * F), Act=e(A, F), Y_perm=e(A, d))
+    if Fs:
+        S.update(H_s=e(T, 2 * Fs), Act_s=e(T, Fs), Y_s=e(T, d))
+    return S
+
+
+def alloc_grads(cfg: Config, device="cuda", with_dbg=False) -> Dict[str, torch.Tensor]:
+    ad, d, E, F, Fs = act_dtype(cfg), cfg.d, cfg.E, cfg.F, cfg.Fs
+    G = dict(dWg=torch.empty(E, d, dtype=torch.float32, device=device),
+             dW13=torch.empty(E, 2 * F, d, dtype=ad, device=device), dW2=torch.empty(E, d, F, dtype=ad, device=device))
+    if with_dbg:
+        G["dbg"] = torch.empty(E, dtype=torch.float32, device=device)
+    if Fs:
+        G.update(dW13s=torch.empty(2 * Fs, d, dtype=ad, device=device), dW2s=torch.empty(d, Fs, dtype=ad, device=device))
+    return G
+
+
+def alloc_workspace(cfg: Config, device="cuda") -> torch.Tensor:
+    f, b = workspace_size(cfg)
+    return torch.empty(max(f, b), dtype=torch.uint8, device=device)

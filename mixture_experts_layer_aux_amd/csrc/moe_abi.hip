@@ -1,0 +1,498 @@
+// The C ABI of libmoe: argument checks, workspace layout and the order of launches.
+// Every entry point validates all of its arguments on the host before it enqueues
+// anything, allocates nothing, and never synchronises the host.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+thread_local char g_err[512] = "";
+}
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+moe_status_t fail(moe_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status_t check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace carving, shared by moe_workspace_size and the calls.
+struct FwdWs {
+  int32_t* cnt_part;   // [nchunk, E] router chunk histograms == permute chunk histograms
+  float* prob_part;    // [nchunk, E]
+  int32_t* blk_base;   // [nchunk, E]
+  int32_t* counts;     // [E]
+  float* prob_sum;     // [E]
+  int32_t* sched;      // [E + 1]
+  size_t bytes;
+};
+
+FwdWs carve_fwd(const moe_config_t& c, void* base) {
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* q = p ? p + off : nullptr;
+    off += align_up(n);
+    return q;
+  };
+  const size_t nch = static_cast<size_t>(permute_num_chunks(c.T));
+  FwdWs w;
+  w.cnt_part = reinterpret_cast<int32_t*>(take(nch * c.E * 4));
+  w.prob_part = reinterpret_cast<float*>(take(nch * c.E * 4));
+  w.blk_base = reinterpret_cast<int32_t*>(take(nch * c.E * 4));
+  w.counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(c.E) * 4));
+  w.prob_sum = reinterpret_cast<float*>(take(static_cast<size_t>(c.E) * 4));
+  w.sched = reinterpret_cast<int32_t*>(take(mfma_schedule_bytes(c.E)));
+  w.bytes = off;
+  return w;
+}
+
+struct BwdWs {
+  void* dYX;       // [A, d] act: dY_perm, then dX_perm
+  void* dH;        // [A, 2F] act
+  float* dw;       // [T, k]
+  float* dlogits;  // [T, E]
+  float* dx_r;     // [T, d]
+  void* dH_s;      // [T, 2Fs] act
+  void* dx_s;      // [T, d] act
+  float* dact;     // fp32 path: [max(A, T), max(F, Fs)]
+  int32_t* sched;  // [E + 1]
+  size_t bytes;
+};
+
+BwdWs carve_bwd(const moe_config_t& c, void* base) {
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* q = p ? p + off : nullptr;
+    off += align_up(n);
+    return q;
+  };
+  const size_t A = static_cast<size_t>(c.T) * c.k, T = static_cast<size_t>(c.T), eb = act_bytes(c);
+  BwdWs w;
+  w.dYX = take(A * c.d * eb);
+  w.dH = take(A * 2 * c.F * eb);
+  w.dw = reinterpret_cast<float*>(take(A * 4));
+  w.dlogits = reinterpret_cast<float*>(take(T * c.E * 4));
+  w.dx_r = reinterpret_cast<float*>(take(T * c.d * 4));
+  w.dH_s = c.Fs ? take(T * 2 * c.Fs * eb) : nullptr;
+  w.dx_s = c.Fs ? take(T * c.d * eb) : nullptr;
+  w.dact = c.act_dtype == MOE_F32 ? reinterpret_cast<float*>(take(std::max(A, T) * std::max(c.F, c.Fs) * 4)) : nullptr;
+  w.sched = reinterpret_cast<int32_t*>(take(mfma_schedule_bytes(c.E)));
+  w.bytes = off;
+  return w;
+}
+
+moe_status_t validate(const moe_config_t* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
+  if (c->T < 1 || c->d < 1 || c->E < 1 || c->k < 1 || c->F < 1 || c->Fs < 0)
+    return fail(MOE_ERR_INVALID_ARG, "sizes must be positive (T=%d d=%d E=%d k=%d F=%d Fs=%d)", c->T, c->d, c->E,
+                c->k, c->F, c->Fs);
+  if (c->k > c->E) return fail(MOE_ERR_INVALID_ARG, "k=%d exceeds E=%d", c->k, c->E);
+  if (c->k > 32) return fail(MOE_ERR_UNSUPPORTED, "k=%d exceeds 32", c->k);
+  if (c->E > 2048) return fail(MOE_ERR_UNSUPPORTED, "E=%d exceeds 2048", c->E);
+  if (static_cast<int64_t>(c->T) * c->k >= (int64_t{1} << 31)) return fail(MOE_ERR_INVALID_ARG, "T*k >= 2^31");
+  if (c->score != MOE_SOFTMAX && c->score != MOE_SIGMOID) return fail(MOE_ERR_INVALID_ARG, "unknown score function");
+  if (c->pre_softmax != 0) return fail(MOE_ERR_UNSUPPORTED, "pre-softmax top-k is not provided");
+  if (c->score == MOE_SOFTMAX && c->k == 1)
+    return fail(MOE_ERR_UNSUPPORTED, "softmax over one selected logit has no gradient; top-1 needs pre-softmax");
+  if (c->aux_coeff != 0.0f && c->score != MOE_SOFTMAX)
+    return fail(MOE_ERR_UNSUPPORTED, "the aux loss is provided for softmax scores only");
+  if (!(c->routed_scaling > 0.0f)) return fail(MOE_ERR_INVALID_ARG, "routed_scaling must be > 0");
+  if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown act dtype");
+  if (c->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "reserved field must be 0");
+  if (c->d % 64 || c->F % 64 || c->Fs % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "d, F and Fs must be multiples of 64 (d=%d F=%d Fs=%d)", c->d, c->F, c->Fs);
+  if (c->act_dtype == MOE_BF16 && (c->F % 128 || c->Fs % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "bf16 path needs F and Fs multiples of 128");
+  return MOE_OK;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define MOE_TRY(x)                  \
+  do {                              \
+    const moe_status_t _s = (x);    \
+    if (_s != MOE_OK) return _s;    \
+  } while (0)
+#define MOE_NEED(p)                                                               \
+  do {                                                                            \
+    if (!(p)) return fail(MOE_ERR_INVALID_ARG, "%s: %s is NULL", __func__, #p);   \
+  } while (0)
+#define MOE_NEED16(p)                                                                          \
+  do {                                                                                         \
+    if (!(p)) return fail(MOE_ERR_INVALID_ARG, "%s: %s is NULL", __func__, #p);                \
+    if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", __func__, #p); \
+  } while (0)
+
+moe_status_t need_ws(size_t have, size_t need, const char* fn) {
+  if (have < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, have, need);
+  return MOE_OK;
+}
+
+hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
+
+// ----------------------------------------------------------------- launch sequences
+moe_status_t run_gate(const moe_config_t& c, const void* x, const float* Wg, const float* bg, float* logits,
+                      hipStream_t s) {
+  GemmDesc g{};
+  g.a_major = K_MAJOR; g.b_major = K_MAJOR; g.ragged = RAGGED_M; g.epi = bg ? EPI_STORE_BIAS : EPI_STORE;
+  g.a_type = c.act_dtype; g.b_type = MOE_F32; g.c_type = MOE_F32;
+  g.N = c.E; g.K = c.d;
+  g.A = x; g.lda = c.d; g.B = Wg; g.ldb = c.d; g.C = logits; g.ldc = c.E; g.bias = bg;
+  g.range_end = c.T;
+  return launch_gemm_fma(g, s);
+}
+
+moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const int32_t* offsets, const void* W13,
+                             const void* W2, const void* x, const void* W13s, const void* W2s, void* H, void* Act,
+                             void* Y_perm, void* H_s, void* Act_s, void* Y_s, int32_t* sched, hipStream_t s) {
+  const int64_t A = static_cast<int64_t>(c.T) * c.k;
+  for (int shared = 0; shared < (c.Fs ? 2 : 1); ++shared) {
+    const int F = shared ? c.Fs : c.F;
+    const void* X = shared ? x : x_perm;
+    void* h = shared ? H_s : H;
+    void* act = shared ? Act_s : Act;
+    GemmDesc g1{};
+    g1.a_major = K_MAJOR; g1.b_major = K_MAJOR; g1.ragged = RAGGED_M;
+    g1.a_type = g1.b_type = g1.c_type = c.act_dtype;
+    g1.N = 2 * F; g1.K = c.d; g1.F = F;
+    g1.A = X; g1.lda = c.d;
+    g1.B = shared ? W13s : W13; g1.ldb = c.d; g1.b_gstride = shared ? 0 : int64_t{2} * F * c.d;
+    g1.C = h; g1.ldc = 2 * F; g1.C2 = act; g1.ldc2 = F;
+    g1.offsets = shared ? nullptr : offsets; g1.G = shared ? 1 : c.E; g1.range_end = c.T; g1.rows_upper = A;
+    GemmDesc g2 = g1;
+    g2.N = c.d; g2.K = F; g2.A = act; g2.lda = F;
+    g2.B = shared ? W2s : W2; g2.ldb = F; g2.b_gstride = shared ? 0 : int64_t{1} * c.d * F;
+    g2.C = shared ? Y_s : Y_perm; g2.ldc = c.d; g2.C2 = nullptr; g2.epi = EPI_STORE;
+    if (c.act_dtype == MOE_BF16) {
+      g1.epi = EPI_SWIGLU_FWD;
+      MOE_TRY(launch_gemm_mfma(g1, sched, s));
+      MOE_TRY(launch_gemm_mfma(g2, sched, s));
+    } else {
+      g1.epi = EPI_STORE;
+      MOE_TRY(launch_gemm_fma(g1, s));
+      MOE_TRY(launch_swiglu_fwd_elementwise(static_cast<const float*>(h), static_cast<float*>(act), shared ? c.T : A,
+                                            F, s));
+      MOE_TRY(launch_gemm_fma(g2, s));
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const int32_t* offsets, const void* W13,
+                             const void* W2, const void* H, const void* Act, const void* dY_perm, void* dH,
+                             void* dX_perm, void* dW13, void* dW2, const void* x, const void* W13s, const void* W2s,
+                             const void* H_s, const void* Act_s, const void* dy, void* dH_s, void* dx_s,
+                             void* dW13s, void* dW2s, int32_t* sched, float* dact, hipStream_t s) {
+  const int64_t A = static_cast<int64_t>(c.T) * c.k;
+  for (int shared = 0; shared < (c.Fs ? 2 : 1); ++shared) {
+    const int F = shared ? c.Fs : c.F;
+    const int32_t* off = shared ? nullptr : offsets;
+    const int G = shared ? 1 : c.E;
+    const int64_t rows = shared ? c.T : A;
+    const void* X = shared ? x : x_perm;
+    const void* h = shared ? H_s : H;
+    const void* act = shared ? Act_s : Act;
+    const void* dY = shared ? dy : dY_perm;
+    void* dh = shared ? dH_s : dH;
+    void* dX = shared ? dx_s : dX_perm;
+    const void* w13 = shared ? W13s : W13;
+    const void* w2 = shared ? W2s : W2;
+    void* dw13 = shared ? dW13s : dW13;
+    void* dw2 = shared ? dW2s : dW2;
+    const int et = c.act_dtype;
+    // (1) fc2 data gradient: dAct = dY W2 (+ SwiGLU backward -> dH)
+    GemmDesc d2{};
+    d2.a_major = K_MAJOR; d2.b_major = MN_MAJOR; d2.ragged = RAGGED_M;
+    d2.a_type = d2.b_type = d2.c_type = et;
+    d2.N = F; d2.K = c.d; d2.F = F;
+    d2.A = dY; d2.lda = c.d;
+    d2.B = w2; d2.ldb = F; d2.b_gstride = shared ? 0 : int64_t{1} * c.d * F;
+    d2.Hin = h; d2.ldh = 2 * F;
+    d2.offsets = off; d2.G = G; d2.range_end = c.T; d2.rows_upper = A;
+    // (2) fc2 weight gradient: dW2 = dY^T Act (reduction over the expert's rows)
+    GemmDesc w2g{};
+    w2g.a_major = MN_MAJOR; w2g.b_major = MN_MAJOR; w2g.ragged = RAGGED_K; w2g.epi = EPI_STORE;
+    w2g.a_type = w2g.b_type = w2g.c_type = et;
+    w2g.M = c.d; w2g.N = F;
+    w2g.A = dY; w2g.lda = c.d; w2g.B = act; w2g.ldb = F;
+    w2g.C = dw2; w2g.ldc = F; w2g.c_gstride = int64_t{1} * c.d * F;
+    w2g.offsets = off; w2g.G = G; w2g.range_end = c.T;
+    // (3) fc1 data gradient: dX = dH W13
+    GemmDesc d1{};
+    d1.a_major = K_MAJOR; d1.b_major = MN_MAJOR; d1.ragged = RAGGED_M; d1.epi = EPI_STORE;
+    d1.a_type = d1.b_type = d1.c_type = et;
+    d1.N = c.d; d1.K = 2 * F;
+    d1.A = dh; d1.lda = 2 * F;
+    d1.B = w13; d1.ldb = c.d; d1.b_gstride = shared ? 0 : int64_t{2} * F * c.d;
+    d1.C = dX; d1.ldc = c.d;
+    d1.offsets = off; d1.G = G; d1.range_end = c.T; d1.rows_upper = A;
+    // (4) fc1 weight gradient: dW13 = dH^T X
+    GemmDesc w1g{};
+    w1g.a_major = MN_MAJOR; w1g.b_major = MN_MAJOR; w1g.ragged = RAGGED_K; w1g.epi = EPI_STORE;
+    w1g.a_type = w1g.b_type = w1g.c_type = et;
+    w1g.M = 2 * F; w1g.N = c.d;
+    w1g.A = dh; w1g.lda = 2 * F; w1g.B = X; w1g.ldb = c.d;
+    w1g.C = dw13; w1g.ldc = c.d; w1g.c_gstride = int64_t{2} * F * c.d;
+    w1g.offsets = off; w1g.G = G; w1g.range_end = c.T;
+    if (et == MOE_BF16) {
+      d2.epi = EPI_SWIGLU_BWD;
+      d2.C = dh; d2.ldc = 2 * F;
+      MOE_TRY(launch_gemm_mfma(d2, sched, s));
+      MOE_TRY(launch_gemm_mfma(w2g, sched, s));
+      MOE_TRY(launch_gemm_mfma(d1, sched, s));
+      MOE_TRY(launch_gemm_mfma(w1g, sched, s));
+    } else {
+      d2.epi = EPI_STORE;
+      d2.C = dact; d2.ldc = F;
+      MOE_TRY(launch_gemm_fma(d2, s));
+      MOE_TRY(launch_swiglu_bwd_elementwise(static_cast<const float*>(h), dact, static_cast<float*>(dh), rows, F, s));
+      MOE_TRY(launch_gemm_fma(w2g, s));
+      MOE_TRY(launch_gemm_fma(d1, s));
+      MOE_TRY(launch_gemm_fma(w1g, s));
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status_t run_gate_bwd(const moe_config_t& c, const void* x, const float* Wg, const float* dlogits, float* dWg,
+                          float* dbg, float* dx_r, hipStream_t s) {
+  GemmDesc gw{};
+  gw.a_major = MN_MAJOR; gw.b_major = MN_MAJOR; gw.ragged = RAGGED_K; gw.epi = EPI_STORE;
+  gw.a_type = MOE_F32; gw.b_type = c.act_dtype; gw.c_type = MOE_F32;
+  gw.M = c.E; gw.N = c.d;
+  gw.A = dlogits; gw.lda = c.E; gw.B = x; gw.ldb = c.d; gw.C = dWg; gw.ldc = c.d;
+  gw.range_end = c.T;
+  MOE_TRY(launch_gemm_fma(gw, s));
+  if (dbg) MOE_TRY(launch_colsum(dlogits, c.T, c.E, dbg, s));
+  if (dx_r) {
+    GemmDesc gx{};
+    gx.a_major = K_MAJOR; gx.b_major = MN_MAJOR; gx.ragged = RAGGED_M; gx.epi = EPI_STORE;
+    gx.a_type = MOE_F32; gx.b_type = MOE_F32; gx.c_type = MOE_F32;
+    gx.N = c.d; gx.K = c.E;
+    gx.A = dlogits; gx.lda = c.E; gx.B = Wg; gx.ldb = c.d; gx.C = dx_r; gx.ldc = c.d;
+    gx.range_end = c.T;
+    MOE_TRY(launch_gemm_fma(gx, s));
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+moe_status_t moe_validate(const moe_config_t* cfg) {
+  const moe_status_t st = validate(cfg);
+  if (st == MOE_OK) g_err[0] = '\0';
+  return st;
+}
+
+moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* fwd_bytes, size_t* bwd_bytes) {
+  MOE_TRY(validate(cfg));
+  if (fwd_bytes) *fwd_bytes = carve_fwd(*cfg, nullptr).bytes;
+  if (bwd_bytes) *bwd_bytes = carve_bwd(*cfg, nullptr).bytes;
+  return MOE_OK;
+}
+
+moe_status_t moe_gate_logits(const moe_config_t* cfg, const void* x, const float* Wg, const float* bg,
+                             float* logits, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED(x); MOE_NEED(Wg); MOE_NEED(logits);
+  return run_gate(*cfg, x, Wg, bg, logits, S(stream));
+}
+
+moe_status_t moe_router_topk(const moe_config_t* cfg, const float* logits, const float* expert_bias, int32_t* idx,
+                             float* w, int32_t* counts, float* prob_sum, float* stats, void* ws, size_t ws_bytes,
+                             void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED(logits); MOE_NEED(idx); MOE_NEED(w); MOE_NEED(counts); MOE_NEED(ws);
+  if (expert_bias && cfg->score != MOE_SIGMOID)
+    return fail(MOE_ERR_UNSUPPORTED, "the expert bias is provided for sigmoid scores only");
+  const FwdWs fw = carve_fwd(*cfg, ws);
+  MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
+  float* ps = prob_sum ? prob_sum : fw.prob_sum;
+  return launch_router_topk(*cfg, logits, expert_bias, idx, w, counts, ps, stats, fw.cnt_part, fw.prob_part,
+                            S(stream));
+}
+
+moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* idx, int32_t* offsets,
+                         int32_t* row_of, int32_t* token_of, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED16(x); MOE_NEED(idx); MOE_NEED(offsets); MOE_NEED(row_of); MOE_NEED(token_of); MOE_NEED16(x_perm);
+  MOE_NEED(ws);
+  const FwdWs fw = carve_fwd(*cfg, ws);
+  MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
+  return launch_permute(*cfg, x, idx, offsets, row_of, token_of, x_perm, fw.cnt_part, fw.blk_base, fw.counts,
+                        false, S(stream));
+}
+
+moe_status_t moe_grouped_gemm_swiglu(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
+                                     const void* W13, const void* W2, const void* x, const void* W13s,
+                                     const void* W2s, void* H, void* Act, void* Y_perm, void* H_s, void* Act_s,
+                                     void* Y_s, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED16(x_perm); MOE_NEED(offsets); MOE_NEED16(W13); MOE_NEED16(W2); MOE_NEED16(H); MOE_NEED16(Act);
+  MOE_NEED16(Y_perm); MOE_NEED(ws);
+  if (cfg->Fs) {
+    MOE_NEED16(x); MOE_NEED16(W13s); MOE_NEED16(W2s); MOE_NEED16(H_s); MOE_NEED16(Act_s); MOE_NEED16(Y_s);
+  }
+  const FwdWs fw = carve_fwd(*cfg, ws);
+  MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
+  return run_experts_fwd(*cfg, x_perm, offsets, W13, W2, x, W13s, W2s, H, Act, Y_perm, H_s, Act_s, Y_s, fw.sched,
+                         S(stream));
+}
+
+moe_status_t moe_unpermute_combine(const moe_config_t* cfg, const void* Y_perm, const int32_t* row_of,
+                                   const float* w, const void* Y_s, void* y, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED16(Y_perm); MOE_NEED(row_of); MOE_NEED(w); MOE_NEED16(y);
+  if (Y_s && !aligned16(Y_s)) return fail(MOE_ERR_INVALID_ARG, "Y_s is not 16-byte aligned");
+  return launch_gather_sum(*cfg, Y_perm, row_of, w, Y_s, nullptr, y, S(stream));
+}
+
+moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, const void* x, const moe_saved_t* sv,
+                           void* y, float* stats, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED(W); MOE_NEED(sv); MOE_NEED16(x); MOE_NEED16(y); MOE_NEED(ws);
+  MOE_NEED(W->Wg); MOE_NEED16(W->W13); MOE_NEED16(W->W2);
+  MOE_NEED(sv->logits); MOE_NEED(sv->idx); MOE_NEED(sv->w); MOE_NEED(sv->counts); MOE_NEED(sv->offsets);
+  MOE_NEED(sv->row_of); MOE_NEED(sv->token_of); MOE_NEED16(sv->x_perm); MOE_NEED16(sv->H); MOE_NEED16(sv->Act);
+  MOE_NEED16(sv->Y_perm);
+  if (cfg->Fs) {
+    MOE_NEED16(W->W13s); MOE_NEED16(W->W2s); MOE_NEED16(sv->H_s); MOE_NEED16(sv->Act_s); MOE_NEED16(sv->Y_s);
+  }
+  if (W->expert_bias && cfg->score != MOE_SIGMOID)
+    return fail(MOE_ERR_UNSUPPORTED, "the expert bias is provided for sigmoid scores only");
+  const FwdWs fw = carve_fwd(*cfg, ws);
+  MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
+  const moe_config_t& c = *cfg;
+  hipStream_t s = S(stream);
+  MOE_TRY(run_gate(c, x, W->Wg, W->bg, sv->logits, s));
+  MOE_TRY(launch_router_topk(c, sv->logits, W->expert_bias, sv->idx, sv->w, sv->counts, fw.prob_sum, stats,
+                             fw.cnt_part, fw.prob_part, s));
+  MOE_TRY(launch_permute(c, x, sv->idx, sv->offsets, sv->row_of, sv->token_of, sv->x_perm, fw.cnt_part, fw.blk_base,
+                         fw.counts, true, s));
+  MOE_TRY(run_experts_fwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, x, W->W13s, W->W2s, sv->H, sv->Act,
+                          sv->Y_perm, sv->H_s, sv->Act_s, sv->Y_s, fw.sched, s));
+  return launch_gather_sum(c, sv->Y_perm, sv->row_of, sv->w, c.Fs ? sv->Y_s : nullptr, nullptr, y, s);
+}
+
+moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const void* dy, const void* Y_perm,
+                                       const int32_t* row_of, const float* w, void* dY_perm, float* dw,
+                                       void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED16(dy); MOE_NEED16(Y_perm); MOE_NEED(row_of); MOE_NEED(w); MOE_NEED16(dY_perm); MOE_NEED(dw);
+  return launch_combine_bwd(*cfg, dy, Y_perm, row_of, w, dY_perm, dw, S(stream));
+}
+
+moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
+                                         const void* W13, const void* W2, const void* H, const void* Act,
+                                         const void* dY_perm, void* dH, void* dX_perm, void* dW13, void* dW2,
+                                         const void* x, const void* W13s, const void* W2s, const void* H_s,
+                                         const void* Act_s, const void* dy, void* dH_s, void* dx_s, void* dW13s,
+                                         void* dW2s, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED16(x_perm); MOE_NEED(offsets); MOE_NEED16(W13); MOE_NEED16(W2); MOE_NEED16(H); MOE_NEED16(Act);
+  MOE_NEED16(dY_perm); MOE_NEED16(dH); MOE_NEED16(dX_perm); MOE_NEED16(dW13); MOE_NEED16(dW2); MOE_NEED(ws);
+  if (cfg->Fs) {
+    MOE_NEED16(x); MOE_NEED16(W13s); MOE_NEED16(W2s); MOE_NEED16(H_s); MOE_NEED16(Act_s); MOE_NEED16(dy);
+    MOE_NEED16(dH_s); MOE_NEED16(dx_s); MOE_NEED16(dW13s); MOE_NEED16(dW2s);
+  }
+  const BwdWs bw = carve_bwd(*cfg, ws);
+  MOE_TRY(need_ws(ws_bytes, bw.bytes, __func__));
+  return run_experts_bwd(*cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, dX_perm, dW13, dW2, x, W13s, W2s, H_s,
+                         Act_s, dy, dH_s, dx_s, dW13s, dW2s, bw.sched, bw.dact, S(stream));
+}
+
+moe_status_t moe_permute_bwd(const moe_config_t* cfg, const void* dX_perm, const int32_t* row_of, const void* dx_s,
+                             const float* dx_r, void* dx, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED16(dX_perm); MOE_NEED(row_of); MOE_NEED16(dx);
+  if (dx_s && !aligned16(dx_s)) return fail(MOE_ERR_INVALID_ARG, "dx_s is not 16-byte aligned");
+  if (dx_r && !aligned16(dx_r)) return fail(MOE_ERR_INVALID_ARG, "dx_r is not 16-byte aligned");
+  return launch_gather_sum(*cfg, dX_perm, row_of, nullptr, dx_s, dx_r, dx, S(stream));
+}
+
+moe_status_t moe_router_bwd(const moe_config_t* cfg, const float* logits, const int32_t* idx, const float* w,
+                            const float* dw, const int32_t* counts, float daux, float* dlogits, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED(logits); MOE_NEED(idx); MOE_NEED(w); MOE_NEED(dw); MOE_NEED(dlogits);
+  if (cfg->aux_coeff != 0.0f && daux != 0.0f) MOE_NEED(counts);
+  return launch_router_bwd(*cfg, logits, idx, w, dw, counts, daux, dlogits, S(stream));
+}
+
+moe_status_t moe_gate_logits_bwd(const moe_config_t* cfg, const void* x, const float* Wg, const float* dlogits,
+                                 float* dWg, float* dbg, float* dx_r, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED(x); MOE_NEED(Wg); MOE_NEED(dlogits); MOE_NEED(dWg);
+  return run_gate_bwd(*cfg, x, Wg, dlogits, dWg, dbg, dx_r, S(stream));
+}
+
+moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, const moe_saved_t* sv, const void* x,
+                           const void* dy, float daux, void* dx, const moe_grads_t* gr, void* ws, size_t ws_bytes,
+                           void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED(W); MOE_NEED(sv); MOE_NEED(gr); MOE_NEED16(x); MOE_NEED16(dy); MOE_NEED16(dx); MOE_NEED(ws);
+  MOE_NEED(W->Wg); MOE_NEED16(W->W13); MOE_NEED16(W->W2);
+  MOE_NEED(sv->logits); MOE_NEED(sv->idx); MOE_NEED(sv->w); MOE_NEED(sv->counts); MOE_NEED(sv->offsets);
+  MOE_NEED(sv->row_of); MOE_NEED16(sv->x_perm); MOE_NEED16(sv->H); MOE_NEED16(sv->Act); MOE_NEED16(sv->Y_perm);
+  MOE_NEED(gr->dWg); MOE_NEED16(gr->dW13); MOE_NEED16(gr->dW2);
+  if (cfg->Fs) {
+    MOE_NEED16(W->W13s); MOE_NEED16(W->W2s); MOE_NEED16(sv->H_s); MOE_NEED16(sv->Act_s);
+    MOE_NEED16(gr->dW13s); MOE_NEED16(gr->dW2s);
+  }
+  const BwdWs bw = carve_bwd(*cfg, ws);
+  MOE_TRY(need_ws(ws_bytes, bw.bytes, __func__));
+  const moe_config_t& c = *cfg;
+  hipStream_t s = S(stream);
+  MOE_TRY(launch_combine_bwd(c, dy, sv->Y_perm, sv->row_of, sv->w, bw.dYX, bw.dw, s));
+  MOE_TRY(run_experts_bwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, sv->H, sv->Act, bw.dYX, bw.dH, bw.dYX,
+                          gr->dW13, gr->dW2, x, W->W13s, W->W2s, sv->H_s, sv->Act_s, dy, bw.dH_s, bw.dx_s, gr->dW13s,
+                          gr->dW2s, bw.sched, bw.dact, s));
+  MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, daux, bw.dlogits, s));
+  MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, s));
+  return launch_gather_sum(c, bw.dYX, sv->row_of, nullptr, c.Fs ? bw.dx_s : nullptr, bw.dx_r, dx, s);
+}
+
+}  // extern "C"

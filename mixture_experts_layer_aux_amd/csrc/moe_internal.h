@@ -1,0 +1,72 @@
+// Internal launcher interface between the C-ABI layer and the kernel translation units.
+#pragma once
+
+#include "moe_common.h"
+
+namespace moe {
+
+inline int act_bytes(const moe_config_t& c) { return c.act_dtype == MOE_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- router
+int router_epl(int E);
+int64_t router_num_blocks(int T);  // == permute_num_chunks(T): both use 64-token chunks
+moe_status_t launch_router_topk(const moe_config_t& c, const float* logits, const float* expert_bias,
+                                int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* stats,
+                                int32_t* cnt_part, float* prob_part, hipStream_t s);
+moe_status_t launch_router_bwd(const moe_config_t& c, const float* logits, const int32_t* idx, const float* w,
+                               const float* dw, const int32_t* counts, float daux, float* dlogits, hipStream_t s);
+moe_status_t launch_colsum(const float* X, int rows, int cols, float* out, hipStream_t s);
+
+// ---------------------------------------------------------------- permute / combine
+int64_t permute_num_chunks(int T);
+moe_status_t launch_permute(const moe_config_t& c, const void* x, const int32_t* idx, int32_t* offsets,
+                            int32_t* row_of, int32_t* token_of, void* x_perm, int32_t* blk_hist,
+                            int32_t* blk_base, int32_t* counts_ws, bool hist_ready, hipStream_t s);
+moe_status_t launch_gather_sum(const moe_config_t& c, const void* Y, const int32_t* row_of, const float* w,
+                               const void* add_act, const float* add_f32, void* out, hipStream_t s);
+moe_status_t launch_combine_bwd(const moe_config_t& c, const void* dy, const void* Y, const int32_t* row_of,
+                                const float* w, void* dY, float* dw, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMMs
+// Storage of an operand: K_MAJOR = [rows][K] (K contiguous), MN_MAJOR = [K][rows].
+enum Major { K_MAJOR = 0, MN_MAJOR = 1 };
+// Grouping: RAGGED_M = group g owns rows [off[g], off[g+1]) of A and C, and B + g*b_gstride;
+//           RAGGED_K = group g owns K rows [off[g], off[g+1]) of A and B, and C + g*c_gstride.
+// offsets == nullptr means one group spanning [0, range_end).
+enum Ragged { RAGGED_M = 0, RAGGED_K = 1 };
+enum Epi { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2, EPI_STORE_BIAS = 3 };
+
+struct GemmDesc {
+  int a_major, b_major, ragged, epi;
+  int a_type, b_type, c_type;  // moe_dtype_t
+  int M, N, K;                  // the non-ragged extents (M or K per group when ragged)
+  const void* A;
+  int64_t lda, a_gstride;
+  const void* B;
+  int64_t ldb, b_gstride;
+  void* C;
+  int64_t ldc, c_gstride;
+  void* C2;                     // EPI_SWIGLU_FWD: Act out [rows][F]
+  int64_t ldc2;
+  const void* Hin;              // EPI_SWIGLU_BWD: saved H [rows][2F]
+  int64_t ldh;
+  const float* bias;            // EPI_STORE_BIAS: [N]
+  int F;                        // SwiGLU: offset of the up half (columns of H / rows of W13)
+  const int32_t* offsets;
+  int G;
+  int range_end;
+  int64_t rows_upper;           // ragged M: upper bound of sum of rows (for grid sizing)
+};
+
+// fp32-accumulating FMA GEMM for fp32 (and mixed fp32/bf16) operands; SwiGLU epilogues are
+// separate elementwise kernels on this path.
+moe_status_t launch_gemm_fma(const GemmDesc& g, hipStream_t s);
+moe_status_t launch_swiglu_fwd_elementwise(const float* H, float* Act, int64_t rows, int F, hipStream_t s);
+moe_status_t launch_swiglu_bwd_elementwise(const float* H, const float* dAct, float* dH, int64_t rows, int F,
+                                           hipStream_t s);
+
+// bf16 MFMA grouped GEMM (gfx950 v_mfma_f32_32x32x16_bf16), fused epilogues.
+size_t mfma_schedule_bytes(int G);
+moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched_ws, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,85 @@
+"""Shared helpers of the GPU parity tests: moving generator bytes to the device and
+measuring errors.  The oracle is called directly by the tests; nothing here computes
+any part of the layer."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from mixture_experts_layer_aux_amd import workloads as W  # noqa: E402
+from oracle import moe_oracle as O  # noqa: E402
+
+# Spec tolerances: max |got - ref| / rms(ref) per tensor.
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+MARGIN = 1e-3
+
+
+def tol(shape) -> float:
+    return TOL_F32 if shape.act == "f32" else TOL_BF16
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def dev():
+    torch = torch_mod()
+    assert torch.cuda.is_available(), "GPU test without a GPU"
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dtype=None):
+    """numpy storage array -> device tensor (uint16 arrays become bfloat16 with the same bits)."""
+    torch = torch_mod()
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev()).view(torch.bfloat16)
+    t = torch.from_numpy(a).to(dev())
+    return t if dtype is None else t.to(dtype)
+
+
+def to_np(t) -> np.ndarray:
+    """device tensor -> float64 numpy (exact for bf16 and fp32)."""
+    torch = torch_mod()
+    if t.dtype in (torch.int32, torch.int64):
+        return t.cpu().numpy()
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def f64(a, act):
+    return None if a is None else W.to_f32(a, act).astype(np.float64)
+
+
+def rel_err(got, ref, mask=None) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if mask is not None:
+        got, ref = got[mask], ref[mask]
+    if ref.size == 0:
+        return 0.0
+    rms = np.sqrt(np.mean(ref ** 2))
+    return float(np.max(np.abs(got - ref)) / rms) if rms > 0 else float(np.max(np.abs(got - ref)))
+
+
+def spec_of(shape) -> "O.LayerSpec":
+    return O.LayerSpec(E=shape.E, k=shape.k, score=shape.score, scaling=shape.scaling, aux_coeff=shape.aux_coeff)
+
+
+def oracle_inputs(inp, shape):
+    """fp64 copies of every input of one layer."""
+    a = shape.act
+    return dict(x=f64(inp["x"], a), Wg=inp["Wg"].astype(np.float64),
+                bg=None if inp["bg"] is None else inp["bg"].astype(np.float64),
+                expert_bias=None if inp["expert_bias"] is None else inp["expert_bias"].astype(np.float64),
+                W13=f64(inp["W13"], a), W2=f64(inp["W2"], a), W13s=f64(inp.get("W13s"), a),
+                W2s=f64(inp.get("W2s"), a), dy=f64(inp.get("dy"), a))

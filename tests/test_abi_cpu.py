@@ -1,0 +1,126 @@
+"""Host-side checks of libmoe that need no GPU: the library loads, exports every entry
+point include/moe.h declares, and every argument check fails before anything is launched
+(the calls below never reach a kernel launch)."""
+import ctypes
+import os
+import re
+from dataclasses import replace
+
+import pytest
+
+from mixture_experts_layer_aux_amd import _lib as L
+from mixture_experts_layer_aux_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|moe_status_t)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = L.load()
+    names = header_functions()
+    assert len(names) == 16
+    assert sorted(L.EXPORTED) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _status(cfg):
+    return L.load().moe_validate(ctypes.byref(cfg))
+
+
+def test_valid_configs():
+    for c in W.CONFIGS.values():
+        assert _status(L.config_from_shape(c)) == L.MOE_OK
+    for c in W.SMALL.values():
+        assert _status(L.config_from_shape(c)) == L.MOE_OK
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(k=9, E=8), L.MOE_ERR_INVALID_ARG),
+    (dict(k=33, E=64), L.MOE_ERR_UNSUPPORTED),
+    (dict(E=4096), L.MOE_ERR_UNSUPPORTED),
+    (dict(k=1), L.MOE_ERR_UNSUPPORTED),               # softmax top-1 needs pre-softmax
+    (dict(pre_softmax=1), L.MOE_ERR_UNSUPPORTED),
+    (dict(score=L.MOE_SIGMOID, aux_coeff=1e-3), L.MOE_ERR_UNSUPPORTED),
+    (dict(d=100), L.MOE_ERR_UNSUPPORTED),
+    (dict(F=192), L.MOE_ERR_UNSUPPORTED),             # bf16 needs F % 128 == 0
+    (dict(T=0), L.MOE_ERR_INVALID_ARG),
+    (dict(T=2 ** 28, k=8), L.MOE_ERR_INVALID_ARG),    # T * k >= 2^31
+    (dict(routed_scaling=0.0), L.MOE_ERR_INVALID_ARG),
+    (dict(act_dtype=7), L.MOE_ERR_INVALID_ARG),
+    (dict(reserved=1), L.MOE_ERR_INVALID_ARG),
+])
+def test_config_rules(change, status):
+    cfg = L.config_from_shape(W.CONFIGS[2])
+    for k, v in change.items():
+        setattr(cfg, k, v)
+    assert _status(cfg) == status
+    assert L.load().moe_last_error()
+
+
+def test_sigmoid_top1_is_allowed_and_fp32_f192_is_allowed():
+    cfg = L.config_from_shape(replace(W.CONFIGS[3], k=1))
+    assert _status(cfg) == L.MOE_OK
+    cfg = L.config_from_shape(replace(W.CONFIGS[1], F=192))
+    assert _status(cfg) == L.MOE_OK
+
+
+def test_workspace_sizes_cover_the_backward_buffers():
+    for c in W.CONFIGS.values():
+        f, b = L.workspace_size(L.config_from_shape(c))
+        eb = 2 if c.act == "bf16" else 4
+        A = c.T * c.k
+        assert f > 0
+        # dY_perm/dX_perm, dH, dlogits, dx_r at least
+        assert b >= A * c.d * eb + A * 2 * c.F * eb + c.T * c.E * 4 + c.T * c.d * 4
+
+
+P = ctypes.c_void_p
+
+
+def test_entry_points_reject_bad_arguments_before_launching():
+    lib = L.load()
+    cfg = L.config_from_shape(W.CONFIGS[2])
+    fake = P(1 << 20)           # never dereferenced: every call below fails its checks first
+    odd = P((1 << 20) + 2)
+    nul = P(None)
+    s = P(None)
+    # NULL config
+    assert lib.moe_gate_logits(None, fake, fake, nul, fake, s) == L.MOE_ERR_INVALID_ARG
+    # NULL required pointer
+    assert lib.moe_gate_logits(ctypes.byref(cfg), nul, fake, nul, fake, s) == L.MOE_ERR_INVALID_ARG
+    assert b"x is NULL" in lib.moe_last_error()
+    # workspace too small
+    st = lib.moe_router_topk(ctypes.byref(cfg), fake, nul, fake, fake, fake, nul, nul, fake, ctypes.c_size_t(8), s)
+    assert st == L.MOE_ERR_WORKSPACE
+    # expert bias with softmax scores
+    st = lib.moe_router_topk(ctypes.byref(cfg), fake, fake, fake, fake, fake, nul, nul, fake, ctypes.c_size_t(1 << 40), s)
+    assert st == L.MOE_ERR_UNSUPPORTED
+    # misaligned activation pointer
+    st = lib.moe_permute(ctypes.byref(cfg), odd, fake, fake, fake, fake, fake, fake, ctypes.c_size_t(1 << 40), s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"aligned" in lib.moe_last_error()
+    # invalid configuration reaches no launch either
+    bad = L.config_from_shape(replace(W.CONFIGS[2], k=1))
+    st = lib.moe_unpermute_combine(ctypes.byref(bad), fake, fake, fake, nul, fake, s)
+    assert st == L.MOE_ERR_UNSUPPORTED
+    # the layer calls check their structs
+    st = lib.moe_layer_fwd(ctypes.byref(cfg), None, fake, None, fake, nul, fake, ctypes.c_size_t(1 << 40), s)
+    assert st == L.MOE_ERR_INVALID_ARG
+    w = L.Weights()
+    sv = L.Saved()
+    st = lib.moe_layer_fwd(ctypes.byref(cfg), ctypes.byref(w), fake, ctypes.byref(sv), fake, nul, fake,
+                           ctypes.c_size_t(1 << 40), s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"Wg" in lib.moe_last_error()
+    st = lib.moe_router_bwd(ctypes.byref(cfg), fake, fake, fake, fake, nul, ctypes.c_float(1.0), fake, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"counts" in lib.moe_last_error()
+
+
+def test_status_strings():
+    lib = L.load()
+    for s in range(5):
+        assert lib.moe_status_string(s)

@@ -1,0 +1,253 @@
+"""Per-step parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Integer results (indices, counts, offsets, rows) must be bit-exact; floating-point
+results must be within the benchmark spec's tolerance (max |err| / rms(ref)): 1e-4 for fp32
+activations, 2e-2 for bf16.  Inputs are the seeded generator's bytes; both sides consume
+the same bytes.
+"""
+import numpy as np
+import pytest
+
+from helpers import MARGIN, O, W, dev, f64, oracle_inputs, rel_err, spec_of, to_dev, to_np, tol, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+SMALL_IDS = sorted(W.SMALL)
+
+
+def _lib():
+    from mixture_experts_layer_aux_amd import _lib as L
+    L.load()
+    return L
+
+
+def _router_case(shape, logits32, expert_bias):
+    torch = torch_mod()
+    L = _lib()
+    cfg = L.config_from_shape(shape)
+    T, E, k = shape.T, shape.E, shape.k
+    lg = to_dev(logits32)
+    eb = to_dev(expert_bias)
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev())
+    w = torch.empty(T, k, dtype=torch.float32, device=dev())
+    counts = torch.empty(E, dtype=torch.int32, device=dev())
+    ps = torch.empty(E, dtype=torch.float32, device=dev())
+    stats = torch.empty(L.MOE_NSTATS, dtype=torch.float32, device=dev())
+    ws = L.alloc_workspace(cfg, dev())
+    L.router_topk(cfg, lg, eb, idx, w, counts, ps, stats, ws)
+    torch.cuda.synchronize()
+    spec = spec_of(shape)
+    r = O.route(logits32.astype(np.float64), spec, None if expert_bias is None else expert_bias.astype(np.float64))
+    assert np.array_equal(to_np(idx), r["idx"]), "top-k indices differ"
+    assert np.array_equal(to_np(counts), r["counts"]), "counts differ"
+    assert to_np(counts).sum() == T * k
+    np.testing.assert_allclose(to_np(w), r["w"], rtol=2e-6, atol=1e-7)
+    st = to_np(stats)
+    assert st[1] == pytest.approx(r["maxvio"], rel=1e-5, abs=1e-6)
+    assert st[2] == int((r["counts"] == 0).sum())
+    assert st[3] == r["counts"].max()
+    if shape.score == "softmax":
+        np.testing.assert_allclose(to_np(ps), r["prob_sum"], rtol=2e-5, atol=1e-5)
+        assert st[0] == pytest.approx(r["aux"], rel=2e-5, abs=1e-9)
+    return r
+
+
+@pytest.mark.parametrize("cid", SMALL_IDS)
+def test_router_small_configs(cid):
+    shape = W.SMALL[cid]
+    inp = W.make_inputs(shape, seed=cid, with_dy=False, with_experts=False)
+    logits = O.gate_logits(f64(inp["x"], shape.act), inp["Wg"], inp["bg"]).astype(np.float32)
+    _router_case(shape, logits, inp["expert_bias"])
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_router_full_size(cid):
+    shape = W.CONFIGS[cid]
+    inp = W.make_inputs(shape, seed=cid, with_dy=False, with_experts=False)
+    logits = O.gate_logits(f64(inp["x"], shape.act), inp["Wg"], inp["bg"]).astype(np.float32)
+    _router_case(shape, logits, inp["expert_bias"])
+
+
+@pytest.mark.parametrize("score,k,E,scaling", [("softmax", 4, 16, 1.0), ("softmax", 8, 300, 2.5),
+                                               ("sigmoid", 1, 8, 1.0), ("sigmoid", 6, 64, 2.5),
+                                               ("softmax", 32, 2048, 1.0), ("softmax", 2, 2, 1.0)])
+def test_router_ties_and_variants(score, k, E, scaling):
+    shape = W.LayerShape("router-edge", T=333, d=64, E=E, k=k, F=128, score=score, act="f32", scaling=scaling,
+                         aux_coeff=0.01 if score == "softmax" else 0.0)
+    rng = np.random.default_rng(E * 7 + k)
+    # quantised logits: many exact ties, so the lowest-index rule decides
+    logits = (rng.integers(-3, 4, size=(shape.T, E)) * 0.5).astype(np.float32)
+    bias = (rng.integers(-2, 3, size=E) * 0.125).astype(np.float32) if score == "sigmoid" else None
+    _router_case(shape, logits, bias)
+
+
+@pytest.mark.parametrize("cid", SMALL_IDS)
+def test_permute_bit_exact(cid):
+    torch = torch_mod()
+    L = _lib()
+    shape = W.SMALL[cid]
+    cfg = L.config_from_shape(shape)
+    inp = W.make_inputs(shape, seed=cid, with_dy=False, with_experts=False)
+    logits = O.gate_logits(f64(inp["x"], shape.act), inp["Wg"], inp["bg"])
+    idx = O.route(logits, spec_of(shape), inp["expert_bias"])["idx"]
+    T, k, E, d = shape.T, shape.k, shape.E, shape.d
+    x = to_dev(inp["x"])
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev())
+    row_of = torch.empty(T, k, dtype=torch.int32, device=dev())
+    token_of = torch.empty(T * k, dtype=torch.int32, device=dev())
+    x_perm = torch.empty(T * k, d, dtype=x.dtype, device=dev())
+    ws = L.alloc_workspace(cfg, dev())
+    L.permute(cfg, x, to_dev(idx.astype(np.int32)), offsets, row_of, token_of, x_perm, ws)
+    torch.cuda.synchronize()
+    p = O.permutation(idx, E)
+    assert np.array_equal(to_np(offsets), p.offsets)
+    assert np.array_equal(to_np(row_of), p.row_of)
+    assert np.array_equal(to_np(token_of), p.token_of)
+    # the moved rows are exact copies
+    assert torch.equal(x_perm, x[torch.from_numpy(p.token_of).to(dev())])
+
+
+def _expert_inputs(shape, cid):
+    inp = W.make_inputs(shape, seed=cid)
+    o = oracle_inputs(inp, shape)
+    logits = O.gate_logits(o["x"], o["Wg"], o["bg"])
+    r = O.route(logits, spec_of(shape), o["expert_bias"])
+    p = O.permutation(r["idx"], shape.E)
+    return inp, o, r, p
+
+
+@pytest.mark.parametrize("cid", SMALL_IDS)
+def test_grouped_experts_forward_and_backward(cid):
+    torch = torch_mod()
+    L = _lib()
+    shape = W.SMALL[cid]
+    cfg = L.config_from_shape(shape)
+    inp, o, r, p = _expert_inputs(shape, cid)
+    T, k, E, d, F, Fs, A = shape.T, shape.k, shape.E, shape.d, shape.F, shape.Fs, shape.A
+    x = to_dev(inp["x"])
+    ad = x.dtype
+    x_perm = x[torch.from_numpy(p.token_of).to(dev())].contiguous()
+    off = to_dev(p.offsets.astype(np.int32))
+    W13, W2 = to_dev(inp["W13"]), to_dev(inp["W2"])
+    W13s, W2s = to_dev(inp["W13s"]), to_dev(inp["W2s"])
+    e = lambda *s: torch.empty(*s, dtype=ad, device=dev())  # noqa: E731
+    H, Act, Yp = e(A, 2 * F), e(A, F), e(A, d)
+    H_s, Act_s, Y_s = (e(T, 2 * Fs), e(T, Fs), e(T, d)) if Fs else (None, None, None)
+    ws = L.alloc_workspace(cfg, dev())
+    L.grouped_gemm_swiglu(cfg, x_perm, off, W13, W2, x if Fs else None, W13s, W2s, H, Act, Yp, H_s, Act_s, Y_s, ws)
+    # backward with a generator upstream gradient on the permuted rows
+    dYp_np = W.random_rows(A, d, seed=100 + cid, act=shape.act)
+    dYp = to_dev(dYp_np)
+    dH, dXp = e(A, 2 * F), e(A, d)
+    dW13, dW2 = e(E, 2 * F, d), e(E, d, F)
+    dy = to_dev(inp["dy"])
+    dH_s, dx_s = (e(T, 2 * Fs), e(T, d)) if Fs else (None, None)
+    dW13s, dW2s = (e(2 * Fs, d), e(d, Fs)) if Fs else (None, None)
+    L.grouped_gemm_swiglu_bwd(cfg, x_perm, off, W13, W2, H, Act, dYp, dH, dXp, dW13, dW2, x if Fs else None, W13s,
+                              W2s, H_s, Act_s, dy if Fs else None, dH_s, dx_s, dW13s, dW2s, ws)
+    torch.cuda.synchronize()
+    tl = tol(shape)
+    xp = o["x"][p.token_of]
+    dYo = f64(dYp_np, shape.act)
+    ref = dict(H=np.zeros((A, 2 * F)), Act=np.zeros((A, F)), Y=np.zeros((A, d)), dH=np.zeros((A, 2 * F)),
+               dX=np.zeros((A, d)), dW13=np.zeros((E, 2 * F, d)), dW2=np.zeros((E, d, F)))
+    for ex in range(E):
+        a, b = p.offsets[ex], p.offsets[ex + 1]
+        if b == a:
+            continue
+        h, act, y = O.swiglu_forward(xp[a:b], o["W13"][ex], o["W2"][ex])
+        ref["H"][a:b], ref["Act"][a:b], ref["Y"][a:b] = h, act, y
+        # the backward is evaluated at the GPU's stored forward activations' exact values? no:
+        # at the oracle's own (unrounded) H, which is the definition
+        g = O.swiglu_backward(xp[a:b], o["W13"][ex], o["W2"][ex], h, dYo[a:b])
+        ref["dH"][a:b], ref["dX"][a:b], ref["dW13"][ex], ref["dW2"][ex] = g["dH"], g["dX"], g["dW13"], g["dW2"]
+    for name, got in (("H", H), ("Act", Act), ("Y", Yp), ("dH", dH), ("dX", dXp), ("dW13", dW13), ("dW2", dW2)):
+        err = rel_err(to_np(got), ref[name])
+        assert err < tl, f"{name}: {err:.3e}"
+    empty = np.where(np.diff(p.offsets) == 0)[0]
+    for ex in empty:                       # experts with no rows: exact-zero gradients
+        assert torch.count_nonzero(dW13[ex]) == 0 and torch.count_nonzero(dW2[ex]) == 0
+    if Fs:
+        hs, acts, ys = O.swiglu_forward(o["x"], o["W13s"], o["W2s"])
+        gs = O.swiglu_backward(o["x"], o["W13s"], o["W2s"], hs, o["dy"])
+        for name, got, rf in (("H_s", H_s, hs), ("Act_s", Act_s, acts), ("Y_s", Y_s, ys), ("dH_s", dH_s, gs["dH"]),
+                              ("dx_s", dx_s, gs["dX"]), ("dW13s", dW13s, gs["dW13"]), ("dW2s", dW2s, gs["dW2"])):
+            err = rel_err(to_np(got), rf)
+            assert err < tl, f"{name}: {err:.3e}"
+
+
+@pytest.mark.parametrize("cid", SMALL_IDS)
+def test_combine_and_backward_pieces(cid):
+    torch = torch_mod()
+    L = _lib()
+    shape = W.SMALL[cid]
+    cfg = L.config_from_shape(shape)
+    inp, o, r, p = _expert_inputs(shape, cid)
+    T, k, E, d, A = shape.T, shape.k, shape.E, shape.d, shape.A
+    Yp_np = W.random_rows(A, d, seed=200 + cid, act=shape.act)
+    Ys_np = W.random_rows(T, d, seed=300 + cid, act=shape.act)
+    dy_np = inp["dy"]
+    Yp, Ys, dy = to_dev(Yp_np), to_dev(Ys_np), to_dev(dy_np)
+    row_of = to_dev(p.row_of.astype(np.int32))
+    wt = to_dev(r["w"].astype(np.float32))
+    y = torch.empty(T, d, dtype=Yp.dtype, device=dev())
+    L.unpermute_combine(cfg, Yp, row_of, wt, Ys, y)
+    dYp = torch.empty_like(Yp)
+    dw = torch.empty(T, k, dtype=torch.float32, device=dev())
+    L.unpermute_combine_bwd(cfg, dy, Yp, row_of, wt, dYp, dw)
+    dXp_np = W.random_rows(A, d, seed=400 + cid, act=shape.act)
+    dxs_np = W.random_rows(T, d, seed=500 + cid, act=shape.act)
+    dxr_np = W.random_rows(T, d, seed=600 + cid, act="f32")
+    dx = torch.empty(T, d, dtype=Yp.dtype, device=dev())
+    L.permute_bwd(cfg, to_dev(dXp_np), row_of, to_dev(dxs_np), to_dev(dxr_np), dx)
+    torch.cuda.synchronize()
+    a = shape.act
+    w32 = r["w"].astype(np.float32).astype(np.float64)
+    Ypo, Yso, dyo = f64(Yp_np, a), f64(Ys_np, a), f64(dy_np, a)
+    y_ref = np.einsum("tk,tkd->td", w32, Ypo[p.row_of]) + Yso
+    tl = tol(shape)
+    assert rel_err(to_np(y), y_ref) < tl
+    dYp_ref = np.zeros((A, d))
+    dYp_ref[p.row_of.ravel()] = (w32[:, :, None] * dyo[:, None, :]).reshape(-1, d)
+    assert rel_err(to_np(dYp), dYp_ref) < tl
+    dw_ref = np.einsum("td,tkd->tk", dyo, Ypo[p.row_of])
+    assert rel_err(to_np(dw), dw_ref) < 1e-5
+    dx_ref = f64(dXp_np, a)[p.row_of].sum(1) + f64(dxs_np, a) + dxr_np.astype(np.float64)
+    assert rel_err(to_np(dx), dx_ref) < tl
+
+
+@pytest.mark.parametrize("cid", SMALL_IDS)
+def test_router_and_gate_backward(cid):
+    torch = torch_mod()
+    L = _lib()
+    shape = W.SMALL[cid]
+    cfg = L.config_from_shape(shape)
+    inp = W.make_inputs(shape, seed=cid, with_experts=False)
+    o = oracle_inputs(dict(inp, W13=None, W2=None), shape)
+    T, k, E, d = shape.T, shape.k, shape.E, shape.d
+    logits = O.gate_logits(o["x"], o["Wg"], o["bg"]).astype(np.float32)
+    spec = spec_of(shape)
+    r = O.route(logits.astype(np.float64), spec, o["expert_bias"])
+    dw_np = W.random_rows(T, k, seed=700 + cid, act="f32")
+    dl = torch.empty(T, E, dtype=torch.float32, device=dev())
+    L.router_bwd(cfg, to_dev(logits), to_dev(r["idx"].astype(np.int32)), to_dev(r["w"].astype(np.float32)),
+                 to_dev(dw_np), to_dev(r["counts"].astype(np.int32)), 1.0, dl)
+    # gate: logits and the two gate-gradient GEMMs on a generator dlogits
+    lg = torch.empty(T, E, dtype=torch.float32, device=dev())
+    x = to_dev(inp["x"])
+    Wg = to_dev(inp["Wg"])
+    L.gate_logits(cfg, x, Wg, to_dev(inp["bg"]), lg)
+    dl_np = W.random_rows(T, E, seed=800 + cid, act="f32")
+    dWg = torch.empty(E, d, dtype=torch.float32, device=dev())
+    dbg = torch.empty(E, dtype=torch.float32, device=dev())
+    dxr = torch.empty(T, d, dtype=torch.float32, device=dev())
+    L.gate_logits_bwd(cfg, x, Wg, to_dev(dl_np), dWg, dbg, dxr)
+    torch.cuda.synchronize()
+    ref = O.router_backward(logits.astype(np.float64), r["idx"], r["w"].astype(np.float32).astype(np.float64),
+                            dw_np.astype(np.float64), spec, counts=r["counts"], daux=1.0)
+    assert rel_err(to_np(dl), ref) < 1e-5
+    assert rel_err(to_np(lg), O.gate_logits(o["x"], o["Wg"], o["bg"])) < 1e-5
+    dlo = dl_np.astype(np.float64)
+    assert rel_err(to_np(dWg), dlo.T @ o["x"]) < 1e-5
+    assert rel_err(to_np(dbg), dlo.sum(0)) < 1e-5
+    assert rel_err(to_np(dxr), dlo @ o["Wg"]) < 1e-5
