@@ -13,7 +13,8 @@
  * FFN width, Fs shared-expert width (0 = none), A = T*k routed rows.
  *
  * Layouts (all row-major, contiguous):
- *   x, y, dy, dx          [T, d]      activation dtype (act_dtype)
+ *   x                     [T, d]      activation dtype (act_dtype)
+ *   y, dy, dx             [T, d]      fp32
  *   Wg                    [E, d]      fp32        router weight ([HB] §3.4 Count and size)
  *   W13                   [E, 2F, d]  act dtype   fc1 of each expert, gate rows then up rows
  *   W2                    [E, d, F]   act dtype   fc2 of each expert
@@ -22,9 +23,18 @@
  *   idx [T, k] int32, w [T, k] fp32   slot j: j-th best expert (key descending, ties to the
  *                                     lower expert index) and its mixing weight
  *   counts [E] int32, offsets [E+1] int32, row_of [T, k] int32, token_of [A] int32
- *   x_perm, Y_perm        [A, d]      act dtype, rows grouped by expert ascending, and by
+ *   x_perm                [A, d]      act dtype, rows grouped by expert ascending, and by
  *                                     token ascending inside an expert
- *   H [A, 2F], Act [A, F]             act dtype
+ *   H [A, 2F] fp32, Act [A, F] act dtype   fc1 output (gate half, then up half), SwiGLU
+ *   Y_perm [A, d], Y_s [T, d]         fp32 expert outputs (same row order as x_perm)
+ *   dX_perm [A, d]                    fp32 per-row input gradients
+ *   dW13, dW2, dW13s, dW2s            fp32 weight gradients, shaped like the weights
+ *
+ * Precision: every GEMM multiplies act-dtype operands (bf16 on the matrix cores) with
+ * fp32 accumulation.  Only GEMM operands are stored in bf16 (x_perm, Act, dY_perm, dH);
+ * everything that is summed or differentiated further (H, expert outputs, per-row input
+ * gradients, y, dx, weight gradients) stays fp32: one bf16 rounding of a value five to six
+ * standard deviations out is already 2e-2 of the tensor's RMS.
  *
  * Errors: every argument is checked on the host before anything is launched.  A call
  * that fails a check launches nothing and returns MOE_ERR_INVALID_ARG,
@@ -102,22 +112,22 @@ typedef struct moe_saved {
   int32_t* row_of;   /* [T, k] */
   int32_t* token_of; /* [A] */
   void* x_perm;      /* [A, d] */
-  void* H;           /* [A, 2F] */
+  void* H;           /* [A, 2F] fp32 */
   void* Act;         /* [A, F] */
-  void* Y_perm;      /* [A, d] */
-  void* H_s;         /* [T, 2Fs] or NULL when Fs == 0 */
+  void* Y_perm;      /* [A, d] fp32 */
+  void* H_s;         /* [T, 2Fs] fp32, or NULL when Fs == 0 */
   void* Act_s;       /* [T, Fs]  or NULL */
-  void* Y_s;         /* [T, d]   or NULL */
+  void* Y_s;         /* [T, d]   fp32, or NULL */
 } moe_saved_t;
 
 /* Gradients written by moe_layer_bwd (overwritten, not accumulated). */
 typedef struct moe_grads {
   float* dWg;  /* [E, d] fp32 */
   float* dbg;  /* [E] fp32, or NULL */
-  void* dW13;  /* [E, 2F, d] act dtype; experts with no rows get exact zeros */
-  void* dW2;   /* [E, d, F] act dtype */
-  void* dW13s; /* [2Fs, d] or NULL when Fs == 0 */
-  void* dW2s;  /* [d, Fs]  or NULL */
+  float* dW13;  /* [E, 2F, d]; experts with no rows get exact zeros */
+  float* dW2;   /* [E, d, F] */
+  float* dW13s; /* [2Fs, d] or NULL when Fs == 0 */
+  float* dW2s;  /* [d, Fs]  or NULL */
 } moe_grads_t;
 
 const char* moe_status_string(moe_status_t status);
@@ -157,8 +167,8 @@ moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* 
 
 /* Grouped SwiGLU experts ([HB] §3.4 Count and size, Activation): for each expert e, on its
  * rows [offsets[e], offsets[e+1]):  H = X W13[e]^T, Act = silu(H[:, :F]) * H[:, F:],
- * Y_perm = Act W2[e]^T.  When Fs > 0 the shared expert runs the same on x (all T rows)
- * into H_s, Act_s, Y_s ([HB] §3.4 Shared experts). */
+ * Y_perm = Act W2[e]^T (fp32).  When Fs > 0 the shared expert runs the same on x (all T
+ * rows) into H_s, Act_s, Y_s ([HB] §3.4 Shared experts). */
 moe_status_t moe_grouped_gemm_swiglu(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
                                      const void* W13, const void* W2, const void* x, const void* W13s,
                                      const void* W2s, void* H, void* Act, void* Y_perm, void* H_s,
@@ -168,13 +178,13 @@ moe_status_t moe_grouped_gemm_swiglu(const moe_config_t* cfg, const void* x_perm
  * sum of the selected outputs, coordinate by coordinate; [HB] §3.4 Shared experts: the
  * shared output is added at weight 1):
  *   y[t] = sum_j w[t, j] * Y_perm[row_of[t, j]] (+ Y_s[t]), fp32 accumulation, slot order. */
-moe_status_t moe_unpermute_combine(const moe_config_t* cfg, const void* Y_perm, const int32_t* row_of,
-                                   const float* w, const void* Y_s, void* y, void* stream);
+moe_status_t moe_unpermute_combine(const moe_config_t* cfg, const float* Y_perm, const int32_t* row_of,
+                                   const float* w, const float* Y_s, float* y, void* stream);
 
 /* Whole forward: gate logits, router, permute, grouped experts (+ shared), combine.
  * Fills *saved for the backward.  stats as in moe_router_topk (NULL ok). */
 moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* weights, const void* x,
-                           const moe_saved_t* saved, void* y, float* stats, void* ws, size_t ws_bytes,
+                           const moe_saved_t* saved, float* y, float* stats, void* ws, size_t ws_bytes,
                            void* stream);
 
 /* ---------------------------------------------------------------- backward pieces
@@ -182,29 +192,30 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* weights
  * the router, selection carries none ([LC] "How the router learns without an
  * expert-selection answer key"). */
 
-/* dY_perm[row_of[t, j]] = w[t, j] * dy[t];  dw[t, j] = <dy[t], Y_perm[row_of[t, j]]>. */
-moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const void* dy, const void* Y_perm,
+/* dY_perm[row_of[t, j]] = w[t, j] * dy[t] (act dtype);  dw[t, j] = <dy[t], Y_perm[row_of[t, j]]>;
+ * dY_s (NULL ok) = dy in the act dtype: the shared expert's upstream gradient. */
+moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const float* dy, const float* Y_perm,
                                        const int32_t* row_of, const float* w, void* dY_perm, float* dw,
-                                       void* stream);
+                                       void* dY_s, void* stream);
 
 /* Expert backward, per expert e on its rows (and the shared expert on all T rows with
- * upstream gradient dy, when Fs > 0):
+ * upstream gradient dY_s [T, d] act dtype, when Fs > 0):
  *   dAct = dY W2[e];  dH = [dAct * up * silu'(gate), dAct * silu(gate)];
  *   dW2[e] = dY^T Act;  dX = dH W13[e];  dW13[e] = dH^T X.
- * dX_perm may alias dY_perm (dY_perm is consumed before dX_perm is written).
- * dH [A, 2F] and dH_s [T, 2Fs] are outputs too.  dx_s [T, d] receives the shared
- * expert's input gradient. */
+ * dX_perm (fp32) may alias dY_perm when the buffer holds A*d fp32 values (dY_perm is
+ * consumed before dX_perm is written).  dH [A, 2F] and dH_s [T, 2Fs] (act dtype) are
+ * outputs too.  dx_s [T, d] fp32 receives the shared expert's input gradient. */
 moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
                                          const void* W13, const void* W2, const void* H, const void* Act,
                                          const void* dY_perm, void* dH, void* dX_perm, void* dW13, void* dW2,
                                          const void* x, const void* W13s, const void* W2s, const void* H_s,
-                                         const void* Act_s, const void* dy, void* dH_s, void* dx_s,
+                                         const void* Act_s, const void* dY_s, void* dH_s, void* dx_s,
                                          void* dW13s, void* dW2s, void* ws, size_t ws_bytes, void* stream);
 
 /* Unpermute-reduce: dx[t] = sum_j dX_perm[row_of[t, j]] (+ dx_s[t]) (+ dx_r[t]),
- * fp32 accumulation in that order.  dx_s act dtype or NULL; dx_r fp32 or NULL. */
-moe_status_t moe_permute_bwd(const moe_config_t* cfg, const void* dX_perm, const int32_t* row_of,
-                             const void* dx_s, const float* dx_r, void* dx, void* stream);
+ * fp32 accumulation in that order.  All fp32; dx_s and dx_r may be NULL. */
+moe_status_t moe_permute_bwd(const moe_config_t* cfg, const float* dX_perm, const int32_t* row_of,
+                             const float* dx_s, const float* dx_r, float* dx, void* stream);
 
 /* Router backward: dlogits [T, E] from dw [T, k] through the weights of the selected
  * experts, plus daux times the aux-loss gradient through the full softmax (counts held
@@ -219,7 +230,7 @@ moe_status_t moe_gate_logits_bwd(const moe_config_t* cfg, const void* x, const f
 
 /* Whole backward from the saved forward tensors. */
 moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* weights, const moe_saved_t* saved,
-                           const void* x, const void* dy, float daux, void* dx, const moe_grads_t* grads,
+                           const void* x, const float* dy, float daux, float* dx, const moe_grads_t* grads,
                            void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -175,51 +175,59 @@ def grouped_gemm_swiglu(cfg, x_perm, offsets, W13, W2, x, W13s, W2s, H, Act, Y_p
         ctypes.byref(cfg), _P(_ptr(x_perm, ad, A * d, "x_perm")), _P(_ptr(offsets, torch.int32, E + 1, "offsets")),
         _P(_ptr(W13, ad, E * 2 * F * d, "W13")), _P(_ptr(W2, ad, E * d * F, "W2")),
         _P(_ptr(x, ad, T * d, "x")), _P(_ptr(W13s, ad, 2 * Fs * d, "W13s")), _P(_ptr(W2s, ad, d * Fs, "W2s")),
-        _P(_ptr(H, ad, A * 2 * F, "H")), _P(_ptr(Act, ad, A * F, "Act")), _P(_ptr(Y_perm, ad, A * d, "Y_perm")),
-        _P(_ptr(H_s, ad, T * 2 * Fs, "H_s")), _P(_ptr(Act_s, ad, T * Fs, "Act_s")), _P(_ptr(Y_s, ad, T * d, "Y_s")),
+        _P(_ptr(H, torch.float32, A * 2 * F, "H")), _P(_ptr(Act, ad, A * F, "Act")),
+        _P(_ptr(Y_perm, torch.float32, A * d, "Y_perm")),
+        _P(_ptr(H_s, torch.float32, T * 2 * Fs, "H_s")), _P(_ptr(Act_s, ad, T * Fs, "Act_s")),
+        _P(_ptr(Y_s, torch.float32, T * d, "Y_s")),
         _P(wp), ctypes.c_size_t(wn), _P(_stream(stream))))
 
 
 def unpermute_combine(cfg, Y_perm, row_of, w, Y_s, y, stream=None):
-    ad, A = act_dtype(cfg), cfg.T * cfg.k
-    _check(load().moe_unpermute_combine(ctypes.byref(cfg), _P(_ptr(Y_perm, ad, A * cfg.d, "Y_perm")),
-                                        _P(_ptr(row_of, torch.int32, A, "row_of")), _P(_ptr(w, torch.float32, A, "w")),
-                                        _P(_ptr(Y_s, ad, cfg.T * cfg.d, "Y_s")), _P(_ptr(y, ad, cfg.T * cfg.d, "y")),
+    A, f32 = cfg.T * cfg.k, torch.float32
+    _check(load().moe_unpermute_combine(ctypes.byref(cfg), _P(_ptr(Y_perm, f32, A * cfg.d, "Y_perm")),
+                                        _P(_ptr(row_of, torch.int32, A, "row_of")), _P(_ptr(w, f32, A, "w")),
+                                        _P(_ptr(Y_s, f32, cfg.T * cfg.d, "Y_s")), _P(_ptr(y, f32, cfg.T * cfg.d, "y")),
                                         _P(_stream(stream))))
 
 
-def unpermute_combine_bwd(cfg, dy, Y_perm, row_of, w, dY_perm, dw, stream=None):
-    ad, A = act_dtype(cfg), cfg.T * cfg.k
-    _check(load().moe_unpermute_combine_bwd(ctypes.byref(cfg), _P(_ptr(dy, ad, cfg.T * cfg.d, "dy")),
-                                            _P(_ptr(Y_perm, ad, A * cfg.d, "Y_perm")),
+def unpermute_combine_bwd(cfg, dy, Y_perm, row_of, w, dY_perm, dw, dY_s=None, stream=None):
+    ad, A, f32 = act_dtype(cfg), cfg.T * cfg.k, torch.float32
+    _check(load().moe_unpermute_combine_bwd(ctypes.byref(cfg), _P(_ptr(dy, f32, cfg.T * cfg.d, "dy")),
+                                            _P(_ptr(Y_perm, f32, A * cfg.d, "Y_perm")),
                                             _P(_ptr(row_of, torch.int32, A, "row_of")),
-                                            _P(_ptr(w, torch.float32, A, "w")),
+                                            _P(_ptr(w, f32, A, "w")),
                                             _P(_ptr(dY_perm, ad, A * cfg.d, "dY_perm")),
-                                            _P(_ptr(dw, torch.float32, A, "dw")), _P(_stream(stream))))
+                                            _P(_ptr(dw, f32, A, "dw")), _P(_ptr(dY_s, ad, cfg.T * cfg.d, "dY_s")),
+                                            _P(_stream(stream))))
 
 
 def grouped_gemm_swiglu_bwd(cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, dX_perm, dW13, dW2, x, W13s, W2s,
-                            H_s, Act_s, dy, dH_s, dx_s, dW13s, dW2s, ws, stream=None):
+                            H_s, Act_s, dY_s, dH_s, dx_s, dW13s, dW2s, ws, stream=None):
     ad, A, T, d, E, F, Fs = act_dtype(cfg), cfg.T * cfg.k, cfg.T, cfg.d, cfg.E, cfg.F, cfg.Fs
     wp, wn = _ws(ws)
     _check(load().moe_grouped_gemm_swiglu_bwd(
         ctypes.byref(cfg), _P(_ptr(x_perm, ad, A * d, "x_perm")), _P(_ptr(offsets, torch.int32, E + 1, "offsets")),
-        _P(_ptr(W13, ad, E * 2 * F * d, "W13")), _P(_ptr(W2, ad, E * d * F, "W2")), _P(_ptr(H, ad, A * 2 * F, "H")),
+        _P(_ptr(W13, ad, E * 2 * F * d, "W13")), _P(_ptr(W2, ad, E * d * F, "W2")),
+        _P(_ptr(H, torch.float32, A * 2 * F, "H")),
         _P(_ptr(Act, ad, A * F, "Act")), _P(_ptr(dY_perm, ad, A * d, "dY_perm")), _P(_ptr(dH, ad, A * 2 * F, "dH")),
-        _P(_ptr(dX_perm, ad, A * d, "dX_perm")), _P(_ptr(dW13, ad, E * 2 * F * d, "dW13")),
-        _P(_ptr(dW2, ad, E * d * F, "dW2")), _P(_ptr(x, ad, T * d, "x")), _P(_ptr(W13s, ad, 2 * Fs * d, "W13s")),
-        _P(_ptr(W2s, ad, d * Fs, "W2s")), _P(_ptr(H_s, ad, T * 2 * Fs, "H_s")), _P(_ptr(Act_s, ad, T * Fs, "Act_s")),
-        _P(_ptr(dy, ad, T * d, "dy")), _P(_ptr(dH_s, ad, T * 2 * Fs, "dH_s")), _P(_ptr(dx_s, ad, T * d, "dx_s")),
-        _P(_ptr(dW13s, ad, 2 * Fs * d, "dW13s")), _P(_ptr(dW2s, ad, d * Fs, "dW2s")), _P(wp), ctypes.c_size_t(wn),
+        _P(_ptr(dX_perm, torch.float32, A * d, "dX_perm")), _P(_ptr(dW13, torch.float32, E * 2 * F * d, "dW13")),
+        _P(_ptr(dW2, torch.float32, E * d * F, "dW2")), _P(_ptr(x, ad, T * d, "x")),
+        _P(_ptr(W13s, ad, 2 * Fs * d, "W13s")),
+        _P(_ptr(W2s, ad, d * Fs, "W2s")), _P(_ptr(H_s, torch.float32, T * 2 * Fs, "H_s")),
+        _P(_ptr(Act_s, ad, T * Fs, "Act_s")),
+        _P(_ptr(dY_s, ad, T * d, "dY_s")), _P(_ptr(dH_s, ad, T * 2 * Fs, "dH_s")), _P(_ptr(dx_s, torch.float32, T * d, "dx_s")),
+        _P(_ptr(dW13s, torch.float32, 2 * Fs * d, "dW13s")), _P(_ptr(dW2s, torch.float32, d * Fs, "dW2s")), _P(wp),
+        ctypes.c_size_t(wn),
         _P(_stream(stream))))
 
 
 def permute_bwd(cfg, dX_perm, row_of, dx_s, dx_r, dx, stream=None):
     ad, A = act_dtype(cfg), cfg.T * cfg.k
-    _check(load().moe_permute_bwd(ctypes.byref(cfg), _P(_ptr(dX_perm, ad, A * cfg.d, "dX_perm")),
-                                  _P(_ptr(row_of, torch.int32, A, "row_of")), _P(_ptr(dx_s, ad, cfg.T * cfg.d, "dx_s")),
+    _check(load().moe_permute_bwd(ctypes.byref(cfg), _P(_ptr(dX_perm, torch.float32, A * cfg.d, "dX_perm")),
+                                  _P(_ptr(row_of, torch.int32, A, "row_of")),
+                                  _P(_ptr(dx_s, torch.float32, cfg.T * cfg.d, "dx_s")),
                                   _P(_ptr(dx_r, torch.float32, cfg.T * cfg.d, "dx_r")),
-                                  _P(_ptr(dx, ad, cfg.T * cfg.d, "dx")), _P(_stream(stream))))
+                                  _P(_ptr(dx, torch.float32, cfg.T * cfg.d, "dx")), _P(_stream(stream))))
 
 
 def router_bwd(cfg, logits, idx, w, dw, counts, daux, dlogits, stream=None):
@@ -253,8 +261,8 @@ def _saved_struct(cfg, S: Dict[str, torch.Tensor]) -> Saved:
     ad, T, d, E, F, Fs, A = act_dtype(cfg), cfg.T, cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.T * cfg.k
     spec = dict(logits=(torch.float32, T * E), idx=(torch.int32, A), w=(torch.float32, A), counts=(torch.int32, E),
                 offsets=(torch.int32, E + 1), row_of=(torch.int32, A), token_of=(torch.int32, A),
-                x_perm=(ad, A * d), H=(ad, A * 2 * F), Act=(ad, A * F), Y_perm=(ad, A * d),
-                H_s=(ad, T * 2 * Fs), Act_s=(ad, T * Fs), Y_s=(ad, T * d))
+                x_perm=(ad, A * d), H=(torch.float32, A * 2 * F), Act=(ad, A * F), Y_perm=(torch.float32, A * d),
+                H_s=(torch.float32, T * 2 * Fs), Act_s=(ad, T * Fs), Y_s=(torch.float32, T * d))
     return Saved(**{n: _ptr(S.get(n), dt, ne, n) for n, (dt, ne) in spec.items()})
 
 
@@ -264,7 +272,7 @@ def layer_fwd(cfg, W, x, S, y, stats, ws, stream=None):
     ws_ = _weights_struct(cfg, W)
     ss = _saved_struct(cfg, S)
     _check(load().moe_layer_fwd(ctypes.byref(cfg), ctypes.byref(ws_), _P(_ptr(x, ad, cfg.T * cfg.d, "x")),
-                                ctypes.byref(ss), _P(_ptr(y, ad, cfg.T * cfg.d, "y")),
+                                ctypes.byref(ss), _P(_ptr(y, torch.float32, cfg.T * cfg.d, "y")),
                                 _P(_ptr(stats, torch.float32, MOE_NSTATS, "stats")), _P(wp), ctypes.c_size_t(wn),
                                 _P(_stream(stream))))
 
@@ -274,12 +282,13 @@ def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None):
     ad, d, E, F, Fs = act_dtype(cfg), cfg.d, cfg.E, cfg.F, cfg.Fs
     ws_ = _weights_struct(cfg, W)
     ss = _saved_struct(cfg, S)
-    gs = Grads(dWg=_ptr(G["dWg"], torch.float32, E * d, "dWg"), dbg=_ptr(G.get("dbg"), torch.float32, E, "dbg"),
-               dW13=_ptr(G["dW13"], ad, E * 2 * F * d, "dW13"), dW2=_ptr(G["dW2"], ad, E * d * F, "dW2"),
-               dW13s=_ptr(G.get("dW13s"), ad, 2 * Fs * d, "dW13s"), dW2s=_ptr(G.get("dW2s"), ad, d * Fs, "dW2s"))
+    f32 = torch.float32
+    gs = Grads(dWg=_ptr(G["dWg"], f32, E * d, "dWg"), dbg=_ptr(G.get("dbg"), f32, E, "dbg"),
+               dW13=_ptr(G["dW13"], f32, E * 2 * F * d, "dW13"), dW2=_ptr(G["dW2"], f32, E * d * F, "dW2"),
+               dW13s=_ptr(G.get("dW13s"), f32, 2 * Fs * d, "dW13s"), dW2s=_ptr(G.get("dW2s"), f32, d * Fs, "dW2s"))
     _check(load().moe_layer_bwd(ctypes.byref(cfg), ctypes.byref(ws_), ctypes.byref(ss),
-                                _P(_ptr(x, ad, cfg.T * d, "x")), _P(_ptr(dy, ad, cfg.T * d, "dy")),
-                                ctypes.c_float(daux), _P(_ptr(dx, ad, cfg.T * d, "dx")), ctypes.byref(gs), _P(wp),
+                                _P(_ptr(x, ad, cfg.T * d, "x")), _P(_ptr(dy, f32, cfg.T * d, "dy")),
+                                ctypes.c_float(daux), _P(_ptr(dx, f32, cfg.T * d, "dx")), ctypes.byref(gs), _P(wp),
                                 ctypes.c_size_t(wn), _P(_stream(stream))))
 
 
@@ -290,20 +299,21 @@ def alloc_saved(cfg: Config, device="cuda") -> Dict[str, torch.Tensor]:
     e = lambda *s, dt=ad: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
     S = dict(logits=e(T, E, dt=torch.float32), idx=e(T, cfg.k, dt=torch.int32), w=e(T, cfg.k, dt=torch.float32),
              counts=e(E, dt=torch.int32), offsets=e(E + 1, dt=torch.int32), row_of=e(T, cfg.k, dt=torch.int32),
-             token_of=e(A, dt=torch.int32), x_perm=e(A, d), H=e(A, 2 * F), Act=e(A, F), Y_perm=e(A, d))
+             token_of=e(A, dt=torch.int32), x_perm=e(A, d), H=e(A, 2 * F, dt=torch.float32), Act=e(A, F),
+             Y_perm=e(A, d, dt=torch.float32))
     if Fs:
-        S.update(H_s=e(T, 2 * Fs), Act_s=e(T, Fs), Y_s=e(T, d))
+        S.update(H_s=e(T, 2 * Fs, dt=torch.float32), Act_s=e(T, Fs), Y_s=e(T, d, dt=torch.float32))
     return S
 
 
 def alloc_grads(cfg: Config, device="cuda", with_dbg=False) -> Dict[str, torch.Tensor]:
-    ad, d, E, F, Fs = act_dtype(cfg), cfg.d, cfg.E, cfg.F, cfg.Fs
-    G = dict(dWg=torch.empty(E, d, dtype=torch.float32, device=device),
-             dW13=torch.empty(E, 2 * F, d, dtype=ad, device=device), dW2=torch.empty(E, d, F, dtype=ad, device=device))
+    d, E, F, Fs, f32 = cfg.d, cfg.E, cfg.F, cfg.Fs, torch.float32
+    G = dict(dWg=torch.empty(E, d, dtype=f32, device=device),
+             dW13=torch.empty(E, 2 * F, d, dtype=f32, device=device), dW2=torch.empty(E, d, F, dtype=f32, device=device))
     if with_dbg:
-        G["dbg"] = torch.empty(E, dtype=torch.float32, device=device)
+        G["dbg"] = torch.empty(E, dtype=f32, device=device)
     if Fs:
-        G.update(dW13s=torch.empty(2 * Fs, d, dtype=ad, device=device), dW2s=torch.empty(d, Fs, dtype=ad, device=device))
+        G.update(dW13s=torch.empty(2 * Fs, d, dtype=f32, device=device), dW2s=torch.empty(d, Fs, dtype=f32, device=device))
     return G
 
 

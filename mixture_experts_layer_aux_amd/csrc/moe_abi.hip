@@ -72,13 +72,14 @@ FwdWs carve_fwd(const moe_config_t& c, void* base) {
 }
 
 struct BwdWs {
-  void* dYX;       // [A, d] act: dY_perm, then dX_perm
+  void* dYX;       // [A, d]: dY_perm (act dtype), then dX_perm (fp32) once dY_perm is consumed
   void* dH;        // [A, 2F] act
   float* dw;       // [T, k]
   float* dlogits;  // [T, E]
   float* dx_r;     // [T, d]
   void* dH_s;      // [T, 2Fs] act
-  void* dx_s;      // [T, d] act
+  void* dx_s;      // [T, d] fp32
+  void* dY_s;      // [T, d] act: the shared expert's upstream gradient
   float* dact;     // fp32 path: [max(A, T), max(F, Fs)]
   int32_t* sched;  // [E + 1]
   size_t bytes;
@@ -94,13 +95,14 @@ BwdWs carve_bwd(const moe_config_t& c, void* base) {
   };
   const size_t A = static_cast<size_t>(c.T) * c.k, T = static_cast<size_t>(c.T), eb = act_bytes(c);
   BwdWs w;
-  w.dYX = take(A * c.d * eb);
+  w.dYX = take(A * c.d * 4);
   w.dH = take(A * 2 * c.F * eb);
   w.dw = reinterpret_cast<float*>(take(A * 4));
   w.dlogits = reinterpret_cast<float*>(take(T * c.E * 4));
   w.dx_r = reinterpret_cast<float*>(take(T * c.d * 4));
   w.dH_s = c.Fs ? take(T * 2 * c.Fs * eb) : nullptr;
-  w.dx_s = c.Fs ? take(T * c.d * eb) : nullptr;
+  w.dx_s = c.Fs ? take(T * c.d * 4) : nullptr;
+  w.dY_s = c.Fs ? take(T * c.d * eb) : nullptr;
   w.dact = c.act_dtype == MOE_F32 ? reinterpret_cast<float*>(take(std::max(A, T) * std::max(c.F, c.Fs) * 4)) : nullptr;
   w.sched = reinterpret_cast<int32_t*>(take(mfma_schedule_bytes(c.E)));
   w.bytes = off;
@@ -179,13 +181,15 @@ moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const in
     void* act = shared ? Act_s : Act;
     GemmDesc g1{};
     g1.a_major = K_MAJOR; g1.b_major = K_MAJOR; g1.ragged = RAGGED_M;
-    g1.a_type = g1.b_type = g1.c_type = c.act_dtype;
+    g1.a_type = g1.b_type = c.act_dtype;
+    g1.c_type = MOE_F32;  // H is kept in fp32 for the SwiGLU backward
     g1.N = 2 * F; g1.K = c.d; g1.F = F;
     g1.A = X; g1.lda = c.d;
     g1.B = shared ? W13s : W13; g1.ldb = c.d; g1.b_gstride = shared ? 0 : int64_t{2} * F * c.d;
     g1.C = h; g1.ldc = 2 * F; g1.C2 = act; g1.ldc2 = F;
     g1.offsets = shared ? nullptr : offsets; g1.G = shared ? 1 : c.E; g1.range_end = c.T; g1.rows_upper = A;
     GemmDesc g2 = g1;
+    g2.c_type = MOE_F32;  // expert outputs are kept in fp32 for the combine
     g2.N = c.d; g2.K = F; g2.A = act; g2.lda = F;
     g2.B = shared ? W2s : W2; g2.ldb = F; g2.b_gstride = shared ? 0 : int64_t{1} * c.d * F;
     g2.C = shared ? Y_s : Y_perm; g2.ldc = c.d; g2.C2 = nullptr; g2.epi = EPI_STORE;
@@ -207,7 +211,7 @@ moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const in
 moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const int32_t* offsets, const void* W13,
                              const void* W2, const void* H, const void* Act, const void* dY_perm, void* dH,
                              void* dX_perm, void* dW13, void* dW2, const void* x, const void* W13s, const void* W2s,
-                             const void* H_s, const void* Act_s, const void* dy, void* dH_s, void* dx_s,
+                             const void* H_s, const void* Act_s, const void* dY_s, void* dH_s, void* dx_s,
                              void* dW13s, void* dW2s, int32_t* sched, float* dact, hipStream_t s) {
   const int64_t A = static_cast<int64_t>(c.T) * c.k;
   for (int shared = 0; shared < (c.Fs ? 2 : 1); ++shared) {
@@ -218,7 +222,7 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
     const void* X = shared ? x : x_perm;
     const void* h = shared ? H_s : H;
     const void* act = shared ? Act_s : Act;
-    const void* dY = shared ? dy : dY_perm;
+    const void* dY = shared ? dY_s : dY_perm;
     void* dh = shared ? dH_s : dH;
     void* dX = shared ? dx_s : dX_perm;
     const void* w13 = shared ? W13s : W13;
@@ -238,7 +242,8 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
     // (2) fc2 weight gradient: dW2 = dY^T Act (reduction over the expert's rows)
     GemmDesc w2g{};
     w2g.a_major = MN_MAJOR; w2g.b_major = MN_MAJOR; w2g.ragged = RAGGED_K; w2g.epi = EPI_STORE;
-    w2g.a_type = w2g.b_type = w2g.c_type = et;
+    w2g.a_type = w2g.b_type = et;
+    w2g.c_type = MOE_F32;
     w2g.M = c.d; w2g.N = F;
     w2g.A = dY; w2g.lda = c.d; w2g.B = act; w2g.ldb = F;
     w2g.C = dw2; w2g.ldc = F; w2g.c_gstride = int64_t{1} * c.d * F;
@@ -246,7 +251,8 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
     // (3) fc1 data gradient: dX = dH W13
     GemmDesc d1{};
     d1.a_major = K_MAJOR; d1.b_major = MN_MAJOR; d1.ragged = RAGGED_M; d1.epi = EPI_STORE;
-    d1.a_type = d1.b_type = d1.c_type = et;
+    d1.a_type = d1.b_type = et;
+    d1.c_type = MOE_F32;  // per-row input gradients in fp32 for the unpermute-reduce
     d1.N = c.d; d1.K = 2 * F;
     d1.A = dh; d1.lda = 2 * F;
     d1.B = w13; d1.ldb = c.d; d1.b_gstride = shared ? 0 : int64_t{2} * F * c.d;
@@ -255,7 +261,8 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
     // (4) fc1 weight gradient: dW13 = dH^T X
     GemmDesc w1g{};
     w1g.a_major = MN_MAJOR; w1g.b_major = MN_MAJOR; w1g.ragged = RAGGED_K; w1g.epi = EPI_STORE;
-    w1g.a_type = w1g.b_type = w1g.c_type = et;
+    w1g.a_type = w1g.b_type = et;
+    w1g.c_type = MOE_F32;
     w1g.M = 2 * F; w1g.N = c.d;
     w1g.A = dh; w1g.lda = 2 * F; w1g.B = X; w1g.ldb = c.d;
     w1g.C = dw13; w1g.ldc = c.d; w1g.c_gstride = int64_t{2} * F * c.d;
@@ -383,16 +390,17 @@ moe_status_t moe_grouped_gemm_swiglu(const moe_config_t* cfg, const void* x_perm
                          S(stream));
 }
 
-moe_status_t moe_unpermute_combine(const moe_config_t* cfg, const void* Y_perm, const int32_t* row_of,
-                                   const float* w, const void* Y_s, void* y, void* stream) {
+moe_status_t moe_unpermute_combine(const moe_config_t* cfg, const float* Y_perm, const int32_t* row_of,
+                                   const float* w, const float* Y_s, float* y, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED16(Y_perm); MOE_NEED(row_of); MOE_NEED(w); MOE_NEED16(y);
   if (Y_s && !aligned16(Y_s)) return fail(MOE_ERR_INVALID_ARG, "Y_s is not 16-byte aligned");
-  return launch_gather_sum(*cfg, Y_perm, row_of, w, Y_s, nullptr, y, S(stream));
+  return launch_combine(*cfg, static_cast<const float*>(Y_perm), row_of, w, static_cast<const float*>(Y_s),
+                        static_cast<float*>(y), S(stream));
 }
 
 moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, const void* x, const moe_saved_t* sv,
-                           void* y, float* stats, void* ws, size_t ws_bytes, void* stream) {
+                           float* y, float* stats, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED(W); MOE_NEED(sv); MOE_NEED16(x); MOE_NEED16(y); MOE_NEED(ws);
   MOE_NEED(W->Wg); MOE_NEED16(W->W13); MOE_NEED16(W->W2);
@@ -415,43 +423,45 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, cons
                          fw.counts, true, s));
   MOE_TRY(run_experts_fwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, x, W->W13s, W->W2s, sv->H, sv->Act,
                           sv->Y_perm, sv->H_s, sv->Act_s, sv->Y_s, fw.sched, s));
-  return launch_gather_sum(c, sv->Y_perm, sv->row_of, sv->w, c.Fs ? sv->Y_s : nullptr, nullptr, y, s);
+  return launch_combine(c, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w,
+                        c.Fs ? static_cast<const float*>(sv->Y_s) : nullptr, static_cast<float*>(y), s);
 }
 
-moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const void* dy, const void* Y_perm,
+moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const float* dy, const float* Y_perm,
                                        const int32_t* row_of, const float* w, void* dY_perm, float* dw,
-                                       void* stream) {
+                                       void* dY_s, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED16(dy); MOE_NEED16(Y_perm); MOE_NEED(row_of); MOE_NEED(w); MOE_NEED16(dY_perm); MOE_NEED(dw);
-  return launch_combine_bwd(*cfg, dy, Y_perm, row_of, w, dY_perm, dw, S(stream));
+  if (dY_s && !aligned16(dY_s)) return fail(MOE_ERR_INVALID_ARG, "dY_s is not 16-byte aligned");
+  return launch_combine_bwd(*cfg, dy, Y_perm, row_of, w, dY_perm, dw, dY_s, S(stream));
 }
 
 moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
                                          const void* W13, const void* W2, const void* H, const void* Act,
                                          const void* dY_perm, void* dH, void* dX_perm, void* dW13, void* dW2,
                                          const void* x, const void* W13s, const void* W2s, const void* H_s,
-                                         const void* Act_s, const void* dy, void* dH_s, void* dx_s, void* dW13s,
+                                         const void* Act_s, const void* dY_s, void* dH_s, void* dx_s, void* dW13s,
                                          void* dW2s, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED16(x_perm); MOE_NEED(offsets); MOE_NEED16(W13); MOE_NEED16(W2); MOE_NEED16(H); MOE_NEED16(Act);
   MOE_NEED16(dY_perm); MOE_NEED16(dH); MOE_NEED16(dX_perm); MOE_NEED16(dW13); MOE_NEED16(dW2); MOE_NEED(ws);
   if (cfg->Fs) {
-    MOE_NEED16(x); MOE_NEED16(W13s); MOE_NEED16(W2s); MOE_NEED16(H_s); MOE_NEED16(Act_s); MOE_NEED16(dy);
+    MOE_NEED16(x); MOE_NEED16(W13s); MOE_NEED16(W2s); MOE_NEED16(H_s); MOE_NEED16(Act_s); MOE_NEED16(dY_s);
     MOE_NEED16(dH_s); MOE_NEED16(dx_s); MOE_NEED16(dW13s); MOE_NEED16(dW2s);
   }
   const BwdWs bw = carve_bwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, bw.bytes, __func__));
   return run_experts_bwd(*cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, dX_perm, dW13, dW2, x, W13s, W2s, H_s,
-                         Act_s, dy, dH_s, dx_s, dW13s, dW2s, bw.sched, bw.dact, S(stream));
+                         Act_s, dY_s, dH_s, dx_s, dW13s, dW2s, bw.sched, bw.dact, S(stream));
 }
 
-moe_status_t moe_permute_bwd(const moe_config_t* cfg, const void* dX_perm, const int32_t* row_of, const void* dx_s,
-                             const float* dx_r, void* dx, void* stream) {
+moe_status_t moe_permute_bwd(const moe_config_t* cfg, const float* dX_perm, const int32_t* row_of, const float* dx_s,
+                             const float* dx_r, float* dx, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED16(dX_perm); MOE_NEED(row_of); MOE_NEED16(dx);
   if (dx_s && !aligned16(dx_s)) return fail(MOE_ERR_INVALID_ARG, "dx_s is not 16-byte aligned");
   if (dx_r && !aligned16(dx_r)) return fail(MOE_ERR_INVALID_ARG, "dx_r is not 16-byte aligned");
-  return launch_gather_sum(*cfg, dX_perm, row_of, nullptr, dx_s, dx_r, dx, S(stream));
+  return launch_unpermute_reduce(*cfg, dX_perm, row_of, dx_s, dx_r, dx, S(stream));
 }
 
 moe_status_t moe_router_bwd(const moe_config_t* cfg, const float* logits, const int32_t* idx, const float* w,
@@ -470,7 +480,7 @@ moe_status_t moe_gate_logits_bwd(const moe_config_t* cfg, const void* x, const f
 }
 
 moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, const moe_saved_t* sv, const void* x,
-                           const void* dy, float daux, void* dx, const moe_grads_t* gr, void* ws, size_t ws_bytes,
+                           const float* dy, float daux, float* dx, const moe_grads_t* gr, void* ws, size_t ws_bytes,
                            void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED(W); MOE_NEED(sv); MOE_NEED(gr); MOE_NEED16(x); MOE_NEED16(dy); MOE_NEED16(dx); MOE_NEED(ws);
@@ -486,13 +496,17 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_TRY(need_ws(ws_bytes, bw.bytes, __func__));
   const moe_config_t& c = *cfg;
   hipStream_t s = S(stream);
-  MOE_TRY(launch_combine_bwd(c, dy, sv->Y_perm, sv->row_of, sv->w, bw.dYX, bw.dw, s));
+  // the shared expert's upstream gradient is dy itself, in the activation dtype
+  void* dY_s = c.Fs ? (c.act_dtype == MOE_F32 ? const_cast<float*>(dy) : bw.dY_s) : nullptr;
+  MOE_TRY(launch_combine_bwd(c, dy, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, bw.dYX, bw.dw,
+                             c.act_dtype == MOE_F32 ? nullptr : dY_s, s));
   MOE_TRY(run_experts_bwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, sv->H, sv->Act, bw.dYX, bw.dH, bw.dYX,
-                          gr->dW13, gr->dW2, x, W->W13s, W->W2s, sv->H_s, sv->Act_s, dy, bw.dH_s, bw.dx_s, gr->dW13s,
+                          gr->dW13, gr->dW2, x, W->W13s, W->W2s, sv->H_s, sv->Act_s, dY_s, bw.dH_s, bw.dx_s, gr->dW13s,
                           gr->dW2s, bw.sched, bw.dact, s));
   MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, daux, bw.dlogits, s));
   MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, s));
-  return launch_gather_sum(c, bw.dYX, sv->row_of, nullptr, c.Fs ? bw.dx_s : nullptr, bw.dx_r, dx, s);
+  return launch_unpermute_reduce(c, static_cast<const float*>(bw.dYX), sv->row_of,
+                                 c.Fs ? static_cast<const float*>(bw.dx_s) : nullptr, bw.dx_r, dx, s);
 }
 
 }  // extern "C"

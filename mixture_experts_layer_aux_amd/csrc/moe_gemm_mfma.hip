@@ -24,9 +24,9 @@
 //     workgroups are dealt round-robin to the 8 XCDs, so each XCD walks a contiguous
 //     run of tiles (expert, column tile, row tile) and the tiles sharing a weight tile
 //     or an activation tile run together on one L2;
-//   * fused epilogues: SwiGLU (forward: H and Act from the same accumulators, the gate
-//     and up rows of W13 interleaved per 32-row block of the B tile) and the SwiGLU
-//     backward (reads the saved H, writes dH).
+//   * fused epilogues: SwiGLU (forward: H in fp32 and Act in bf16 from the same
+//     accumulators, the gate and up rows of W13 interleaved per 32-row block of the B
+//     tile) and the SwiGLU backward (reads the saved fp32 H, writes dH in bf16).
 #include "moe_internal.h"
 
 namespace moe {
@@ -45,11 +45,11 @@ struct MfmaArgs {
   int64_t lda;
   const uint16_t* B;
   int64_t ldb, b_gstride;
-  uint16_t* C;
+  void* C;
   int64_t ldc, c_gstride;
   uint16_t* C2;
   int64_t ldc2;
-  const uint16_t* H;
+  const float* H;
   int64_t ldh;
   const int32_t* offsets;
   const int32_t* tile_prefix;
@@ -58,8 +58,6 @@ struct MfmaArgs {
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int r, int kc) { return r * 64 + ((kc ^ swz(r)) << 3); }
-
-__device__ __forceinline__ float bf(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
 
 // 8 x 8 transpose of bf16: in[kk] holds columns 0..7 of row kk; out[cc] holds rows 0..7
 // of column cc.
@@ -93,7 +91,7 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
   for (int g = threadIdx.x; g <= G; g += 1024) prefix[g] = g == 0 ? 0 : s[g - 1];
 }
 
-template <int AMAJ, int BMAJ, int RAG, int EPI>
+template <int AMAJ, int BMAJ, int RAG, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * TILE];
   const int tid = threadIdx.x;
@@ -266,7 +264,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
   // ------------------------------------------------------------ epilogue
   // acc[i][j][e] is row wm*128 + i*32 + 8*(e/4) + 4*(lane/32) + e%4, column
   // wn*128 + j*32 + lane%32 of the tile.
-  uint16_t* C = p.C + (RAG == RAGGED_K ? static_cast<int64_t>(grp) * p.c_gstride : 0);
+  const int64_t cg = RAG == RAGGED_K ? static_cast<int64_t>(grp) * p.c_gstride : 0;
+  uint16_t* C = static_cast<uint16_t*>(p.C) + cg;
+  float* Cf = static_cast<float*>(p.C) + cg;
   const int rbase = row_begin + wm * 128 + 4 * (lane >> 5);
   if (EPI == EPI_SWIGLU_FWD) {
 #pragma unroll
@@ -279,8 +279,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
           const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
           if (row < row_end) {
             const float gt = acc[i][2 * q][e], up = acc[i][2 * q + 1][e];
-            C[static_cast<int64_t>(row) * p.ldc + col] = f32_to_bf16(gt);
-            C[static_cast<int64_t>(row) * p.ldc + p.F + col] = f32_to_bf16(up);
+            Cf[static_cast<int64_t>(row) * p.ldc + col] = gt;
+            Cf[static_cast<int64_t>(row) * p.ldc + p.F + col] = up;
             p.C2[static_cast<int64_t>(row) * p.ldc2 + col] = f32_to_bf16(silu_f(gt) * up);
           }
         }
@@ -299,10 +299,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
           const float v = acc[i][j][e];
           if (EPI == EPI_SWIGLU_BWD) {
             const int64_t hr = static_cast<int64_t>(row) * p.ldh;
-            const float gt = bf(p.H[hr + col]), up = bf(p.H[hr + p.F + col]);
+            const float gt = p.H[hr + col], up = p.H[hr + p.F + col];
             const float sg = sigmoid_f(gt);
             C[static_cast<int64_t>(row) * p.ldc + col] = f32_to_bf16(v * up * sg * (1.0f + gt * (1.0f - sg)));
             C[static_cast<int64_t>(row) * p.ldc + p.F + col] = f32_to_bf16(v * gt * sg);
+          } else if (OUT_F32) {
+            Cf[static_cast<int64_t>(row) * p.ldc + col] = v;
           } else {
             C[static_cast<int64_t>(row) * p.ldc + col] = f32_to_bf16(v);
           }
@@ -311,9 +313,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
   }
 }
 
-template <int AMAJ, int BMAJ, int RAG, int EPI>
+template <int AMAJ, int BMAJ, int RAG, int EPI, bool OUT_F32>
 void launch_kernel(const MfmaArgs& a, int64_t grid, hipStream_t s) {
-  gemm_mfma_kernel<AMAJ, BMAJ, RAG, EPI><<<static_cast<unsigned>(grid), NTHR, 0, s>>>(a);
+  gemm_mfma_kernel<AMAJ, BMAJ, RAG, EPI, OUT_F32><<<static_cast<unsigned>(grid), NTHR, 0, s>>>(a);
 }
 
 }  // namespace
@@ -321,20 +323,22 @@ void launch_kernel(const MfmaArgs& a, int64_t grid, hipStream_t s) {
 size_t mfma_schedule_bytes(int G) { return static_cast<size_t>(G + 1) * sizeof(int32_t); }
 
 moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) {
-  if (g.a_type != MOE_BF16 || g.b_type != MOE_BF16 || g.c_type != MOE_BF16)
+  if (g.a_type != MOE_BF16 || g.b_type != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: bf16 operands only");
+  const bool out_f32 = g.c_type == MOE_F32;
+
   MfmaArgs a{};
   a.A = static_cast<const uint16_t*>(g.A);
   a.lda = g.lda;
   a.B = static_cast<const uint16_t*>(g.B);
   a.ldb = g.ldb;
   a.b_gstride = g.b_gstride;
-  a.C = static_cast<uint16_t*>(g.C);
+  a.C = g.C;
   a.ldc = g.ldc;
   a.c_gstride = g.c_gstride;
   a.C2 = static_cast<uint16_t*>(g.C2);
   a.ldc2 = g.ldc2;
-  a.H = static_cast<const uint16_t*>(g.Hin);
+  a.H = static_cast<const float*>(g.Hin);
   a.ldh = g.ldh;
   a.offsets = g.offsets;
   a.tile_prefix = sched;
@@ -361,16 +365,16 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
     grid = static_cast<int64_t>(g.offsets ? g.G : 1) * a.nM * a.nN;
   }
   if (grid == 0) return MOE_OK;
-#define MOE_MF(AM, BMJ, RG, EP)                                       \
-  if (g.a_major == AM && g.b_major == BMJ && g.ragged == RG && g.epi == EP) { \
-    launch_kernel<AM, BMJ, RG, EP>(a, grid, s);                       \
-    return check_launch("gemm_mfma");                                 \
+#define MOE_MF(AM, BMJ, RG, EP, OF)                                                              \
+  if (g.a_major == AM && g.b_major == BMJ && g.ragged == RG && g.epi == EP && out_f32 == OF) { \
+    launch_kernel<AM, BMJ, RG, EP, OF>(a, grid, s);                                              \
+    return check_launch("gemm_mfma");                                                            \
   }
-  MOE_MF(K_MAJOR, K_MAJOR, RAGGED_M, EPI_SWIGLU_FWD)   // fc1 + SwiGLU
-  MOE_MF(K_MAJOR, K_MAJOR, RAGGED_M, EPI_STORE)        // fc2
-  MOE_MF(K_MAJOR, MN_MAJOR, RAGGED_M, EPI_SWIGLU_BWD)  // fc2 data gradient + SwiGLU backward
-  MOE_MF(K_MAJOR, MN_MAJOR, RAGGED_M, EPI_STORE)       // fc1 data gradient
-  MOE_MF(MN_MAJOR, MN_MAJOR, RAGGED_K, EPI_STORE)      // weight gradients
+  MOE_MF(K_MAJOR, K_MAJOR, RAGGED_M, EPI_SWIGLU_FWD, true)    // fc1 + SwiGLU -> H (fp32), Act (bf16)
+  MOE_MF(K_MAJOR, K_MAJOR, RAGGED_M, EPI_STORE, true)         // fc2 -> Y (fp32)
+  MOE_MF(K_MAJOR, MN_MAJOR, RAGGED_M, EPI_SWIGLU_BWD, false)  // fc2 data gradient + SwiGLU backward -> dH (bf16)
+  MOE_MF(K_MAJOR, MN_MAJOR, RAGGED_M, EPI_STORE, true)        // fc1 data gradient -> dX (fp32)
+  MOE_MF(MN_MAJOR, MN_MAJOR, RAGGED_K, EPI_STORE, true)       // weight gradients (fp32)
 #undef MOE_MF
   return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: unsupported operand combination");
 }

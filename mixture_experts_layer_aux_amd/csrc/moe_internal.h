@@ -22,10 +22,14 @@ int64_t permute_num_chunks(int T);
 moe_status_t launch_permute(const moe_config_t& c, const void* x, const int32_t* idx, int32_t* offsets,
                             int32_t* row_of, int32_t* token_of, void* x_perm, int32_t* blk_hist,
                             int32_t* blk_base, int32_t* counts_ws, bool hist_ready, hipStream_t s);
-moe_status_t launch_gather_sum(const moe_config_t& c, const void* Y, const int32_t* row_of, const float* w,
-                               const void* add_act, const float* add_f32, void* out, hipStream_t s);
-moe_status_t launch_combine_bwd(const moe_config_t& c, const void* dy, const void* Y, const int32_t* row_of,
-                                const float* w, void* dY, float* dw, hipStream_t s);
+// y = sum_j w Y_perm[row] + Y_s  (all fp32)
+moe_status_t launch_combine(const moe_config_t& c, const float* Y, const int32_t* row_of, const float* w,
+                            const float* Y_s, float* y, hipStream_t s);
+// dx = sum_j dX_perm[row] + dx_s + dx_r  (all fp32)
+moe_status_t launch_unpermute_reduce(const moe_config_t& c, const float* dX, const int32_t* row_of,
+                                     const float* dx_s, const float* dx_r, float* dx, hipStream_t s);
+moe_status_t launch_combine_bwd(const moe_config_t& c, const float* dy, const float* Y, const int32_t* row_of,
+                                const float* w, void* dY, float* dw, void* dY_s, hipStream_t s);
 
 // ---------------------------------------------------------------- GEMMs
 // Storage of an operand: K_MAJOR = [rows][K] (K contiguous), MN_MAJOR = [K][rows].
@@ -48,7 +52,7 @@ struct GemmDesc {
   int64_t ldc, c_gstride;
   void* C2;                     // EPI_SWIGLU_FWD: Act out [rows][F]
   int64_t ldc2;
-  const void* Hin;              // EPI_SWIGLU_BWD: saved H [rows][2F]
+  const void* Hin;              // EPI_SWIGLU_BWD: saved H [rows][2F], fp32
   int64_t ldh;
   const float* bias;            // EPI_STORE_BIAS: [N]
   int F;                        // SwiGLU: offset of the up half (columns of H / rows of W13)

@@ -122,11 +122,11 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
   }
 }
 
-// 16-byte unit <-> fp32 lanes for the two storage types.
-template <typename T> struct Unit;
-template <> struct Unit<uint16_t> {
-  static constexpr int N = 8;
-  __device__ __forceinline__ static void to_f32(const uint4& v, float* f) {
+// Groups of 8 consecutive elements <-> fp32, for the two storage types.
+template <typename T> struct G8;
+template <> struct G8<uint16_t> {
+  __device__ __forceinline__ static void load(const void* base, int64_t g, float* f) {
+    const uint4 v = static_cast<const uint4*>(base)[g];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -134,101 +134,105 @@ template <> struct Unit<uint16_t> {
       f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   }
-  __device__ __forceinline__ static uint4 from_f32(const float* f) {
-    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                      pack_bf16x2(f[6], f[7]));
+  __device__ __forceinline__ static void store(void* base, int64_t g, const float* f) {
+    static_cast<uint4*>(base)[g] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                              pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
   }
 };
-template <> struct Unit<float> {
-  static constexpr int N = 4;
-  __device__ __forceinline__ static void to_f32(const uint4& v, float* f) {
-    f[0] = __uint_as_float(v.x);
-    f[1] = __uint_as_float(v.y);
-    f[2] = __uint_as_float(v.z);
-    f[3] = __uint_as_float(v.w);
+template <> struct G8<float> {
+  __device__ __forceinline__ static void load(const void* base, int64_t g, float* f) {
+    const float4* p = static_cast<const float4*>(base) + 2 * g;
+    const float4 a = p[0], b = p[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
   }
-  __device__ __forceinline__ static uint4 from_f32(const float* f) {
-    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+  __device__ __forceinline__ static void store(void* base, int64_t g, const float* f) {
+    float4* p = static_cast<float4*>(base) + 2 * g;
+    p[0] = make_float4(f[0], f[1], f[2], f[3]);
+    p[1] = make_float4(f[4], f[5], f[6], f[7]);
   }
 };
 
-// y[t] = sum_j w[t,j] * Y[row_of[t,j]] (+ add_act[t]) (+ add_f32[t]); w NULL means 1.
-// Also the unpermute-reduce of the backward (w NULL, two addends).
-template <typename T>
-__global__ __launch_bounds__(256) void gather_sum_kernel(const uint4* __restrict__ Y, int Tn, int units, int k,
+// out[t] = sum_j w[t,j] * Y[row_of[t,j]] (+ add1[t]) (+ add2[t]), fp32 accumulation in
+// slot order then addend order; w NULL means 1.  The combine (Y fp32 expert outputs,
+// add1 the shared expert's output) and the unpermute-reduce of the backward (Y the
+// per-row input gradients, add1 the shared expert's, add2 the router's) share it.
+template <typename TY, typename TA1, typename TO>
+__global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict__ Y, int Tn, int groups, int k,
                                                          const int32_t* __restrict__ row_of,
                                                          const float* __restrict__ w,
-                                                         const uint4* __restrict__ add_act,
-                                                         const float4* __restrict__ add_f32,
-                                                         uint4* __restrict__ out) {
-  constexpr int N = Unit<T>::N;
+                                                         const void* __restrict__ add1,
+                                                         const float* __restrict__ add2, void* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
   const int my_r = lane < k ? row_of[static_cast<int64_t>(t) * k + lane] : 0;
   const float my_w = (lane < k && w) ? w[static_cast<int64_t>(t) * k + lane] : 1.0f;
-  for (int u = lane; u < units; u += 64) {
-    float acc[N];
+  for (int u = lane; u < groups; u += 64) {
+    float acc[8];
 #pragma unroll
-    for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
     for (int j = 0; j < k; ++j) {
       const int r = __shfl(my_r, j, 64);
       const float wj = __shfl(my_w, j, 64);
-      float f[N];
-      Unit<T>::to_f32(Y[static_cast<int64_t>(r) * units + u], f);
+      float f[8];
+      G8<TY>::load(Y, static_cast<int64_t>(r) * groups + u, f);
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] += wj * f[i];
+      for (int i = 0; i < 8; ++i) acc[i] += wj * f[i];
     }
-    if (add_act) {
-      float f[N];
-      Unit<T>::to_f32(add_act[static_cast<int64_t>(t) * units + u], f);
+    const int64_t gi = static_cast<int64_t>(t) * groups + u;
+    if (add1) {
+      float f[8];
+      G8<TA1>::load(add1, gi, f);
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] += f[i];
+      for (int i = 0; i < 8; ++i) acc[i] += f[i];
     }
-    if (add_f32) {
-      const float4* p = add_f32 + (static_cast<int64_t>(t) * units + u) * (N / 4);
+    if (add2) {
+      float f[8];
+      G8<float>::load(add2, gi, f);
 #pragma unroll
-      for (int q = 0; q < N / 4; ++q) {
-        const float4 v = p[q];
-        acc[4 * q] += v.x;
-        acc[4 * q + 1] += v.y;
-        acc[4 * q + 2] += v.z;
-        acc[4 * q + 3] += v.w;
-      }
+      for (int i = 0; i < 8; ++i) acc[i] += f[i];
     }
-    out[static_cast<int64_t>(t) * units + u] = Unit<T>::from_f32(acc);
+    G8<TO>::store(out, gi, acc);
   }
 }
 
-// dY_perm[row_of[t,j]] = w[t,j] * dy[t];  dw[t,j] = <dy[t], Y_perm[row_of[t,j]]>.
-template <typename T>
-__global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dy,
-                                                          const uint4* __restrict__ Y, int Tn, int units,
+// dY_perm[row_of[t,j]] = w[t,j] * dy[t]  (activation dtype);
+// dw[t,j] = <dy[t], Y_perm[row_of[t,j]]>  (fp32, fixed butterfly order);
+// dY_s[t] = dy[t] in the activation dtype, the shared expert's upstream gradient (optional).
+template <typename TACT>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restrict__ dy,
+                                                          const float* __restrict__ Y, int Tn, int groups,
                                                           int k, const int32_t* __restrict__ row_of,
-                                                          const float* __restrict__ w,
-                                                          uint4* __restrict__ dY, float* __restrict__ dw) {
-  constexpr int N = Unit<T>::N;
+                                                          const float* __restrict__ w, void* __restrict__ dY,
+                                                          float* __restrict__ dw, void* __restrict__ dY_s) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
   const int my_r = lane < k ? row_of[static_cast<int64_t>(t) * k + lane] : 0;
   const float my_w = lane < k ? w[static_cast<int64_t>(t) * k + lane] : 0.0f;
-  const uint4* dyt = dy + static_cast<int64_t>(t) * units;
+  const int64_t t0 = static_cast<int64_t>(t) * groups;
+  if (dY_s)
+    for (int u = lane; u < groups; u += 64) {
+      float g[8];
+      G8<float>::load(dy, t0 + u, g);
+      G8<TACT>::store(dY_s, t0 + u, g);
+    }
   float my_dw = 0.0f;
   for (int j = 0; j < k; ++j) {
     const int r = __shfl(my_r, j, 64);
     const float wj = __shfl(my_w, j, 64);
     float part = 0.0f;
-    for (int u = lane; u < units; u += 64) {
-      float g[N], y[N];
-      Unit<T>::to_f32(dyt[u], g);
-      Unit<T>::to_f32(Y[static_cast<int64_t>(r) * units + u], y);
+    for (int u = lane; u < groups; u += 64) {
+      float g[8], y[8];
+      G8<float>::load(dy, t0 + u, g);
+      G8<float>::load(Y, static_cast<int64_t>(r) * groups + u, y);
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
+      for (int i = 0; i < 8; ++i) {
         part += g[i] * y[i];
         g[i] *= wj;
       }
-      dY[static_cast<int64_t>(r) * units + u] = Unit<T>::from_f32(g);
+      G8<TACT>::store(dY, static_cast<int64_t>(r) * groups + u, g);
     }
     part = wave_sum(part);
     if (lane == j) my_dw = part;
@@ -256,33 +260,31 @@ moe_status_t launch_permute(const moe_config_t& c, const void* x, const int32_t*
   return check_launch("permute");
 }
 
-moe_status_t launch_gather_sum(const moe_config_t& c, const void* Y, const int32_t* row_of, const float* w,
-                               const void* add_act, const float* add_f32, void* out, hipStream_t s) {
-  const int units = static_cast<int>(static_cast<int64_t>(c.d) * act_bytes(c) / 16);
-  const int grid = static_cast<int>(ceil_div(c.T, 4));
-  if (c.act_dtype == MOE_BF16)
-    gather_sum_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint4*>(Y), c.T, units, c.k, row_of, w,
-                                                     static_cast<const uint4*>(add_act),
-                                                     reinterpret_cast<const float4*>(add_f32),
-                                                     static_cast<uint4*>(out));
-  else
-    gather_sum_kernel<float><<<grid, 256, 0, s>>>(static_cast<const uint4*>(Y), c.T, units, c.k, row_of, w,
-                                                  static_cast<const uint4*>(add_act),
-                                                  reinterpret_cast<const float4*>(add_f32),
-                                                  static_cast<uint4*>(out));
-  return check_launch("gather_sum");
+moe_status_t launch_combine(const moe_config_t& c, const float* Y, const int32_t* row_of, const float* w,
+                            const float* Y_s, float* y, hipStream_t s) {
+  const int groups = c.d / 8;
+  gather_sum_kernel<float, float, float><<<static_cast<int>(ceil_div(c.T, 4)), 256, 0, s>>>(
+      Y, c.T, groups, c.k, row_of, w, Y_s, nullptr, y);
+  return check_launch("combine");
 }
 
-moe_status_t launch_combine_bwd(const moe_config_t& c, const void* dy, const void* Y, const int32_t* row_of,
-                                const float* w, void* dY, float* dw, hipStream_t s) {
-  const int units = static_cast<int>(static_cast<int64_t>(c.d) * act_bytes(c) / 16);
+moe_status_t launch_unpermute_reduce(const moe_config_t& c, const float* dX, const int32_t* row_of,
+                                     const float* dx_s, const float* dx_r, float* dx, hipStream_t s) {
+  const int groups = c.d / 8;
+  const int grid = static_cast<int>(ceil_div(c.T, 4));
+  gather_sum_kernel<float, float, float><<<grid, 256, 0, s>>>(dX, c.T, groups, c.k, row_of, nullptr, dx_s, dx_r,
+                                                              dx);
+  return check_launch("unpermute_reduce");
+}
+
+moe_status_t launch_combine_bwd(const moe_config_t& c, const float* dy, const float* Y, const int32_t* row_of,
+                                const float* w, void* dY, float* dw, void* dY_s, hipStream_t s) {
+  const int groups = c.d / 8;
   const int grid = static_cast<int>(ceil_div(c.T, 4));
   if (c.act_dtype == MOE_BF16)
-    combine_bwd_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint4*>(dy), static_cast<const uint4*>(Y),
-                                                      c.T, units, c.k, row_of, w, static_cast<uint4*>(dY), dw);
+    combine_bwd_kernel<uint16_t><<<grid, 256, 0, s>>>(dy, Y, c.T, groups, c.k, row_of, w, dY, dw, dY_s);
   else
-    combine_bwd_kernel<float><<<grid, 256, 0, s>>>(static_cast<const uint4*>(dy), static_cast<const uint4*>(Y),
-                                                   c.T, units, c.k, row_of, w, static_cast<uint4*>(dY), dw);
+    combine_bwd_kernel<float><<<grid, 256, 0, s>>>(dy, Y, c.T, groups, c.k, row_of, w, dY, dw, dY_s);
   return check_launch("combine_bwd");
 }
 

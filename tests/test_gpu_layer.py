@@ -10,7 +10,8 @@ is compared when no token moved.
 import numpy as np
 import pytest
 
-from helpers import MARGIN, O, W, dev, oracle_inputs, rel_err, spec_of, to_dev, to_np, tol, torch_mod
+from helpers import (MARGIN, O, W, check_expert_grads, check_grad, dev, oracle_inputs, rel_err, spec_of, to_dev,
+                     to_np, tol, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,12 +23,13 @@ def _run_layer(shape, inp):
     d = dev()
     Wt = dict(Wg=to_dev(inp["Wg"]), bg=to_dev(inp["bg"]), expert_bias=to_dev(inp["expert_bias"]),
               W13=to_dev(inp["W13"]), W2=to_dev(inp["W2"]), W13s=to_dev(inp["W13s"]), W2s=to_dev(inp["W2s"]))
-    x, dy = to_dev(inp["x"]), to_dev(inp["dy"])
+    x = to_dev(inp["x"])
+    dy = to_dev(W.to_f32(inp["dy"], shape.act).copy())     # upstream gradient, fp32
     S = L.alloc_saved(cfg, d)
     G = L.alloc_grads(cfg, d, with_dbg=inp["bg"] is not None)
     ws = L.alloc_workspace(cfg, d)
-    y = torch.empty_like(x)
-    dx = torch.empty_like(x)
+    y = torch.empty(shape.T, shape.d, dtype=torch.float32, device=d)
+    dx = torch.empty(shape.T, shape.d, dtype=torch.float32, device=d)
     stats = torch.empty(L.MOE_NSTATS, dtype=torch.float32, device=d)
     L.layer_fwd(cfg, Wt, x, S, y, stats, ws)
     L.layer_bwd(cfg, Wt, S, x, dy, 1.0, dx, G, ws)
@@ -60,20 +62,20 @@ def _check_layer(shape, seed):
     if not moved.any():
         assert np.array_equal(to_np(got["S_counts"]), r["counts"])
         assert st[1] == pytest.approx(r["maxvio"], rel=1e-6)
-        assert rel_err(to_np(got["dWg"]), b["dWg"]) < tl, "dWg"
+        check_grad("dWg", to_np(got["dWg"]), b["dWg"], shape)
         if "dbg" in got:
-            assert rel_err(to_np(got["dbg"]), b["dbg"]) < tl, "dbg"
+            check_grad("dbg", to_np(got["dbg"]), b["dbg"], shape)
     same = np.ones(shape.E, dtype=bool)
     for t in np.where(moved)[0]:
         same[idx_gpu[t]] = False
         same[r["idx"][t]] = False
     assert same.sum() >= shape.E - 2 * shape.k * moved.sum()
-    dW13, dW2 = to_np(got["dW13"]), to_np(got["dW2"])
-    assert rel_err(dW13[same], b["dW13"][same]) < tl, "dW13"
-    assert rel_err(dW2[same], b["dW2"][same]) < tl, "dW2"
+    ids = np.where(same)[0]
+    check_expert_grads("dW13", to_np(got["dW13"]), b["dW13"], r["counts"], shape, ids)
+    check_expert_grads("dW2", to_np(got["dW2"]), b["dW2"], r["counts"], shape, ids)
     if shape.Fs:
-        assert rel_err(to_np(got["dW13s"]), b["dW13s"]) < tl, "dW13s"
-        assert rel_err(to_np(got["dW2s"]), b["dW2s"]) < tl, "dW2s"
+        check_grad("dW13s", to_np(got["dW13s"]), b["dW13s"], shape)
+        check_grad("dW2s", to_np(got["dW2s"]), b["dW2s"], shape)
     return got
 
 

@@ -8,7 +8,8 @@ the same bytes.
 import numpy as np
 import pytest
 
-from helpers import MARGIN, O, W, dev, f64, oracle_inputs, rel_err, spec_of, to_dev, to_np, tol, torch_mod
+from helpers import (O, W, check_expert_grads, check_grad, dev, f64, oracle_inputs, rel_err, spec_of, storage_ok,
+                     to_dev, to_np, tol, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -131,18 +132,19 @@ def test_grouped_experts_forward_and_backward(cid):
     W13, W2 = to_dev(inp["W13"]), to_dev(inp["W2"])
     W13s, W2s = to_dev(inp["W13s"]), to_dev(inp["W2s"])
     e = lambda *s: torch.empty(*s, dtype=ad, device=dev())  # noqa: E731
-    H, Act, Yp = e(A, 2 * F), e(A, F), e(A, d)
-    H_s, Act_s, Y_s = (e(T, 2 * Fs), e(T, Fs), e(T, d)) if Fs else (None, None, None)
+    e32 = lambda *s: torch.empty(*s, dtype=torch.float32, device=dev())  # noqa: E731
+    H, Act, Yp = e32(A, 2 * F), e(A, F), e32(A, d)
+    H_s, Act_s, Y_s = (e32(T, 2 * Fs), e(T, Fs), e32(T, d)) if Fs else (None, None, None)
     ws = L.alloc_workspace(cfg, dev())
     L.grouped_gemm_swiglu(cfg, x_perm, off, W13, W2, x if Fs else None, W13s, W2s, H, Act, Yp, H_s, Act_s, Y_s, ws)
     # backward with a generator upstream gradient on the permuted rows
     dYp_np = W.random_rows(A, d, seed=100 + cid, act=shape.act)
     dYp = to_dev(dYp_np)
-    dH, dXp = e(A, 2 * F), e(A, d)
-    dW13, dW2 = e(E, 2 * F, d), e(E, d, F)
-    dy = to_dev(inp["dy"])
-    dH_s, dx_s = (e(T, 2 * Fs), e(T, d)) if Fs else (None, None)
-    dW13s, dW2s = (e(2 * Fs, d), e(d, Fs)) if Fs else (None, None)
+    dH, dXp = e(A, 2 * F), e32(A, d)
+    dW13, dW2 = e32(E, 2 * F, d), e32(E, d, F)
+    dy = to_dev(inp["dy"])                       # the shared expert's upstream gradient, act dtype
+    dH_s, dx_s = (e(T, 2 * Fs), e32(T, d)) if Fs else (None, None)
+    dW13s, dW2s = (e32(2 * Fs, d), e32(d, Fs)) if Fs else (None, None)
     L.grouped_gemm_swiglu_bwd(cfg, x_perm, off, W13, W2, H, Act, dYp, dH, dXp, dW13, dW2, x if Fs else None, W13s,
                               W2s, H_s, Act_s, dy if Fs else None, dH_s, dx_s, dW13s, dW2s, ws)
     torch.cuda.synchronize()
@@ -157,23 +159,31 @@ def test_grouped_experts_forward_and_backward(cid):
             continue
         h, act, y = O.swiglu_forward(xp[a:b], o["W13"][ex], o["W2"][ex])
         ref["H"][a:b], ref["Act"][a:b], ref["Y"][a:b] = h, act, y
-        # the backward is evaluated at the GPU's stored forward activations' exact values? no:
-        # at the oracle's own (unrounded) H, which is the definition
         g = O.swiglu_backward(xp[a:b], o["W13"][ex], o["W2"][ex], h, dYo[a:b])
         ref["dH"][a:b], ref["dX"][a:b], ref["dW13"][ex], ref["dW2"][ex] = g["dH"], g["dX"], g["dW13"], g["dW2"]
-    for name, got in (("H", H), ("Act", Act), ("Y", Yp), ("dH", dH), ("dX", dXp), ("dW13", dW13), ("dW2", dW2)):
+    # H (fp32), Act and dH (act dtype): one rounding of values computed from exact inputs
+    for name, got, st in (("H", H, "f32"), ("Act", Act, shape.act), ("dH", dH, shape.act)):
+        q = storage_ok(to_np(got), ref[name], st)
+        assert q <= 1.0, f"{name}: {q:.3f} of the storage-rounding bound"
+    # per-row products of stored (rounded) intermediates: the per-token bar
+    for name, got in (("Y", Yp), ("dX", dXp)):
         err = rel_err(to_np(got), ref[name])
         assert err < tl, f"{name}: {err:.3e}"
-    empty = np.where(np.diff(p.offsets) == 0)[0]
-    for ex in empty:                       # experts with no rows: exact-zero gradients
-        assert torch.count_nonzero(dW13[ex]) == 0 and torch.count_nonzero(dW2[ex]) == 0
+    counts = np.diff(p.offsets)
+    check_expert_grads("dW13", to_np(dW13), ref["dW13"], counts, shape)
+    check_expert_grads("dW2", to_np(dW2), ref["dW2"], counts, shape)
     if Fs:
         hs, acts, ys = O.swiglu_forward(o["x"], o["W13s"], o["W2s"])
         gs = O.swiglu_backward(o["x"], o["W13s"], o["W2s"], hs, o["dy"])
-        for name, got, rf in (("H_s", H_s, hs), ("Act_s", Act_s, acts), ("Y_s", Y_s, ys), ("dH_s", dH_s, gs["dH"]),
-                              ("dx_s", dx_s, gs["dX"]), ("dW13s", dW13s, gs["dW13"]), ("dW2s", dW2s, gs["dW2"])):
+        for name, got, rf, st in (("H_s", H_s, hs, "f32"), ("Act_s", Act_s, acts, shape.act),
+                                  ("dH_s", dH_s, gs["dH"], shape.act)):
+            q = storage_ok(to_np(got), rf, st)
+            assert q <= 1.0, f"{name}: {q:.3f} of the storage-rounding bound"
+        for name, got, rf in (("Y_s", Y_s, ys), ("dx_s", dx_s, gs["dX"])):
             err = rel_err(to_np(got), rf)
             assert err < tl, f"{name}: {err:.3e}"
+        check_grad("dW13s", to_np(dW13s), gs["dW13"], shape)
+        check_grad("dW2s", to_np(dW2s), gs["dW2"], shape)
 
 
 @pytest.mark.parametrize("cid", SMALL_IDS)
@@ -184,35 +194,38 @@ def test_combine_and_backward_pieces(cid):
     cfg = L.config_from_shape(shape)
     inp, o, r, p = _expert_inputs(shape, cid)
     T, k, E, d, A = shape.T, shape.k, shape.E, shape.d, shape.A
-    Yp_np = W.random_rows(A, d, seed=200 + cid, act=shape.act)
-    Ys_np = W.random_rows(T, d, seed=300 + cid, act=shape.act)
-    dy_np = inp["dy"]
+    Yp_np = W.random_rows(A, d, seed=200 + cid, act="f32")
+    Ys_np = W.random_rows(T, d, seed=300 + cid, act="f32")
+    dy_np = W.random_rows(T, d, seed=350 + cid, act="f32")
     Yp, Ys, dy = to_dev(Yp_np), to_dev(Ys_np), to_dev(dy_np)
     row_of = to_dev(p.row_of.astype(np.int32))
     wt = to_dev(r["w"].astype(np.float32))
-    y = torch.empty(T, d, dtype=Yp.dtype, device=dev())
+    ad = torch.bfloat16 if shape.act == "bf16" else torch.float32
+    y = torch.empty(T, d, dtype=torch.float32, device=dev())
     L.unpermute_combine(cfg, Yp, row_of, wt, Ys, y)
-    dYp = torch.empty_like(Yp)
+    dYp = torch.empty(A, d, dtype=ad, device=dev())
+    dYs = torch.empty(T, d, dtype=ad, device=dev())
     dw = torch.empty(T, k, dtype=torch.float32, device=dev())
-    L.unpermute_combine_bwd(cfg, dy, Yp, row_of, wt, dYp, dw)
-    dXp_np = W.random_rows(A, d, seed=400 + cid, act=shape.act)
-    dxs_np = W.random_rows(T, d, seed=500 + cid, act=shape.act)
+    L.unpermute_combine_bwd(cfg, dy, Yp, row_of, wt, dYp, dw, dYs)
+    dXp_np = W.random_rows(A, d, seed=400 + cid, act="f32")
+    dxs_np = W.random_rows(T, d, seed=500 + cid, act="f32")
     dxr_np = W.random_rows(T, d, seed=600 + cid, act="f32")
-    dx = torch.empty(T, d, dtype=Yp.dtype, device=dev())
+    dx = torch.empty(T, d, dtype=torch.float32, device=dev())
     L.permute_bwd(cfg, to_dev(dXp_np), row_of, to_dev(dxs_np), to_dev(dxr_np), dx)
     torch.cuda.synchronize()
     a = shape.act
     w32 = r["w"].astype(np.float32).astype(np.float64)
-    Ypo, Yso, dyo = f64(Yp_np, a), f64(Ys_np, a), f64(dy_np, a)
+    Ypo, Yso, dyo = (v.astype(np.float64) for v in (Yp_np, Ys_np, dy_np))
     y_ref = np.einsum("tk,tkd->td", w32, Ypo[p.row_of]) + Yso
     tl = tol(shape)
     assert rel_err(to_np(y), y_ref) < tl
     dYp_ref = np.zeros((A, d))
     dYp_ref[p.row_of.ravel()] = (w32[:, :, None] * dyo[:, None, :]).reshape(-1, d)
-    assert rel_err(to_np(dYp), dYp_ref) < tl
+    assert storage_ok(to_np(dYp), dYp_ref, a) <= 1.0     # one rounding of w * dy
+    assert storage_ok(to_np(dYs), dyo, a) <= 1.0         # one rounding of dy
     dw_ref = np.einsum("td,tkd->tk", dyo, Ypo[p.row_of])
     assert rel_err(to_np(dw), dw_ref) < 1e-5
-    dx_ref = f64(dXp_np, a)[p.row_of].sum(1) + f64(dxs_np, a) + dxr_np.astype(np.float64)
+    dx_ref = dXp_np.astype(np.float64)[p.row_of].sum(1) + dxs_np.astype(np.float64) + dxr_np.astype(np.float64)
     assert rel_err(to_np(dx), dx_ref) < tl
 
 
