@@ -1,0 +1,245 @@
+"""Benchmark: one MoE layer forward + backward on one MI355X, through the libmoe C ABI.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--config 3] [--no-cpu-baseline]
+
+A step is the whole hot path on one batch: gate logits, router, permute, grouped SwiGLU
+experts (+ shared expert), combine, and the backward of all of it (combine backward,
+expert data and weight gradients, router backward, gate backward, unpermute-reduce).
+Inputs are seeded synthetic tensors of the named layer, resident in HBM before timing.
+Each C-ABI call of a step is bracketed by HIP events on the launch stream, so every
+phase's duration is measured live over the timed steps.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# Published MI355X peaks.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+
+PHASES = ["gate", "router", "permute", "experts_fwd", "combine", "combine_bwd", "experts_bwd", "router_bwd",
+          "gate_bwd", "unpermute_reduce"]
+
+
+def algorithmic(shape):
+    """Algorithmic work per step (the counts the design doc documents)."""
+    T, d, E, k, F, Fs = shape.T, shape.d, shape.E, shape.k, shape.F, shape.Fs
+    A = T * k
+    eb = 2 if shape.act == "bf16" else 4
+    gemm_fwd = 6.0 * d * (F * A + Fs * T)          # fc1 (2 x d x 2F) + fc2 (2 x F x d) per row
+    return dict(
+        grouped_gemm_flop=3.0 * gemm_fwd,          # forward + data gradient + weight gradient
+        gate_flop=6.0 * T * E * d,                 # logits, dWg, dx_r
+        # bytes each HBM-bound phase must move at least once
+        router_bytes=T * E * 4 + T * k * 8 + E * 8,
+        permute_bytes=T * d * eb + A * d * eb + A * 4 * 3,
+        combine_bytes=A * d * 4 + (T * d * 4 if Fs else 0) + T * k * 8 + T * d * 4,
+        combine_bwd_bytes=T * d * 4 + A * d * 4 + A * d * eb + (T * d * eb if Fs else 0) + T * k * 12,
+        unpermute_reduce_bytes=A * d * 4 + (T * d * 4 if Fs else 0) + T * d * 4 + T * d * 4 + T * k * 4,
+    )
+
+
+def cpu_baseline(shape, inp, tokens: int):
+    """The fp64 oracle's layer forward + backward on the first `tokens` tokens of the same
+    inputs, timed on the host cores.  The fp64 copies of the weights of the experts those
+    tokens reach (and of the router and shared expert) are made before the clock starts."""
+    from threadpoolctl import threadpool_info
+
+    from mixture_experts_layer_aux_amd import workloads as W
+    from oracle import moe_oracle as O
+
+    act = shape.act
+    x = W.to_f32(inp["x"][:tokens], act).astype(np.float64)
+    dy = W.to_f32(inp["dy"][:tokens], act).astype(np.float64)
+    spec = O.LayerSpec(E=shape.E, k=shape.k, score=shape.score, scaling=shape.scaling, aux_coeff=shape.aux_coeff)
+    Wg = inp["Wg"].astype(np.float64)
+    idx = O.route(O.gate_logits(x, Wg, inp["bg"]), spec, inp["expert_bias"])["idx"]
+    experts = sorted(set(idx.ravel().tolist()))
+    W13 = {e: W.to_f32(inp["W13"][e], act).astype(np.float64) for e in experts}
+    W2 = {e: W.to_f32(inp["W2"][e], act).astype(np.float64) for e in experts}
+    W13s = W.to_f32(inp["W13s"], act).astype(np.float64) if shape.Fs else None
+    W2s = W.to_f32(inp["W2s"], act).astype(np.float64) if shape.Fs else None
+    t0 = time.perf_counter()
+    f = O.layer_forward(x, Wg, W13, W2, spec, bg=inp["bg"], expert_bias=inp["expert_bias"], W13s=W13s, W2s=W2s)
+    O.layer_backward(f, x, Wg, W13, W2, dy, spec, W13s=W13s, W2s=W2s, sparse_expert_grads=True)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return dict(value=round(tokens / dt, 4), unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=(f"fp64 oracle forward+backward of the first {tokens} of {shape.T} tokens of the "
+                        f"{shape.name} layer ({len(experts)} experts reached), {dt:.1f} s on {threads} "
+                        f"BLAS threads; fp64 weight copies made before timing"))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0 = by layer)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
+              "(expert-parallel sharding across GPUs is not built)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from mixture_experts_layer_aux_amd import _lib as L
+    from mixture_experts_layer_aux_amd import workloads as W
+
+    if not os.path.exists(L.LIB_PATH):
+        from mixture_experts_layer_aux_amd import build as B
+        B.build()
+    L.load()
+    shape = W.CONFIGS[args.config]
+    cfg = L.config_from_shape(shape)
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    inp = W.make_inputs(shape, seed=args.config)
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] {shape.name}: inputs generated in {t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    def up(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    T, d, E, k, F, Fs, A = shape.T, shape.d, shape.E, shape.k, shape.F, shape.Fs, shape.A
+    Wt = dict(Wg=up(inp["Wg"]), bg=up(inp["bg"]), expert_bias=up(inp["expert_bias"]), W13=up(inp["W13"]),
+              W2=up(inp["W2"]), W13s=up(inp["W13s"]), W2s=up(inp["W2s"]))
+    x = up(inp["x"])
+    dy = up(W.to_f32(inp["dy"], shape.act))
+    S = L.alloc_saved(cfg, dev)
+    G = L.alloc_grads(cfg, dev, with_dbg=inp["bg"] is not None)
+    ws = L.alloc_workspace(cfg, dev)
+    f32, ad = torch.float32, L.act_dtype(cfg)
+    y = torch.empty(T, d, dtype=f32, device=dev)
+    dx = torch.empty(T, d, dtype=f32, device=dev)
+    stats = torch.empty(L.MOE_NSTATS, dtype=f32, device=dev)
+    # backward scratch owned by the caller (the piecewise calls name every tensor)
+    dYX = torch.empty(A * d, dtype=f32, device=dev)          # dY_perm (act dtype) then dX_perm (fp32)
+    dY_perm = dYX.view(torch.uint8)[: A * d * (2 if ad == torch.bfloat16 else 4)].view(ad).view(A, d)
+    dX_perm = dYX.view(A, d)
+    dH = torch.empty(A, 2 * F, dtype=ad, device=dev)
+    dw = torch.empty(T, k, dtype=f32, device=dev)
+    dlogits = torch.empty(T, E, dtype=f32, device=dev)
+    dx_r = torch.empty(T, d, dtype=f32, device=dev)
+    dH_s = torch.empty(T, 2 * Fs, dtype=ad, device=dev) if Fs else None
+    dx_s = torch.empty(T, d, dtype=f32, device=dev) if Fs else None
+    dY_s = torch.empty(T, d, dtype=ad, device=dev) if Fs else None
+    torch.cuda.synchronize()
+
+    def step(ev):
+        i = 0
+
+        def mark():
+            nonlocal i
+            if ev is not None:
+                ev[i].record()
+            i += 1
+
+        mark()
+        L.gate_logits(cfg, x, Wt["Wg"], Wt["bg"], S["logits"])
+        mark()
+        L.router_topk(cfg, S["logits"], Wt["expert_bias"], S["idx"], S["w"], S["counts"], None, stats, ws)
+        mark()
+        L.permute(cfg, x, S["idx"], S["offsets"], S["row_of"], S["token_of"], S["x_perm"], ws)
+        mark()
+        L.grouped_gemm_swiglu(cfg, S["x_perm"], S["offsets"], Wt["W13"], Wt["W2"], x if Fs else None, Wt["W13s"],
+                              Wt["W2s"], S["H"], S["Act"], S["Y_perm"], S.get("H_s"), S.get("Act_s"), S.get("Y_s"), ws)
+        mark()
+        L.unpermute_combine(cfg, S["Y_perm"], S["row_of"], S["w"], S.get("Y_s"), y)
+        mark()
+        L.unpermute_combine_bwd(cfg, dy, S["Y_perm"], S["row_of"], S["w"], dY_perm, dw, dY_s)
+        mark()
+        L.grouped_gemm_swiglu_bwd(cfg, S["x_perm"], S["offsets"], Wt["W13"], Wt["W2"], S["H"], S["Act"], dY_perm,
+                                  dH, dX_perm, G["dW13"], G["dW2"], x if Fs else None, Wt["W13s"], Wt["W2s"],
+                                  S.get("H_s"), S.get("Act_s"), dY_s, dH_s, dx_s, G.get("dW13s"), G.get("dW2s"), ws)
+        mark()
+        L.router_bwd(cfg, S["logits"], S["idx"], S["w"], dw, S["counts"], 1.0, dlogits)
+        mark()
+        L.gate_logits_bwd(cfg, x, Wt["Wg"], dlogits, G["dWg"], G.get("dbg"), dx_r)
+        mark()
+        L.permute_bwd(cfg, dX_perm, S["row_of"], dx_s, dx_r, dx)
+        mark()
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(PHASES) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    phase_ms = {p: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]))
+                for i, p in enumerate(PHASES)}
+    ms_step = elapsed * 1e3 / args.steps
+    st = stats.cpu().numpy()
+
+    alg = algorithmic(shape)
+    gemm_ms = phase_ms["experts_fwd"] + phase_ms["experts_bwd"]
+    gemm_tflops = alg["grouped_gemm_flop"] / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if shape.act == "bf16" else PEAK_FP32_TFLOPS
+
+    def hbm(p, key):
+        gbps = alg[key] / (phase_ms[p] * 1e-3) / 1e9
+        return dict(ms=round(phase_ms[p], 4), bytes=int(alg[key]), achieved_gbps=round(gbps, 1),
+                    frac=round(gbps / PEAK_HBM_GBPS, 4))
+
+    layer_flop = alg["grouped_gemm_flop"] + alg["gate_flop"]
+    out = dict(
+        metric="MoE layer fwd+bwd tokens/s on 1 MI355X",
+        value=round(T / (ms_step * 1e-3), 1),
+        unit="tokens/s",
+        n_gpus=1,
+        steps=args.steps,
+        warmup=args.warmup,
+        ms_per_step=round(ms_step, 3),
+        higher_is_better=True,
+        scaling="weak",
+        vs_baseline=None,
+        dtype="bf16" if shape.act == "bf16" else "f32",
+        data="synthetic (seeded generator, random-init weights)",
+        config=dict(workload=shape.name, T=T, d=d, E=E, k=k, F=F, Fs=Fs, score=shape.score,
+                    bias=shape.bias, aux_coeff=shape.aux_coeff, parallelism="single GPU"),
+        roofline=dict(kernel="grouped expert GEMMs (bf16 MFMA, all expert projections of fwd + bwd)",
+                      bound="mfma", achieved=round(gemm_tflops, 2), peak=peak, unit="TFLOP/s",
+                      frac=round(gemm_tflops / peak, 4), traffic=None,
+                      flop_per_step=alg["grouped_gemm_flop"], ms_per_step=round(gemm_ms, 3)),
+        layer_tflops=round(layer_flop / (ms_step * 1e-3) / 1e12, 2),
+        phases_ms={p: round(v, 4) for p, v in phase_ms.items()},
+        hbm_phases=dict(router=hbm("router", "router_bytes"), permute=hbm("permute", "permute_bytes"),
+                        combine=hbm("combine", "combine_bytes"), combine_bwd=hbm("combine_bwd", "combine_bwd_bytes"),
+                        unpermute_reduce=hbm("unpermute_reduce", "unpermute_reduce_bytes")),
+        gate_gemm=dict(ms=round(phase_ms["gate"] + phase_ms["gate_bwd"], 4), flop=alg["gate_flop"],
+                       tflops=round(alg["gate_flop"] / ((phase_ms["gate"] + phase_ms["gate_bwd"]) * 1e-3) / 1e12, 2),
+                       peak_fp32=PEAK_FP32_TFLOPS),
+        load=dict(maxvio=round(float(st[1]), 4), empty_experts=int(st[2]), max_count=int(st[3]),
+                  mean_count=T * k / E),
+    )
+    if not args.no_cpu_baseline:
+        tokens = args.cpu_tokens or {1: 128, 2: 8192, 3: 24, 4: 1024, 5: 256}[args.config]
+        out["cpu_baseline"] = cpu_baseline(shape, inp, min(tokens, T))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

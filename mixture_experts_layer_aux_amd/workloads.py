@@ -235,3 +235,17 @@ def to_f32(a: Optional[np.ndarray], act: str) -> Optional[np.ndarray]:
     if act == "bf16" and a.dtype == np.uint16:
         return bf16_bits_to_f32(a)
     return a.astype(np.float32, copy=False)
+
+
+class ExpertView:
+    """Per-expert fp32 view of a stacked expert-weight array, converted on access
+    (lets a CPU consumer walk a large bf16 stack one expert at a time)."""
+
+    def __init__(self, stack: np.ndarray, act: str):
+        self.stack, self.act = stack, act
+
+    def __len__(self) -> int:
+        return self.stack.shape[0]
+
+    def __getitem__(self, e: int) -> np.ndarray:
+        return to_f32(self.stack[e], self.act)

@@ -264,7 +264,8 @@ def layer_forward(x, Wg, W13, W2, spec: LayerSpec, bg=None, expert_bias=None,
     ([LC] "An expert transforms numbers inside the model": the weighted sum of the
     selected experts' outputs, coordinate by coordinate; [HB] §3.4 Shared experts:
     without a gate the shared output is added at weight 1).
-    `idx` may be given to evaluate the layer at a fixed routing.
+    `idx` may be given to evaluate the layer at a fixed routing.  W13 and W2 only need
+    per-expert indexing (W13[e] -> [2F, d]), so a lazily converted stack works.
     """
     x = _d(x)
     T, d = x.shape
@@ -277,7 +278,7 @@ def layer_forward(x, Wg, W13, W2, spec: LayerSpec, bg=None, expert_bias=None,
     perm = permutation(r["idx"], spec.E)
     A = T * spec.k
     xp = x[perm.token_of]
-    F2 = np.asarray(W13).shape[1]
+    F2 = 2 * np.shape(W2[int(r["idx"].ravel()[0])])[1]
     H = np.zeros((A, F2))
     Act = np.zeros((A, F2 // 2))
     Yp = np.zeros((A, d))
@@ -332,8 +333,12 @@ def router_backward(logits, idx, w, dw, spec: LayerSpec, counts=None, daux: floa
 
 
 def layer_backward(fwd: Dict[str, object], x, Wg, W13, W2, dy, spec: LayerSpec,
-                   W13s=None, W2s=None, daux: float = 1.0) -> Dict[str, np.ndarray]:
+                   W13s=None, W2s=None, daux: float = 1.0, sparse_expert_grads: bool = False
+                   ) -> Dict[str, np.ndarray]:
     """Gradients of L = sum(dy * y) + daux * aux with respect to every input.
+
+    With sparse_expert_grads the expert weight gradients come back as {e: array} for the
+    experts that received rows (the others are zero), instead of full [E, ...] stacks.
 
     The expert path gets its gradient through the weighted sum ([LC] "How the router
     learns without an expert-selection answer key": the signal reaches the router only
@@ -351,8 +356,11 @@ def layer_backward(fwd: Dict[str, object], x, Wg, W13, W2, dy, spec: LayerSpec,
     dYp[rows.ravel()] = (w[:, :, None] * dy[:, None, :]).reshape(-1, d)
     xp = fwd["x_perm"]
     dXp = np.zeros_like(xp)
-    dW13 = np.zeros(np.asarray(W13).shape)
-    dW2 = np.zeros(np.asarray(W2).shape)
+    if sparse_expert_grads:
+        dW13, dW2 = {}, {}
+    else:
+        dW13 = np.zeros((spec.E,) + np.shape(W13[0]))
+        dW2 = np.zeros((spec.E,) + np.shape(W2[0]))
     dH = np.zeros_like(fwd["H"])
     for e in range(spec.E):
         a, b = perm.offsets[e], perm.offsets[e + 1]
