@@ -5,25 +5,33 @@
 // projection: each expert owns a ragged block of rows (forward, data gradient) or a
 // ragged block of the reduction dimension (weight gradient).
 //
-// Design (per workgroup: 256 threads = 4 waves in a 2x2 grid):
-//   * 256 x 256 output tile, 64-deep K steps, each wave a 128 x 128 sub-tile held as
-//     4 x 4 accumulators of v_mfma_f32_32x32x16_bf16 (16 fp32 per lane each);
-//   * both operands staged in LDS as [256 rows][64 k] bf16 with an XOR swizzle of the
-//     16-byte chunk index ((r ^ (r >> 3)) & 7) so that fragment reads (32 consecutive
-//     rows, one chunk) and transposing writes (rows 8 apart) spread over all banks;
-//   * double-buffered LDS (2 x 64 KB): the next K step is fetched into registers while
-//     the current one is multiplied, then written to the other buffer; one barrier per
-//     step;
-//   * operands stored K-contiguous are copied in 16-byte chunks; operands stored
-//     row-contiguous (the weights in the data-gradient GEMMs, both operands of the
-//     weight-gradient GEMMs) are read as 8 x 8 bf16 blocks and transposed in registers;
-//   * a device-built tile list (per-expert prefix of row tiles) so the host never
-//     reads the expert counts; empty experts get no tiles (forward) or exact-zero
-//     gradients (weight gradient, zero-length reduction);
-//   * row-ragged launches map workgroup h to tile (h mod 8) * ceil(tiles / 8) + h / 8:
-//     workgroups are dealt round-robin to the 8 XCDs, so each XCD walks a contiguous
-//     run of tiles (expert, column tile, row tile) and the tiles sharing a weight tile
-//     or an activation tile run together on one L2;
+// Design (per workgroup: 512 threads = 8 waves in a 2 x 4 grid):
+//   * 256 x 256 output tile, each wave a 128 x 64 sub-tile held as 4 x 2 accumulators of
+//     v_mfma_f32_32x32x16_bf16 (128 fp32 per lane);
+//   * operands go from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane), 64
+//     K values per stage, double-buffered (2 stages of 64 KB): the next stage is in flight
+//     while the current one is multiplied, and no VGPRs stage the data;
+//   * buffer descriptors bound every load: rows past the end of a ragged reduction (weight
+//     gradient) and past the end of an operand read as zeros, so no tail handling exists
+//     in the loop;
+//   * operands contiguous in K are stored [rows][64 k] with the 16-byte chunk index XORed
+//     by (r ^ (r >> 3)) & 7, and read with ds_read_b128; operands contiguous in rows (the
+//     weights of the data gradients, both operands of the weight gradients) are stored
+//     as loaded, [64 k][256 rows] with the chunk index XORed by 4 * (k & 3), and
+//     read with the gfx950 transposing ds_read_b64_tr_b16 (a 16-lane group reads 4 k-rows
+//     of 16 columns and gets back, per lane, one column's 4 k values), so no operand is
+//     ever transposed through registers;
+//   * the MFMA takes the B fragment first, so the accumulator comes out transposed and
+//     each lane owns four consecutive output columns: every epilogue load and store is a
+//     16-byte (fp32) or 8-byte (bf16) vector;
+//   * a device-built tile list (per-expert prefix of row tiles) so the host never reads
+//     the expert counts; empty experts get no tiles (forward) or exact-zero gradients
+//     (weight gradient, zero-length reduction);
+//   * workgroups are dealt round-robin to the 8 XCDs, so workgroup h runs on XCD h mod 8.
+//     Row-ragged launches map h to tile (h mod 8) * ceil(tiles / 8) + h / 8, so each XCD
+//     walks a contiguous run of tiles (expert, column tile, row tile) and tiles sharing a
+//     weight or activation tile run together on one L2; reduction-ragged launches give
+//     each XCD one eighth of every expert's tiles;
 //   * fused epilogues: SwiGLU (forward: H in fp32 and Act in bf16 from the same
 //     accumulators, the gate and up rows of W13 interleaved per 32-row block of the B
 //     tile) and the SwiGLU backward (reads the saved fp32 H, writes dH in bf16).
@@ -34,11 +42,22 @@ namespace moe {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHR = 256;
-constexpr int TILE = 256 * 64;  // bf16 elements of one operand tile
+constexpr int BM = 256, BN = 256, BK = 64, STAGES = 2;
+// Waves of a workgroup: WAVES_M x WAVES_N, each owning a (BM / WAVES_M) x (BN / WAVES_N)
+// sub-tile as (BM / WAVES_M / 32) x (BN / WAVES_N / 32) accumulators of 32 x 32.
+constexpr int WAVES_M = 2, WAVES_N = 4, NWAVES = WAVES_M * WAVES_N, NTHR = 64 * NWAVES;
+constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, NI = WTM / 32, NJ = WTN / 32;
+constexpr int KCH = BK / 8;                         // 16-byte chunks per K-contiguous row
+constexpr int DMA_PER_WAVE = (BK / 2) / NWAVES;     // one-KB blocks per operand per stage per wave
+constexpr int TILE = 256 * BK;          // bf16 elements of one operand tile of one stage
+constexpr int STAGE_ELEMS = 2 * TILE;   // A then B
+constexpr int BLOCK_ELEMS = 512;        // one wave-wide 16-byte-per-lane LDS DMA = 1 KB
+// 4th descriptor dword of a raw (untyped, 32-bit element) buffer on gfx9.
+constexpr int kRsrcFlags = 0x00020000;
 
 struct MfmaArgs {
   const uint16_t* A;
@@ -54,22 +73,38 @@ struct MfmaArgs {
   const int32_t* offsets;
   const int32_t* tile_prefix;
   int G, M, N, K, F, range_end, nN, nM;
+  int b_rows_bytes;  // K-major B: bytes of one group's weight matrix (bounds the DMA)
 };
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int r, int kc) { return r * 64 + ((kc ^ swz(r)) << 3); }
+// K-contiguous layout: element (r, k) of a stage tile at r * BK + ((k/8) ^ swk(r)) * 8 + k%8
+// (XORs that measured conflict-free for 32 consecutive rows read at one 16-byte chunk).
+__device__ __forceinline__ int swk(int r) { return KCH == 8 ? ((r ^ (r >> 3)) & 7) : ((r >> 2) & 3); }
+// Row-contiguous layout: element (k, c) at k * 256 + ((c/8) ^ swm(k)) * 8 + c%8; the 4 k-rows
+// a 16-lane transposing read touches land 4 chunks apart, so two such groups (32 lanes)
+// cover 16 distinct chunks.
+__device__ __forceinline__ int swm(int k) { return (k & 3) << 2; }
 
-// 8 x 8 transpose of bf16: in[kk] holds columns 0..7 of row kk; out[cc] holds rows 0..7
-// of column cc.
-__device__ __forceinline__ void transpose8x8(const u32x4_t (&in)[8], u32x4_t (&out)[8]) {
-#pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
-#pragma unroll
-    for (int pq = 0; pq < 4; ++pq) {
-      const uint32_t a = in[2 * pq][cc >> 1], b = in[2 * pq + 1][cc >> 1];
-      out[cc][pq] = (cc & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-    }
-  }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcFlags);
+}
+
+// Waits until at most n of this wave's buffer loads are outstanding (n rounded down to a
+// multiple of 4, at most 24).
+__device__ __forceinline__ void wait_vm(int n) {
+  // s_waitcnt simm16: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt (7) in
+  // bits 6:4 and lgkmcnt (15) in bits 11:8 left at their maxima
+  if (n >= 24) __builtin_amdgcn_s_waitcnt(0x4F78);
+  else if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);
+  else if (n >= 12) __builtin_amdgcn_s_waitcnt(0x0F7C);
+  else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);
+  else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Tiles of a row-ragged launch: group g has ceil(rows_g / 256) row tiles.
@@ -93,11 +128,11 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
 
 template <int AMAJ, int BMAJ, int RAG, int EPI, bool OUT_F32>
 __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE_ELEMS];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
   // ------------------------------------------------------------ tile of this workgroup
   int grp, mt, nt;
@@ -132,11 +167,16 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
     k_begin = 0;
     k_end = p.K;
   } else {
-    const int L = blockIdx.x;
+    // Reduction-ragged (weight gradient): a tile's work grows with its expert's rows, so
+    // every expert's tiles are split into 8 equal runs, one per XCD; inside a run the
+    // column tile varies fastest, so the tiles sharing a slice of A sit together on one L2.
     const int per = p.nM * p.nN;
-    if (L >= p.G * per) return;
-    grp = L / per;
-    const int local = L - grp * per;
+    const int run = (per + 7) >> 3;
+    const int h = blockIdx.x;
+    const int q = h >> 3;
+    grp = q / run;
+    const int local = (h & 7) * run + (q - grp * run);
+    if (grp >= p.G || local >= per) return;
     mt = local / p.nN;
     nt = local - mt * p.nN;
     row_begin = mt * BM;
@@ -147,169 +187,193 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
   const int n0 = nt * BN;
   const uint16_t* Bg = p.B + (RAG == RAGGED_M ? static_cast<int64_t>(grp) * p.b_gstride : 0);
 
-  // ------------------------------------------------------------ global -> registers
-  u32x4_t ra[8], rb[8];
-  auto load_a = [&](int k0) {
+  // ------------------------------------------------------------ HBM -> LDS (DMA)
+  // Each wave moves 4 one-KB blocks of A and 4 of B per stage.  voff*: per-lane byte
+  // offsets of those blocks relative to the stage's base (constant over the K loop).
+  int voffA[DMA_PER_WAVE], voffB[DMA_PER_WAVE];
+#pragma unroll
+  for (int q = 0; q < DMA_PER_WAVE; ++q) {
+    const int blk = wave * DMA_PER_WAVE + q;
     if (AMAJ == K_MAJOR) {
-      const int kc = tid & 7;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int r = (tid >> 3) + 32 * q;
-        const int grow = min(row_begin + r, row_end - 1);
-        ra[q] = *reinterpret_cast<const u32x4_t*>(p.A + static_cast<int64_t>(grow) * p.lda + k0 + kc * 8);
-      }
+      const int r = blk * (64 / KCH) + lane / KCH;
+      const int c = (lane % KCH) ^ swk(r);
+      voffA[q] = r * static_cast<int>(p.lda) * 2 + c * 16;
     } else {
-      const int cb = tid & 31, kb = tid >> 5;
-      const int col = min(row_begin + cb * 8, p.M - 8);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int kr = k0 + kb * 8 + kk;
-        if (kr < k_end)
-          ra[kk] = *reinterpret_cast<const u32x4_t*>(p.A + static_cast<int64_t>(kr) * p.lda + col);
-        else
-          ra[kk] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+      const int kr = blk * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ swm(kr);
+      voffA[q] = kr * static_cast<int>(p.lda) * 2 + (row_begin + c * 8) * 2;
     }
-  };
-  auto load_b = [&](int k0) {
     if (BMAJ == K_MAJOR) {
-      const int kc = tid & 7;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        int n;
-        if (EPI == EPI_SWIGLU_FWD)
-          n = ((q & 1) ? p.F : 0) + nt * 128 + (q >> 1) * 32 + (tid >> 3);
-        else
-          n = min(n0 + (tid >> 3) + 32 * q, p.N - 1);
-        rb[q] = *reinterpret_cast<const u32x4_t*>(Bg + static_cast<int64_t>(n) * p.ldb + k0 + kc * 8);
-      }
+      const int r = blk * (64 / KCH) + lane / KCH;
+      const int c = (lane % KCH) ^ swk(r);
+      int n;
+      if (EPI == EPI_SWIGLU_FWD)  // B-tile block j of 32 rows: gate rows if j is even, up rows if odd
+        n = (((r >> 5) & 1) ? p.F : 0) + nt * 128 + (r >> 6) * 32 + (r & 31);
+      else
+        n = n0 + r;
+      voffB[q] = n * static_cast<int>(p.ldb) * 2 + c * 16;
     } else {
-      const int cb = tid & 31, kb = tid >> 5;
-      const int col = min(n0 + cb * 8, p.N - 8);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int kr = k0 + kb * 8 + kk;
-        if (kr < k_end)
-          rb[kk] = *reinterpret_cast<const u32x4_t*>(Bg + static_cast<int64_t>(kr) * p.ldb + col);
-        else
-          rb[kk] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+      const int kr = blk * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ swm(kr);
+      voffB[q] = kr * static_cast<int>(p.ldb) * 2 + (n0 + c * 8) * 2;
     }
+  }
+  const int a_rows = min(BM, row_end - row_begin);  // K-major A rows that exist (RAGGED_M)
+  auto issue_stage = [&](int st) {
+    const int k0 = k_begin + st * BK;
+    uint16_t* dst = lds + (st % STAGES) * STAGE_ELEMS;
+    __amdgpu_buffer_rsrc_t ra, rb;
+    if (AMAJ == K_MAJOR)
+      ra = make_rsrc(p.A + static_cast<int64_t>(row_begin) * p.lda + k0,
+                     (a_rows - 1) * static_cast<int>(p.lda) * 2 + BK * 2);
+    else
+      ra = make_rsrc(p.A + static_cast<int64_t>(k0) * p.lda, min(BK, k_end - k0) * static_cast<int>(p.lda) * 2);
+    if (BMAJ == K_MAJOR)
+      rb = make_rsrc(Bg + k0, p.b_rows_bytes - k0 * 2);
+    else
+      rb = make_rsrc(Bg + static_cast<int64_t>(k0) * p.ldb, min(BK, k_end - k0) * static_cast<int>(p.ldb) * 2);
+#pragma unroll
+    for (int q = 0; q < DMA_PER_WAVE; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(dst + (wave * DMA_PER_WAVE + q) * BLOCK_ELEMS), 16,
+                                               voffA[q], 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < DMA_PER_WAVE; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dst + TILE + (wave * DMA_PER_WAVE + q) * BLOCK_ELEMS),
+                                               16, voffB[q], 0, 0, 0);
   };
-  // ------------------------------------------------------------ registers -> LDS
-  auto store_tile = [&](uint16_t* dst, const u32x4_t (&rg)[8], int major) {
+
+  // ------------------------------------------------------------ LDS -> fragments
+  // Fragment of a 32-row block at row offset rb0 for substep ks (16 k): lane l gets rows
+  // rb0 + l%32, k = 16 ks + 8 (l/32) + 0..7.
+  auto frag = [&](const uint16_t* t, int major, int rb0, int ks) -> bf16x8_t {
     if (major == K_MAJOR) {
-      const int kc = tid & 7;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int r = (tid >> 3) + 32 * q;
-        *reinterpret_cast<u32x4_t*>(dst + lds_off(r, kc)) = rg[q];
-      }
+      const int r = rb0 + (lane & 31);
+      const int c = (ks * 2 + (lane >> 5)) ^ swk(r);
+      return *reinterpret_cast<const bf16x8_t*>(t + r * BK + c * 8);
     } else {
-      const int cb = tid & 31, kb = tid >> 5;
-      u32x4_t t[8];
-      transpose8x8(rg, t);
+      const int j = lane & 15, g = lane >> 4;
+      const int col = rb0 + 16 * (g & 1) + 4 * (j & 3);
+      i16x4_t h[2];
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) *reinterpret_cast<u32x4_t*>(dst + lds_off(cb * 8 + cc, kb)) = t[cc];
+      for (int hh = 0; hh < 2; ++hh) {
+        const int kr = ks * 16 + 8 * (g >> 1) + 4 * hh + (j >> 2);
+        const uint16_t* a = t + kr * 256 + (((col >> 3) ^ swm(kr)) << 3) + (col & 7);
+        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)a);
+      }
+      const i16x4_t lo = h[0], hi = h[1];
+      typedef short i16x8_t __attribute__((ext_vector_type(8)));
+      const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8_t, v);
     }
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
-  if (nk > 0) {
-    load_a(k_begin);
-    load_b(k_begin);
-    store_tile(lds, ra, AMAJ);
-    store_tile(lds + TILE, rb, BMAJ);
-  }
-  __syncthreads();
+  // prologue: stages 0 .. STAGES-2 in flight
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue_stage(st);
   for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < nk) {
-      load_a(k_begin + (it + 1) * BK);
-      load_b(k_begin + (it + 1) * BK);
-    }
-    const uint16_t* As = lds + cur * 2 * TILE;
+    // stage `it` has landed once at most (stages issued after it) * 8 loads are pending
+    const int ahead = min(STAGES - 2, nk - 1 - it);
+    wait_vm(ahead * 2 * DMA_PER_WAVE);
+    block_barrier();  // every wave's part of stage `it` is in LDS; stage it-1 is consumed
+    if (it + STAGES - 1 < nk) issue_stage(it + STAGES - 1);
+    const uint16_t* As = lds + (it % STAGES) * STAGE_ELEMS;
     const uint16_t* Bs = As + TILE;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t a[4], b[4];
-      const int kc = ks * 2 + (lane >> 5);
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t fa[NI], fb[NJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(wm * 128 + i * 32 + (lane & 31), kc));
+      for (int i = 0; i < NI; ++i) fa[i] = frag(As, AMAJ, wm * WTM + i * 32, ks);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(wn * 128 + j * 32 + (lane & 31), kc));
+      for (int j = 0; j < NJ; ++j) fb[j] = frag(Bs, BMAJ, wn * WTN + j * 32, ks);
+      // B fragment first: the accumulator comes out transposed (see the epilogue)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
-    if (it + 1 < nk) {
-      uint16_t* nxt = lds + (cur ^ 1) * 2 * TILE;
-      store_tile(nxt, ra, AMAJ);
-      store_tile(nxt + TILE, rb, BMAJ);
-    }
-    __syncthreads();
   }
 
   // ------------------------------------------------------------ epilogue
-  // acc[i][j][e] is row wm*128 + i*32 + 8*(e/4) + 4*(lane/32) + e%4, column
-  // wn*128 + j*32 + lane%32 of the tile.
+  // acc[i][j][4q + c] is row wm*WTM + i*32 + lane%32 and column
+  // wn*WTN + j*32 + 8q + 4*(lane/32) + c of the tile (c = 0..3: consecutive columns).
   const int64_t cg = RAG == RAGGED_K ? static_cast<int64_t>(grp) * p.c_gstride : 0;
   uint16_t* C = static_cast<uint16_t*>(p.C) + cg;
   float* Cf = static_cast<float*>(p.C) + cg;
-  const int rbase = row_begin + wm * 128 + 4 * (lane >> 5);
+  const int cbase = 4 * (lane >> 5);
   if (EPI == EPI_SWIGLU_FWD) {
+    // B-tile block 2p holds gate rows and block 2p + 1 the matching up rows
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i) {
+      const int row = row_begin + wm * WTM + i * 32 + (lane & 31);
+      if (row >= row_end) continue;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int col = nt * 128 + wn * 64 + q * 32 + (lane & 31);
+      for (int pq = 0; pq < NJ / 2; ++pq)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
-          if (row < row_end) {
-            const float gt = acc[i][2 * q][e], up = acc[i][2 * q + 1][e];
-            Cf[static_cast<int64_t>(row) * p.ldc + col] = gt;
-            Cf[static_cast<int64_t>(row) * p.ldc + p.F + col] = up;
-            p.C2[static_cast<int64_t>(row) * p.ldc2 + col] = f32_to_bf16(silu_f(gt) * up);
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * 128 + wn * (WTN / 2) + pq * 32 + 8 * q + cbase;
+          float4 gt, up;
+          gt.x = acc[i][2 * pq][4 * q]; gt.y = acc[i][2 * pq][4 * q + 1];
+          gt.z = acc[i][2 * pq][4 * q + 2]; gt.w = acc[i][2 * pq][4 * q + 3];
+          up.x = acc[i][2 * pq + 1][4 * q]; up.y = acc[i][2 * pq + 1][4 * q + 1];
+          up.z = acc[i][2 * pq + 1][4 * q + 2]; up.w = acc[i][2 * pq + 1][4 * q + 3];
+          float* hrow = Cf + static_cast<int64_t>(row) * p.ldc;
+          *reinterpret_cast<float4*>(hrow + col) = gt;
+          *reinterpret_cast<float4*>(hrow + p.F + col) = up;
+          uint2 av;
+          av.x = pack_bf16x2(silu_f(gt.x) * up.x, silu_f(gt.y) * up.y);
+          av.y = pack_bf16x2(silu_f(gt.z) * up.z, silu_f(gt.w) * up.w);
+          *reinterpret_cast<uint2*>(p.C2 + static_cast<int64_t>(row) * p.ldc2 + col) = av;
         }
-      }
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i) {
+      const int row = row_begin + wm * WTM + i * 32 + (lane & 31);
+      if (row >= row_end) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 128 + j * 32 + (lane & 31);
-        if (col >= p.N) continue;
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = rbase + i * 32 + 8 * (e >> 2) + (e & 3);
-          if (row >= row_end) continue;
-          const float v = acc[i][j][e];
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * WTN + j * 32 + 8 * q + cbase;
+          if (col >= p.N) continue;
+          const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+          const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
           if (EPI == EPI_SWIGLU_BWD) {
-            const int64_t hr = static_cast<int64_t>(row) * p.ldh;
-            const float gt = p.H[hr + col], up = p.H[hr + p.F + col];
-            const float sg = sigmoid_f(gt);
-            C[static_cast<int64_t>(row) * p.ldc + col] = f32_to_bf16(v * up * sg * (1.0f + gt * (1.0f - sg)));
-            C[static_cast<int64_t>(row) * p.ldc + p.F + col] = f32_to_bf16(v * gt * sg);
+            const float* hrow = p.H + static_cast<int64_t>(row) * p.ldh;
+            const float4 gt = *reinterpret_cast<const float4*>(hrow + col);
+            const float4 up = *reinterpret_cast<const float4*>(hrow + p.F + col);
+            const float g[4] = {gt.x, gt.y, gt.z, gt.w}, u[4] = {up.x, up.y, up.z, up.w};
+            const float dv[4] = {v0, v1, v2, v3};
+            float dg[4], du[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float sg = sigmoid_f(g[c]);
+              dg[c] = dv[c] * u[c] * sg * (1.0f + g[c] * (1.0f - sg));
+              du[c] = dv[c] * g[c] * sg;
+            }
+            uint16_t* drow = C + static_cast<int64_t>(row) * p.ldc;
+            *reinterpret_cast<uint2*>(drow + col) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+            *reinterpret_cast<uint2*>(drow + p.F + col) =
+                make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
           } else if (OUT_F32) {
-            Cf[static_cast<int64_t>(row) * p.ldc + col] = v;
+            *reinterpret_cast<float4*>(Cf + static_cast<int64_t>(row) * p.ldc + col) = make_float4(v0, v1, v2, v3);
           } else {
-            C[static_cast<int64_t>(row) * p.ldc + col] = f32_to_bf16(v);
+            *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * p.ldc + col) =
+                make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
           }
         }
-      }
+    }
   }
 }
 
@@ -348,6 +412,11 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
   a.K = g.K;
   a.F = g.F;
   a.range_end = g.range_end;
+  if (g.b_major == K_MAJOR) {
+    const int64_t bytes = static_cast<int64_t>(g.epi == EPI_SWIGLU_FWD ? 2 * g.F : g.N) * g.ldb * 2;
+    if (bytes >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: weight matrix above 2 GB");
+    a.b_rows_bytes = static_cast<int>(bytes);
+  }
   int64_t grid;
   if (g.ragged == RAGGED_M) {
     a.nN = static_cast<int>(g.epi == EPI_SWIGLU_FWD ? ceil_div(g.N, 256) : ceil_div(g.N, BN));
@@ -362,7 +431,7 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
   } else {
     a.nM = static_cast<int>(ceil_div(g.M, BM));
     a.nN = static_cast<int>(ceil_div(g.N, BN));
-    grid = static_cast<int64_t>(g.offsets ? g.G : 1) * a.nM * a.nN;
+    grid = 8 * static_cast<int64_t>(g.offsets ? g.G : 1) * ceil_div(static_cast<int64_t>(a.nM) * a.nN, 8);
   }
   if (grid == 0) return MOE_OK;
 #define MOE_MF(AM, BMJ, RG, EP, OF)                                                              \
