@@ -7,7 +7,12 @@ experts (+ shared expert), combine, and the backward of all of it (combine backw
 expert data and weight gradients, router backward, gate backward, unpermute-reduce).
 Inputs are seeded synthetic tensors of the named layer, resident in HBM before timing.
 Each C-ABI call of a step is bracketed by HIP events on the launch stream, so every
-phase's duration is measured live over the timed steps.  Prints one JSON line.
+phase's duration is measured live over the timed steps.  The expert backward runs as its
+data gradients followed by four grouped weight-gradient calls of one kernel launch each; the
+routed fc1 weight gradient, the longest single kernel of the step, is the one the roofline
+object reports.  Prints one JSON line.
+
+    python bench.py --copy-calibration   # only 3 x 1 GiB device copies, for counter scaling
 """
 from __future__ import annotations
 
@@ -27,8 +32,13 @@ PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBPS = 8000.0
 
-PHASES = ["gate", "router", "permute", "experts_fwd", "combine", "combine_bwd", "experts_bwd", "router_bwd",
-          "gate_bwd", "unpermute_reduce"]
+PHASES = ["gate", "router", "permute", "experts_fwd", "combine", "combine_bwd", "experts_bwd_data", "wgrad_fc2",
+          "wgrad_fc1", "wgrad_shared", "router_bwd", "gate_bwd", "unpermute_reduce"]
+GEMM_PHASES = ["experts_fwd", "experts_bwd_data", "wgrad_fc2", "wgrad_fc1", "wgrad_shared"]
+# The kernel the roofline object reports: the routed fc1 weight gradient, one launch of the
+# grouped GEMM with a ragged reduction, the longest single kernel of the step.
+ROOFLINE_PHASE = "wgrad_fc1"
+GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_aux_amd", "csrc", "moe_gemm_mfma.hip")
 
 
 def algorithmic(shape):
@@ -39,6 +49,9 @@ def algorithmic(shape):
     gemm_fwd = 6.0 * d * (F * A + Fs * T)          # fc1 (2 x d x 2F) + fc2 (2 x F x d) per row
     return dict(
         grouped_gemm_flop=3.0 * gemm_fwd,          # forward + data gradient + weight gradient
+        wgrad_fc1_flop=2.0 * A * 2 * F * d,        # dW13 = dH^T x_perm over the routed rows
+        # dW13 written once in fp32, dH and x_perm read once, the offsets
+        wgrad_fc1_bytes=E * 2 * F * d * 4 + A * 2 * F * eb + A * d * eb + (E + 1) * 4,
         gate_flop=6.0 * T * E * d,                 # logits, dWg, dx_r
         # bytes each HBM-bound phase must move at least once
         router_bytes=T * E * 4 + T * k * 8 + E * 8,
@@ -47,6 +60,46 @@ def algorithmic(shape):
         combine_bwd_bytes=T * d * 4 + A * d * 4 + A * d * eb + (T * d * eb if Fs else 0) + T * k * 12,
         unpermute_reduce_bytes=A * d * 4 + (T * d * 4 if Fs else 0) + T * d * 4 + T * d * 4 + T * k * 4,
     )
+
+
+def measured_traffic(shape):
+    """HBM bytes per launch of the roofline kernel from the committed rocprofv3 counter
+    summary, or None when there is none for this layer or the GEMM source has changed since
+    the counters were taken (the summary records the source's sha256)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"wgrad_fc1_{shape.name}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                key, val = line[2:].split(": ", 1)
+                fields[key.strip("` ")] = val.strip().strip("`")
+    with open(GEMM_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("gemm_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
+def roofline(alg, ms, peak_tflops, shape):
+    """Roofline of one launch of the routed fc1 weight-gradient kernel: the bound is the
+    resource whose peak gives the longer time for its algorithmic work."""
+    flop, nbytes = alg["wgrad_fc1_flop"], alg["wgrad_fc1_bytes"]
+    t_mfma = flop / (peak_tflops * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
+    s = ms * 1e-3
+    common = dict(kernel="routed fc1 weight gradient dW13 = dH^T x_perm (one grouped-GEMM launch, bf16 MFMA, "
+                         "fp32 output)", launch_ms=round(ms, 4), flop_per_launch=flop, bytes_per_launch=int(nbytes),
+                  mfma_frac=round(flop / s / 1e12 / peak_tflops, 4), hbm_frac=round(nbytes / s / 1e9 / PEAK_HBM_GBPS, 4))
+    if t_hbm >= t_mfma:
+        gbps = nbytes / s / 1e9
+        return dict(bound="hbm", achieved=round(gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                    frac=round(gbps / PEAK_HBM_GBPS, 4), traffic=measured_traffic(shape), **common)
+    tf = flop / s / 1e12
+    return dict(bound="mfma", achieved=round(tf, 2), peak=peak_tflops, unit="TFLOP/s", frac=round(tf / peak_tflops, 4),
+                traffic=measured_traffic(shape), **common)
 
 
 def cpu_baseline(shape, inp, tokens: int):
@@ -88,6 +141,9 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0 = by layer)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 3 device copies of 1 GiB each (the known-size kernel that scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not supported "
@@ -95,6 +151,15 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(copy_bytes_read=src.numel() * 4, copy_bytes_written=dst.numel() * 4, copies=3)))
+        return 0
 
     from mixture_experts_layer_aux_amd import _lib as L
     from mixture_experts_layer_aux_amd import workloads as W
@@ -132,9 +197,9 @@ def main() -> int:
     dx = torch.empty(T, d, dtype=f32, device=dev)
     stats = torch.empty(L.MOE_NSTATS, dtype=f32, device=dev)
     # backward scratch owned by the caller (the piecewise calls name every tensor)
-    dYX = torch.empty(A * d, dtype=f32, device=dev)          # dY_perm (act dtype) then dX_perm (fp32)
-    dY_perm = dYX.view(torch.uint8)[: A * d * (2 if ad == torch.bfloat16 else 4)].view(ad).view(A, d)
-    dX_perm = dYX.view(A, d)
+    # dY_perm must outlive the data gradients here: the fc2 weight gradient runs after them
+    dY_perm = torch.empty(A, d, dtype=ad, device=dev)
+    dX_perm = torch.empty(A, d, dtype=f32, device=dev)
     dH = torch.empty(A, 2 * F, dtype=ad, device=dev)
     dw = torch.empty(T, k, dtype=f32, device=dev)
     dlogits = torch.empty(T, E, dtype=f32, device=dev)
@@ -168,8 +233,16 @@ def main() -> int:
         L.unpermute_combine_bwd(cfg, dy, S["Y_perm"], S["row_of"], S["w"], dY_perm, dw, dY_s)
         mark()
         L.grouped_gemm_swiglu_bwd(cfg, S["x_perm"], S["offsets"], Wt["W13"], Wt["W2"], S["H"], S["Act"], dY_perm,
-                                  dH, dX_perm, G["dW13"], G["dW2"], x if Fs else None, Wt["W13s"], Wt["W2s"],
-                                  S.get("H_s"), S.get("Act_s"), dY_s, dH_s, dx_s, G.get("dW13s"), G.get("dW2s"), ws)
+                                  dH, dX_perm, None, None, x if Fs else None, Wt["W13s"], Wt["W2s"],
+                                  S.get("H_s"), S.get("Act_s"), dY_s, dH_s, dx_s, None, None, ws)
+        mark()
+        L.grouped_wgrad(cfg, S["offsets"], E, A, dY_perm, d, S["Act"], F, G["dW2"])
+        mark()
+        L.grouped_wgrad(cfg, S["offsets"], E, A, dH, 2 * F, S["x_perm"], d, G["dW13"])
+        mark()
+        if Fs:
+            L.grouped_wgrad(cfg, None, 1, T, dH_s, 2 * Fs, x, d, G["dW13s"])
+            L.grouped_wgrad(cfg, None, 1, T, dY_s, d, S["Act_s"], Fs, G["dW2s"])
         mark()
         L.router_bwd(cfg, S["logits"], S["idx"], S["w"], dw, S["counts"], 1.0, dlogits)
         mark()
@@ -194,9 +267,10 @@ def main() -> int:
     st = stats.cpu().numpy()
 
     alg = algorithmic(shape)
-    gemm_ms = phase_ms["experts_fwd"] + phase_ms["experts_bwd"]
+    gemm_ms = sum(phase_ms[p] for p in GEMM_PHASES)
     gemm_tflops = alg["grouped_gemm_flop"] / (gemm_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if shape.act == "bf16" else PEAK_FP32_TFLOPS
+    roof = roofline(alg, phase_ms[ROOFLINE_PHASE], peak, shape)
 
     def hbm(p, key):
         gbps = alg[key] / (phase_ms[p] * 1e-3) / 1e9
@@ -219,10 +293,10 @@ def main() -> int:
         data="synthetic (seeded generator, random-init weights)",
         config=dict(workload=shape.name, T=T, d=d, E=E, k=k, F=F, Fs=Fs, score=shape.score,
                     bias=shape.bias, aux_coeff=shape.aux_coeff, parallelism="single GPU"),
-        roofline=dict(kernel="grouped expert GEMMs (bf16 MFMA, all expert projections of fwd + bwd)",
-                      bound="mfma", achieved=round(gemm_tflops, 2), peak=peak, unit="TFLOP/s",
-                      frac=round(gemm_tflops / peak, 4), traffic=None,
-                      flop_per_step=alg["grouped_gemm_flop"], ms_per_step=round(gemm_ms, 3)),
+        roofline=roof,
+        grouped_gemm=dict(kernels="every expert projection of fwd + bwd (routed and shared)",
+                          flop_per_step=alg["grouped_gemm_flop"], ms_per_step=round(gemm_ms, 3),
+                          tflops=round(gemm_tflops, 2), peak=peak, frac=round(gemm_tflops / peak, 4)),
         layer_tflops=round(layer_flop / (ms_step * 1e-3) / 1e12, 2),
         phases_ms={p: round(v, 4) for p, v in phase_ms.items()},
         hbm_phases=dict(router=hbm("router", "router_bytes"), permute=hbm("permute", "permute_bytes"),
@@ -235,7 +309,7 @@ def main() -> int:
                   mean_count=T * k / E),
     )
     if not args.no_cpu_baseline:
-        tokens = args.cpu_tokens or {1: 128, 2: 8192, 3: 24, 4: 1024, 5: 256}[args.config]
+        tokens = args.cpu_tokens or {1: 128, 2: 8192, 3: 48, 4: 1024, 5: 256}[args.config]
         out["cpu_baseline"] = cpu_baseline(shape, inp, min(tokens, T))
     print(json.dumps(out), flush=True)
     return 0

@@ -204,13 +204,28 @@ moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const float* dy,
  *   dW2[e] = dY^T Act;  dX = dH W13[e];  dW13[e] = dH^T X.
  * dX_perm (fp32) may alias dY_perm when the buffer holds A*d fp32 values (dY_perm is
  * consumed before dX_perm is written).  dH [A, 2F] and dH_s [T, 2Fs] (act dtype) are
- * outputs too.  dx_s [T, d] fp32 receives the shared expert's input gradient. */
+ * outputs too.  dx_s [T, d] fp32 receives the shared expert's input gradient.
+ * dW13 and dW2 may both be NULL (then dW13s and dW2s must be NULL too): only the data
+ * gradients are computed, and the weight gradients can follow from moe_grouped_wgrad. */
 moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
                                          const void* W13, const void* W2, const void* H, const void* Act,
                                          const void* dY_perm, void* dH, void* dX_perm, void* dW13, void* dW2,
                                          const void* x, const void* W13s, const void* W2s, const void* H_s,
                                          const void* Act_s, const void* dY_s, void* dH_s, void* dx_s,
                                          void* dW13s, void* dW2s, void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped weight gradient (the expert weight gradients of [HB] §3.4's FFN, by the chain
+ * rule): for each group g over its rows [offsets[g], offsets[g+1]),
+ *   dW[g] = dY_g^T X_g,   fp32 accumulation, fp32 output (overwritten).
+ * dY [rows, N] and X [rows, K] in the act dtype, row-major; dW [groups, N, K] fp32.
+ * The routed experts: (dH, x_perm) -> dW13 with N = 2F, K = d, and (dY_perm, Act) -> dW2
+ * with N = d, K = F.  offsets NULL: one group over rows [0, rows) (the shared expert, on
+ * all T tokens).  A group with no rows gets exact zeros.  offsets[groups] <= rows is the
+ * caller's promise (device data is not read on the host).  One kernel launch.
+ * Errors: groups outside [1, 4096], groups != 1 without offsets, rows outside [0, 2^31),
+ * N or K not a positive multiple of 64 -> MOE_ERR_INVALID_ARG. */
+moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, int32_t groups, int64_t rows,
+                               const void* dY, int32_t N, const void* X, int32_t K, float* dW, void* stream);
 
 /* Unpermute-reduce: dx[t] = sum_j dX_perm[row_of[t, j]] (+ dx_s[t]) (+ dx_r[t]),
  * fp32 accumulation in that order.  All fp32; dx_s and dx_r may be NULL. */

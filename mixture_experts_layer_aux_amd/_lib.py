@@ -24,7 +24,7 @@ MOE_NSTATS = 4
 EXPORTED = (
     "moe_status_string", "moe_last_error", "moe_validate", "moe_workspace_size", "moe_gate_logits",
     "moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu", "moe_unpermute_combine", "moe_layer_fwd",
-    "moe_unpermute_combine_bwd", "moe_grouped_gemm_swiglu_bwd", "moe_permute_bwd", "moe_router_bwd",
+    "moe_unpermute_combine_bwd", "moe_grouped_gemm_swiglu_bwd", "moe_grouped_wgrad", "moe_permute_bwd", "moe_router_bwd",
     "moe_gate_logits_bwd", "moe_layer_bwd",
 )
 
@@ -219,6 +219,17 @@ def grouped_gemm_swiglu_bwd(cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, 
         _P(_ptr(dW13s, torch.float32, 2 * Fs * d, "dW13s")), _P(_ptr(dW2s, torch.float32, d * Fs, "dW2s")), _P(wp),
         ctypes.c_size_t(wn),
         _P(_stream(stream))))
+
+
+def grouped_wgrad(cfg, offsets, groups, rows, dY, N, X, K, dW, stream=None):
+    """dW[g] = dY_g^T X_g per group of rows (offsets None: one group of `rows` rows)."""
+    ad = act_dtype(cfg)
+    if offsets is not None and offsets.numel() != groups + 1:
+        raise ValueError(f"offsets: expected {groups + 1} entries, got {offsets.numel()}")
+    _check(load().moe_grouped_wgrad(
+        ctypes.byref(cfg), _P(_ptr(offsets, torch.int32, groups + 1, "offsets")), ctypes.c_int32(groups),
+        ctypes.c_int64(rows), _P(_ptr(dY, ad, rows * N, "dY")), ctypes.c_int32(N), _P(_ptr(X, ad, rows * K, "X")),
+        ctypes.c_int32(K), _P(_ptr(dW, torch.float32, groups * N * K, "dW")), _P(_stream(stream))))
 
 
 def permute_bwd(cfg, dX_perm, row_of, dx_s, dx_r, dx, stream=None):

@@ -208,6 +208,20 @@ moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const in
   return MOE_OK;
 }
 
+// dW[g] = dY_g^T X_g over the rows of each group (reduction-ragged); fp32 output.
+moe_status_t run_wgrad(int act_dtype, const int32_t* off, int G, int64_t rows, const void* dY, int N, const void* X,
+                       int K, void* dW, hipStream_t s) {
+  GemmDesc w{};
+  w.a_major = MN_MAJOR; w.b_major = MN_MAJOR; w.ragged = RAGGED_K; w.epi = EPI_STORE;
+  w.a_type = w.b_type = act_dtype;
+  w.c_type = MOE_F32;
+  w.M = N; w.N = K;
+  w.A = dY; w.lda = N; w.B = X; w.ldb = K;
+  w.C = dW; w.ldc = K; w.c_gstride = int64_t{1} * N * K;
+  w.offsets = off; w.G = G; w.range_end = static_cast<int>(rows);
+  return act_dtype == MOE_BF16 ? launch_gemm_mfma(w, nullptr, s) : launch_gemm_fma(w, s);
+}
+
 moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const int32_t* offsets, const void* W13,
                              const void* W2, const void* H, const void* Act, const void* dY_perm, void* dH,
                              void* dX_perm, void* dW13, void* dW2, const void* x, const void* W13s, const void* W2s,
@@ -239,15 +253,6 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
     d2.B = w2; d2.ldb = F; d2.b_gstride = shared ? 0 : int64_t{1} * c.d * F;
     d2.Hin = h; d2.ldh = 2 * F;
     d2.offsets = off; d2.G = G; d2.range_end = c.T; d2.rows_upper = A;
-    // (2) fc2 weight gradient: dW2 = dY^T Act (reduction over the expert's rows)
-    GemmDesc w2g{};
-    w2g.a_major = MN_MAJOR; w2g.b_major = MN_MAJOR; w2g.ragged = RAGGED_K; w2g.epi = EPI_STORE;
-    w2g.a_type = w2g.b_type = et;
-    w2g.c_type = MOE_F32;
-    w2g.M = c.d; w2g.N = F;
-    w2g.A = dY; w2g.lda = c.d; w2g.B = act; w2g.ldb = F;
-    w2g.C = dw2; w2g.ldc = F; w2g.c_gstride = int64_t{1} * c.d * F;
-    w2g.offsets = off; w2g.G = G; w2g.range_end = c.T;
     // (3) fc1 data gradient: dX = dH W13
     GemmDesc d1{};
     d1.a_major = K_MAJOR; d1.b_major = MN_MAJOR; d1.ragged = RAGGED_M; d1.epi = EPI_STORE;
@@ -258,31 +263,21 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
     d1.B = w13; d1.ldb = c.d; d1.b_gstride = shared ? 0 : int64_t{2} * F * c.d;
     d1.C = dX; d1.ldc = c.d;
     d1.offsets = off; d1.G = G; d1.range_end = c.T; d1.rows_upper = A;
-    // (4) fc1 weight gradient: dW13 = dH^T X
-    GemmDesc w1g{};
-    w1g.a_major = MN_MAJOR; w1g.b_major = MN_MAJOR; w1g.ragged = RAGGED_K; w1g.epi = EPI_STORE;
-    w1g.a_type = w1g.b_type = et;
-    w1g.c_type = MOE_F32;
-    w1g.M = 2 * F; w1g.N = c.d;
-    w1g.A = dh; w1g.lda = 2 * F; w1g.B = X; w1g.ldb = c.d;
-    w1g.C = dw13; w1g.ldc = c.d; w1g.c_gstride = int64_t{2} * F * c.d;
-    w1g.offsets = off; w1g.G = G; w1g.range_end = c.T;
     if (et == MOE_BF16) {
       d2.epi = EPI_SWIGLU_BWD;
       d2.C = dh; d2.ldc = 2 * F;
       MOE_TRY(launch_gemm_mfma(d2, sched, s));
-      MOE_TRY(launch_gemm_mfma(w2g, sched, s));
-      MOE_TRY(launch_gemm_mfma(d1, sched, s));
-      MOE_TRY(launch_gemm_mfma(w1g, sched, s));
     } else {
       d2.epi = EPI_STORE;
       d2.C = dact; d2.ldc = F;
       MOE_TRY(launch_gemm_fma(d2, s));
       MOE_TRY(launch_swiglu_bwd_elementwise(static_cast<const float*>(h), dact, static_cast<float*>(dh), rows, F, s));
-      MOE_TRY(launch_gemm_fma(w2g, s));
-      MOE_TRY(launch_gemm_fma(d1, s));
-      MOE_TRY(launch_gemm_fma(w1g, s));
     }
+    // (2) fc2 weight gradient dW2 = dY^T Act, before dX may overwrite an aliased dY
+    if (dw2) MOE_TRY(run_wgrad(et, off, G, rows, dY, c.d, act, F, dw2, s));
+    MOE_TRY(et == MOE_BF16 ? launch_gemm_mfma(d1, sched, s) : launch_gemm_fma(d1, s));
+    // (4) fc1 weight gradient dW13 = dH^T X
+    if (dw13) MOE_TRY(run_wgrad(et, off, G, rows, dh, 2 * F, X, c.d, dw13, s));
   }
   return MOE_OK;
 }
@@ -444,15 +439,31 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
                                          void* dW2s, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED16(x_perm); MOE_NEED(offsets); MOE_NEED16(W13); MOE_NEED16(W2); MOE_NEED16(H); MOE_NEED16(Act);
-  MOE_NEED16(dY_perm); MOE_NEED16(dH); MOE_NEED16(dX_perm); MOE_NEED16(dW13); MOE_NEED16(dW2); MOE_NEED(ws);
+  MOE_NEED16(dY_perm); MOE_NEED16(dH); MOE_NEED16(dX_perm); MOE_NEED(ws);
+  const bool wgrad = dW13 || dW2;
+  if (wgrad) { MOE_NEED16(dW13); MOE_NEED16(dW2); }
   if (cfg->Fs) {
     MOE_NEED16(x); MOE_NEED16(W13s); MOE_NEED16(W2s); MOE_NEED16(H_s); MOE_NEED16(Act_s); MOE_NEED16(dY_s);
-    MOE_NEED16(dH_s); MOE_NEED16(dx_s); MOE_NEED16(dW13s); MOE_NEED16(dW2s);
+    MOE_NEED16(dH_s); MOE_NEED16(dx_s);
+    if (wgrad) { MOE_NEED16(dW13s); MOE_NEED16(dW2s); }
+    else if (dW13s || dW2s) return fail(MOE_ERR_INVALID_ARG, "shared weight gradients given without routed ones");
   }
   const BwdWs bw = carve_bwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, bw.bytes, __func__));
   return run_experts_bwd(*cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, dX_perm, dW13, dW2, x, W13s, W2s, H_s,
                          Act_s, dY_s, dH_s, dx_s, dW13s, dW2s, bw.sched, bw.dact, S(stream));
+}
+
+moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, int32_t groups, int64_t rows,
+                               const void* dY, int32_t N, const void* X, int32_t K, float* dW, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED16(dY); MOE_NEED16(X); MOE_NEED16(dW);
+  if (groups < 1 || groups > 4096) return fail(MOE_ERR_INVALID_ARG, "groups must be in [1, 4096]");
+  if (!offsets && groups != 1) return fail(MOE_ERR_INVALID_ARG, "without offsets there is exactly one group");
+  if (rows < 0 || rows >= (int64_t{1} << 31)) return fail(MOE_ERR_INVALID_ARG, "rows must be in [0, 2^31)");
+  if (N < 64 || K < 64 || N % 64 || K % 64) return fail(MOE_ERR_INVALID_ARG, "N and K must be positive multiples of 64");
+  if (static_cast<int64_t>(N) * K * 4 >= (int64_t{1} << 40)) return fail(MOE_ERR_INVALID_ARG, "dW group too large");
+  return run_wgrad(cfg->act_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream));
 }
 
 moe_status_t moe_permute_bwd(const moe_config_t* cfg, const float* dX_perm, const int32_t* row_of, const float* dx_s,

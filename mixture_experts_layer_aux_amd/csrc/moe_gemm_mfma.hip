@@ -53,6 +53,7 @@ constexpr int WAVES_M = 2, WAVES_N = 4, NWAVES = WAVES_M * WAVES_N, NTHR = 64 * 
 constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, NI = WTM / 32, NJ = WTN / 32;
 constexpr int KCH = BK / 8;                         // 16-byte chunks per K-contiguous row
 constexpr int DMA_PER_WAVE = (BK / 2) / NWAVES;     // one-KB blocks per operand per stage per wave
+constexpr int NDMA = 2 * DMA_PER_WAVE;               // LDS-DMA instructions per wave per stage
 constexpr int TILE = 256 * BK;          // bf16 elements of one operand tile of one stage
 constexpr int STAGE_ELEMS = 2 * TILE;   // A then B
 constexpr int BLOCK_ELEMS = 512;        // one wave-wide 16-byte-per-lane LDS DMA = 1 KB
@@ -219,10 +220,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
     }
   }
   const int a_rows = min(BM, row_end - row_begin);  // K-major A rows that exist (RAGGED_M)
-  auto issue_stage = [&](int st) {
+  auto stage_rsrc = [&](int st, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rb) {
     const int k0 = k_begin + st * BK;
-    uint16_t* dst = lds + (st % STAGES) * STAGE_ELEMS;
-    __amdgpu_buffer_rsrc_t ra, rb;
     if (AMAJ == K_MAJOR)
       ra = make_rsrc(p.A + static_cast<int64_t>(row_begin) * p.lda + k0,
                      (a_rows - 1) * static_cast<int>(p.lda) * 2 + BK * 2);
@@ -232,14 +231,24 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
       rb = make_rsrc(Bg + k0, p.b_rows_bytes - k0 * 2);
     else
       rb = make_rsrc(Bg + static_cast<int64_t>(k0) * p.ldb, min(BK, k_end - k0) * static_cast<int>(p.ldb) * 2);
-#pragma unroll
-    for (int q = 0; q < DMA_PER_WAVE; ++q)
+  };
+  // Stage st, DMA instruction q of this wave: q < DMA_PER_WAVE moves a block of A, the
+  // rest blocks of B.
+  auto issue_one = [&](int st, int q, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb) {
+    uint16_t* dst = lds + (st % STAGES) * STAGE_ELEMS;
+    if (q < DMA_PER_WAVE)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(dst + (wave * DMA_PER_WAVE + q) * BLOCK_ELEMS), 16,
                                                voffA[q], 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (lds_void_t*)(dst + TILE + (wave * DMA_PER_WAVE + q - DMA_PER_WAVE) * BLOCK_ELEMS), 16,
+          voffB[q - DMA_PER_WAVE], 0, 0, 0);
+  };
+  auto issue_stage = [&](int st) {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    stage_rsrc(st, ra, rb);
 #pragma unroll
-    for (int q = 0; q < DMA_PER_WAVE; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dst + TILE + (wave * DMA_PER_WAVE + q) * BLOCK_ELEMS),
-                                               16, voffB[q], 0, 0, 0);
+    for (int q = 0; q < NDMA; ++q) issue_one(st, q, ra, rb);
   };
 
   // ------------------------------------------------------------ LDS -> fragments
@@ -281,11 +290,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
   for (int st = 0; st < STAGES - 1; ++st)
     if (st < nk) issue_stage(st);
   for (int it = 0; it < nk; ++it) {
-    // stage `it` has landed once at most (stages issued after it) * 8 loads are pending
+    // stage `it` has landed once at most (stages issued after it) * NDMA loads of this wave
+    // are pending
     const int ahead = min(STAGES - 2, nk - 1 - it);
-    wait_vm(ahead * 2 * DMA_PER_WAVE);
+    wait_vm(ahead * NDMA);
     block_barrier();  // every wave's part of stage `it` is in LDS; stage it-1 is consumed
-    if (it + STAGES - 1 < nk) issue_stage(it + STAGES - 1);
+    if (it + STAGES - 1 < nk) issue_stage(it + STAGES - 1);  // into the slot stage it-1 freed
     const uint16_t* As = lds + (it % STAGES) * STAGE_ELEMS;
     const uint16_t* Bs = As + TILE;
 #pragma unroll

@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_declared_entry_point():
     lib = L.load()
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(L.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -118,6 +118,20 @@ def test_entry_points_reject_bad_arguments_before_launching():
     assert st == L.MOE_ERR_INVALID_ARG and b"Wg" in lib.moe_last_error()
     st = lib.moe_router_bwd(ctypes.byref(cfg), fake, fake, fake, fake, nul, ctypes.c_float(1.0), fake, s)
     assert st == L.MOE_ERR_INVALID_ARG and b"counts" in lib.moe_last_error()
+    # grouped weight gradient: group count, offsets and sizes are checked on the host
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(0), i64(64), fake, i32(64), fake, i32(64), fake, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"groups" in lib.moe_last_error()
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), nul, i32(2), i64(64), fake, i32(64), fake, i32(64), fake, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"one group" in lib.moe_last_error()
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(64), fake, i32(96), fake, i32(64), fake, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"multiples of 64" in lib.moe_last_error()
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(-1), fake, i32(64), fake, i32(64), fake, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"rows" in lib.moe_last_error()
+    # expert backward: routed weight gradients are both given or both NULL
+    st = lib.moe_grouped_gemm_swiglu_bwd(ctypes.byref(cfg), *([fake] * 9), fake, nul, *([nul] * 10), fake,
+                                         ctypes.c_size_t(1 << 40), s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"dW2" in lib.moe_last_error()
 
 
 def test_status_strings():

@@ -147,7 +147,24 @@ def test_grouped_experts_forward_and_backward(cid):
     dW13s, dW2s = (e32(2 * Fs, d), e32(d, Fs)) if Fs else (None, None)
     L.grouped_gemm_swiglu_bwd(cfg, x_perm, off, W13, W2, H, Act, dYp, dH, dXp, dW13, dW2, x if Fs else None, W13s,
                               W2s, H_s, Act_s, dy if Fs else None, dH_s, dx_s, dW13s, dW2s, ws)
+    # the same backward as data gradients only, then the four weight gradients through
+    # moe_grouped_wgrad: the same kernels on the same inputs, so the same bits
+    dH2, dXp2 = e(A, 2 * F), e32(A, d)
+    dH2_s, dx2_s = (e(T, 2 * Fs), e32(T, d)) if Fs else (None, None)
+    L.grouped_gemm_swiglu_bwd(cfg, x_perm, off, W13, W2, H, Act, dYp, dH2, dXp2, None, None, x if Fs else None, W13s,
+                              W2s, H_s, Act_s, dy if Fs else None, dH2_s, dx2_s, None, None, ws)
+    sW13, sW2 = e32(E, 2 * F, d), e32(E, d, F)
+    L.grouped_wgrad(cfg, off, E, A, dH2, 2 * F, x_perm, d, sW13)
+    L.grouped_wgrad(cfg, off, E, A, dYp, d, Act, F, sW2)
+    split = [(dH, dH2), (dXp, dXp2), (dW13, sW13), (dW2, sW2)]
+    if Fs:
+        sW13s, sW2s = e32(2 * Fs, d), e32(d, Fs)
+        L.grouped_wgrad(cfg, None, 1, T, dH2_s, 2 * Fs, x, d, sW13s)
+        L.grouped_wgrad(cfg, None, 1, T, dy, d, Act_s, Fs, sW2s)
+        split += [(dH_s, dH2_s), (dx_s, dx2_s), (dW13s, sW13s), (dW2s, sW2s)]
     torch.cuda.synchronize()
+    for i, (a, b) in enumerate(split):
+        assert torch.equal(a, b), f"split backward differs from the fused one (output {i})"
     tl = tol(shape)
     xp = o["x"][p.token_of]
     dYo = f64(dYp_np, shape.act)
