@@ -46,7 +46,9 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int BM = 256, BN = 256, BK = 64, STAGES = 2;
+constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
+// Main-loop schedule: wave groups alternating memory and compute phases (see the loop).
+constexpr bool PING_PONG = true;
 // Waves of a workgroup: WAVES_M x WAVES_N, each owning a (BM / WAVES_M) x (BN / WAVES_N)
 // sub-tile as (BM / WAVES_M / 32) x (BN / WAVES_N / 32) accumulators of 32 x 32.
 constexpr int WAVES_M = 2, WAVES_N = 4, NWAVES = WAVES_M * WAVES_N, NTHR = 64 * NWAVES;
@@ -100,6 +102,11 @@ __device__ __forceinline__ void wait_vm(int n) {
   else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);
   else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F74);
   else __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
+// Waits until this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0; vmcnt (63) and expcnt (7) at their maxima
   asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ void block_barrier() {
@@ -169,8 +176,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
     k_end = p.K;
   } else {
     // Reduction-ragged (weight gradient): a tile's work grows with its expert's rows, so
-    // every expert's tiles are split into 8 equal runs, one per XCD; inside a run the
-    // column tile varies fastest, so the tiles sharing a slice of A sit together on one L2.
+    // every expert's tiles are split into 8 equal runs, one per XCD.  The runs follow a
+    // blocked order: bands of WG_BAND row tiles, walked column by column with the row tile
+    // fastest, so the ~32 tiles one XCD holds at a time span WG_BAND slices of A and about
+    // 8 of B (instead of 1-2 of A and every slice of B), and L2 serves the rest.
+    constexpr int WG_BAND = 4;
     const int per = p.nM * p.nN;
     const int run = (per + 7) >> 3;
     const int h = blockIdx.x;
@@ -178,8 +188,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
     grp = q / run;
     const int local = (h & 7) * run + (q - grp * run);
     if (grp >= p.G || local >= per) return;
-    mt = local / p.nN;
-    nt = local - mt * p.nN;
+    const int band = local / (WG_BAND * p.nN);
+    const int rem = local - band * WG_BAND * p.nN;
+    const int bh = min(WG_BAND, p.nM - band * WG_BAND);
+    nt = rem / bh;
+    mt = band * WG_BAND + (rem - nt * bh);
     row_begin = mt * BM;
     row_end = p.M;
     k_begin = p.offsets ? p.offsets[grp] : 0;
@@ -285,32 +298,90 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
-  // prologue: stages 0 .. STAGES-2 in flight
+  if (PING_PONG) {
+    // Two wave groups, waves 0-3 (rows 0-127 of the tile) and 4-7 (rows 128-255); wave w
+    // and w+4 share a SIMD.  Every stage is a memory phase (read the stage's fragments
+    // from LDS into registers, issue this wave's DMA part of stage it+D, wait for its part
+    // of stage it+1) and a compute phase (MFMAs from registers only), each ended by a
+    // workgroup barrier.  The second group runs one phase behind the first, so on every
+    // SIMD one wave issues MFMAs while the other is in its memory phase, and a wave stalled
+    // on a DMA issue no longer idles the matrix core.  Slot reuse: stage it+D overwrites
+    // the slot of stage it-1, which both groups finished reading one barrier earlier.
+    constexpr int D = STAGES - 1;
+    const bool late = wm == 1;
 #pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
-    if (st < nk) issue_stage(st);
-  for (int it = 0; it < nk; ++it) {
-    // stage `it` has landed once at most (stages issued after it) * NDMA loads of this wave
-    // are pending
-    const int ahead = min(STAGES - 2, nk - 1 - it);
-    wait_vm(ahead * NDMA);
-    block_barrier();  // every wave's part of stage `it` is in LDS; stage it-1 is consumed
-    if (it + STAGES - 1 < nk) issue_stage(it + STAGES - 1);  // into the slot stage it-1 freed
-    const uint16_t* As = lds + (it % STAGES) * STAGE_ELEMS;
-    const uint16_t* Bs = As + TILE;
+    for (int st = 0; st < D; ++st)
+      if (st < nk) issue_stage(st);
+    wait_vm(max(0, min(D, nk) - 1) * NDMA);
+    block_barrier();
+    if (late) block_barrier();
+    for (int it = 0; it < nk; ++it) {
+      const uint16_t* As = lds + (it % STAGES) * STAGE_ELEMS;
+      const uint16_t* Bs = As + TILE;
+      bf16x8_t fa[BK / 16][NI], fb[BK / 16][NJ];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t fa[NI], fb[NJ];
+      for (int ks = 0; ks < BK / 16; ++ks) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) fa[i] = frag(As, AMAJ, wm * WTM + i * 32, ks);
+        for (int i = 0; i < NI; ++i) fa[ks][i] = frag(As, AMAJ, wm * WTM + i * 32, ks);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) fb[j] = frag(Bs, BMAJ, wn * WTN + j * 32, ks);
-      // B fragment first: the accumulator comes out transposed (see the epilogue)
+        for (int j = 0; j < NJ; ++j) fb[ks][j] = frag(Bs, BMAJ, wn * WTN + j * 32, ks);
+      }
+      if (it + D < nk) issue_stage(it + D);
+      wait_lgkm0();  // fragments in registers before the slot may be refilled
+      wait_vm(max(0, min(it + D, nk - 1) - (it + 1)) * NDMA);  // own part of stage it+1 landed
+      __builtin_amdgcn_sched_barrier(0);
+      block_barrier();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+      for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      block_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!late) block_barrier();
+  } else {
+    // prologue: stages 0 .. STAGES-2 in flight
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+      if (st < nk) issue_stage(st);
+    for (int it = 0; it < nk; ++it) {
+      // stage `it` has landed once at most (stages issued after it) * NDMA loads of this
+      // wave are pending
+      const int ahead = min(STAGES - 2, nk - 1 - it);
+      wait_vm(ahead * NDMA);
+      block_barrier();  // every wave's part of stage `it` is in LDS; stage it-1 is consumed
+      if (it + STAGES - 1 < nk) issue_stage(it + STAGES - 1);  // into the slot stage it-1 freed
+      const uint16_t* As = lds + (it % STAGES) * STAGE_ELEMS;
+      const uint16_t* Bs = As + TILE;
+      // Fragments are double-buffered over the 16-wide substeps: the reads of substep ks+1
+      // are in flight while the MFMAs of substep ks run.
+      bf16x8_t fa[2][NI], fb[2][NJ];
+      auto load_frags = [&](int ks, bf16x8_t* a, bf16x8_t* b) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) a[i] = frag(As, AMAJ, wm * WTM + i * 32, ks);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) b[j] = frag(Bs, BMAJ, wn * WTN + j * 32, ks);
+      };
+      load_frags(0, fa[0], fb[0]);
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        if (ks + 1 < BK / 16) load_frags(ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        // keep the scheduler from sinking these reads below the MFMAs (it would, to save
+        // registers, and expose the LDS latency before every MFMA pair)
+        __builtin_amdgcn_sched_barrier(0);
+        // B fragment first: the accumulator comes out transposed (see the epilogue)
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
