@@ -8,16 +8,21 @@
 // Design (per workgroup: 512 threads = 8 waves in a 2 x 4 grid):
 //   * 256 x 256 output tile, each wave a 128 x 64 sub-tile held as 4 x 2 accumulators of
 //     v_mfma_f32_32x32x16_bf16 (128 fp32 per lane);
-//   * operands go from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane), 64
-//     K values per stage, double-buffered (2 stages of 64 KB): the next stage is in flight
-//     while the current one is multiplied, and no VGPRs stage the data;
+//   * operands go from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane), 32
+//     K values per stage, through a ring of 4 stages (128 KB): three stages are in flight
+//     while one is read, and no VGPRs stage the data;
+//   * ping-pong: waves 0-3 and 4-7 (wave w and w+4 share a SIMD) alternate a memory phase
+//     (the stage's fragments into registers, this wave's DMA part of a later stage, waits)
+//     and a compute phase (MFMAs only), one workgroup barrier apart and one phase out of
+//     step, so the matrix core of every SIMD is fed while the other wave is stalled on LDS
+//     or on issuing DMA;
 //   * buffer descriptors bound every load: rows past the end of a ragged reduction (weight
 //     gradient) and past the end of an operand read as zeros, so no tail handling exists
 //     in the loop;
-//   * operands contiguous in K are stored [rows][64 k] with the 16-byte chunk index XORed
-//     by (r ^ (r >> 3)) & 7, and read with ds_read_b128; operands contiguous in rows (the
+//   * operands contiguous in K are stored [rows][32 k] with the 16-byte chunk index XORed
+//     by (r >> 2) & 3, and read with ds_read_b128; operands contiguous in rows (the
 //     weights of the data gradients, both operands of the weight gradients) are stored
-//     as loaded, [64 k][256 rows] with the chunk index XORed by 4 * (k & 3), and
+//     as loaded, [32 k][256 rows] with the chunk index XORed by 4 * (k & 3), and
 //     read with the gfx950 transposing ds_read_b64_tr_b16 (a 16-lane group reads 4 k-rows
 //     of 16 columns and gets back, per lane, one column's 4 k values), so no operand is
 //     ever transposed through registers;
@@ -31,7 +36,7 @@
 //     Row-ragged launches map h to tile (h mod 8) * ceil(tiles / 8) + h / 8, so each XCD
 //     walks a contiguous run of tiles (expert, column tile, row tile) and tiles sharing a
 //     weight or activation tile run together on one L2; reduction-ragged launches give
-//     each XCD one eighth of every expert's tiles;
+//     each XCD one eighth of every expert's tiles, walked in bands of 4 row tiles;
 //   * fused epilogues: SwiGLU (forward: H in fp32 and Act in bf16 from the same
 //     accumulators, the gate and up rows of W13 interleaved per 32-row block of the B
 //     tile) and the SwiGLU backward (reads the saved fp32 H, writes dH in bf16).

@@ -17,8 +17,10 @@ namespace moe {
 
 namespace {
 
-constexpr int kRouterWaves = 4;
-constexpr int kRouterTokensPerBlock = 64;   // 16 tokens per wave
+constexpr int kRouterWaves = 8;
+// 64 tokens per block (8 per wave): a block's expert histogram is also the permute's
+// chunk histogram, so this must equal the permute chunk.
+constexpr int kRouterTokensPerBlock = 64;
 
 struct Best {
   double key;
@@ -31,7 +33,7 @@ __device__ __forceinline__ bool better(double ka, int ea, double kb, int eb) {
 }
 
 template <int EPL>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(64 * kRouterWaves) void router_topk_kernel(const float* __restrict__ logits,
                                                           const float* __restrict__ expert_bias,
                                                           int T, int E, int k, int score, float scaling,
                                                           int32_t* __restrict__ idx, float* __restrict__ w,
@@ -156,20 +158,22 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   }
 }
 
-// Column sums of the per-block partials, in block order.  256 threads = 64 experts x 4
-// interleaved block subsets; the 4 subset sums are then added in a fixed order.
-__global__ __launch_bounds__(256) void router_finalize_kernel(const int32_t* __restrict__ cnt_part,
-                                                              const float* __restrict__ prob_part, int nblk,
-                                                              int E, int32_t* __restrict__ counts,
-                                                              float* __restrict__ prob_sum) {
-  __shared__ int sc[4][64];
-  __shared__ float sp[4][64];
+// Column sums of the per-block partials in a fixed order: 1024 threads = 64 experts x 16
+// interleaved block subsets, each subset summed in block order, then the 16 subset sums
+// added by a fixed pairwise tree.
+__global__ __launch_bounds__(1024) void router_finalize_kernel(const int32_t* __restrict__ cnt_part,
+                                                               const float* __restrict__ prob_part, int nblk,
+                                                               int E, int32_t* __restrict__ counts,
+                                                               float* __restrict__ prob_sum) {
+  constexpr int R = 16;
+  __shared__ int sc[R][64];
+  __shared__ float sp[R][64];
   const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
   const int e = blockIdx.x * 64 + c;
   int ci = 0;
   float pf = 0.0f;
   if (e < E) {
-    for (int b = r; b < nblk; b += 4) {
+    for (int b = r; b < nblk; b += R) {
       ci += cnt_part[static_cast<int64_t>(b) * E + e];
       if (prob_part) pf += prob_part[static_cast<int64_t>(b) * E + e];
     }
@@ -177,9 +181,16 @@ __global__ __launch_bounds__(256) void router_finalize_kernel(const int32_t* __r
   sc[r][c] = ci;
   sp[r][c] = pf;
   __syncthreads();
+  for (int h = R / 2; h > 0; h >>= 1) {
+    if (r < h) {
+      sc[r][c] += sc[r + h][c];
+      sp[r][c] += sp[r + h][c];
+    }
+    __syncthreads();
+  }
   if (r == 0 && e < E) {
-    counts[e] = sc[0][c] + sc[1][c] + sc[2][c] + sc[3][c];
-    if (prob_part && prob_sum) prob_sum[e] = ((sp[0][c] + sp[1][c]) + sp[2][c]) + sp[3][c];
+    counts[e] = sc[0][c];
+    if (prob_part && prob_sum) prob_sum[e] = sp[0][c];
   }
 }
 
@@ -336,12 +347,17 @@ moe_status_t launch_router_topk(const moe_config_t& c, const float* logits, cons
                                 int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* stats,
                                 int32_t* cnt_part, float* prob_part, hipStream_t s) {
   const int nblk = static_cast<int>(router_num_blocks(c.T));
+  if (nblk != permute_num_chunks(c.T)) return fail(MOE_ERR_UNSUPPORTED, "router blocks differ from permute chunks");
   const size_t shm = static_cast<size_t>(c.E) * sizeof(int) + static_cast<size_t>(kRouterWaves) * c.E * sizeof(float);
   const int epl = router_epl(c.E);
   float* pp = c.score == MOE_SOFTMAX ? prob_part : nullptr;
 #define MOE_ROUTER_CASE(N)                                                                              \
   case N:                                                                                               \
-    router_topk_kernel<N><<<nblk, 256, shm, s>>>(logits, expert_bias, c.T, c.E, c.k, c.score,          \
+    if (shm > 65536 &&                                                                                  \
+        hipFuncSetAttribute(reinterpret_cast<const void*>(router_topk_kernel<N>),                       \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)) != hipSuccess) \
+      return fail(MOE_ERR_HIP, "router: cannot raise the LDS limit to %zu bytes", shm);                 \
+    router_topk_kernel<N><<<nblk, 64 * kRouterWaves, shm, s>>>(logits, expert_bias, c.T, c.E, c.k, c.score,          \
                                                  c.routed_scaling, idx, w, cnt_part, pp);               \
     break;
   switch (epl) {
@@ -355,7 +371,7 @@ moe_status_t launch_router_topk(const moe_config_t& c, const float* logits, cons
       return fail(MOE_ERR_UNSUPPORTED, "router: E=%d too large", c.E);
   }
 #undef MOE_ROUTER_CASE
-  router_finalize_kernel<<<static_cast<int>(ceil_div(c.E, 64)), 256, 0, s>>>(cnt_part, pp, nblk, c.E, counts,
+  router_finalize_kernel<<<static_cast<int>(ceil_div(c.E, 64)), 1024, 0, s>>>(cnt_part, pp, nblk, c.E, counts,
                                                                             c.score == MOE_SOFTMAX ? prob_sum : nullptr);
   if (stats) {
     // for softmax, prob_sum is never NULL here (the C-ABI layer supplies workspace)
