@@ -24,6 +24,8 @@ Readings where the pages leave a step open (the same list is kept with the desig
   * the aux loss uses the full softmax over all E experts as the router probability,
     and counts carry no gradient.
   * the shared expert is ungated and added at weight 1.
+  * fp8 experts: OCP e4m3 codes with one fp32 scale (amax / 448) per 128 x 128 weight
+    block and per token per 128 activation columns; quotient and rounding in fp32.
 """
 from __future__ import annotations
 
@@ -387,6 +389,127 @@ def layer_loss(x, Wg, W13, W2, dy, spec: LayerSpec, bg=None, expert_bias=None,
     """L = sum(dy * y) + daux * aux, the scalar whose gradient layer_backward returns."""
     f = layer_forward(x, Wg, W13, W2, spec, bg=bg, expert_bias=expert_bias, W13s=W13s, W2s=W2s)
     return float(np.sum(_d(dy) * f["y"]) + daux * f["route"]["aux"])
+
+
+# ------------------------------------------------------------------------ fp8 experts
+#
+# The pages give no low-precision recipe for the expert GEMMs ([HB] §3.1 Precision only
+# asks for an fp32 router).  The reading taken for the fp8 layer:
+#   * format: OCP e4m3 (E4M3FN): sign, 4 exponent bits with bias 7, 3 mantissa bits;
+#     the largest finite magnitude is 448 (exponent 15, mantissa 6), there is no infinity;
+#   * one fp32 scale per block (128 x 128 for expert weights, 1 x 128 per token for
+#     activations): scale = amax / 448 evaluated in fp32, or 1 for an all-zero block;
+#   * code = the e4m3 value nearest to v / scale (the quotient in fp32), ties to the even
+#     code, magnitudes above 448 saturated to 448; the sign bit is the sign of v;
+#   * value = decode(code) * scale.
+# Both decisions that produce integers (the quotient and its rounding) are taken in fp32,
+# the precision of the kernel, so that both sides pick the same codes.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_magnitudes() -> np.ndarray:
+    """The 127 non-negative finite e4m3 values, indexed by their codes 0x00..0x7E."""
+    out = np.zeros(127)
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        out[c] = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+_E4M3 = e4m3_magnitudes()
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """uint8 codes (never 0x7F or 0xFF) -> float64 values."""
+    c = np.asarray(codes).astype(np.int64)
+    mag = _E4M3[c & 0x7F]
+    return np.where(c & 0x80, -mag, mag)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Values (exactly representable in fp32) -> e4m3 codes, by the rule above."""
+    v = np.asarray(v, dtype=np.float32).astype(f64)
+    a = np.minimum(np.abs(v), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_E4M3, a, side="left"), 0, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = _E4M3[hi] - a
+    d_lo = a - _E4M3[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == 0.0, 0, code)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_blocks(v, block_rows: int, block_cols: int = 128):
+    """v [R, C] -> (codes uint8 [R, C], scales float32 [R / block_rows, C / block_cols]).
+
+    One scale per block of block_rows x block_cols, by the rule above.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    R, C = v.shape
+    assert R % block_rows == 0 and C % block_cols == 0
+    blocks = np.abs(v).reshape(R // block_rows, block_rows, C // block_cols, block_cols)
+    amax = blocks.max(axis=(1, 3)).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    full = np.repeat(np.repeat(scale, block_rows, axis=0), block_cols, axis=1)
+    return e4m3_encode(v / full), scale
+
+
+def dequantize_blocks(codes, scales, block_rows: int, block_cols: int = 128) -> np.ndarray:
+    """decode(code) * scale in float64."""
+    full = np.repeat(np.repeat(_d(scales), block_rows, axis=0), block_cols, axis=1)
+    return e4m3_decode(codes) * full
+
+
+def layer_forward_fp8(x, Wg, W13q, W13_scale, W2q, W2_scale, spec: "LayerSpec", bg=None,
+                      expert_bias=None) -> Dict[str, object]:
+    """The layer forward with e4m3 expert weights and activations.
+
+    Routing as in layer_forward (fp32-exact logits of the given x).  The expert GEMMs take
+    x quantised per token per 128 columns, the weights given as codes and 128 x 128
+    block scales, and the SwiGLU output quantised per token per 128 columns after a cast
+    to fp32; every product and sum after dequantisation is exact (float64).
+    """
+    x = _d(x)
+    T, d = x.shape
+    logits = gate_logits(x, Wg, bg)
+    r = route(logits, spec, expert_bias)
+    perm = permutation(r["idx"], spec.E)
+    xq, xs = quantize_blocks(x.astype(np.float32), 1)
+    xd = dequantize_blocks(xq, xs, 1)
+    xp = xd[perm.token_of]
+    F = np.shape(W2q[int(r["idx"].ravel()[0])])[1]
+    A = T * spec.k
+    H = np.zeros((A, 2 * F))
+    Act = np.zeros((A, F))
+    Actq = np.zeros((A, F), dtype=np.uint8)
+    Acts = np.ones((A, F // 128), dtype=np.float32)
+    Yp = np.zeros((A, d))
+    for e in range(spec.E):
+        a, b = perm.offsets[e], perm.offsets[e + 1]
+        if b == a:
+            continue
+        w13 = dequantize_blocks(W13q[e], W13_scale[e], 128)
+        w2 = dequantize_blocks(W2q[e], W2_scale[e], 128)
+        H[a:b] = xp[a:b] @ w13.T
+        Act[a:b] = silu(H[a:b, :F]) * H[a:b, F:]
+        Actq[a:b], Acts[a:b] = quantize_blocks(Act[a:b].astype(np.float32), 1)
+        Yp[a:b] = dequantize_blocks(Actq[a:b], Acts[a:b], 1) @ w2.T
+    y = np.einsum("tk,tkd->td", r["w"], Yp[perm.row_of])
+    return dict(logits=logits, route=r, perm=perm, x_q=xq, x_scale=xs, H=H, Act=Act, Act_q=Actq,
+                Act_scale=Acts, Y_perm=Yp, y=y)
+
+
+def router_path_backward(fwd: Dict[str, object], x, Wg, dy, spec: "LayerSpec", daux: float = 1.0):
+    """The backward through the mixing weights only (combine -> router -> gate GEMM), as
+    for a layer whose expert weights are frozen: dw, dlogits, dWg, dbg and the input
+    gradient of the router path.  Same formulas as layer_backward."""
+    x, dy = _d(x), _d(dy)
+    r, perm = fwd["route"], fwd["perm"]
+    dw = np.einsum("td,tkd->tk", dy, fwd["Y_perm"][perm.row_of])
+    dl = router_backward(fwd["logits"], r["idx"], r["w"], dw, spec, counts=r["counts"], daux=daux)
+    return dict(dw=dw, dlogits=dl, dWg=dl.T @ x, dbg=dl.sum(axis=0), dx_router=dl @ _d(Wg))
 
 
 def expert_param_count(d: int, F: int) -> int:

@@ -318,3 +318,99 @@ def test_backward_matches_central_differences(case):
             fd = (lp - lm) / (2 * h)
             an = b[gname].reshape(-1)[i]
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (pname, i, fd, an)
+
+
+# ------------------------------------------------------------------ fp8 (e4m3) quantiser
+
+def _torch_e4m3(v):
+    """torch's own float32 -> float8_e4m3fn cast (round to nearest even, no saturation)."""
+    return torch.as_tensor(np.asarray(v, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_table_and_rounding_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    finite = codes[(codes & 0x7F) != 0x7F]
+    ref = torch.as_tensor(finite).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(O.e4m3_decode(finite), ref)
+    assert O.E4M3_MAX == ref.max() == 448.0
+    # every finite code round-trips
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(finite)), finite)
+    # random values inside the range, plus every midpoint between neighbouring codes
+    rng = np.random.default_rng(7)
+    v = np.concatenate([rng.standard_normal(20000) * 30, rng.standard_normal(2000) * 1e-3,
+                        (O._E4M3[1:] + O._E4M3[:-1]) / 2, -(O._E4M3[1:] + O._E4M3[:-1]) / 2]).astype(np.float32)
+    v = v[np.abs(v) <= 448]
+    assert np.array_equal(O.e4m3_encode(v), _torch_e4m3(v))
+
+
+def test_e4m3_saturation_and_signed_zero():
+    assert list(O.e4m3_encode(np.array([448, 449, 464, 1e6, -500], dtype=np.float32))) == [0x7E] * 4 + [0xFE]
+    assert list(O.e4m3_encode(np.array([0.0, -0.0, -1e-30, 2.0 ** -10], dtype=np.float32))) == [0x00, 0x80, 0x80, 0x00]
+
+
+def test_block_quantiser_scale_rule_and_bounds():
+    rng = np.random.default_rng(3)
+    v = (rng.standard_normal((256, 384)) * rng.uniform(0.01, 5, size=(256, 1))).astype(np.float32)
+    v[:128, 128:256] = 0.0                       # an all-zero 128 x 128 block
+    for br in (1, 128):
+        q, s = O.quantize_blocks(v, br)
+        assert q.shape == v.shape and s.shape == (256 // br, 3) and s.dtype == np.float32
+        blocks = np.abs(v).reshape(256 // br, br, 3, 128).max(axis=(1, 3))
+        assert np.array_equal(s, np.where(blocks > 0, blocks.astype(np.float32) / np.float32(448), 1).astype(np.float32))
+        # the quantised values are torch's rounding of v / scale
+        full = np.repeat(np.repeat(s, br, axis=0), 128, axis=1)
+        assert np.array_equal(q, _torch_e4m3(np.minimum(np.abs(v / full), 448) * np.sign(v / full)) |
+                              np.where(np.signbit(v), 0x80, 0).astype(np.uint8))
+        # each block's largest magnitude lands on +-448
+        deq = O.dequantize_blocks(q, s, br)
+        nz = blocks > 0
+        big = np.abs(O.e4m3_decode(q)).reshape(256 // br, br, 3, 128).max(axis=(1, 3))
+        assert np.all(big[nz] == 448.0) and np.all(big[~nz] == 0.0)
+        # error within half a step: 2^-4 relative for normal codes, 2^-10 scale for subnormal ones
+        bound = np.maximum(2.0 ** -4 * np.abs(v), 2.0 ** -10 * full)
+        assert np.all(np.abs(deq - v) <= bound)
+        # idempotent on codes
+        q2, _ = O.quantize_blocks(deq.astype(np.float32), br)
+        assert np.array_equal(q2, q)
+
+
+def test_fp8_layer_equals_exact_layer_up_to_act_rounding():
+    """With x and the weights exactly on the e4m3 grids, the fp8 layer differs from the
+    exact layer only by the per-token rounding of Act, which is bounded element by element."""
+    rng = np.random.default_rng(11)
+    T, d, E, k, F = 24, 256, 4, 2, 128
+    spec = O.LayerSpec(E=E, k=k, score="softmax")
+    # x: e4m3 codes times a per-row power of two, with a 448 in every 128-block so scale = 2^j
+    codes = rng.integers(0, 0x7E, size=(T, d)).astype(np.uint8) | (rng.integers(0, 2, size=(T, d)) * 0x80).astype(np.uint8)
+    codes[:, ::128] = 0x7E
+    x = O.e4m3_decode(codes) * (2.0 ** rng.integers(-12, -6, size=(T, 1)))
+    W13m = rng.standard_normal((E, 2 * F, d)).astype(np.float32) * 0.05
+    W2m = rng.standard_normal((E, d, F)).astype(np.float32) * 0.05
+    q13 = [O.quantize_blocks(W13m[e], 128) for e in range(E)]
+    q2 = [O.quantize_blocks(W2m[e], 128) for e in range(E)]
+    W13q, W13s = np.stack([a for a, _ in q13]), np.stack([b for _, b in q13])
+    W2q, W2s = np.stack([a for a, _ in q2]), np.stack([b for _, b in q2])
+    Wg = rng.standard_normal((E, d)) / 16
+    f8 = O.layer_forward_fp8(x, Wg, W13q, W13s, W2q, W2s, spec)
+    # x survives quantisation exactly
+    assert np.array_equal(O.dequantize_blocks(f8["x_q"], f8["x_scale"], 1), x)
+    W13d = np.stack([O.dequantize_blocks(W13q[e], W13s[e], 128) for e in range(E)])
+    W2d = np.stack([O.dequantize_blocks(W2q[e], W2s[e], 128) for e in range(E)])
+    ex = O.layer_forward(x, Wg, W13d, W2d, spec)
+    assert np.array_equal(f8["route"]["idx"], ex["route"]["idx"])
+    assert np.allclose(f8["H"], ex["H"], rtol=1e-12, atol=0)
+    # |dAct| <= half a step of the Act grid of its row
+    full = np.repeat(f8["Act_scale"].astype(np.float64), 128, axis=1)
+    dact_bound = np.maximum(2.0 ** -4 * np.abs(f8["Act"]), 2.0 ** -10 * full)
+    deq = O.dequantize_blocks(f8["Act_q"], f8["Act_scale"], 1)
+    assert np.all(np.abs(deq - f8["Act"]) <= dact_bound)
+    # propagate the bound through fc2 and the combine
+    perm, r = f8["perm"], f8["route"]
+    yb = np.zeros((T * k, d))
+    for e in range(E):
+        a, b = perm.offsets[e], perm.offsets[e + 1]
+        yb[a:b] = dact_bound[a:b] @ np.abs(W2d[e]).T
+    bound = np.einsum("tk,tkd->td", np.abs(r["w"]), yb[perm.row_of])
+    diff = np.abs(f8["y"] - ex["y"])
+    assert np.all(diff <= bound * (1 + 1e-9) + 1e-15)
+    assert diff.max() > 0          # the Act rounding did happen
