@@ -30,6 +30,11 @@
  *   dX_perm [A, d]                    fp32 per-row input gradients
  *   dW13, dW2, dW13s, dW2s            fp32 weight gradients, shaped like the weights
  *
+ * fp8 experts (w_dtype == MOE_FP8_E4M3): W13 and W2 hold e4m3 codes (one byte each)
+ * with one fp32 scale per 128 x 128 block; x_perm and Act hold e4m3 codes with one scale
+ * per row per 128 columns (x_perm_scale, Act_scale); H and Y_perm stay fp32.  The pages
+ * give no low-precision expert recipe; the one taken is documented at moe_quantize_fp8.
+ *
  * Precision: every GEMM multiplies act-dtype operands (bf16 on the matrix cores) with
  * fp32 accumulation.  Only GEMM operands are stored in bf16 (x_perm, Act, dY_perm, dH);
  * everything that is summed or differentiated further (H, expert outputs, per-row input
@@ -63,7 +68,7 @@ typedef enum {
   MOE_ERR_HIP = 4
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
 
 /* [HB] §3.1 Router scoring, Gating function. */
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_t;
@@ -80,7 +85,9 @@ typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_t;
  *   softmax with k == 1 needs pre-softmax, which is not provided: UNSUPPORTED
  *   ([HB] §3.1 Output scale: a softmax over one logit has no gradient);
  *   pre_softmax must be 0 (UNSUPPORTED otherwise);
- *   aux_coeff != 0 only with softmax scores (UNSUPPORTED otherwise).
+ *   aux_coeff != 0 only with softmax scores (UNSUPPORTED otherwise);
+ *   w_dtype == MOE_FP8_E4M3 (fp8 experts, see moe_quantize_fp8) needs act_dtype == bf16,
+ *   Fs == 0, d % 128 == 0 and F % 128 == 0 (UNSUPPORTED otherwise).
  */
 typedef struct moe_config {
   int32_t T, d, E, k, F, Fs;
@@ -88,8 +95,8 @@ typedef struct moe_config {
   int32_t pre_softmax;    /* must be 0 */
   float routed_scaling;   /* multiplies the renormalised weights ([HB] §3.1 Output scale) */
   float aux_coeff;        /* Switch aux-loss coefficient ([HB] §3.3 Aux loss) */
-  int32_t act_dtype;      /* moe_dtype_t of activations and expert weights */
-  int32_t reserved;       /* must be 0 */
+  int32_t act_dtype;      /* moe_dtype_t of activations (and of expert weights when w_dtype == 0) */
+  int32_t w_dtype;        /* 0: expert weights in act_dtype; MOE_FP8_E4M3: e4m3 codes + scales */
 } moe_config_t;
 
 typedef struct moe_weights {
@@ -100,6 +107,8 @@ typedef struct moe_weights {
   const void* W2;           /* [E, d, F] */
   const void* W13s;         /* [2Fs, d], NULL when Fs == 0 */
   const void* W2s;          /* [d, Fs],  NULL when Fs == 0 */
+  const float* W13_scale;   /* fp8 weights only: [E, 2F/128, d/128] fp32 block scales */
+  const float* W2_scale;    /* fp8 weights only: [E, d/128, F/128] fp32 block scales */
 } moe_weights_t;
 
 /* Tensors the forward writes and the backward reads (all caller-owned). */
@@ -118,6 +127,8 @@ typedef struct moe_saved {
   void* H_s;         /* [T, 2Fs] fp32, or NULL when Fs == 0 */
   void* Act_s;       /* [T, Fs]  or NULL */
   void* Y_s;         /* [T, d]   fp32, or NULL */
+  float* x_perm_scale; /* fp8 weights only: [A, d/128], the scales of x_perm's e4m3 rows */
+  float* Act_scale;    /* fp8 weights only: [A, F/128], the scales of Act's e4m3 rows */
 } moe_saved_t;
 
 /* Gradients written by moe_layer_bwd (overwritten, not accumulated). */
@@ -182,7 +193,10 @@ moe_status_t moe_unpermute_combine(const moe_config_t* cfg, const float* Y_perm,
                                    const float* w, const float* Y_s, float* y, void* stream);
 
 /* Whole forward: gate logits, router, permute, grouped experts (+ shared), combine.
- * Fills *saved for the backward.  stats as in moe_router_topk (NULL ok). */
+ * Fills *saved for the backward.  stats as in moe_router_topk (NULL ok).
+ * fp8 experts: x (bf16) is quantised per token per 128 before the permute, the weights
+ * are e4m3 codes with weights->W13_scale / W2_scale, and saved->x_perm, saved->Act hold
+ * codes with saved->x_perm_scale, saved->Act_scale. */
 moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* weights, const void* x,
                            const moe_saved_t* saved, float* y, float* stats, void* ws, size_t ws_bytes,
                            void* stream);
@@ -193,7 +207,8 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* weights
  * expert-selection answer key"). */
 
 /* dY_perm[row_of[t, j]] = w[t, j] * dy[t] (act dtype);  dw[t, j] = <dy[t], Y_perm[row_of[t, j]]>;
- * dY_s (NULL ok) = dy in the act dtype: the shared expert's upstream gradient. */
+ * dY_s (NULL ok) = dy in the act dtype: the shared expert's upstream gradient.
+ * dY_perm may be NULL when only dw is wanted (fp8 experts, whose weights are frozen). */
 moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const float* dy, const float* Y_perm,
                                        const int32_t* row_of, const float* w, void* dY_perm, float* dw,
                                        void* dY_s, void* stream);
@@ -227,6 +242,39 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
 moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, int32_t groups, int64_t rows,
                                const void* dY, int32_t N, const void* X, int32_t K, float* dW, void* stream);
 
+/* ---------------------------------------------------------------- fp8 experts
+ * e4m3 block quantiser (the fp8 recipe is a reading: the pages leave low-precision expert
+ * GEMMs open, [HB] §3.1 Precision asks only for an fp32 router).  src [rows, cols] is
+ * bf16 (src_dtype MOE_BF16) or fp32 (MOE_F32), row-major; every block of block_rows x 128
+ * gets one fp32 scale = amax / 448 computed in fp32 (1 for an all-zero block) and the
+ * codes q = e4m3(v / scale): the quotient in fp32, rounded to the nearest e4m3 value
+ * (ties to the even code), magnitudes above 448 saturated, sign bit = sign of v.
+ * q [rows, cols] uint8; scale [rows / block_rows, cols / 128] fp32.
+ * block_rows is 1 (activations: per token per 128) or 128 (weights: 128 x 128 blocks).
+ * Errors: cols % 128 != 0, rows % block_rows != 0, rows < 1, other block_rows or dtypes
+ * -> MOE_ERR_INVALID_ARG.  Weight quantisation for fp8 experts runs through this call
+ * (one call per expert matrix, or one call over the [E*2F, d] stack). */
+moe_status_t moe_quantize_fp8(int32_t src_dtype, const void* src, int64_t rows, int32_t cols, int32_t block_rows,
+                              uint8_t* q, float* scale, void* stream);
+
+/* moe_permute for e4m3 rows: the same grouping (offsets, row_of, token_of) of x_q [T, d]
+ * uint8 codes into x_perm [A, d] uint8, with their scales x_scale [T, d/128] -> x_perm_scale
+ * [A, d/128].  Needs cfg->w_dtype == MOE_FP8_E4M3. */
+moe_status_t moe_permute_fp8(const moe_config_t* cfg, const uint8_t* x_q, const float* x_scale, const int32_t* idx,
+                             int32_t* offsets, int32_t* row_of, int32_t* token_of, uint8_t* x_perm,
+                             float* x_perm_scale, void* ws, size_t ws_bytes, void* stream);
+
+/* Grouped SwiGLU experts with e4m3 weights and activations (cfg->w_dtype == MOE_FP8_E4M3):
+ * per expert e on its rows, H = deq(x_perm) deq(W13[e])^T (fp32; the products of codes
+ * accumulate on the matrix cores per 128-wide K block, then the two block scales apply);
+ * Act = silu(H[:, :F]) * H[:, F:] in fp32, quantised per row per 128 columns by the rule
+ * of moe_quantize_fp8 into Act [A, F] uint8 + Act_scale [A, F/128];
+ * Y_perm = deq(Act) deq(W2[e])^T (fp32).  H may be NULL (not written). */
+moe_status_t moe_grouped_gemm_swiglu_fp8(const moe_config_t* cfg, const uint8_t* x_perm, const float* x_perm_scale,
+                                         const int32_t* offsets, const uint8_t* W13, const float* W13_scale,
+                                         const uint8_t* W2, const float* W2_scale, float* H, uint8_t* Act,
+                                         float* Act_scale, float* Y_perm, void* ws, size_t ws_bytes, void* stream);
+
 /* Unpermute-reduce: dx[t] = sum_j dX_perm[row_of[t, j]] (+ dx_s[t]) (+ dx_r[t]),
  * fp32 accumulation in that order.  All fp32; dx_s and dx_r may be NULL. */
 moe_status_t moe_permute_bwd(const moe_config_t* cfg, const float* dX_perm, const int32_t* row_of,
@@ -243,7 +291,10 @@ moe_status_t moe_router_bwd(const moe_config_t* cfg, const float* logits, const 
 moe_status_t moe_gate_logits_bwd(const moe_config_t* cfg, const void* x, const float* Wg,
                                  const float* dlogits, float* dWg, float* dbg, float* dx_r, void* stream);
 
-/* Whole backward from the saved forward tensors. */
+/* Whole backward from the saved forward tensors.
+ * fp8 experts are frozen (no expert gradients): grads->dW13, dW2, dW13s, dW2s must be
+ * NULL, and the call computes the router path only -- dw, dlogits, dWg, dbg, and
+ * dx = dlogits Wg, the input gradient through the router. */
 moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* weights, const moe_saved_t* saved,
                            const void* x, const float* dy, float daux, float* dx, const moe_grads_t* grads,
                            void* ws, size_t ws_bytes, void* stream);

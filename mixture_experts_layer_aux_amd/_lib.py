@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_NSTATS = 4
 
@@ -25,6 +25,7 @@ EXPORTED = (
     "moe_status_string", "moe_last_error", "moe_validate", "moe_workspace_size", "moe_gate_logits",
     "moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu", "moe_unpermute_combine", "moe_layer_fwd",
     "moe_unpermute_combine_bwd", "moe_grouped_gemm_swiglu_bwd", "moe_grouped_wgrad", "moe_permute_bwd", "moe_router_bwd",
+    "moe_quantize_fp8", "moe_permute_fp8", "moe_grouped_gemm_swiglu_fp8",
     "moe_gate_logits_bwd", "moe_layer_bwd",
 )
 
@@ -39,19 +40,20 @@ class Config(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("F", ctypes.c_int32), ("Fs", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("pre_softmax", ctypes.c_int32), ("routed_scaling", ctypes.c_float), ("aux_coeff", ctypes.c_float),
-                ("act_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
 
 
 class Weights(ctypes.Structure):
-    _fields_ = [("Wg", _P), ("bg", _P), ("expert_bias", _P), ("W13", _P), ("W2", _P), ("W13s", _P), ("W2s", _P)]
+    _fields_ = [("Wg", _P), ("bg", _P), ("expert_bias", _P), ("W13", _P), ("W2", _P), ("W13s", _P), ("W2s", _P),
+                ("W13_scale", _P), ("W2_scale", _P)]
 
 
 class Saved(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("logits", "idx", "w", "counts", "offsets", "row_of", "token_of", "x_perm", "H",
-                                  "Act", "Y_perm", "H_s", "Act_s", "Y_s")]
+                                  "Act", "Y_perm", "H_s", "Act_s", "Y_s", "x_perm_scale", "Act_scale")]
 
 
 class Grads(ctypes.Structure):
@@ -84,14 +86,19 @@ def _check(status: int) -> None:
         raise MoeError(status, f"{lib.moe_status_string(status).decode()}: {lib.moe_last_error().decode()}")
 
 
-def make_config(T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux_coeff=0.0, act="bf16") -> Config:
+def make_config(T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux_coeff=0.0, act="bf16", wq="") -> Config:
+    """wq: "" (expert weights in the activation dtype) or "fp8" (e4m3 codes + block scales)."""
     return Config(T=T, d=d, E=E, k=k, F=F, Fs=Fs, score=MOE_SOFTMAX if score == "softmax" else MOE_SIGMOID,
                   pre_softmax=0, routed_scaling=scaling, aux_coeff=aux_coeff,
-                  act_dtype=MOE_BF16 if act == "bf16" else MOE_F32, reserved=0)
+                  act_dtype=MOE_BF16 if act == "bf16" else MOE_F32, w_dtype=MOE_FP8_E4M3 if wq == "fp8" else 0)
 
 
 def config_from_shape(s) -> Config:
-    return make_config(s.T, s.d, s.E, s.k, s.F, s.Fs, s.score, s.scaling, s.aux_coeff, s.act)
+    return make_config(s.T, s.d, s.E, s.k, s.F, s.Fs, s.score, s.scaling, s.aux_coeff, s.act, getattr(s, "wq", ""))
+
+
+def is_fp8(cfg: Config) -> bool:
+    return cfg.w_dtype == MOE_FP8_E4M3
 
 
 def act_dtype(cfg: Config) -> torch.dtype:
@@ -232,6 +239,44 @@ def grouped_wgrad(cfg, offsets, groups, rows, dY, N, X, K, dW, stream=None):
         ctypes.c_int32(K), _P(_ptr(dW, torch.float32, groups * N * K, "dW")), _P(_stream(stream))))
 
 
+def quantize_fp8(src, block_rows, q, scale, stream=None):
+    """e4m3 codes q [rows, cols] and fp32 scales [rows / block_rows, cols / 128] of src
+    (bf16 or fp32, [rows, cols] contiguous)."""
+    if src.dim() != 2:
+        raise ValueError("src must be 2-D")
+    rows, cols = src.shape
+    sd = MOE_BF16 if src.dtype == torch.bfloat16 else MOE_F32
+    _check(load().moe_quantize_fp8(
+        ctypes.c_int32(sd), _P(_ptr(src, src.dtype, rows * cols, "src")), ctypes.c_int64(rows), ctypes.c_int32(cols),
+        ctypes.c_int32(block_rows), _P(_ptr(q, torch.uint8, rows * cols, "q")),
+        _P(_ptr(scale, torch.float32, (rows // max(block_rows, 1)) * (cols // 128), "scale")), _P(_stream(stream))))
+
+
+def permute_fp8(cfg, x_q, x_scale, idx, offsets, row_of, token_of, x_perm, x_perm_scale, ws, stream=None):
+    A, T, d, E = cfg.T * cfg.k, cfg.T, cfg.d, cfg.E
+    wp, wn = _ws(ws)
+    _check(load().moe_permute_fp8(
+        ctypes.byref(cfg), _P(_ptr(x_q, torch.uint8, T * d, "x_q")), _P(_ptr(x_scale, torch.float32, T * (d // 128), "x_scale")),
+        _P(_ptr(idx, torch.int32, A, "idx")), _P(_ptr(offsets, torch.int32, E + 1, "offsets")),
+        _P(_ptr(row_of, torch.int32, A, "row_of")), _P(_ptr(token_of, torch.int32, A, "token_of")),
+        _P(_ptr(x_perm, torch.uint8, A * d, "x_perm")), _P(_ptr(x_perm_scale, torch.float32, A * (d // 128), "x_perm_scale")),
+        _P(wp), ctypes.c_size_t(wn), _P(_stream(stream))))
+
+
+def grouped_gemm_swiglu_fp8(cfg, x_perm, x_perm_scale, offsets, W13, W13_scale, W2, W2_scale, H, Act, Act_scale,
+                            Y_perm, ws, stream=None):
+    A, d, E, F = cfg.T * cfg.k, cfg.d, cfg.E, cfg.F
+    wp, wn = _ws(ws)
+    u8, f32 = torch.uint8, torch.float32
+    _check(load().moe_grouped_gemm_swiglu_fp8(
+        ctypes.byref(cfg), _P(_ptr(x_perm, u8, A * d, "x_perm")), _P(_ptr(x_perm_scale, f32, A * (d // 128), "x_perm_scale")),
+        _P(_ptr(offsets, torch.int32, E + 1, "offsets")), _P(_ptr(W13, u8, E * 2 * F * d, "W13")),
+        _P(_ptr(W13_scale, f32, E * (2 * F // 128) * (d // 128), "W13_scale")), _P(_ptr(W2, u8, E * d * F, "W2")),
+        _P(_ptr(W2_scale, f32, E * (d // 128) * (F // 128), "W2_scale")), _P(_ptr(H, f32, A * 2 * F, "H")),
+        _P(_ptr(Act, u8, A * F, "Act")), _P(_ptr(Act_scale, f32, A * (F // 128), "Act_scale")),
+        _P(_ptr(Y_perm, f32, A * d, "Y_perm")), _P(wp), ctypes.c_size_t(wn), _P(_stream(stream))))
+
+
 def permute_bwd(cfg, dX_perm, row_of, dx_s, dx_r, dx, stream=None):
     ad, A = act_dtype(cfg), cfg.T * cfg.k
     _check(load().moe_permute_bwd(ctypes.byref(cfg), _P(_ptr(dX_perm, torch.float32, A * cfg.d, "dX_perm")),
@@ -262,18 +307,23 @@ def gate_logits_bwd(cfg, x, Wg, dlogits, dWg, dbg, dx_r, stream=None):
 
 def _weights_struct(cfg, W: Dict[str, torch.Tensor]) -> Weights:
     ad, d, E, F, Fs = act_dtype(cfg), cfg.d, cfg.E, cfg.F, cfg.Fs
+    wd = torch.uint8 if is_fp8(cfg) else ad
     return Weights(Wg=_ptr(W["Wg"], torch.float32, E * d, "Wg"), bg=_ptr(W.get("bg"), torch.float32, E, "bg"),
                    expert_bias=_ptr(W.get("expert_bias"), torch.float32, E, "expert_bias"),
-                   W13=_ptr(W["W13"], ad, E * 2 * F * d, "W13"), W2=_ptr(W["W2"], ad, E * d * F, "W2"),
-                   W13s=_ptr(W.get("W13s"), ad, 2 * Fs * d, "W13s"), W2s=_ptr(W.get("W2s"), ad, d * Fs, "W2s"))
+                   W13=_ptr(W["W13"], wd, E * 2 * F * d, "W13"), W2=_ptr(W["W2"], wd, E * d * F, "W2"),
+                   W13s=_ptr(W.get("W13s"), ad, 2 * Fs * d, "W13s"), W2s=_ptr(W.get("W2s"), ad, d * Fs, "W2s"),
+                   W13_scale=_ptr(W.get("W13_scale"), torch.float32, E * (2 * F // 128) * (d // 128), "W13_scale"),
+                   W2_scale=_ptr(W.get("W2_scale"), torch.float32, E * (d // 128) * (F // 128), "W2_scale"))
 
 
 def _saved_struct(cfg, S: Dict[str, torch.Tensor]) -> Saved:
     ad, T, d, E, F, Fs, A = act_dtype(cfg), cfg.T, cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.T * cfg.k
+    qd = torch.uint8 if is_fp8(cfg) else ad
     spec = dict(logits=(torch.float32, T * E), idx=(torch.int32, A), w=(torch.float32, A), counts=(torch.int32, E),
                 offsets=(torch.int32, E + 1), row_of=(torch.int32, A), token_of=(torch.int32, A),
-                x_perm=(ad, A * d), H=(torch.float32, A * 2 * F), Act=(ad, A * F), Y_perm=(torch.float32, A * d),
-                H_s=(torch.float32, T * 2 * Fs), Act_s=(ad, T * Fs), Y_s=(torch.float32, T * d))
+                x_perm=(qd, A * d), H=(torch.float32, A * 2 * F), Act=(qd, A * F), Y_perm=(torch.float32, A * d),
+                H_s=(torch.float32, T * 2 * Fs), Act_s=(ad, T * Fs), Y_s=(torch.float32, T * d),
+                x_perm_scale=(torch.float32, A * (d // 128)), Act_scale=(torch.float32, A * (F // 128)))
     return Saved(**{n: _ptr(S.get(n), dt, ne, n) for n, (dt, ne) in spec.items()})
 
 
@@ -295,7 +345,7 @@ def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None):
     ss = _saved_struct(cfg, S)
     f32 = torch.float32
     gs = Grads(dWg=_ptr(G["dWg"], f32, E * d, "dWg"), dbg=_ptr(G.get("dbg"), f32, E, "dbg"),
-               dW13=_ptr(G["dW13"], f32, E * 2 * F * d, "dW13"), dW2=_ptr(G["dW2"], f32, E * d * F, "dW2"),
+               dW13=_ptr(G.get("dW13"), f32, E * 2 * F * d, "dW13"), dW2=_ptr(G.get("dW2"), f32, E * d * F, "dW2"),
                dW13s=_ptr(G.get("dW13s"), f32, 2 * Fs * d, "dW13s"), dW2s=_ptr(G.get("dW2s"), f32, d * Fs, "dW2s"))
     _check(load().moe_layer_bwd(ctypes.byref(cfg), ctypes.byref(ws_), ctypes.byref(ss),
                                 _P(_ptr(x, ad, cfg.T * d, "x")), _P(_ptr(dy, f32, cfg.T * d, "dy")),
@@ -308,10 +358,13 @@ def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None):
 def alloc_saved(cfg: Config, device="cuda") -> Dict[str, torch.Tensor]:
     ad, T, d, E, F, Fs, A = act_dtype(cfg), cfg.T, cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.T * cfg.k
     e = lambda *s, dt=ad: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
+    qd = torch.uint8 if is_fp8(cfg) else ad
     S = dict(logits=e(T, E, dt=torch.float32), idx=e(T, cfg.k, dt=torch.int32), w=e(T, cfg.k, dt=torch.float32),
              counts=e(E, dt=torch.int32), offsets=e(E + 1, dt=torch.int32), row_of=e(T, cfg.k, dt=torch.int32),
-             token_of=e(A, dt=torch.int32), x_perm=e(A, d), H=e(A, 2 * F, dt=torch.float32), Act=e(A, F),
-             Y_perm=e(A, d, dt=torch.float32))
+             token_of=e(A, dt=torch.int32), x_perm=e(A, d, dt=qd), H=e(A, 2 * F, dt=torch.float32),
+             Act=e(A, F, dt=qd), Y_perm=e(A, d, dt=torch.float32))
+    if is_fp8(cfg):
+        S.update(x_perm_scale=e(A, d // 128, dt=torch.float32), Act_scale=e(A, F // 128, dt=torch.float32))
     if Fs:
         S.update(H_s=e(T, 2 * Fs, dt=torch.float32), Act_s=e(T, Fs), Y_s=e(T, d, dt=torch.float32))
     return S
@@ -319,8 +372,10 @@ def alloc_saved(cfg: Config, device="cuda") -> Dict[str, torch.Tensor]:
 
 def alloc_grads(cfg: Config, device="cuda", with_dbg=False) -> Dict[str, torch.Tensor]:
     d, E, F, Fs, f32 = cfg.d, cfg.E, cfg.F, cfg.Fs, torch.float32
-    G = dict(dWg=torch.empty(E, d, dtype=f32, device=device),
-             dW13=torch.empty(E, 2 * F, d, dtype=f32, device=device), dW2=torch.empty(E, d, F, dtype=f32, device=device))
+    G = dict(dWg=torch.empty(E, d, dtype=f32, device=device))
+    if not is_fp8(cfg):   # fp8 experts are frozen: no expert weight gradients
+        G.update(dW13=torch.empty(E, 2 * F, d, dtype=f32, device=device),
+                 dW2=torch.empty(E, d, F, dtype=f32, device=device))
     if with_dbg:
         G["dbg"] = torch.empty(E, dtype=f32, device=device)
     if Fs:

@@ -48,6 +48,9 @@ struct FwdWs {
   int32_t* counts;     // [E]
   float* prob_sum;     // [E]
   int32_t* sched;      // [E + 1]
+  uint8_t* xq;         // fp8 experts: [T, d] e4m3 codes of x
+  float* xs;           // fp8 experts: [T, d/128] their scales
+  float* act32;        // fp8 experts: [A, F] fp32 SwiGLU output before quantisation
   size_t bytes;
 };
 
@@ -66,7 +69,15 @@ FwdWs carve_fwd(const moe_config_t& c, void* base) {
   w.blk_base = reinterpret_cast<int32_t*>(take(nch * c.E * 4));
   w.counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(c.E) * 4));
   w.prob_sum = reinterpret_cast<float*>(take(static_cast<size_t>(c.E) * 4));
-  w.sched = reinterpret_cast<int32_t*>(take(mfma_schedule_bytes(c.E)));
+  w.sched = reinterpret_cast<int32_t*>(take(std::max(mfma_schedule_bytes(c.E), fp8_schedule_bytes(c.E))));
+  w.xq = nullptr;
+  w.xs = w.act32 = nullptr;
+  if (c.w_dtype == MOE_FP8_E4M3) {
+    const size_t T = c.T, A = T * c.k;
+    w.xq = reinterpret_cast<uint8_t*>(take(T * c.d));
+    w.xs = reinterpret_cast<float*>(take(T * (c.d / 128) * 4));
+    w.act32 = reinterpret_cast<float*>(take(A * c.F * 4));
+  }
   w.bytes = off;
   return w;
 }
@@ -126,7 +137,12 @@ moe_status_t validate(const moe_config_t* c) {
     return fail(MOE_ERR_UNSUPPORTED, "the aux loss is provided for softmax scores only");
   if (!(c->routed_scaling > 0.0f)) return fail(MOE_ERR_INVALID_ARG, "routed_scaling must be > 0");
   if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown act dtype");
-  if (c->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "reserved field must be 0");
+  if (c->w_dtype != 0 && c->w_dtype != MOE_FP8_E4M3) return fail(MOE_ERR_INVALID_ARG, "unknown weight dtype");
+  if (c->w_dtype == MOE_FP8_E4M3) {
+    if (c->act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts need bf16 activations");
+    if (c->Fs) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts: a shared expert is not provided");
+    if (c->d % 128 || c->F % 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts need d and F multiples of 128");
+  }
   if (c->d % 64 || c->F % 64 || c->Fs % 64)
     return fail(MOE_ERR_UNSUPPORTED, "d, F and Fs must be multiples of 64 (d=%d F=%d Fs=%d)", c->d, c->F, c->Fs);
   if (c->act_dtype == MOE_BF16 && (c->F % 128 || c->Fs % 128))
@@ -220,6 +236,18 @@ moe_status_t run_wgrad(int act_dtype, const int32_t* off, int G, int64_t rows, c
   w.C = dW; w.ldc = K; w.c_gstride = int64_t{1} * N * K;
   w.offsets = off; w.G = G; w.range_end = static_cast<int>(rows);
   return act_dtype == MOE_BF16 ? launch_gemm_mfma(w, nullptr, s) : launch_gemm_fma(w, s);
+}
+
+// fp8 experts: fc1 (+ SwiGLU -> act32, H), Act quantised per row per 128, fc2 -> Y_perm.
+moe_status_t run_experts_fp8(const moe_config_t& c, const uint8_t* x_perm, const float* xps, const int32_t* offsets,
+                             const uint8_t* W13, const float* W13_scale, const uint8_t* W2, const float* W2_scale,
+                             float* H, uint8_t* Act, float* Act_scale, float* Y_perm, float* act32, int32_t* sched,
+                             hipStream_t s) {
+  const int64_t A = static_cast<int64_t>(c.T) * c.k;
+  MOE_TRY(launch_gemm_fp8(true, x_perm, xps, W13, W13_scale, act32, H, offsets, c.E, A, 2 * c.F, c.d, c.F, sched, s));
+  MOE_TRY(launch_quantize_fp8(MOE_F32, act32, A, c.F, 1, Act, Act_scale, s));
+  return launch_gemm_fp8(false, Act, Act_scale, W2, W2_scale, Y_perm, nullptr, offsets, c.E, A, c.d, c.F, c.F, sched,
+                         s);
 }
 
 moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const int32_t* offsets, const void* W13,
@@ -400,8 +428,15 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_NEED(W); MOE_NEED(sv); MOE_NEED16(x); MOE_NEED16(y); MOE_NEED(ws);
   MOE_NEED(W->Wg); MOE_NEED16(W->W13); MOE_NEED16(W->W2);
   MOE_NEED(sv->logits); MOE_NEED(sv->idx); MOE_NEED(sv->w); MOE_NEED(sv->counts); MOE_NEED(sv->offsets);
-  MOE_NEED(sv->row_of); MOE_NEED(sv->token_of); MOE_NEED16(sv->x_perm); MOE_NEED16(sv->H); MOE_NEED16(sv->Act);
+  MOE_NEED(sv->row_of); MOE_NEED(sv->token_of); MOE_NEED16(sv->x_perm); MOE_NEED16(sv->Act);
   MOE_NEED16(sv->Y_perm);
+  const bool fp8 = cfg->w_dtype == MOE_FP8_E4M3;
+  if (fp8) {
+    MOE_NEED(W->W13_scale); MOE_NEED(W->W2_scale); MOE_NEED(sv->x_perm_scale); MOE_NEED(sv->Act_scale);
+    if (sv->H && !aligned16(sv->H)) return fail(MOE_ERR_INVALID_ARG, "H is not 16-byte aligned");
+  } else {
+    MOE_NEED16(sv->H);
+  }
   if (cfg->Fs) {
     MOE_NEED16(W->W13s); MOE_NEED16(W->W2s); MOE_NEED16(sv->H_s); MOE_NEED16(sv->Act_s); MOE_NEED16(sv->Y_s);
   }
@@ -414,6 +449,20 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_TRY(run_gate(c, x, W->Wg, W->bg, sv->logits, s));
   MOE_TRY(launch_router_topk(c, sv->logits, W->expert_bias, sv->idx, sv->w, sv->counts, fw.prob_sum, stats,
                              fw.cnt_part, fw.prob_part, s));
+  if (fp8) {
+    // x is quantised per token per 128 before the permute, so the permute moves e4m3 rows
+    const int64_t A = static_cast<int64_t>(c.T) * c.k;
+    MOE_TRY(launch_quantize_fp8(MOE_BF16, x, c.T, c.d, 1, fw.xq, fw.xs, s));
+    MOE_TRY(launch_permute(c, fw.xq, sv->idx, sv->offsets, sv->row_of, sv->token_of, sv->x_perm, fw.cnt_part,
+                           fw.blk_base, fw.counts, true, s, 1));
+    MOE_TRY(launch_gather_scales(fw.xs, sv->token_of, A, c.d / 128, sv->x_perm_scale, s));
+    MOE_TRY(run_experts_fp8(c, static_cast<const uint8_t*>(sv->x_perm), sv->x_perm_scale, sv->offsets,
+                            static_cast<const uint8_t*>(W->W13), W->W13_scale, static_cast<const uint8_t*>(W->W2),
+                            W->W2_scale, static_cast<float*>(sv->H), static_cast<uint8_t*>(sv->Act), sv->Act_scale,
+                            static_cast<float*>(sv->Y_perm), fw.act32, fw.sched, s));
+    return launch_combine(c, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, nullptr,
+                          static_cast<float*>(y), s);
+  }
   MOE_TRY(launch_permute(c, x, sv->idx, sv->offsets, sv->row_of, sv->token_of, sv->x_perm, fw.cnt_part, fw.blk_base,
                          fw.counts, true, s));
   MOE_TRY(run_experts_fwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, x, W->W13s, W->W2s, sv->H, sv->Act,
@@ -426,7 +475,8 @@ moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const float* dy,
                                        const int32_t* row_of, const float* w, void* dY_perm, float* dw,
                                        void* dY_s, void* stream) {
   MOE_TRY(validate(cfg));
-  MOE_NEED16(dy); MOE_NEED16(Y_perm); MOE_NEED(row_of); MOE_NEED(w); MOE_NEED16(dY_perm); MOE_NEED(dw);
+  MOE_NEED16(dy); MOE_NEED16(Y_perm); MOE_NEED(row_of); MOE_NEED(w); MOE_NEED(dw);
+  if (dY_perm && !aligned16(dY_perm)) return fail(MOE_ERR_INVALID_ARG, "dY_perm is not 16-byte aligned");
   if (dY_s && !aligned16(dY_s)) return fail(MOE_ERR_INVALID_ARG, "dY_s is not 16-byte aligned");
   return launch_combine_bwd(*cfg, dy, Y_perm, row_of, w, dY_perm, dw, dY_s, S(stream));
 }
@@ -466,6 +516,48 @@ moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, 
   return run_wgrad(cfg->act_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream));
 }
 
+moe_status_t moe_quantize_fp8(int32_t src_dtype, const void* src, int64_t rows, int32_t cols, int32_t block_rows,
+                              uint8_t* q, float* scale, void* stream) {
+  MOE_NEED16(src); MOE_NEED16(q); MOE_NEED(scale);
+  if (src_dtype != MOE_BF16 && src_dtype != MOE_F32) return fail(MOE_ERR_INVALID_ARG, "src dtype must be bf16 or fp32");
+  if (block_rows != 1 && block_rows != 128) return fail(MOE_ERR_INVALID_ARG, "block_rows must be 1 or 128");
+  if (rows < 1 || cols < 128 || cols % 128) return fail(MOE_ERR_INVALID_ARG, "rows >= 1 and cols a multiple of 128");
+  if (rows % block_rows) return fail(MOE_ERR_INVALID_ARG, "rows must be a multiple of block_rows");
+  if (rows * cols >= (int64_t{1} << 40)) return fail(MOE_ERR_INVALID_ARG, "matrix too large");
+  return launch_quantize_fp8(src_dtype, src, rows, cols, block_rows, q, scale, S(stream));
+}
+
+moe_status_t moe_permute_fp8(const moe_config_t* cfg, const uint8_t* x_q, const float* x_scale, const int32_t* idx,
+                             int32_t* offsets, int32_t* row_of, int32_t* token_of, uint8_t* x_perm,
+                             float* x_perm_scale, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate(cfg));
+  if (cfg->w_dtype != MOE_FP8_E4M3) return fail(MOE_ERR_INVALID_ARG, "moe_permute_fp8 needs w_dtype fp8");
+  MOE_NEED16(x_q); MOE_NEED(x_scale); MOE_NEED(idx); MOE_NEED(offsets); MOE_NEED(row_of); MOE_NEED(token_of);
+  MOE_NEED16(x_perm); MOE_NEED(x_perm_scale); MOE_NEED(ws);
+  const FwdWs fw = carve_fwd(*cfg, ws);
+  MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
+  hipStream_t s = S(stream);
+  MOE_TRY(launch_permute(*cfg, x_q, idx, offsets, row_of, token_of, x_perm, fw.cnt_part, fw.blk_base, fw.counts,
+                         false, s, 1));
+  return launch_gather_scales(x_scale, token_of, static_cast<int64_t>(cfg->T) * cfg->k, cfg->d / 128, x_perm_scale,
+                              s);
+}
+
+moe_status_t moe_grouped_gemm_swiglu_fp8(const moe_config_t* cfg, const uint8_t* x_perm, const float* x_perm_scale,
+                                         const int32_t* offsets, const uint8_t* W13, const float* W13_scale,
+                                         const uint8_t* W2, const float* W2_scale, float* H, uint8_t* Act,
+                                         float* Act_scale, float* Y_perm, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate(cfg));
+  if (cfg->w_dtype != MOE_FP8_E4M3) return fail(MOE_ERR_INVALID_ARG, "moe_grouped_gemm_swiglu_fp8 needs w_dtype fp8");
+  MOE_NEED16(x_perm); MOE_NEED(x_perm_scale); MOE_NEED(offsets); MOE_NEED16(W13); MOE_NEED(W13_scale);
+  MOE_NEED16(W2); MOE_NEED(W2_scale); MOE_NEED16(Act); MOE_NEED(Act_scale); MOE_NEED16(Y_perm); MOE_NEED(ws);
+  if (H && !aligned16(H)) return fail(MOE_ERR_INVALID_ARG, "H is not 16-byte aligned");
+  const FwdWs fw = carve_fwd(*cfg, ws);
+  MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
+  return run_experts_fp8(*cfg, x_perm, x_perm_scale, offsets, W13, W13_scale, W2, W2_scale, H, Act, Act_scale, Y_perm,
+                         fw.act32, fw.sched, S(stream));
+}
+
 moe_status_t moe_permute_bwd(const moe_config_t* cfg, const float* dX_perm, const int32_t* row_of, const float* dx_s,
                              const float* dx_r, float* dx, void* stream) {
   MOE_TRY(validate(cfg));
@@ -497,8 +589,21 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_NEED(W); MOE_NEED(sv); MOE_NEED(gr); MOE_NEED16(x); MOE_NEED16(dy); MOE_NEED16(dx); MOE_NEED(ws);
   MOE_NEED(W->Wg); MOE_NEED16(W->W13); MOE_NEED16(W->W2);
   MOE_NEED(sv->logits); MOE_NEED(sv->idx); MOE_NEED(sv->w); MOE_NEED(sv->counts); MOE_NEED(sv->offsets);
-  MOE_NEED(sv->row_of); MOE_NEED16(sv->x_perm); MOE_NEED16(sv->H); MOE_NEED16(sv->Act); MOE_NEED16(sv->Y_perm);
-  MOE_NEED(gr->dWg); MOE_NEED16(gr->dW13); MOE_NEED16(gr->dW2);
+  MOE_NEED(sv->row_of); MOE_NEED16(sv->Y_perm); MOE_NEED(gr->dWg);
+  if (cfg->w_dtype == MOE_FP8_E4M3) {
+    // frozen e4m3 experts: the backward runs through the mixing weights only
+    if (gr->dW13 || gr->dW2 || gr->dW13s || gr->dW2s)
+      return fail(MOE_ERR_INVALID_ARG, "fp8 experts are frozen: expert weight gradients must be NULL");
+    const BwdWs bw = carve_bwd(*cfg, ws);
+    MOE_TRY(need_ws(ws_bytes, bw.bytes, __func__));
+    const moe_config_t& c = *cfg;
+    hipStream_t s = S(stream);
+    MOE_TRY(launch_combine_bwd(c, dy, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, nullptr, bw.dw,
+                               nullptr, s));
+    MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, daux, bw.dlogits, s));
+    return run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, dx, s);
+  }
+  MOE_NEED16(sv->x_perm); MOE_NEED16(sv->H); MOE_NEED16(sv->Act); MOE_NEED16(gr->dW13); MOE_NEED16(gr->dW2);
   if (cfg->Fs) {
     MOE_NEED16(W->W13s); MOE_NEED16(W->W2s); MOE_NEED16(sv->H_s); MOE_NEED16(sv->Act_s);
     MOE_NEED16(gr->dW13s); MOE_NEED16(gr->dW2s);

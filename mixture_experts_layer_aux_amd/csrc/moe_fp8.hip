@@ -1,0 +1,454 @@
+// fp8 (e4m3) experts: the block quantiser, the permute of e4m3 rows and their scales, and
+// the grouped SwiGLU GEMM on the gfx950 fp8 matrix cores.
+//
+// Recipe (a reading: The Ultimate MoE Training Handbook leaves low-precision expert GEMMs
+// open, §3.1 Precision asks only for an fp32 router): OCP e4m3 codes, one fp32 scale per
+// block = amax / 448 in fp32 (1 for an all-zero block), code = nearest e4m3 value to the
+// fp32 quotient v / scale, ties to the even code, saturated to 448.  Weights use 128 x 128
+// blocks, activations 1 x 128 (per token per 128 columns).
+//
+// GEMM design (per workgroup: 512 threads = 8 waves in a 4 x 2 grid):
+//   * 256 x 128 output tile, each wave 64 x 64 as 2 x 2 accumulators of
+//     v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, fp32 out);
+//   * one stage = one 128-wide K block = one scale block: both operands (128 bytes per row)
+//     and the 256 row scales of the A operand go from HBM into LDS by buffer_load ... lds,
+//     through a ring of 3 stages (147 KB);
+//   * per K block, each accumulator pair is formed from zero by two MFMAs and added to the
+//     fp32 accumulator times (row scale x weight-block scale): the block scales of both
+//     operands apply exactly once per block;
+//   * operand rows are stored 128 bytes wide with the 16-byte chunk index XORed by
+//     (r ^ (r >> 3)) & 7, and read with ds_read_b128 (lane l: row l % 32, bytes
+//     32 (l / 32) .. +31 of each 64-wide half);
+//   * the B fragment goes first, so each lane owns one output row and four consecutive
+//     columns per register quad (vector epilogue stores);
+//   * fc1's B tile interleaves 32 gate rows and 32 up rows, so the SwiGLU epilogue finds a
+//     gate value and its up value in the same lane; it writes H (fp32, optional) and Act
+//     (fp32) for the per-row quantiser.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr float kE4M3Max = 448.0f;
+
+// fp32 -> e4m3 code by the rule above.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 31) << 7;
+  const float a = fabsf(x);
+  uint32_t mag;
+  if (!(a < kE4M3Max)) {
+    mag = 0x7E;                                              // 448, and saturation
+  } else if (a < 0.015625f) {                                // below 2^-6: subnormal codes
+    mag = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));  // steps of 2^-9, ties to even
+  } else {
+    // keep 3 mantissa bits, round the 20 dropped bits to nearest even; the exponent
+    // rebias (127 -> 7) is a subtraction on the combined exponent|mantissa field
+    const uint32_t u = __float_as_uint(a);
+    const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+    mag = min((r >> 20) - (120u << 3), 0x7Eu);
+  }
+  return sign | mag;
+}
+
+__device__ __forceinline__ float block_scale(float amax) {
+  return amax > 0.0f ? __fdiv_rn(amax, kE4M3Max) : 1.0f;
+}
+
+template <typename T> __device__ __forceinline__ void load8(const T* p, float* f);
+template <> __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* f) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+template <> __device__ __forceinline__ void load8<float>(const float* p, float* f) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+__device__ __forceinline__ uint2 encode8(const float* f, float scale) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= e4m3_code(__fdiv_rn(f[i], scale)) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= e4m3_code(__fdiv_rn(f[4 + i], scale)) << (8 * i);
+  return make_uint2(lo, hi);
+}
+
+// Blocks of 1 x 128: 16 lanes per block, 8 values per lane; a 256-thread workgroup covers
+// 16 blocks.  nblk = rows * cols / 128.
+template <typename T>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const T* __restrict__ src, int64_t nblk,
+                                                         uint8_t* __restrict__ q, float* __restrict__ scale) {
+  const int64_t blk = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const bool live = blk < nblk;
+  float f[8];
+  float amax = 0.0f;
+  if (live) {
+    load8<T>(src + blk * 128 + sub * 8, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+  if (!live) return;
+  const float s = block_scale(amax);
+  *reinterpret_cast<uint2*>(q + blk * 128 + sub * 8) = encode8(f, s);
+  if (sub == 0) scale[blk] = s;
+}
+
+// Blocks of 128 x 128: one 256-thread workgroup per block; thread t owns columns
+// 8 (t % 16) .. +7 of rows t / 16 + 16 i.
+template <typename T>
+__global__ __launch_bounds__(256) void quant_tiles_kernel(const T* __restrict__ src, int cols, int nbc,
+                                                          uint8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ float red[4];
+  const int br = blockIdx.x / nbc, bc = blockIdx.x - br * nbc;
+  const int c0 = bc * 128 + (threadIdx.x & 15) * 8;
+  const int r0 = br * 128 + (threadIdx.x >> 4);
+  float f[8][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    load8<T>(src + static_cast<int64_t>(r0 + 16 * i) * cols + c0, f[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[i][e]));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = block_scale(amax);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint2*>(q + static_cast<int64_t>(r0 + 16 * i) * cols + c0) = encode8(f[i], s);
+  if (threadIdx.x == 0) scale[blockIdx.x] = s;
+}
+
+// x_perm_scale[row] = x_scale[token_of[row]], nb floats per row.
+__global__ __launch_bounds__(256) void gather_scales_kernel(const float* __restrict__ xs, const int32_t* __restrict__ token_of,
+                                                            int64_t A, int nb, float* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= A * nb) return;
+  const int64_t r = i / nb;
+  const int b = static_cast<int>(i - r * nb);
+  out[i] = xs[static_cast<int64_t>(token_of[r]) * nb + b];
+}
+
+// ------------------------------------------------------------------ grouped fp8 GEMM
+
+constexpr int BM = 256, BN = 128, BKB = 128, STAGES = 3;  // BKB: K bytes (= values) per stage
+constexpr int WAVES_M = 4, WAVES_N = 2, NWAVES = 8, NTHR = 512;
+constexpr int NI = 2, NJ = 2;                              // 32 x 32 blocks per wave
+constexpr int A_BYTES = BM * BKB, B_BYTES = BN * BKB;     // 32 KB, 16 KB
+constexpr int S_BYTES = BM * 4;                           // A row scales of one stage
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
+constexpr int A_DMA = A_BYTES / 1024 / NWAVES;            // 4 one-KB loads per wave
+constexpr int B_DMA = B_BYTES / 1024 / NWAVES;            // 2
+constexpr int kRsrcFlags = 0x00020000;
+enum { FP8_SWIGLU = 0, FP8_STORE = 1 };
+
+struct Fp8Args {
+  const uint8_t* A;       // [rows, K] codes
+  const float* A_scale;   // [rows, K/128]
+  const uint8_t* B;       // [G, N, K] codes
+  const float* B_scale;   // [G, N/128, K/128]
+  float* C;               // STORE: [rows, N]; SWIGLU: Act fp32 [rows, F]
+  float* H;               // SWIGLU: [rows, 2F] or NULL
+  const int32_t* offsets;
+  const int32_t* tile_prefix;
+  int G, N, K, F, nN;
+};
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcFlags);
+}
+
+// Waits until at most n (a multiple of 1 up to 8, rounded down) of this wave's vector
+// memory operations are outstanding.
+__device__ __forceinline__ void wait_vm_upto8(int n) {
+  // s_waitcnt simm16: vmcnt in bits 3:0 (and 15:14), expcnt 7 in 6:4, lgkmcnt 15 in 11:8
+  switch (n >= 8 ? 8 : (n < 0 ? 0 : n)) {
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(1024) void fp8_tile_prefix_kernel(const int32_t* __restrict__ offsets, int G,
+                                                               int32_t* __restrict__ prefix) {
+  __shared__ int s[4096];
+  for (int g = threadIdx.x; g < 4096; g += 1024) s[g] = g < G ? (offsets[g + 1] - offsets[g] + BM - 1) / BM : 0;
+  __syncthreads();
+  for (int off = 1; off < 4096; off <<= 1) {
+    int a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = threadIdx.x + 1024 * u;
+      a[u] = i >= off ? s[i - off] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s[threadIdx.x + 1024 * u] += a[u];
+    __syncthreads();
+  }
+  for (int g = threadIdx.x; g <= G; g += 1024) prefix[g] = g == 0 ? 0 : s[g - 1];
+}
+
+constexpr int kMaxKB = 128;  // K <= 16384
+
+template <int EPI>
+__global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE_BYTES];
+  __shared__ float s_bs[NJ][kMaxKB];  // the tile's weight-block scales, one row per fragment j
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+  // tile: workgroup h runs on XCD h % 8; each XCD walks a contiguous run of
+  // (expert, column tile, row tile)
+  const int h = blockIdx.x;
+  const int total = p.tile_prefix[p.G] * p.nN;
+  const int chunk = (total + 7) >> 3;
+  const int qh = h >> 3;
+  const int L = (h & 7) * chunk + qh;
+  if (qh >= chunk || L >= total) return;
+  int lo = 0, hi = p.G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.tile_prefix[mid] * p.nN <= L) lo = mid; else hi = mid - 1;
+  }
+  const int g = lo;
+  const int base = p.tile_prefix[g];
+  const int mtiles = p.tile_prefix[g + 1] - base;
+  const int local = L - base * p.nN;
+  const int nt = local / mtiles, mt = local - nt * mtiles;
+  const int row_begin = p.offsets[g] + mt * BM, row_end = p.offsets[g + 1];
+  const int a_rows = min(BM, row_end - row_begin);
+  const int KB = p.K / 128;
+  const uint8_t* Bg = p.B + static_cast<int64_t>(g) * p.N * p.K;
+  const float* Bsg = p.B_scale + static_cast<int64_t>(g) * (p.N / 128) * KB;
+
+  // B-tile row r -> weight row: fc1 interleaves 32 gate rows and 32 up rows
+  auto brow = [&](int r) -> int {
+    return EPI == FP8_SWIGLU ? (((r >> 5) & 1) ? p.F : 0) + nt * 64 + (r >> 6) * 32 + (r & 31) : nt * BN + r;
+  };
+  // per-lane DMA offsets (bytes from the stage's base)
+  int voffA[A_DMA], voffB[B_DMA];
+#pragma unroll
+  for (int q = 0; q < A_DMA; ++q) {
+    const int r = (wave * A_DMA + q) * 8 + (lane >> 3);
+    voffA[q] = r * p.K + (((lane & 7) ^ swz(r)) << 4);
+  }
+#pragma unroll
+  for (int q = 0; q < B_DMA; ++q) {
+    const int r = (wave * B_DMA + q) * 8 + (lane >> 3);
+    voffB[q] = brow(r) * p.K + (((lane & 7) ^ swz(r)) << 4);
+  }
+  const int voffS = (wave * 64 + lane) * KB * 4;  // waves 0-3 carry the 256 row scales
+  const int ndma = A_DMA + B_DMA + (wave < 4 ? 1 : 0);
+
+  auto issue = [&](int st) {
+    uint8_t* dst = lds + (st % STAGES) * STAGE_BYTES;
+    const int k0 = st * BKB;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(p.A + static_cast<int64_t>(row_begin) * p.K + k0, (a_rows - 1) * p.K + BKB);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg + k0, (p.N - 1) * p.K + BKB);
+#pragma unroll
+    for (int q = 0; q < A_DMA; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(dst + (wave * A_DMA + q) * 1024), 16, voffA[q], 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < B_DMA; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dst + A_BYTES + (wave * B_DMA + q) * 1024), 16,
+                                               voffB[q], 0, 0, 0);
+    if (wave < 4) {
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(p.A_scale + static_cast<int64_t>(row_begin) * KB + st, ((a_rows - 1) * KB + 1) * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + A_BYTES + B_BYTES + wave * 256), 4, voffS, 0, 0,
+                                               0);
+    }
+  };
+  // fragment of a 32-row block at r0, 64-wide half hh: row r0 + lane % 32, bytes
+  // 64 hh + 32 (lane / 32) .. +31
+  auto frag = [&](const uint8_t* t, int r0, int hh) -> i32x8_t {
+    const int r = r0 + (lane & 31);
+    const int c = hh * 4 + 2 * (lane >> 5);
+    const uint4 v0 = *reinterpret_cast<const uint4*>(t + r * BKB + ((c ^ swz(r)) << 4));
+    const uint4 v1 = *reinterpret_cast<const uint4*>(t + r * BKB + (((c + 1) ^ swz(r)) << 4));
+    const i32x8_t v = {static_cast<int>(v0.x), static_cast<int>(v0.y), static_cast<int>(v0.z), static_cast<int>(v0.w),
+                       static_cast<int>(v1.x), static_cast<int>(v1.y), static_cast<int>(v1.z), static_cast<int>(v1.w)};
+    return v;
+  };
+  // The weight-block scales of this tile (every wave's fragment j falls in the same
+  // 128-row block), staged in LDS once: loaded per K block in the loop they would be
+  // vector loads whose waits would also wait for the stage DMA issued before them.
+  for (int t = tid; t < NJ * KB; t += NTHR) {
+    const int j = t / KB, kb = t - j * KB;
+    s_bs[j][kb] = Bsg[(brow(j * 32) / 128) * KB + kb];
+  }
+  __syncthreads();
+
+  f32x16_t acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int nk = KB;
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nk) issue(st);
+  for (int it = 0; it < nk; ++it) {
+    wait_vm_upto8(min(STAGES - 2, nk - 1 - it) * ndma);
+    block_barrier();  // stage it is in LDS; stage it-1 is consumed
+    const uint8_t* As = lds + (it % STAGES) * STAGE_BYTES;
+    const uint8_t* Bs = As + A_BYTES;
+    const float* Ss = reinterpret_cast<const float*>(As + A_BYTES + B_BYTES);
+    i32x8_t fa[NI][2], fb[NJ][2];
+    float sa[NI], sb[NJ];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      fa[i][0] = frag(As, wm * 64 + i * 32, 0);
+      fa[i][1] = frag(As, wm * 64 + i * 32, 1);
+      sa[i] = Ss[wm * 64 + i * 32 + (lane & 31)];
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      fb[j][0] = frag(Bs, wn * 64 + j * 32, 0);
+      fb[j][1] = frag(Bs, wn * 64 + j * 32, 1);
+      sb[j] = s_bs[j][it];
+    }
+    // the stage's reads go out before the next DMA is issued: the compiler would
+    // otherwise wait for that DMA before any LDS read that follows it
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + STAGES - 1 < nk) issue(it + STAGES - 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        f32x16_t t = {};
+        t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][0], fa[i][0], t, 0, 0, 0, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j][1], fa[i][1], t, 0, 0, 0, 0, 0, 0);
+        const float f = sa[i] * sb[j];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf(t[e], f, acc[i][j][e]);
+      }
+  }
+
+  // epilogue: acc[i][j][4q + c] is row wm*64 + i*32 + lane%32, column
+  // wn*64 + j*32 + 8q + 4(lane/32) + c of the B tile
+  const int cb = 4 * (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = row_begin + wm * 64 + i * 32 + (lane & 31);
+    if (row >= row_end) continue;
+    if (EPI == FP8_SWIGLU) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = nt * 64 + wn * 32 + 8 * q + cb;
+        float4 gt, up, act;
+        gt.x = acc[i][0][4 * q]; gt.y = acc[i][0][4 * q + 1]; gt.z = acc[i][0][4 * q + 2]; gt.w = acc[i][0][4 * q + 3];
+        up.x = acc[i][1][4 * q]; up.y = acc[i][1][4 * q + 1]; up.z = acc[i][1][4 * q + 2]; up.w = acc[i][1][4 * q + 3];
+        act.x = silu_f(gt.x) * up.x; act.y = silu_f(gt.y) * up.y;
+        act.z = silu_f(gt.z) * up.z; act.w = silu_f(gt.w) * up.w;
+        if (p.H) {
+          float* hrow = p.H + static_cast<int64_t>(row) * 2 * p.F;
+          *reinterpret_cast<float4*>(hrow + col) = gt;
+          *reinterpret_cast<float4*>(hrow + p.F + col) = up;
+        }
+        *reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.F + col) = act;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * BN + wn * 64 + j * 32 + 8 * q + cb;
+          *reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.N + col) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+    }
+  }
+}
+
+}  // namespace
+
+moe_status_t launch_quantize_fp8(int src_dtype, const void* src, int64_t rows, int cols, int block_rows, uint8_t* q,
+                                 float* scale, hipStream_t s) {
+  if (block_rows == 1) {
+    const int64_t nblk = rows * (cols / 128);
+    const int64_t grid = ceil_div(nblk, 16);
+    if (src_dtype == MOE_BF16)
+      quant_rows_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), nblk, q, scale);
+    else
+      quant_rows_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(src), nblk, q, scale);
+  } else {
+    const int nbc = cols / 128;
+    const int64_t grid = (rows / 128) * nbc;
+    if (src_dtype == MOE_BF16)
+      quant_tiles_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(src), cols, nbc, q, scale);
+    else
+      quant_tiles_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(src), cols, nbc, q, scale);
+  }
+  return check_launch("quantize_fp8");
+}
+
+moe_status_t launch_gather_scales(const float* xs, const int32_t* token_of, int64_t A, int nb, float* out,
+                                  hipStream_t s) {
+  if (A == 0) return MOE_OK;
+  gather_scales_kernel<<<ceil_div(A * nb, 256), 256, 0, s>>>(xs, token_of, A, nb, out);
+  return check_launch("gather_scales");
+}
+
+size_t fp8_schedule_bytes(int E) { return static_cast<size_t>(E + 1) * 4; }
+
+// fc1 (+ SwiGLU -> H, Act fp32) when act32 != NULL and C is NULL, else fc2 -> C.
+moe_status_t launch_gemm_fp8(bool swiglu, const uint8_t* A, const float* A_scale, const uint8_t* B,
+                             const float* B_scale, float* C, float* H, const int32_t* offsets, int G, int64_t rows_upper,
+                             int N, int K, int F, int32_t* sched, hipStream_t s) {
+  if (G > 4096) return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: more than 4096 experts");
+  if (K > 128 * kMaxKB || K % 128 || N % 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: K must be a multiple of 128 up to 16384");
+  if (static_cast<int64_t>(N) * K >= (int64_t{1} << 31) || rows_upper * K >= (int64_t{1} << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: operand above 2 GB");
+  Fp8Args a{};
+  a.A = A; a.A_scale = A_scale; a.B = B; a.B_scale = B_scale; a.C = C; a.H = H;
+  a.offsets = offsets; a.tile_prefix = sched; a.G = G; a.N = N; a.K = K; a.F = F;
+  a.nN = swiglu ? F / 64 : N / BN;
+  fp8_tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, G, sched);
+  const int64_t upper = (ceil_div(rows_upper, BM) + G) * a.nN;
+  const int64_t grid = ceil_div(upper, 8) * 8;
+  if (grid == 0) return MOE_OK;
+  if (swiglu)
+    fp8_gemm_kernel<FP8_SWIGLU><<<grid, NTHR, 0, s>>>(a);
+  else
+    fp8_gemm_kernel<FP8_STORE><<<grid, NTHR, 0, s>>>(a);
+  return check_launch("gemm_fp8");
+}
+
+}  // namespace moe

@@ -19,9 +19,11 @@ moe_status_t launch_colsum(const float* X, int rows, int cols, float* out, hipSt
 
 // ---------------------------------------------------------------- permute / combine
 int64_t permute_num_chunks(int T);
+// elem_bytes: bytes per element of x (0: the activation dtype's; 1 for e4m3 rows)
 moe_status_t launch_permute(const moe_config_t& c, const void* x, const int32_t* idx, int32_t* offsets,
                             int32_t* row_of, int32_t* token_of, void* x_perm, int32_t* blk_hist,
-                            int32_t* blk_base, int32_t* counts_ws, bool hist_ready, hipStream_t s);
+                            int32_t* blk_base, int32_t* counts_ws, bool hist_ready, hipStream_t s,
+                            int elem_bytes = 0);
 // y = sum_j w Y_perm[row] + Y_s  (all fp32)
 moe_status_t launch_combine(const moe_config_t& c, const float* Y, const int32_t* row_of, const float* w,
                             const float* Y_s, float* y, hipStream_t s);
@@ -30,6 +32,17 @@ moe_status_t launch_unpermute_reduce(const moe_config_t& c, const float* dX, con
                                      const float* dx_s, const float* dx_r, float* dx, hipStream_t s);
 moe_status_t launch_combine_bwd(const moe_config_t& c, const float* dy, const float* Y, const int32_t* row_of,
                                 const float* w, void* dY, float* dw, void* dY_s, hipStream_t s);
+
+// ---------------------------------------------------------------- fp8 experts
+moe_status_t launch_quantize_fp8(int src_dtype, const void* src, int64_t rows, int cols, int block_rows, uint8_t* q,
+                                 float* scale, hipStream_t s);
+moe_status_t launch_gather_scales(const float* xs, const int32_t* token_of, int64_t A, int nb, float* out,
+                                  hipStream_t s);
+size_t fp8_schedule_bytes(int E);
+// swiglu: fc1 of width N = 2F, Act (fp32) -> C [rows, F], H (optional); else C [rows, N]
+moe_status_t launch_gemm_fp8(bool swiglu, const uint8_t* A, const float* A_scale, const uint8_t* B,
+                             const float* B_scale, float* C, float* H, const int32_t* offsets, int G, int64_t rows_upper,
+                             int N, int K, int F, int32_t* sched, hipStream_t s);
 
 // ---------------------------------------------------------------- GEMMs
 // Storage of an operand: K_MAJOR = [rows][K] (K contiguous), MN_MAJOR = [K][rows].

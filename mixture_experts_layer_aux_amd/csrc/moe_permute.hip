@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restric
         part += g[i] * y[i];
         g[i] *= wj;
       }
-      G8<TACT>::store(dY, static_cast<int64_t>(r) * groups + u, g);
+      if (dY) G8<TACT>::store(dY, static_cast<int64_t>(r) * groups + u, g);
     }
     part = wave_sum(part);
     if (lane == j) my_dw = part;
@@ -246,7 +246,8 @@ int64_t permute_num_chunks(int T) { return ceil_div(T, kChunk); }
 
 moe_status_t launch_permute(const moe_config_t& c, const void* x, const int32_t* idx, int32_t* offsets,
                             int32_t* row_of, int32_t* token_of, void* x_perm, int32_t* blk_hist,
-                            int32_t* blk_base, int32_t* counts_ws, bool hist_ready, hipStream_t s) {
+                            int32_t* blk_base, int32_t* counts_ws, bool hist_ready, hipStream_t s,
+                            int elem_bytes) {
   const int nblk = static_cast<int>(permute_num_chunks(c.T));
   if (!hist_ready)
     chunk_hist_kernel<<<nblk, 64, c.E * sizeof(int), s>>>(idx, c.T, c.E, c.k, blk_hist);
@@ -254,7 +255,7 @@ moe_status_t launch_permute(const moe_config_t& c, const void* x, const int32_t*
   offsets_kernel<<<1, 1024, 0, s>>>(counts_ws, c.E, offsets);
   permute_index_kernel<<<nblk, 64, c.E * sizeof(unsigned long long), s>>>(idx, c.T, c.E, c.k, offsets, blk_base,
                                                                           row_of, token_of);
-  const int units = static_cast<int>(static_cast<int64_t>(c.d) * act_bytes(c) / 16);
+  const int units = static_cast<int>(static_cast<int64_t>(c.d) * (elem_bytes ? elem_bytes : act_bytes(c)) / 16);
   permute_copy_kernel<<<static_cast<int>(ceil_div(c.T, 4)), 256, 0, s>>>(
       static_cast<const uint4*>(x), c.T, units, c.k, row_of, static_cast<uint4*>(x_perm));
   return check_launch("permute");

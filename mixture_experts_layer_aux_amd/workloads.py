@@ -61,6 +61,8 @@ class LayerShape:
     init: str = "std002"        # "fan_in" | "std002"
     bias: str = "none"          # "none" | "expert_bias" | "zipf" | "skew"
     skew_beta: float = 0.0      # hot-expert logit bias for bias == "skew"
+    wq: str = ""                # "fp8": expert weights are given as fp32 masters, to be
+                                # quantised to e4m3 in 128 x 128 blocks by each side
 
     @property
     def A(self) -> int:
@@ -81,8 +83,8 @@ CONFIGS: Dict[int, LayerShape] = {
                   score="sigmoid", act="bf16", aux_coeff=0.0, bias="expert_bias"),
     4: LayerShape("qwen3-next-shaped-bf16", T=32768, d=2048, E=512, k=10, F=512, Fs=512,
                   score="softmax", act="bf16", aux_coeff=0.0, bias="zipf"),
-    5: LayerShape("skewed-896x16-bf16", T=16384, d=4096, E=896, k=16, F=512, Fs=0,
-                  score="softmax", act="bf16", aux_coeff=0.0, bias="skew", skew_beta=1.46),
+    5: LayerShape("skewed-896x16-fp8", T=16384, d=4096, E=896, k=16, F=512, Fs=0,
+                  score="softmax", act="bf16", aux_coeff=0.0, bias="skew", skew_beta=1.46, wq="fp8"),
 }
 
 # Reduced layers with the same router, bias law and dtype as the full ones, at sizes the
@@ -95,8 +97,10 @@ SMALL: Dict[int, LayerShape] = {
                F=256, Fs=384),
     4: replace(CONFIGS[4], name="qwen3-next-shaped-reduced", T=2048, d=512, E=64, k=10,
                F=128, Fs=256),
-    5: replace(CONFIGS[5], name="skewed-reduced", T=1024, d=512, E=112, k=16, F=128),
+    5: replace(CONFIGS[5], name="skewed-reduced-bf16", T=1024, d=512, E=112, k=16, F=128, wq=""),
 }
+# The skewed layer with its e4m3 experts, at the reduced size.
+SMALL_FP8 = replace(CONFIGS[5], name="skewed-reduced-fp8", T=1024, d=512, E=112, k=16, F=128)
 
 
 def _stream(seed: int, tid: int, chunk: int = 0) -> np.random.Generator:
@@ -196,8 +200,9 @@ def make_inputs(shape: LayerShape, seed: int, with_dy: bool = True, threads: Opt
         bg, eb = selection_bias(shape, seed)
         out["bg"], out["expert_bias"] = bg, eb
         if with_experts:
-            out["W13"] = _expert_stack(seed, _TID_W13, E, 2 * F, d, weight_std(shape, d), act, pool)
-            out["W2"] = _expert_stack(seed, _TID_W2, E, d, F, weight_std(shape, F), act, pool)
+            wact = "f32" if shape.wq == "fp8" else act     # fp8 experts: fp32 masters
+            out["W13"] = _expert_stack(seed, _TID_W13, E, 2 * F, d, weight_std(shape, d), wact, pool)
+            out["W2"] = _expert_stack(seed, _TID_W2, E, d, F, weight_std(shape, F), wact, pool)
             if Fs:
                 out["W13s"] = _normal_rows(seed, _TID_W13S, 2 * Fs, d, weight_std(shape, d), act, pool)
                 out["W2s"] = _normal_rows(seed, _TID_W2S, d, Fs, weight_std(shape, Fs), act, pool)
@@ -212,8 +217,9 @@ def expert_weights(shape: LayerShape, seed: int, experts, threads: Optional[int]
     """Regenerates the routed weights of only the listed experts (same bytes as make_inputs)."""
     d, F = shape.d, shape.F
     with ThreadPoolExecutor(_threads(threads)) as pool:
-        W13 = _expert_stack(seed, _TID_W13, shape.E, 2 * F, d, weight_std(shape, d), shape.act, pool, experts)
-        W2 = _expert_stack(seed, _TID_W2, shape.E, d, F, weight_std(shape, F), shape.act, pool, experts)
+        wact = "f32" if shape.wq == "fp8" else shape.act
+        W13 = _expert_stack(seed, _TID_W13, shape.E, 2 * F, d, weight_std(shape, d), wact, pool, experts)
+        W2 = _expert_stack(seed, _TID_W2, shape.E, d, F, weight_std(shape, F), wact, pool, experts)
     return W13, W2
 
 

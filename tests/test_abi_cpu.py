@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_declared_entry_point():
     lib = L.load()
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 20
     assert sorted(L.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -53,7 +53,10 @@ def test_valid_configs():
     (dict(T=2 ** 28, k=8), L.MOE_ERR_INVALID_ARG),    # T * k >= 2^31
     (dict(routed_scaling=0.0), L.MOE_ERR_INVALID_ARG),
     (dict(act_dtype=7), L.MOE_ERR_INVALID_ARG),
-    (dict(reserved=1), L.MOE_ERR_INVALID_ARG),
+    (dict(w_dtype=7), L.MOE_ERR_INVALID_ARG),
+    (dict(w_dtype=L.MOE_FP8_E4M3, act_dtype=L.MOE_F32, F=1024), L.MOE_ERR_UNSUPPORTED),   # fp8 needs bf16 x
+    (dict(w_dtype=L.MOE_FP8_E4M3, d=2048 + 64), L.MOE_ERR_UNSUPPORTED),                  # fp8 needs d % 128
+    (dict(w_dtype=L.MOE_FP8_E4M3, Fs=1024), L.MOE_ERR_UNSUPPORTED),                      # no fp8 shared expert
 ])
 def test_config_rules(change, status):
     cfg = L.config_from_shape(W.CONFIGS[2])
@@ -61,6 +64,33 @@ def test_config_rules(change, status):
         setattr(cfg, k, v)
     assert _status(cfg) == status
     assert L.load().moe_last_error()
+
+
+def test_fp8_layers_validate():
+    assert _status(L.config_from_shape(W.CONFIGS[5])) == L.MOE_OK
+    assert _status(L.config_from_shape(W.SMALL_FP8)) == L.MOE_OK
+    assert L.is_fp8(L.config_from_shape(W.CONFIGS[5]))
+
+
+def test_quantize_fp8_rejects_bad_shapes_before_launching():
+    lib = L.load()
+    fake = P(1 << 20)
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    assert lib.moe_quantize_fp8(i32(L.MOE_BF16), fake, i64(4), i32(100), i32(1), fake, fake, P(None)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(i32(L.MOE_BF16), fake, i64(100), i32(128), i32(128), fake, fake, P(None)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(i32(L.MOE_BF16), fake, i64(128), i32(128), i32(64), fake, fake, P(None)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_fp8(i32(9), fake, i64(128), i32(128), i32(1), fake, fake, P(None)) == L.MOE_ERR_INVALID_ARG
+    # the fp8 layer calls need the fp8 config, and the fp8 backward refuses expert gradients
+    cfg = L.config_from_shape(W.CONFIGS[2])
+    st = lib.moe_permute_fp8(ctypes.byref(cfg), *([fake] * 8), fake, ctypes.c_size_t(1 << 40), P(None))
+    assert st == L.MOE_ERR_INVALID_ARG and b"fp8" in lib.moe_last_error()
+    c8 = L.config_from_shape(W.CONFIGS[5])
+    w = L.Weights(Wg=1 << 20, W13=1 << 20, W2=1 << 20)
+    sv = L.Saved(**{n: 1 << 20 for n, _ in L.Saved._fields_})
+    g = L.Grads(dWg=1 << 20, dW13=1 << 20)
+    st = lib.moe_layer_bwd(ctypes.byref(c8), ctypes.byref(w), ctypes.byref(sv), fake, fake, ctypes.c_float(1.0), fake,
+                           ctypes.byref(g), fake, ctypes.c_size_t(1 << 40), P(None))
+    assert st == L.MOE_ERR_INVALID_ARG and b"frozen" in lib.moe_last_error()
 
 
 def test_sigmoid_top1_is_allowed_and_fp32_f192_is_allowed():
