@@ -133,6 +133,104 @@ def cpu_baseline(shape, inp, tokens: int):
                         f"BLAS threads; fp64 weight copies made before timing"))
 
 
+PHASES_FP8 = ["gate", "router", "quantize_x", "permute", "experts_fwd", "combine", "combine_bwd", "router_bwd",
+              "gate_bwd"]
+PEAK_FP8_TFLOPS = 5033.2
+
+
+def bench_fp8(args, shape, cfg, inp, up, dev) -> int:
+    """The layer with e4m3 experts: the forward plus the backward through the router path
+    (the experts are frozen).  The e4m3 weights come from the fp32 masters through the
+    library's quantiser before timing."""
+    import torch
+
+    from mixture_experts_layer_aux_amd import _lib as L
+    from mixture_experts_layer_aux_amd import workloads as W
+
+    T, d, E, k, F, A = shape.T, shape.d, shape.E, shape.k, shape.F, shape.A
+    f32, u8 = torch.float32, torch.uint8
+    e = lambda *s_, dt=f32: torch.empty(*s_, dtype=dt, device=dev)  # noqa: E731
+    W13m, W2m = up(inp["W13"]), up(inp["W2"])
+    W13q, W13s = e(E, 2 * F, d, dt=u8), e(E * 2 * F // 128, d // 128)
+    W2q, W2s = e(E, d, F, dt=u8), e(E * d // 128, F // 128)
+    L.quantize_fp8(W13m.view(E * 2 * F, d), 128, W13q.view(E * 2 * F, d), W13s)
+    L.quantize_fp8(W2m.view(E * d, F), 128, W2q.view(E * d, F), W2s)
+    torch.cuda.synchronize()
+    del W13m, W2m
+    Wg, bg = up(inp["Wg"]), up(inp["bg"])
+    x = up(inp["x"])
+    dy = up(W.to_f32(inp["dy"], shape.act))
+    S = L.alloc_saved(cfg, dev)
+    ws = L.alloc_workspace(cfg, dev)
+    xq, xs = e(T, d, dt=u8), e(T, d // 128)
+    y, dx, dw, dlogits = e(T, d), e(T, d), e(T, k), e(T, E)
+    dWg, dbg = e(E, d), (e(E) if bg is not None else None)
+    stats = e(L.MOE_NSTATS)
+
+    def step(ev):
+        i = 0
+
+        def mark():
+            nonlocal i
+            if ev is not None:
+                ev[i].record()
+            i += 1
+
+        mark()
+        L.gate_logits(cfg, x, Wg, bg, S["logits"])
+        mark()
+        L.router_topk(cfg, S["logits"], None, S["idx"], S["w"], S["counts"], None, stats, ws)
+        mark()
+        L.quantize_fp8(x, 1, xq, xs)
+        mark()
+        L.permute_fp8(cfg, xq, xs, S["idx"], S["offsets"], S["row_of"], S["token_of"], S["x_perm"],
+                      S["x_perm_scale"], ws)
+        mark()
+        L.grouped_gemm_swiglu_fp8(cfg, S["x_perm"], S["x_perm_scale"], S["offsets"], W13q, W13s.view(-1), W2q,
+                                  W2s.view(-1), None, S["Act"], S["Act_scale"], S["Y_perm"], ws)
+        mark()
+        L.unpermute_combine(cfg, S["Y_perm"], S["row_of"], S["w"], None, y)
+        mark()
+        L.unpermute_combine_bwd(cfg, dy, S["Y_perm"], S["row_of"], S["w"], None, dw, None)
+        mark()
+        L.router_bwd(cfg, S["logits"], S["idx"], S["w"], dw, S["counts"], 1.0, dlogits)
+        mark()
+        L.gate_logits_bwd(cfg, x, Wg, dlogits, dWg, dbg, dx)
+        mark()
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(PHASES_FP8) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        step(events[st])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    phase_ms = {p: float(np.mean([events[st][i].elapsed_time(events[st][i + 1]) for st in range(args.steps)]))
+                for i, p in enumerate(PHASES_FP8)}
+    ms_step = elapsed * 1e3 / args.steps
+    st_ = stats.cpu().numpy()
+    flop = 6.0 * d * F * A                                   # fc1 (4 d F) + fc2 (2 d F) per routed row
+    ms = phase_ms["experts_fwd"]
+    tf = flop / (ms * 1e-3) / 1e12
+    out = dict(
+        metric="MoE layer fwd+bwd tokens/s on 1 MI355X", value=round(T / (ms_step * 1e-3), 1), unit="tokens/s",
+        n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=round(ms_step, 3), higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="fp8-e4m3 experts, bf16 activations",
+        data="synthetic (seeded generator, random-init weights)",
+        config=dict(workload=shape.name, T=T, d=d, E=E, k=k, F=F, Fs=0, score=shape.score, bias=shape.bias,
+                    passes="forward + router-path backward (frozen fp8 experts)", parallelism="single GPU"),
+        roofline=dict(kernel="grouped fp8 SwiGLU experts forward (fc1 GEMM + Act quantiser + fc2 GEMM)",
+                      bound="mfma", achieved=round(tf, 2), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                      frac=round(tf / PEAK_FP8_TFLOPS, 4), traffic=None, flop_per_step=flop, ms_per_step=round(ms, 4)),
+        phases_ms={p: round(v, 4) for p, v in phase_ms.items()},
+        load=dict(maxvio=round(float(st_[1]), 4), empty_experts=int(st_[2]), max_count=int(st_[3]),
+                  mean_count=T * k / E))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +283,8 @@ def main() -> int:
         return torch.from_numpy(a).to(dev)
 
     T, d, E, k, F, Fs, A = shape.T, shape.d, shape.E, shape.k, shape.F, shape.Fs, shape.A
+    if shape.wq == "fp8":
+        return bench_fp8(args, shape, cfg, inp, up, dev)
     Wt = dict(Wg=up(inp["Wg"]), bg=up(inp["bg"]), expert_bias=up(inp["expert_bias"]), W13=up(inp["W13"]),
               W2=up(inp["W2"]), W13s=up(inp["W13s"]), W2s=up(inp["W2s"]))
     x = up(inp["x"])
