@@ -177,7 +177,7 @@ def bench_fp8(args, shape, cfg, inp, up, dev) -> int:
             i += 1
 
         mark()
-        L.gate_logits(cfg, x, Wg, bg, S["logits"])
+        L.gate_logits(cfg, x, Wg, bg, S["logits"], ws)
         mark()
         L.router_topk(cfg, S["logits"], None, S["idx"], S["w"], S["counts"], None, stats, ws)
         mark()
@@ -195,7 +195,7 @@ def bench_fp8(args, shape, cfg, inp, up, dev) -> int:
         mark()
         L.router_bwd(cfg, S["logits"], S["idx"], S["w"], dw, S["counts"], 1.0, dlogits)
         mark()
-        L.gate_logits_bwd(cfg, x, Wg, dlogits, dWg, dbg, dx)
+        L.gate_logits_bwd(cfg, x, Wg, dlogits, dWg, dbg, dx, ws)
         mark()
 
     for _ in range(args.warmup):
@@ -319,7 +319,7 @@ def main() -> int:
             i += 1
 
         mark()
-        L.gate_logits(cfg, x, Wt["Wg"], Wt["bg"], S["logits"])
+        L.gate_logits(cfg, x, Wt["Wg"], Wt["bg"], S["logits"], ws)
         mark()
         L.router_topk(cfg, S["logits"], Wt["expert_bias"], S["idx"], S["w"], S["counts"], None, stats, ws)
         mark()
@@ -346,7 +346,7 @@ def main() -> int:
         mark()
         L.router_bwd(cfg, S["logits"], S["idx"], S["w"], dw, S["counts"], 1.0, dlogits)
         mark()
-        L.gate_logits_bwd(cfg, x, Wt["Wg"], dlogits, G["dWg"], G.get("dbg"), dx_r)
+        L.gate_logits_bwd(cfg, x, Wt["Wg"], dlogits, G["dWg"], G.get("dbg"), dx_r, ws)
         mark()
         L.permute_bwd(cfg, dX_perm, S["row_of"], dx_s, dx_r, dx)
         mark()

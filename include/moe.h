@@ -152,9 +152,12 @@ moe_status_t moe_validate(const moe_config_t* cfg);
 moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* fwd_bytes, size_t* bwd_bytes);
 
 /* Router logits = x Wg^T (+ bg), fp32 ([HB] §3.1 Router scoring, Precision: the router's
- * linear layer runs in fp32).  x act dtype [T, d]; logits [T, E]. */
+ * linear layer runs in fp32).  x act dtype [T, d]; logits [T, E].  With bf16 activations
+ * and E % 16 == 0 it runs on the bf16 matrix cores through an exact three-way bf16 split
+ * of Wg (every product exact, fp32 accumulation); otherwise as an fp32 FMA GEMM.
+ * ws: the workspace of moe_workspace_size (scratch for the split and the partial sums). */
 moe_status_t moe_gate_logits(const moe_config_t* cfg, const void* x, const float* Wg, const float* bg,
-                             float* logits, void* stream);
+                             float* logits, void* ws, size_t ws_bytes, void* stream);
 
 /* Top-k router ([HB] §3.1 Gating function and Output scale; §3.3 Aux loss):
  *   keys: softmax -> the logits; sigmoid -> sigma(l) + expert_bias, evaluated in fp64;
@@ -287,9 +290,13 @@ moe_status_t moe_router_bwd(const moe_config_t* cfg, const float* logits, const 
                             const float* dw, const int32_t* counts, float daux, float* dlogits, void* stream);
 
 /* Gate backward: dWg = dlogits^T x [E, d]; dbg = column sums of dlogits (NULL ok);
- * dx_r = dlogits Wg [T, d] fp32 (NULL ok). */
+ * dx_r = dlogits Wg [T, d] fp32 (NULL ok).  On the matrix cores like moe_gate_logits, with
+ * dlogits split three ways (dWg) and both operands split (dx_r: the six part products
+ * whose sum reaches fp32 precision); column sums in a fixed order.  ws as in
+ * moe_gate_logits. */
 moe_status_t moe_gate_logits_bwd(const moe_config_t* cfg, const void* x, const float* Wg,
-                                 const float* dlogits, float* dWg, float* dbg, float* dx_r, void* stream);
+                                 const float* dlogits, float* dWg, float* dbg, float* dx_r, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /* Whole backward from the saved forward tensors.
  * fp8 experts are frozen (no expert gradients): grads->dW13, dW2, dW13s, dW2s must be

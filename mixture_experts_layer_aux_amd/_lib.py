@@ -144,12 +144,14 @@ def _ws(ws: torch.Tensor) -> Tuple[int, int]:
 
 # ----------------------------------------------------------------- entry points
 
-def gate_logits(cfg, x, Wg, bg, logits, stream=None):
+def gate_logits(cfg, x, Wg, bg, logits, ws, stream=None):
     ad = act_dtype(cfg)
+    wp, wn = _ws(ws)
     _check(load().moe_gate_logits(ctypes.byref(cfg), _P(_ptr(x, ad, cfg.T * cfg.d, "x")),
                                   _P(_ptr(Wg, torch.float32, cfg.E * cfg.d, "Wg")),
                                   _P(_ptr(bg, torch.float32, cfg.E, "bg")),
-                                  _P(_ptr(logits, torch.float32, cfg.T * cfg.E, "logits")), _P(_stream(stream))))
+                                  _P(_ptr(logits, torch.float32, cfg.T * cfg.E, "logits")), _P(wp), ctypes.c_size_t(wn),
+                                  _P(_stream(stream))))
 
 
 def router_topk(cfg, logits, expert_bias, idx, w, counts, prob_sum, stats, ws, stream=None):
@@ -295,14 +297,16 @@ def router_bwd(cfg, logits, idx, w, dw, counts, daux, dlogits, stream=None):
                                  _P(_stream(stream))))
 
 
-def gate_logits_bwd(cfg, x, Wg, dlogits, dWg, dbg, dx_r, stream=None):
+def gate_logits_bwd(cfg, x, Wg, dlogits, dWg, dbg, dx_r, ws, stream=None):
     ad = act_dtype(cfg)
+    wp, wn = _ws(ws)
     _check(load().moe_gate_logits_bwd(ctypes.byref(cfg), _P(_ptr(x, ad, cfg.T * cfg.d, "x")),
                                       _P(_ptr(Wg, torch.float32, cfg.E * cfg.d, "Wg")),
                                       _P(_ptr(dlogits, torch.float32, cfg.T * cfg.E, "dlogits")),
                                       _P(_ptr(dWg, torch.float32, cfg.E * cfg.d, "dWg")),
                                       _P(_ptr(dbg, torch.float32, cfg.E, "dbg")),
-                                      _P(_ptr(dx_r, torch.float32, cfg.T * cfg.d, "dx_r")), _P(_stream(stream))))
+                                      _P(_ptr(dx_r, torch.float32, cfg.T * cfg.d, "dx_r")), _P(wp),
+                                      ctypes.c_size_t(wn), _P(_stream(stream))))
 
 
 def _weights_struct(cfg, W: Dict[str, torch.Tensor]) -> Weights:

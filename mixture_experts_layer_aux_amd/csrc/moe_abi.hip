@@ -51,6 +51,7 @@ struct FwdWs {
   uint8_t* xq;         // fp8 experts: [T, d] e4m3 codes of x
   float* xs;           // fp8 experts: [T, d/128] their scales
   float* act32;        // fp8 experts: [A, F] fp32 SwiGLU output before quantisation
+  void* gate;          // router GEMM scratch (gate_fwd_ws_bytes)
   size_t bytes;
 };
 
@@ -78,6 +79,7 @@ FwdWs carve_fwd(const moe_config_t& c, void* base) {
     w.xs = reinterpret_cast<float*>(take(T * (c.d / 128) * 4));
     w.act32 = reinterpret_cast<float*>(take(A * c.F * 4));
   }
+  w.gate = take(gate_fwd_ws_bytes(c));
   w.bytes = off;
   return w;
 }
@@ -93,6 +95,7 @@ struct BwdWs {
   void* dY_s;      // [T, d] act: the shared expert's upstream gradient
   float* dact;     // fp32 path: [max(A, T), max(F, Fs)]
   int32_t* sched;  // [E + 1]
+  void* gate;      // router GEMM scratch (gate_bwd_ws_bytes)
   size_t bytes;
 };
 
@@ -116,6 +119,7 @@ BwdWs carve_bwd(const moe_config_t& c, void* base) {
   w.dY_s = c.Fs ? take(T * c.d * eb) : nullptr;
   w.dact = c.act_dtype == MOE_F32 ? reinterpret_cast<float*>(take(std::max(A, T) * std::max(c.F, c.Fs) * 4)) : nullptr;
   w.sched = reinterpret_cast<int32_t*>(take(mfma_schedule_bytes(c.E)));
+  w.gate = take(gate_bwd_ws_bytes(c));
   w.bytes = off;
   return w;
 }
@@ -176,7 +180,8 @@ hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 
 // ----------------------------------------------------------------- launch sequences
 moe_status_t run_gate(const moe_config_t& c, const void* x, const float* Wg, const float* bg, float* logits,
-                      hipStream_t s) {
+                      void* gate_ws, hipStream_t s) {
+  if (gate_on_mfma(c)) return launch_gate_fwd_mfma(c, x, Wg, bg, logits, gate_ws, s);
   GemmDesc g{};
   g.a_major = K_MAJOR; g.b_major = K_MAJOR; g.ragged = RAGGED_M; g.epi = bg ? EPI_STORE_BIAS : EPI_STORE;
   g.a_type = c.act_dtype; g.b_type = MOE_F32; g.c_type = MOE_F32;
@@ -311,7 +316,8 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
 }
 
 moe_status_t run_gate_bwd(const moe_config_t& c, const void* x, const float* Wg, const float* dlogits, float* dWg,
-                          float* dbg, float* dx_r, hipStream_t s) {
+                          float* dbg, float* dx_r, void* gate_ws, hipStream_t s) {
+  if (gate_on_mfma(c)) return launch_gate_bwd_mfma(c, x, Wg, dlogits, dWg, dbg, dx_r, gate_ws, s);
   GemmDesc gw{};
   gw.a_major = MN_MAJOR; gw.b_major = MN_MAJOR; gw.ragged = RAGGED_K; gw.epi = EPI_STORE;
   gw.a_type = MOE_F32; gw.b_type = c.act_dtype; gw.c_type = MOE_F32;
@@ -319,7 +325,7 @@ moe_status_t run_gate_bwd(const moe_config_t& c, const void* x, const float* Wg,
   gw.A = dlogits; gw.lda = c.E; gw.B = x; gw.ldb = c.d; gw.C = dWg; gw.ldc = c.d;
   gw.range_end = c.T;
   MOE_TRY(launch_gemm_fma(gw, s));
-  if (dbg) MOE_TRY(launch_colsum(dlogits, c.T, c.E, dbg, s));
+  if (dbg) MOE_TRY(launch_colsum_ws(dlogits, c.T, c.E, dbg, static_cast<float*>(gate_ws), s));
   if (dx_r) {
     GemmDesc gx{};
     gx.a_major = K_MAJOR; gx.b_major = MN_MAJOR; gx.ragged = RAGGED_M; gx.epi = EPI_STORE;
@@ -366,10 +372,12 @@ moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* fwd_bytes, size
 }
 
 moe_status_t moe_gate_logits(const moe_config_t* cfg, const void* x, const float* Wg, const float* bg,
-                             float* logits, void* stream) {
+                             float* logits, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate(cfg));
-  MOE_NEED(x); MOE_NEED(Wg); MOE_NEED(logits);
-  return run_gate(*cfg, x, Wg, bg, logits, S(stream));
+  MOE_NEED(x); MOE_NEED(Wg); MOE_NEED(logits); MOE_NEED(ws);
+  const FwdWs fw = carve_fwd(*cfg, ws);
+  MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
+  return run_gate(*cfg, x, Wg, bg, logits, fw.gate, S(stream));
 }
 
 moe_status_t moe_router_topk(const moe_config_t* cfg, const float* logits, const float* expert_bias, int32_t* idx,
@@ -446,7 +454,7 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
   const moe_config_t& c = *cfg;
   hipStream_t s = S(stream);
-  MOE_TRY(run_gate(c, x, W->Wg, W->bg, sv->logits, s));
+  MOE_TRY(run_gate(c, x, W->Wg, W->bg, sv->logits, fw.gate, s));
   MOE_TRY(launch_router_topk(c, sv->logits, W->expert_bias, sv->idx, sv->w, sv->counts, fw.prob_sum, stats,
                              fw.cnt_part, fw.prob_part, s));
   if (fp8) {
@@ -576,10 +584,12 @@ moe_status_t moe_router_bwd(const moe_config_t* cfg, const float* logits, const 
 }
 
 moe_status_t moe_gate_logits_bwd(const moe_config_t* cfg, const void* x, const float* Wg, const float* dlogits,
-                                 float* dWg, float* dbg, float* dx_r, void* stream) {
+                                 float* dWg, float* dbg, float* dx_r, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate(cfg));
-  MOE_NEED(x); MOE_NEED(Wg); MOE_NEED(dlogits); MOE_NEED(dWg);
-  return run_gate_bwd(*cfg, x, Wg, dlogits, dWg, dbg, dx_r, S(stream));
+  MOE_NEED(x); MOE_NEED(Wg); MOE_NEED(dlogits); MOE_NEED(dWg); MOE_NEED(ws);
+  const BwdWs bw = carve_bwd(*cfg, ws);
+  MOE_TRY(need_ws(ws_bytes, bw.bytes, __func__));
+  return run_gate_bwd(*cfg, x, Wg, dlogits, dWg, dbg, dx_r, bw.gate, S(stream));
 }
 
 moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, const moe_saved_t* sv, const void* x,
@@ -601,7 +611,7 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
     MOE_TRY(launch_combine_bwd(c, dy, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, nullptr, bw.dw,
                                nullptr, s));
     MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, daux, bw.dlogits, s));
-    return run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, dx, s);
+    return run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, dx, bw.gate, s);
   }
   MOE_NEED16(sv->x_perm); MOE_NEED16(sv->H); MOE_NEED16(sv->Act); MOE_NEED16(gr->dW13); MOE_NEED16(gr->dW2);
   if (cfg->Fs) {
@@ -620,7 +630,7 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
                           gr->dW13, gr->dW2, x, W->W13s, W->W2s, sv->H_s, sv->Act_s, dY_s, bw.dH_s, bw.dx_s, gr->dW13s,
                           gr->dW2s, bw.sched, bw.dact, s));
   MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, daux, bw.dlogits, s));
-  MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, s));
+  MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, bw.gate, s));
   return launch_unpermute_reduce(c, static_cast<const float*>(bw.dYX), sv->row_of,
                                  c.Fs ? static_cast<const float*>(bw.dx_s) : nullptr, bw.dx_r, dx, s);
 }

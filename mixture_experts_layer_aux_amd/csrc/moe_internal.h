@@ -15,7 +15,6 @@ moe_status_t launch_router_topk(const moe_config_t& c, const float* logits, cons
                                 int32_t* cnt_part, float* prob_part, hipStream_t s);
 moe_status_t launch_router_bwd(const moe_config_t& c, const float* logits, const int32_t* idx, const float* w,
                                const float* dw, const int32_t* counts, float daux, float* dlogits, hipStream_t s);
-moe_status_t launch_colsum(const float* X, int rows, int cols, float* out, hipStream_t s);
 
 // ---------------------------------------------------------------- permute / combine
 int64_t permute_num_chunks(int T);
@@ -32,6 +31,25 @@ moe_status_t launch_unpermute_reduce(const moe_config_t& c, const float* dX, con
                                      const float* dx_s, const float* dx_r, float* dx, hipStream_t s);
 moe_status_t launch_combine_bwd(const moe_config_t& c, const float* dy, const float* Y, const int32_t* row_of,
                                 const float* w, void* dY, float* dw, void* dY_s, hipStream_t s);
+
+#define MOE_TRY_INTERNAL(x)      \
+  do {                           \
+    const moe_status_t _st = (x); \
+    if (_st != MOE_OK) return _st; \
+  } while (0)
+
+// ---------------------------------------------------------------- router GEMMs (fp32)
+// On the bf16 matrix cores through exact bf16 splits of the fp32 operand when the
+// activations are bf16 and E % 16 == 0; the fp32 FMA GEMM otherwise.
+bool gate_on_mfma(const moe_config_t& c);
+size_t gate_fwd_ws_bytes(const moe_config_t& c);
+size_t gate_bwd_ws_bytes(const moe_config_t& c);
+moe_status_t launch_gate_fwd_mfma(const moe_config_t& c, const void* x, const float* Wg, const float* bg,
+                                  float* logits, void* ws, hipStream_t s);
+moe_status_t launch_gate_bwd_mfma(const moe_config_t& c, const void* x, const float* Wg, const float* dlogits,
+                                  float* dWg, float* dbg, float* dx_r, void* ws, hipStream_t s);
+// column sums in a fixed order; part: ceil(rows / 256) * cols floats of scratch
+moe_status_t launch_colsum_ws(const float* X, int rows, int cols, float* out, float* part, hipStream_t s);
 
 // ---------------------------------------------------------------- fp8 experts
 moe_status_t launch_quantize_fp8(int src_dtype, const void* src, int64_t rows, int cols, int block_rows, uint8_t* q,

@@ -316,22 +316,6 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
     if (lane + 64 * i < E) out[lane + 64 * i] = val[i];
 }
 
-// Column sums of a [rows, cols] fp32 matrix in a fixed order (4 contiguous row quarters,
-// then their sums in quarter order).
-__global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ X, int rows, int cols,
-                                                     float* __restrict__ out) {
-  __shared__ float part[4][64];
-  const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
-  const int col = blockIdx.x * 64 + c;
-  const int q = (rows + 3) / 4;
-  const int r0 = r * q, r1 = min(rows, r0 + q);
-  float s = 0.0f;
-  if (col < cols)
-    for (int i = r0; i < r1; ++i) s += X[static_cast<int64_t>(i) * cols + col];
-  part[r][c] = s;
-  __syncthreads();
-  if (r == 0 && col < cols) out[col] = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
-}
 
 }  // namespace
 
@@ -403,9 +387,5 @@ moe_status_t launch_router_bwd(const moe_config_t& c, const float* logits, const
   return check_launch("router_bwd");
 }
 
-moe_status_t launch_colsum(const float* X, int rows, int cols, float* out, hipStream_t s) {
-  colsum_kernel<<<static_cast<int>(ceil_div(cols, 64)), 256, 0, s>>>(X, rows, cols, out);
-  return check_launch("colsum");
-}
 
 }  // namespace moe

@@ -121,9 +121,9 @@ def test_entry_points_reject_bad_arguments_before_launching():
     nul = P(None)
     s = P(None)
     # NULL config
-    assert lib.moe_gate_logits(None, fake, fake, nul, fake, s) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_gate_logits(None, fake, fake, nul, fake, fake, ctypes.c_size_t(1 << 40), s) == L.MOE_ERR_INVALID_ARG
     # NULL required pointer
-    assert lib.moe_gate_logits(ctypes.byref(cfg), nul, fake, nul, fake, s) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_gate_logits(ctypes.byref(cfg), nul, fake, nul, fake, fake, ctypes.c_size_t(1 << 40), s) == L.MOE_ERR_INVALID_ARG
     assert b"x is NULL" in lib.moe_last_error()
     # workspace too small
     st = lib.moe_router_topk(ctypes.byref(cfg), fake, nul, fake, fake, fake, nul, nul, fake, ctypes.c_size_t(8), s)

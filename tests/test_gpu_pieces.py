@@ -252,6 +252,7 @@ def test_router_and_gate_backward(cid):
     L = _lib()
     shape = W.SMALL[cid]
     cfg = L.config_from_shape(shape)
+    ws = L.alloc_workspace(cfg, dev())
     inp = W.make_inputs(shape, seed=cid, with_experts=False)
     o = oracle_inputs(dict(inp, W13=None, W2=None), shape)
     T, k, E, d = shape.T, shape.k, shape.E, shape.d
@@ -266,12 +267,12 @@ def test_router_and_gate_backward(cid):
     lg = torch.empty(T, E, dtype=torch.float32, device=dev())
     x = to_dev(inp["x"])
     Wg = to_dev(inp["Wg"])
-    L.gate_logits(cfg, x, Wg, to_dev(inp["bg"]), lg)
+    L.gate_logits(cfg, x, Wg, to_dev(inp["bg"]), lg, ws)
     dl_np = W.random_rows(T, E, seed=800 + cid, act="f32")
     dWg = torch.empty(E, d, dtype=torch.float32, device=dev())
     dbg = torch.empty(E, dtype=torch.float32, device=dev())
     dxr = torch.empty(T, d, dtype=torch.float32, device=dev())
-    L.gate_logits_bwd(cfg, x, Wg, to_dev(dl_np), dWg, dbg, dxr)
+    L.gate_logits_bwd(cfg, x, Wg, to_dev(dl_np), dWg, dbg, dxr, ws)
     torch.cuda.synchronize()
     ref = O.router_backward(logits.astype(np.float64), r["idx"], r["w"].astype(np.float32).astype(np.float64),
                             dw_np.astype(np.float64), spec, counts=r["counts"], daux=1.0)
