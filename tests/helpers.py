@@ -119,6 +119,28 @@ def storage_ok(got, ref, act) -> float:
     return float(np.max(np.abs(got - ref) / bound))
 
 
+# A token's selected set may differ between the fp32 GPU logits and the fp64 oracle only
+# when its k-th and (k+1)-th keys are this close; two selected experts may swap slots only
+# when their keys are this close.
+NEAR_TIE = 1e-5
+
+
+def routing_moved(idx_gpu, r) -> np.ndarray:
+    """Tokens whose selected expert SET differs from the oracle's.  Asserts that every such
+    token sits at a near-tie of the k-th key, and that where the sets agree the GPU's slot
+    order is the oracle's descending key order up to near-ties."""
+    idx_gpu = np.asarray(idx_gpu, dtype=np.int64)
+    moved = np.any(np.sort(idx_gpu, axis=1) != np.sort(r["idx"], axis=1), axis=1)
+    bad = np.where(moved & (r["margin"] >= NEAR_TIE))[0]
+    assert bad.size == 0, (f"{bad.size} token(s) routed to a different set with a clear margin; token {bad[0]}: "
+                           f"gpu {sorted(idx_gpu[bad[0]].tolist())} oracle {sorted(r['idx'][bad[0]].tolist())} "
+                           f"margin {r['margin'][bad[0]]:.3e}") if bad.size else ""
+    same = ~moved
+    kg = np.take_along_axis(r["keys"][same], idx_gpu[same], axis=1)
+    assert np.all(np.diff(kg, axis=1) <= NEAR_TIE), "selected experts out of key order beyond a near-tie"
+    return moved
+
+
 def spec_of(shape) -> "O.LayerSpec":
     return O.LayerSpec(E=shape.E, k=shape.k, score=shape.score, scaling=shape.scaling, aux_coeff=shape.aux_coeff)
 
