@@ -299,6 +299,12 @@ moe_status_t moe_gate_logits_bwd(const moe_config_t* cfg, const void* x, const f
                                  size_t ws_bytes, void* stream);
 
 /* Whole backward from the saved forward tensors.
+ * bf16/fp32 experts: the expert weight gradients (dW2 = dY^T Act, dW13 = dH^T X, routed
+ * and shared) run on a second stream of the library -- one per device, default priority,
+ * created on the first call -- that waits on `stream` for dY_perm and dH and is joined
+ * back into `stream` before the call returns, so work queued on `stream` afterwards sees
+ * every output.  That stream and its events are per device, not per call: calls on one
+ * device must not be issued concurrently from several host threads.
  * fp8 experts are frozen (no expert gradients): grads->dW13, dW2, dW13s, dW2s must be
  * NULL, and the call computes the router path only -- dw, dlogits, dWg, dbg, and
  * dx = dlogits Wg, the input gradient through the router. */

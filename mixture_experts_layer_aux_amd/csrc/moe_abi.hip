@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -85,7 +86,9 @@ FwdWs carve_fwd(const moe_config_t& c, void* base) {
 }
 
 struct BwdWs {
-  void* dYX;       // [A, d]: dY_perm (act dtype), then dX_perm (fp32) once dY_perm is consumed
+  void* dY;        // [A, d] act: dY_perm
+  float* dX;       // [A, d] fp32: dX_perm (its own buffer, so the fc2 weight gradient can still
+                   // read dY_perm while the fc1 data gradient writes dX_perm)
   void* dH;        // [A, 2F] act
   float* dw;       // [T, k]
   float* dlogits;  // [T, E]
@@ -109,7 +112,8 @@ BwdWs carve_bwd(const moe_config_t& c, void* base) {
   };
   const size_t A = static_cast<size_t>(c.T) * c.k, T = static_cast<size_t>(c.T), eb = act_bytes(c);
   BwdWs w;
-  w.dYX = take(A * c.d * 4);
+  w.dY = take(A * c.d * eb);
+  w.dX = reinterpret_cast<float*>(take(A * c.d * 4));
   w.dH = take(A * 2 * c.F * eb);
   w.dw = reinterpret_cast<float*>(take(A * 4));
   w.dlogits = reinterpret_cast<float*>(take(T * c.E * 4));
@@ -177,6 +181,46 @@ moe_status_t need_ws(size_t have, size_t need, const char* fn) {
 }
 
 hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
+
+// A second stream per device for the expert weight gradients of moe_layer_bwd: they need
+// only dY_perm and dH, so they run beside the data gradients (HBM-heavy fp32 weight
+// gradients next to MFMA-heavy data gradients).  Default priority; created on first use.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t dy = nullptr, dh = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+moe_status_t side_stream(SideStream** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_HIP, "side stream: no current device");
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    hipStream_t st = nullptr;
+    hipEvent_t e[3] = {nullptr, nullptr, nullptr};
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess)
+      return fail(MOE_ERR_HIP, "side stream: hipStreamCreateWithFlags failed");
+    for (hipEvent_t& ev : e)
+      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
+        return fail(MOE_ERR_HIP, "side stream: hipEventCreateWithFlags failed");
+    ss.dy = e[0]; ss.dh = e[1]; ss.join = e[2];
+    ss.s = st;
+  }
+  *out = &ss;
+  return MOE_OK;
+}
+
+// Makes `waiter` wait for the work queued on `from` so far (no-op on one stream).
+moe_status_t fork(hipStream_t from, hipEvent_t ev, hipStream_t waiter) {
+  if (from == waiter) return MOE_OK;
+  if (hipEventRecord(ev, from) != hipSuccess || hipStreamWaitEvent(waiter, ev, 0) != hipSuccess)
+    return fail(MOE_ERR_HIP, "stream fork/join failed");
+  return MOE_OK;
+}
 
 // ----------------------------------------------------------------- launch sequences
 moe_status_t run_gate(const moe_config_t& c, const void* x, const float* Wg, const float* bg, float* logits,
@@ -259,7 +303,11 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
                              const void* W2, const void* H, const void* Act, const void* dY_perm, void* dH,
                              void* dX_perm, void* dW13, void* dW2, const void* x, const void* W13s, const void* W2s,
                              const void* H_s, const void* Act_s, const void* dY_s, void* dH_s, void* dx_s,
-                             void* dW13s, void* dW2s, int32_t* sched, float* dact, hipStream_t s) {
+                             void* dW13s, void* dW2s, int32_t* sched, float* dact, hipStream_t s,
+                             hipStream_t s2 = nullptr, hipEvent_t ev_dh = nullptr) {
+  // s2 (when given, with dY_perm and dX_perm distinct) runs the weight gradients; its
+  // caller has made it wait for dY_perm and joins it back.
+  if (!s2) s2 = s;
   const int64_t A = static_cast<int64_t>(c.T) * c.k;
   for (int shared = 0; shared < (c.Fs ? 2 : 1); ++shared) {
     const int F = shared ? c.Fs : c.F;
@@ -306,11 +354,12 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
       MOE_TRY(launch_gemm_fma(d2, s));
       MOE_TRY(launch_swiglu_bwd_elementwise(static_cast<const float*>(h), dact, static_cast<float*>(dh), rows, F, s));
     }
-    // (2) fc2 weight gradient dW2 = dY^T Act, before dX may overwrite an aliased dY
-    if (dw2) MOE_TRY(run_wgrad(et, off, G, rows, dY, c.d, act, F, dw2, s));
+    // (2) fc2 weight gradient dW2 = dY^T Act, queued before dX may overwrite an aliased dY
+    if (dw2) MOE_TRY(run_wgrad(et, off, G, rows, dY, c.d, act, F, dw2, s2));
+    MOE_TRY(fork(s, ev_dh, s2));  // dH ready for the fc1 weight gradient
     MOE_TRY(et == MOE_BF16 ? launch_gemm_mfma(d1, sched, s) : launch_gemm_fma(d1, s));
     // (4) fc1 weight gradient dW13 = dH^T X
-    if (dw13) MOE_TRY(run_wgrad(et, off, G, rows, dh, 2 * F, X, c.d, dw13, s));
+    if (dw13) MOE_TRY(run_wgrad(et, off, G, rows, dh, 2 * F, X, c.d, dw13, s2));
   }
   return MOE_OK;
 }
@@ -624,15 +673,19 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   hipStream_t s = S(stream);
   // the shared expert's upstream gradient is dy itself, in the activation dtype
   void* dY_s = c.Fs ? (c.act_dtype == MOE_F32 ? const_cast<float*>(dy) : bw.dY_s) : nullptr;
-  MOE_TRY(launch_combine_bwd(c, dy, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, bw.dYX, bw.dw,
+  MOE_TRY(launch_combine_bwd(c, dy, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, bw.dY, bw.dw,
                              c.act_dtype == MOE_F32 ? nullptr : dY_s, s));
-  MOE_TRY(run_experts_bwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, sv->H, sv->Act, bw.dYX, bw.dH, bw.dYX,
-                          gr->dW13, gr->dW2, x, W->W13s, W->W2s, sv->H_s, sv->Act_s, dY_s, bw.dH_s, bw.dx_s, gr->dW13s,
-                          gr->dW2s, bw.sched, bw.dact, s));
+  SideStream* ss = nullptr;
+  MOE_TRY(side_stream(&ss));
+  MOE_TRY(fork(s, ss->dy, ss->s));  // dY_perm (and the shared expert's dY) ready
+  MOE_TRY(run_experts_bwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, sv->H, sv->Act, bw.dY, bw.dH, bw.dX, gr->dW13,
+                          gr->dW2, x, W->W13s, W->W2s, sv->H_s, sv->Act_s, dY_s, bw.dH_s, bw.dx_s, gr->dW13s,
+                          gr->dW2s, bw.sched, bw.dact, s, ss->s, ss->dh));
   MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, daux, bw.dlogits, s));
   MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, bw.gate, s));
-  return launch_unpermute_reduce(c, static_cast<const float*>(bw.dYX), sv->row_of,
-                                 c.Fs ? static_cast<const float*>(bw.dx_s) : nullptr, bw.dx_r, dx, s);
+  MOE_TRY(launch_unpermute_reduce(c, bw.dX, sv->row_of, c.Fs ? static_cast<const float*>(bw.dx_s) : nullptr,
+                                  bw.dx_r, dx, s));
+  return fork(ss->s, ss->join, s);  // the caller's stream sees the weight gradients too
 }
 
 }  // extern "C"

@@ -106,8 +106,8 @@ def test_workspace_sizes_cover_the_backward_buffers():
         eb = 2 if c.act == "bf16" else 4
         A = c.T * c.k
         assert f > 0
-        # dY_perm/dX_perm, dH, dlogits, dx_r at least
-        assert b >= A * c.d * eb + A * 2 * c.F * eb + c.T * c.E * 4 + c.T * c.d * 4
+        # dY_perm, dX_perm (fp32, its own buffer), dH, dlogits, dx_r at least
+        assert b >= A * c.d * eb + A * c.d * 4 + A * 2 * c.F * eb + c.T * c.E * 4 + c.T * c.d * 4
 
 
 P = ctypes.c_void_p
