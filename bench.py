@@ -238,6 +238,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--entry-points", action="store_true",
+                    help="also time the layer through moe_layer_fwd + moe_layer_bwd (reported beside value)")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0 = by layer)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 3 device copies of 1 GiB each (the known-size kernel that scales the "
@@ -366,6 +368,24 @@ def main() -> int:
     ms_step = elapsed * 1e3 / args.steps
     st = stats.cpu().numpy()
 
+    # --entry-points: the same layer through the two product entry points, moe_layer_fwd and
+    # moe_layer_bwd (the backward overlaps the expert weight gradients on a second stream).
+    # Off by default, so a profile of the default command holds the timed kernels only.
+    layer_ms = None
+    if args.entry_points:
+        def layer_step():
+            L.layer_fwd(cfg, Wt, x, S, y, stats, ws)
+            L.layer_bwd(cfg, Wt, S, x, dy, 1.0, dx, G, ws)
+
+        for _ in range(args.warmup):
+            layer_step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            layer_step()
+        torch.cuda.synchronize()
+        layer_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+
     alg = algorithmic(shape)
     gemm_ms = sum(phase_ms[p] for p in GEMM_PHASES)
     gemm_tflops = alg["grouped_gemm_flop"] / (gemm_ms * 1e-3) / 1e12
@@ -398,6 +418,9 @@ def main() -> int:
                           flop_per_step=alg["grouped_gemm_flop"], ms_per_step=round(gemm_ms, 3),
                           tflops=round(gemm_tflops, 2), peak=peak, frac=round(gemm_tflops / peak, 4)),
         layer_tflops=round(layer_flop / (ms_step * 1e-3) / 1e12, 2),
+        layer_entry_points=None if layer_ms is None else dict(
+            calls="moe_layer_fwd + moe_layer_bwd", ms_per_step=round(layer_ms, 3),
+            tokens_per_s=round(T / (layer_ms * 1e-3), 1)),
         phases_ms={p: round(v, 4) for p, v in phase_ms.items()},
         hbm_phases=dict(router=hbm("router", "router_bytes"), permute=hbm("permute", "permute_bytes"),
                         combine=hbm("combine", "combine_bytes"), combine_bwd=hbm("combine_bwd", "combine_bwd_bytes"),
