@@ -102,6 +102,16 @@ def roofline(alg, ms, peak_tflops, shape):
                 traffic=measured_traffic(shape), **common)
 
 
+def gate_engine(shape):
+    """Where the router GEMMs run: on the bf16 matrix cores through exact three-way bf16
+    splits of the fp32 operand (bf16 activations, E % 16 == 0: 4x the algorithmic FLOP are
+    executed over forward and backward), else fp32 FMA tiles."""
+    if shape.act == "bf16" and shape.E % 16 == 0:
+        return dict(engine="bf16 MFMA, exact 3-way split of the fp32 operand", flop_executed_per_flop=4.0,
+                    peak=PEAK_BF16_TFLOPS)
+    return dict(engine="fp32 FMA", flop_executed_per_flop=1.0, peak=PEAK_FP32_TFLOPS)
+
+
 def cpu_baseline(shape, inp, tokens: int):
     """The fp64 oracle's layer forward + backward on the first `tokens` tokens of the same
     inputs, timed on the host cores.  The fp64 copies of the weights of the experts those
@@ -427,7 +437,7 @@ def main() -> int:
                         unpermute_reduce=hbm("unpermute_reduce", "unpermute_reduce_bytes")),
         gate_gemm=dict(ms=round(phase_ms["gate"] + phase_ms["gate_bwd"], 4), flop=alg["gate_flop"],
                        tflops=round(alg["gate_flop"] / ((phase_ms["gate"] + phase_ms["gate_bwd"]) * 1e-3) / 1e12, 2),
-                       peak_fp32=PEAK_FP32_TFLOPS),
+                       **gate_engine(shape)),
         load=dict(maxvio=round(float(st[1]), 4), empty_experts=int(st[2]), max_count=int(st[3]),
                   mean_count=T * k / E),
     )
