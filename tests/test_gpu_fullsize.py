@@ -106,3 +106,106 @@ def test_full_size_layer_on_sampled_outputs(cid):
     for e0 in np.where(counts == 0)[0][:4]:
         if not np.any(idx_gpu[moved] == e0):
             assert not torch.any(got["dW13"][e0]) and not torch.any(got["dW2"][e0]), f"expert {e0} has no rows"
+
+
+class _LazyQuantised:
+    """Per-expert e4m3 codes and scales of a stacked fp32 master, made by the oracle's
+    quantiser on first access (a full-size stack is too large to quantise whole on the host)."""
+
+    def __init__(self, master):
+        self.master, self.cache = master, {}
+        E, R, C = master.shape
+        self.q, self.s = _View(self, 0, (E, R, C)), _View(self, 1, (E, R // 128, C // 128))
+
+    def get(self, e):
+        if e not in self.cache:
+            self.cache[e] = O.quantize_blocks(self.master[e], 128)
+        return self.cache[e]
+
+
+class _View:
+    def __init__(self, owner, which, shape):
+        self.owner, self.which, self.shape = owner, which, shape
+
+    def __getitem__(self, e):
+        return self.owner.get(int(e))[self.which]
+
+
+def test_full_size_fp8_layer_on_sampled_tokens():
+    """The e4m3 skewed layer at full size: GPU weight quantisation and the permuted e4m3 rows
+    bit-exact for the sampled tokens' experts, y and the router-path dx within the flip
+    bound of the reduced fp8 test, routing of every token against the oracle's."""
+    from test_gpu_fp8 import _check_within, _flip_bound
+    torch = torch_mod()
+    from mixture_experts_layer_aux_amd import _lib as L
+    shape = W.CONFIGS[5]
+    T, d, E, k, F = shape.T, shape.d, shape.E, shape.k, shape.F
+    spec = spec_of(shape)
+    cfg = L.config_from_shape(shape)
+    inp = W.make_inputs(shape, seed=5)
+    print(f"full-size fp8 layer {shape.name}: T={T} d={d} E={E} k={k} F={F}", flush=True)
+    dv = dev()
+    q13 = torch.empty(E, 2 * F, d, dtype=torch.uint8, device=dv)
+    s13 = torch.empty(E * 2 * F // 128, d // 128, dtype=torch.float32, device=dv)
+    q2 = torch.empty(E, d, F, dtype=torch.uint8, device=dv)
+    s2 = torch.empty(E * d // 128, F // 128, dtype=torch.float32, device=dv)
+    m = to_dev(inp["W13"])
+    L.quantize_fp8(m.view(E * 2 * F, d), 128, q13.view(E * 2 * F, d), s13)
+    del m
+    m = to_dev(inp["W2"])
+    L.quantize_fp8(m.view(E * d, F), 128, q2.view(E * d, F), s2)
+    del m
+    Wt = dict(Wg=to_dev(inp["Wg"]), bg=to_dev(inp["bg"]), W13=q13, W13_scale=s13.view(-1), W2=q2,
+              W2_scale=s2.view(-1))
+    x = to_dev(inp["x"])
+    dy = to_dev(W.to_f32(inp["dy"], shape.act).copy())
+    S = L.alloc_saved(cfg, dv)
+    G = L.alloc_grads(cfg, dv, with_dbg=True)
+    ws = L.alloc_workspace(cfg, dv)
+    y = torch.empty(T, d, dtype=torch.float32, device=dv)
+    dx = torch.empty(T, d, dtype=torch.float32, device=dv)
+    stats = torch.empty(L.MOE_NSTATS, dtype=torch.float32, device=dv)
+    L.layer_fwd(cfg, Wt, x, S, y, stats, ws)
+    L.layer_bwd(cfg, Wt, S, x, dy, 1.0, dx, G, ws)
+    torch.cuda.synchronize()
+    x64 = f64(inp["x"], shape.act)
+    logits = O.gate_logits(x64, inp["Wg"], inp["bg"])
+    assert rel_err(to_np(S["logits"]), logits) < 1e-5, "logits"
+    r = O.route(logits, spec, inp["expert_bias"])
+    moved = routing_moved(to_np(S["idx"]), r)
+    if not moved.any():
+        assert np.array_equal(to_np(S["counts"]), r["counts"])
+    rng = np.random.default_rng(1005)
+    toks = np.sort(rng.choice(np.where(r["margin"] > MARGIN)[0], size=4, replace=False))
+    lw13, lw2 = _LazyQuantised(inp["W13"]), _LazyQuantised(inp["W2"])
+    row_of = to_np(S["row_of"])
+    idx_gpu = to_np(S["idx"])
+    dy64 = f64(inp["dy"], shape.act)
+    for t in toks:
+        f = O.layer_forward_fp8(x64[t:t + 1], inp["Wg"], lw13.q, lw13.s, lw2.q, lw2.s, spec, bg=inp["bg"])
+        assert np.array_equal(np.sort(f["route"]["idx"][0]), np.sort(r["idx"][t]))
+        # the GPU's e4m3 weights of this token's experts and its permuted e4m3 rows
+        for e in r["idx"][t]:
+            oq, os_ = lw13.get(int(e))
+            assert np.array_equal(q13[e].cpu().numpy(), oq), f"W13 codes of expert {e}"
+            assert np.array_equal(s13.view(E, 2 * F // 128, d // 128)[e].cpu().numpy(), os_), f"W13 scales of {e}"
+            oq, os_ = lw2.get(int(e))
+            assert np.array_equal(q2[e].cpu().numpy(), oq), f"W2 codes of expert {e}"
+            assert np.array_equal(s2.view(E, d // 128, F // 128)[e].cpu().numpy(), os_), f"W2 scales of {e}"
+        for j in range(k):
+            rw = int(row_of[t, j])
+            assert np.array_equal(S["x_perm"][rw].cpu().numpy(), f["x_q"][0]), "permuted e4m3 row"
+            assert np.array_equal(S["x_perm_scale"][rw].cpu().numpy(), f["x_scale"][0]), "permuted row scales"
+        # y_t within the legitimate Act-rounding flips (the GPU's slot order may differ)
+        rf = f["route"]
+        bY = _flip_bound(f, lw2.q, lw2.s, spec)
+        ybound = np.einsum("tk,tkd->td", np.abs(rf["w"]), bY[f["perm"].row_of])
+        _check_within(to_np(y[t:t + 1]), f["y"], ybound, 2e-3, f"y[{t}]")
+        # router-path dx_t (aux off): the bound through dw, the selected softmax and Wg
+        b = O.router_path_backward(f, x64[t:t + 1], inp["Wg"], dy64[t:t + 1], spec)
+        bdw = np.einsum("td,tkd->tk", np.abs(dy64[t:t + 1]), bY[f["perm"].row_of])
+        w = np.abs(rf["w"])
+        bdl = w * bdw + w * np.sum(w * bdw, axis=1, keepdims=True)
+        bdx = np.einsum("tk,tkd->td", bdl, np.abs(inp["Wg"].astype(np.float64))[rf["idx"]])
+        _check_within(to_np(dx[t:t + 1]), b["dx_router"], bdx, 2e-2, f"dx[{t}] (router path)")
+        assert np.array_equal(np.sort(idx_gpu[t]), np.sort(rf["idx"][0]))
