@@ -172,7 +172,23 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
+    // slots four at a time: the four rows are loaded before any is added, so each lane
+    // has four loads in flight; the sum still runs in slot order
+    int j = 0;
+    for (; j + 4 <= k; j += 4) {
+      float f[4][8], wj[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = __shfl(my_r, j + q, 64);
+        wj[q] = __shfl(my_w, j + q, 64);
+        G8<TY>::load(Y, static_cast<int64_t>(r) * groups + u, f[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += wj[q] * f[q][i];
+    }
+    for (; j < k; ++j) {
       const int r = __shfl(my_r, j, 64);
       const float wj = __shfl(my_w, j, 64);
       float f[8];
@@ -198,9 +214,11 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
 }
 
 // dY_perm[row_of[t,j]] = w[t,j] * dy[t]  (activation dtype);
-// dw[t,j] = <dy[t], Y_perm[row_of[t,j]]>  (fp32, fixed butterfly order);
-// dY_s[t] = dy[t] in the activation dtype, the shared expert's upstream gradient (optional).
-template <typename TACT>
+// dw[t,j] = <dy[t], Y_perm[row_of[t,j]]>  (fp32: per lane over its columns in order, then
+// a fixed butterfly across the wave);  dY_s[t] = dy[t] in the activation dtype (optional).
+// One wave per token, one pass over the columns: dy is loaded once per column group and the
+// k rows four at a time; KMAX >= k partial sums live in registers.
+template <typename TACT, int KMAX>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restrict__ dy,
                                                           const float* __restrict__ Y, int Tn, int groups,
                                                           int k, const int32_t* __restrict__ row_of,
@@ -212,30 +230,46 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restric
   const int my_r = lane < k ? row_of[static_cast<int64_t>(t) * k + lane] : 0;
   const float my_w = lane < k ? w[static_cast<int64_t>(t) * k + lane] : 0.0f;
   const int64_t t0 = static_cast<int64_t>(t) * groups;
-  if (dY_s)
-    for (int u = lane; u < groups; u += 64) {
-      float g[8];
-      G8<float>::load(dy, t0 + u, g);
-      G8<TACT>::store(dY_s, t0 + u, g);
-    }
-  float my_dw = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const int r = __shfl(my_r, j, 64);
-    const float wj = __shfl(my_w, j, 64);
-    float part = 0.0f;
-    for (int u = lane; u < groups; u += 64) {
-      float g[8], y[8];
-      G8<float>::load(dy, t0 + u, g);
-      G8<float>::load(Y, static_cast<int64_t>(r) * groups + u, y);
+  float part[KMAX];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        part += g[i] * y[i];
-        g[i] *= wj;
+  for (int j = 0; j < KMAX; ++j) part[j] = 0.0f;
+  for (int u = lane; u < groups; u += 64) {
+    float g[8];
+    G8<float>::load(dy, t0 + u, g);
+    if (dY_s) G8<TACT>::store(dY_s, t0 + u, g);
+#pragma unroll
+    for (int j0 = 0; j0 < KMAX; j0 += 4) {
+      if (j0 < k) {
+        float y[4][8];
+        int r[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          r[q] = __shfl(my_r, j0 + q, 64);
+          if (j0 + q < k) G8<float>::load(Y, static_cast<int64_t>(r[q]) * groups + u, y[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (j0 + q < k) {
+            const float wj = __shfl(my_w, j0 + q, 64);
+            float gw[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              part[j0 + q] += g[i] * y[q][i];
+              gw[i] = g[i] * wj;
+            }
+            if (dY) G8<TACT>::store(dY, static_cast<int64_t>(r[q]) * groups + u, gw);
+          }
+        }
       }
-      if (dY) G8<TACT>::store(dY, static_cast<int64_t>(r) * groups + u, g);
     }
-    part = wave_sum(part);
-    if (lane == j) my_dw = part;
+  }
+  float my_dw = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      const float v = wave_sum(part[j]);
+      if (lane == j) my_dw = v;
+    }
   }
   if (lane < k) dw[static_cast<int64_t>(t) * k + lane] = my_dw;
 }
@@ -282,11 +316,18 @@ moe_status_t launch_combine_bwd(const moe_config_t& c, const float* dy, const fl
                                 const float* w, void* dY, float* dw, void* dY_s, hipStream_t s) {
   const int groups = c.d / 8;
   const int grid = static_cast<int>(ceil_div(c.T, 4));
-  if (c.act_dtype == MOE_BF16)
-    combine_bwd_kernel<uint16_t><<<grid, 256, 0, s>>>(dy, Y, c.T, groups, c.k, row_of, w, dY, dw, dY_s);
-  else
-    combine_bwd_kernel<float><<<grid, 256, 0, s>>>(dy, Y, c.T, groups, c.k, row_of, w, dY, dw, dY_s);
-  return check_launch("combine_bwd");
+  const bool bf = c.act_dtype == MOE_BF16;
+#define MOE_CB(KM)                                                                                        \
+  if (c.k <= KM) {                                                                                        \
+    if (bf) combine_bwd_kernel<uint16_t, KM><<<grid, 256, 0, s>>>(dy, Y, c.T, groups, c.k, row_of, w, dY, dw, dY_s); \
+    else combine_bwd_kernel<float, KM><<<grid, 256, 0, s>>>(dy, Y, c.T, groups, c.k, row_of, w, dY, dw, dY_s);      \
+    return check_launch("combine_bwd");                                                                   \
+  }
+  MOE_CB(8)
+  MOE_CB(16)
+  MOE_CB(32)
+#undef MOE_CB
+  return fail(MOE_ERR_UNSUPPORTED, "combine_bwd: k above 32");
 }
 
 }  // namespace moe
