@@ -42,7 +42,8 @@ GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_aux_amd", "csrc", "moe_g
 
 
 def algorithmic(shape):
-    """Algorithmic work per step (the counts the design doc documents)."""
+    """Algorithmic work per step: the bytes each HBM-bound kernel must move and the FLOP
+    each GEMM must compute, at minimum."""
     T, d, E, k, F, Fs = shape.T, shape.d, shape.E, shape.k, shape.F, shape.Fs
     A = T * k
     eb = 2 if shape.act == "bf16" else 4
@@ -278,7 +279,7 @@ def main() -> int:
         from mixture_experts_layer_aux_amd import build as B
         B.build()
     L.load()
-    shape = W.CONFIGS[args.config]
+    shape = W.LAYERS[args.config]
     cfg = L.config_from_shape(shape)
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()

@@ -74,7 +74,7 @@ class LayerShape:
 #    top-8, expert ffn 1024, aux loss) for the small bf16 layer;
 #  - the shapes the summary page lists (DeepSeek-V3 1 shared + 256 routed top-8,
 #    Qwen3-Next 512 experts, Kimi K3 16-of-896) for the three large layers.
-CONFIGS: Dict[int, LayerShape] = {
+LAYERS: Dict[int, LayerShape] = {
     1: LayerShape("tiny-fp32", T=128, d=64, E=8, k=2, F=128, Fs=0, score="softmax",
                   act="f32", aux_coeff=1.0, init="fan_in"),
     2: LayerShape("small-bf16", T=8192, d=2048, E=64, k=8, F=1024, Fs=0, score="softmax",
@@ -91,16 +91,16 @@ CONFIGS: Dict[int, LayerShape] = {
 # fp64 oracle finishes in seconds while still spanning several GEMM tiles (256 x 256
 # output tiles, 64-deep K steps) and a ragged tail in every expert.
 SMALL: Dict[int, LayerShape] = {
-    1: CONFIGS[1],
-    2: replace(CONFIGS[2], name="small-bf16-reduced", T=1024, d=512, E=16, k=4, F=384),
-    3: replace(CONFIGS[3], name="deepseek-v3-shaped-reduced", T=1024, d=768, E=32, k=8,
+    1: LAYERS[1],
+    2: replace(LAYERS[2], name="small-bf16-reduced", T=1024, d=512, E=16, k=4, F=384),
+    3: replace(LAYERS[3], name="deepseek-v3-shaped-reduced", T=1024, d=768, E=32, k=8,
                F=256, Fs=384),
-    4: replace(CONFIGS[4], name="qwen3-next-shaped-reduced", T=2048, d=512, E=64, k=10,
+    4: replace(LAYERS[4], name="qwen3-next-shaped-reduced", T=2048, d=512, E=64, k=10,
                F=128, Fs=256),
-    5: replace(CONFIGS[5], name="skewed-reduced-bf16", T=1024, d=512, E=112, k=16, F=128, wq=""),
+    5: replace(LAYERS[5], name="skewed-reduced-bf16", T=1024, d=512, E=112, k=16, F=128, wq=""),
 }
 # The skewed layer with its e4m3 experts, at the reduced size.
-SMALL_FP8 = replace(CONFIGS[5], name="skewed-reduced-fp8", T=1024, d=512, E=112, k=16, F=128)
+SMALL_FP8 = replace(LAYERS[5], name="skewed-reduced-fp8", T=1024, d=512, E=112, k=16, F=128)
 
 
 def _stream(seed: int, tid: int, chunk: int = 0) -> np.random.Generator:

@@ -34,7 +34,7 @@ def _status(cfg):
 
 
 def test_valid_configs():
-    for c in W.CONFIGS.values():
+    for c in W.LAYERS.values():
         assert _status(L.config_from_shape(c)) == L.MOE_OK
     for c in W.SMALL.values():
         assert _status(L.config_from_shape(c)) == L.MOE_OK
@@ -59,7 +59,7 @@ def test_valid_configs():
     (dict(w_dtype=L.MOE_FP8_E4M3, Fs=1024), L.MOE_ERR_UNSUPPORTED),                      # no fp8 shared expert
 ])
 def test_config_rules(change, status):
-    cfg = L.config_from_shape(W.CONFIGS[2])
+    cfg = L.config_from_shape(W.LAYERS[2])
     for k, v in change.items():
         setattr(cfg, k, v)
     assert _status(cfg) == status
@@ -67,9 +67,9 @@ def test_config_rules(change, status):
 
 
 def test_fp8_layers_validate():
-    assert _status(L.config_from_shape(W.CONFIGS[5])) == L.MOE_OK
+    assert _status(L.config_from_shape(W.LAYERS[5])) == L.MOE_OK
     assert _status(L.config_from_shape(W.SMALL_FP8)) == L.MOE_OK
-    assert L.is_fp8(L.config_from_shape(W.CONFIGS[5]))
+    assert L.is_fp8(L.config_from_shape(W.LAYERS[5]))
 
 
 def test_quantize_fp8_rejects_bad_shapes_before_launching():
@@ -81,10 +81,10 @@ def test_quantize_fp8_rejects_bad_shapes_before_launching():
     assert lib.moe_quantize_fp8(i32(L.MOE_BF16), fake, i64(128), i32(128), i32(64), fake, fake, P(None)) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_quantize_fp8(i32(9), fake, i64(128), i32(128), i32(1), fake, fake, P(None)) == L.MOE_ERR_INVALID_ARG
     # the fp8 layer calls need the fp8 config, and the fp8 backward refuses expert gradients
-    cfg = L.config_from_shape(W.CONFIGS[2])
+    cfg = L.config_from_shape(W.LAYERS[2])
     st = lib.moe_permute_fp8(ctypes.byref(cfg), *([fake] * 8), fake, ctypes.c_size_t(1 << 40), P(None))
     assert st == L.MOE_ERR_INVALID_ARG and b"fp8" in lib.moe_last_error()
-    c8 = L.config_from_shape(W.CONFIGS[5])
+    c8 = L.config_from_shape(W.LAYERS[5])
     w = L.Weights(Wg=1 << 20, W13=1 << 20, W2=1 << 20)
     sv = L.Saved(**{n: 1 << 20 for n, _ in L.Saved._fields_})
     g = L.Grads(dWg=1 << 20, dW13=1 << 20)
@@ -94,14 +94,14 @@ def test_quantize_fp8_rejects_bad_shapes_before_launching():
 
 
 def test_sigmoid_top1_is_allowed_and_fp32_f192_is_allowed():
-    cfg = L.config_from_shape(replace(W.CONFIGS[3], k=1))
+    cfg = L.config_from_shape(replace(W.LAYERS[3], k=1))
     assert _status(cfg) == L.MOE_OK
-    cfg = L.config_from_shape(replace(W.CONFIGS[1], F=192))
+    cfg = L.config_from_shape(replace(W.LAYERS[1], F=192))
     assert _status(cfg) == L.MOE_OK
 
 
 def test_workspace_sizes_cover_the_backward_buffers():
-    for c in W.CONFIGS.values():
+    for c in W.LAYERS.values():
         f, b = L.workspace_size(L.config_from_shape(c))
         eb = 2 if c.act == "bf16" else 4
         A = c.T * c.k
@@ -115,7 +115,7 @@ P = ctypes.c_void_p
 
 def test_entry_points_reject_bad_arguments_before_launching():
     lib = L.load()
-    cfg = L.config_from_shape(W.CONFIGS[2])
+    cfg = L.config_from_shape(W.LAYERS[2])
     fake = P(1 << 20)           # never dereferenced: every call below fails its checks first
     odd = P((1 << 20) + 2)
     nul = P(None)
@@ -135,7 +135,7 @@ def test_entry_points_reject_bad_arguments_before_launching():
     st = lib.moe_permute(ctypes.byref(cfg), odd, fake, fake, fake, fake, fake, fake, ctypes.c_size_t(1 << 40), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"aligned" in lib.moe_last_error()
     # invalid configuration reaches no launch either
-    bad = L.config_from_shape(replace(W.CONFIGS[2], k=1))
+    bad = L.config_from_shape(replace(W.LAYERS[2], k=1))
     st = lib.moe_unpermute_combine(ctypes.byref(bad), fake, fake, fake, nul, fake, s)
     assert st == L.MOE_ERR_UNSUPPORTED
     # the layer calls check their structs

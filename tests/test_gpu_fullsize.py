@@ -53,7 +53,7 @@ def _run_full(shape, inp):
 @pytest.mark.parametrize("cid", [2, 3, 4])
 def test_full_size_layer_on_sampled_outputs(cid):
     torch = torch_mod()
-    shape = W.CONFIGS[cid]
+    shape = W.LAYERS[cid]
     spec = spec_of(shape)
     inp = W.make_inputs(shape, seed=cid)
     print(f"full-size layer {shape.name}: T={shape.T} d={shape.d} E={shape.E} k={shape.k} F={shape.F}", flush=True)
@@ -138,7 +138,7 @@ def test_full_size_fp8_layer_on_sampled_tokens():
     from test_gpu_fp8 import _check_within, _flip_bound
     torch = torch_mod()
     from mixture_experts_layer_aux_amd import _lib as L
-    shape = W.CONFIGS[5]
+    shape = W.LAYERS[5]
     T, d, E, k, F = shape.T, shape.d, shape.E, shape.k, shape.F
     spec = spec_of(shape)
     cfg = L.config_from_shape(shape)

@@ -63,7 +63,7 @@ def test_router_small_configs(cid):
 
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
 def test_router_full_size(cid):
-    shape = W.CONFIGS[cid]
+    shape = W.LAYERS[cid]
     inp = W.make_inputs(shape, seed=cid, with_dy=False, with_experts=False)
     logits = O.gate_logits(f64(inp["x"], shape.act), inp["Wg"], inp["bg"]).astype(np.float32)
     _router_case(shape, logits, inp["expert_bias"])
