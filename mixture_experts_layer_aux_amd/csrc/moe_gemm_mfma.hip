@@ -422,6 +422,41 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
           *reinterpret_cast<uint2*>(p.C2 + static_cast<int64_t>(row) * p.ldc2 + col) = av;
         }
     }
+  } else if (EPI == EPI_STORE && OUT_F32) {
+    // fp32 tile through LDS, so that every global store instruction writes one whole
+    // 1 KB row of the tile (eight full cache lines) instead of 16-byte pieces of 32 rows.
+    // Two passes of 128 tile rows (64 per wave row) fill the 128 KB of LDS exactly: pass h
+    // takes accumulator rows i = 2h, 2h+1 of every wave.  LDS row lr (pass-local, 0-127)
+    // holds 64 float4 chunks with chunk c at lr * 64 + (c ^ (lr & 63)).
+    float4* L4 = reinterpret_cast<float4*>(lds);
+    static_assert(STAGES * STAGE_ELEMS * 2 >= 128 * BN * 4, "epilogue staging needs 128 KB of LDS");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      block_barrier();  // the previous use of LDS (main loop or pass 0 stores) is over
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * h + ii;
+        const int lr = wm * 64 + ii * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = (wn * WTN + j * 32 + 8 * q + cbase) >> 2;
+            L4[lr * 64 + (c ^ (lr & 63))] =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          }
+      }
+      block_barrier();
+      // wave w stores pass rows 16w .. 16w+15; lane l the 16 bytes of chunk l
+      const int col = n0 + 4 * lane;
+#pragma unroll 4
+      for (int rr = 0; rr < 16; ++rr) {
+        const int lr = wave * 16 + rr;
+        const int row = row_begin + (lr >> 6) * WTM + h * 64 + (lr & 63);
+        if (row < row_end && col < p.N)
+          *reinterpret_cast<float4*>(Cf + static_cast<int64_t>(row) * p.ldc + col) = L4[lr * 64 + (lane ^ (lr & 63))];
+      }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
