@@ -393,26 +393,48 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
   // ------------------------------------------------------------ epilogue
   // acc[i][j][4q + c] is row wm*WTM + i*32 + lane%32 and column
   // wn*WTN + j*32 + 8q + 4*(lane/32) + c of the tile (c = 0..3: consecutive columns).
+  // The tile goes through LDS in two passes of 128 rows (pass h takes accumulator rows
+  // i = 2h, 2h+1 of every wave; 128 KB, the whole of LDS), row-major with the 16-byte chunk
+  // c of pass row lr at lr * 64 + (c ^ (lr & 63)).  Each wave then works on whole tile rows,
+  // so every global access of the epilogue is a contiguous run of a row (a 1 KB row of fp32
+  // per instruction for the plain store) instead of 16-byte pieces of 32 rows.
   const int64_t cg = RAG == RAGGED_K ? static_cast<int64_t>(grp) * p.c_gstride : 0;
   uint16_t* C = static_cast<uint16_t*>(p.C) + cg;
   float* Cf = static_cast<float*>(p.C) + cg;
   const int cbase = 4 * (lane >> 5);
-  if (EPI == EPI_SWIGLU_FWD) {
-    // B-tile block 2p holds gate rows and block 2p + 1 the matching up rows
+  float4* L4 = reinterpret_cast<float4*>(lds);
+  static_assert(STAGES * STAGE_ELEMS * 2 >= 128 * BN * 4, "epilogue staging needs 128 KB of LDS");
+  auto pass_row = [&](int lr, int h) { return row_begin + (lr >> 6) * WTM + h * 64 + (lr & 63); };
+  auto chunk = [&](int lr, int c) -> const float4& { return L4[lr * 64 + (c ^ (lr & 63))]; };
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = row_begin + wm * WTM + i * 32 + (lane & 31);
-      if (row >= row_end) continue;
+  for (int h = 0; h < 2; ++h) {
+    block_barrier();  // the previous use of LDS (main loop, or the previous pass) is over
 #pragma unroll
-      for (int pq = 0; pq < NJ / 2; ++pq)
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * h + ii;
+      const int lr = wm * 64 + ii * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = nt * 128 + wn * (WTN / 2) + pq * 32 + 8 * q + cbase;
-          float4 gt, up;
-          gt.x = acc[i][2 * pq][4 * q]; gt.y = acc[i][2 * pq][4 * q + 1];
-          gt.z = acc[i][2 * pq][4 * q + 2]; gt.w = acc[i][2 * pq][4 * q + 3];
-          up.x = acc[i][2 * pq + 1][4 * q]; up.y = acc[i][2 * pq + 1][4 * q + 1];
-          up.z = acc[i][2 * pq + 1][4 * q + 2]; up.w = acc[i][2 * pq + 1][4 * q + 3];
+          const int c = (wn * WTN + j * 32 + 8 * q + cbase) >> 2;
+          L4[lr * 64 + (c ^ (lr & 63))] =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+    }
+    block_barrier();
+    if (EPI == EPI_SWIGLU_FWD) {
+      // tile column blocks of 32 alternate gate and up (block 2b gate, 2b + 1 up, for
+      // output columns nt*128 + 32b ..); two rows per step, 32 lanes per row, lane l the
+      // output columns 4l .. 4l+3 of its row
+      const int l = lane & 31;
+      const int cgate = (l >> 3) * 16 + (l & 7), col = nt * 128 + 4 * l;
+#pragma unroll 2
+      for (int rr = 0; rr < 8; ++rr) {
+        const int lr = wave * 16 + 2 * rr + (lane >> 5);
+        const int row = pass_row(lr, h);
+        if (row < row_end) {
+          const float4 gt = chunk(lr, cgate), up = chunk(lr, cgate + 8);
           float* hrow = Cf + static_cast<int64_t>(row) * p.ldc;
           *reinterpret_cast<float4*>(hrow + col) = gt;
           *reinterpret_cast<float4*>(hrow + p.F + col) = up;
@@ -421,82 +443,44 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
           av.y = pack_bf16x2(silu_f(gt.z) * up.z, silu_f(gt.w) * up.w);
           *reinterpret_cast<uint2*>(p.C2 + static_cast<int64_t>(row) * p.ldc2 + col) = av;
         }
-    }
-  } else if (EPI == EPI_STORE && OUT_F32) {
-    // fp32 tile through LDS, so that every global store instruction writes one whole
-    // 1 KB row of the tile (eight full cache lines) instead of 16-byte pieces of 32 rows.
-    // Two passes of 128 tile rows (64 per wave row) fill the 128 KB of LDS exactly: pass h
-    // takes accumulator rows i = 2h, 2h+1 of every wave.  LDS row lr (pass-local, 0-127)
-    // holds 64 float4 chunks with chunk c at lr * 64 + (c ^ (lr & 63)).
-    float4* L4 = reinterpret_cast<float4*>(lds);
-    static_assert(STAGES * STAGE_ELEMS * 2 >= 128 * BN * 4, "epilogue staging needs 128 KB of LDS");
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      block_barrier();  // the previous use of LDS (main loop or pass 0 stores) is over
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * h + ii;
-        const int lr = wm * 64 + ii * 32 + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c = (wn * WTN + j * 32 + 8 * q + cbase) >> 2;
-            L4[lr * 64 + (c ^ (lr & 63))] =
-                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          }
       }
-      block_barrier();
-      // wave w stores pass rows 16w .. 16w+15; lane l the 16 bytes of chunk l
+    } else {
+      // one row per step, lane l the tile columns 4l .. 4l+3
       const int col = n0 + 4 * lane;
 #pragma unroll 4
       for (int rr = 0; rr < 16; ++rr) {
         const int lr = wave * 16 + rr;
-        const int row = row_begin + (lr >> 6) * WTM + h * 64 + (lr & 63);
-        if (row < row_end && col < p.N)
-          *reinterpret_cast<float4*>(Cf + static_cast<int64_t>(row) * p.ldc + col) = L4[lr * 64 + (lane ^ (lr & 63))];
-      }
-    }
-  } else {
+        const int row = pass_row(lr, h);
+        if (row >= row_end || col >= p.N) continue;
+        const float4 v = chunk(lr, lane);
+        if (EPI == EPI_SWIGLU_BWD) {
+          // dAct -> dH: gate and up halves from the saved fp32 H
+          const float* hrow = p.H + static_cast<int64_t>(row) * p.ldh;
+          const float4 gt = *reinterpret_cast<const float4*>(hrow + col);
+          const float4 up = *reinterpret_cast<const float4*>(hrow + p.F + col);
+          const float g[4] = {gt.x, gt.y, gt.z, gt.w}, u[4] = {up.x, up.y, up.z, up.w};
+          const float dv[4] = {v.x, v.y, v.z, v.w};
+          float dg[4], du[4];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = row_begin + wm * WTM + i * 32 + (lane & 31);
-      if (row >= row_end) continue;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * WTN + j * 32 + 8 * q + cbase;
-          if (col >= p.N) continue;
-          const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
-          const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-          if (EPI == EPI_SWIGLU_BWD) {
-            const float* hrow = p.H + static_cast<int64_t>(row) * p.ldh;
-            const float4 gt = *reinterpret_cast<const float4*>(hrow + col);
-            const float4 up = *reinterpret_cast<const float4*>(hrow + p.F + col);
-            const float g[4] = {gt.x, gt.y, gt.z, gt.w}, u[4] = {up.x, up.y, up.z, up.w};
-            const float dv[4] = {v0, v1, v2, v3};
-            float dg[4], du[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float sg = sigmoid_f(g[c]);
-              dg[c] = dv[c] * u[c] * sg * (1.0f + g[c] * (1.0f - sg));
-              du[c] = dv[c] * g[c] * sg;
-            }
-            uint16_t* drow = C + static_cast<int64_t>(row) * p.ldc;
-            *reinterpret_cast<uint2*>(drow + col) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-            *reinterpret_cast<uint2*>(drow + p.F + col) =
-                make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-          } else if (OUT_F32) {
-            *reinterpret_cast<float4*>(Cf + static_cast<int64_t>(row) * p.ldc + col) = make_float4(v0, v1, v2, v3);
-          } else {
-            *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * p.ldc + col) =
-                make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+          for (int c = 0; c < 4; ++c) {
+            const float sg = sigmoid_f(g[c]);
+            dg[c] = dv[c] * u[c] * sg * (1.0f + g[c] * (1.0f - sg));
+            du[c] = dv[c] * g[c] * sg;
           }
+          uint16_t* drow = C + static_cast<int64_t>(row) * p.ldc;
+          *reinterpret_cast<uint2*>(drow + col) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+          *reinterpret_cast<uint2*>(drow + p.F + col) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+        } else if (OUT_F32) {
+          *reinterpret_cast<float4*>(Cf + static_cast<int64_t>(row) * p.ldc + col) = v;
+        } else {
+          *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * p.ldc + col) =
+              make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
         }
+      }
     }
   }
 }
+
 
 template <int AMAJ, int BMAJ, int RAG, int EPI, bool OUT_F32>
 void launch_kernel(const MfmaArgs& a, int64_t grid, hipStream_t s) {
