@@ -362,40 +362,60 @@ __global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
   }
 
   // epilogue: acc[i][j][4q + c] is row wm*64 + i*32 + lane%32, column
-  // wn*64 + j*32 + 8q + 4(lane/32) + c of the B tile
+  // wn*64 + j*32 + 8q + 4(lane/32) + c of the B tile.  The 256 x 128 fp32 tile goes through
+  // LDS (row-major, 16-byte chunk c of row r at r * 32 + (c ^ (r & 31))), so that the global
+  // writes run along whole rows instead of 16-byte pieces of 32 rows.
+  float4* L4 = reinterpret_cast<float4*>(lds);
+  static_assert(STAGES * STAGE_BYTES >= BM * BN * 4, "epilogue staging needs the tile in LDS");
+  block_barrier();  // every wave is done with the last stage
   const int cb = 4 * (lane >> 5);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int row = row_begin + wm * 64 + i * 32 + (lane & 31);
-    if (row >= row_end) continue;
-    if (EPI == FP8_SWIGLU) {
+    const int r = wm * 64 + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = nt * 64 + wn * 32 + 8 * q + cb;
-        float4 gt, up, act;
-        gt.x = acc[i][0][4 * q]; gt.y = acc[i][0][4 * q + 1]; gt.z = acc[i][0][4 * q + 2]; gt.w = acc[i][0][4 * q + 3];
-        up.x = acc[i][1][4 * q]; up.y = acc[i][1][4 * q + 1]; up.z = acc[i][1][4 * q + 2]; up.w = acc[i][1][4 * q + 3];
-        act.x = silu_f(gt.x) * up.x; act.y = silu_f(gt.y) * up.y;
-        act.z = silu_f(gt.z) * up.z; act.w = silu_f(gt.w) * up.w;
-        if (p.H) {
-          float* hrow = p.H + static_cast<int64_t>(row) * 2 * p.F;
-          *reinterpret_cast<float4*>(hrow + col) = gt;
-          *reinterpret_cast<float4*>(hrow + p.F + col) = up;
-        }
-        *reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.F + col) = act;
+        const int c = (wn * 64 + j * 32 + 8 * q + cb) >> 2;
+        L4[r * 32 + (c ^ (r & 31))] =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nt * BN + wn * 64 + j * 32 + 8 * q + cb;
-          *reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.N + col) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        }
+  }
+  block_barrier();
+  if (EPI == FP8_SWIGLU) {
+    // B-tile column blocks of 32 alternate gate and up; four rows per step, 16 lanes per
+    // row, lane l the output columns 4l .. 4l+3 of nt*64 ..
+    const int l = lane & 15;
+    const int cgate = (l >> 3) * 16 + (l & 7), col = nt * 64 + 4 * l;
+#pragma unroll 2
+    for (int rr = 0; rr < 8; ++rr) {
+      const int r = wave * 32 + rr * 4 + (lane >> 4);
+      const int row = row_begin + r;
+      if (row >= row_end) continue;
+      const float4 gt = L4[r * 32 + (cgate ^ (r & 31))], up = L4[r * 32 + ((cgate + 8) ^ (r & 31))];
+      float4 act;
+      act.x = silu_f(gt.x) * up.x; act.y = silu_f(gt.y) * up.y;
+      act.z = silu_f(gt.z) * up.z; act.w = silu_f(gt.w) * up.w;
+      if (p.H) {
+        float* hrow = p.H + static_cast<int64_t>(row) * 2 * p.F;
+        *reinterpret_cast<float4*>(hrow + col) = gt;
+        *reinterpret_cast<float4*>(hrow + p.F + col) = up;
+      }
+      *reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.F + col) = act;
+    }
+  } else {
+    // two rows per step, 32 lanes per row, lane l the columns 4l .. 4l+3 of nt*BN ..
+    const int l = lane & 31, col = nt * BN + 4 * l;
+#pragma unroll 4
+    for (int rr = 0; rr < 16; ++rr) {
+      const int r = wave * 32 + rr * 2 + (lane >> 5);
+      const int row = row_begin + r;
+      if (row >= row_end) continue;
+      *reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.N + col) = L4[r * 32 + (l ^ (r & 31))];
     }
   }
 }
+
 
 }  // namespace
 
