@@ -123,33 +123,39 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
 }
 
 // Groups of 8 consecutive elements <-> fp32, for the two storage types.
-template <typename T> struct G8;
-template <> struct G8<uint16_t> {
-  __device__ __forceinline__ static void load(const void* base, int64_t g, float* f) {
-    const uint4 v = static_cast<const uint4*>(base)[g];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// Row strips: a row of d values is walked in blocks of up to 512 values (64 lanes x 8);
+// in a block of nb lanes, lane l holds the 4-value chunks c0 = 128 m + l and c1 = c0 + nb,
+// so each access instruction of the wave covers one contiguous run of the row (whole cache
+// lines) rather than every other 16 bytes of it.
+template <typename T> struct R8;
+template <> struct R8<float> {
+  __device__ __forceinline__ static void load(const void* base, int64_t row, int c0, int c1, float* f) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + row);
+    const float4 a = p[c0], b = p[c1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  __device__ __forceinline__ static void store(void* base, int64_t row, int c0, int c1, const float* f) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + row);
+    p[c0] = make_float4(f[0], f[1], f[2], f[3]);
+    p[c1] = make_float4(f[4], f[5], f[6], f[7]);
+  }
+};
+template <> struct R8<uint16_t> {
+  __device__ __forceinline__ static void load(const void* base, int64_t row, int c0, int c1, float* f) {
+    const uint2* p = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + row);
+    const uint2 a = p[c0], b = p[c1];
+    const uint32_t w[4] = {a.x, a.y, b.x, b.y};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = __uint_as_float(w[i] << 16);
       f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   }
-  __device__ __forceinline__ static void store(void* base, int64_t g, const float* f) {
-    static_cast<uint4*>(base)[g] = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                                              pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
-  }
-};
-template <> struct G8<float> {
-  __device__ __forceinline__ static void load(const void* base, int64_t g, float* f) {
-    const float4* p = static_cast<const float4*>(base) + 2 * g;
-    const float4 a = p[0], b = p[1];
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-  }
-  __device__ __forceinline__ static void store(void* base, int64_t g, const float* f) {
-    float4* p = static_cast<float4*>(base) + 2 * g;
-    p[0] = make_float4(f[0], f[1], f[2], f[3]);
-    p[1] = make_float4(f[4], f[5], f[6], f[7]);
+  __device__ __forceinline__ static void store(void* base, int64_t row, int c0, int c1, const float* f) {
+    uint2* p = reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + row);
+    p[c0] = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+    p[c1] = make_uint2(pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
   }
 };
 
@@ -168,7 +174,13 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
   if (t >= Tn) return;
   const int my_r = lane < k ? row_of[static_cast<int64_t>(t) * k + lane] : 0;
   const float my_w = (lane < k && w) ? w[static_cast<int64_t>(t) * k + lane] : 1.0f;
-  for (int u = lane; u < groups; u += 64) {
+  const int d = groups * 8;
+  // every lane stays in the loop (the row shuffles read lanes of the whole wave); lanes
+  // past the end of a short last block only skip their memory accesses
+  for (int m = 0; 64 * m < groups; ++m) {
+    const int nb = min(64, groups - 64 * m);
+    const bool on = lane < nb;
+    const int c0 = 128 * m + lane, c1 = c0 + nb;
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -176,12 +188,12 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
     // has four loads in flight; the sum still runs in slot order
     int j = 0;
     for (; j + 4 <= k; j += 4) {
-      float f[4][8], wj[4];
+      float f[4][8] = {}, wj[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = __shfl(my_r, j + q, 64);
         wj[q] = __shfl(my_w, j + q, 64);
-        G8<TY>::load(Y, static_cast<int64_t>(r) * groups + u, f[q]);
+        if (on) R8<TY>::load(Y, static_cast<int64_t>(r) * d, c0, c1, f[q]);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -191,25 +203,26 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
     for (; j < k; ++j) {
       const int r = __shfl(my_r, j, 64);
       const float wj = __shfl(my_w, j, 64);
-      float f[8];
-      G8<TY>::load(Y, static_cast<int64_t>(r) * groups + u, f);
+      float f[8] = {};
+      if (on) R8<TY>::load(Y, static_cast<int64_t>(r) * d, c0, c1, f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += wj * f[i];
     }
-    const int64_t gi = static_cast<int64_t>(t) * groups + u;
+    if (!on) continue;
+    const int64_t gi = static_cast<int64_t>(t) * d;
     if (add1) {
       float f[8];
-      G8<TA1>::load(add1, gi, f);
+      R8<TA1>::load(add1, gi, c0, c1, f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += f[i];
     }
     if (add2) {
       float f[8];
-      G8<float>::load(add2, gi, f);
+      R8<float>::load(add2, gi, c0, c1, f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += f[i];
     }
-    G8<TO>::store(out, gi, acc);
+    R8<TO>::store(out, gi, c0, c1, acc);
   }
 }
 
@@ -229,14 +242,20 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restric
   if (t >= Tn) return;
   const int my_r = lane < k ? row_of[static_cast<int64_t>(t) * k + lane] : 0;
   const float my_w = lane < k ? w[static_cast<int64_t>(t) * k + lane] : 0.0f;
-  const int64_t t0 = static_cast<int64_t>(t) * groups;
+  const int d = groups * 8;
+  const int64_t t0 = static_cast<int64_t>(t) * d;
   float part[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) part[j] = 0.0f;
-  for (int u = lane; u < groups; u += 64) {
+  for (int m = 0; 64 * m < groups; ++m) {
+    const int nb = min(64, groups - 64 * m);
+    const bool on = lane < nb;  // all lanes stay for the shuffles; off lanes add zeros
+    const int c0 = 128 * m + lane, c1 = c0 + nb;
     float g[8];
-    G8<float>::load(dy, t0 + u, g);
-    if (dY_s) G8<TACT>::store(dY_s, t0 + u, g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g[i] = 0.0f;
+    if (on) R8<float>::load(dy, t0, c0, c1, g);
+    if (on && dY_s) R8<TACT>::store(dY_s, t0, c0, c1, g);
 #pragma unroll
     for (int j0 = 0; j0 < KMAX; j0 += 4) {
       if (j0 < k) {
@@ -245,7 +264,9 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restric
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           r[q] = __shfl(my_r, j0 + q, 64);
-          if (j0 + q < k) G8<float>::load(Y, static_cast<int64_t>(r[q]) * groups + u, y[q]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) y[q][i] = 0.0f;
+          if (on && j0 + q < k) R8<float>::load(Y, static_cast<int64_t>(r[q]) * d, c0, c1, y[q]);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -257,7 +278,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restric
               part[j0 + q] += g[i] * y[q][i];
               gw[i] = g[i] * wj;
             }
-            if (dY) G8<TACT>::store(dY, static_cast<int64_t>(r[q]) * groups + u, gw);
+            if (on && dY) R8<TACT>::store(dY, static_cast<int64_t>(r[q]) * d, c0, c1, gw);
           }
         }
       }
