@@ -27,8 +27,10 @@
 //     of 16 columns and gets back, per lane, one column's 4 k values), so no operand is
 //     ever transposed through registers;
 //   * the MFMA takes the B fragment first, so the accumulator comes out transposed and
-//     each lane owns four consecutive output columns: every epilogue load and store is a
-//     16-byte (fp32) or 8-byte (bf16) vector;
+//     each lane owns four consecutive output columns of one row;
+//   * the epilogue stages the tile through LDS in two passes of 128 rows and then works on
+//     whole tile rows, so its global loads and stores are contiguous runs of a row (a 1 KB
+//     row of fp32 per store instruction) rather than 16 bytes of each of 32 rows;
 //   * a device-built tile list (per-expert prefix of row tiles) so the host never reads
 //     the expert counts; empty experts get no tiles (forward) or exact-zero gradients
 //     (weight gradient, zero-length reduction);
