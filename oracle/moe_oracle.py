@@ -21,8 +21,10 @@ Readings where the pages leave a step open (the same list is kept with the desig
     then index ascending.
   * sigmoid selection keys sigma(l) + bias are evaluated in float64 from the fp32
     logits and fp32 bias.
-  * the aux loss uses the full softmax over all E experts as the router probability,
-    and counts carry no gradient.
+  * the aux loss uses the full softmax over all E experts as the router probability
+    (sigmoid and sqrt(softplus): the scores normalised over all E), and counts carry
+    no gradient; the sequence-wise loss reads tokens in [S, B] order.
+  * pre-softmax top-k ranks the logits (the same order as the probabilities).
   * the shared expert is ungated and added at weight 1.
   * fp8 experts: OCP e4m3 codes with one fp32 scale (amax / 448) per 128 x 128 weight
     block and per token per 128 activation columns; quotient and rounding in fp32.
@@ -61,24 +63,56 @@ def sigmoid(z):
     return 1.0 / (1.0 + np.exp(-z))
 
 
+def softplus(z):
+    """log(1 + e^z), evaluated as max(z, 0) + log(1 + e^-|z|) so that it never overflows."""
+    z = _d(z)
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def score_values(logits, score: str):
+    """Per-expert scores of the two elementwise gating functions.
+
+    [HB] §3.1 Router scoring, Gating function: sigmoid s = 1 / (1 + e^-l), or the
+    square root of softplus, s = sqrt(log(1 + e^l)).  Both are increasing in l.
+    """
+    if score == "sigmoid":
+        return sigmoid(logits)
+    if score == "sqrtsoftplus":
+        return np.sqrt(softplus(logits))
+    raise ValueError(score)
+
+
+def score_derivative(logits, score: str):
+    """ds/dl of score_values: s (1 - s) for sigmoid; sigma(l) / (2 sqrt(softplus(l))) for
+    sqrt(softplus) (softplus' = sigma).  Derived by the chain rule."""
+    l = _d(logits)
+    if score == "sigmoid":
+        s = sigmoid(l)
+        return s * (1.0 - s)
+    if score == "sqrtsoftplus":
+        return sigmoid(l) / (2.0 * np.sqrt(softplus(l)))
+    raise ValueError(score)
+
+
 def selection_keys(logits, score: str, expert_bias=None):
     """The values top-k ranks.
 
     [HB] §3.1 Router scoring, Gating function: the softmax router (renormalised,
     the default) takes top-k on the raw logits and applies softmax to the k selected;
-    the sigmoid router takes top-k on sigma(l), or on sigma(l) + expert_bias when the
-    loss-free bias is on ([HB] §3.3 Load balancing, Loss-free bias: the bias changes
-    only which experts are selected).
+    the sigmoid and sqrt(softplus) routers take top-k on their scores s(l), or on
+    s(l) + expert_bias when the loss-free bias is on ([HB] §3.3 Load balancing,
+    Loss-free bias: the bias changes only which experts are selected; the bias is
+    refused with softmax).  Pre-softmax top-k ranks the full softmax, which is
+    increasing in the logit, so it ranks the logits too (the logits are used, so that
+    two logits fp32 would round to one probability still rank apart).
     """
     l = _d(logits)
     if score == "softmax":
         if expert_bias is not None:
-            raise ValueError("the expert bias is only defined for sigmoid scores")
+            raise ValueError("the expert bias is only defined for sigmoid and sqrt(softplus) scores")
         return l
-    if score == "sigmoid":
-        s = sigmoid(l)
-        return s if expert_bias is None else s + _d(expert_bias)[None, :]
-    raise ValueError(score)
+    s = score_values(l, score)
+    return s if expert_bias is None else s + _d(expert_bias)[None, :]
 
 
 def topk(keys, k: int):
@@ -101,23 +135,27 @@ def margins(keys, k: int):
     return s[:, k - 1] - s[:, k]
 
 
-def mixing_weights(logits, idx, score: str, scaling: float = 1.0):
+def mixing_weights(logits, idx, score: str, scaling: float = 1.0, pre_softmax: bool = False):
     """Mixing weights of the selected experts, shape [T, k].
 
     [HB] §3.1 Router scoring, Gating function and Output scale:
       softmax: softmax over the k selected logits (equal to the full softmax
                renormalised over the top-k);
-      sigmoid: sigma(l_S) / (sum sigma(l_S) + 1e-20) for k > 1, sigma(l_S) for k == 1;
+      softmax with pre-softmax: the full softmax over all E, read at the selected
+               experts, not renormalised (the flag turns renormalisation off);
+      sigmoid / sqrt(softplus): s(l_S) / (sum s(l_S) + 1e-20) for k > 1, s(l_S) for k == 1;
       then the routed scaling factor multiplies the result.
     """
     l = _d(logits)
     lS = np.take_along_axis(l, idx, axis=1)
     k = idx.shape[1]
-    if score == "softmax":
+    if score == "softmax" and pre_softmax:
+        w = np.take_along_axis(softmax_full(l), idx, axis=1)
+    elif score == "softmax":
         z = np.exp(lS - lS.max(axis=1, keepdims=True))
         w = z / z.sum(axis=1, keepdims=True)
-    elif score == "sigmoid":
-        s = sigmoid(lS)
+    elif score in ("sigmoid", "sqrtsoftplus"):
+        s = score_values(lS, score)
         w = s / (s.sum(axis=1, keepdims=True) + 1e-20) if k > 1 else s
     else:
         raise ValueError(score)
@@ -147,6 +185,106 @@ def aux_loss(counts, probs, k: int, coeff: float):
     f = np.asarray(counts, dtype=f64) / (T * k)
     P = probs.mean(axis=0)
     return coeff * E * float(np.sum(f * P))
+
+
+def aux_probs(logits, score: str):
+    """The router probabilities the balancing losses average, [T, E].
+
+    softmax: the full softmax over all E experts.  sigmoid / sqrt(softplus): the scores
+    normalised over all E experts, s / (sum_e s + 1e-20), so that each row sums to 1 and
+    P_e is a mean probability as the aux loss of [HB] §3.3 asks (the pages name "mean
+    router probability" but do not print how the scores for the loss are formed; this is
+    the reading taken).
+    """
+    if score == "softmax":
+        return softmax_full(logits)
+    s = score_values(logits, score)
+    return s / (s.sum(axis=1, keepdims=True) + 1e-20)
+
+
+def logsumexp_rows(logits):
+    """lse_t = log sum_e exp(l_te), with the row maximum taken out first."""
+    l = _d(logits)
+    m = l.max(axis=1)
+    return m + np.log(np.exp(l - m[:, None]).sum(axis=1))
+
+
+def z_loss(logits, coeff: float):
+    """Router z-loss: coeff * mean over tokens of (logsumexp of the token's logits)^2.
+
+    [HB] §3.1 Router scoring, Precision: a penalty on the logits' logsumexp, squared and
+    averaged over the tokens, times the coefficient (ST-MoE's 1e-3 is the value named).
+    """
+    return coeff * float(np.mean(logsumexp_rows(logits) ** 2))
+
+
+def sequence_of_token(T: int, seq_len: int):
+    """Sequence index of every token.  Tokens are ordered [S, B] (position-major, the
+    layout the printed sequence-wise loss reshapes from [S*B, E] to [S, B*E]): token
+    t = s * B + b is position s of sequence b, B = T / S."""
+    if seq_len < 1 or T % seq_len:
+        raise ValueError("seq_len must divide T")
+    B = T // seq_len
+    return np.arange(T) % B
+
+
+def sequence_counts(idx, E: int, seq_len: int):
+    """counts[b, e]: how many (token, slot) pairs of sequence b chose expert e."""
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    B = T // seq_len
+    seq = sequence_of_token(T, seq_len)
+    out = np.zeros((B, E), dtype=np.int64)
+    np.add.at(out, (np.repeat(seq, k), idx.ravel()), 1)
+    return out
+
+
+def seq_aux_loss(idx, probs, k: int, seq_len: int, coeff: float):
+    """Sequence-wise balance loss: the micro-batch aux loss applied to each sequence on
+    its own, then averaged over the B sequences.
+
+    [HB] §3.3 Load balancing, Scope: seq_aux_loss balances per sequence (DeepSeek-V3 keeps
+    one at a coefficient of 1e-4 beside the loss-free bias).  For sequence b with S
+    tokens: coeff * E * sum_e f_be P_be, f_be = counts[b, e] / (k S), P_be the mean of
+    its tokens' probabilities for e; the result is the mean over b.
+    """
+    probs = _d(probs)
+    T, E = probs.shape
+    B = T // seq_len
+    seq = sequence_of_token(T, seq_len)
+    cnt = sequence_counts(idx, E, seq_len)
+    total = 0.0
+    for b in range(B):
+        f = cnt[b] / (k * seq_len)
+        P = probs[seq == b].mean(axis=0)
+        total += coeff * E * float(np.sum(f * P))
+    return total / B
+
+
+def expert_bias_update(expert_bias, counts, rate: float, centered: bool = False):
+    """One step of the loss-free balancing bias, in fp32 (the bias is kept in fp32).
+
+    [HB] §3.3 Load balancing, Loss-free bias: every step each expert's bias moves by the
+    fixed update rate, up when the expert got fewer than the mean load and down when it
+    got more; the comparison with the mean is made on integers, count * E against the
+    total count, so it is exact: direction = sign(total - count * E).  The centered
+    variant subtracts the mean of the steps (Moonlight, Trinity Mini), so the mean bias
+    does not drift.  Each fp32 operation below is one rounding, in this order:
+      step_e = direction_e * rate                       (exact: direction is -1, 0 or 1)
+      centered: m = (rate * sum_e direction_e) / E,  step_e = step_e - m
+      bias_e = bias_e + step_e
+    """
+    c = np.asarray(counts, dtype=np.int64)
+    E = c.shape[0]
+    total = int(c.sum())
+    direction = np.sign(total - c * E).astype(np.int64)
+    b = np.asarray(expert_bias, dtype=np.float32)
+    r = np.float32(rate)
+    step = direction.astype(np.float32) * r
+    if centered:
+        m = np.float32(np.float32(r * np.float32(direction.sum())) / np.float32(E))
+        step = (step - m).astype(np.float32)
+    return (b + step).astype(np.float32)
 
 
 def max_violation(counts):
@@ -235,26 +373,37 @@ def swiglu_backward(X, W13, W2, H, dY):
 class LayerSpec:
     E: int
     k: int
-    score: str = "softmax"
+    score: str = "softmax"          # "softmax" | "sigmoid" | "sqrtsoftplus"
     scaling: float = 1.0
     aux_coeff: float = 0.0
+    pre_softmax: bool = False       # softmax only: weights from the full softmax, no renormalisation
+    z_coeff: float = 0.0            # router z-loss coefficient
+    seq_aux_coeff: float = 0.0      # sequence-wise balance loss coefficient
+    seq_len: int = 0                # S of that loss (tokens ordered [S, B])
 
 
 def route(logits, spec: LayerSpec, expert_bias=None) -> Dict[str, np.ndarray]:
-    """Router: keys -> top-k -> weights -> counts and load statistics."""
+    """Router: keys -> top-k -> weights -> counts and load statistics and losses.
+
+    The balancing losses (aux, z, sequence-wise) are all reported; a zero coefficient
+    gives a zero loss.
+    """
     keys = selection_keys(logits, spec.score, expert_bias)
     idx = topk(keys, spec.k)
-    w = mixing_weights(logits, idx, spec.score, spec.scaling)
+    w = mixing_weights(logits, idx, spec.score, spec.scaling, spec.pre_softmax)
     counts = expert_counts(idx, spec.E)
     out = dict(keys=keys, idx=idx, w=w, counts=counts, margin=margins(keys, spec.k),
                maxvio=max_violation(counts))
-    if spec.score == "softmax":
-        p = softmax_full(logits)
-        out["prob_sum"] = p.sum(axis=0)
-        out["aux"] = aux_loss(counts, p, spec.k, spec.aux_coeff)
+    p = aux_probs(logits, spec.score)
+    out["prob_sum"] = p.sum(axis=0)
+    out["aux"] = aux_loss(counts, p, spec.k, spec.aux_coeff)
+    out["z"] = z_loss(logits, spec.z_coeff)
+    if spec.seq_len:
+        out["seq_counts"] = sequence_counts(idx, spec.E, spec.seq_len)
+        out["seq_aux"] = seq_aux_loss(idx, p, spec.k, spec.seq_len, spec.seq_aux_coeff)
     else:
-        out["prob_sum"] = None
-        out["aux"] = 0.0
+        out["seq_counts"] = None
+        out["seq_aux"] = 0.0
     return out
 
 
@@ -275,8 +424,10 @@ def layer_forward(x, Wg, W13, W2, spec: LayerSpec, bg=None, expert_bias=None,
     r = route(logits, spec, expert_bias)
     if idx is not None:
         r["idx"] = np.asarray(idx, dtype=np.int64)
-        r["w"] = mixing_weights(logits, r["idx"], spec.score, spec.scaling)
+        r["w"] = mixing_weights(logits, r["idx"], spec.score, spec.scaling, spec.pre_softmax)
         r["counts"] = expert_counts(r["idx"], spec.E)
+        if spec.seq_len:
+            r["seq_counts"] = sequence_counts(r["idx"], spec.E, spec.seq_len)
     perm = permutation(r["idx"], spec.E)
     A = T * spec.k
     xp = x[perm.token_of]
@@ -298,15 +449,22 @@ def layer_forward(x, Wg, W13, W2, spec: LayerSpec, bg=None, expert_bias=None,
                 shared=shared, y=y)
 
 
-def router_backward(logits, idx, w, dw, spec: LayerSpec, counts=None, daux: float = 1.0):
-    """d(loss)/d(logits) from the mixing-weight gradient dw [T, k] and the aux loss.
+def router_backward(logits, idx, w, dw, spec: LayerSpec, counts=None, daux: float = 1.0, seq_counts=None):
+    """d(loss)/d(logits) from the mixing-weight gradient dw [T, k] and the balancing losses.
 
-    Softmax over the selected set S with weights w = c * p (c the scaling factor):
-      dl_S = w * dw - (w / c) * <w, dw>, zero off S.
-    Sigmoid renormalised (k > 1), z = sum sigma(l_S) + 1e-20, w = c * s / z:
-      ds = (c / z) * (dw - <dw, s> / z),  dl_S = ds * s * (1 - s).
-    Aux: with g_e = coeff * E * f_e / T (counts held constant),
-      dl_t += daux * p_t * (g - <g, p_t>), p_t the full softmax.
+    Selected set S, scaling factor c:
+      softmax (renormalised), w = c * softmax(l_S):  dl_S = w * dw - (w / c) * <w, dw>;
+      softmax with pre-softmax, w = c * p_S, p the full softmax: through the full softmax
+        with the upstream gradient c * dw at the selected experts (below);
+      sigmoid / sqrt(softplus) renormalised (k > 1), z = sum s(l_S) + 1e-20, w = c * s / z:
+        ds = (c / z) * (dw - <dw, s> / z),  dl_S = ds * s'(l_S);  k == 1: ds = c * dw.
+    Balancing losses, counts held constant, q_t the aux probabilities of the token:
+      aux:      g_e = coeff * E * counts_e / (k T^2);
+      seq aux:  g_e = coeff * E * seq_counts[b(t), e] / (k S^2 B);
+      through q: softmax q: dl_t += q_t * (G - <G, q_t>);  normalised scores
+        q = s / Z (Z = sum_e s + 1e-20): dl_t += s'(l_t) * (G - <G, q_t>) / Z,
+      G = daux * (the g above) (+ c * dw scattered to S for pre-softmax);
+      z-loss:   dl_t += daux * z_coeff * (2 / T) * lse_t * softmax(l_t).
     """
     l = _d(logits)
     T, E = l.shape
@@ -315,22 +473,38 @@ def router_backward(logits, idx, w, dw, spec: LayerSpec, counts=None, daux: floa
     dw = _d(dw)
     w = _d(w)
     dl = np.zeros_like(l)
-    if spec.score == "softmax":
+    G = np.zeros_like(l)
+    if spec.score == "softmax" and spec.pre_softmax:
+        np.put_along_axis(G, idx, c * dw, axis=1)
+    elif spec.score == "softmax":
         dlS = w * dw - (w / c) * np.sum(w * dw, axis=1, keepdims=True)
+        np.put_along_axis(dl, idx, dlS, axis=1)
     else:
-        s = sigmoid(np.take_along_axis(l, idx, axis=1))
+        lS = np.take_along_axis(l, idx, axis=1)
+        s = score_values(lS, spec.score)
         if k > 1:
             z = s.sum(axis=1, keepdims=True) + 1e-20
             ds = (c / z) * (dw - np.sum(dw * s, axis=1, keepdims=True) / z)
         else:
             ds = c * dw
-        dlS = ds * s * (1.0 - s)
-    np.put_along_axis(dl, idx, dlS, axis=1)
-    if spec.score == "softmax" and spec.aux_coeff != 0.0 and daux != 0.0:
-        p = softmax_full(l)
-        f = np.asarray(counts, dtype=f64) / (T * k)
-        g = spec.aux_coeff * E * f / T
-        dl += daux * p * (g[None, :] - (p @ g)[:, None])
+        np.put_along_axis(dl, idx, ds * score_derivative(lS, spec.score), axis=1)
+    if daux != 0.0 and spec.aux_coeff != 0.0:
+        G += daux * spec.aux_coeff * E * np.asarray(counts, dtype=f64)[None, :] / (k * T * T)
+    if daux != 0.0 and spec.seq_aux_coeff != 0.0:
+        S = spec.seq_len
+        B = T // S
+        sc = np.asarray(seq_counts, dtype=f64)
+        G += daux * spec.seq_aux_coeff * E * sc[sequence_of_token(T, S)] / (k * S * S * B)
+    if np.any(G):
+        q = aux_probs(l, spec.score)
+        Gq = np.sum(G * q, axis=1, keepdims=True)
+        if spec.score == "softmax":
+            dl += q * (G - Gq)
+        else:
+            Z = score_values(l, spec.score).sum(axis=1, keepdims=True) + 1e-20
+            dl += score_derivative(l, spec.score) * (G - Gq) / Z
+    if daux != 0.0 and spec.z_coeff != 0.0:
+        dl += daux * spec.z_coeff * (2.0 / T) * logsumexp_rows(l)[:, None] * softmax_full(l)
     return dl
 
 
@@ -375,7 +549,8 @@ def layer_backward(fwd: Dict[str, object], x, Wg, W13, W2, dy, spec: LayerSpec,
         gs = swiglu_backward(x, W13s, W2s, fwd["shared"]["H"], dy)
         dx = dx + gs["dX"]
         out.update(dW13s=gs["dW13"], dW2s=gs["dW2"], dH_s=gs["dH"])
-    dlogits = router_backward(fwd["logits"], idx, w, dw, spec, counts=r["counts"], daux=daux)
+    dlogits = router_backward(fwd["logits"], idx, w, dw, spec, counts=r["counts"], daux=daux,
+                              seq_counts=r.get("seq_counts"))
     out["dlogits"] = dlogits
     out["dWg"] = dlogits.T @ x
     out["dbg"] = dlogits.sum(axis=0)
@@ -386,9 +561,11 @@ def layer_backward(fwd: Dict[str, object], x, Wg, W13, W2, dy, spec: LayerSpec,
 
 def layer_loss(x, Wg, W13, W2, dy, spec: LayerSpec, bg=None, expert_bias=None,
                W13s=None, W2s=None, daux: float = 1.0) -> float:
-    """L = sum(dy * y) + daux * aux, the scalar whose gradient layer_backward returns."""
+    """L = sum(dy * y) + daux * (aux + z + seq_aux), the scalar whose gradient
+    layer_backward returns."""
     f = layer_forward(x, Wg, W13, W2, spec, bg=bg, expert_bias=expert_bias, W13s=W13s, W2s=W2s)
-    return float(np.sum(_d(dy) * f["y"]) + daux * f["route"]["aux"])
+    r = f["route"]
+    return float(np.sum(_d(dy) * f["y"]) + daux * (r["aux"] + r["z"] + r["seq_aux"]))
 
 
 # ------------------------------------------------------------------------ fp8 experts
@@ -508,7 +685,8 @@ def router_path_backward(fwd: Dict[str, object], x, Wg, dy, spec: "LayerSpec", d
     x, dy = _d(x), _d(dy)
     r, perm = fwd["route"], fwd["perm"]
     dw = np.einsum("td,tkd->tk", dy, fwd["Y_perm"][perm.row_of])
-    dl = router_backward(fwd["logits"], r["idx"], r["w"], dw, spec, counts=r["counts"], daux=daux)
+    dl = router_backward(fwd["logits"], r["idx"], r["w"], dw, spec, counts=r["counts"], daux=daux,
+                         seq_counts=r.get("seq_counts"))
     return dict(dw=dw, dlogits=dl, dWg=dl.T @ x, dbg=dl.sum(axis=0), dx_router=dl @ _d(Wg))
 
 

@@ -32,7 +32,7 @@ def _ffn_torch(x, W13, W2):
     return (torch.nn.functional.silu(h[:, :F]) * h[:, F:]) @ W2.T
 
 
-def _rand_layer(rng, T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux=0.0, bias=None):
+def _rand_layer(rng, T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux=0.0, bias=None, **extra):
     x = rng.standard_normal((T, d))
     Wg = rng.standard_normal((E, d)) / np.sqrt(d)
     W13 = rng.standard_normal((E, 2 * F, d)) / np.sqrt(d)
@@ -42,7 +42,7 @@ def _rand_layer(rng, T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux=0.0,
     bg = rng.standard_normal(E) * 0.3 if bias == "bg" else None
     eb = rng.standard_normal(E) * 0.1 if bias == "expert_bias" else None
     dy = rng.standard_normal((T, d))
-    spec = O.LayerSpec(E=E, k=k, score=score, scaling=scaling, aux_coeff=aux)
+    spec = O.LayerSpec(E=E, k=k, score=score, scaling=scaling, aux_coeff=aux, **extra)
     return dict(x=x, Wg=Wg, W13=W13, W2=W2, W13s=W13s, W2s=W2s, bg=bg, expert_bias=eb, dy=dy), spec
 
 
@@ -287,11 +287,22 @@ def test_layer_against_independent_token_loop():
     dict(score="softmax", k=3, aux=0.0, Fs=4, scaling=2.5, bias=None),
     dict(score="sigmoid", k=2, aux=0.0, Fs=4, scaling=1.0, bias="expert_bias"),
     dict(score="sigmoid", k=1, aux=0.0, Fs=0, scaling=1.3, bias=None),
+    # the balancing losses and router variants
+    dict(score="softmax", k=1, aux=0.4, Fs=0, scaling=1.0, bias="bg", extra=dict(pre_softmax=True, z_coeff=0.05)),
+    dict(score="softmax", k=2, aux=0.0, Fs=0, scaling=2.5, bias=None,
+         extra=dict(pre_softmax=True, seq_aux_coeff=0.3, seq_len=4)),
+    dict(score="softmax", k=2, aux=0.2, Fs=0, scaling=1.0, bias=None,
+         extra=dict(z_coeff=0.02, seq_aux_coeff=0.5, seq_len=8)),
+    dict(score="sigmoid", k=2, aux=0.3, Fs=4, scaling=1.0, bias="expert_bias",
+         extra=dict(z_coeff=0.01, seq_aux_coeff=0.4, seq_len=4)),
+    dict(score="sqrtsoftplus", k=2, aux=0.0, Fs=0, scaling=1.7, bias="expert_bias",
+         extra=dict(seq_aux_coeff=0.6, seq_len=16)),
+    dict(score="sqrtsoftplus", k=1, aux=0.5, Fs=0, scaling=1.0, bias=None, extra=dict(z_coeff=0.03)),
 ])
 def test_backward_matches_central_differences(case):
     rng = np.random.default_rng(14)
     L, spec = _rand_layer(rng, T=16, d=8, E=4, k=case["k"], F=8, Fs=case["Fs"], score=case["score"],
-                          scaling=case["scaling"], aux=case["aux"], bias=case["bias"])
+                          scaling=case["scaling"], aux=case["aux"], bias=case["bias"], **case.get("extra", {}))
     keys = O.selection_keys(O.gate_logits(L["x"], L["Wg"], L["bg"]), spec.score, L["expert_bias"])
     assert O.margins(keys, spec.k).min() > 1e-4           # far from a routing flip
     kw = dict(bg=L["bg"], expert_bias=L["expert_bias"], W13s=L["W13s"], W2s=L["W2s"])
@@ -414,3 +425,159 @@ def test_fp8_layer_equals_exact_layer_up_to_act_rounding():
     diff = np.abs(f8["y"] - ex["y"])
     assert np.all(diff <= bound * (1 + 1e-9) + 1e-15)
     assert diff.max() > 0          # the Act rounding did happen
+
+
+# ------------------------------------------------- router variants and balancing losses
+
+def test_z_loss_closed_form_and_library_logsumexp():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(21)
+    T, E, c = 50, 16, 1e-3
+    # equal logits: lse = v + ln E for every token
+    v = 1.7
+    assert O.z_loss(np.full((T, E), v), c) == pytest.approx(c * (v + math.log(E)) ** 2, rel=1e-14)
+    l = rng.standard_normal((T, E)) * 3 + 40.0       # large shared offset: no overflow
+    assert O.z_loss(l, c) == pytest.approx(c * np.mean(logsumexp(l, axis=1) ** 2), rel=1e-13)
+    # a shared shift u moves every lse by u
+    u = -2.5
+    np.testing.assert_allclose(O.logsumexp_rows(l + u), O.logsumexp_rows(l) + u, rtol=1e-14)
+
+
+def test_seq_aux_loss_reduces_to_aux_and_matches_printed_code_form():
+    rng = np.random.default_rng(22)
+    E, k, S, B, c = 12, 3, 20, 5, 0.01
+    T = S * B
+    l = rng.standard_normal((T, E))
+    idx = O.topk(l, k)
+    p = O.softmax_full(l)
+    # one sequence: the micro-batch loss
+    assert O.seq_aux_loss(idx, p, k, T, c) == pytest.approx(O.aux_loss(O.expert_counts(idx, E), p, k, c), rel=1e-14)
+    # flat probabilities: coeff, whatever the load
+    assert O.seq_aux_loss(idx, np.full((T, E), 1.0 / E), k, S, c) == pytest.approx(c, rel=1e-14)
+    # the printed code form: reshape [S*B, E] -> [S, B*E], per-(sequence, expert) counts,
+    # the Switch formula with S tokens, divided by B
+    probs = torch.as_tensor(p).reshape(S, B * E)
+    rmap = torch.zeros(T, E, dtype=torch.float64)
+    rmap.scatter_(1, torch.as_tensor(idx), 1.0)
+    tpe = rmap.reshape(S, B * E).sum(0)
+    code = float(torch.sum(probs.sum(0) * tpe) * (E * c / (k * S * S))) / B
+    assert O.seq_aux_loss(idx, p, k, S, c) == pytest.approx(code, rel=1e-13)
+    # a per-sequence loop that gathers sequence b's tokens b, b + B, b + 2B, ...
+    loop = np.mean([O.aux_loss(O.expert_counts(idx[b::B], E), p[b::B], k, c) for b in range(B)])
+    assert O.seq_aux_loss(idx, p, k, S, c) == pytest.approx(loop, rel=1e-13)
+    cnt = O.sequence_counts(idx, E, S)
+    assert cnt.shape == (B, E) and np.all(cnt.sum(axis=1) == S * k)
+
+
+def test_pre_softmax_weights_are_full_probabilities():
+    rng = np.random.default_rng(23)
+    T, E = 40, 10
+    l = rng.standard_normal((T, E)) * 2
+    probs = torch.softmax(torch.as_tensor(l), dim=1)
+    for k in (1, 3, E):
+        tv, ti = torch.topk(probs, k, dim=1)              # library top-k on the probabilities
+        idx = O.topk(O.selection_keys(l, "softmax"), k)
+        assert np.array_equal(idx, ti.numpy())
+        w = O.mixing_weights(l, idx, "softmax", 1.0, pre_softmax=True)
+        np.testing.assert_allclose(w, tv.numpy(), rtol=1e-14)
+        if k < E:
+            assert np.all(w.sum(axis=1) < 1.0)            # no renormalisation
+        else:
+            np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-14)
+    # top-1 with pre-softmax: the weight is the top probability and the router gets a
+    # gradient (post-softmax top-1 gives weight 1 and none)
+    spec = O.LayerSpec(E=E, k=1, pre_softmax=True)
+    idx = O.topk(l, 1)
+    w = O.mixing_weights(l, idx, "softmax", 1.0, pre_softmax=True)
+    dl = O.router_backward(l, idx, w, np.ones((T, 1)), spec)
+    assert np.abs(dl).max() > 1e-3
+    # d w_top / d l for dw = 1: p_top (1 - p_top) at the top expert, -p_top p_e elsewhere
+    pt = probs.numpy()
+    ref = -pt * pt[np.arange(T), idx[:, 0]][:, None]
+    ref[np.arange(T), idx[:, 0]] = pt[np.arange(T), idx[:, 0]] * (1 - pt[np.arange(T), idx[:, 0]])
+    np.testing.assert_allclose(dl, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_sqrt_softplus_scores():
+    rng = np.random.default_rng(24)
+    l = rng.standard_normal((30, 9)) * 4
+    ref = torch.nn.functional.softplus(torch.as_tensor(l)).sqrt().numpy()
+    np.testing.assert_allclose(O.score_values(l, "sqrtsoftplus"), ref, rtol=1e-14)
+    assert O.score_values(np.array([0.0]), "sqrtsoftplus")[0] == pytest.approx(math.sqrt(math.log(2.0)), rel=1e-15)
+    # no overflow far out: softplus(l) -> l
+    assert O.score_values(np.array([800.0]), "sqrtsoftplus")[0] == pytest.approx(math.sqrt(800.0), rel=1e-15)
+    # the three gating functions rank experts alike
+    for k in (1, 4):
+        a = O.topk(O.selection_keys(l, "softmax"), k)
+        assert np.array_equal(a, O.topk(O.selection_keys(l, "sigmoid"), k))
+        assert np.array_equal(a, O.topk(O.selection_keys(l, "sqrtsoftplus"), k))
+    # for positive logits the ratio of two weights tends to sqrt of the ratio of the logits
+    L1, L2 = 3.0, 1.2
+    for a, tol in ((10.0, 1e-2), (1000.0, 1e-4)):
+        lg = np.array([[a * L1, a * L2, -50.0]])
+        w = O.mixing_weights(lg, np.array([[0, 1]]), "sqrtsoftplus")
+        assert w[0, 0] / w[0, 1] == pytest.approx(math.sqrt(L1 / L2), rel=tol)
+    # derivative against the library's autograd
+    t = torch.as_tensor(l, dtype=torch.float64).requires_grad_(True)
+    torch.nn.functional.softplus(t).sqrt().sum().backward()
+    np.testing.assert_allclose(O.score_derivative(l, "sqrtsoftplus"), t.grad.numpy(), rtol=1e-13)
+
+
+def test_normalised_aux_probabilities_for_sigmoid_scores():
+    rng = np.random.default_rng(25)
+    l = rng.standard_normal((20, 7))
+    for score in ("sigmoid", "sqrtsoftplus"):
+        q = O.aux_probs(l, score)
+        np.testing.assert_allclose(q.sum(axis=1), 1.0, rtol=1e-14)
+        s = expit(l) if score == "sigmoid" else np.sqrt(np.log1p(np.exp(l)))
+        np.testing.assert_allclose(q, s / s.sum(axis=1, keepdims=True), rtol=1e-13)
+
+
+def test_expert_bias_update_printed_rule_and_properties():
+    rng = np.random.default_rng(26)
+    E, T, k, rate = 16, 256, 4, 1e-3
+    # a few hot experts and many just under the mean load
+    counts = np.full(E, T * k // E - 3, dtype=np.int64)
+    counts[:3] += (T * k - counts.sum()) // 3
+    counts[0] += T * k - counts.sum()
+    assert counts.sum() == T * k
+    bias = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    new = O.expert_bias_update(bias, counts, rate)
+    # the printed form, in torch: direction = sign(total - count * E), bias += direction * rate
+    tc = torch.as_tensor(counts)
+    direction = torch.sign(tc.sum(-1, keepdim=True) - tc * E)
+    code = torch.as_tensor(bias) + direction.to(torch.float32) * rate
+    assert np.array_equal(new, code.numpy())
+    over, under = counts * E > T * k, counts * E < T * k
+    assert np.all(new[over] < bias[over]) and np.all(new[under] > bias[under])
+    # an expert exactly at the mean keeps its bias; the integer comparison is exact where
+    # the mean total / E is not an integer
+    c2 = np.array([3, 2, 2], dtype=np.int64)            # mean 7/3
+    b2 = O.expert_bias_update(np.zeros(3, np.float32), c2, 0.5)
+    assert list(b2) == [-0.5, 0.5, 0.5]
+    c3 = np.array([4, 4, 4, 4], dtype=np.int64)
+    assert np.array_equal(O.expert_bias_update(bias[:4], c3, rate), bias[:4])
+    # most steps point up here: the sign update lifts the mean bias; the centered update
+    # keeps it (to fp32 rounding), and both route alike (a shared shift keeps the top-k)
+    cen = O.expert_bias_update(bias, counts, rate, centered=True)
+    assert new.mean() - bias.mean() > 0.5 * rate
+    assert abs(float(cen.astype(np.float64).sum() - bias.astype(np.float64).sum())) < E * 1e-7
+    s = O.sigmoid(rng.standard_normal((T, E)))
+    assert np.array_equal(O.topk(s + new.astype(np.float64), k), O.topk(s + (cen + (new - cen).mean()).astype(np.float64), k)) or \
+        np.allclose(new - cen, (new - cen).mean(), atol=1e-9)
+
+
+def test_expert_bias_update_balances_a_fixed_batch():
+    # the loop of the loss-free bias on one batch: repeated sign steps bring MaxVio down
+    rng = np.random.default_rng(27)
+    T, E, k = 512, 16, 2
+    l = rng.standard_normal((T, E)) + np.linspace(-1.5, 1.5, E)[None, :]
+    s = O.sigmoid(l)
+    bias = np.zeros(E, np.float32)
+    first = None
+    for step in range(400):
+        counts = O.expert_counts(O.topk(s + bias.astype(np.float64), k), E)
+        mv = O.max_violation(counts)
+        first = mv if first is None else first
+        bias = O.expert_bias_update(bias, counts, 2e-3)
+    assert first > 1.0 and mv < 0.25 * first
