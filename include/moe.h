@@ -70,33 +70,42 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
 
-/* [HB] §3.1 Router scoring, Gating function. */
-typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_t;
+/* [HB] §3.1 Router scoring, Gating function: softmax, sigmoid, or the square root of
+ * softplus, s = sqrt(log(1 + e^l)). */
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1, MOE_SQRTSOFTPLUS = 2 } moe_score_t;
 
-#define MOE_NSTATS 4 /* stats[]: aux loss, MaxVio, number of empty experts, max count */
+/* stats[]: aux loss, MaxVio, number of empty experts, max count, router z-loss,
+ * sequence-wise aux loss (each loss already multiplied by its coefficient). */
+#define MOE_NSTATS 6
 
 /*
  * The layer's settings, mirroring the flags of [HB] §2.5 Your first MoE (number of
  * experts, expert FFN width, top-k), §3.1 (score function, routed scaling factor),
- * §3.3 Aux loss (coefficient) and §3.4 Shared experts (shared width).
+ * §3.3 Aux loss (coefficient) and §3.4 Shared experts (shared width), plus the
+ * balancing losses of §3.1 Precision (z-loss) and §3.3 Scope (sequence-wise loss).
  * Rules checked by moe_validate:
  *   1 <= k <= min(E, 32), E <= 2048, T >= 1, T*k < 2^31, d % 64 == 0, F % 64 == 0,
  *   Fs % 64 == 0; bf16: F % 128 == 0 and Fs % 128 == 0;
- *   softmax with k == 1 needs pre-softmax, which is not provided: UNSUPPORTED
- *   ([HB] §3.1 Output scale: a softmax over one logit has no gradient);
- *   pre_softmax must be 0 (UNSUPPORTED otherwise);
- *   aux_coeff != 0 only with softmax scores (UNSUPPORTED otherwise);
+ *   pre_softmax is 0 or 1 and only with softmax scores (UNSUPPORTED otherwise);
+ *   softmax with k == 1 needs pre_softmax (UNSUPPORTED otherwise: [HB] §3.1 Output
+ *   scale, a softmax over one selected logit gives the router no gradient);
+ *   aux_coeff, z_coeff, seq_aux_coeff finite and >= 0; seq_aux_coeff > 0 needs
+ *   seq_len >= 1 dividing T (INVALID_ARG otherwise) and T / seq_len <= 65535;
  *   w_dtype == MOE_FP8_E4M3 (fp8 experts, see moe_quantize_fp8) needs act_dtype == bf16,
  *   Fs == 0, d % 128 == 0 and F % 128 == 0 (UNSUPPORTED otherwise).
  */
 typedef struct moe_config {
   int32_t T, d, E, k, F, Fs;
   int32_t score;          /* moe_score_t */
-  int32_t pre_softmax;    /* must be 0 */
+  int32_t pre_softmax;    /* softmax only: 1 = top-k of the full softmax, weights not renormalised */
   float routed_scaling;   /* multiplies the renormalised weights ([HB] §3.1 Output scale) */
   float aux_coeff;        /* Switch aux-loss coefficient ([HB] §3.3 Aux loss) */
   int32_t act_dtype;      /* moe_dtype_t of activations (and of expert weights when w_dtype == 0) */
   int32_t w_dtype;        /* 0: expert weights in act_dtype; MOE_FP8_E4M3: e4m3 codes + scales */
+  float z_coeff;          /* router z-loss coefficient ([HB] §3.1 Precision); 0 = off */
+  float seq_aux_coeff;    /* sequence-wise aux-loss coefficient ([HB] §3.3 Scope); 0 = off */
+  int32_t seq_len;        /* S of the sequence-wise loss: tokens are ordered [S, B], token
+                             t = s * B + b is position s of sequence b, B = T / S */
 } moe_config_t;
 
 typedef struct moe_weights {
@@ -129,6 +138,7 @@ typedef struct moe_saved {
   void* Y_s;         /* [T, d]   fp32, or NULL */
   float* x_perm_scale; /* fp8 weights only: [A, d/128], the scales of x_perm's e4m3 rows */
   float* Act_scale;    /* fp8 weights only: [A, F/128], the scales of Act's e4m3 rows */
+  int32_t* seq_counts; /* [B, E] tokens of sequence b routed to e; needed when seq_aux_coeff > 0 */
 } moe_saved_t;
 
 /* Gradients written by moe_layer_bwd (overwritten, not accumulated). */
@@ -159,17 +169,34 @@ moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* fwd_bytes, size
 moe_status_t moe_gate_logits(const moe_config_t* cfg, const void* x, const float* Wg, const float* bg,
                              float* logits, void* ws, size_t ws_bytes, void* stream);
 
-/* Top-k router ([HB] §3.1 Gating function and Output scale; §3.3 Aux loss):
- *   keys: softmax -> the logits; sigmoid -> sigma(l) + expert_bias, evaluated in fp64;
+/* Top-k router ([HB] §3.1 Gating function and Output scale; §3.3 Aux loss, Scope):
+ *   keys: softmax -> the logits (also with pre_softmax: the full softmax ranks as the
+ *         logits do); sigmoid / sqrt(softplus) -> s(l) + expert_bias, evaluated in fp64;
  *   idx: top-k of the keys, ties to the lower expert index;
- *   w:   softmax over the k selected logits, or sigma(l_S) / (sum + 1e-20) (k > 1), times
+ *   w:   softmax over the k selected logits; with pre_softmax the full softmax at the
+ *        selected experts; or s(l_S) / (sum + 1e-20) (k > 1), s(l_S) (k == 1); times
  *        routed_scaling;
- *   counts[e]: tokens routed to e; prob_sum[e] = sum_t softmax(l_t)_e (softmax only, NULL ok);
- *   stats[MOE_NSTATS] (NULL ok): aux = coeff * E * sum_e f_e P_e, MaxVio, empty experts,
- *   max count.  expert_bias must be NULL for softmax. */
+ *   counts[e]: tokens routed to e;
+ *   prob_sum[e] = sum_t q_te (NULL ok), q the aux probabilities: the full softmax, or the
+ *        scores normalised over all E, s / (sum_e s + 1e-20);
+ *   stats[MOE_NSTATS] (NULL ok): aux = aux_coeff * E * sum_e f_e P_e, MaxVio, empty
+ *        experts, max count, z = z_coeff * mean_t logsumexp(l_t)^2, and the sequence-wise
+ *        loss seq_aux_coeff * mean_b E sum_e f_be P_be over the B = T / seq_len sequences;
+ *   seq_counts [B, E] (needed when seq_aux_coeff > 0, else ignored): per-sequence counts.
+ *   expert_bias must be NULL for softmax. */
 moe_status_t moe_router_topk(const moe_config_t* cfg, const float* logits, const float* expert_bias,
                              int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* stats,
-                             void* ws, size_t ws_bytes, void* stream);
+                             int32_t* seq_counts, void* ws, size_t ws_bytes, void* stream);
+
+/* Loss-free balancing bias, one update ([HB] §3.3 Load balancing, Loss-free bias):
+ *   direction_e = sign(sum(counts) - counts[e] * E)   (integers: exact),
+ *   step_e = direction_e * rate;  centered != 0: step_e -= (rate * sum_e direction_e) / E;
+ *   expert_bias[e] += step_e,
+ * each operation one fp32 rounding in that order.  counts [E] int32 (for example the
+ * router's counts, or their sum over the micro-batches of a step, below 2^31);
+ * expert_bias [E] fp32, updated in place.  Errors: rate not finite -> INVALID_ARG. */
+moe_status_t moe_expert_bias_update(const moe_config_t* cfg, const int32_t* counts, float rate, int32_t centered,
+                                    float* expert_bias, void* stream);
 
 /* Dropless permutation ([LC] "Read the timeline before blaming the network": tokens are
  * grouped by expert before the expert matmuls): offsets = exclusive prefix of the
@@ -196,7 +223,8 @@ moe_status_t moe_unpermute_combine(const moe_config_t* cfg, const float* Y_perm,
                                    const float* w, const float* Y_s, float* y, void* stream);
 
 /* Whole forward: gate logits, router, permute, grouped experts (+ shared), combine.
- * Fills *saved for the backward.  stats as in moe_router_topk (NULL ok).
+ * Fills *saved for the backward.  stats as in moe_router_topk (NULL ok); saved->seq_counts
+ * receives the per-sequence counts when seq_aux_coeff > 0.
  * fp8 experts: x (bf16) is quantised per token per 128 before the permute, the weights
  * are e4m3 codes with weights->W13_scale / W2_scale, and saved->x_perm, saved->Act hold
  * codes with saved->x_perm_scale, saved->Act_scale. */
@@ -205,7 +233,7 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* weights
                            void* stream);
 
 /* ---------------------------------------------------------------- backward pieces
- * Derivatives of L = sum(dy * y) + daux * aux; mixing weights carry the gradient to
+ * Derivatives of L = sum(dy * y) + daux * (aux + z + seq_aux); mixing weights carry the gradient to
  * the router, selection carries none ([LC] "How the router learns without an
  * expert-selection answer key"). */
 
@@ -284,10 +312,14 @@ moe_status_t moe_permute_bwd(const moe_config_t* cfg, const float* dX_perm, cons
                              const float* dx_s, const float* dx_r, float* dx, void* stream);
 
 /* Router backward: dlogits [T, E] from dw [T, k] through the weights of the selected
- * experts, plus daux times the aux-loss gradient through the full softmax (counts held
- * constant).  counts may be NULL when aux_coeff == 0 or daux == 0. */
+ * experts (pre_softmax: through the full softmax), plus daux times the gradients of the
+ * aux loss and the sequence-wise loss through the aux probabilities (counts held
+ * constant) and of the z-loss through the softmax of the logits.  counts may be NULL
+ * when aux_coeff == 0 or daux == 0; seq_counts [B, E] may be NULL when seq_aux_coeff == 0
+ * or daux == 0. */
 moe_status_t moe_router_bwd(const moe_config_t* cfg, const float* logits, const int32_t* idx, const float* w,
-                            const float* dw, const int32_t* counts, float daux, float* dlogits, void* stream);
+                            const float* dw, const int32_t* counts, const int32_t* seq_counts, float daux,
+                            float* dlogits, void* stream);
 
 /* Gate backward: dWg = dlogits^T x [E, d]; dbg = column sums of dlogits (NULL ok);
  * dx_r = dlogits Wg [T, d] fp32 (NULL ok).  On the matrix cores like moe_gate_logits, with

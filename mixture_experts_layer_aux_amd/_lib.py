@@ -18,15 +18,17 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
-MOE_SOFTMAX, MOE_SIGMOID = 0, 1
-MOE_NSTATS = 4
+MOE_SOFTMAX, MOE_SIGMOID, MOE_SQRTSOFTPLUS = 0, 1, 2
+_SCORES = {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID, "sqrtsoftplus": MOE_SQRTSOFTPLUS}
+# stats[]: aux, MaxVio, empty experts, max count, z-loss, sequence-wise aux loss
+MOE_NSTATS = 6
 
 EXPORTED = (
     "moe_status_string", "moe_last_error", "moe_validate", "moe_workspace_size", "moe_gate_logits",
     "moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu", "moe_unpermute_combine", "moe_layer_fwd",
     "moe_unpermute_combine_bwd", "moe_grouped_gemm_swiglu_bwd", "moe_grouped_wgrad", "moe_permute_bwd", "moe_router_bwd",
     "moe_quantize_fp8", "moe_permute_fp8", "moe_grouped_gemm_swiglu_fp8",
-    "moe_gate_logits_bwd", "moe_layer_bwd",
+    "moe_gate_logits_bwd", "moe_layer_bwd", "moe_expert_bias_update",
 )
 
 
@@ -40,7 +42,8 @@ class Config(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("F", ctypes.c_int32), ("Fs", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("pre_softmax", ctypes.c_int32), ("routed_scaling", ctypes.c_float), ("aux_coeff", ctypes.c_float),
-                ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32)]
+                ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("z_coeff", ctypes.c_float),
+                ("seq_aux_coeff", ctypes.c_float), ("seq_len", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -53,7 +56,8 @@ class Weights(ctypes.Structure):
 
 class Saved(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("logits", "idx", "w", "counts", "offsets", "row_of", "token_of", "x_perm", "H",
-                                  "Act", "Y_perm", "H_s", "Act_s", "Y_s", "x_perm_scale", "Act_scale")]
+                                  "Act", "Y_perm", "H_s", "Act_s", "Y_s", "x_perm_scale", "Act_scale",
+                                  "seq_counts")]
 
 
 class Grads(ctypes.Structure):
@@ -86,15 +90,26 @@ def _check(status: int) -> None:
         raise MoeError(status, f"{lib.moe_status_string(status).decode()}: {lib.moe_last_error().decode()}")
 
 
-def make_config(T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux_coeff=0.0, act="bf16", wq="") -> Config:
+def make_config(T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux_coeff=0.0, act="bf16", wq="",
+                pre_softmax=False, z_coeff=0.0, seq_aux_coeff=0.0, seq_len=0) -> Config:
     """wq: "" (expert weights in the activation dtype) or "fp8" (e4m3 codes + block scales)."""
-    return Config(T=T, d=d, E=E, k=k, F=F, Fs=Fs, score=MOE_SOFTMAX if score == "softmax" else MOE_SIGMOID,
-                  pre_softmax=0, routed_scaling=scaling, aux_coeff=aux_coeff,
-                  act_dtype=MOE_BF16 if act == "bf16" else MOE_F32, w_dtype=MOE_FP8_E4M3 if wq == "fp8" else 0)
+    return Config(T=T, d=d, E=E, k=k, F=F, Fs=Fs, score=_SCORES[score], pre_softmax=int(bool(pre_softmax)),
+                  routed_scaling=scaling, aux_coeff=aux_coeff, act_dtype=MOE_BF16 if act == "bf16" else MOE_F32,
+                  w_dtype=MOE_FP8_E4M3 if wq == "fp8" else 0, z_coeff=z_coeff, seq_aux_coeff=seq_aux_coeff,
+                  seq_len=seq_len)
 
 
-def config_from_shape(s) -> Config:
-    return make_config(s.T, s.d, s.E, s.k, s.F, s.Fs, s.score, s.scaling, s.aux_coeff, s.act, getattr(s, "wq", ""))
+def config_from_shape(s, **extra) -> Config:
+    kw = dict(pre_softmax=getattr(s, "pre_softmax", False), z_coeff=getattr(s, "z_coeff", 0.0),
+              seq_aux_coeff=getattr(s, "seq_aux_coeff", 0.0), seq_len=getattr(s, "seq_len", 0))
+    kw.update(extra)
+    return make_config(s.T, s.d, s.E, s.k, s.F, s.Fs, s.score, s.scaling, s.aux_coeff, s.act, getattr(s, "wq", ""),
+                       **kw)
+
+
+def num_sequences(cfg: Config) -> int:
+    """B of the sequence-wise loss (0 when it is off)."""
+    return cfg.T // cfg.seq_len if cfg.seq_aux_coeff != 0.0 and cfg.seq_len > 0 else 0
 
 
 def is_fp8(cfg: Config) -> bool:
@@ -154,16 +169,25 @@ def gate_logits(cfg, x, Wg, bg, logits, ws, stream=None):
                                   _P(_stream(stream))))
 
 
-def router_topk(cfg, logits, expert_bias, idx, w, counts, prob_sum, stats, ws, stream=None):
+def router_topk(cfg, logits, expert_bias, idx, w, counts, prob_sum, stats, ws, stream=None, seq_counts=None):
     wp, wn = _ws(ws)
     TK = cfg.T * cfg.k
+    nsc = num_sequences(cfg) * cfg.E
     _check(load().moe_router_topk(ctypes.byref(cfg), _P(_ptr(logits, torch.float32, cfg.T * cfg.E, "logits")),
                                   _P(_ptr(expert_bias, torch.float32, cfg.E, "expert_bias")),
                                   _P(_ptr(idx, torch.int32, TK, "idx")), _P(_ptr(w, torch.float32, TK, "w")),
                                   _P(_ptr(counts, torch.int32, cfg.E, "counts")),
                                   _P(_ptr(prob_sum, torch.float32, cfg.E, "prob_sum")),
-                                  _P(_ptr(stats, torch.float32, MOE_NSTATS, "stats")), _P(wp), ctypes.c_size_t(wn),
+                                  _P(_ptr(stats, torch.float32, MOE_NSTATS, "stats")),
+                                  _P(_ptr(seq_counts, torch.int32, nsc, "seq_counts")), _P(wp), ctypes.c_size_t(wn),
                                   _P(_stream(stream))))
+
+
+def expert_bias_update(cfg, counts, rate, centered, expert_bias, stream=None):
+    _check(load().moe_expert_bias_update(ctypes.byref(cfg), _P(_ptr(counts, torch.int32, cfg.E, "counts")),
+                                         ctypes.c_float(rate), ctypes.c_int32(int(bool(centered))),
+                                         _P(_ptr(expert_bias, torch.float32, cfg.E, "expert_bias")),
+                                         _P(_stream(stream))))
 
 
 def permute(cfg, x, idx, offsets, row_of, token_of, x_perm, ws, stream=None):
@@ -288,11 +312,12 @@ def permute_bwd(cfg, dX_perm, row_of, dx_s, dx_r, dx, stream=None):
                                   _P(_ptr(dx, torch.float32, cfg.T * cfg.d, "dx")), _P(_stream(stream))))
 
 
-def router_bwd(cfg, logits, idx, w, dw, counts, daux, dlogits, stream=None):
+def router_bwd(cfg, logits, idx, w, dw, counts, daux, dlogits, stream=None, seq_counts=None):
     A = cfg.T * cfg.k
     _check(load().moe_router_bwd(ctypes.byref(cfg), _P(_ptr(logits, torch.float32, cfg.T * cfg.E, "logits")),
                                  _P(_ptr(idx, torch.int32, A, "idx")), _P(_ptr(w, torch.float32, A, "w")),
                                  _P(_ptr(dw, torch.float32, A, "dw")), _P(_ptr(counts, torch.int32, cfg.E, "counts")),
+                                 _P(_ptr(seq_counts, torch.int32, num_sequences(cfg) * cfg.E, "seq_counts")),
                                  ctypes.c_float(daux), _P(_ptr(dlogits, torch.float32, cfg.T * cfg.E, "dlogits")),
                                  _P(_stream(stream))))
 
@@ -327,7 +352,8 @@ def _saved_struct(cfg, S: Dict[str, torch.Tensor]) -> Saved:
                 offsets=(torch.int32, E + 1), row_of=(torch.int32, A), token_of=(torch.int32, A),
                 x_perm=(qd, A * d), H=(torch.float32, A * 2 * F), Act=(qd, A * F), Y_perm=(torch.float32, A * d),
                 H_s=(torch.float32, T * 2 * Fs), Act_s=(ad, T * Fs), Y_s=(torch.float32, T * d),
-                x_perm_scale=(torch.float32, A * (d // 128)), Act_scale=(torch.float32, A * (F // 128)))
+                x_perm_scale=(torch.float32, A * (d // 128)), Act_scale=(torch.float32, A * (F // 128)),
+                seq_counts=(torch.int32, num_sequences(cfg) * E))
     return Saved(**{n: _ptr(S.get(n), dt, ne, n) for n, (dt, ne) in spec.items()})
 
 
@@ -371,6 +397,8 @@ def alloc_saved(cfg: Config, device="cuda") -> Dict[str, torch.Tensor]:
         S.update(x_perm_scale=e(A, d // 128, dt=torch.float32), Act_scale=e(A, F // 128, dt=torch.float32))
     if Fs:
         S.update(H_s=e(T, 2 * Fs, dt=torch.float32), Act_s=e(T, Fs), Y_s=e(T, d, dt=torch.float32))
+    if num_sequences(cfg):
+        S["seq_counts"] = e(num_sequences(cfg), E, dt=torch.int32)
     return S
 
 

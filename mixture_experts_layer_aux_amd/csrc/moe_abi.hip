@@ -1,6 +1,7 @@
 // The C ABI of libmoe: argument checks, workspace layout and the order of launches.
 // Every entry point validates all of its arguments on the host before it enqueues
 // anything, allocates nothing, and never synchronises the host.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -45,6 +46,10 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct FwdWs {
   int32_t* cnt_part;   // [nchunk, E] router chunk histograms == permute chunk histograms
   float* prob_part;    // [nchunk, E]
+  float* z_part;       // [nchunk]
+  float* pnorm;        // [T, 2] (sequence-wise loss only)
+  int32_t* seq_cnt_part;  // router_seq_part_elems
+  float* seq_prob_part;   // router_seq_part_elems
   int32_t* blk_base;   // [nchunk, E]
   int32_t* counts;     // [E]
   float* prob_sum;     // [E]
@@ -68,6 +73,11 @@ FwdWs carve_fwd(const moe_config_t& c, void* base) {
   FwdWs w;
   w.cnt_part = reinterpret_cast<int32_t*>(take(nch * c.E * 4));
   w.prob_part = reinterpret_cast<float*>(take(nch * c.E * 4));
+  w.z_part = reinterpret_cast<float*>(take(nch * 4));
+  const size_t nseq = router_seq_part_elems(c);
+  w.pnorm = nseq ? reinterpret_cast<float*>(take(static_cast<size_t>(c.T) * 8)) : nullptr;
+  w.seq_cnt_part = nseq ? reinterpret_cast<int32_t*>(take(nseq * 4)) : nullptr;
+  w.seq_prob_part = nseq ? reinterpret_cast<float*>(take(nseq * 4)) : nullptr;
   w.blk_base = reinterpret_cast<int32_t*>(take(nch * c.E * 4));
   w.counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(c.E) * 4));
   w.prob_sum = reinterpret_cast<float*>(take(static_cast<size_t>(c.E) * 4));
@@ -128,6 +138,17 @@ BwdWs carve_bwd(const moe_config_t& c, void* base) {
   return w;
 }
 
+RouterWs router_ws(const FwdWs& f) {
+  RouterWs r;
+  r.cnt_part = f.cnt_part;
+  r.prob_part = f.prob_part;
+  r.z_part = f.z_part;
+  r.pnorm = f.pnorm;
+  r.seq_cnt_part = f.seq_cnt_part;
+  r.seq_prob_part = f.seq_prob_part;
+  return r;
+}
+
 moe_status_t validate(const moe_config_t* c) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
   if (c->T < 1 || c->d < 1 || c->E < 1 || c->k < 1 || c->F < 1 || c->Fs < 0)
@@ -137,12 +158,20 @@ moe_status_t validate(const moe_config_t* c) {
   if (c->k > 32) return fail(MOE_ERR_UNSUPPORTED, "k=%d exceeds 32", c->k);
   if (c->E > 2048) return fail(MOE_ERR_UNSUPPORTED, "E=%d exceeds 2048", c->E);
   if (static_cast<int64_t>(c->T) * c->k >= (int64_t{1} << 31)) return fail(MOE_ERR_INVALID_ARG, "T*k >= 2^31");
-  if (c->score != MOE_SOFTMAX && c->score != MOE_SIGMOID) return fail(MOE_ERR_INVALID_ARG, "unknown score function");
-  if (c->pre_softmax != 0) return fail(MOE_ERR_UNSUPPORTED, "pre-softmax top-k is not provided");
-  if (c->score == MOE_SOFTMAX && c->k == 1)
+  if (c->score != MOE_SOFTMAX && c->score != MOE_SIGMOID && c->score != MOE_SQRTSOFTPLUS)
+    return fail(MOE_ERR_INVALID_ARG, "unknown score function");
+  if (c->pre_softmax != 0 && c->pre_softmax != 1) return fail(MOE_ERR_INVALID_ARG, "pre_softmax must be 0 or 1");
+  if (c->pre_softmax && c->score != MOE_SOFTMAX)
+    return fail(MOE_ERR_UNSUPPORTED, "pre-softmax top-k is a softmax setting");
+  if (c->score == MOE_SOFTMAX && c->k == 1 && !c->pre_softmax)
     return fail(MOE_ERR_UNSUPPORTED, "softmax over one selected logit has no gradient; top-1 needs pre-softmax");
-  if (c->aux_coeff != 0.0f && c->score != MOE_SOFTMAX)
-    return fail(MOE_ERR_UNSUPPORTED, "the aux loss is provided for softmax scores only");
+  if (!(c->aux_coeff >= 0.0f && c->aux_coeff < INFINITY) || !(c->z_coeff >= 0.0f && c->z_coeff < INFINITY) ||
+      !(c->seq_aux_coeff >= 0.0f && c->seq_aux_coeff < INFINITY))
+    return fail(MOE_ERR_INVALID_ARG, "loss coefficients must be finite and >= 0");
+  if (c->seq_aux_coeff != 0.0f && (c->seq_len < 1 || c->T % c->seq_len))
+    return fail(MOE_ERR_INVALID_ARG, "seq_len=%d must be >= 1 and divide T=%d", c->seq_len, c->T);
+  if (c->seq_aux_coeff != 0.0f && c->T / c->seq_len > 65535)
+    return fail(MOE_ERR_UNSUPPORTED, "more than 65535 sequences (T / seq_len) for the sequence-wise loss");
   if (!(c->routed_scaling > 0.0f)) return fail(MOE_ERR_INVALID_ARG, "routed_scaling must be > 0");
   if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown act dtype");
   if (c->w_dtype != 0 && c->w_dtype != MOE_FP8_E4M3) return fail(MOE_ERR_INVALID_ARG, "unknown weight dtype");
@@ -430,17 +459,26 @@ moe_status_t moe_gate_logits(const moe_config_t* cfg, const void* x, const float
 }
 
 moe_status_t moe_router_topk(const moe_config_t* cfg, const float* logits, const float* expert_bias, int32_t* idx,
-                             float* w, int32_t* counts, float* prob_sum, float* stats, void* ws, size_t ws_bytes,
-                             void* stream) {
+                             float* w, int32_t* counts, float* prob_sum, float* stats, int32_t* seq_counts, void* ws,
+                             size_t ws_bytes, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED(logits); MOE_NEED(idx); MOE_NEED(w); MOE_NEED(counts); MOE_NEED(ws);
-  if (expert_bias && cfg->score != MOE_SIGMOID)
-    return fail(MOE_ERR_UNSUPPORTED, "the expert bias is provided for sigmoid scores only");
+  if (cfg->seq_aux_coeff != 0.0f) MOE_NEED(seq_counts);
+  if (expert_bias && cfg->score == MOE_SOFTMAX)
+    return fail(MOE_ERR_UNSUPPORTED, "the expert bias is provided for sigmoid and sqrt(softplus) scores only");
   const FwdWs fw = carve_fwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
   float* ps = prob_sum ? prob_sum : fw.prob_sum;
-  return launch_router_topk(*cfg, logits, expert_bias, idx, w, counts, ps, stats, fw.cnt_part, fw.prob_part,
+  return launch_router_topk(*cfg, logits, expert_bias, idx, w, counts, ps, stats, seq_counts, router_ws(fw),
                             S(stream));
+}
+
+moe_status_t moe_expert_bias_update(const moe_config_t* cfg, const int32_t* counts, float rate, int32_t centered,
+                                    float* expert_bias, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED(counts); MOE_NEED(expert_bias);
+  if (!(rate > -INFINITY && rate < INFINITY)) return fail(MOE_ERR_INVALID_ARG, "rate must be finite");
+  return launch_bias_update(counts, cfg->E, rate, centered ? 1 : 0, expert_bias, S(stream));
 }
 
 moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* idx, int32_t* offsets,
@@ -497,15 +535,16 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   if (cfg->Fs) {
     MOE_NEED16(W->W13s); MOE_NEED16(W->W2s); MOE_NEED16(sv->H_s); MOE_NEED16(sv->Act_s); MOE_NEED16(sv->Y_s);
   }
-  if (W->expert_bias && cfg->score != MOE_SIGMOID)
-    return fail(MOE_ERR_UNSUPPORTED, "the expert bias is provided for sigmoid scores only");
+  if (W->expert_bias && cfg->score == MOE_SOFTMAX)
+    return fail(MOE_ERR_UNSUPPORTED, "the expert bias is provided for sigmoid and sqrt(softplus) scores only");
+  if (cfg->seq_aux_coeff != 0.0f) MOE_NEED(sv->seq_counts);
   const FwdWs fw = carve_fwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
   const moe_config_t& c = *cfg;
   hipStream_t s = S(stream);
   MOE_TRY(run_gate(c, x, W->Wg, W->bg, sv->logits, fw.gate, s));
   MOE_TRY(launch_router_topk(c, sv->logits, W->expert_bias, sv->idx, sv->w, sv->counts, fw.prob_sum, stats,
-                             fw.cnt_part, fw.prob_part, s));
+                             sv->seq_counts, router_ws(fw), s));
   if (fp8) {
     // x is quantised per token per 128 before the permute, so the permute moves e4m3 rows
     const int64_t A = static_cast<int64_t>(c.T) * c.k;
@@ -625,11 +664,14 @@ moe_status_t moe_permute_bwd(const moe_config_t* cfg, const float* dX_perm, cons
 }
 
 moe_status_t moe_router_bwd(const moe_config_t* cfg, const float* logits, const int32_t* idx, const float* w,
-                            const float* dw, const int32_t* counts, float daux, float* dlogits, void* stream) {
+                            const float* dw, const int32_t* counts, const int32_t* seq_counts, float daux,
+                            float* dlogits, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED(logits); MOE_NEED(idx); MOE_NEED(w); MOE_NEED(dw); MOE_NEED(dlogits);
+  if (!(daux > -INFINITY && daux < INFINITY)) return fail(MOE_ERR_INVALID_ARG, "daux must be finite");
   if (cfg->aux_coeff != 0.0f && daux != 0.0f) MOE_NEED(counts);
-  return launch_router_bwd(*cfg, logits, idx, w, dw, counts, daux, dlogits, S(stream));
+  if (cfg->seq_aux_coeff != 0.0f && daux != 0.0f) MOE_NEED(seq_counts);
+  return launch_router_bwd(*cfg, logits, idx, w, dw, counts, seq_counts, daux, dlogits, S(stream));
 }
 
 moe_status_t moe_gate_logits_bwd(const moe_config_t* cfg, const void* x, const float* Wg, const float* dlogits,
@@ -649,6 +691,8 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_NEED(W->Wg); MOE_NEED16(W->W13); MOE_NEED16(W->W2);
   MOE_NEED(sv->logits); MOE_NEED(sv->idx); MOE_NEED(sv->w); MOE_NEED(sv->counts); MOE_NEED(sv->offsets);
   MOE_NEED(sv->row_of); MOE_NEED16(sv->Y_perm); MOE_NEED(gr->dWg);
+  if (!(daux > -INFINITY && daux < INFINITY)) return fail(MOE_ERR_INVALID_ARG, "daux must be finite");
+  if (cfg->seq_aux_coeff != 0.0f && daux != 0.0f) MOE_NEED(sv->seq_counts);
   if (cfg->w_dtype == MOE_FP8_E4M3) {
     // frozen e4m3 experts: the backward runs through the mixing weights only
     if (gr->dW13 || gr->dW2 || gr->dW13s || gr->dW2s)
@@ -659,7 +703,7 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
     hipStream_t s = S(stream);
     MOE_TRY(launch_combine_bwd(c, dy, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, nullptr, bw.dw,
                                nullptr, s));
-    MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, daux, bw.dlogits, s));
+    MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, sv->seq_counts, daux, bw.dlogits, s));
     return run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, dx, bw.gate, s);
   }
   MOE_NEED16(sv->x_perm); MOE_NEED16(sv->H); MOE_NEED16(sv->Act); MOE_NEED16(gr->dW13); MOE_NEED16(gr->dW2);
@@ -681,7 +725,7 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_TRY(run_experts_bwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, sv->H, sv->Act, bw.dY, bw.dH, bw.dX, gr->dW13,
                           gr->dW2, x, W->W13s, W->W2s, sv->H_s, sv->Act_s, dY_s, bw.dH_s, bw.dx_s, gr->dW13s,
                           gr->dW2s, bw.sched, bw.dact, s, ss->s, ss->dh));
-  MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, daux, bw.dlogits, s));
+  MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, sv->seq_counts, daux, bw.dlogits, s));
   MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, bw.gate, s));
   MOE_TRY(launch_unpermute_reduce(c, bw.dX, sv->row_of, c.Fs ? static_cast<const float*>(bw.dx_s) : nullptr,
                                   bw.dx_r, dx, s));

@@ -10,11 +10,24 @@ inline int act_bytes(const moe_config_t& c) { return c.act_dtype == MOE_BF16 ? 2
 // ---------------------------------------------------------------- router
 int router_epl(int E);
 int64_t router_num_blocks(int T);  // == permute_num_chunks(T): both use 64-token chunks
+// Router scratch, carved from the caller's workspace.
+struct RouterWs {
+  int32_t* cnt_part;       // [nblk, E] block histograms (== the permute's chunk histograms)
+  float* prob_part;        // [nblk, E] block sums of the aux probabilities
+  float* z_part;           // [nblk]    block sums of logsumexp^2
+  float* pnorm;            // [T, 2]    per-token (m, 1/Z) of the aux probabilities
+  int32_t* seq_cnt_part;   // [B, ceil(S/64), E]
+  float* seq_prob_part;    // [B, ceil(S/64), E]
+};
+// elements of each per-sequence partial (0 when the sequence-wise loss is off)
+size_t router_seq_part_elems(const moe_config_t& c);
 moe_status_t launch_router_topk(const moe_config_t& c, const float* logits, const float* expert_bias,
                                 int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* stats,
-                                int32_t* cnt_part, float* prob_part, hipStream_t s);
+                                int32_t* seq_counts, const RouterWs& rw, hipStream_t s);
 moe_status_t launch_router_bwd(const moe_config_t& c, const float* logits, const int32_t* idx, const float* w,
-                               const float* dw, const int32_t* counts, float daux, float* dlogits, hipStream_t s);
+                               const float* dw, const int32_t* counts, const int32_t* seq_counts, float daux,
+                               float* dlogits, hipStream_t s);
+moe_status_t launch_bias_update(const int32_t* counts, int E, float rate, int centered, float* bias, hipStream_t s);
 
 // ---------------------------------------------------------------- permute / combine
 int64_t permute_num_chunks(int T);

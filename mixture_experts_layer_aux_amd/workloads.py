@@ -63,6 +63,10 @@ class LayerShape:
     skew_beta: float = 0.0      # hot-expert logit bias for bias == "skew"
     wq: str = ""                # "fp8": expert weights are given as fp32 masters, to be
                                 # quantised to e4m3 in 128 x 128 blocks by each side
+    pre_softmax: bool = False   # softmax only: top-k of the full softmax, no renormalisation
+    z_coeff: float = 0.0        # router z-loss coefficient
+    seq_aux_coeff: float = 0.0  # sequence-wise balance loss coefficient
+    seq_len: int = 0            # S of that loss (tokens ordered [S, B])
 
     @property
     def A(self) -> int:

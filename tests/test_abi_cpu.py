@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_declared_entry_point():
     lib = L.load()
     names = header_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     assert sorted(L.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -45,8 +45,13 @@ def test_valid_configs():
     (dict(k=33, E=64), L.MOE_ERR_UNSUPPORTED),
     (dict(E=4096), L.MOE_ERR_UNSUPPORTED),
     (dict(k=1), L.MOE_ERR_UNSUPPORTED),               # softmax top-1 needs pre-softmax
-    (dict(pre_softmax=1), L.MOE_ERR_UNSUPPORTED),
-    (dict(score=L.MOE_SIGMOID, aux_coeff=1e-3), L.MOE_ERR_UNSUPPORTED),
+    (dict(pre_softmax=2), L.MOE_ERR_INVALID_ARG),
+    (dict(score=L.MOE_SIGMOID, pre_softmax=1), L.MOE_ERR_UNSUPPORTED),   # pre-softmax is a softmax setting
+    (dict(score=3), L.MOE_ERR_INVALID_ARG),
+    (dict(z_coeff=-1e-3), L.MOE_ERR_INVALID_ARG),
+    (dict(aux_coeff=float("inf")), L.MOE_ERR_INVALID_ARG),
+    (dict(seq_aux_coeff=1e-4, seq_len=0), L.MOE_ERR_INVALID_ARG),        # the loss needs a sequence length
+    (dict(seq_aux_coeff=1e-4, seq_len=3000), L.MOE_ERR_INVALID_ARG),     # that divides T
     (dict(d=100), L.MOE_ERR_UNSUPPORTED),
     (dict(F=192), L.MOE_ERR_UNSUPPORTED),             # bf16 needs F % 128 == 0
     (dict(T=0), L.MOE_ERR_INVALID_ARG),
@@ -93,6 +98,44 @@ def test_quantize_fp8_rejects_bad_shapes_before_launching():
     assert st == L.MOE_ERR_INVALID_ARG and b"frozen" in lib.moe_last_error()
 
 
+def test_router_variants_and_balancing_losses_validate():
+    base = L.config_from_shape(W.LAYERS[2])
+    ok = [dict(k=1, pre_softmax=1), dict(pre_softmax=1), dict(score=L.MOE_SQRTSOFTPLUS),
+          dict(score=L.MOE_SIGMOID, aux_coeff=1e-3), dict(z_coeff=1e-3),
+          dict(seq_aux_coeff=1e-4, seq_len=2048), dict(seq_aux_coeff=1e-4, seq_len=1)]
+    for change in ok:
+        cfg = L.config_from_shape(W.LAYERS[2])
+        for k, v in change.items():
+            setattr(cfg, k, v)
+        assert _status(cfg) == L.MOE_OK, change
+    # the per-sequence partials are part of the forward workspace only when the loss is on
+    f0, _ = L.workspace_size(base)
+    cfg = L.config_from_shape(W.LAYERS[2], seq_aux_coeff=1e-4, seq_len=2048)
+    f1, _ = L.workspace_size(cfg)
+    assert f1 - f0 >= 2 * 4 * (8192 // 64) * 64 + 8 * 8192
+
+
+def test_bias_update_and_sequence_counts_are_checked_before_launching():
+    lib = L.load()
+    fake, nul, s = P(1 << 20), P(None), P(None)
+    cfg = L.config_from_shape(W.LAYERS[3])
+    st = lib.moe_expert_bias_update(ctypes.byref(cfg), fake, ctypes.c_float(float("nan")), ctypes.c_int32(0), fake, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"rate" in lib.moe_last_error()
+    st = lib.moe_expert_bias_update(ctypes.byref(cfg), nul, ctypes.c_float(1e-3), ctypes.c_int32(0), fake, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"counts" in lib.moe_last_error()
+    cq = L.config_from_shape(W.LAYERS[2], seq_aux_coeff=1e-4, seq_len=2048)
+    st = lib.moe_router_topk(ctypes.byref(cq), fake, nul, fake, fake, fake, nul, nul, nul, fake,
+                             ctypes.c_size_t(1 << 40), s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"seq_counts" in lib.moe_last_error()
+    st = lib.moe_router_bwd(ctypes.byref(cq), fake, fake, fake, fake, fake, nul, ctypes.c_float(1.0), fake, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"seq_counts" in lib.moe_last_error()
+    # a non-finite upstream gradient of the losses is refused
+    c0 = L.config_from_shape(W.LAYERS[1])
+    c0.seq_aux_coeff, c0.seq_len = 0.1, 64
+    assert lib.moe_router_bwd(ctypes.byref(c0), fake, fake, fake, fake, nul, nul, ctypes.c_float(float("nan")),
+                              fake, s) == L.MOE_ERR_INVALID_ARG
+
+
 def test_sigmoid_top1_is_allowed_and_fp32_f192_is_allowed():
     cfg = L.config_from_shape(replace(W.LAYERS[3], k=1))
     assert _status(cfg) == L.MOE_OK
@@ -126,10 +169,11 @@ def test_entry_points_reject_bad_arguments_before_launching():
     assert lib.moe_gate_logits(ctypes.byref(cfg), nul, fake, nul, fake, fake, ctypes.c_size_t(1 << 40), s) == L.MOE_ERR_INVALID_ARG
     assert b"x is NULL" in lib.moe_last_error()
     # workspace too small
-    st = lib.moe_router_topk(ctypes.byref(cfg), fake, nul, fake, fake, fake, nul, nul, fake, ctypes.c_size_t(8), s)
+    st = lib.moe_router_topk(ctypes.byref(cfg), fake, nul, fake, fake, fake, nul, nul, nul, fake, ctypes.c_size_t(8), s)
     assert st == L.MOE_ERR_WORKSPACE
     # expert bias with softmax scores
-    st = lib.moe_router_topk(ctypes.byref(cfg), fake, fake, fake, fake, fake, nul, nul, fake, ctypes.c_size_t(1 << 40), s)
+    st = lib.moe_router_topk(ctypes.byref(cfg), fake, fake, fake, fake, fake, nul, nul, nul, fake,
+                             ctypes.c_size_t(1 << 40), s)
     assert st == L.MOE_ERR_UNSUPPORTED
     # misaligned activation pointer
     st = lib.moe_permute(ctypes.byref(cfg), odd, fake, fake, fake, fake, fake, fake, ctypes.c_size_t(1 << 40), s)
@@ -146,7 +190,7 @@ def test_entry_points_reject_bad_arguments_before_launching():
     st = lib.moe_layer_fwd(ctypes.byref(cfg), ctypes.byref(w), fake, ctypes.byref(sv), fake, nul, fake,
                            ctypes.c_size_t(1 << 40), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"Wg" in lib.moe_last_error()
-    st = lib.moe_router_bwd(ctypes.byref(cfg), fake, fake, fake, fake, nul, ctypes.c_float(1.0), fake, s)
+    st = lib.moe_router_bwd(ctypes.byref(cfg), fake, fake, fake, fake, nul, nul, ctypes.c_float(1.0), fake, s)
     assert st == L.MOE_ERR_INVALID_ARG and b"counts" in lib.moe_last_error()
     # grouped weight gradient: group count, offsets and sizes are checked on the host
     i32, i64 = ctypes.c_int32, ctypes.c_int64
