@@ -242,6 +242,57 @@ def bench_fp8(args, shape, cfg, inp, up, dev) -> int:
     return 0
 
 
+# Sequence length of each layer's batch for the sequence-wise loss (tokens in [S, B] order):
+# 4 x 2048 for the small layer (as it is named), 4096-token sequences for the others.
+SEQ_LEN = {1: 32, 2: 2048, 3: 4096, 4: 4096, 5: 4096}
+
+
+def bench_balancing(args, shape, L, S, expert_bias, dw, dlogits, dev):
+    """The balancing step around the router, timed with HIP events on the launch stream:
+    the router with the sequence-wise loss (1e-4, DeepSeek-V3's value) and, for softmax
+    routers, the z-loss (1e-3, ST-MoE's value) on; its backward with those losses; and the
+    sign update of the expert bias (rate 1e-3) for the sigmoid and sqrt(softplus) routers."""
+    import torch
+    T, E, k = shape.T, shape.E, shape.k
+    cid = args.config
+    z = 1e-3 if shape.score == "softmax" else 0.0
+    cfg = L.config_from_shape(shape, z_coeff=z, seq_aux_coeff=1e-4, seq_len=SEQ_LEN[cid])
+    B = L.num_sequences(cfg)
+    sc = torch.empty(B, E, dtype=torch.int32, device=dev)
+    st = torch.empty(L.MOE_NSTATS, dtype=torch.float32, device=dev)
+    ws = torch.empty(L.workspace_size(cfg)[0], dtype=torch.uint8, device=dev)   # the router needs the forward part
+    bias = expert_bias.clone() if expert_bias is not None else None
+    runs = max(args.steps, 5)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(runs + 1)]
+        ev[0].record()
+        for i in range(runs):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(runs)]))
+
+    def fwd():
+        L.router_topk(cfg, S["logits"], expert_bias, S["idx"], S["w"], S["counts"], None, st, ws, seq_counts=sc)
+
+    out = dict(recipe=f"sequence-wise aux loss 1e-4 over {B} sequences of {SEQ_LEN[cid]} tokens"
+               + (", z-loss 1e-3" if z else ", sign update of the expert bias at rate 1e-3"),
+               router_ms=round(timed(fwd), 4))
+    out["router_bwd_ms"] = round(timed(lambda: L.router_bwd(cfg, S["logits"], S["idx"], S["w"], dw, S["counts"], 1.0,
+                                                           dlogits, seq_counts=sc)), 4)
+    if bias is not None:
+        out["bias_update_ms"] = round(timed(lambda: L.expert_bias_update(cfg, S["counts"], 1e-3, False, bias)), 4)
+    # bytes the sequence pass must move on top of the router's: the logits again, idx, and
+    # the per-token normalisers written and read
+    seq_bytes = T * E * 4 + T * k * 4 + 2 * T * 8
+    vals = st.cpu().numpy()
+    out.update(seq_pass_bytes=seq_bytes, z_loss=float(vals[4]), seq_aux_loss=float(vals[5]))
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -442,6 +493,7 @@ def main() -> int:
         load=dict(maxvio=round(float(st[1]), 4), empty_experts=int(st[2]), max_count=int(st[3]),
                   mean_count=T * k / E),
     )
+    out["balancing"] = bench_balancing(args, shape, L, S, Wt["expert_bias"], dw, dlogits, dev)
     if not args.no_cpu_baseline:
         tokens = args.cpu_tokens or {1: 128, 2: 8192, 3: 48, 4: 1024, 5: 256}[args.config]
         out["cpu_baseline"] = cpu_baseline(shape, inp, min(tokens, T))
