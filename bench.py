@@ -41,9 +41,10 @@ ROOFLINE_PHASE = "wgrad_fc1"
 GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_aux_amd", "csrc", "moe_gemm_mfma.hip")
 
 
-def algorithmic(shape):
+def algorithmic(shape, wgrad_bytes=4):
     """Algorithmic work per step: the bytes each HBM-bound kernel must move and the FLOP
-    each GEMM must compute, at minimum."""
+    each GEMM must compute, at minimum.  wgrad_bytes: bytes per expert weight-gradient
+    element (2 for bf16, 4 for fp32)."""
     T, d, E, k, F, Fs = shape.T, shape.d, shape.E, shape.k, shape.F, shape.Fs
     A = T * k
     eb = 2 if shape.act == "bf16" else 4
@@ -51,8 +52,8 @@ def algorithmic(shape):
     return dict(
         grouped_gemm_flop=3.0 * gemm_fwd,          # forward + data gradient + weight gradient
         wgrad_fc1_flop=2.0 * A * 2 * F * d,        # dW13 = dH^T x_perm over the routed rows
-        # dW13 written once in fp32, dH and x_perm read once, the offsets
-        wgrad_fc1_bytes=E * 2 * F * d * 4 + A * 2 * F * eb + A * d * eb + (E + 1) * 4,
+        # dW13 written once, dH and x_perm read once, the offsets
+        wgrad_fc1_bytes=E * 2 * F * d * wgrad_bytes + A * 2 * F * eb + A * d * eb + (E + 1) * 4,
         gate_flop=6.0 * T * E * d,                 # logits, dWg, dx_r
         # bytes each HBM-bound phase must move at least once
         router_bytes=T * E * 4 + T * k * 8 + E * 8,
@@ -84,7 +85,7 @@ def measured_traffic(shape):
     return int(fields["traffic_bytes_per_launch"])
 
 
-def roofline(alg, ms, peak_tflops, shape):
+def roofline(alg, ms, peak_tflops, shape, wgrad_name="fp32"):
     """Roofline of one launch of the routed fc1 weight-gradient kernel: the bound is the
     resource whose peak gives the longer time for its algorithmic work."""
     flop, nbytes = alg["wgrad_fc1_flop"], alg["wgrad_fc1_bytes"]
@@ -92,7 +93,8 @@ def roofline(alg, ms, peak_tflops, shape):
     t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
     s = ms * 1e-3
     common = dict(kernel="routed fc1 weight gradient dW13 = dH^T x_perm (one grouped-GEMM launch, bf16 MFMA, "
-                         "fp32 output)", launch_ms=round(ms, 4), flop_per_launch=flop, bytes_per_launch=int(nbytes),
+                         f"{wgrad_name} output)", launch_ms=round(ms, 4), flop_per_launch=flop,
+                  bytes_per_launch=int(nbytes),
                   mfma_frac=round(flop / s / 1e12 / peak_tflops, 4), hbm_frac=round(nbytes / s / 1e9 / PEAK_HBM_GBPS, 4))
     if t_hbm >= t_mfma:
         gbps = nbytes / s / 1e9
@@ -242,6 +244,36 @@ def bench_fp8(args, shape, cfg, inp, up, dev) -> int:
     return 0
 
 
+def bench_wgrad_f32(args, shape, L, S, dY_perm, dH, dev, phase_ms):
+    """The two routed weight-gradient launches again with fp32 output (the other option of
+    the weight-gradient dtype), timed with HIP events on the launch stream, beside the
+    step's bf16 ones."""
+    import torch
+    T, d, E, k, F = shape.T, shape.d, shape.E, shape.k, shape.F
+    A = T * k
+    c32 = L.config_from_shape(shape, wgrad="f32")
+    dW13 = torch.empty(E, 2 * F, d, dtype=torch.float32, device=dev)
+    dW2 = torch.empty(E, d, F, dtype=torch.float32, device=dev)
+    runs = max(args.steps // 2, 3)
+    res = {}
+    for name, fn in (("wgrad_fc1", lambda: L.grouped_wgrad(c32, S["offsets"], E, A, dH, 2 * F, S["x_perm"], d, dW13)),
+                     ("wgrad_fc2", lambda: L.grouped_wgrad(c32, S["offsets"], E, A, dY_perm, d, S["Act"], F, dW2))):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(runs + 1)]
+        ev[0].record()
+        for i in range(runs):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        res[name + "_ms"] = round(float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(runs)])), 4)
+    del dW13, dW2
+    res["step_ms_estimate"] = round(sum(phase_ms.values()) - phase_ms["wgrad_fc1"] - phase_ms["wgrad_fc2"]
+                                    + res["wgrad_fc1_ms"] + res["wgrad_fc2_ms"], 3)
+    res["note"] = ("fp32 output of the routed weight gradients (bench.py --wgrad f32 times the whole step that way); "
+                   "the shared expert's two launches are small and not repeated")
+    return res
+
+
 # Sequence length of each layer's batch for the sequence-wise loss (tokens in [S, B] order):
 # 4 x 2048 for the small layer (as it is named), 4096-token sequences for the others.
 SEQ_LEN = {1: 32, 2: 2048, 3: 4096, 4: 4096, 5: 4096}
@@ -300,6 +332,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--wgrad", choices=["default", "f32"], default="default",
+                    help="dtype of the expert weight gradients: the activation dtype (default) or fp32")
     ap.add_argument("--entry-points", action="store_true",
                     help="also time the layer through moe_layer_fwd + moe_layer_bwd (reported beside value)")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0 = by layer)")
@@ -331,7 +365,7 @@ def main() -> int:
         B.build()
     L.load()
     shape = W.LAYERS[args.config]
-    cfg = L.config_from_shape(shape)
+    cfg = L.config_from_shape(shape, **({"wgrad": "f32"} if args.wgrad == "f32" else {}))
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
     inp = W.make_inputs(shape, seed=args.config)
@@ -448,11 +482,12 @@ def main() -> int:
         torch.cuda.synchronize()
         layer_ms = (time.perf_counter() - t1) * 1e3 / args.steps
 
-    alg = algorithmic(shape)
+    wbf16 = cfg.wgrad_dtype == L.MOE_BF16
+    alg = algorithmic(shape, 2 if wbf16 else 4)
     gemm_ms = sum(phase_ms[p] for p in GEMM_PHASES)
     gemm_tflops = alg["grouped_gemm_flop"] / (gemm_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if shape.act == "bf16" else PEAK_FP32_TFLOPS
-    roof = roofline(alg, phase_ms[ROOFLINE_PHASE], peak, shape)
+    roof = roofline(alg, phase_ms[ROOFLINE_PHASE], peak, shape, "bf16" if wbf16 else "fp32")
 
     def hbm(p, key):
         gbps = alg[key] / (phase_ms[p] * 1e-3) / 1e9
@@ -474,7 +509,8 @@ def main() -> int:
         dtype="bf16" if shape.act == "bf16" else "f32",
         data="synthetic (seeded generator, random-init weights)",
         config=dict(workload=shape.name, T=T, d=d, E=E, k=k, F=F, Fs=Fs, score=shape.score,
-                    bias=shape.bias, aux_coeff=shape.aux_coeff, parallelism="single GPU"),
+                    bias=shape.bias, aux_coeff=shape.aux_coeff, wgrad_dtype="bf16" if wbf16 else "f32",
+                    parallelism="single GPU"),
         roofline=roof,
         grouped_gemm=dict(kernels="every expert projection of fwd + bwd (routed and shared)",
                           flop_per_step=alg["grouped_gemm_flop"], ms_per_step=round(gemm_ms, 3),
@@ -494,6 +530,8 @@ def main() -> int:
                   mean_count=T * k / E),
     )
     out["balancing"] = bench_balancing(args, shape, L, S, Wt["expert_bias"], dw, dlogits, dev)
+    if wbf16:
+        out["wgrad_f32"] = bench_wgrad_f32(args, shape, L, S, dY_perm, dH, dev, phase_ms)
     if not args.no_cpu_baseline:
         tokens = args.cpu_tokens or {1: 128, 2: 8192, 3: 48, 4: 1024, 5: 256}[args.config]
         out["cpu_baseline"] = cpu_baseline(shape, inp, min(tokens, T))

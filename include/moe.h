@@ -28,7 +28,7 @@
  *   H [A, 2F] fp32, Act [A, F] act dtype   fc1 output (gate half, then up half), SwiGLU
  *   Y_perm [A, d], Y_s [T, d]         fp32 expert outputs (same row order as x_perm)
  *   dX_perm [A, d]                    fp32 per-row input gradients
- *   dW13, dW2, dW13s, dW2s            fp32 weight gradients, shaped like the weights
+ *   dW13, dW2, dW13s, dW2s            weight gradients, shaped like the weights, in wgrad_dtype
  *
  * fp8 experts (w_dtype == MOE_FP8_E4M3): W13 and W2 hold e4m3 codes (one byte each)
  * with one fp32 scale per 128 x 128 block; x_perm and Act hold e4m3 codes with one scale
@@ -38,8 +38,10 @@
  * Precision: every GEMM multiplies act-dtype operands (bf16 on the matrix cores) with
  * fp32 accumulation.  Only GEMM operands are stored in bf16 (x_perm, Act, dY_perm, dH);
  * everything that is summed or differentiated further (H, expert outputs, per-row input
- * gradients, y, dx, weight gradients) stays fp32: one bf16 rounding of a value five to six
- * standard deviations out is already 2e-2 of the tensor's RMS.
+ * gradients, y, dx, router weight gradients) stays fp32: one bf16 rounding of a value five
+ * to six standard deviations out is already 2e-2 of the tensor's RMS.  The expert weight
+ * gradients are stored in wgrad_dtype: fp32, or bf16 (each element rounded once, to
+ * nearest even, from its fp32 accumulator), like the bf16 weights they belong to.
  *
  * Errors: every argument is checked on the host before anything is launched.  A call
  * that fails a check launches nothing and returns MOE_ERR_INVALID_ARG,
@@ -106,6 +108,8 @@ typedef struct moe_config {
   float seq_aux_coeff;    /* sequence-wise aux-loss coefficient ([HB] §3.3 Scope); 0 = off */
   int32_t seq_len;        /* S of the sequence-wise loss: tokens are ordered [S, B], token
                              t = s * B + b is position s of sequence b, B = T / S */
+  int32_t wgrad_dtype;    /* moe_dtype_t of the expert weight gradients: MOE_F32 (0), or
+                             MOE_BF16 with bf16 activations (INVALID_ARG / UNSUPPORTED otherwise) */
 } moe_config_t;
 
 typedef struct moe_weights {
@@ -145,10 +149,10 @@ typedef struct moe_saved {
 typedef struct moe_grads {
   float* dWg;  /* [E, d] fp32 */
   float* dbg;  /* [E] fp32, or NULL */
-  float* dW13;  /* [E, 2F, d]; experts with no rows get exact zeros */
-  float* dW2;   /* [E, d, F] */
-  float* dW13s; /* [2Fs, d] or NULL when Fs == 0 */
-  float* dW2s;  /* [d, Fs]  or NULL */
+  void* dW13;   /* [E, 2F, d] in wgrad_dtype; experts with no rows get exact zeros */
+  void* dW2;    /* [E, d, F] */
+  void* dW13s;  /* [2Fs, d] or NULL when Fs == 0 */
+  void* dW2s;   /* [d, Fs]  or NULL */
 } moe_grads_t;
 
 const char* moe_status_string(moe_status_t status);
@@ -262,8 +266,8 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
 
 /* Grouped weight gradient (the expert weight gradients of [HB] §3.4's FFN, by the chain
  * rule): for each group g over its rows [offsets[g], offsets[g+1]),
- *   dW[g] = dY_g^T X_g,   fp32 accumulation, fp32 output (overwritten).
- * dY [rows, N] and X [rows, K] in the act dtype, row-major; dW [groups, N, K] fp32.
+ *   dW[g] = dY_g^T X_g,   fp32 accumulation, output in cfg->wgrad_dtype (overwritten).
+ * dY [rows, N] and X [rows, K] in the act dtype, row-major; dW [groups, N, K].
  * The routed experts: (dH, x_perm) -> dW13 with N = 2F, K = d, and (dY_perm, Act) -> dW2
  * with N = d, K = F.  offsets NULL: one group over rows [0, rows) (the shared expert, on
  * all T tokens).  A group with no rows gets exact zeros.  offsets[groups] <= rows is the
@@ -271,7 +275,7 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
  * Errors: groups outside [1, 4096], groups != 1 without offsets, rows outside [0, 2^31),
  * N or K not a positive multiple of 64 -> MOE_ERR_INVALID_ARG. */
 moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, int32_t groups, int64_t rows,
-                               const void* dY, int32_t N, const void* X, int32_t K, float* dW, void* stream);
+                               const void* dY, int32_t N, const void* X, int32_t K, void* dW, void* stream);
 
 /* ---------------------------------------------------------------- fp8 experts
  * e4m3 block quantiser (the fp8 recipe is a reading: the pages leave low-precision expert

@@ -43,7 +43,7 @@ class Config(ctypes.Structure):
                 ("F", ctypes.c_int32), ("Fs", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("pre_softmax", ctypes.c_int32), ("routed_scaling", ctypes.c_float), ("aux_coeff", ctypes.c_float),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("z_coeff", ctypes.c_float),
-                ("seq_aux_coeff", ctypes.c_float), ("seq_len", ctypes.c_int32)]
+                ("seq_aux_coeff", ctypes.c_float), ("seq_len", ctypes.c_int32), ("wgrad_dtype", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -91,12 +91,14 @@ def _check(status: int) -> None:
 
 
 def make_config(T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux_coeff=0.0, act="bf16", wq="",
-                pre_softmax=False, z_coeff=0.0, seq_aux_coeff=0.0, seq_len=0) -> Config:
-    """wq: "" (expert weights in the activation dtype) or "fp8" (e4m3 codes + block scales)."""
+                pre_softmax=False, z_coeff=0.0, seq_aux_coeff=0.0, seq_len=0, wgrad=None) -> Config:
+    """wq: "" (expert weights in the activation dtype) or "fp8" (e4m3 codes + block scales).
+    wgrad: dtype of the expert weight gradients, "bf16" or "f32"; None = the activation dtype."""
+    wgrad = act if wgrad is None else wgrad
     return Config(T=T, d=d, E=E, k=k, F=F, Fs=Fs, score=_SCORES[score], pre_softmax=int(bool(pre_softmax)),
                   routed_scaling=scaling, aux_coeff=aux_coeff, act_dtype=MOE_BF16 if act == "bf16" else MOE_F32,
                   w_dtype=MOE_FP8_E4M3 if wq == "fp8" else 0, z_coeff=z_coeff, seq_aux_coeff=seq_aux_coeff,
-                  seq_len=seq_len)
+                  seq_len=seq_len, wgrad_dtype=MOE_BF16 if wgrad == "bf16" else MOE_F32)
 
 
 def config_from_shape(s, **extra) -> Config:
@@ -118,6 +120,11 @@ def is_fp8(cfg: Config) -> bool:
 
 def act_dtype(cfg: Config) -> torch.dtype:
     return torch.bfloat16 if cfg.act_dtype == MOE_BF16 else torch.float32
+
+
+def wgrad_dtype(cfg: Config) -> torch.dtype:
+    """torch dtype of the expert weight gradients."""
+    return torch.bfloat16 if cfg.wgrad_dtype == MOE_BF16 else torch.float32
 
 
 def validate(cfg: Config) -> None:
@@ -243,13 +250,14 @@ def grouped_gemm_swiglu_bwd(cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, 
         _P(_ptr(W13, ad, E * 2 * F * d, "W13")), _P(_ptr(W2, ad, E * d * F, "W2")),
         _P(_ptr(H, torch.float32, A * 2 * F, "H")),
         _P(_ptr(Act, ad, A * F, "Act")), _P(_ptr(dY_perm, ad, A * d, "dY_perm")), _P(_ptr(dH, ad, A * 2 * F, "dH")),
-        _P(_ptr(dX_perm, torch.float32, A * d, "dX_perm")), _P(_ptr(dW13, torch.float32, E * 2 * F * d, "dW13")),
-        _P(_ptr(dW2, torch.float32, E * d * F, "dW2")), _P(_ptr(x, ad, T * d, "x")),
+        _P(_ptr(dX_perm, torch.float32, A * d, "dX_perm")), _P(_ptr(dW13, wgrad_dtype(cfg), E * 2 * F * d, "dW13")),
+        _P(_ptr(dW2, wgrad_dtype(cfg), E * d * F, "dW2")), _P(_ptr(x, ad, T * d, "x")),
         _P(_ptr(W13s, ad, 2 * Fs * d, "W13s")),
         _P(_ptr(W2s, ad, d * Fs, "W2s")), _P(_ptr(H_s, torch.float32, T * 2 * Fs, "H_s")),
         _P(_ptr(Act_s, ad, T * Fs, "Act_s")),
         _P(_ptr(dY_s, ad, T * d, "dY_s")), _P(_ptr(dH_s, ad, T * 2 * Fs, "dH_s")), _P(_ptr(dx_s, torch.float32, T * d, "dx_s")),
-        _P(_ptr(dW13s, torch.float32, 2 * Fs * d, "dW13s")), _P(_ptr(dW2s, torch.float32, d * Fs, "dW2s")), _P(wp),
+        _P(_ptr(dW13s, wgrad_dtype(cfg), 2 * Fs * d, "dW13s")), _P(_ptr(dW2s, wgrad_dtype(cfg), d * Fs, "dW2s")),
+        _P(wp),
         ctypes.c_size_t(wn),
         _P(_stream(stream))))
 
@@ -262,7 +270,7 @@ def grouped_wgrad(cfg, offsets, groups, rows, dY, N, X, K, dW, stream=None):
     _check(load().moe_grouped_wgrad(
         ctypes.byref(cfg), _P(_ptr(offsets, torch.int32, groups + 1, "offsets")), ctypes.c_int32(groups),
         ctypes.c_int64(rows), _P(_ptr(dY, ad, rows * N, "dY")), ctypes.c_int32(N), _P(_ptr(X, ad, rows * K, "X")),
-        ctypes.c_int32(K), _P(_ptr(dW, torch.float32, groups * N * K, "dW")), _P(_stream(stream))))
+        ctypes.c_int32(K), _P(_ptr(dW, wgrad_dtype(cfg), groups * N * K, "dW")), _P(_stream(stream))))
 
 
 def quantize_fp8(src, block_rows, q, scale, stream=None):
@@ -374,9 +382,10 @@ def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None):
     ws_ = _weights_struct(cfg, W)
     ss = _saved_struct(cfg, S)
     f32 = torch.float32
+    wd = wgrad_dtype(cfg)
     gs = Grads(dWg=_ptr(G["dWg"], f32, E * d, "dWg"), dbg=_ptr(G.get("dbg"), f32, E, "dbg"),
-               dW13=_ptr(G.get("dW13"), f32, E * 2 * F * d, "dW13"), dW2=_ptr(G.get("dW2"), f32, E * d * F, "dW2"),
-               dW13s=_ptr(G.get("dW13s"), f32, 2 * Fs * d, "dW13s"), dW2s=_ptr(G.get("dW2s"), f32, d * Fs, "dW2s"))
+               dW13=_ptr(G.get("dW13"), wd, E * 2 * F * d, "dW13"), dW2=_ptr(G.get("dW2"), wd, E * d * F, "dW2"),
+               dW13s=_ptr(G.get("dW13s"), wd, 2 * Fs * d, "dW13s"), dW2s=_ptr(G.get("dW2s"), wd, d * Fs, "dW2s"))
     _check(load().moe_layer_bwd(ctypes.byref(cfg), ctypes.byref(ws_), ctypes.byref(ss),
                                 _P(_ptr(x, ad, cfg.T * d, "x")), _P(_ptr(dy, f32, cfg.T * d, "dy")),
                                 ctypes.c_float(daux), _P(_ptr(dx, f32, cfg.T * d, "dx")), ctypes.byref(gs), _P(wp),
@@ -403,15 +412,15 @@ def alloc_saved(cfg: Config, device="cuda") -> Dict[str, torch.Tensor]:
 
 
 def alloc_grads(cfg: Config, device="cuda", with_dbg=False) -> Dict[str, torch.Tensor]:
-    d, E, F, Fs, f32 = cfg.d, cfg.E, cfg.F, cfg.Fs, torch.float32
+    d, E, F, Fs, f32, wd = cfg.d, cfg.E, cfg.F, cfg.Fs, torch.float32, wgrad_dtype(cfg)
     G = dict(dWg=torch.empty(E, d, dtype=f32, device=device))
     if not is_fp8(cfg):   # fp8 experts are frozen: no expert weight gradients
-        G.update(dW13=torch.empty(E, 2 * F, d, dtype=f32, device=device),
-                 dW2=torch.empty(E, d, F, dtype=f32, device=device))
+        G.update(dW13=torch.empty(E, 2 * F, d, dtype=wd, device=device),
+                 dW2=torch.empty(E, d, F, dtype=wd, device=device))
     if with_dbg:
         G["dbg"] = torch.empty(E, dtype=f32, device=device)
     if Fs:
-        G.update(dW13s=torch.empty(2 * Fs, d, dtype=f32, device=device), dW2s=torch.empty(d, Fs, dtype=f32, device=device))
+        G.update(dW13s=torch.empty(2 * Fs, d, dtype=wd, device=device), dW2s=torch.empty(d, Fs, dtype=wd, device=device))
     return G
 
 

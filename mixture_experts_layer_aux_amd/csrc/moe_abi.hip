@@ -174,6 +174,10 @@ moe_status_t validate(const moe_config_t* c) {
     return fail(MOE_ERR_UNSUPPORTED, "more than 65535 sequences (T / seq_len) for the sequence-wise loss");
   if (!(c->routed_scaling > 0.0f)) return fail(MOE_ERR_INVALID_ARG, "routed_scaling must be > 0");
   if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown act dtype");
+  if (c->wgrad_dtype != MOE_F32 && c->wgrad_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown weight-gradient dtype");
+  if (c->wgrad_dtype == MOE_BF16 && c->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "bf16 weight gradients need bf16 activations");
   if (c->w_dtype != 0 && c->w_dtype != MOE_FP8_E4M3) return fail(MOE_ERR_INVALID_ARG, "unknown weight dtype");
   if (c->w_dtype == MOE_FP8_E4M3) {
     if (c->act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "fp8 experts need bf16 activations");
@@ -302,13 +306,14 @@ moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const in
   return MOE_OK;
 }
 
-// dW[g] = dY_g^T X_g over the rows of each group (reduction-ragged); fp32 output.
-moe_status_t run_wgrad(int act_dtype, const int32_t* off, int G, int64_t rows, const void* dY, int N, const void* X,
-                       int K, void* dW, hipStream_t s) {
+// dW[g] = dY_g^T X_g over the rows of each group (reduction-ragged); fp32 accumulation,
+// output in the weight-gradient dtype.
+moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G, int64_t rows, const void* dY, int N,
+                       const void* X, int K, void* dW, hipStream_t s) {
   GemmDesc w{};
   w.a_major = MN_MAJOR; w.b_major = MN_MAJOR; w.ragged = RAGGED_K; w.epi = EPI_STORE;
   w.a_type = w.b_type = act_dtype;
-  w.c_type = MOE_F32;
+  w.c_type = wgrad_dtype;
   w.M = N; w.N = K;
   w.A = dY; w.lda = N; w.B = X; w.ldb = K;
   w.C = dW; w.ldc = K; w.c_gstride = int64_t{1} * N * K;
@@ -384,11 +389,11 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
       MOE_TRY(launch_swiglu_bwd_elementwise(static_cast<const float*>(h), dact, static_cast<float*>(dh), rows, F, s));
     }
     // (2) fc2 weight gradient dW2 = dY^T Act, queued before dX may overwrite an aliased dY
-    if (dw2) MOE_TRY(run_wgrad(et, off, G, rows, dY, c.d, act, F, dw2, s2));
+    if (dw2) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dY, c.d, act, F, dw2, s2));
     MOE_TRY(fork(s, ev_dh, s2));  // dH ready for the fc1 weight gradient
     MOE_TRY(et == MOE_BF16 ? launch_gemm_mfma(d1, sched, s) : launch_gemm_fma(d1, s));
     // (4) fc1 weight gradient dW13 = dH^T X
-    if (dw13) MOE_TRY(run_wgrad(et, off, G, rows, dh, 2 * F, X, c.d, dw13, s2));
+    if (dw13) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dh, 2 * F, X, c.d, dw13, s2));
   }
   return MOE_OK;
 }
@@ -601,7 +606,7 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
 }
 
 moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, int32_t groups, int64_t rows,
-                               const void* dY, int32_t N, const void* X, int32_t K, float* dW, void* stream) {
+                               const void* dY, int32_t N, const void* X, int32_t K, void* dW, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED16(dY); MOE_NEED16(X); MOE_NEED16(dW);
   if (groups < 1 || groups > 4096) return fail(MOE_ERR_INVALID_ARG, "groups must be in [1, 4096]");
@@ -609,7 +614,7 @@ moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, 
   if (rows < 0 || rows >= (int64_t{1} << 31)) return fail(MOE_ERR_INVALID_ARG, "rows must be in [0, 2^31)");
   if (N < 64 || K < 64 || N % 64 || K % 64) return fail(MOE_ERR_INVALID_ARG, "N and K must be positive multiples of 64");
   if (static_cast<int64_t>(N) * K * 4 >= (int64_t{1} << 40)) return fail(MOE_ERR_INVALID_ARG, "dW group too large");
-  return run_wgrad(cfg->act_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream));
+  return run_wgrad(cfg->act_dtype, cfg->wgrad_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream));
 }
 
 moe_status_t moe_quantize_fp8(int32_t src_dtype, const void* src, int64_t rows, int32_t cols, int32_t block_rows,

@@ -551,6 +551,7 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
   MOE_MF(K_MAJOR, MN_MAJOR, RAGGED_M, EPI_SWIGLU_BWD, false)  // fc2 data gradient + SwiGLU backward -> dH (bf16)
   MOE_MF(K_MAJOR, MN_MAJOR, RAGGED_M, EPI_STORE, true)        // fc1 data gradient -> dX (fp32)
   MOE_MF(MN_MAJOR, MN_MAJOR, RAGGED_K, EPI_STORE, true)       // weight gradients (fp32)
+  MOE_MF(MN_MAJOR, MN_MAJOR, RAGGED_K, EPI_STORE, false)      // weight gradients (bf16, rounded once from fp32)
 #undef MOE_MF
   return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: unsupported operand combination");
 }

@@ -52,6 +52,8 @@ def test_valid_configs():
     (dict(aux_coeff=float("inf")), L.MOE_ERR_INVALID_ARG),
     (dict(seq_aux_coeff=1e-4, seq_len=0), L.MOE_ERR_INVALID_ARG),        # the loss needs a sequence length
     (dict(seq_aux_coeff=1e-4, seq_len=3000), L.MOE_ERR_INVALID_ARG),     # that divides T
+    (dict(wgrad_dtype=7), L.MOE_ERR_INVALID_ARG),
+    (dict(wgrad_dtype=L.MOE_BF16, act_dtype=L.MOE_F32), L.MOE_ERR_UNSUPPORTED),  # bf16 gradients need bf16 x
     (dict(d=100), L.MOE_ERR_UNSUPPORTED),
     (dict(F=192), L.MOE_ERR_UNSUPPORTED),             # bf16 needs F % 128 == 0
     (dict(T=0), L.MOE_ERR_INVALID_ARG),
@@ -134,6 +136,13 @@ def test_bias_update_and_sequence_counts_are_checked_before_launching():
     c0.seq_aux_coeff, c0.seq_len = 0.1, 64
     assert lib.moe_router_bwd(ctypes.byref(c0), fake, fake, fake, fake, nul, nul, ctypes.c_float(float("nan")),
                               fake, s) == L.MOE_ERR_INVALID_ARG
+
+
+def test_weight_gradient_dtype_defaults_to_the_activation_dtype():
+    assert L.config_from_shape(W.LAYERS[3]).wgrad_dtype == L.MOE_BF16
+    assert L.config_from_shape(W.LAYERS[1]).wgrad_dtype == L.MOE_F32
+    c = L.config_from_shape(W.LAYERS[3], wgrad="f32")
+    assert c.wgrad_dtype == L.MOE_F32 and _status(c) == L.MOE_OK
 
 
 def test_sigmoid_top1_is_allowed_and_fp32_f192_is_allowed():

@@ -16,10 +16,10 @@ from helpers import (MARGIN, O, W, check_expert_grads, check_grad, dev, oracle_i
 pytestmark = pytest.mark.gpu
 
 
-def _run_layer(shape, inp):
+def _run_layer(shape, inp, **cfg_extra):
     torch = torch_mod()
     from mixture_experts_layer_aux_amd import _lib as L
-    cfg = L.config_from_shape(shape)
+    cfg = L.config_from_shape(shape, **cfg_extra)
     d = dev()
     Wt = dict(Wg=to_dev(inp["Wg"]), bg=to_dev(inp["bg"]), expert_bias=to_dev(inp["expert_bias"]),
               W13=to_dev(inp["W13"]), W2=to_dev(inp["W2"]), W13s=to_dev(inp["W13s"]), W2s=to_dev(inp["W2s"]))
@@ -37,9 +37,9 @@ def _run_layer(shape, inp):
     return dict(y=y, dx=dx, stats=stats, **{f"S_{k}": v for k, v in S.items()}, **G)
 
 
-def _check_layer(shape, seed):
+def _check_layer(shape, seed, **cfg_extra):
     inp = W.make_inputs(shape, seed=seed)
-    got = _run_layer(shape, inp)
+    got = _run_layer(shape, inp, **cfg_extra)
     o = oracle_inputs(inp, shape)
     spec = spec_of(shape)
     f = O.layer_forward(o["x"], o["Wg"], o["W13"], o["W2"], spec, bg=o["bg"], expert_bias=o["expert_bias"],
@@ -91,6 +91,12 @@ def test_layer_determinism():
     b = _run_layer(shape, inp)
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+def test_layer_fp32_weight_gradients():
+    """The fp32 weight-gradient option of a bf16 layer (the default is bf16)."""
+    got = _check_layer(W.SMALL[3], seed=3, wgrad="f32")
+    assert got["dW13"].dtype == torch_mod().float32
 
 
 @pytest.mark.parametrize("variant", ["scaling", "no_shared_sigmoid", "k_equals_E", "one_row_experts"])

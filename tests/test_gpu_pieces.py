@@ -133,6 +133,7 @@ def test_grouped_experts_forward_and_backward(cid):
     W13s, W2s = to_dev(inp["W13s"]), to_dev(inp["W2s"])
     e = lambda *s: torch.empty(*s, dtype=ad, device=dev())  # noqa: E731
     e32 = lambda *s: torch.empty(*s, dtype=torch.float32, device=dev())  # noqa: E731
+    ew = lambda *s: torch.empty(*s, dtype=L.wgrad_dtype(cfg), device=dev())  # noqa: E731
     H, Act, Yp = e32(A, 2 * F), e(A, F), e32(A, d)
     H_s, Act_s, Y_s = (e32(T, 2 * Fs), e(T, Fs), e32(T, d)) if Fs else (None, None, None)
     ws = L.alloc_workspace(cfg, dev())
@@ -141,10 +142,10 @@ def test_grouped_experts_forward_and_backward(cid):
     dYp_np = W.random_rows(A, d, seed=100 + cid, act=shape.act)
     dYp = to_dev(dYp_np)
     dH, dXp = e(A, 2 * F), e32(A, d)
-    dW13, dW2 = e32(E, 2 * F, d), e32(E, d, F)
+    dW13, dW2 = ew(E, 2 * F, d), ew(E, d, F)
     dy = to_dev(inp["dy"])                       # the shared expert's upstream gradient, act dtype
     dH_s, dx_s = (e(T, 2 * Fs), e32(T, d)) if Fs else (None, None)
-    dW13s, dW2s = (e32(2 * Fs, d), e32(d, Fs)) if Fs else (None, None)
+    dW13s, dW2s = (ew(2 * Fs, d), ew(d, Fs)) if Fs else (None, None)
     L.grouped_gemm_swiglu_bwd(cfg, x_perm, off, W13, W2, H, Act, dYp, dH, dXp, dW13, dW2, x if Fs else None, W13s,
                               W2s, H_s, Act_s, dy if Fs else None, dH_s, dx_s, dW13s, dW2s, ws)
     # the same backward as data gradients only, then the four weight gradients through
@@ -153,15 +154,30 @@ def test_grouped_experts_forward_and_backward(cid):
     dH2_s, dx2_s = (e(T, 2 * Fs), e32(T, d)) if Fs else (None, None)
     L.grouped_gemm_swiglu_bwd(cfg, x_perm, off, W13, W2, H, Act, dYp, dH2, dXp2, None, None, x if Fs else None, W13s,
                               W2s, H_s, Act_s, dy if Fs else None, dH2_s, dx2_s, None, None, ws)
-    sW13, sW2 = e32(E, 2 * F, d), e32(E, d, F)
+    sW13, sW2 = ew(E, 2 * F, d), ew(E, d, F)
     L.grouped_wgrad(cfg, off, E, A, dH2, 2 * F, x_perm, d, sW13)
     L.grouped_wgrad(cfg, off, E, A, dYp, d, Act, F, sW2)
     split = [(dH, dH2), (dXp, dXp2), (dW13, sW13), (dW2, sW2)]
     if Fs:
-        sW13s, sW2s = e32(2 * Fs, d), e32(d, Fs)
+        sW13s, sW2s = ew(2 * Fs, d), ew(d, Fs)
         L.grouped_wgrad(cfg, None, 1, T, dH2_s, 2 * Fs, x, d, sW13s)
         L.grouped_wgrad(cfg, None, 1, T, dy, d, Act_s, Fs, sW2s)
         split += [(dH_s, dH2_s), (dx_s, dx2_s), (dW13s, sW13s), (dW2s, sW2s)]
+    if cfg.wgrad_dtype == L.MOE_BF16:
+        # the fp32-output weight gradients of the same kernel: the bf16 ones are exactly
+        # their round-to-nearest-even
+        c32 = L.config_from_shape(shape, wgrad="f32")
+        fW13, fW2 = e32(E, 2 * F, d), e32(E, d, F)
+        L.grouped_wgrad(c32, off, E, A, dH2, 2 * F, x_perm, d, fW13)
+        L.grouped_wgrad(c32, off, E, A, dYp, d, Act, F, fW2)
+        split += [(dW13, fW13.to(torch.bfloat16)), (dW2, fW2.to(torch.bfloat16))]
+        if Fs:
+            fW13s, fW2s = e32(2 * Fs, d), e32(d, Fs)
+            L.grouped_wgrad(c32, None, 1, T, dH2_s, 2 * Fs, x, d, fW13s)
+            L.grouped_wgrad(c32, None, 1, T, dy, d, Act_s, Fs, fW2s)
+            split += [(dW13s, fW13s.to(torch.bfloat16)), (dW2s, fW2s.to(torch.bfloat16))]
+            fW13s_np, fW2s_np = to_np(fW13s), to_np(fW2s)
+        fW13_np, fW2_np = to_np(fW13), to_np(fW2)
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(split):
         assert torch.equal(a, b), f"split backward differs from the fused one (output {i})"
@@ -189,6 +205,9 @@ def test_grouped_experts_forward_and_backward(cid):
     counts = np.diff(p.offsets)
     check_expert_grads("dW13", to_np(dW13), ref["dW13"], counts, shape)
     check_expert_grads("dW2", to_np(dW2), ref["dW2"], counts, shape)
+    if cfg.wgrad_dtype == L.MOE_BF16:    # the fp32 option against the oracle too
+        check_expert_grads("dW13 (fp32)", fW13_np, ref["dW13"], counts, shape)
+        check_expert_grads("dW2 (fp32)", fW2_np, ref["dW2"], counts, shape)
     if Fs:
         hs, acts, ys = O.swiglu_forward(o["x"], o["W13s"], o["W2s"])
         gs = O.swiglu_backward(o["x"], o["W13s"], o["W2s"], hs, o["dy"])
@@ -201,6 +220,9 @@ def test_grouped_experts_forward_and_backward(cid):
             assert err < tl, f"{name}: {err:.3e}"
         check_grad("dW13s", to_np(dW13s), gs["dW13"], shape)
         check_grad("dW2s", to_np(dW2s), gs["dW2"], shape)
+        if cfg.wgrad_dtype == L.MOE_BF16:
+            check_grad("dW13s (fp32)", fW13s_np, gs["dW13"], shape)
+            check_grad("dW2s (fp32)", fW2s_np, gs["dW2"], shape)
 
 
 @pytest.mark.parametrize("cid", SMALL_IDS)
