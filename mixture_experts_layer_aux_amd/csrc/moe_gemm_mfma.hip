@@ -305,6 +305,21 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
+  if (RAG == RAGGED_K && EPI == EPI_STORE && nk == 0) {
+    // A group without rows: its gradient tile is exact zeros, written straight out with
+    // 16-byte stores along whole tile rows (no accumulators, no LDS staging, no barrier).
+    constexpr int EB = OUT_F32 ? 4 : 2;    // bytes per output element
+    constexpr int TPR = BN * EB / 16;      // threads per tile row
+    constexpr int RPI = NTHR / TPR;        // tile rows per pass of the workgroup
+    const int col = n0 + (tid % TPR) * (16 / EB);
+    if (col < p.N) {
+      char* base = static_cast<char*>(p.C) + static_cast<int64_t>(grp) * p.c_gstride * EB;
+      for (int r = tid / TPR; r < BM && row_begin + r < row_end; r += RPI)
+        *reinterpret_cast<uint4*>(base + (static_cast<int64_t>(row_begin + r) * p.ldc + col) * EB) =
+            make_uint4(0u, 0u, 0u, 0u);
+    }
+    return;
+  }
   if (PING_PONG) {
     // Two wave groups, waves 0-3 (rows 0-127 of the tile) and 4-7 (rows 128-255); wave w
     // and w+4 share a SIMD.  Every stage is a memory phase (read the stage's fragments
