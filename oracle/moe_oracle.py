@@ -287,6 +287,49 @@ def expert_bias_update(expert_bias, counts, rate: float, centered: bool = False)
     return (b + step).astype(np.float32)
 
 
+def quantile_route(scores, beta, k: int, update: bool = True):
+    """Quantile balancing, one micro-batch ([HB] §3.3 Load balancing, Quantile).
+
+    The bias is solved for instead of stepped: each expert ranks the tokens by their score
+    for it and reads off the score that only its target share of tokens beats.  With the
+    router in fp32 (the precision the pages ask for), every value below is one fp32
+    rounding, so the selections are exactly reproducible:
+      keys = scores - beta; per token the k + 1 largest keys, key descending, ties to the
+        lower expert index: the first k are the selected experts, and the (k+1)-th key is
+        the token's alpha;
+      with update (T k a multiple of E): target = T k / E tokens per expert, and expert e's
+        solved bias is the (target + 1)-th largest of scores[:, e] - alpha over the tokens.
+    scores [T, E], beta [E].  Returns idx [T, k], alpha [T] fp32, beta_local [E] fp32 (None
+    without update).
+    """
+    s = np.asarray(scores, dtype=np.float32)
+    b = np.asarray(beta, dtype=np.float32)
+    T, E = s.shape
+    if k + 1 > E:
+        raise ValueError("quantile routing needs k < E")
+    keys = (s - b[None, :]).astype(np.float32)
+    order = np.argsort(-keys, axis=1, kind="stable")[:, :k + 1]
+    idx = order[:, :k].astype(np.int64)
+    alpha = keys[np.arange(T), order[:, k]]
+    if not update:
+        return idx, alpha, None
+    if (T * k) % E:
+        raise ValueError("quantile balancing needs T * k to be a multiple of E")
+    target = T * k // E
+    v = (s - alpha[:, None]).astype(np.float32)
+    beta_local = -np.sort(-v, axis=0)[target, :]
+    return idx, alpha, beta_local.astype(np.float32)
+
+
+def quantile_bias_update(beta, beta_local_avg, ema: float):
+    """The step update of the quantile bias ([HB] §3.3 Quantile): an exponential moving
+    average that keeps `ema` of the previous bias and mixes in the rest of the new solution
+    (the solutions of the step's micro-batches, averaged by the caller), then the mean over
+    the experts is taken out.  float64."""
+    new = ema * _d(beta) + (1.0 - ema) * _d(beta_local_avg)
+    return new - new.mean()
+
+
 def max_violation(counts):
     """MaxVio = (busiest expert's load - mean load) / mean load.
 

@@ -581,3 +581,69 @@ def test_expert_bias_update_balances_a_fixed_batch():
         first = mv if first is None else first
         bias = O.expert_bias_update(bias, counts, 2e-3)
     assert first > 1.0 and mv < 0.25 * first
+
+
+# ------------------------------------------------------------------- quantile balancing
+
+def test_quantile_route_matches_printed_code_form():
+    # the printed form in torch fp32: (scores - beta).topk(k + 1, dim=1); alpha = its last
+    # value; (scores - alpha).topk(T k / E + 1, dim=0).values[-1]; continuous scores, so no
+    # ties leave the order open
+    rng = np.random.default_rng(31)
+    T, E, k = 96, 12, 3
+    scores = rng.random((T, E)).astype(np.float32)
+    beta = (rng.standard_normal(E) * 0.05).astype(np.float32)
+    ts, tb = torch.as_tensor(scores), torch.as_tensor(beta)
+    top = (ts - tb).topk(k + 1, dim=1)
+    alpha = top.values[:, -1:]
+    bl = (ts - alpha).topk(T * k // E + 1, dim=0).values[-1]
+    idx, a, b = O.quantile_route(scores, beta, k)
+    assert np.array_equal(idx, top.indices[:, :-1].numpy())
+    assert np.array_equal(a, alpha[:, 0].numpy())
+    assert np.array_equal(b, bl.numpy())
+
+
+def test_quantile_bias_is_the_target_share_quantile():
+    # the solved bias is the score that only the expert's target share of tokens beats: it
+    # is the (target + 1)-th largest of scores - alpha, so at most target = T k / E values
+    # lie above it and at least target + 1 at or above it (every token's (k+1)-th expert
+    # gives exactly 0, so ties at 0 are part of the method)
+    rng = np.random.default_rng(32)
+    T, E, k = 400, 16, 2
+    target = T * k // E
+    scores = rng.random((T, E)).astype(np.float32) ** 3
+    idx, alpha, bl = O.quantile_route(scores, np.zeros(E, np.float32), k)
+    v = (scores - alpha[:, None]).astype(np.float32)
+    above, at_or_above = (v > bl[None, :]).sum(axis=0), (v >= bl[None, :]).sum(axis=0)
+    assert np.all(above <= target) and np.all(at_or_above >= target + 1)
+    assert np.any(above == target)
+    # brute force on one column: sort it, count down target places
+    col = sorted(v[:, 5].tolist(), reverse=True)
+    assert bl[5] == col[target]
+    # ties in the keys go to the lower expert index, as in the router
+    tie = np.zeros((1, 4), np.float32)
+    assert list(O.quantile_route(tie, np.zeros(4, np.float32), 2, update=False)[0][0]) == [0, 1]
+    with pytest.raises(ValueError):
+        O.quantile_route(scores[:7], np.zeros(E, np.float32), k)     # 7 * 2 is not a multiple of 16
+
+
+def test_quantile_balancing_evens_a_fixed_batch_and_update_is_centered():
+    # routing one skewed batch repeatedly with its own solved bias (no smoothing) brings the
+    # load close to even within a few steps; the update keeps the mean bias at zero
+    rng = np.random.default_rng(33)
+    T, E, k = 1024, 16, 2
+    logits = rng.standard_normal((T, E)) + np.linspace(-2.0, 2.0, E)[None, :]
+    scores = O.softmax_full(logits).astype(np.float32)
+    beta = np.zeros(E, np.float32)
+    mv = []
+    for _ in range(6):
+        idx, _, bl = O.quantile_route(scores, beta, k)
+        mv.append(O.max_violation(O.expert_counts(idx, E)))
+        beta = O.quantile_bias_update(beta, bl, 0.0).astype(np.float32)
+    assert mv[0] > 2.0 and mv[-1] < 0.1 * mv[0]
+    nb = O.quantile_bias_update(rng.standard_normal(E), rng.standard_normal(E), 0.9)
+    assert abs(nb.mean()) < 1e-15
+    # ema = 1 keeps the old bias (centred), ema = 0 takes the new solution (centred)
+    b0, b1 = rng.standard_normal(E), rng.standard_normal(E)
+    np.testing.assert_allclose(O.quantile_bias_update(b0, b1, 1.0), b0 - b0.mean(), atol=1e-15)
+    np.testing.assert_allclose(O.quantile_bias_update(b0, b1, 0.0), b1 - b1.mean(), atol=1e-15)
