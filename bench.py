@@ -317,6 +317,19 @@ def bench_balancing(args, shape, L, S, expert_bias, dw, dlogits, dev):
                                                            dlogits, seq_counts=sc)), 4)
     if bias is not None:
         out["bias_update_ms"] = round(timed(lambda: L.expert_bias_update(cfg, S["counts"], 1e-3, False, bias)), 4)
+    # quantile balancing on the same logits: the router's scores (sigmoid, or the full
+    # softmax), bias solved from zero, then the EMA update (0.9)
+    scores = (torch.sigmoid(S["logits"]) if shape.score != "softmax" else torch.softmax(S["logits"], dim=1)).contiguous()
+    qbeta = torch.zeros(E, dtype=torch.float32, device=dev)
+    qidx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    qalpha = torch.empty(T, dtype=torch.float32, device=dev)
+    qlocal = torch.empty(E, dtype=torch.float32, device=dev)
+    if (T * k) % E == 0 and k < E:
+        out["quantile_router_ms"] = round(timed(lambda: L.router_quantile(cfg, scores, qbeta, qidx, qalpha, qlocal,
+                                                                          ws)), 4)
+        out["quantile_update_ms"] = round(timed(lambda: L.quantile_bias_update(cfg, qlocal, 0.9, qbeta)), 4)
+        # scores read once for the top-(k+1) and once per radix pass (4), alpha and idx
+        out["quantile_bytes"] = 5 * T * E * 4 + T * k * 4 + 5 * T * 4
     # bytes the sequence pass must move on top of the router's: the logits again, idx, and
     # the per-token normalisers written and read
     seq_bytes = T * E * 4 + T * k * 4 + 2 * T * 8

@@ -202,6 +202,26 @@ moe_status_t moe_router_topk(const moe_config_t* cfg, const float* logits, const
 moe_status_t moe_expert_bias_update(const moe_config_t* cfg, const int32_t* counts, float rate, int32_t centered,
                                     float* expert_bias, void* stream);
 
+/* Quantile balancing, one micro-batch ([HB] §3.3 Load balancing, Quantile): the selection
+ * bias is solved for instead of stepped.  All in fp32 (the router precision):
+ *   keys = scores - beta; per token the k + 1 largest keys, key descending, ties to the
+ *   lower expert index: idx [T, k] gets the first k, alpha [T] the (k+1)-th key;
+ *   beta_local (NULL: routing only) [E]: per expert the (T k / E + 1)-th largest of
+ *   scores[:, e] - alpha over the T tokens, the value only the expert's target share of
+ *   T k / E tokens lies above.
+ * scores [T, E] fp32 are the router's scores (for example the softmax probabilities or the
+ * sigmoid scores), beta [E] fp32 the current bias.  ws: the forward workspace.
+ * Errors: k >= E; beta_local requested and T * k not a multiple of E -> INVALID_ARG. */
+moe_status_t moe_router_quantile(const moe_config_t* cfg, const float* scores, const float* beta, int32_t* idx,
+                                 float* alpha, float* beta_local, void* ws, size_t ws_bytes, void* stream);
+
+/* The step update of the quantile bias ([HB] §3.3 Quantile, the EMA):
+ *   beta = ema * beta + (1 - ema) * beta_local, then the mean over the E experts is
+ *   subtracted (summed in fp64 in a fixed order).  beta_local: the step's solution (the
+ *   average over its micro-batches is the caller's).  Errors: ema outside [0, 1] -> INVALID_ARG. */
+moe_status_t moe_quantile_bias_update(const moe_config_t* cfg, const float* beta_local, float ema, float* beta,
+                                      void* stream);
+
 /* Dropless permutation ([LC] "Read the timeline before blaming the network": tokens are
  * grouped by expert before the expert matmuls): offsets = exclusive prefix of the
  * per-expert counts; row_of[t, j] = row of (t, j); token_of[row] = t;

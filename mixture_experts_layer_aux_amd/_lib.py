@@ -28,7 +28,8 @@ EXPORTED = (
     "moe_router_topk", "moe_permute", "moe_grouped_gemm_swiglu", "moe_unpermute_combine", "moe_layer_fwd",
     "moe_unpermute_combine_bwd", "moe_grouped_gemm_swiglu_bwd", "moe_grouped_wgrad", "moe_permute_bwd", "moe_router_bwd",
     "moe_quantize_fp8", "moe_permute_fp8", "moe_grouped_gemm_swiglu_fp8",
-    "moe_gate_logits_bwd", "moe_layer_bwd", "moe_expert_bias_update",
+    "moe_gate_logits_bwd", "moe_layer_bwd", "moe_expert_bias_update", "moe_router_quantile",
+    "moe_quantile_bias_update",
 )
 
 
@@ -195,6 +196,24 @@ def expert_bias_update(cfg, counts, rate, centered, expert_bias, stream=None):
                                          ctypes.c_float(rate), ctypes.c_int32(int(bool(centered))),
                                          _P(_ptr(expert_bias, torch.float32, cfg.E, "expert_bias")),
                                          _P(_stream(stream))))
+
+
+def router_quantile(cfg, scores, beta, idx, alpha, beta_local, ws, stream=None):
+    """Quantile balancing of one micro-batch: idx, alpha and (unless beta_local is None) the
+    solved bias."""
+    wp, wn = _ws(ws)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    _check(load().moe_router_quantile(ctypes.byref(cfg), _P(_ptr(scores, torch.float32, T * E, "scores")),
+                                      _P(_ptr(beta, torch.float32, E, "beta")), _P(_ptr(idx, torch.int32, T * k, "idx")),
+                                      _P(_ptr(alpha, torch.float32, T, "alpha")),
+                                      _P(_ptr(beta_local, torch.float32, E, "beta_local")), _P(wp),
+                                      ctypes.c_size_t(wn), _P(_stream(stream))))
+
+
+def quantile_bias_update(cfg, beta_local, ema, beta, stream=None):
+    _check(load().moe_quantile_bias_update(ctypes.byref(cfg), _P(_ptr(beta_local, torch.float32, cfg.E, "beta_local")),
+                                           ctypes.c_float(ema), _P(_ptr(beta, torch.float32, cfg.E, "beta")),
+                                           _P(_stream(stream))))
 
 
 def permute(cfg, x, idx, offsets, row_of, token_of, x_perm, ws, stream=None):

@@ -50,6 +50,7 @@ struct FwdWs {
   float* pnorm;        // [T, 2] (sequence-wise loss only)
   int32_t* seq_cnt_part;  // router_seq_part_elems
   float* seq_prob_part;   // router_seq_part_elems
+  void* quantile;      // quantile_ws_bytes(E): histograms and radix-select state
   int32_t* blk_base;   // [nchunk, E]
   int32_t* counts;     // [E]
   float* prob_sum;     // [E]
@@ -78,6 +79,7 @@ FwdWs carve_fwd(const moe_config_t& c, void* base) {
   w.pnorm = nseq ? reinterpret_cast<float*>(take(static_cast<size_t>(c.T) * 8)) : nullptr;
   w.seq_cnt_part = nseq ? reinterpret_cast<int32_t*>(take(nseq * 4)) : nullptr;
   w.seq_prob_part = nseq ? reinterpret_cast<float*>(take(nseq * 4)) : nullptr;
+  w.quantile = take(quantile_ws_bytes(c.E));
   w.blk_base = reinterpret_cast<int32_t*>(take(nch * c.E * 4));
   w.counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(c.E) * 4));
   w.prob_sum = reinterpret_cast<float*>(take(static_cast<size_t>(c.E) * 4));
@@ -484,6 +486,27 @@ moe_status_t moe_expert_bias_update(const moe_config_t* cfg, const int32_t* coun
   MOE_NEED(counts); MOE_NEED(expert_bias);
   if (!(rate > -INFINITY && rate < INFINITY)) return fail(MOE_ERR_INVALID_ARG, "rate must be finite");
   return launch_bias_update(counts, cfg->E, rate, centered ? 1 : 0, expert_bias, S(stream));
+}
+
+moe_status_t moe_router_quantile(const moe_config_t* cfg, const float* scores, const float* beta, int32_t* idx,
+                                 float* alpha, float* beta_local, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED(scores); MOE_NEED(beta); MOE_NEED(idx); MOE_NEED(alpha); MOE_NEED(ws);
+  if (cfg->k >= cfg->E) return fail(MOE_ERR_INVALID_ARG, "quantile routing needs k < E (k=%d E=%d)", cfg->k, cfg->E);
+  if (beta_local && (static_cast<int64_t>(cfg->T) * cfg->k) % cfg->E)
+    return fail(MOE_ERR_INVALID_ARG, "quantile balancing needs T*k (%lld) to be a multiple of E=%d",
+                static_cast<long long>(cfg->T) * cfg->k, cfg->E);
+  const FwdWs fw = carve_fwd(*cfg, ws);
+  MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
+  return launch_router_quantile(*cfg, scores, beta, idx, alpha, beta_local, fw.quantile, S(stream));
+}
+
+moe_status_t moe_quantile_bias_update(const moe_config_t* cfg, const float* beta_local, float ema, float* beta,
+                                      void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED(beta_local); MOE_NEED(beta);
+  if (!(ema >= 0.0f && ema <= 1.0f)) return fail(MOE_ERR_INVALID_ARG, "ema must be in [0, 1]");
+  return launch_quantile_update(beta_local, cfg->E, ema, beta, S(stream));
 }
 
 moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* idx, int32_t* offsets,

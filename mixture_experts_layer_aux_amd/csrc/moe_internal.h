@@ -28,6 +28,11 @@ moe_status_t launch_router_bwd(const moe_config_t& c, const float* logits, const
                                const float* dw, const int32_t* counts, const int32_t* seq_counts, float daux,
                                float* dlogits, hipStream_t s);
 moe_status_t launch_bias_update(const int32_t* counts, int E, float rate, int centered, float* bias, hipStream_t s);
+// quantile balancing (moe_quantile.hip); ws: quantile_ws_bytes(E) bytes
+size_t quantile_ws_bytes(int E);
+moe_status_t launch_router_quantile(const moe_config_t& c, const float* scores, const float* beta, int32_t* idx,
+                                    float* alpha, float* beta_local, void* ws, hipStream_t s);
+moe_status_t launch_quantile_update(const float* beta_local, int E, float ema, float* beta, hipStream_t s);
 
 // ---------------------------------------------------------------- permute / combine
 int64_t permute_num_chunks(int T);

@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_declared_entry_point():
     lib = L.load()
     names = header_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     assert sorted(L.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -143,6 +143,26 @@ def test_weight_gradient_dtype_defaults_to_the_activation_dtype():
     assert L.config_from_shape(W.LAYERS[1]).wgrad_dtype == L.MOE_F32
     c = L.config_from_shape(W.LAYERS[3], wgrad="f32")
     assert c.wgrad_dtype == L.MOE_F32 and _status(c) == L.MOE_OK
+
+
+def test_quantile_calls_check_their_arguments_before_launching():
+    lib = L.load()
+    fake, nul, s = P(1 << 20), P(None), P(None)
+    cfg = L.config_from_shape(W.LAYERS[2])                      # T=8192, k=8, E=64: T k % E == 0
+    st = lib.moe_router_quantile(ctypes.byref(cfg), fake, fake, fake, nul, fake, fake, ctypes.c_size_t(1 << 40), s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"alpha" in lib.moe_last_error()
+    odd = L.config_from_shape(W.LAYERS[2])
+    odd.T = 8191                                                # T k not a multiple of E
+    st = lib.moe_router_quantile(ctypes.byref(odd), fake, fake, fake, fake, fake, fake, ctypes.c_size_t(1 << 40), s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"multiple" in lib.moe_last_error()
+    full = L.config_from_shape(W.LAYERS[2])
+    full.k = full.E = 8
+    st = lib.moe_router_quantile(ctypes.byref(full), fake, fake, fake, fake, nul, fake, ctypes.c_size_t(1 << 40), s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"k < E" in lib.moe_last_error()
+    st = lib.moe_router_quantile(ctypes.byref(cfg), fake, fake, fake, fake, fake, fake, ctypes.c_size_t(16), s)
+    assert st == L.MOE_ERR_WORKSPACE
+    st = lib.moe_quantile_bias_update(ctypes.byref(cfg), fake, ctypes.c_float(1.5), fake, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"ema" in lib.moe_last_error()
 
 
 def test_sigmoid_top1_is_allowed_and_fp32_f192_is_allowed():

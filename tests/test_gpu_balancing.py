@@ -217,3 +217,57 @@ def test_layer_with_variants_and_losses(name):
         # dx carries the router path (with every loss gradient) through the gate GEMM
         assert rel_err(to_np(dx), b["dx"], safe) < tl, "dx"
         check_grad("dWg", to_np(G["dWg"]), b["dWg"], shape)
+
+
+# quantile balancing: (T, E, k, scores law, solve)
+_QUANTILE_CASES = {
+    "softmax_64x8": (2048, 64, 8, "softmax", True),
+    "sigmoid_256x8_bias": (1024, 256, 8, "sigmoid", True),
+    "ragged_12x2": (300, 12, 2, "softmax", True),
+    "wide_896x16": (1792, 896, 16, "softmax", True),
+    "route_only_odd_T": (333, 40, 3, "sigmoid", False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_QUANTILE_CASES))
+def test_quantile_router_bit_exact(name):
+    torch = torch_mod()
+    L = _lib()
+    T, E, k, law, solve = _QUANTILE_CASES[name]
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    logits = rng.standard_normal((T, E)) * 1.5 + np.linspace(-1.0, 1.0, E)[None, :]
+    scores = (O.softmax_full(logits) if law == "softmax" else O.sigmoid(logits)).astype(np.float32)
+    beta = (rng.standard_normal(E) * (0.01 if law == "softmax" else 0.1)).astype(np.float32)
+    if name == "sigmoid_256x8_bias":   # scores and bias on a coarse grid: many exact ties
+        scores = (np.round(scores * 16) / 16).astype(np.float32)
+        beta = (np.round(beta * 32) / 32).astype(np.float32)
+    cfg = L.make_config(T, 64, E, k, 128, act="f32", score="sigmoid" if law == "sigmoid" else "softmax")
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev())
+    alpha = torch.empty(T, dtype=torch.float32, device=dev())
+    bl = torch.full((E,), float("nan"), dtype=torch.float32, device=dev()) if solve else None
+    ws = L.alloc_workspace(cfg, dev())
+    print(f"quantile case {name}: T={T} E={E} k={k}", flush=True)
+    L.router_quantile(cfg, to_dev(scores), to_dev(beta), idx, alpha, bl, ws)
+    torch.cuda.synchronize()
+    ridx, ralpha, rbl = O.quantile_route(scores, beta, k, update=solve)
+    assert np.array_equal(to_np(idx), ridx), "selected experts differ"
+    assert np.array_equal(to_np(alpha).astype(np.float32).view(np.uint32), ralpha.view(np.uint32)), "alpha differs"
+    if solve:
+        got = to_np(bl).astype(np.float32)
+        assert np.all(got == rbl), "solved bias differs"
+
+
+def test_quantile_bias_update_matches_oracle():
+    torch = torch_mod()
+    L = _lib()
+    rng = np.random.default_rng(41)
+    for E, ema in ((256, 0.9), (896, 0.0), (7, 1.0)):
+        beta = (rng.standard_normal(E) * 0.1).astype(np.float32)
+        local = (rng.standard_normal(E) * 0.1).astype(np.float32)
+        cfg = L.make_config(64 * E, 64, E, 1, 128, act="f32", score="sigmoid")
+        b = to_dev(beta.copy())
+        L.quantile_bias_update(cfg, to_dev(local), ema, b)
+        torch.cuda.synchronize()
+        ref = O.quantile_bias_update(beta, local, ema)
+        np.testing.assert_allclose(to_np(b), ref, rtol=1e-6, atol=2e-8)
+        assert abs(to_np(b).mean()) < 1e-7
