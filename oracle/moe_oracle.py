@@ -378,35 +378,100 @@ def silu(g):
     return g / (1.0 + np.exp(-g))
 
 
-def swiglu_forward(X, W13, W2):
-    """One bias-free SwiGLU expert on rows X.
+@dataclass(frozen=True)
+class GLU:
+    """The gated activation between an expert's projections ([HB] §3.4 Activation).
+
+    kind "swiglu": silu(gate) * up;
+    kind "clamp":  the hard clamp: gate clamped from above at c, up clamped to [-c, c],
+                   then silu(gate) * up;
+    kind "situ":   SiTU-GLU: s tanh(gate / s) sigma(gate) * up', with up' = s_l tanh(up / s_l)
+                   when s_l > 0, else up (c is s, c_linear is s_l).
+    """
+    kind: str = "swiglu"
+    c: float = 0.0
+    c_linear: float = 0.0
+
+
+SWIGLU = GLU()
+
+
+def glu_forward(H, glu: GLU = SWIGLU):
+    """Act from H = [gate | up] (gate half first)."""
+    H = _d(H)
+    F = H.shape[1] // 2
+    g, u = H[:, :F], H[:, F:]
+    if glu.kind == "swiglu":
+        return silu(g) * u
+    if glu.kind == "clamp":
+        return silu(np.minimum(g, glu.c)) * np.clip(u, -glu.c, glu.c)
+    if glu.kind == "situ":
+        a = glu.c * np.tanh(g / glu.c) * sigmoid(g)
+        ul = glu.c_linear * np.tanh(u / glu.c_linear) if glu.c_linear > 0 else u
+        return a * ul
+    raise ValueError(glu.kind)
+
+
+def glu_backward(H, dAct, glu: GLU = SWIGLU):
+    """dH = [dgate | dup] by the chain rule (derived; the pages print the forward only).
+
+    silu'(g) = sigma(g) (1 + g (1 - sigma(g)));  a clamp passes the gradient where its
+    input lies inside the closed interval and none outside;  d/dx [s tanh(x/s) sigma(x)] =
+    (1 - tanh^2(x/s)) sigma(x) + s tanh(x/s) sigma(x) (1 - sigma(x));
+    d/dx [s_l tanh(x/s_l)] = 1 - tanh^2(x/s_l).
+    """
+    H, dAct = _d(H), _d(dAct)
+    F = H.shape[1] // 2
+    g, u = H[:, :F], H[:, F:]
+    if glu.kind in ("swiglu", "clamp"):
+        gc, uc = (g, u) if glu.kind == "swiglu" else (np.minimum(g, glu.c), np.clip(u, -glu.c, glu.c))
+        s = sigmoid(gc)
+        dg = dAct * uc * s * (1.0 + gc * (1.0 - s))
+        du = dAct * gc * s
+        if glu.kind == "clamp":
+            dg = np.where(g <= glu.c, dg, 0.0)
+            du = np.where(np.abs(u) <= glu.c, du, 0.0)
+        return np.concatenate([dg, du], axis=1)
+    if glu.kind == "situ":
+        sc = glu.c
+        th, s = np.tanh(g / sc), sigmoid(g)
+        a = sc * th * s
+        da = (1.0 - th * th) * s + sc * th * s * (1.0 - s)
+        if glu.c_linear > 0:
+            tl = np.tanh(u / glu.c_linear)
+            ul, dul = glu.c_linear * tl, 1.0 - tl * tl
+        else:
+            ul, dul = u, np.ones_like(u)
+        return np.concatenate([dAct * ul * da, dAct * a * dul], axis=1)
+    raise ValueError(glu.kind)
+
+
+def swiglu_forward(X, W13, W2, glu: GLU = SWIGLU):
+    """One bias-free gated expert on rows X.
 
     [HB] §3.4 Experts, Count and size (fc1 is twice the expert width for a gated
     linear unit; fc2 maps the width back to d) and Activation (the GLU splits fc1's
-    output in two halves, gate first, and multiplies silu(gate) by the up half).
-    Returns H = X W13^T [n, 2F], Act = silu(H_gate) * H_up [n, F], Y = Act W2^T [n, d].
+    output in two halves, gate first, and multiplies silu(gate) by the up half; the clamp
+    and SiTU-GLU variants bound it).
+    Returns H = X W13^T [n, 2F], Act = glu(H) [n, F], Y = Act W2^T [n, d].
     """
     H = _d(X) @ _d(W13).T
-    F = H.shape[1] // 2
-    Act = silu(H[:, :F]) * H[:, F:]
+    Act = glu_forward(H, glu)
     Y = Act @ _d(W2).T
     return H, Act, Y
 
 
-def swiglu_backward(X, W13, W2, H, dY):
+def swiglu_backward(X, W13, W2, H, dY, glu: GLU = SWIGLU):
     """Backward of swiglu_forward by the chain rule (derived, not printed on the pages).
 
-    dAct = dY W2; with s = sigma(g): silu'(g) = s (1 + g (1 - s));
-    dH_gate = dAct * up * silu'(g), dH_up = dAct * silu(g);
+    dAct = dY W2; dH = glu_backward(H, dAct) (for plain SwiGLU, with s = sigma(g):
+    dH_gate = dAct * up * s (1 + g (1 - s)), dH_up = dAct * silu(g));
     dX = dH W13, dW13 = dH^T X, dW2 = dY^T Act.
     """
     X, W13, W2, H, dY = map(_d, (X, W13, W2, H, dY))
-    F = H.shape[1] // 2
-    g, u = H[:, :F], H[:, F:]
-    s = sigmoid(g)
-    act = g * s * u
+    act = glu_forward(H, glu)
     dAct = dY @ W2
-    dH = np.concatenate([dAct * u * s * (1.0 + g * (1.0 - s)), dAct * g * s], axis=1)
+    dH = glu_backward(H, dAct, glu)
     return dict(dX=dH @ W13, dW13=dH.T @ X, dW2=dY.T @ act, dH=dH, dAct=dAct)
 
 
@@ -423,6 +488,7 @@ class LayerSpec:
     z_coeff: float = 0.0            # router z-loss coefficient
     seq_aux_coeff: float = 0.0      # sequence-wise balance loss coefficient
     seq_len: int = 0                # S of that loss (tokens ordered [S, B])
+    glu: GLU = SWIGLU               # the experts' gated activation
 
 
 def route(logits, spec: LayerSpec, expert_bias=None) -> Dict[str, np.ndarray]:
@@ -481,11 +547,11 @@ def layer_forward(x, Wg, W13, W2, spec: LayerSpec, bg=None, expert_bias=None,
     for e in range(spec.E):
         a, b = perm.offsets[e], perm.offsets[e + 1]
         if b > a:
-            H[a:b], Act[a:b], Yp[a:b] = swiglu_forward(xp[a:b], W13[e], W2[e])
+            H[a:b], Act[a:b], Yp[a:b] = swiglu_forward(xp[a:b], W13[e], W2[e], spec.glu)
     y = np.einsum("tk,tkd->td", r["w"], Yp[perm.row_of])
     shared = None
     if W13s is not None:
-        Hs, Acts, Ys = swiglu_forward(x, W13s, W2s)
+        Hs, Acts, Ys = swiglu_forward(x, W13s, W2s, spec.glu)
         y = y + Ys
         shared = dict(H=Hs, Act=Acts, Y=Ys)
     return dict(logits=logits, route=r, perm=perm, x_perm=xp, H=H, Act=Act, Y_perm=Yp,
@@ -584,12 +650,12 @@ def layer_backward(fwd: Dict[str, object], x, Wg, W13, W2, dy, spec: LayerSpec,
     for e in range(spec.E):
         a, b = perm.offsets[e], perm.offsets[e + 1]
         if b > a:
-            g = swiglu_backward(xp[a:b], W13[e], W2[e], fwd["H"][a:b], dYp[a:b])
+            g = swiglu_backward(xp[a:b], W13[e], W2[e], fwd["H"][a:b], dYp[a:b], spec.glu)
             dXp[a:b], dW13[e], dW2[e], dH[a:b] = g["dX"], g["dW13"], g["dW2"], g["dH"]
     dx = dXp[rows].sum(axis=1)
     out = dict(dw=dw, dY_perm=dYp, dX_perm=dXp, dH=dH, dW13=dW13, dW2=dW2)
     if W13s is not None:
-        gs = swiglu_backward(x, W13s, W2s, fwd["shared"]["H"], dy)
+        gs = swiglu_backward(x, W13s, W2s, fwd["shared"]["H"], dy, spec.glu)
         dx = dx + gs["dX"]
         out.update(dW13s=gs["dW13"], dW2s=gs["dW2"], dH_s=gs["dH"])
     dlogits = router_backward(fwd["logits"], idx, w, dw, spec, counts=r["counts"], daux=daux,
@@ -713,7 +779,7 @@ def layer_forward_fp8(x, Wg, W13q, W13_scale, W2q, W2_scale, spec: "LayerSpec", 
         w13 = dequantize_blocks(W13q[e], W13_scale[e], 128)
         w2 = dequantize_blocks(W2q[e], W2_scale[e], 128)
         H[a:b] = xp[a:b] @ w13.T
-        Act[a:b] = silu(H[a:b, :F]) * H[a:b, F:]
+        Act[a:b] = glu_forward(H[a:b], spec.glu)
         Actq[a:b], Acts[a:b] = quantize_blocks(Act[a:b].astype(np.float32), 1)
         Yp[a:b] = dequantize_blocks(Actq[a:b], Acts[a:b], 1) @ w2.T
     y = np.einsum("tk,tkd->td", r["w"], Yp[perm.row_of])

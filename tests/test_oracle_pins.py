@@ -298,6 +298,10 @@ def test_layer_against_independent_token_loop():
     dict(score="sqrtsoftplus", k=2, aux=0.0, Fs=0, scaling=1.7, bias="expert_bias",
          extra=dict(seq_aux_coeff=0.6, seq_len=16)),
     dict(score="sqrtsoftplus", k=1, aux=0.5, Fs=0, scaling=1.0, bias=None, extra=dict(z_coeff=0.03)),
+    # the clamped SwiGLU and SiTU-GLU experts
+    dict(score="softmax", k=2, aux=0.0, Fs=4, scaling=1.0, bias=None, extra=dict(glu=O.GLU("clamp", 0.35))),
+    dict(score="sigmoid", k=2, aux=0.0, Fs=4, scaling=1.0, bias=None, extra=dict(glu=O.GLU("situ", 0.6, 0.5))),
+    dict(score="softmax", k=3, aux=0.1, Fs=0, scaling=1.0, bias=None, extra=dict(glu=O.GLU("situ", 0.8, 0.0))),
 ])
 def test_backward_matches_central_differences(case):
     rng = np.random.default_rng(14)
@@ -647,3 +651,47 @@ def test_quantile_balancing_evens_a_fixed_batch_and_update_is_centered():
     b0, b1 = rng.standard_normal(E), rng.standard_normal(E)
     np.testing.assert_allclose(O.quantile_bias_update(b0, b1, 1.0), b0 - b0.mean(), atol=1e-15)
     np.testing.assert_allclose(O.quantile_bias_update(b0, b1, 0.0), b1 - b1.mean(), atol=1e-15)
+
+
+# ------------------------------------------------------------------ activation variants
+
+def _glu_torch(H, glu):
+    """The printed forms, in torch: glu() with the clamp (gate from above, up on both sides),
+    and situ_glu() with tanh_soft_clamp."""
+    H = torch.as_tensor(H, dtype=torch.float64).requires_grad_(True)
+    g, u = torch.chunk(H, 2, dim=-1)
+    if glu.kind == "clamp":
+        out = torch.nn.functional.silu(g.clamp(min=None, max=glu.c)) * u.clamp(min=-glu.c, max=glu.c)
+    elif glu.kind == "situ":
+        tsc = lambda x, sc: sc * torch.tanh(x / sc)  # noqa: E731
+        ul = tsc(u, glu.c_linear) if glu.c_linear > 0 else u
+        out = tsc(g, glu.c) * torch.sigmoid(g) * ul
+    else:
+        out = torch.nn.functional.silu(g) * u
+    return H, out
+
+
+@pytest.mark.parametrize("glu", [O.GLU("clamp", 0.7), O.GLU("clamp", 10.0), O.GLU("situ", 4.0, 25.0),
+                                 O.GLU("situ", 0.5, 0.0), O.SWIGLU])
+def test_glu_variants_match_printed_forms_and_autograd(glu):
+    rng = np.random.default_rng(51)
+    H = rng.standard_normal((40, 24)) * 3.0
+    H[0, 0], H[0, 12] = glu.c + 0.25, -(glu.c + 0.25)      # clamped on both halves
+    Ht, out = _glu_torch(H, glu)
+    np.testing.assert_allclose(O.glu_forward(H, glu), out.detach().numpy(), rtol=1e-13, atol=1e-14)
+    dAct = rng.standard_normal((40, 12))
+    out.backward(torch.as_tensor(dAct))
+    np.testing.assert_allclose(O.glu_backward(H, dAct, glu), Ht.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_glu_variants_reduce_to_swiglu():
+    rng = np.random.default_rng(52)
+    H = rng.standard_normal((30, 16))
+    plain = O.glu_forward(H)
+    np.testing.assert_allclose(O.glu_forward(H, O.GLU("clamp", 1e6)), plain, rtol=1e-15)
+    # s tanh(x / s) -> x as s grows, so SiTU-GLU -> silu(gate) * up
+    np.testing.assert_allclose(O.glu_forward(H, O.GLU("situ", 1e5, 0.0)), plain, rtol=1e-8, atol=1e-12)
+    # a clamped unit passes no gradient to its input
+    Hc = np.array([[5.0, -1.0, 0.3, 7.0]])
+    dH = O.glu_backward(Hc, np.ones((1, 2)), O.GLU("clamp", 2.0))
+    assert dH[0, 0] == 0.0 and dH[0, 3] == 0.0 and dH[0, 1] != 0.0 and dH[0, 2] != 0.0
