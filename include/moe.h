@@ -80,6 +80,14 @@ typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1, MOE_SQRTSOFTPLUS = 2 } moe_scor
  * sequence-wise aux loss (each loss already multiplied by its coefficient). */
 #define MOE_NSTATS 6
 
+/* The experts' gated activation on H = [gate | up] ([HB] §3.4 Activation):
+ *   MOE_GLU_SWIGLU  Act = silu(gate) * up;
+ *   MOE_GLU_CLAMP   the hard clamp: gate clamped from above at c and up to [-c, c], then
+ *                   SwiGLU (the gradient passes where the input lies inside the interval);
+ *   MOE_GLU_SITU    SiTU-GLU: s tanh(gate / s) sigmoid(gate) * up', with
+ *                   up' = s_l tanh(up / s_l) when s_l > 0, else up. */
+typedef enum { MOE_GLU_SWIGLU = 0, MOE_GLU_CLAMP = 1, MOE_GLU_SITU = 2 } moe_glu_t;
+
 /*
  * The layer's settings, mirroring the flags of [HB] §2.5 Your first MoE (number of
  * experts, expert FFN width, top-k), §3.1 (score function, routed scaling factor),
@@ -93,6 +101,8 @@ typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1, MOE_SQRTSOFTPLUS = 2 } moe_scor
  *   scale, a softmax over one selected logit gives the router no gradient);
  *   aux_coeff, z_coeff, seq_aux_coeff finite and >= 0; seq_aux_coeff > 0 needs
  *   seq_len >= 1 dividing T (INVALID_ARG otherwise) and T / seq_len <= 65535;
+ *   glu_kind MOE_GLU_CLAMP needs glu_c finite > 0; MOE_GLU_SITU needs glu_c finite > 0 and
+ *   glu_c_linear finite >= 0 (INVALID_ARG otherwise);
  *   w_dtype == MOE_FP8_E4M3 (fp8 experts, see moe_quantize_fp8) needs act_dtype == bf16,
  *   Fs == 0, d % 128 == 0 and F % 128 == 0 (UNSUPPORTED otherwise).
  */
@@ -110,6 +120,9 @@ typedef struct moe_config {
                              t = s * B + b is position s of sequence b, B = T / S */
   int32_t wgrad_dtype;    /* moe_dtype_t of the expert weight gradients: MOE_F32 (0), or
                              MOE_BF16 with bf16 activations (INVALID_ARG / UNSUPPORTED otherwise) */
+  int32_t glu_kind;       /* moe_glu_t: the experts' gated activation ([HB] §3.4 Activation) */
+  float glu_c;            /* MOE_GLU_CLAMP: the limit c; MOE_GLU_SITU: the gate cap s */
+  float glu_c_linear;     /* MOE_GLU_SITU: the up-half cap s_l (0 = no cap) */
 } moe_config_t;
 
 typedef struct moe_weights {

@@ -22,6 +22,8 @@ MOE_SOFTMAX, MOE_SIGMOID, MOE_SQRTSOFTPLUS = 0, 1, 2
 _SCORES = {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID, "sqrtsoftplus": MOE_SQRTSOFTPLUS}
 # stats[]: aux, MaxVio, empty experts, max count, z-loss, sequence-wise aux loss
 MOE_NSTATS = 6
+MOE_GLU_SWIGLU, MOE_GLU_CLAMP, MOE_GLU_SITU = 0, 1, 2
+_GLUS = {"swiglu": MOE_GLU_SWIGLU, "clamp": MOE_GLU_CLAMP, "situ": MOE_GLU_SITU}
 
 EXPORTED = (
     "moe_status_string", "moe_last_error", "moe_validate", "moe_workspace_size", "moe_gate_logits",
@@ -44,7 +46,8 @@ class Config(ctypes.Structure):
                 ("F", ctypes.c_int32), ("Fs", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("pre_softmax", ctypes.c_int32), ("routed_scaling", ctypes.c_float), ("aux_coeff", ctypes.c_float),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("z_coeff", ctypes.c_float),
-                ("seq_aux_coeff", ctypes.c_float), ("seq_len", ctypes.c_int32), ("wgrad_dtype", ctypes.c_int32)]
+                ("seq_aux_coeff", ctypes.c_float), ("seq_len", ctypes.c_int32), ("wgrad_dtype", ctypes.c_int32),
+                ("glu_kind", ctypes.c_int32), ("glu_c", ctypes.c_float), ("glu_c_linear", ctypes.c_float)]
 
 
 _P = ctypes.c_void_p
@@ -92,19 +95,25 @@ def _check(status: int) -> None:
 
 
 def make_config(T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux_coeff=0.0, act="bf16", wq="",
-                pre_softmax=False, z_coeff=0.0, seq_aux_coeff=0.0, seq_len=0, wgrad=None) -> Config:
+                pre_softmax=False, z_coeff=0.0, seq_aux_coeff=0.0, seq_len=0, wgrad=None,
+                glu="swiglu", glu_c=0.0, glu_c_linear=0.0) -> Config:
     """wq: "" (expert weights in the activation dtype) or "fp8" (e4m3 codes + block scales).
-    wgrad: dtype of the expert weight gradients, "bf16" or "f32"; None = the activation dtype."""
+    wgrad: dtype of the expert weight gradients, "bf16" or "f32"; None = the activation dtype.
+    glu: the experts' gated activation, "swiglu", "clamp" (limit glu_c) or "situ" (gate cap
+    glu_c, up cap glu_c_linear, 0 = none)."""
     wgrad = act if wgrad is None else wgrad
     return Config(T=T, d=d, E=E, k=k, F=F, Fs=Fs, score=_SCORES[score], pre_softmax=int(bool(pre_softmax)),
                   routed_scaling=scaling, aux_coeff=aux_coeff, act_dtype=MOE_BF16 if act == "bf16" else MOE_F32,
                   w_dtype=MOE_FP8_E4M3 if wq == "fp8" else 0, z_coeff=z_coeff, seq_aux_coeff=seq_aux_coeff,
-                  seq_len=seq_len, wgrad_dtype=MOE_BF16 if wgrad == "bf16" else MOE_F32)
+                  seq_len=seq_len, wgrad_dtype=MOE_BF16 if wgrad == "bf16" else MOE_F32, glu_kind=_GLUS[glu],
+                  glu_c=glu_c, glu_c_linear=glu_c_linear)
 
 
 def config_from_shape(s, **extra) -> Config:
     kw = dict(pre_softmax=getattr(s, "pre_softmax", False), z_coeff=getattr(s, "z_coeff", 0.0),
-              seq_aux_coeff=getattr(s, "seq_aux_coeff", 0.0), seq_len=getattr(s, "seq_len", 0))
+              seq_aux_coeff=getattr(s, "seq_aux_coeff", 0.0), seq_len=getattr(s, "seq_len", 0),
+              glu=getattr(s, "glu", "swiglu"), glu_c=getattr(s, "glu_c", 0.0),
+              glu_c_linear=getattr(s, "glu_c_linear", 0.0))
     kw.update(extra)
     return make_config(s.T, s.d, s.E, s.k, s.F, s.Fs, s.score, s.scaling, s.aux_coeff, s.act, getattr(s, "wq", ""),
                        **kw)

@@ -170,6 +170,12 @@ moe_status_t validate(const moe_config_t* c) {
   if (!(c->aux_coeff >= 0.0f && c->aux_coeff < INFINITY) || !(c->z_coeff >= 0.0f && c->z_coeff < INFINITY) ||
       !(c->seq_aux_coeff >= 0.0f && c->seq_aux_coeff < INFINITY))
     return fail(MOE_ERR_INVALID_ARG, "loss coefficients must be finite and >= 0");
+  if (c->glu_kind != MOE_GLU_SWIGLU && c->glu_kind != MOE_GLU_CLAMP && c->glu_kind != MOE_GLU_SITU)
+    return fail(MOE_ERR_INVALID_ARG, "unknown gated activation");
+  if (c->glu_kind != MOE_GLU_SWIGLU && !(c->glu_c > 0.0f && c->glu_c < INFINITY))
+    return fail(MOE_ERR_INVALID_ARG, "the activation bound glu_c must be finite and > 0");
+  if (c->glu_kind == MOE_GLU_SITU && !(c->glu_c_linear >= 0.0f && c->glu_c_linear < INFINITY))
+    return fail(MOE_ERR_INVALID_ARG, "glu_c_linear must be finite and >= 0");
   if (c->seq_aux_coeff != 0.0f && (c->seq_len < 1 || c->T % c->seq_len))
     return fail(MOE_ERR_INVALID_ARG, "seq_len=%d must be >= 1 and divide T=%d", c->seq_len, c->T);
   if (c->seq_aux_coeff != 0.0f && c->T / c->seq_len > 65535)
@@ -288,6 +294,7 @@ moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const in
     g1.B = shared ? W13s : W13; g1.ldb = c.d; g1.b_gstride = shared ? 0 : int64_t{2} * F * c.d;
     g1.C = h; g1.ldc = 2 * F; g1.C2 = act; g1.ldc2 = F;
     g1.offsets = shared ? nullptr : offsets; g1.G = shared ? 1 : c.E; g1.range_end = c.T; g1.rows_upper = A;
+    g1.glu = glu_of(c);
     GemmDesc g2 = g1;
     g2.c_type = MOE_F32;  // expert outputs are kept in fp32 for the combine
     g2.N = c.d; g2.K = F; g2.A = act; g2.lda = F;
@@ -300,7 +307,8 @@ moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const in
     } else {
       g1.epi = EPI_STORE;
       MOE_TRY(launch_gemm_fma(g1, s));
-      MOE_TRY(launch_swiglu_fwd_elementwise(static_cast<const float*>(h), static_cast<float*>(act), shared ? c.T : A,
+      MOE_TRY(launch_swiglu_fwd_elementwise(glu_of(c), static_cast<const float*>(h), static_cast<float*>(act),
+                                            shared ? c.T : A,
                                             F, s));
       MOE_TRY(launch_gemm_fma(g2, s));
     }
@@ -329,7 +337,8 @@ moe_status_t run_experts_fp8(const moe_config_t& c, const uint8_t* x_perm, const
                              float* H, uint8_t* Act, float* Act_scale, float* Y_perm, float* act32, int32_t* sched,
                              hipStream_t s) {
   const int64_t A = static_cast<int64_t>(c.T) * c.k;
-  MOE_TRY(launch_gemm_fp8(true, x_perm, xps, W13, W13_scale, act32, H, offsets, c.E, A, 2 * c.F, c.d, c.F, sched, s));
+  MOE_TRY(launch_gemm_fp8(true, x_perm, xps, W13, W13_scale, act32, H, offsets, c.E, A, 2 * c.F, c.d, c.F, sched, s,
+                          glu_of(c)));
   MOE_TRY(launch_quantize_fp8(MOE_F32, act32, A, c.F, 1, Act, Act_scale, s));
   return launch_gemm_fp8(false, Act, Act_scale, W2, W2_scale, Y_perm, nullptr, offsets, c.E, A, c.d, c.F, c.F, sched,
                          s);
@@ -368,7 +377,7 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
     d2.N = F; d2.K = c.d; d2.F = F;
     d2.A = dY; d2.lda = c.d;
     d2.B = w2; d2.ldb = F; d2.b_gstride = shared ? 0 : int64_t{1} * c.d * F;
-    d2.Hin = h; d2.ldh = 2 * F;
+    d2.Hin = h; d2.ldh = 2 * F; d2.glu = glu_of(c);
     d2.offsets = off; d2.G = G; d2.range_end = c.T; d2.rows_upper = A;
     // (3) fc1 data gradient: dX = dH W13
     GemmDesc d1{};
@@ -388,7 +397,8 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
       d2.epi = EPI_STORE;
       d2.C = dact; d2.ldc = F;
       MOE_TRY(launch_gemm_fma(d2, s));
-      MOE_TRY(launch_swiglu_bwd_elementwise(static_cast<const float*>(h), dact, static_cast<float*>(dh), rows, F, s));
+      MOE_TRY(launch_swiglu_bwd_elementwise(glu_of(c), static_cast<const float*>(h), dact, static_cast<float*>(dh),
+                                            rows, F, s));
     }
     // (2) fc2 weight gradient dW2 = dY^T Act, queued before dX may overwrite an aliased dY
     if (dw2) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dY, c.d, act, F, dw2, s2));

@@ -57,6 +57,53 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 __device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
+// The experts' gated activation (The Ultimate MoE Training Handbook, §3.4 Activation):
+// kind 0 SwiGLU, silu(g) u; kind 1 the hard clamp, g clamped from above at c and u to
+// [-c, c] before SwiGLU; kind 2 SiTU-GLU, c tanh(g/c) sigma(g) times u, or times
+// cl tanh(u/cl) when cl > 0.
+struct Glu {
+  int kind;
+  float c, cl;
+};
+__device__ __forceinline__ float glu_f(const Glu& p, float g, float u) {
+  if (p.kind == 1) return silu_f(fminf(g, p.c)) * fminf(fmaxf(u, -p.c), p.c);
+  if (p.kind == 2) {
+    const float ul = p.cl > 0.0f ? p.cl * tanhf(u / p.cl) : u;
+    return p.c * tanhf(g / p.c) * sigmoid_f(g) * ul;
+  }
+  return silu_f(g) * u;
+}
+// dgate, dup from dAct (chain rule; a clamp passes the gradient inside its closed interval).
+__device__ __forceinline__ void glu_grad_f(const Glu& p, float g, float u, float da, float& dg, float& du) {
+  if (p.kind == 2) {
+    const float th = tanhf(g / p.c), s = sigmoid_f(g);
+    const float a = p.c * th * s;
+    const float dadg = (1.0f - th * th) * s + p.c * th * s * (1.0f - s);
+    float ul = u, dul = 1.0f;
+    if (p.cl > 0.0f) {
+      const float tl = tanhf(u / p.cl);
+      ul = p.cl * tl;
+      dul = 1.0f - tl * tl;
+    }
+    dg = da * ul * dadg;
+    du = da * a * dul;
+    return;
+  }
+  float gc = g, uc = u;
+  if (p.kind == 1) {
+    gc = fminf(g, p.c);
+    uc = fminf(fmaxf(u, -p.c), p.c);
+  }
+  const float sg = sigmoid_f(gc);
+  dg = da * uc * sg * (1.0f + gc * (1.0f - sg));
+  du = da * gc * sg;
+  if (p.kind == 1) {
+    if (!(g <= p.c)) dg = 0.0f;
+    if (!(fabsf(u) <= p.c)) du = 0.0f;
+  }
+}
+inline Glu glu_of(const moe_config_t& c) { return Glu{c.glu_kind, c.glu_c, c.glu_c_linear}; }
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------------ host status

@@ -167,6 +167,7 @@ struct Fp8Args {
   const int32_t* offsets;
   const int32_t* tile_prefix;
   int G, N, K, F, nN;
+  Glu glu;                // SWIGLU: the gated activation
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -394,8 +395,8 @@ __global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
       if (row >= row_end) continue;
       const float4 gt = L4[r * 32 + (cgate ^ (r & 31))], up = L4[r * 32 + ((cgate + 8) ^ (r & 31))];
       float4 act;
-      act.x = silu_f(gt.x) * up.x; act.y = silu_f(gt.y) * up.y;
-      act.z = silu_f(gt.z) * up.z; act.w = silu_f(gt.w) * up.w;
+      act.x = glu_f(p.glu, gt.x, up.x); act.y = glu_f(p.glu, gt.y, up.y);
+      act.z = glu_f(p.glu, gt.z, up.z); act.w = glu_f(p.glu, gt.w, up.w);
       if (p.H) {
         float* hrow = p.H + static_cast<int64_t>(row) * 2 * p.F;
         *reinterpret_cast<float4*>(hrow + col) = gt;
@@ -451,14 +452,14 @@ size_t fp8_schedule_bytes(int E) { return static_cast<size_t>(E + 1) * 4; }
 // fc1 (+ SwiGLU -> H, Act fp32) when act32 != NULL and C is NULL, else fc2 -> C.
 moe_status_t launch_gemm_fp8(bool swiglu, const uint8_t* A, const float* A_scale, const uint8_t* B,
                              const float* B_scale, float* C, float* H, const int32_t* offsets, int G, int64_t rows_upper,
-                             int N, int K, int F, int32_t* sched, hipStream_t s) {
+                             int N, int K, int F, int32_t* sched, hipStream_t s, Glu glu) {
   if (G > 4096) return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: more than 4096 experts");
   if (K > 128 * kMaxKB || K % 128 || N % 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: K must be a multiple of 128 up to 16384");
   if (static_cast<int64_t>(N) * K >= (int64_t{1} << 31) || rows_upper * K >= (int64_t{1} << 31))
     return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: operand above 2 GB");
   Fp8Args a{};
   a.A = A; a.A_scale = A_scale; a.B = B; a.B_scale = B_scale; a.C = C; a.H = H;
-  a.offsets = offsets; a.tile_prefix = sched; a.G = G; a.N = N; a.K = K; a.F = F;
+  a.offsets = offsets; a.tile_prefix = sched; a.G = G; a.N = N; a.K = K; a.F = F; a.glu = glu;
   a.nN = swiglu ? F / 64 : N / BN;
   fp8_tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, G, sched);
   const int64_t upper = (ceil_div(rows_upper, BM) + G) * a.nN;

@@ -91,24 +91,32 @@ __global__ __launch_bounds__(256) void gemm_fma_kernel(GemmDesc g) {
   }
 }
 
-__global__ void swiglu_fwd_kernel(const float* __restrict__ H, float* __restrict__ Act, int64_t rows, int F) {
+__global__ void swiglu_fwd_kernel(Glu glu, const float* __restrict__ H, float* __restrict__ Act, int64_t rows,
+                                  int F) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= rows * F) return;
   const int64_t r = i / F;
   const int c = (int)(i % F);
   const float gt = H[r * 2 * F + c], up = H[r * 2 * F + F + c];
-  Act[i] = gt / (1.0f + expf(-gt)) * up;
+  Act[i] = glu.kind == 0 ? gt / (1.0f + expf(-gt)) * up : glu_f(glu, gt, up);
 }
 
-__global__ void swiglu_bwd_kernel(const float* __restrict__ H, const float* __restrict__ dAct,
+__global__ void swiglu_bwd_kernel(Glu glu, const float* __restrict__ H, const float* __restrict__ dAct,
                                   float* __restrict__ dH, int64_t rows, int F) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= rows * F) return;
   const int64_t r = i / F;
   const int c = (int)(i % F);
   const float gt = H[r * 2 * F + c], up = H[r * 2 * F + F + c];
-  const float s = 1.0f / (1.0f + expf(-gt));
   const float da = dAct[i];
+  if (glu.kind != 0) {
+    float dg, du;
+    glu_grad_f(glu, gt, up, da, dg, du);
+    dH[r * 2 * F + c] = dg;
+    dH[r * 2 * F + F + c] = du;
+    return;
+  }
+  const float s = 1.0f / (1.0f + expf(-gt));
   dH[r * 2 * F + c] = da * up * s * (1.0f + gt * (1.0f - s));
   dH[r * 2 * F + F + c] = da * gt * s;
 }
@@ -156,16 +164,16 @@ moe_status_t launch_gemm_fma(const GemmDesc& g, hipStream_t s) {
   return check_launch("gemm_fma");
 }
 
-moe_status_t launch_swiglu_fwd_elementwise(const float* H, float* Act, int64_t rows, int F, hipStream_t s) {
+moe_status_t launch_swiglu_fwd_elementwise(Glu glu, const float* H, float* Act, int64_t rows, int F, hipStream_t s) {
   const int64_t n = rows * F;
-  if (n > 0) swiglu_fwd_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, s>>>(H, Act, rows, F);
+  if (n > 0) swiglu_fwd_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, s>>>(glu, H, Act, rows, F);
   return check_launch("swiglu_fwd");
 }
 
-moe_status_t launch_swiglu_bwd_elementwise(const float* H, const float* dAct, float* dH, int64_t rows, int F,
+moe_status_t launch_swiglu_bwd_elementwise(Glu glu, const float* H, const float* dAct, float* dH, int64_t rows, int F,
                                            hipStream_t s) {
   const int64_t n = rows * F;
-  if (n > 0) swiglu_bwd_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, s>>>(H, dAct, dH, rows, F);
+  if (n > 0) swiglu_bwd_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, s>>>(glu, H, dAct, dH, rows, F);
   return check_launch("swiglu_bwd");
 }
 

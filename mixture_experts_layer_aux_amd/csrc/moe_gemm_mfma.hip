@@ -84,6 +84,7 @@ struct MfmaArgs {
   const int32_t* tile_prefix;
   int G, M, N, K, F, range_end, nN, nM;
   int b_rows_bytes;  // K-major B: bytes of one group's weight matrix (bounds the DMA)
+  Glu glu;           // SwiGLU epilogues: the gated activation
 };
 
 // K-contiguous layout: element (r, k) of a stage tile at r * BK + ((k/8) ^ swk(r)) * 8 + k%8
@@ -456,8 +457,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
           *reinterpret_cast<float4*>(hrow + col) = gt;
           *reinterpret_cast<float4*>(hrow + p.F + col) = up;
           uint2 av;
-          av.x = pack_bf16x2(silu_f(gt.x) * up.x, silu_f(gt.y) * up.y);
-          av.y = pack_bf16x2(silu_f(gt.z) * up.z, silu_f(gt.w) * up.w);
+          av.x = pack_bf16x2(glu_f(p.glu, gt.x, up.x), glu_f(p.glu, gt.y, up.y));
+          av.y = pack_bf16x2(glu_f(p.glu, gt.z, up.z), glu_f(p.glu, gt.w, up.w));
           *reinterpret_cast<uint2*>(p.C2 + static_cast<int64_t>(row) * p.ldc2 + col) = av;
         }
       }
@@ -479,11 +480,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
           const float dv[4] = {v.x, v.y, v.z, v.w};
           float dg[4], du[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float sg = sigmoid_f(g[c]);
-            dg[c] = dv[c] * u[c] * sg * (1.0f + g[c] * (1.0f - sg));
-            du[c] = dv[c] * g[c] * sg;
-          }
+          for (int c = 0; c < 4; ++c) glu_grad_f(p.glu, g[c], u[c], dv[c], dg[c], du[c]);
           uint16_t* drow = C + static_cast<int64_t>(row) * p.ldc;
           *reinterpret_cast<uint2*>(drow + col) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
           *reinterpret_cast<uint2*>(drow + p.F + col) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
@@ -534,6 +531,7 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
   a.K = g.K;
   a.F = g.F;
   a.range_end = g.range_end;
+  a.glu = g.glu;
   if (g.b_major == K_MAJOR) {
     const int64_t bytes = static_cast<int64_t>(g.epi == EPI_SWIGLU_FWD ? 2 * g.F : g.N) * g.ldb * 2;
     if (bytes >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: weight matrix above 2 GB");

@@ -78,7 +78,7 @@ size_t fp8_schedule_bytes(int E);
 // swiglu: fc1 of width N = 2F, Act (fp32) -> C [rows, F], H (optional); else C [rows, N]
 moe_status_t launch_gemm_fp8(bool swiglu, const uint8_t* A, const float* A_scale, const uint8_t* B,
                              const float* B_scale, float* C, float* H, const int32_t* offsets, int G, int64_t rows_upper,
-                             int N, int K, int F, int32_t* sched, hipStream_t s);
+                             int N, int K, int F, int32_t* sched, hipStream_t s, Glu glu = Glu{0, 0.0f, 0.0f});
 
 // ---------------------------------------------------------------- GEMMs
 // Storage of an operand: K_MAJOR = [rows][K] (K contiguous), MN_MAJOR = [K][rows].
@@ -105,6 +105,7 @@ struct GemmDesc {
   int64_t ldh;
   const float* bias;            // EPI_STORE_BIAS: [N]
   int F;                        // SwiGLU: offset of the up half (columns of H / rows of W13)
+  Glu glu;                      // SwiGLU epilogues: the gated activation (zero: plain SwiGLU)
   const int32_t* offsets;
   int G;
   int range_end;
@@ -114,8 +115,8 @@ struct GemmDesc {
 // fp32-accumulating FMA GEMM for fp32 (and mixed fp32/bf16) operands; SwiGLU epilogues are
 // separate elementwise kernels on this path.
 moe_status_t launch_gemm_fma(const GemmDesc& g, hipStream_t s);
-moe_status_t launch_swiglu_fwd_elementwise(const float* H, float* Act, int64_t rows, int F, hipStream_t s);
-moe_status_t launch_swiglu_bwd_elementwise(const float* H, const float* dAct, float* dH, int64_t rows, int F,
+moe_status_t launch_swiglu_fwd_elementwise(Glu glu, const float* H, float* Act, int64_t rows, int F, hipStream_t s);
+moe_status_t launch_swiglu_bwd_elementwise(Glu glu, const float* H, const float* dAct, float* dH, int64_t rows, int F,
                                            hipStream_t s);
 
 // bf16 MFMA grouped GEMM (gfx950 v_mfma_f32_32x32x16_bf16), fused epilogues.

@@ -67,6 +67,9 @@ class LayerShape:
     z_coeff: float = 0.0        # router z-loss coefficient
     seq_aux_coeff: float = 0.0  # sequence-wise balance loss coefficient
     seq_len: int = 0            # S of that loss (tokens ordered [S, B])
+    glu: str = "swiglu"         # the experts' gated activation: "swiglu" | "clamp" | "situ"
+    glu_c: float = 0.0          # clamp: the limit; situ: the gate cap
+    glu_c_linear: float = 0.0   # situ: the up cap (0 = none)
 
     @property
     def A(self) -> int:

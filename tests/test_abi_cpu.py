@@ -53,6 +53,9 @@ def test_valid_configs():
     (dict(seq_aux_coeff=1e-4, seq_len=0), L.MOE_ERR_INVALID_ARG),        # the loss needs a sequence length
     (dict(seq_aux_coeff=1e-4, seq_len=3000), L.MOE_ERR_INVALID_ARG),     # that divides T
     (dict(wgrad_dtype=7), L.MOE_ERR_INVALID_ARG),
+    (dict(glu_kind=3), L.MOE_ERR_INVALID_ARG),
+    (dict(glu_kind=L.MOE_GLU_CLAMP, glu_c=0.0), L.MOE_ERR_INVALID_ARG),          # the clamp needs a limit
+    (dict(glu_kind=L.MOE_GLU_SITU, glu_c=4.0, glu_c_linear=-1.0), L.MOE_ERR_INVALID_ARG),
     (dict(wgrad_dtype=L.MOE_BF16, act_dtype=L.MOE_F32), L.MOE_ERR_UNSUPPORTED),  # bf16 gradients need bf16 x
     (dict(d=100), L.MOE_ERR_UNSUPPORTED),
     (dict(F=192), L.MOE_ERR_UNSUPPORTED),             # bf16 needs F % 128 == 0

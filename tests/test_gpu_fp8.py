@@ -218,6 +218,8 @@ FP8_EDGE = {
     "one_token": (replace(SHAPE, name="fp8-one-token", T=1), 13),
     "ragged_chunk": (replace(SHAPE, name="fp8-ragged", T=200), 11),
     "one_hot_expert": (replace(SHAPE, name="fp8-one-hot", T=256, skew_beta=40.0), 11),
+    # SiTU-GLU in the fp8 fc1 epilogue (The Ultimate MoE Training Handbook, §3.4 Activation)
+    "situ_glu": (replace(SHAPE, name="fp8-situ", T=300, glu="situ", glu_c=0.3, glu_c_linear=0.5), 11),
 }
 
 

@@ -119,10 +119,16 @@ def _expert_inputs(shape, cid):
 
 @pytest.mark.parametrize("cid", SMALL_IDS)
 def test_grouped_experts_forward_and_backward(cid):
+    check_grouped_experts(W.SMALL[cid], cid)
+
+
+def check_grouped_experts(shape, cid):
+    """The grouped experts forward and backward of one layer against the oracle (fused and
+    split backward, both weight-gradient dtypes).  Shared by the activation-variant tests."""
     torch = torch_mod()
     L = _lib()
-    shape = W.SMALL[cid]
     cfg = L.config_from_shape(shape)
+    glu = spec_of(shape).glu
     inp, o, r, p = _expert_inputs(shape, cid)
     T, k, E, d, F, Fs, A = shape.T, shape.k, shape.E, shape.d, shape.F, shape.Fs, shape.A
     x = to_dev(inp["x"])
@@ -190,9 +196,9 @@ def test_grouped_experts_forward_and_backward(cid):
         a, b = p.offsets[ex], p.offsets[ex + 1]
         if b == a:
             continue
-        h, act, y = O.swiglu_forward(xp[a:b], o["W13"][ex], o["W2"][ex])
+        h, act, y = O.swiglu_forward(xp[a:b], o["W13"][ex], o["W2"][ex], glu)
         ref["H"][a:b], ref["Act"][a:b], ref["Y"][a:b] = h, act, y
-        g = O.swiglu_backward(xp[a:b], o["W13"][ex], o["W2"][ex], h, dYo[a:b])
+        g = O.swiglu_backward(xp[a:b], o["W13"][ex], o["W2"][ex], h, dYo[a:b], glu)
         ref["dH"][a:b], ref["dX"][a:b], ref["dW13"][ex], ref["dW2"][ex] = g["dH"], g["dX"], g["dW13"], g["dW2"]
     # H (fp32), Act and dH (act dtype): one rounding of values computed from exact inputs
     for name, got, st in (("H", H, "f32"), ("Act", Act, shape.act), ("dH", dH, shape.act)):
@@ -209,8 +215,8 @@ def test_grouped_experts_forward_and_backward(cid):
         check_expert_grads("dW13 (fp32)", fW13_np, ref["dW13"], counts, shape)
         check_expert_grads("dW2 (fp32)", fW2_np, ref["dW2"], counts, shape)
     if Fs:
-        hs, acts, ys = O.swiglu_forward(o["x"], o["W13s"], o["W2s"])
-        gs = O.swiglu_backward(o["x"], o["W13s"], o["W2s"], hs, o["dy"])
+        hs, acts, ys = O.swiglu_forward(o["x"], o["W13s"], o["W2s"], glu)
+        gs = O.swiglu_backward(o["x"], o["W13s"], o["W2s"], hs, o["dy"], glu)
         for name, got, rf, st in (("H_s", H_s, hs, "f32"), ("Act_s", Act_s, acts, shape.act),
                                   ("dH_s", dH_s, gs["dH"], shape.act)):
             q = storage_ok(to_np(got), rf, st)
