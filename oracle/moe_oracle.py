@@ -126,6 +126,40 @@ def topk(keys, k: int):
     return order[:, :k].astype(np.int64)
 
 
+def group_scores(keys, num_groups: int, m: int):
+    """Per token and group of E / num_groups consecutive experts: the sum of the group's m
+    largest keys, added from the largest down (one rounding order on both sides)."""
+    keys = _d(keys)
+    T, E = keys.shape
+    g = -np.sort(-keys.reshape(T, num_groups, E // num_groups), axis=2)
+    out = np.zeros((T, num_groups))
+    for j in range(m):
+        out = out + g[:, :, j]
+    return out
+
+
+def group_limited_topk(keys, k: int, num_groups: int, group_topk: int):
+    """Group-limited top-k ([HB] §3.1 Gating function: group-limited routing picks groups by
+    summing their best scores).  The experts form num_groups groups of consecutive indices;
+    a group's score is the sum of its best k / group_topk keys (the reading taken: enough
+    picks per kept group to fill k); the group_topk best groups are kept (ties to the lower
+    group index); top-k runs over the experts of the kept groups.
+    Returns (idx [T, k], the kept groups [T, group_topk], the group-score margin [T])."""
+    keys = _d(keys)
+    T, E = keys.shape
+    n = E // num_groups
+    gs = group_scores(keys, num_groups, k // group_topk)
+    order = np.argsort(-gs, axis=1, kind="stable")
+    kept = order[:, :group_topk]
+    gsorted = np.take_along_axis(gs, order, axis=1)
+    gmargin = (gsorted[:, group_topk - 1] - gsorted[:, group_topk] if group_topk < num_groups
+               else np.full(T, np.inf))
+    allowed = np.zeros((T, num_groups), dtype=bool)
+    np.put_along_axis(allowed, kept, True, axis=1)
+    masked = np.where(np.repeat(allowed, n, axis=1), keys, -np.inf)
+    return topk(masked, k), kept, gmargin
+
+
 def margins(keys, k: int):
     """key_k - key_{k+1} per token (inf when k == E): how far a token is from a flip."""
     keys = _d(keys)
@@ -489,6 +523,8 @@ class LayerSpec:
     seq_aux_coeff: float = 0.0      # sequence-wise balance loss coefficient
     seq_len: int = 0                # S of that loss (tokens ordered [S, B])
     glu: GLU = SWIGLU               # the experts' gated activation
+    num_groups: int = 0             # group-limited routing: groups of experts (0 = off)
+    group_topk: int = 0             # groups kept per token
 
 
 def route(logits, spec: LayerSpec, expert_bias=None) -> Dict[str, np.ndarray]:
@@ -498,11 +534,22 @@ def route(logits, spec: LayerSpec, expert_bias=None) -> Dict[str, np.ndarray]:
     gives a zero loss.
     """
     keys = selection_keys(logits, spec.score, expert_bias)
-    idx = topk(keys, spec.k)
+    if spec.num_groups:
+        idx, _, gmargin = group_limited_topk(keys, spec.k, spec.num_groups, spec.group_topk)
+        # the keys a token can still pick from, and the nearer of its two decisions
+        allowed = np.zeros(keys.shape, dtype=bool)
+        n = spec.E // spec.num_groups
+        for j in range(spec.k):
+            g = idx[:, j] // n
+            for q in range(n):
+                allowed[np.arange(keys.shape[0]), g * n + q] = True
+        margin = np.minimum(margins(np.where(allowed, keys, -np.inf), spec.k), gmargin)
+    else:
+        idx = topk(keys, spec.k)
+        margin = margins(keys, spec.k)
     w = mixing_weights(logits, idx, spec.score, spec.scaling, spec.pre_softmax)
     counts = expert_counts(idx, spec.E)
-    out = dict(keys=keys, idx=idx, w=w, counts=counts, margin=margins(keys, spec.k),
-               maxvio=max_violation(counts))
+    out = dict(keys=keys, idx=idx, w=w, counts=counts, margin=margin, maxvio=max_violation(counts))
     p = aux_probs(logits, spec.score)
     out["prob_sum"] = p.sum(axis=0)
     out["aux"] = aux_loss(counts, p, spec.k, spec.aux_coeff)

@@ -695,3 +695,43 @@ def test_glu_variants_reduce_to_swiglu():
     Hc = np.array([[5.0, -1.0, 0.3, 7.0]])
     dH = O.glu_backward(Hc, np.ones((1, 2)), O.GLU("clamp", 2.0))
     assert dH[0, 0] == 0.0 and dH[0, 3] == 0.0 and dH[0, 1] != 0.0 and dH[0, 2] != 0.0
+
+
+# ------------------------------------------------------------------ group-limited routing
+
+def test_group_limited_topk_reductions_and_brute_force():
+    from itertools import combinations
+    rng = np.random.default_rng(61)
+    T, E, k, G = 60, 16, 4, 4
+    keys = rng.standard_normal((T, E))
+    # keeping every group is plain top-k
+    idx, kept, _ = O.group_limited_topk(keys, k, G, G)
+    assert np.array_equal(idx, O.topk(keys, k))
+    for gk in (1, 2, 3):
+        idx, kept, gm = O.group_limited_topk(keys, k, G, gk)
+        n, m = E // G, k // gk
+        for t in range(T):
+            # brute force: every subset of gk groups, scored by the sum of each group's m
+            # best keys; the kept subset has the largest total (unique for random keys)
+            score = [sum(sorted(keys[t, g * n:(g + 1) * n], reverse=True)[:m]) for g in range(G)]
+            best = max(combinations(range(G), gk), key=lambda S: sum(score[g] for g in S))
+            assert sorted(kept[t].tolist()) == sorted(best)
+            # every selected expert lies in a kept group, and they are the k best there
+            assert set((idx[t] // n).tolist()) <= set(kept[t].tolist())
+            pool = [e for g in kept[t] for e in range(g * n, (g + 1) * n)]
+            assert sorted(idx[t].tolist()) == sorted(sorted(pool, key=lambda e: -keys[t, e])[:k])
+            assert gm[t] > 0 if gk < G else gm[t] == np.inf
+    # a token whose plain top-4 spans three groups keeps two: the constraint binds
+    row = np.array([[9, 0, 0, 0, 8, 7, 0, 0, 6, 0, 0, 0, 0, 0, 0, 0]], dtype=float)
+    idx, kept, _ = O.group_limited_topk(row, 4, 4, 2)
+    assert sorted(kept[0].tolist()) == [0, 1] and sorted(idx[0].tolist()) == [0, 1, 4, 5]
+    assert sorted(O.topk(row, 4)[0].tolist()) == [0, 4, 5, 8]
+
+
+def test_group_limited_route_margin_covers_the_group_decision():
+    rng = np.random.default_rng(62)
+    logits = rng.standard_normal((50, 16))
+    spec = O.LayerSpec(E=16, k=4, score="sigmoid", num_groups=4, group_topk=2)
+    r = O.route(logits, spec)
+    _, _, gm = O.group_limited_topk(r["keys"], 4, 4, 2)
+    assert np.all(r["margin"] <= gm)
