@@ -101,6 +101,9 @@ typedef enum { MOE_GLU_SWIGLU = 0, MOE_GLU_CLAMP = 1, MOE_GLU_SITU = 2 } moe_glu
  *   scale, a softmax over one selected logit gives the router no gradient);
  *   aux_coeff, z_coeff, seq_aux_coeff finite and >= 0; seq_aux_coeff > 0 needs
  *   seq_len >= 1 dividing T (INVALID_ARG otherwise) and T / seq_len <= 65535;
+ *   num_groups != 0: 1 <= num_groups <= 64 dividing E, 1 <= group_topk <= min(num_groups, k),
+ *   k / group_topk <= E / num_groups and group_topk * E / num_groups >= k; num_groups == 0
+ *   needs group_topk == 0 (INVALID_ARG otherwise);
  *   glu_kind MOE_GLU_CLAMP needs glu_c finite > 0; MOE_GLU_SITU needs glu_c finite > 0 and
  *   glu_c_linear finite >= 0 (INVALID_ARG otherwise);
  *   w_dtype == MOE_FP8_E4M3 (fp8 experts, see moe_quantize_fp8) needs act_dtype == bf16,
@@ -123,6 +126,10 @@ typedef struct moe_config {
   int32_t glu_kind;       /* moe_glu_t: the experts' gated activation ([HB] §3.4 Activation) */
   float glu_c;            /* MOE_GLU_CLAMP: the limit c; MOE_GLU_SITU: the gate cap s */
   float glu_c_linear;     /* MOE_GLU_SITU: the up-half cap s_l (0 = no cap) */
+  int32_t num_groups;     /* group-limited routing ([HB] §3.1): experts in num_groups groups of
+                             consecutive indices, 0 = off */
+  int32_t group_topk;     /* groups a token keeps: those with the largest sum of their best
+                             k / group_topk selection keys (ties to the lower group) */
 } moe_config_t;
 
 typedef struct moe_weights {

@@ -47,7 +47,8 @@ class Config(ctypes.Structure):
                 ("pre_softmax", ctypes.c_int32), ("routed_scaling", ctypes.c_float), ("aux_coeff", ctypes.c_float),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("z_coeff", ctypes.c_float),
                 ("seq_aux_coeff", ctypes.c_float), ("seq_len", ctypes.c_int32), ("wgrad_dtype", ctypes.c_int32),
-                ("glu_kind", ctypes.c_int32), ("glu_c", ctypes.c_float), ("glu_c_linear", ctypes.c_float)]
+                ("glu_kind", ctypes.c_int32), ("glu_c", ctypes.c_float), ("glu_c_linear", ctypes.c_float),
+                ("num_groups", ctypes.c_int32), ("group_topk", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -96,7 +97,7 @@ def _check(status: int) -> None:
 
 def make_config(T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux_coeff=0.0, act="bf16", wq="",
                 pre_softmax=False, z_coeff=0.0, seq_aux_coeff=0.0, seq_len=0, wgrad=None,
-                glu="swiglu", glu_c=0.0, glu_c_linear=0.0) -> Config:
+                glu="swiglu", glu_c=0.0, glu_c_linear=0.0, num_groups=0, group_topk=0) -> Config:
     """wq: "" (expert weights in the activation dtype) or "fp8" (e4m3 codes + block scales).
     wgrad: dtype of the expert weight gradients, "bf16" or "f32"; None = the activation dtype.
     glu: the experts' gated activation, "swiglu", "clamp" (limit glu_c) or "situ" (gate cap
@@ -106,14 +107,15 @@ def make_config(T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux_coeff=0.0
                   routed_scaling=scaling, aux_coeff=aux_coeff, act_dtype=MOE_BF16 if act == "bf16" else MOE_F32,
                   w_dtype=MOE_FP8_E4M3 if wq == "fp8" else 0, z_coeff=z_coeff, seq_aux_coeff=seq_aux_coeff,
                   seq_len=seq_len, wgrad_dtype=MOE_BF16 if wgrad == "bf16" else MOE_F32, glu_kind=_GLUS[glu],
-                  glu_c=glu_c, glu_c_linear=glu_c_linear)
+                  glu_c=glu_c, glu_c_linear=glu_c_linear, num_groups=num_groups, group_topk=group_topk)
 
 
 def config_from_shape(s, **extra) -> Config:
     kw = dict(pre_softmax=getattr(s, "pre_softmax", False), z_coeff=getattr(s, "z_coeff", 0.0),
               seq_aux_coeff=getattr(s, "seq_aux_coeff", 0.0), seq_len=getattr(s, "seq_len", 0),
               glu=getattr(s, "glu", "swiglu"), glu_c=getattr(s, "glu_c", 0.0),
-              glu_c_linear=getattr(s, "glu_c_linear", 0.0))
+              glu_c_linear=getattr(s, "glu_c_linear", 0.0), num_groups=getattr(s, "num_groups", 0),
+              group_topk=getattr(s, "group_topk", 0))
     kw.update(extra)
     return make_config(s.T, s.d, s.E, s.k, s.F, s.Fs, s.score, s.scaling, s.aux_coeff, s.act, getattr(s, "wq", ""),
                        **kw)

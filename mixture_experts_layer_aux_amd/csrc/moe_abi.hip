@@ -170,6 +170,17 @@ moe_status_t validate(const moe_config_t* c) {
   if (!(c->aux_coeff >= 0.0f && c->aux_coeff < INFINITY) || !(c->z_coeff >= 0.0f && c->z_coeff < INFINITY) ||
       !(c->seq_aux_coeff >= 0.0f && c->seq_aux_coeff < INFINITY))
     return fail(MOE_ERR_INVALID_ARG, "loss coefficients must be finite and >= 0");
+  if (c->num_groups != 0) {
+    if (c->num_groups < 1 || c->num_groups > 64 || c->E % c->num_groups)
+      return fail(MOE_ERR_INVALID_ARG, "num_groups=%d must be in [1, 64] and divide E=%d", c->num_groups, c->E);
+    const int n = c->E / c->num_groups;
+    if (c->group_topk < 1 || c->group_topk > c->num_groups || c->group_topk > c->k || c->k / c->group_topk > n ||
+        c->group_topk * n < c->k)
+      return fail(MOE_ERR_INVALID_ARG, "group_topk=%d does not fit k=%d in groups of %d experts", c->group_topk, c->k,
+                  n);
+  } else if (c->group_topk != 0) {
+    return fail(MOE_ERR_INVALID_ARG, "group_topk without num_groups");
+  }
   if (c->glu_kind != MOE_GLU_SWIGLU && c->glu_kind != MOE_GLU_CLAMP && c->glu_kind != MOE_GLU_SITU)
     return fail(MOE_ERR_INVALID_ARG, "unknown gated activation");
   if (c->glu_kind != MOE_GLU_SWIGLU && !(c->glu_c > 0.0f && c->glu_c < INFINITY))
@@ -503,6 +514,7 @@ moe_status_t moe_router_quantile(const moe_config_t* cfg, const float* scores, c
   MOE_TRY(validate(cfg));
   MOE_NEED(scores); MOE_NEED(beta); MOE_NEED(idx); MOE_NEED(alpha); MOE_NEED(ws);
   if (cfg->k >= cfg->E) return fail(MOE_ERR_INVALID_ARG, "quantile routing needs k < E (k=%d E=%d)", cfg->k, cfg->E);
+  if (cfg->num_groups) return fail(MOE_ERR_UNSUPPORTED, "quantile balancing does not take group-limited routing");
   if (beta_local && (static_cast<int64_t>(cfg->T) * cfg->k) % cfg->E)
     return fail(MOE_ERR_INVALID_ARG, "quantile balancing needs T*k (%lld) to be a multiple of E=%d",
                 static_cast<long long>(cfg->T) * cfg->k, cfg->E);

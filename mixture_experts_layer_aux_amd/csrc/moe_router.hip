@@ -62,7 +62,7 @@ template <int EPL>
 __global__ __launch_bounds__(64 * kRouterWaves) void router_topk_kernel(const float* __restrict__ logits,
                                                           const float* __restrict__ expert_bias,
                                                           int T, int E, int k, int score, int pre_softmax,
-                                                          float scaling,
+                                                          float scaling, int ngroups, int gtopk,
                                                           int32_t* __restrict__ idx, float* __restrict__ w,
                                                           int32_t* __restrict__ cnt_part,
                                                           float* __restrict__ prob_part,
@@ -106,6 +106,62 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_topk_kernel(const fl
         l[i] = 0.0f;
         key[i] = -DBL_MAX;
         taken |= 1u << i;
+      }
+    }
+    if (ngroups > 0) {
+      // group-limited routing: a group's score is the sum of its m = k / gtopk best keys,
+      // added from the largest down; lane g holds group g's score
+      const int n = E / ngroups, m = k / gtopk;
+      double gsc = -DBL_MAX;
+      for (int g = 0; g < ngroups; ++g) {
+        uint32_t used = 0;
+        double sum = 0.0;
+        for (int r = 0; r < m; ++r) {
+          double bk = -DBL_MAX;
+          int be = INT_MAX;
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && e / n == g && !(used & (1u << i)) && better(key[i], e, bk, be)) {
+              bk = key[i];
+              be = e;
+            }
+          }
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) {
+            const double ok = __shfl_xor(bk, o, 64);
+            const int oe = __shfl_xor(be, o, 64);
+            if (better(ok, oe, bk, be)) {
+              bk = ok;
+              be = oe;
+            }
+          }
+          if ((be & 63) == lane) used |= 1u << (be >> 6);
+          sum += bk;
+        }
+        if (lane == g) gsc = sum;
+      }
+      // keep the gtopk best groups, ties to the lower group index
+      uint64_t kept = 0;
+      for (int r = 0; r < gtopk; ++r) {
+        const bool live = lane < ngroups && !((kept >> lane) & 1ull);
+        double bk = live ? gsc : -DBL_MAX;
+        int be = live ? lane : INT_MAX;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          const double ok = __shfl_xor(bk, o, 64);
+          const int oe = __shfl_xor(be, o, 64);
+          if (better(ok, oe, bk, be)) {
+            bk = ok;
+            be = oe;
+          }
+        }
+        kept |= 1ull << be;
+      }
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && !((kept >> (e / n)) & 1ull)) taken |= 1u << i;
       }
     }
     int my_e = -1;
@@ -580,7 +636,8 @@ moe_status_t launch_router_topk(const moe_config_t& c, const float* logits, cons
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)) != hipSuccess) \
       return fail(MOE_ERR_HIP, "router: cannot raise the LDS limit to %zu bytes", shm);                 \
     router_topk_kernel<N><<<nblk, 64 * kRouterWaves, shm, s>>>(logits, expert_bias, c.T, c.E, c.k, c.score,          \
-                                                 c.pre_softmax, c.routed_scaling, idx, w, rw.cnt_part,   \
+                                                 c.pre_softmax, c.routed_scaling, c.num_groups,          \
+                                                 c.group_topk, idx, w, rw.cnt_part,                      \
                                                  rw.prob_part, zp, pn);                                  \
     break;
   switch (epl) {

@@ -70,6 +70,8 @@ class LayerShape:
     glu: str = "swiglu"         # the experts' gated activation: "swiglu" | "clamp" | "situ"
     glu_c: float = 0.0          # clamp: the limit; situ: the gate cap
     glu_c_linear: float = 0.0   # situ: the up cap (0 = none)
+    num_groups: int = 0         # group-limited routing: expert groups (0 = off)
+    group_topk: int = 0         # groups kept per token
 
     @property
     def A(self) -> int:

@@ -144,7 +144,8 @@ def routing_moved(idx_gpu, r) -> np.ndarray:
 def spec_of(shape) -> "O.LayerSpec":
     return O.LayerSpec(E=shape.E, k=shape.k, score=shape.score, scaling=shape.scaling, aux_coeff=shape.aux_coeff,
                        pre_softmax=shape.pre_softmax, z_coeff=shape.z_coeff, seq_aux_coeff=shape.seq_aux_coeff,
-                       seq_len=shape.seq_len, glu=O.GLU(shape.glu, shape.glu_c, shape.glu_c_linear))
+                       seq_len=shape.seq_len, glu=O.GLU(shape.glu, shape.glu_c, shape.glu_c_linear),
+                       num_groups=shape.num_groups, group_topk=shape.group_topk)
 
 
 def oracle_inputs(inp, shape):

@@ -54,6 +54,11 @@ def test_valid_configs():
     (dict(seq_aux_coeff=1e-4, seq_len=3000), L.MOE_ERR_INVALID_ARG),     # that divides T
     (dict(wgrad_dtype=7), L.MOE_ERR_INVALID_ARG),
     (dict(glu_kind=3), L.MOE_ERR_INVALID_ARG),
+    (dict(num_groups=7), L.MOE_ERR_INVALID_ARG),                          # 7 does not divide 64
+    (dict(num_groups=8, group_topk=0), L.MOE_ERR_INVALID_ARG),
+    (dict(num_groups=8, group_topk=9), L.MOE_ERR_INVALID_ARG),
+    (dict(num_groups=32, group_topk=2), L.MOE_ERR_INVALID_ARG),           # 2 groups of 2 cannot hold k = 8
+    (dict(group_topk=2), L.MOE_ERR_INVALID_ARG),
     (dict(glu_kind=L.MOE_GLU_CLAMP, glu_c=0.0), L.MOE_ERR_INVALID_ARG),          # the clamp needs a limit
     (dict(glu_kind=L.MOE_GLU_SITU, glu_c=4.0, glu_c_linear=-1.0), L.MOE_ERR_INVALID_ARG),
     (dict(wgrad_dtype=L.MOE_BF16, act_dtype=L.MOE_F32), L.MOE_ERR_UNSUPPORTED),  # bf16 gradients need bf16 x

@@ -41,6 +41,13 @@ _ROUTER_CASES = {
                                    "normal", "normal"),
     "softmax_many_sequences": (W.LayerShape("r", T=2048, d=64, E=512, k=10, F=128, act="f32", z_coeff=1e-3,
                                             seq_aux_coeff=0.01, seq_len=64), "normal", None),
+    # group-limited routing: DeepSeek-V3's 8 groups, 4 kept, with the selection bias; and
+    # quantised logits whose group scores tie, so the lower group index decides
+    "sigmoid_grouped_8x4": (W.LayerShape("r", T=1024, d=64, E=256, k=8, F=128, act="f32", score="sigmoid",
+                                         num_groups=8, group_topk=4, seq_aux_coeff=1e-4, seq_len=256),
+                            "normal", "normal"),
+    "softmax_grouped_ties": (W.LayerShape("r", T=500, d=64, E=64, k=6, F=128, act="f32", num_groups=16,
+                                          group_topk=3, aux_coeff=0.01), "ties", None),
 }
 
 
@@ -171,6 +178,7 @@ _LAYER_CASES = {
                                 aux_coeff=0.05),
     "sigmoid_seq_aux_fp32": replace(W.LAYERS[1], score="sigmoid", aux_coeff=0.1, z_coeff=0.05, seq_aux_coeff=0.5,
                                     seq_len=32),
+    "grouped_deepseek_reduced": replace(W.SMALL[3], num_groups=8, group_topk=4, seq_aux_coeff=0.2, seq_len=256),
 }
 
 
