@@ -525,6 +525,7 @@ class LayerSpec:
     glu: GLU = SWIGLU               # the experts' gated activation
     num_groups: int = 0             # group-limited routing: groups of experts (0 = off)
     group_topk: int = 0             # groups kept per token
+    shared_gate: bool = False       # a sigmoid gate on the shared expert's output
 
 
 def route(logits, spec: LayerSpec, expert_bias=None) -> Dict[str, np.ndarray]:
@@ -564,13 +565,14 @@ def route(logits, spec: LayerSpec, expert_bias=None) -> Dict[str, np.ndarray]:
 
 
 def layer_forward(x, Wg, W13, W2, spec: LayerSpec, bg=None, expert_bias=None,
-                  W13s=None, W2s=None, idx=None) -> Dict[str, object]:
+                  W13s=None, W2s=None, idx=None, Wsg=None) -> Dict[str, object]:
     """The whole layer forward.
 
-    y_t = sum_j w_tj * Expert_{idx_tj}(x_t) + Shared(x_t)
+    y_t = sum_j w_tj * Expert_{idx_tj}(x_t) + gs_t * Shared(x_t)
     ([LC] "An expert transforms numbers inside the model": the weighted sum of the
     selected experts' outputs, coordinate by coordinate; [HB] §3.4 Shared experts:
-    without a gate the shared output is added at weight 1).
+    without a gate the shared output is added at weight 1, gs_t = 1; with the sigmoid gate,
+    gs_t = sigma(x_t . Wsg), Wsg [d]).
     `idx` may be given to evaluate the layer at a fixed routing.  W13 and W2 only need
     per-expert indexing (W13[e] -> [2F, d]), so a lazily converted stack works.
     """
@@ -599,8 +601,9 @@ def layer_forward(x, Wg, W13, W2, spec: LayerSpec, bg=None, expert_bias=None,
     shared = None
     if W13s is not None:
         Hs, Acts, Ys = swiglu_forward(x, W13s, W2s, spec.glu)
-        y = y + Ys
-        shared = dict(H=Hs, Act=Acts, Y=Ys)
+        gs = sigmoid(x @ _d(Wsg)) if spec.shared_gate else np.ones(T)
+        y = y + gs[:, None] * Ys
+        shared = dict(H=Hs, Act=Acts, Y=Ys, gs=gs)
     return dict(logits=logits, route=r, perm=perm, x_perm=xp, H=H, Act=Act, Y_perm=Yp,
                 shared=shared, y=y)
 
@@ -665,8 +668,8 @@ def router_backward(logits, idx, w, dw, spec: LayerSpec, counts=None, daux: floa
 
 
 def layer_backward(fwd: Dict[str, object], x, Wg, W13, W2, dy, spec: LayerSpec,
-                   W13s=None, W2s=None, daux: float = 1.0, sparse_expert_grads: bool = False
-                   ) -> Dict[str, np.ndarray]:
+                   W13s=None, W2s=None, daux: float = 1.0, sparse_expert_grads: bool = False,
+                   Wsg=None) -> Dict[str, np.ndarray]:
     """Gradients of L = sum(dy * y) + daux * aux with respect to every input.
 
     With sparse_expert_grads the expert weight gradients come back as {e: array} for the
@@ -702,9 +705,15 @@ def layer_backward(fwd: Dict[str, object], x, Wg, W13, W2, dy, spec: LayerSpec,
     dx = dXp[rows].sum(axis=1)
     out = dict(dw=dw, dY_perm=dYp, dX_perm=dXp, dH=dH, dW13=dW13, dW2=dW2)
     if W13s is not None:
-        gs = swiglu_backward(x, W13s, W2s, fwd["shared"]["H"], dy, spec.glu)
-        dx = dx + gs["dX"]
-        out.update(dW13s=gs["dW13"], dW2s=gs["dW2"], dH_s=gs["dH"])
+        sh = fwd["shared"]
+        # the gate: dY_s = gs dy;  d gs_t = <dy_t, Y_s[t]>, through sigma: gs (1 - gs)
+        gsh = swiglu_backward(x, W13s, W2s, sh["H"], sh["gs"][:, None] * dy, spec.glu)
+        dx = dx + gsh["dX"]
+        out.update(dW13s=gsh["dW13"], dW2s=gsh["dW2"], dH_s=gsh["dH"])
+        if spec.shared_gate:
+            dl = sh["gs"] * (1.0 - sh["gs"]) * np.sum(dy * sh["Y"], axis=1)
+            out.update(dl_s=dl, dWsg=dl @ x)
+            dx = dx + dl[:, None] * _d(Wsg)[None, :]
     dlogits = router_backward(fwd["logits"], idx, w, dw, spec, counts=r["counts"], daux=daux,
                               seq_counts=r.get("seq_counts"))
     out["dlogits"] = dlogits
@@ -716,10 +725,10 @@ def layer_backward(fwd: Dict[str, object], x, Wg, W13, W2, dy, spec: LayerSpec,
 
 
 def layer_loss(x, Wg, W13, W2, dy, spec: LayerSpec, bg=None, expert_bias=None,
-               W13s=None, W2s=None, daux: float = 1.0) -> float:
+               W13s=None, W2s=None, daux: float = 1.0, Wsg=None) -> float:
     """L = sum(dy * y) + daux * (aux + z + seq_aux), the scalar whose gradient
     layer_backward returns."""
-    f = layer_forward(x, Wg, W13, W2, spec, bg=bg, expert_bias=expert_bias, W13s=W13s, W2s=W2s)
+    f = layer_forward(x, Wg, W13, W2, spec, bg=bg, expert_bias=expert_bias, W13s=W13s, W2s=W2s, Wsg=Wsg)
     r = f["route"]
     return float(np.sum(_d(dy) * f["y"]) + daux * (r["aux"] + r["z"] + r["seq_aux"]))
 

@@ -43,7 +43,8 @@ def _rand_layer(rng, T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux=0.0,
     eb = rng.standard_normal(E) * 0.1 if bias == "expert_bias" else None
     dy = rng.standard_normal((T, d))
     spec = O.LayerSpec(E=E, k=k, score=score, scaling=scaling, aux_coeff=aux, **extra)
-    return dict(x=x, Wg=Wg, W13=W13, W2=W2, W13s=W13s, W2s=W2s, bg=bg, expert_bias=eb, dy=dy), spec
+    Wsg = rng.standard_normal(d) / np.sqrt(d) if spec.shared_gate else None
+    return dict(x=x, Wg=Wg, W13=W13, W2=W2, W13s=W13s, W2s=W2s, bg=bg, expert_bias=eb, dy=dy, Wsg=Wsg), spec
 
 
 # ------------------------------------------------------------------ worked examples
@@ -302,6 +303,10 @@ def test_layer_against_independent_token_loop():
     dict(score="softmax", k=2, aux=0.0, Fs=4, scaling=1.0, bias=None, extra=dict(glu=O.GLU("clamp", 0.35))),
     dict(score="sigmoid", k=2, aux=0.0, Fs=4, scaling=1.0, bias=None, extra=dict(glu=O.GLU("situ", 0.6, 0.5))),
     dict(score="softmax", k=3, aux=0.1, Fs=0, scaling=1.0, bias=None, extra=dict(glu=O.GLU("situ", 0.8, 0.0))),
+    # the sigmoid gate on the shared expert
+    dict(score="softmax", k=2, aux=0.0, Fs=4, scaling=1.0, bias="bg", extra=dict(shared_gate=True)),
+    dict(score="sigmoid", k=2, aux=0.0, Fs=4, scaling=2.5, bias=None,
+         extra=dict(shared_gate=True, glu=O.GLU("clamp", 0.4))),
 ])
 def test_backward_matches_central_differences(case):
     rng = np.random.default_rng(14)
@@ -309,15 +314,17 @@ def test_backward_matches_central_differences(case):
                           scaling=case["scaling"], aux=case["aux"], bias=case["bias"], **case.get("extra", {}))
     keys = O.selection_keys(O.gate_logits(L["x"], L["Wg"], L["bg"]), spec.score, L["expert_bias"])
     assert O.margins(keys, spec.k).min() > 1e-4           # far from a routing flip
-    kw = dict(bg=L["bg"], expert_bias=L["expert_bias"], W13s=L["W13s"], W2s=L["W2s"])
+    kw = dict(bg=L["bg"], expert_bias=L["expert_bias"], W13s=L["W13s"], W2s=L["W2s"], Wsg=L["Wsg"])
     f = O.layer_forward(L["x"], L["Wg"], L["W13"], L["W2"], spec, **kw)
     b = O.layer_backward(f, L["x"], L["Wg"], L["W13"], L["W2"], L["dy"], spec,
-                         W13s=L["W13s"], W2s=L["W2s"], daux=1.0)
+                         W13s=L["W13s"], W2s=L["W2s"], daux=1.0, Wsg=L["Wsg"])
     names = [("x", "dx"), ("Wg", "dWg"), ("W13", "dW13"), ("W2", "dW2")]
     if L["bg"] is not None:
         names.append(("bg", "dbg"))
     if case["Fs"]:
         names += [("W13s", "dW13s"), ("W2s", "dW2s")]
+    if spec.shared_gate:
+        names.append(("Wsg", "dWsg"))
     h = 1e-6
     for pname, gname in names:
         P = L[pname]
@@ -735,3 +742,18 @@ def test_group_limited_route_margin_covers_the_group_decision():
     r = O.route(logits, spec)
     _, _, gm = O.group_limited_topk(r["keys"], 4, 4, 2)
     assert np.all(r["margin"] <= gm)
+
+
+def test_shared_gate_printed_form_and_limits():
+    # the printed forward: output * sigmoid(linear(hidden, gate_weight)), in torch
+    rng = np.random.default_rng(71)
+    L, spec = _rand_layer(rng, T=20, d=8, E=4, k=2, F=8, Fs=6, shared_gate=True)
+    f = O.layer_forward(L["x"], L["Wg"], L["W13"], L["W2"], spec, W13s=L["W13s"], W2s=L["W2s"], Wsg=L["Wsg"])
+    xs = torch.as_tensor(L["x"])
+    shared = _ffn_torch(L["x"], L["W13s"], L["W2s"]) * torch.sigmoid(torch.nn.functional.linear(
+        xs, torch.as_tensor(L["Wsg"])[None, :]))
+    plain = O.layer_forward(L["x"], L["Wg"], L["W13"], L["W2"], O.LayerSpec(E=4, k=2), W13s=L["W13s"], W2s=L["W2s"])
+    np.testing.assert_allclose(f["y"], plain["y"] - plain["shared"]["Y"] + shared.numpy(), rtol=1e-12, atol=1e-12)
+    # a zero gate weight halves the shared output
+    z = O.layer_forward(L["x"], L["Wg"], L["W13"], L["W2"], spec, W13s=L["W13s"], W2s=L["W2s"], Wsg=np.zeros(8))
+    np.testing.assert_allclose(z["y"], plain["y"] - 0.5 * plain["shared"]["Y"], rtol=1e-12, atol=1e-12)
