@@ -104,6 +104,7 @@ typedef enum { MOE_GLU_SWIGLU = 0, MOE_GLU_CLAMP = 1, MOE_GLU_SITU = 2 } moe_glu
  *   num_groups != 0: 1 <= num_groups <= 64 dividing E, 1 <= group_topk <= min(num_groups, k),
  *   k / group_topk <= E / num_groups and group_topk * E / num_groups >= k; num_groups == 0
  *   needs group_topk == 0 (INVALID_ARG otherwise);
+ *   shared_gate is 0 or 1, and 1 needs Fs > 0 (INVALID_ARG otherwise);
  *   glu_kind MOE_GLU_CLAMP needs glu_c finite > 0; MOE_GLU_SITU needs glu_c finite > 0 and
  *   glu_c_linear finite >= 0 (INVALID_ARG otherwise);
  *   w_dtype == MOE_FP8_E4M3 (fp8 experts, see moe_quantize_fp8) needs act_dtype == bf16,
@@ -130,6 +131,8 @@ typedef struct moe_config {
                              consecutive indices, 0 = off */
   int32_t group_topk;     /* groups a token keeps: those with the largest sum of their best
                              k / group_topk selection keys (ties to the lower group) */
+  int32_t shared_gate;    /* 1: the shared expert's output is scaled by sigma(x . Wsg)
+                             ([HB] §3.4 Shared experts, the gated form); needs Fs > 0 */
 } moe_config_t;
 
 typedef struct moe_weights {
@@ -142,6 +145,7 @@ typedef struct moe_weights {
   const void* W2s;          /* [d, Fs],  NULL when Fs == 0 */
   const float* W13_scale;   /* fp8 weights only: [E, 2F/128, d/128] fp32 block scales */
   const float* W2_scale;    /* fp8 weights only: [E, d/128, F/128] fp32 block scales */
+  const float* Wsg;         /* [d] fp32 gate weight of the shared expert, when shared_gate */
 } moe_weights_t;
 
 /* Tensors the forward writes and the backward reads (all caller-owned). */
@@ -163,6 +167,7 @@ typedef struct moe_saved {
   float* x_perm_scale; /* fp8 weights only: [A, d/128], the scales of x_perm's e4m3 rows */
   float* Act_scale;    /* fp8 weights only: [A, F/128], the scales of Act's e4m3 rows */
   int32_t* seq_counts; /* [B, E] tokens of sequence b routed to e; needed when seq_aux_coeff > 0 */
+  float* gs;           /* [T] the shared expert's gate values, when shared_gate */
 } moe_saved_t;
 
 /* Gradients written by moe_layer_bwd (overwritten, not accumulated). */
@@ -173,6 +178,7 @@ typedef struct moe_grads {
   void* dW2;    /* [E, d, F] */
   void* dW13s;  /* [2Fs, d] or NULL when Fs == 0 */
   void* dW2s;   /* [d, Fs]  or NULL */
+  float* dWsg;  /* [d] fp32, when shared_gate */
 } moe_grads_t;
 
 const char* moe_status_string(moe_status_t status);
@@ -261,10 +267,22 @@ moe_status_t moe_grouped_gemm_swiglu(const moe_config_t* cfg, const void* x_perm
 
 /* Weighted combine ([LC] "An expert transforms numbers inside the model": the weighted
  * sum of the selected outputs, coordinate by coordinate; [HB] §3.4 Shared experts: the
- * shared output is added at weight 1):
- *   y[t] = sum_j w[t, j] * Y_perm[row_of[t, j]] (+ Y_s[t]), fp32 accumulation, slot order. */
+ * shared output is added at weight 1, or at its sigmoid gate gs[t]):
+ *   y[t] = sum_j w[t, j] * Y_perm[row_of[t, j]] (+ gs[t] * Y_s[t]), fp32 accumulation, slot
+ *   order.  gs [T] NULL means 1. */
 moe_status_t moe_unpermute_combine(const moe_config_t* cfg, const float* Y_perm, const int32_t* row_of,
-                                   const float* w, const float* Y_s, float* y, void* stream);
+                                   const float* w, const float* Y_s, const float* gs, float* y, void* stream);
+
+/* The shared expert's sigmoid gate ([HB] §3.4 Shared experts: output * sigmoid(x Wsg)):
+ * gs[t] = sigma(<x[t], Wsg>), the dot in fp32.  x act dtype [T, d], Wsg [d] fp32 (16-byte
+ * aligned), gs [T] fp32. */
+moe_status_t moe_shared_gate(const moe_config_t* cfg, const void* x, const float* Wsg, float* gs, void* stream);
+
+/* Its weight gradient: dWsg = sum_t dl_s[t] x[t] (dl_s from moe_unpermute_combine_bwd),
+ * partial sums over 256-token chunks then over the chunks, in a fixed order.  ws: the
+ * backward workspace. */
+moe_status_t moe_shared_gate_bwd(const moe_config_t* cfg, const void* x, const float* dl_s, float* dWsg, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /* Whole forward: gate logits, router, permute, grouped experts (+ shared), combine.
  * Fills *saved for the backward.  stats as in moe_router_topk (NULL ok); saved->seq_counts
@@ -282,11 +300,13 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* weights
  * expert-selection answer key"). */
 
 /* dY_perm[row_of[t, j]] = w[t, j] * dy[t] (act dtype);  dw[t, j] = <dy[t], Y_perm[row_of[t, j]]>;
- * dY_s (NULL ok) = dy in the act dtype: the shared expert's upstream gradient.
+ * dY_s (NULL ok) = dy in the act dtype: the shared expert's upstream gradient; with its
+ * gate (gs, Y_s and dl_s all given) dY_s = gs[t] dy[t] and
+ * dl_s[t] = gs (1 - gs) <dy[t], Y_s[t]>, the gradient of the gate's logit.
  * dY_perm may be NULL when only dw is wanted (fp8 experts, whose weights are frozen). */
 moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const float* dy, const float* Y_perm,
                                        const int32_t* row_of, const float* w, void* dY_perm, float* dw,
-                                       void* dY_s, void* stream);
+                                       void* dY_s, const float* gs, const float* Y_s, float* dl_s, void* stream);
 
 /* Expert backward, per expert e on its rows (and the shared expert on all T rows with
  * upstream gradient dY_s [T, d] act dtype, when Fs > 0):
@@ -350,10 +370,12 @@ moe_status_t moe_grouped_gemm_swiglu_fp8(const moe_config_t* cfg, const uint8_t*
                                          const uint8_t* W2, const float* W2_scale, float* H, uint8_t* Act,
                                          float* Act_scale, float* Y_perm, void* ws, size_t ws_bytes, void* stream);
 
-/* Unpermute-reduce: dx[t] = sum_j dX_perm[row_of[t, j]] (+ dx_s[t]) (+ dx_r[t]),
- * fp32 accumulation in that order.  All fp32; dx_s and dx_r may be NULL. */
+/* Unpermute-reduce: dx[t] = sum_j dX_perm[row_of[t, j]] (+ dx_s[t]) (+ dx_r[t])
+ * (+ dl_s[t] * Wsg), fp32 accumulation in that order.  All fp32; dx_s, dx_r may be NULL;
+ * dl_s and Wsg (the shared gate's input gradient) both or neither. */
 moe_status_t moe_permute_bwd(const moe_config_t* cfg, const float* dX_perm, const int32_t* row_of,
-                             const float* dx_s, const float* dx_r, float* dx, void* stream);
+                             const float* dx_s, const float* dx_r, const float* dl_s, const float* Wsg, float* dx,
+                             void* stream);
 
 /* Router backward: dlogits [T, E] from dw [T, k] through the weights of the selected
  * experts (pre_softmax: through the full softmax), plus daux times the gradients of the

@@ -31,7 +31,7 @@ EXPORTED = (
     "moe_unpermute_combine_bwd", "moe_grouped_gemm_swiglu_bwd", "moe_grouped_wgrad", "moe_permute_bwd", "moe_router_bwd",
     "moe_quantize_fp8", "moe_permute_fp8", "moe_grouped_gemm_swiglu_fp8",
     "moe_gate_logits_bwd", "moe_layer_bwd", "moe_expert_bias_update", "moe_router_quantile",
-    "moe_quantile_bias_update",
+    "moe_quantile_bias_update", "moe_shared_gate", "moe_shared_gate_bwd",
 )
 
 
@@ -48,7 +48,7 @@ class Config(ctypes.Structure):
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("z_coeff", ctypes.c_float),
                 ("seq_aux_coeff", ctypes.c_float), ("seq_len", ctypes.c_int32), ("wgrad_dtype", ctypes.c_int32),
                 ("glu_kind", ctypes.c_int32), ("glu_c", ctypes.c_float), ("glu_c_linear", ctypes.c_float),
-                ("num_groups", ctypes.c_int32), ("group_topk", ctypes.c_int32)]
+                ("num_groups", ctypes.c_int32), ("group_topk", ctypes.c_int32), ("shared_gate", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -56,17 +56,17 @@ _P = ctypes.c_void_p
 
 class Weights(ctypes.Structure):
     _fields_ = [("Wg", _P), ("bg", _P), ("expert_bias", _P), ("W13", _P), ("W2", _P), ("W13s", _P), ("W2s", _P),
-                ("W13_scale", _P), ("W2_scale", _P)]
+                ("W13_scale", _P), ("W2_scale", _P), ("Wsg", _P)]
 
 
 class Saved(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("logits", "idx", "w", "counts", "offsets", "row_of", "token_of", "x_perm", "H",
                                   "Act", "Y_perm", "H_s", "Act_s", "Y_s", "x_perm_scale", "Act_scale",
-                                  "seq_counts")]
+                                  "seq_counts", "gs")]
 
 
 class Grads(ctypes.Structure):
-    _fields_ = [(n, _P) for n in ("dWg", "dbg", "dW13", "dW2", "dW13s", "dW2s")]
+    _fields_ = [(n, _P) for n in ("dWg", "dbg", "dW13", "dW2", "dW13s", "dW2s", "dWsg")]
 
 
 _lib = None
@@ -97,7 +97,7 @@ def _check(status: int) -> None:
 
 def make_config(T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux_coeff=0.0, act="bf16", wq="",
                 pre_softmax=False, z_coeff=0.0, seq_aux_coeff=0.0, seq_len=0, wgrad=None,
-                glu="swiglu", glu_c=0.0, glu_c_linear=0.0, num_groups=0, group_topk=0) -> Config:
+                glu="swiglu", glu_c=0.0, glu_c_linear=0.0, num_groups=0, group_topk=0, shared_gate=False) -> Config:
     """wq: "" (expert weights in the activation dtype) or "fp8" (e4m3 codes + block scales).
     wgrad: dtype of the expert weight gradients, "bf16" or "f32"; None = the activation dtype.
     glu: the experts' gated activation, "swiglu", "clamp" (limit glu_c) or "situ" (gate cap
@@ -107,7 +107,8 @@ def make_config(T, d, E, k, F, Fs=0, score="softmax", scaling=1.0, aux_coeff=0.0
                   routed_scaling=scaling, aux_coeff=aux_coeff, act_dtype=MOE_BF16 if act == "bf16" else MOE_F32,
                   w_dtype=MOE_FP8_E4M3 if wq == "fp8" else 0, z_coeff=z_coeff, seq_aux_coeff=seq_aux_coeff,
                   seq_len=seq_len, wgrad_dtype=MOE_BF16 if wgrad == "bf16" else MOE_F32, glu_kind=_GLUS[glu],
-                  glu_c=glu_c, glu_c_linear=glu_c_linear, num_groups=num_groups, group_topk=group_topk)
+                  glu_c=glu_c, glu_c_linear=glu_c_linear, num_groups=num_groups, group_topk=group_topk,
+                  shared_gate=int(bool(shared_gate)))
 
 
 def config_from_shape(s, **extra) -> Config:
@@ -115,7 +116,7 @@ def config_from_shape(s, **extra) -> Config:
               seq_aux_coeff=getattr(s, "seq_aux_coeff", 0.0), seq_len=getattr(s, "seq_len", 0),
               glu=getattr(s, "glu", "swiglu"), glu_c=getattr(s, "glu_c", 0.0),
               glu_c_linear=getattr(s, "glu_c_linear", 0.0), num_groups=getattr(s, "num_groups", 0),
-              group_topk=getattr(s, "group_topk", 0))
+              group_topk=getattr(s, "group_topk", 0), shared_gate=getattr(s, "shared_gate", False))
     kw.update(extra)
     return make_config(s.T, s.d, s.E, s.k, s.F, s.Fs, s.score, s.scaling, s.aux_coeff, s.act, getattr(s, "wq", ""),
                        **kw)
@@ -252,15 +253,31 @@ def grouped_gemm_swiglu(cfg, x_perm, offsets, W13, W2, x, W13s, W2s, H, Act, Y_p
         _P(wp), ctypes.c_size_t(wn), _P(_stream(stream))))
 
 
-def unpermute_combine(cfg, Y_perm, row_of, w, Y_s, y, stream=None):
+def unpermute_combine(cfg, Y_perm, row_of, w, Y_s, y, stream=None, gs=None):
     A, f32 = cfg.T * cfg.k, torch.float32
     _check(load().moe_unpermute_combine(ctypes.byref(cfg), _P(_ptr(Y_perm, f32, A * cfg.d, "Y_perm")),
                                         _P(_ptr(row_of, torch.int32, A, "row_of")), _P(_ptr(w, f32, A, "w")),
-                                        _P(_ptr(Y_s, f32, cfg.T * cfg.d, "Y_s")), _P(_ptr(y, f32, cfg.T * cfg.d, "y")),
-                                        _P(_stream(stream))))
+                                        _P(_ptr(Y_s, f32, cfg.T * cfg.d, "Y_s")), _P(_ptr(gs, f32, cfg.T, "gs")),
+                                        _P(_ptr(y, f32, cfg.T * cfg.d, "y")), _P(_stream(stream))))
 
 
-def unpermute_combine_bwd(cfg, dy, Y_perm, row_of, w, dY_perm, dw, dY_s=None, stream=None):
+def shared_gate(cfg, x, Wsg, gs, stream=None):
+    """gs = sigmoid(x Wsg): the shared expert's gate."""
+    _check(load().moe_shared_gate(ctypes.byref(cfg), _P(_ptr(x, act_dtype(cfg), cfg.T * cfg.d, "x")),
+                                  _P(_ptr(Wsg, torch.float32, cfg.d, "Wsg")), _P(_ptr(gs, torch.float32, cfg.T, "gs")),
+                                  _P(_stream(stream))))
+
+
+def shared_gate_bwd(cfg, x, dl_s, dWsg, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(load().moe_shared_gate_bwd(ctypes.byref(cfg), _P(_ptr(x, act_dtype(cfg), cfg.T * cfg.d, "x")),
+                                      _P(_ptr(dl_s, torch.float32, cfg.T, "dl_s")),
+                                      _P(_ptr(dWsg, torch.float32, cfg.d, "dWsg")), _P(wp), ctypes.c_size_t(wn),
+                                      _P(_stream(stream))))
+
+
+def unpermute_combine_bwd(cfg, dy, Y_perm, row_of, w, dY_perm, dw, dY_s=None, stream=None, gs=None, Y_s=None,
+                          dl_s=None):
     ad, A, f32 = act_dtype(cfg), cfg.T * cfg.k, torch.float32
     _check(load().moe_unpermute_combine_bwd(ctypes.byref(cfg), _P(_ptr(dy, f32, cfg.T * cfg.d, "dy")),
                                             _P(_ptr(Y_perm, f32, A * cfg.d, "Y_perm")),
@@ -268,7 +285,8 @@ def unpermute_combine_bwd(cfg, dy, Y_perm, row_of, w, dY_perm, dw, dY_s=None, st
                                             _P(_ptr(w, f32, A, "w")),
                                             _P(_ptr(dY_perm, ad, A * cfg.d, "dY_perm")),
                                             _P(_ptr(dw, f32, A, "dw")), _P(_ptr(dY_s, ad, cfg.T * cfg.d, "dY_s")),
-                                            _P(_stream(stream))))
+                                            _P(_ptr(gs, f32, cfg.T, "gs")), _P(_ptr(Y_s, f32, cfg.T * cfg.d, "Y_s")),
+                                            _P(_ptr(dl_s, f32, cfg.T, "dl_s")), _P(_stream(stream))))
 
 
 def grouped_gemm_swiglu_bwd(cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, dX_perm, dW13, dW2, x, W13s, W2s,
@@ -341,12 +359,13 @@ def grouped_gemm_swiglu_fp8(cfg, x_perm, x_perm_scale, offsets, W13, W13_scale, 
         _P(_ptr(Y_perm, f32, A * d, "Y_perm")), _P(wp), ctypes.c_size_t(wn), _P(_stream(stream))))
 
 
-def permute_bwd(cfg, dX_perm, row_of, dx_s, dx_r, dx, stream=None):
+def permute_bwd(cfg, dX_perm, row_of, dx_s, dx_r, dx, stream=None, dl_s=None, Wsg=None):
     ad, A = act_dtype(cfg), cfg.T * cfg.k
     _check(load().moe_permute_bwd(ctypes.byref(cfg), _P(_ptr(dX_perm, torch.float32, A * cfg.d, "dX_perm")),
                                   _P(_ptr(row_of, torch.int32, A, "row_of")),
                                   _P(_ptr(dx_s, torch.float32, cfg.T * cfg.d, "dx_s")),
                                   _P(_ptr(dx_r, torch.float32, cfg.T * cfg.d, "dx_r")),
+                                  _P(_ptr(dl_s, torch.float32, cfg.T, "dl_s")), _P(_ptr(Wsg, torch.float32, cfg.d, "Wsg")),
                                   _P(_ptr(dx, torch.float32, cfg.T * cfg.d, "dx")), _P(_stream(stream))))
 
 
@@ -380,7 +399,8 @@ def _weights_struct(cfg, W: Dict[str, torch.Tensor]) -> Weights:
                    W13=_ptr(W["W13"], wd, E * 2 * F * d, "W13"), W2=_ptr(W["W2"], wd, E * d * F, "W2"),
                    W13s=_ptr(W.get("W13s"), ad, 2 * Fs * d, "W13s"), W2s=_ptr(W.get("W2s"), ad, d * Fs, "W2s"),
                    W13_scale=_ptr(W.get("W13_scale"), torch.float32, E * (2 * F // 128) * (d // 128), "W13_scale"),
-                   W2_scale=_ptr(W.get("W2_scale"), torch.float32, E * (d // 128) * (F // 128), "W2_scale"))
+                   W2_scale=_ptr(W.get("W2_scale"), torch.float32, E * (d // 128) * (F // 128), "W2_scale"),
+                   Wsg=_ptr(W.get("Wsg"), torch.float32, d, "Wsg"))
 
 
 def _saved_struct(cfg, S: Dict[str, torch.Tensor]) -> Saved:
@@ -391,7 +411,7 @@ def _saved_struct(cfg, S: Dict[str, torch.Tensor]) -> Saved:
                 x_perm=(qd, A * d), H=(torch.float32, A * 2 * F), Act=(qd, A * F), Y_perm=(torch.float32, A * d),
                 H_s=(torch.float32, T * 2 * Fs), Act_s=(ad, T * Fs), Y_s=(torch.float32, T * d),
                 x_perm_scale=(torch.float32, A * (d // 128)), Act_scale=(torch.float32, A * (F // 128)),
-                seq_counts=(torch.int32, num_sequences(cfg) * E))
+                seq_counts=(torch.int32, num_sequences(cfg) * E), gs=(torch.float32, T))
     return Saved(**{n: _ptr(S.get(n), dt, ne, n) for n, (dt, ne) in spec.items()})
 
 
@@ -415,7 +435,8 @@ def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None):
     wd = wgrad_dtype(cfg)
     gs = Grads(dWg=_ptr(G["dWg"], f32, E * d, "dWg"), dbg=_ptr(G.get("dbg"), f32, E, "dbg"),
                dW13=_ptr(G.get("dW13"), wd, E * 2 * F * d, "dW13"), dW2=_ptr(G.get("dW2"), wd, E * d * F, "dW2"),
-               dW13s=_ptr(G.get("dW13s"), wd, 2 * Fs * d, "dW13s"), dW2s=_ptr(G.get("dW2s"), wd, d * Fs, "dW2s"))
+               dW13s=_ptr(G.get("dW13s"), wd, 2 * Fs * d, "dW13s"), dW2s=_ptr(G.get("dW2s"), wd, d * Fs, "dW2s"),
+               dWsg=_ptr(G.get("dWsg"), f32, d, "dWsg"))
     _check(load().moe_layer_bwd(ctypes.byref(cfg), ctypes.byref(ws_), ctypes.byref(ss),
                                 _P(_ptr(x, ad, cfg.T * d, "x")), _P(_ptr(dy, f32, cfg.T * d, "dy")),
                                 ctypes.c_float(daux), _P(_ptr(dx, f32, cfg.T * d, "dx")), ctypes.byref(gs), _P(wp),
@@ -438,6 +459,8 @@ def alloc_saved(cfg: Config, device="cuda") -> Dict[str, torch.Tensor]:
         S.update(H_s=e(T, 2 * Fs, dt=torch.float32), Act_s=e(T, Fs), Y_s=e(T, d, dt=torch.float32))
     if num_sequences(cfg):
         S["seq_counts"] = e(num_sequences(cfg), E, dt=torch.int32)
+    if cfg.shared_gate:
+        S["gs"] = e(T, dt=torch.float32)
     return S
 
 
@@ -451,6 +474,8 @@ def alloc_grads(cfg: Config, device="cuda", with_dbg=False) -> Dict[str, torch.T
         G["dbg"] = torch.empty(E, dtype=f32, device=device)
     if Fs:
         G.update(dW13s=torch.empty(2 * Fs, d, dtype=wd, device=device), dW2s=torch.empty(d, Fs, dtype=wd, device=device))
+    if cfg.shared_gate:
+        G["dWsg"] = torch.empty(d, dtype=f32, device=device)
     return G
 
 

@@ -108,6 +108,8 @@ struct BwdWs {
   void* dH_s;      // [T, 2Fs] act
   void* dx_s;      // [T, d] fp32
   void* dY_s;      // [T, d] act: the shared expert's upstream gradient
+  float* dl_s;     // [T]: the shared gate's logit gradient
+  float* sg_part;  // shared_gate_part_bytes: partial sums of its weight gradient
   float* dact;     // fp32 path: [max(A, T), max(F, Fs)]
   int32_t* sched;  // [E + 1]
   void* gate;      // router GEMM scratch (gate_bwd_ws_bytes)
@@ -133,6 +135,8 @@ BwdWs carve_bwd(const moe_config_t& c, void* base) {
   w.dH_s = c.Fs ? take(T * 2 * c.Fs * eb) : nullptr;
   w.dx_s = c.Fs ? take(T * c.d * 4) : nullptr;
   w.dY_s = c.Fs ? take(T * c.d * eb) : nullptr;
+  w.dl_s = c.shared_gate ? reinterpret_cast<float*>(take(T * 4)) : nullptr;
+  w.sg_part = c.shared_gate ? reinterpret_cast<float*>(take(shared_gate_part_bytes(c))) : nullptr;
   w.dact = c.act_dtype == MOE_F32 ? reinterpret_cast<float*>(take(std::max(A, T) * std::max(c.F, c.Fs) * 4)) : nullptr;
   w.sched = reinterpret_cast<int32_t*>(take(mfma_schedule_bytes(c.E)));
   w.gate = take(gate_bwd_ws_bytes(c));
@@ -170,6 +174,8 @@ moe_status_t validate(const moe_config_t* c) {
   if (!(c->aux_coeff >= 0.0f && c->aux_coeff < INFINITY) || !(c->z_coeff >= 0.0f && c->z_coeff < INFINITY) ||
       !(c->seq_aux_coeff >= 0.0f && c->seq_aux_coeff < INFINITY))
     return fail(MOE_ERR_INVALID_ARG, "loss coefficients must be finite and >= 0");
+  if (c->shared_gate != 0 && c->shared_gate != 1) return fail(MOE_ERR_INVALID_ARG, "shared_gate must be 0 or 1");
+  if (c->shared_gate && c->Fs == 0) return fail(MOE_ERR_INVALID_ARG, "shared_gate needs a shared expert (Fs > 0)");
   if (c->num_groups != 0) {
     if (c->num_groups < 1 || c->num_groups > 64 || c->E % c->num_groups)
       return fail(MOE_ERR_INVALID_ARG, "num_groups=%d must be in [1, 64] and divide E=%d", c->num_groups, c->E);
@@ -559,12 +565,29 @@ moe_status_t moe_grouped_gemm_swiglu(const moe_config_t* cfg, const void* x_perm
 }
 
 moe_status_t moe_unpermute_combine(const moe_config_t* cfg, const float* Y_perm, const int32_t* row_of,
-                                   const float* w, const float* Y_s, float* y, void* stream) {
+                                   const float* w, const float* Y_s, const float* gs, float* y, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED16(Y_perm); MOE_NEED(row_of); MOE_NEED(w); MOE_NEED16(y);
   if (Y_s && !aligned16(Y_s)) return fail(MOE_ERR_INVALID_ARG, "Y_s is not 16-byte aligned");
-  return launch_combine(*cfg, static_cast<const float*>(Y_perm), row_of, w, static_cast<const float*>(Y_s),
+  if (gs && !Y_s) return fail(MOE_ERR_INVALID_ARG, "gs without Y_s");
+  return launch_combine(*cfg, static_cast<const float*>(Y_perm), row_of, w, static_cast<const float*>(Y_s), gs,
                         static_cast<float*>(y), S(stream));
+}
+
+moe_status_t moe_shared_gate(const moe_config_t* cfg, const void* x, const float* Wsg, float* gs, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED16(x); MOE_NEED16(Wsg); MOE_NEED(gs);
+  return launch_shared_gate(*cfg, x, Wsg, gs, S(stream));
+}
+
+moe_status_t moe_shared_gate_bwd(const moe_config_t* cfg, const void* x, const float* dl_s, float* dWsg, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED(x); MOE_NEED(dl_s); MOE_NEED(dWsg); MOE_NEED(ws);
+  if (!cfg->shared_gate) return fail(MOE_ERR_INVALID_ARG, "moe_shared_gate_bwd needs shared_gate = 1");
+  const BwdWs bw = carve_bwd(*cfg, ws);
+  MOE_TRY(need_ws(ws_bytes, bw.bytes, __func__));
+  return launch_shared_gate_bwd(*cfg, x, dl_s, dWsg, bw.sg_part, S(stream));
 }
 
 moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, const void* x, const moe_saved_t* sv,
@@ -588,11 +611,13 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   if (W->expert_bias && cfg->score == MOE_SOFTMAX)
     return fail(MOE_ERR_UNSUPPORTED, "the expert bias is provided for sigmoid and sqrt(softplus) scores only");
   if (cfg->seq_aux_coeff != 0.0f) MOE_NEED(sv->seq_counts);
+  if (cfg->shared_gate) { MOE_NEED16(W->Wsg); MOE_NEED(sv->gs); }
   const FwdWs fw = carve_fwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
   const moe_config_t& c = *cfg;
   hipStream_t s = S(stream);
   MOE_TRY(run_gate(c, x, W->Wg, W->bg, sv->logits, fw.gate, s));
+  if (c.shared_gate) MOE_TRY(launch_shared_gate(c, x, W->Wsg, sv->gs, s));
   MOE_TRY(launch_router_topk(c, sv->logits, W->expert_bias, sv->idx, sv->w, sv->counts, fw.prob_sum, stats,
                              sv->seq_counts, router_ws(fw), s));
   if (fp8) {
@@ -606,7 +631,7 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, cons
                             static_cast<const uint8_t*>(W->W13), W->W13_scale, static_cast<const uint8_t*>(W->W2),
                             W->W2_scale, static_cast<float*>(sv->H), static_cast<uint8_t*>(sv->Act), sv->Act_scale,
                             static_cast<float*>(sv->Y_perm), fw.act32, fw.sched, s));
-    return launch_combine(c, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, nullptr,
+    return launch_combine(c, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, nullptr, nullptr,
                           static_cast<float*>(y), s);
   }
   MOE_TRY(launch_permute(c, x, sv->idx, sv->offsets, sv->row_of, sv->token_of, sv->x_perm, fw.cnt_part, fw.blk_base,
@@ -614,17 +639,21 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_TRY(run_experts_fwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, x, W->W13s, W->W2s, sv->H, sv->Act,
                           sv->Y_perm, sv->H_s, sv->Act_s, sv->Y_s, fw.sched, s));
   return launch_combine(c, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w,
-                        c.Fs ? static_cast<const float*>(sv->Y_s) : nullptr, static_cast<float*>(y), s);
+                        c.Fs ? static_cast<const float*>(sv->Y_s) : nullptr, c.shared_gate ? sv->gs : nullptr,
+                        static_cast<float*>(y), s);
 }
 
 moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const float* dy, const float* Y_perm,
                                        const int32_t* row_of, const float* w, void* dY_perm, float* dw,
-                                       void* dY_s, void* stream) {
+                                       void* dY_s, const float* gs, const float* Y_s, float* dl_s, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED16(dy); MOE_NEED16(Y_perm); MOE_NEED(row_of); MOE_NEED(w); MOE_NEED(dw);
   if (dY_perm && !aligned16(dY_perm)) return fail(MOE_ERR_INVALID_ARG, "dY_perm is not 16-byte aligned");
   if (dY_s && !aligned16(dY_s)) return fail(MOE_ERR_INVALID_ARG, "dY_s is not 16-byte aligned");
-  return launch_combine_bwd(*cfg, dy, Y_perm, row_of, w, dY_perm, dw, dY_s, S(stream));
+  if ((gs != nullptr) != (dl_s != nullptr) || (gs != nullptr) != (Y_s != nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "the shared gate needs gs, Y_s and dl_s together");
+  if (Y_s && !aligned16(Y_s)) return fail(MOE_ERR_INVALID_ARG, "Y_s is not 16-byte aligned");
+  return launch_combine_bwd(*cfg, dy, Y_perm, row_of, w, dY_perm, dw, dY_s, gs, Y_s, dl_s, S(stream));
 }
 
 moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
@@ -705,12 +734,14 @@ moe_status_t moe_grouped_gemm_swiglu_fp8(const moe_config_t* cfg, const uint8_t*
 }
 
 moe_status_t moe_permute_bwd(const moe_config_t* cfg, const float* dX_perm, const int32_t* row_of, const float* dx_s,
-                             const float* dx_r, float* dx, void* stream) {
+                             const float* dx_r, const float* dl_s, const float* Wsg, float* dx, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED16(dX_perm); MOE_NEED(row_of); MOE_NEED16(dx);
   if (dx_s && !aligned16(dx_s)) return fail(MOE_ERR_INVALID_ARG, "dx_s is not 16-byte aligned");
   if (dx_r && !aligned16(dx_r)) return fail(MOE_ERR_INVALID_ARG, "dx_r is not 16-byte aligned");
-  return launch_unpermute_reduce(*cfg, dX_perm, row_of, dx_s, dx_r, dx, S(stream));
+  if ((dl_s != nullptr) != (Wsg != nullptr)) return fail(MOE_ERR_INVALID_ARG, "dl_s and Wsg go together");
+  if (Wsg && !aligned16(Wsg)) return fail(MOE_ERR_INVALID_ARG, "Wsg is not 16-byte aligned");
+  return launch_unpermute_reduce(*cfg, dX_perm, row_of, dx_s, dx_r, dl_s, Wsg, dx, S(stream));
 }
 
 moe_status_t moe_router_bwd(const moe_config_t* cfg, const float* logits, const int32_t* idx, const float* w,
@@ -752,7 +783,7 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
     const moe_config_t& c = *cfg;
     hipStream_t s = S(stream);
     MOE_TRY(launch_combine_bwd(c, dy, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, nullptr, bw.dw,
-                               nullptr, s));
+                               nullptr, nullptr, nullptr, nullptr, s));
     MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, sv->seq_counts, daux, bw.dlogits, s));
     return run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, dx, bw.gate, s);
   }
@@ -761,14 +792,18 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
     MOE_NEED16(W->W13s); MOE_NEED16(W->W2s); MOE_NEED16(sv->H_s); MOE_NEED16(sv->Act_s);
     MOE_NEED16(gr->dW13s); MOE_NEED16(gr->dW2s);
   }
+  if (cfg->shared_gate) { MOE_NEED16(W->Wsg); MOE_NEED16(sv->gs); MOE_NEED16(sv->Y_s); MOE_NEED(gr->dWsg); }
   const BwdWs bw = carve_bwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, bw.bytes, __func__));
   const moe_config_t& c = *cfg;
   hipStream_t s = S(stream);
-  // the shared expert's upstream gradient is dy itself, in the activation dtype
-  void* dY_s = c.Fs ? (c.act_dtype == MOE_F32 ? const_cast<float*>(dy) : bw.dY_s) : nullptr;
+  // the shared expert's upstream gradient is dy itself in the activation dtype (an fp32
+  // layer reads dy in place), or gs dy behind its gate
+  const bool dy_in_place = c.act_dtype == MOE_F32 && !c.shared_gate;
+  void* dY_s = c.Fs ? (dy_in_place ? const_cast<float*>(dy) : bw.dY_s) : nullptr;
   MOE_TRY(launch_combine_bwd(c, dy, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, bw.dY, bw.dw,
-                             c.act_dtype == MOE_F32 ? nullptr : dY_s, s));
+                             dy_in_place ? nullptr : dY_s, c.shared_gate ? sv->gs : nullptr,
+                             c.shared_gate ? static_cast<const float*>(sv->Y_s) : nullptr, bw.dl_s, s));
   SideStream* ss = nullptr;
   MOE_TRY(side_stream(&ss));
   MOE_TRY(fork(s, ss->dy, ss->s));  // dY_perm (and the shared expert's dY) ready
@@ -777,8 +812,10 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
                           gr->dW2s, bw.sched, bw.dact, s, ss->s, ss->dh));
   MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, sv->seq_counts, daux, bw.dlogits, s));
   MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, bw.gate, s));
+  if (c.shared_gate) MOE_TRY(launch_shared_gate_bwd(c, x, bw.dl_s, gr->dWsg, bw.sg_part, s));
   MOE_TRY(launch_unpermute_reduce(c, bw.dX, sv->row_of, c.Fs ? static_cast<const float*>(bw.dx_s) : nullptr,
-                                  bw.dx_r, dx, s));
+                                  bw.dx_r, c.shared_gate ? bw.dl_s : nullptr, c.shared_gate ? W->Wsg : nullptr, dx,
+                                  s));
   return fork(ss->s, ss->join, s);  // the caller's stream sees the weight gradients too
 }
 

@@ -41,14 +41,21 @@ moe_status_t launch_permute(const moe_config_t& c, const void* x, const int32_t*
                             int32_t* row_of, int32_t* token_of, void* x_perm, int32_t* blk_hist,
                             int32_t* blk_base, int32_t* counts_ws, bool hist_ready, hipStream_t s,
                             int elem_bytes = 0);
-// y = sum_j w Y_perm[row] + Y_s  (all fp32)
+// y = sum_j w Y_perm[row] + gs Y_s  (all fp32; gs NULL means 1)
 moe_status_t launch_combine(const moe_config_t& c, const float* Y, const int32_t* row_of, const float* w,
-                            const float* Y_s, float* y, hipStream_t s);
-// dx = sum_j dX_perm[row] + dx_s + dx_r  (all fp32)
+                            const float* Y_s, const float* gs, float* y, hipStream_t s);
+// dx = sum_j dX_perm[row] + dx_s + dx_r + dl_s Wsg  (all fp32; NULL terms skipped)
 moe_status_t launch_unpermute_reduce(const moe_config_t& c, const float* dX, const int32_t* row_of,
-                                     const float* dx_s, const float* dx_r, float* dx, hipStream_t s);
+                                     const float* dx_s, const float* dx_r, const float* dl_s, const float* Wsg,
+                                     float* dx, hipStream_t s);
 moe_status_t launch_combine_bwd(const moe_config_t& c, const float* dy, const float* Y, const int32_t* row_of,
-                                const float* w, void* dY, float* dw, void* dY_s, hipStream_t s);
+                                const float* w, void* dY, float* dw, void* dY_s, const float* gs, const float* Ys,
+                                float* dl_s, hipStream_t s);
+// the shared expert's sigmoid gate: gs = sigma(x Wsg); dWsg = x^T dl_s (part: scratch)
+size_t shared_gate_part_bytes(const moe_config_t& c);
+moe_status_t launch_shared_gate(const moe_config_t& c, const void* x, const float* Wsg, float* gs, hipStream_t s);
+moe_status_t launch_shared_gate_bwd(const moe_config_t& c, const void* x, const float* dl_s, float* dWsg,
+                                    float* part, hipStream_t s);
 
 #define MOE_TRY_INTERNAL(x)      \
   do {                           \

@@ -159,16 +159,21 @@ template <> struct R8<uint16_t> {
   }
 };
 
-// out[t] = sum_j w[t,j] * Y[row_of[t,j]] (+ add1[t]) (+ add2[t]), fp32 accumulation in
-// slot order then addend order; w NULL means 1.  The combine (Y fp32 expert outputs,
-// add1 the shared expert's output) and the unpermute-reduce of the backward (Y the
-// per-row input gradients, add1 the shared expert's, add2 the router's) share it.
+// out[t] = sum_j w[t,j] * Y[row_of[t,j]] (+ a1_scale[t] * add1[t]) (+ add2[t])
+//          (+ r1_coef[t] * r1_vec), fp32 accumulation in slot order then addend order; w
+// NULL means 1, a1_scale NULL means 1.  The combine (Y fp32 expert outputs, add1 the
+// shared expert's output, a1_scale its sigmoid gate) and the unpermute-reduce of the
+// backward (Y the per-row input gradients, add1 the shared expert's, add2 the router's,
+// r1 the shared gate's input gradient dl_t Wsg) share it.
 template <typename TY, typename TA1, typename TO>
 __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict__ Y, int Tn, int groups, int k,
                                                          const int32_t* __restrict__ row_of,
                                                          const float* __restrict__ w,
                                                          const void* __restrict__ add1,
-                                                         const float* __restrict__ add2, void* __restrict__ out) {
+                                                         const float* __restrict__ a1_scale,
+                                                         const float* __restrict__ add2,
+                                                         const float* __restrict__ r1_coef,
+                                                         const float* __restrict__ r1_vec, void* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
@@ -213,8 +218,14 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
     if (add1) {
       float f[8];
       R8<TA1>::load(add1, gi, c0, c1, f);
+      if (a1_scale) {
+        const float sc = a1_scale[t];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += f[i];
+        for (int i = 0; i < 8; ++i) acc[i] += sc * f[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += f[i];
+      }
     }
     if (add2) {
       float f[8];
@@ -222,13 +233,22 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += f[i];
     }
+    if (r1_coef) {
+      float v[8];
+      R8<float>::load(r1_vec, 0, c0, c1, v);
+      const float cf = r1_coef[t];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += cf * v[i];
+    }
     R8<TO>::store(out, gi, c0, c1, acc);
   }
 }
 
 // dY_perm[row_of[t,j]] = w[t,j] * dy[t]  (activation dtype);
 // dw[t,j] = <dy[t], Y_perm[row_of[t,j]]>  (fp32: per lane over its columns in order, then
-// a fixed butterfly across the wave);  dY_s[t] = dy[t] in the activation dtype (optional).
+// a fixed butterfly across the wave);  dY_s[t] = dy[t] in the activation dtype (optional),
+// times gs[t] for a gated shared expert, and then dl_s[t] = gs (1 - gs) <dy[t], Y_s[t]>,
+// the gradient of the gate's logit.
 // One wave per token, one pass over the columns: dy is loaded once per column group and the
 // k rows four at a time; KMAX >= k partial sums live in registers.
 template <typename TACT, int KMAX>
@@ -236,10 +256,15 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restric
                                                           const float* __restrict__ Y, int Tn, int groups,
                                                           int k, const int32_t* __restrict__ row_of,
                                                           const float* __restrict__ w, void* __restrict__ dY,
-                                                          float* __restrict__ dw, void* __restrict__ dY_s) {
+                                                          float* __restrict__ dw, void* __restrict__ dY_s,
+                                                          const float* __restrict__ gs,
+                                                          const float* __restrict__ Ys,
+                                                          float* __restrict__ dl_s) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
+  const float gs_t = gs ? gs[t] : 1.0f;
+  float part_s = 0.0f;
   const int my_r = lane < k ? row_of[static_cast<int64_t>(t) * k + lane] : 0;
   const float my_w = lane < k ? w[static_cast<int64_t>(t) * k + lane] : 0.0f;
   const int d = groups * 8;
@@ -255,7 +280,24 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restric
 #pragma unroll
     for (int i = 0; i < 8; ++i) g[i] = 0.0f;
     if (on) R8<float>::load(dy, t0, c0, c1, g);
-    if (on && dY_s) R8<TACT>::store(dY_s, t0, c0, c1, g);
+    if (on && dY_s) {
+      if (gs) {
+        float gg[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gg[i] = gs_t * g[i];
+        R8<TACT>::store(dY_s, t0, c0, c1, gg);
+      } else {
+        R8<TACT>::store(dY_s, t0, c0, c1, g);
+      }
+    }
+    if (Ys) {
+      float ys[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ys[i] = 0.0f;
+      if (on) R8<float>::load(Ys, t0, c0, c1, ys);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) part_s += g[i] * ys[i];
+    }
 #pragma unroll
     for (int j0 = 0; j0 < KMAX; j0 += 4) {
       if (j0 < k) {
@@ -293,6 +335,58 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restric
     }
   }
   if (lane < k) dw[static_cast<int64_t>(t) * k + lane] = my_dw;
+  if (dl_s) {
+    const float v = wave_sum(part_s);
+    if (lane == 0) dl_s[t] = gs_t * (1.0f - gs_t) * v;
+  }
+}
+
+// The shared expert's sigmoid gate (The Ultimate MoE Training Handbook, §3.4 Shared
+// experts): gs[t] = sigma(<x[t], Wsg>), one wave per token, fp32 dot in a fixed order.
+template <typename TX>
+__global__ __launch_bounds__(256) void shared_gate_kernel(const void* __restrict__ x, const float* __restrict__ Wsg,
+                                                          int Tn, int groups, float* __restrict__ gs) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int64_t t0 = static_cast<int64_t>(t) * groups * 8;
+  float acc = 0.0f;
+  for (int m = 0; 64 * m < groups; ++m) {
+    const int nb = min(64, groups - 64 * m);
+    if (lane < nb) {
+      const int c0 = 128 * m + lane, c1 = c0 + nb;
+      float f[8], v[8];
+      R8<TX>::load(x, t0, c0, c1, f);
+      R8<float>::load(Wsg, 0, c0, c1, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += f[i] * v[i];
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) gs[t] = 1.0f / (1.0f + expf(-acc));
+}
+
+// dWsg = sum_t dl_s[t] x[t]: per chunk of 256 tokens and column, partial sums in token
+// order; then the chunks summed in order.
+constexpr int kGateChunk = 256;
+template <typename TX>
+__global__ __launch_bounds__(256) void shared_gate_wgrad_part_kernel(const void* __restrict__ x,
+                                                                     const float* __restrict__ dl, int Tn, int d,
+                                                                     float* __restrict__ part) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= d) return;
+  const int t0 = blockIdx.y * kGateChunk, t1 = min(Tn, t0 + kGateChunk);
+  float acc = 0.0f;
+  for (int t = t0; t < t1; ++t) acc += dl[t] * Elem<TX>::load(static_cast<const TX*>(x), static_cast<int64_t>(t) * d + c);
+  part[static_cast<int64_t>(blockIdx.y) * d + c] = acc;
+}
+__global__ __launch_bounds__(256) void shared_gate_wgrad_final_kernel(const float* __restrict__ part, int nchunk,
+                                                                      int d, float* __restrict__ dWsg) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= d) return;
+  float acc = 0.0f;
+  for (int q = 0; q < nchunk; ++q) acc += part[static_cast<int64_t>(q) * d + c];
+  dWsg[c] = acc;
 }
 
 }  // namespace
@@ -317,31 +411,60 @@ moe_status_t launch_permute(const moe_config_t& c, const void* x, const int32_t*
 }
 
 moe_status_t launch_combine(const moe_config_t& c, const float* Y, const int32_t* row_of, const float* w,
-                            const float* Y_s, float* y, hipStream_t s) {
+                            const float* Y_s, const float* gs, float* y, hipStream_t s) {
   const int groups = c.d / 8;
   gather_sum_kernel<float, float, float><<<static_cast<int>(ceil_div(c.T, 4)), 256, 0, s>>>(
-      Y, c.T, groups, c.k, row_of, w, Y_s, nullptr, y);
+      Y, c.T, groups, c.k, row_of, w, Y_s, gs, nullptr, nullptr, nullptr, y);
   return check_launch("combine");
 }
 
 moe_status_t launch_unpermute_reduce(const moe_config_t& c, const float* dX, const int32_t* row_of,
-                                     const float* dx_s, const float* dx_r, float* dx, hipStream_t s) {
+                                     const float* dx_s, const float* dx_r, const float* dl_s, const float* Wsg,
+                                     float* dx, hipStream_t s) {
   const int groups = c.d / 8;
   const int grid = static_cast<int>(ceil_div(c.T, 4));
-  gather_sum_kernel<float, float, float><<<grid, 256, 0, s>>>(dX, c.T, groups, c.k, row_of, nullptr, dx_s, dx_r,
-                                                              dx);
+  gather_sum_kernel<float, float, float><<<grid, 256, 0, s>>>(dX, c.T, groups, c.k, row_of, nullptr, dx_s, nullptr,
+                                                              dx_r, dl_s, dl_s ? Wsg : nullptr, dx);
   return check_launch("unpermute_reduce");
 }
 
+size_t shared_gate_part_bytes(const moe_config_t& c) {
+  return c.shared_gate ? static_cast<size_t>(ceil_div(c.T, kGateChunk)) * c.d * 4 : 0;
+}
+
+moe_status_t launch_shared_gate(const moe_config_t& c, const void* x, const float* Wsg, float* gs, hipStream_t s) {
+  const int grid = static_cast<int>(ceil_div(c.T, 4));
+  if (c.act_dtype == MOE_BF16)
+    shared_gate_kernel<uint16_t><<<grid, 256, 0, s>>>(x, Wsg, c.T, c.d / 8, gs);
+  else
+    shared_gate_kernel<float><<<grid, 256, 0, s>>>(x, Wsg, c.T, c.d / 8, gs);
+  return check_launch("shared_gate");
+}
+
+moe_status_t launch_shared_gate_bwd(const moe_config_t& c, const void* x, const float* dl_s, float* dWsg,
+                                    float* part, hipStream_t s) {
+  const int nchunk = static_cast<int>(ceil_div(c.T, kGateChunk));
+  const dim3 grid(static_cast<unsigned>(ceil_div(c.d, 256)), static_cast<unsigned>(nchunk));
+  if (c.act_dtype == MOE_BF16)
+    shared_gate_wgrad_part_kernel<uint16_t><<<grid, 256, 0, s>>>(x, dl_s, c.T, c.d, part);
+  else
+    shared_gate_wgrad_part_kernel<float><<<grid, 256, 0, s>>>(x, dl_s, c.T, c.d, part);
+  shared_gate_wgrad_final_kernel<<<static_cast<int>(ceil_div(c.d, 256)), 256, 0, s>>>(part, nchunk, c.d, dWsg);
+  return check_launch("shared_gate_bwd");
+}
+
 moe_status_t launch_combine_bwd(const moe_config_t& c, const float* dy, const float* Y, const int32_t* row_of,
-                                const float* w, void* dY, float* dw, void* dY_s, hipStream_t s) {
+                                const float* w, void* dY, float* dw, void* dY_s, const float* gs, const float* Ys,
+                                float* dl_s, hipStream_t s) {
   const int groups = c.d / 8;
   const int grid = static_cast<int>(ceil_div(c.T, 4));
   const bool bf = c.act_dtype == MOE_BF16;
 #define MOE_CB(KM)                                                                                        \
   if (c.k <= KM) {                                                                                        \
-    if (bf) combine_bwd_kernel<uint16_t, KM><<<grid, 256, 0, s>>>(dy, Y, c.T, groups, c.k, row_of, w, dY, dw, dY_s); \
-    else combine_bwd_kernel<float, KM><<<grid, 256, 0, s>>>(dy, Y, c.T, groups, c.k, row_of, w, dY, dw, dY_s);      \
+    if (bf) combine_bwd_kernel<uint16_t, KM><<<grid, 256, 0, s>>>(dy, Y, c.T, groups, c.k, row_of, w, dY, dw, dY_s, \
+                                                                  gs, Ys, dl_s);                            \
+    else combine_bwd_kernel<float, KM><<<grid, 256, 0, s>>>(dy, Y, c.T, groups, c.k, row_of, w, dY, dw, dY_s,    \
+                                                            gs, Ys, dl_s);                                  \
     return check_launch("combine_bwd");                                                                   \
   }
   MOE_CB(8)

@@ -41,7 +41,7 @@ from typing import Dict, Optional
 import numpy as np
 
 # tensor ids of the independent streams
-_TID_X, _TID_WG, _TID_BIAS, _TID_W13, _TID_W2, _TID_W13S, _TID_W2S, _TID_DY, _TID_LOGITS, _TID_AUX = range(10)
+_TID_X, _TID_WG, _TID_BIAS, _TID_W13, _TID_W2, _TID_W13S, _TID_W2S, _TID_DY, _TID_LOGITS, _TID_AUX, _TID_WSG = range(11)
 _ROW_CHUNK = 256
 
 
@@ -72,6 +72,7 @@ class LayerShape:
     glu_c_linear: float = 0.0   # situ: the up cap (0 = none)
     num_groups: int = 0         # group-limited routing: expert groups (0 = off)
     group_topk: int = 0         # groups kept per token
+    shared_gate: bool = False   # a sigmoid gate on the shared expert (gate weight Wsg [d], fp32)
 
     @property
     def A(self) -> int:
@@ -215,8 +216,10 @@ def make_inputs(shape: LayerShape, seed: int, with_dy: bool = True, threads: Opt
             if Fs:
                 out["W13s"] = _normal_rows(seed, _TID_W13S, 2 * Fs, d, weight_std(shape, d), act, pool)
                 out["W2s"] = _normal_rows(seed, _TID_W2S, d, Fs, weight_std(shape, Fs), act, pool)
+                out["Wsg"] = (_normal_rows(seed, _TID_WSG, 1, d, weight_std(shape, d), "f32", pool)[0]
+                              if shape.shared_gate else None)
             else:
-                out["W13s"] = out["W2s"] = None
+                out["W13s"] = out["W2s"] = out["Wsg"] = None
         if with_dy:
             out["dy"] = _normal_rows(seed, _TID_DY, T, d, 1.0, act, pool)
     return out

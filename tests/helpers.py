@@ -145,7 +145,7 @@ def spec_of(shape) -> "O.LayerSpec":
     return O.LayerSpec(E=shape.E, k=shape.k, score=shape.score, scaling=shape.scaling, aux_coeff=shape.aux_coeff,
                        pre_softmax=shape.pre_softmax, z_coeff=shape.z_coeff, seq_aux_coeff=shape.seq_aux_coeff,
                        seq_len=shape.seq_len, glu=O.GLU(shape.glu, shape.glu_c, shape.glu_c_linear),
-                       num_groups=shape.num_groups, group_topk=shape.group_topk)
+                       num_groups=shape.num_groups, group_topk=shape.group_topk, shared_gate=shape.shared_gate)
 
 
 def oracle_inputs(inp, shape):
@@ -155,4 +155,5 @@ def oracle_inputs(inp, shape):
                 bg=None if inp["bg"] is None else inp["bg"].astype(np.float64),
                 expert_bias=None if inp["expert_bias"] is None else inp["expert_bias"].astype(np.float64),
                 W13=f64(inp["W13"], a), W2=f64(inp["W2"], a), W13s=f64(inp.get("W13s"), a),
-                W2s=f64(inp.get("W2s"), a), dy=f64(inp.get("dy"), a))
+                W2s=f64(inp.get("W2s"), a), dy=f64(inp.get("dy"), a),
+                Wsg=None if inp.get("Wsg") is None else inp["Wsg"].astype(np.float64))

@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_declared_entry_point():
     lib = L.load()
     names = header_functions()
-    assert len(names) == 23
+    assert len(names) == 25
     assert sorted(L.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -54,6 +54,8 @@ def test_valid_configs():
     (dict(seq_aux_coeff=1e-4, seq_len=3000), L.MOE_ERR_INVALID_ARG),     # that divides T
     (dict(wgrad_dtype=7), L.MOE_ERR_INVALID_ARG),
     (dict(glu_kind=3), L.MOE_ERR_INVALID_ARG),
+    (dict(shared_gate=1), L.MOE_ERR_INVALID_ARG),                         # the small layer has no shared expert
+    (dict(shared_gate=2, Fs=1024), L.MOE_ERR_INVALID_ARG),
     (dict(num_groups=7), L.MOE_ERR_INVALID_ARG),                          # 7 does not divide 64
     (dict(num_groups=8, group_topk=0), L.MOE_ERR_INVALID_ARG),
     (dict(num_groups=8, group_topk=9), L.MOE_ERR_INVALID_ARG),
@@ -217,7 +219,7 @@ def test_entry_points_reject_bad_arguments_before_launching():
     assert st == L.MOE_ERR_INVALID_ARG and b"aligned" in lib.moe_last_error()
     # invalid configuration reaches no launch either
     bad = L.config_from_shape(replace(W.LAYERS[2], k=1))
-    st = lib.moe_unpermute_combine(ctypes.byref(bad), fake, fake, fake, nul, fake, s)
+    st = lib.moe_unpermute_combine(ctypes.byref(bad), fake, fake, fake, nul, nul, fake, s)
     assert st == L.MOE_ERR_UNSUPPORTED
     # the layer calls check their structs
     st = lib.moe_layer_fwd(ctypes.byref(cfg), None, fake, None, fake, nul, fake, ctypes.c_size_t(1 << 40), s)

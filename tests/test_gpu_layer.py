@@ -22,7 +22,8 @@ def _run_layer(shape, inp, **cfg_extra):
     cfg = L.config_from_shape(shape, **cfg_extra)
     d = dev()
     Wt = dict(Wg=to_dev(inp["Wg"]), bg=to_dev(inp["bg"]), expert_bias=to_dev(inp["expert_bias"]),
-              W13=to_dev(inp["W13"]), W2=to_dev(inp["W2"]), W13s=to_dev(inp["W13s"]), W2s=to_dev(inp["W2s"]))
+              W13=to_dev(inp["W13"]), W2=to_dev(inp["W2"]), W13s=to_dev(inp["W13s"]), W2s=to_dev(inp["W2s"]),
+              Wsg=to_dev(inp.get("Wsg")))
     x = to_dev(inp["x"])
     dy = to_dev(W.to_f32(inp["dy"], shape.act).copy())     # upstream gradient, fp32
     S = L.alloc_saved(cfg, d)
@@ -43,9 +44,9 @@ def _check_layer(shape, seed, **cfg_extra):
     o = oracle_inputs(inp, shape)
     spec = spec_of(shape)
     f = O.layer_forward(o["x"], o["Wg"], o["W13"], o["W2"], spec, bg=o["bg"], expert_bias=o["expert_bias"],
-                        W13s=o["W13s"], W2s=o["W2s"])
+                        W13s=o["W13s"], W2s=o["W2s"], Wsg=o["Wsg"])
     b = O.layer_backward(f, o["x"], o["Wg"], o["W13"], o["W2"], o["dy"], spec, W13s=o["W13s"], W2s=o["W2s"],
-                         daux=1.0)
+                         daux=1.0, Wsg=o["Wsg"])
     r = f["route"]
     tl = tol(shape)
     safe = r["margin"] > MARGIN
@@ -74,6 +75,12 @@ def _check_layer(shape, seed, **cfg_extra):
     if shape.Fs:
         check_grad("dW13s", to_np(got["dW13s"]), b["dW13s"], shape)
         check_grad("dW2s", to_np(got["dW2s"]), b["dW2s"], shape)
+    if getattr(shape, "shared_gate", False):
+        # the gate values and its weight gradient (a sum over all tokens, fp32)
+        gs_err = np.abs(to_np(got["S_gs"]) - f["shared"]["gs"]).max()
+        assert gs_err < 1e-5 if shape.act == "bf16" else gs_err < 1e-6, f"gs: {gs_err:.2e}"
+        if not moved.any():
+            check_grad("dWsg", to_np(got["dWsg"]), b["dWsg"], shape)
     return got
 
 
