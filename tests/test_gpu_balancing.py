@@ -279,3 +279,38 @@ def test_quantile_bias_update_matches_oracle():
         ref = O.quantile_bias_update(beta, local, ema)
         np.testing.assert_allclose(to_np(b), ref, rtol=1e-6, atol=2e-8)
         assert abs(to_np(b).mean()) < 1e-7
+
+
+def test_full_size_deepseek_balancing_and_quantile():
+    """The DeepSeek-V3-shaped layer at its real size (T=16384, E=256, k=8): the router with
+    8 groups of which 4 are kept, the selection bias and the sequence-wise loss over 4
+    sequences of 4096, and quantile balancing on the same logits; both sides get the same
+    fp32 logits (and fp32 scores), so routing, counts, per-sequence counts, alpha and the
+    solved bias are bit-exact."""
+    torch = torch_mod()
+    L = _lib()
+    base = W.LAYERS[3]
+    shape = replace(base, num_groups=8, group_topk=4, seq_aux_coeff=1e-4, seq_len=4096)
+    inp = W.make_inputs(shape, seed=3, with_dy=False, with_experts=False)
+    logits = O.gate_logits(f64(inp["x"], shape.act), inp["Wg"], inp["bg"]).astype(np.float32)
+    _, g = _route_gpu(shape, logits, inp["expert_bias"])
+    r = O.route(logits.astype(np.float64), spec_of(shape), inp["expert_bias"].astype(np.float64))
+    assert np.array_equal(g["idx"], r["idx"])
+    assert np.array_equal(g["counts"], r["counts"])
+    assert np.array_equal(g["seq_counts"], r["seq_counts"])
+    assert g["stats"][5] == pytest.approx(r["seq_aux"], rel=2e-5)
+    # quantile balancing on the sigmoid scores of the same logits
+    scores = (1.0 / (1.0 + np.exp(-logits.astype(np.float64)))).astype(np.float32)
+    beta = (inp["expert_bias"] * np.float32(0.1)).astype(np.float32)
+    cfg = L.config_from_shape(base)
+    T, E, k = base.T, base.E, base.k
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev())
+    alpha = torch.empty(T, dtype=torch.float32, device=dev())
+    bl = torch.empty(E, dtype=torch.float32, device=dev())
+    ws = L.alloc_workspace(cfg, dev())
+    L.router_quantile(cfg, to_dev(scores), to_dev(beta), idx, alpha, bl, ws)
+    torch.cuda.synchronize()
+    ridx, ralpha, rbl = O.quantile_route(scores, beta, k)
+    assert np.array_equal(to_np(idx), ridx)
+    assert np.array_equal(to_np(alpha).astype(np.float32).view(np.uint32), ralpha.view(np.uint32))
+    assert np.all(to_np(bl).astype(np.float32) == rbl)
