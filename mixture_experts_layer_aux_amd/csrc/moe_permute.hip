@@ -112,12 +112,14 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int my_r = lane < k ? row_of[static_cast<int64_t>(t) * k + lane] : 0;
-  const uint4* src = x + static_cast<int64_t>(t) * units;
+  typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+  const u32x4_nt* src = reinterpret_cast<const u32x4_nt*>(x) + static_cast<int64_t>(t) * units;
+  u32x4_nt* dst = reinterpret_cast<u32x4_nt*>(x_perm);
   for (int u = lane; u < units; u += 64) {
-    const uint4 v = src[u];
+    const u32x4_nt v = src[u];
     for (int j = 0; j < k; ++j) {
       const int r = __shfl(my_r, j, 64);
-      x_perm[static_cast<int64_t>(r) * units + u] = v;
+      __builtin_nontemporal_store(v, dst + static_cast<int64_t>(r) * units + u);   // written once
     }
   }
 }
@@ -127,24 +129,42 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const uint4* __restri
 // in a block of nb lanes, lane l holds the 4-value chunks c0 = 128 m + l and c1 = c0 + nb,
 // so each access instruction of the wave covers one contiguous run of the row (whole cache
 // lines) rather than every other 16 bytes of it.
+// NT: a stream touched once (each expert-output row in the combine, dy, the written
+// gradients), loaded and stored with the non-temporal hint so it does not displace reused
+// data (the gate weight, rows still to be gathered) from the caches.
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+template <bool NT, typename V>
+__device__ __forceinline__ V ld(const V* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT, typename V>
+__device__ __forceinline__ void st(V* p, V v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 template <typename T> struct R8;
 template <> struct R8<float> {
+  template <bool NT = false>
   __device__ __forceinline__ static void load(const void* base, int64_t row, int c0, int c1, float* f) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + row);
-    const float4 a = p[c0], b = p[c1];
+    const f32x4_nt* p = reinterpret_cast<const f32x4_nt*>(static_cast<const float*>(base) + row);
+    const f32x4_nt a = ld<NT>(p + c0), b = ld<NT>(p + c1);
     f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
   }
+  template <bool NT = false>
   __device__ __forceinline__ static void store(void* base, int64_t row, int c0, int c1, const float* f) {
-    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + row);
-    p[c0] = make_float4(f[0], f[1], f[2], f[3]);
-    p[c1] = make_float4(f[4], f[5], f[6], f[7]);
+    f32x4_nt* p = reinterpret_cast<f32x4_nt*>(static_cast<float*>(base) + row);
+    st<NT>(p + c0, f32x4_nt{f[0], f[1], f[2], f[3]});
+    st<NT>(p + c1, f32x4_nt{f[4], f[5], f[6], f[7]});
   }
 };
 template <> struct R8<uint16_t> {
+  template <bool NT = false>
   __device__ __forceinline__ static void load(const void* base, int64_t row, int c0, int c1, float* f) {
-    const uint2* p = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + row);
-    const uint2 a = p[c0], b = p[c1];
+    const u32x2_nt* p = reinterpret_cast<const u32x2_nt*>(static_cast<const uint16_t*>(base) + row);
+    const u32x2_nt a = ld<NT>(p + c0), b = ld<NT>(p + c1);
     const uint32_t w[4] = {a.x, a.y, b.x, b.y};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -152,10 +172,11 @@ template <> struct R8<uint16_t> {
       f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   }
+  template <bool NT = false>
   __device__ __forceinline__ static void store(void* base, int64_t row, int c0, int c1, const float* f) {
-    uint2* p = reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + row);
-    p[c0] = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
-    p[c1] = make_uint2(pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    u32x2_nt* p = reinterpret_cast<u32x2_nt*>(static_cast<uint16_t*>(base) + row);
+    st<NT>(p + c0, u32x2_nt{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])});
+    st<NT>(p + c1, u32x2_nt{pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])});
   }
 };
 
@@ -198,7 +219,7 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
       for (int q = 0; q < 4; ++q) {
         const int r = __shfl(my_r, j + q, 64);
         wj[q] = __shfl(my_w, j + q, 64);
-        if (on) R8<TY>::load(Y, static_cast<int64_t>(r) * d, c0, c1, f[q]);
+        if (on) R8<TY>::template load<true>(Y, static_cast<int64_t>(r) * d, c0, c1, f[q]);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -209,7 +230,7 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
       const int r = __shfl(my_r, j, 64);
       const float wj = __shfl(my_w, j, 64);
       float f[8] = {};
-      if (on) R8<TY>::load(Y, static_cast<int64_t>(r) * d, c0, c1, f);
+      if (on) R8<TY>::template load<true>(Y, static_cast<int64_t>(r) * d, c0, c1, f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += wj * f[i];
     }
@@ -217,7 +238,7 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
     const int64_t gi = static_cast<int64_t>(t) * d;
     if (add1) {
       float f[8];
-      R8<TA1>::load(add1, gi, c0, c1, f);
+      R8<TA1>::template load<true>(add1, gi, c0, c1, f);
       if (a1_scale) {
         const float sc = a1_scale[t];
 #pragma unroll
@@ -229,7 +250,7 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
     }
     if (add2) {
       float f[8];
-      R8<float>::load(add2, gi, c0, c1, f);
+      R8<float>::load<true>(add2, gi, c0, c1, f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += f[i];
     }
@@ -240,7 +261,7 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += cf * v[i];
     }
-    R8<TO>::store(out, gi, c0, c1, acc);
+    R8<TO>::template store<true>(out, gi, c0, c1, acc);
   }
 }
 
@@ -279,22 +300,22 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restric
     float g[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) g[i] = 0.0f;
-    if (on) R8<float>::load(dy, t0, c0, c1, g);
+    if (on) R8<float>::load<true>(dy, t0, c0, c1, g);
     if (on && dY_s) {
       if (gs) {
         float gg[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) gg[i] = gs_t * g[i];
-        R8<TACT>::store(dY_s, t0, c0, c1, gg);
+        R8<TACT>::template store<true>(dY_s, t0, c0, c1, gg);
       } else {
-        R8<TACT>::store(dY_s, t0, c0, c1, g);
+        R8<TACT>::template store<true>(dY_s, t0, c0, c1, g);
       }
     }
     if (Ys) {
       float ys[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) ys[i] = 0.0f;
-      if (on) R8<float>::load(Ys, t0, c0, c1, ys);
+      if (on) R8<float>::load<true>(Ys, t0, c0, c1, ys);
 #pragma unroll
       for (int i = 0; i < 8; ++i) part_s += g[i] * ys[i];
     }
@@ -308,7 +329,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restric
           r[q] = __shfl(my_r, j0 + q, 64);
 #pragma unroll
           for (int i = 0; i < 8; ++i) y[q][i] = 0.0f;
-          if (on && j0 + q < k) R8<float>::load(Y, static_cast<int64_t>(r[q]) * d, c0, c1, y[q]);
+          if (on && j0 + q < k) R8<float>::load<true>(Y, static_cast<int64_t>(r[q]) * d, c0, c1, y[q]);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -320,7 +341,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const float* __restric
               part[j0 + q] += g[i] * y[q][i];
               gw[i] = g[i] * wj;
             }
-            if (on && dY) R8<TACT>::store(dY, static_cast<int64_t>(r[q]) * d, c0, c1, gw);
+            if (on && dY) R8<TACT>::template store<true>(dY, static_cast<int64_t>(r[q]) * d, c0, c1, gw);
           }
         }
       }
