@@ -170,7 +170,12 @@ typedef struct moe_saved {
   float* gs;           /* [T] the shared expert's gate values, when shared_gate */
 } moe_saved_t;
 
-/* Gradients written by moe_layer_bwd (overwritten, not accumulated). */
+/* Gradients written by moe_layer_bwd.  accumulate = 0 overwrites them; accumulate = 1
+ * adds this call's gradients into the values the buffers hold (gradient accumulation over
+ * micro-batches): each element becomes old + new in fp32, with the fp32 sum of one call
+ * formed exactly as when overwriting; a bf16 gradient is rounded once from
+ * old + the fp32 accumulator.  An expert without rows leaves its gradients untouched
+ * (overwriting writes exact zeros).  Any other accumulate value -> MOE_ERR_INVALID_ARG. */
 typedef struct moe_grads {
   float* dWg;  /* [E, d] fp32 */
   float* dbg;  /* [E] fp32, or NULL */
@@ -179,6 +184,7 @@ typedef struct moe_grads {
   void* dW13s;  /* [2Fs, d] or NULL when Fs == 0 */
   void* dW2s;   /* [d, Fs]  or NULL */
   float* dWsg;  /* [d] fp32, when shared_gate */
+  int32_t accumulate; /* 0: overwrite, 1: add into the buffers */
 } moe_grads_t;
 
 const char* moe_status_string(moe_status_t status);
@@ -326,16 +332,19 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
 
 /* Grouped weight gradient (the expert weight gradients of [HB] §3.4's FFN, by the chain
  * rule): for each group g over its rows [offsets[g], offsets[g+1]),
- *   dW[g] = dY_g^T X_g,   fp32 accumulation, output in cfg->wgrad_dtype (overwritten).
+ *   dW[g] = dY_g^T X_g,   fp32 accumulation, output in cfg->wgrad_dtype; overwritten
+ * (accumulate = 0), or added into dW (accumulate = 1: old + the fp32 sum, one rounding
+ * for bf16; a group with no rows is then left as it is).
  * dY [rows, N] and X [rows, K] in the act dtype, row-major; dW [groups, N, K].
  * The routed experts: (dH, x_perm) -> dW13 with N = 2F, K = d, and (dY_perm, Act) -> dW2
  * with N = d, K = F.  offsets NULL: one group over rows [0, rows) (the shared expert, on
  * all T tokens).  A group with no rows gets exact zeros.  offsets[groups] <= rows is the
  * caller's promise (device data is not read on the host).  One kernel launch.
  * Errors: groups outside [1, 4096], groups != 1 without offsets, rows outside [0, 2^31),
- * N or K not a positive multiple of 64 -> MOE_ERR_INVALID_ARG. */
+ * N or K not a positive multiple of 64, accumulate not 0 or 1 -> MOE_ERR_INVALID_ARG. */
 moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, int32_t groups, int64_t rows,
-                               const void* dY, int32_t N, const void* X, int32_t K, void* dW, void* stream);
+                               const void* dY, int32_t N, const void* X, int32_t K, void* dW, int32_t accumulate,
+                               void* stream);
 
 /* ---------------------------------------------------------------- fp8 experts
  * e4m3 block quantiser (the fp8 recipe is a reading: the pages leave low-precision expert
@@ -405,7 +414,9 @@ moe_status_t moe_gate_logits_bwd(const moe_config_t* cfg, const void* x, const f
  * device must not be issued concurrently from several host threads.
  * fp8 experts are frozen (no expert gradients): grads->dW13, dW2, dW13s, dW2s must be
  * NULL, and the call computes the router path only -- dw, dlogits, dWg, dbg, and
- * dx = dlogits Wg, the input gradient through the router. */
+ * dx = dlogits Wg, the input gradient through the router.
+ * grads->accumulate = 1 adds every weight gradient into its buffer (see moe_grads_t); dx
+ * is overwritten either way. */
 moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* weights, const moe_saved_t* saved,
                            const void* x, const float* dy, float daux, float* dx, const moe_grads_t* grads,
                            void* ws, size_t ws_bytes, void* stream);

@@ -66,7 +66,8 @@ class Saved(ctypes.Structure):
 
 
 class Grads(ctypes.Structure):
-    _fields_ = [(n, _P) for n in ("dWg", "dbg", "dW13", "dW2", "dW13s", "dW2s", "dWsg")]
+    _fields_ = [(n, _P) for n in ("dWg", "dbg", "dW13", "dW2", "dW13s", "dW2s", "dWsg")] + [
+        ("accumulate", ctypes.c_int32)]
 
 
 _lib = None
@@ -310,15 +311,17 @@ def grouped_gemm_swiglu_bwd(cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, 
         _P(_stream(stream))))
 
 
-def grouped_wgrad(cfg, offsets, groups, rows, dY, N, X, K, dW, stream=None):
-    """dW[g] = dY_g^T X_g per group of rows (offsets None: one group of `rows` rows)."""
+def grouped_wgrad(cfg, offsets, groups, rows, dY, N, X, K, dW, stream=None, accumulate=False):
+    """dW[g] = dY_g^T X_g per group of rows (offsets None: one group of `rows` rows);
+    accumulate: dW[g] += dY_g^T X_g."""
     ad = act_dtype(cfg)
     if offsets is not None and offsets.numel() != groups + 1:
         raise ValueError(f"offsets: expected {groups + 1} entries, got {offsets.numel()}")
     _check(load().moe_grouped_wgrad(
         ctypes.byref(cfg), _P(_ptr(offsets, torch.int32, groups + 1, "offsets")), ctypes.c_int32(groups),
         ctypes.c_int64(rows), _P(_ptr(dY, ad, rows * N, "dY")), ctypes.c_int32(N), _P(_ptr(X, ad, rows * K, "X")),
-        ctypes.c_int32(K), _P(_ptr(dW, wgrad_dtype(cfg), groups * N * K, "dW")), _P(_stream(stream))))
+        ctypes.c_int32(K), _P(_ptr(dW, wgrad_dtype(cfg), groups * N * K, "dW")), ctypes.c_int32(int(accumulate)),
+        _P(_stream(stream))))
 
 
 def quantize_fp8(src, block_rows, q, scale, stream=None):
@@ -426,7 +429,8 @@ def layer_fwd(cfg, W, x, S, y, stats, ws, stream=None):
                                 _P(_stream(stream))))
 
 
-def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None):
+def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None, accumulate=False):
+    """The layer's backward; accumulate: add the weight gradients into G's buffers."""
     wp, wn = _ws(ws)
     ad, d, E, F, Fs = act_dtype(cfg), cfg.d, cfg.E, cfg.F, cfg.Fs
     ws_ = _weights_struct(cfg, W)
@@ -436,7 +440,7 @@ def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None):
     gs = Grads(dWg=_ptr(G["dWg"], f32, E * d, "dWg"), dbg=_ptr(G.get("dbg"), f32, E, "dbg"),
                dW13=_ptr(G.get("dW13"), wd, E * 2 * F * d, "dW13"), dW2=_ptr(G.get("dW2"), wd, E * d * F, "dW2"),
                dW13s=_ptr(G.get("dW13s"), wd, 2 * Fs * d, "dW13s"), dW2s=_ptr(G.get("dW2s"), wd, d * Fs, "dW2s"),
-               dWsg=_ptr(G.get("dWsg"), f32, d, "dWsg"))
+               dWsg=_ptr(G.get("dWsg"), f32, d, "dWsg"), accumulate=int(accumulate))
     _check(load().moe_layer_bwd(ctypes.byref(cfg), ctypes.byref(ws_), ctypes.byref(ss),
                                 _P(_ptr(x, ad, cfg.T * d, "x")), _P(_ptr(dy, f32, cfg.T * d, "dy")),
                                 ctypes.c_float(daux), _P(_ptr(dx, f32, cfg.T * d, "dx")), ctypes.byref(gs), _P(wp),

@@ -336,7 +336,7 @@ moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const in
 // dW[g] = dY_g^T X_g over the rows of each group (reduction-ragged); fp32 accumulation,
 // output in the weight-gradient dtype.
 moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G, int64_t rows, const void* dY, int N,
-                       const void* X, int K, void* dW, hipStream_t s) {
+                       const void* X, int K, void* dW, hipStream_t s, int beta) {
   GemmDesc w{};
   w.a_major = MN_MAJOR; w.b_major = MN_MAJOR; w.ragged = RAGGED_K; w.epi = EPI_STORE;
   w.a_type = w.b_type = act_dtype;
@@ -345,6 +345,7 @@ moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G
   w.A = dY; w.lda = N; w.B = X; w.ldb = K;
   w.C = dW; w.ldc = K; w.c_gstride = int64_t{1} * N * K;
   w.offsets = off; w.G = G; w.range_end = static_cast<int>(rows);
+  w.beta = beta;
   return act_dtype == MOE_BF16 ? launch_gemm_mfma(w, nullptr, s) : launch_gemm_fma(w, s);
 }
 
@@ -366,7 +367,7 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
                              void* dX_perm, void* dW13, void* dW2, const void* x, const void* W13s, const void* W2s,
                              const void* H_s, const void* Act_s, const void* dY_s, void* dH_s, void* dx_s,
                              void* dW13s, void* dW2s, int32_t* sched, float* dact, hipStream_t s,
-                             hipStream_t s2 = nullptr, hipEvent_t ev_dh = nullptr) {
+                             hipStream_t s2 = nullptr, hipEvent_t ev_dh = nullptr, int beta = 0) {
   // s2 (when given, with dY_perm and dX_perm distinct) runs the weight gradients; its
   // caller has made it wait for dY_perm and joins it back.
   if (!s2) s2 = s;
@@ -418,26 +419,27 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
                                             rows, F, s));
     }
     // (2) fc2 weight gradient dW2 = dY^T Act, queued before dX may overwrite an aliased dY
-    if (dw2) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dY, c.d, act, F, dw2, s2));
+    if (dw2) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dY, c.d, act, F, dw2, s2, beta));
     MOE_TRY(fork(s, ev_dh, s2));  // dH ready for the fc1 weight gradient
     MOE_TRY(et == MOE_BF16 ? launch_gemm_mfma(d1, sched, s) : launch_gemm_fma(d1, s));
     // (4) fc1 weight gradient dW13 = dH^T X
-    if (dw13) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dh, 2 * F, X, c.d, dw13, s2));
+    if (dw13) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dh, 2 * F, X, c.d, dw13, s2, beta));
   }
   return MOE_OK;
 }
 
 moe_status_t run_gate_bwd(const moe_config_t& c, const void* x, const float* Wg, const float* dlogits, float* dWg,
-                          float* dbg, float* dx_r, void* gate_ws, hipStream_t s) {
-  if (gate_on_mfma(c)) return launch_gate_bwd_mfma(c, x, Wg, dlogits, dWg, dbg, dx_r, gate_ws, s);
+                          float* dbg, float* dx_r, void* gate_ws, hipStream_t s, int beta = 0) {
+  if (gate_on_mfma(c)) return launch_gate_bwd_mfma(c, x, Wg, dlogits, dWg, dbg, dx_r, gate_ws, s, beta);
   GemmDesc gw{};
   gw.a_major = MN_MAJOR; gw.b_major = MN_MAJOR; gw.ragged = RAGGED_K; gw.epi = EPI_STORE;
   gw.a_type = MOE_F32; gw.b_type = c.act_dtype; gw.c_type = MOE_F32;
   gw.M = c.E; gw.N = c.d;
   gw.A = dlogits; gw.lda = c.E; gw.B = x; gw.ldb = c.d; gw.C = dWg; gw.ldc = c.d;
   gw.range_end = c.T;
+  gw.beta = beta;
   MOE_TRY(launch_gemm_fma(gw, s));
-  if (dbg) MOE_TRY(launch_colsum_ws(dlogits, c.T, c.E, dbg, static_cast<float*>(gate_ws), s));
+  if (dbg) MOE_TRY(launch_colsum_ws(dlogits, c.T, c.E, dbg, static_cast<float*>(gate_ws), s, beta));
   if (dx_r) {
     GemmDesc gx{};
     gx.a_major = K_MAJOR; gx.b_major = MN_MAJOR; gx.ragged = RAGGED_M; gx.epi = EPI_STORE;
@@ -680,7 +682,8 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
 }
 
 moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, int32_t groups, int64_t rows,
-                               const void* dY, int32_t N, const void* X, int32_t K, void* dW, void* stream) {
+                               const void* dY, int32_t N, const void* X, int32_t K, void* dW, int32_t accumulate,
+                               void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED16(dY); MOE_NEED16(X); MOE_NEED16(dW);
   if (groups < 1 || groups > 4096) return fail(MOE_ERR_INVALID_ARG, "groups must be in [1, 4096]");
@@ -688,7 +691,8 @@ moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, 
   if (rows < 0 || rows >= (int64_t{1} << 31)) return fail(MOE_ERR_INVALID_ARG, "rows must be in [0, 2^31)");
   if (N < 64 || K < 64 || N % 64 || K % 64) return fail(MOE_ERR_INVALID_ARG, "N and K must be positive multiples of 64");
   if (static_cast<int64_t>(N) * K * 4 >= (int64_t{1} << 40)) return fail(MOE_ERR_INVALID_ARG, "dW group too large");
-  return run_wgrad(cfg->act_dtype, cfg->wgrad_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream));
+  if (accumulate != 0 && accumulate != 1) return fail(MOE_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  return run_wgrad(cfg->act_dtype, cfg->wgrad_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream), accumulate);
 }
 
 moe_status_t moe_quantize_fp8(int32_t src_dtype, const void* src, int64_t rows, int32_t cols, int32_t block_rows,
@@ -774,6 +778,8 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_NEED(sv->row_of); MOE_NEED16(sv->Y_perm); MOE_NEED(gr->dWg);
   if (!(daux > -INFINITY && daux < INFINITY)) return fail(MOE_ERR_INVALID_ARG, "daux must be finite");
   if (cfg->seq_aux_coeff != 0.0f && daux != 0.0f) MOE_NEED(sv->seq_counts);
+  if (gr->accumulate != 0 && gr->accumulate != 1) return fail(MOE_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  const int beta = gr->accumulate;
   if (cfg->w_dtype == MOE_FP8_E4M3) {
     // frozen e4m3 experts: the backward runs through the mixing weights only
     if (gr->dW13 || gr->dW2 || gr->dW13s || gr->dW2s)
@@ -785,7 +791,7 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
     MOE_TRY(launch_combine_bwd(c, dy, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, nullptr, bw.dw,
                                nullptr, nullptr, nullptr, nullptr, s));
     MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, sv->seq_counts, daux, bw.dlogits, s));
-    return run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, dx, bw.gate, s);
+    return run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, dx, bw.gate, s, beta);
   }
   MOE_NEED16(sv->x_perm); MOE_NEED16(sv->H); MOE_NEED16(sv->Act); MOE_NEED16(gr->dW13); MOE_NEED16(gr->dW2);
   if (cfg->Fs) {
@@ -809,10 +815,10 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_TRY(fork(s, ss->dy, ss->s));  // dY_perm (and the shared expert's dY) ready
   MOE_TRY(run_experts_bwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, sv->H, sv->Act, bw.dY, bw.dH, bw.dX, gr->dW13,
                           gr->dW2, x, W->W13s, W->W2s, sv->H_s, sv->Act_s, dY_s, bw.dH_s, bw.dx_s, gr->dW13s,
-                          gr->dW2s, bw.sched, bw.dact, s, ss->s, ss->dh));
+                          gr->dW2s, bw.sched, bw.dact, s, ss->s, ss->dh, beta));
   MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, sv->seq_counts, daux, bw.dlogits, s));
-  MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, bw.gate, s));
-  if (c.shared_gate) MOE_TRY(launch_shared_gate_bwd(c, x, bw.dl_s, gr->dWsg, bw.sg_part, s));
+  MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, bw.gate, s, beta));
+  if (c.shared_gate) MOE_TRY(launch_shared_gate_bwd(c, x, bw.dl_s, gr->dWsg, bw.sg_part, s, beta));
   MOE_TRY(launch_unpermute_reduce(c, bw.dX, sv->row_of, c.Fs ? static_cast<const float*>(bw.dx_s) : nullptr,
                                   bw.dx_r, c.shared_gate ? bw.dl_s : nullptr, c.shared_gate ? W->Wsg : nullptr, dx,
                                   s));

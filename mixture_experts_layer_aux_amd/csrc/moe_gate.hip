@@ -35,10 +35,11 @@ __global__ __launch_bounds__(256) void split_parts_kernel(const float* __restric
   for (int q = 0; q < nslot; ++q) o[q * slot_stride] = p[(pat >> (2 * q)) & 3u];
 }
 
-// out[r][c] = (in[r][c] + in[r][c + stride]) + in[r][c + 2 stride] (+ bias[c])
+// out[r][c] = (in[r][c] + in[r][c + stride]) + in[r][c + 2 stride] (+ bias[c]), added into
+// out when beta
 __global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict__ in, int64_t rows, int cols,
                                                         int64_t in_ld, int64_t stride, float* __restrict__ out,
-                                                        int64_t out_ld, const float* __restrict__ bias) {
+                                                        int64_t out_ld, const float* __restrict__ bias, int beta) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= rows * cols) return;
   const int64_t r = i / cols;
@@ -46,6 +47,7 @@ __global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict_
   const float* p = in + r * in_ld + c;
   float v = (p[0] + p[stride]) + p[2 * stride];
   if (bias) v += bias[c];
+  if (beta) v = out[r * out_ld + c] + v;
   out[r * out_ld + c] = v;
 }
 
@@ -62,12 +64,12 @@ __global__ __launch_bounds__(256) void colsum_part_kernel(const float* __restric
   part[static_cast<int64_t>(blockIdx.y) * cols + col] = s;
 }
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int nchunk, int cols,
-                                                           float* __restrict__ out) {
+                                                           float* __restrict__ out, int beta) {
   const int col = blockIdx.x * 256 + threadIdx.x;
   if (col >= cols) return;
   float s = 0.0f;
   for (int q = 0; q < nchunk; ++q) s += part[static_cast<int64_t>(q) * cols + col];
-  out[col] = s;
+  out[col] = beta ? out[col] + s : s;
 }
 
 // slot patterns (2 bits per slot: part index 0 = hi, 1 = mid, 2 = lo)
@@ -84,10 +86,10 @@ moe_status_t split(const float* src, int64_t rows, int cols, uint16_t* out, int6
 }
 
 moe_status_t sum3(const float* in, int64_t rows, int cols, int64_t in_ld, int64_t stride, float* out, int64_t out_ld,
-                  const float* bias, hipStream_t s) {
+                  const float* bias, hipStream_t s, int beta = 0) {
   const int64_t n = rows * cols;
   if (n == 0) return MOE_OK;
-  sum_parts_kernel<<<ceil_div(n, 256), 256, 0, s>>>(in, rows, cols, in_ld, stride, out, out_ld, bias);
+  sum_parts_kernel<<<ceil_div(n, 256), 256, 0, s>>>(in, rows, cols, in_ld, stride, out, out_ld, bias, beta);
   return check_launch("gate sum");
 }
 
@@ -129,16 +131,16 @@ moe_status_t launch_gate_fwd_mfma(const moe_config_t& c, const void* x, const fl
   return sum3(C3, c.T, c.E, 3 * c.E, c.E, logits, c.E, bg, s);
 }
 
-moe_status_t launch_colsum_ws(const float* X, int rows, int cols, float* out, float* part, hipStream_t s) {
+moe_status_t launch_colsum_ws(const float* X, int rows, int cols, float* out, float* part, hipStream_t s, int beta) {
   const int nchunk = static_cast<int>(ceil_div(rows, kColChunk));
   if (nchunk == 0) return MOE_OK;
   colsum_part_kernel<<<dim3(static_cast<unsigned>(ceil_div(cols, 256)), nchunk), 256, 0, s>>>(X, rows, cols, part);
-  colsum_final_kernel<<<static_cast<unsigned>(ceil_div(cols, 256)), 256, 0, s>>>(part, nchunk, cols, out);
+  colsum_final_kernel<<<static_cast<unsigned>(ceil_div(cols, 256)), 256, 0, s>>>(part, nchunk, cols, out, beta);
   return check_launch("colsum");
 }
 
 moe_status_t launch_gate_bwd_mfma(const moe_config_t& c, const void* x, const float* Wg, const float* dlogits,
-                                  float* dWg, float* dbg, float* dx_r, void* ws, hipStream_t s) {
+                                  float* dWg, float* dbg, float* dx_r, void* ws, hipStream_t s, int beta) {
   const int64_t T = c.T, E = c.E, d = c.d;
   char* p = static_cast<char*>(ws);
   float* part = reinterpret_cast<float*>(carve(p, ceil_div(c.T, kColChunk) * E * 4));
@@ -155,8 +157,8 @@ moe_status_t launch_gate_bwd_mfma(const moe_config_t& c, const void* x, const fl
   gw.A = D3; gw.lda = 3 * E; gw.B = x; gw.ldb = d; gw.C = C3; gw.ldc = d;
   gw.range_end = c.T; gw.G = 1;
   MOE_TRY_INTERNAL(launch_gemm_mfma(gw, nullptr, s));
-  MOE_TRY_INTERNAL(sum3(C3, E, c.d, d, E * d, dWg, d, nullptr, s));
-  if (dbg) MOE_TRY_INTERNAL(launch_colsum_ws(dlogits, c.T, c.E, dbg, part, s));
+  MOE_TRY_INTERNAL(sum3(C3, E, c.d, d, E * d, dWg, d, nullptr, s, beta));
+  if (dbg) MOE_TRY_INTERNAL(launch_colsum_ws(dlogits, c.T, c.E, dbg, part, s, beta));
   if (dx_r) {
     // dx_r = dlogits Wg: six part products stacked along the reduction
     MOE_TRY_INTERNAL(split(dlogits, T, c.E, A6, 6 * E, E, 6, kPatA6, s));

@@ -86,6 +86,7 @@ __global__ __launch_bounds__(256) void gemm_fma_kernel(GemmDesc g) {
       if (n >= g.N) continue;
       float v = acc[i][j];
       if (EPI == EPI_STORE_BIAS) v += g.bias[n];
+      if (g.beta) v += C[(int64_t)m * g.ldc + n];
       C[(int64_t)m * g.ldc + n] = v;
     }
   }

@@ -85,6 +85,7 @@ struct MfmaArgs {
   int G, M, N, K, F, range_end, nN, nM;
   int b_rows_bytes;  // K-major B: bytes of one group's weight matrix (bounds the DMA)
   Glu glu;           // SwiGLU epilogues: the gated activation
+  int beta;          // EPI_STORE: 1 = add into C
 };
 
 // K-contiguous layout: element (r, k) of a stage tile at r * BK + ((k/8) ^ swk(r)) * 8 + k%8
@@ -308,7 +309,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
   const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
   if (RAG == RAGGED_K && EPI == EPI_STORE && nk == 0) {
     // A group without rows: its gradient tile is exact zeros, written straight out with
-    // 16-byte stores along whole tile rows (no accumulators, no LDS staging, no barrier).
+    // 16-byte stores along whole tile rows (no accumulators, no LDS staging, no barrier);
+    // accumulating into C leaves it as it is.
+    if (p.beta) return;
     constexpr int EB = OUT_F32 ? 4 : 2;    // bytes per output element
     constexpr int TPR = BN * EB / 16;      // threads per tile row
     constexpr int RPI = NTHR / TPR;        // tile rows per pass of the workgroup
@@ -485,10 +488,24 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
           *reinterpret_cast<uint2*>(drow + col) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
           *reinterpret_cast<uint2*>(drow + p.F + col) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
         } else if (OUT_F32) {
-          *reinterpret_cast<float4*>(Cf + static_cast<int64_t>(row) * p.ldc + col) = v;
+          float4* dst = reinterpret_cast<float4*>(Cf + static_cast<int64_t>(row) * p.ldc + col);
+          if (p.beta) {
+            const float4 o = *dst;
+            *dst = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+          } else {
+            *dst = v;
+          }
         } else {
-          *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * p.ldc + col) =
-              make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+          uint2* dst = reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * p.ldc + col);
+          float4 w = v;
+          if (p.beta) {   // one rounding of old + fp32 accumulator
+            const uint2 o = *dst;
+            w.x += __uint_as_float(o.x << 16);
+            w.y += __uint_as_float(o.x & 0xFFFF0000u);
+            w.z += __uint_as_float(o.y << 16);
+            w.w += __uint_as_float(o.y & 0xFFFF0000u);
+          }
+          *dst = make_uint2(pack_bf16x2(w.x, w.y), pack_bf16x2(w.z, w.w));
         }
       }
     }
@@ -532,6 +549,7 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
   a.F = g.F;
   a.range_end = g.range_end;
   a.glu = g.glu;
+  a.beta = g.beta;
   if (g.b_major == K_MAJOR) {
     const int64_t bytes = static_cast<int64_t>(g.epi == EPI_SWIGLU_FWD ? 2 * g.F : g.N) * g.ldb * 2;
     if (bytes >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: weight matrix above 2 GB");

@@ -55,7 +55,7 @@ moe_status_t launch_combine_bwd(const moe_config_t& c, const float* dy, const fl
 size_t shared_gate_part_bytes(const moe_config_t& c);
 moe_status_t launch_shared_gate(const moe_config_t& c, const void* x, const float* Wsg, float* gs, hipStream_t s);
 moe_status_t launch_shared_gate_bwd(const moe_config_t& c, const void* x, const float* dl_s, float* dWsg,
-                                    float* part, hipStream_t s);
+                                    float* part, hipStream_t s, int beta = 0);
 
 #define MOE_TRY_INTERNAL(x)      \
   do {                           \
@@ -72,9 +72,10 @@ size_t gate_bwd_ws_bytes(const moe_config_t& c);
 moe_status_t launch_gate_fwd_mfma(const moe_config_t& c, const void* x, const float* Wg, const float* bg,
                                   float* logits, void* ws, hipStream_t s);
 moe_status_t launch_gate_bwd_mfma(const moe_config_t& c, const void* x, const float* Wg, const float* dlogits,
-                                  float* dWg, float* dbg, float* dx_r, void* ws, hipStream_t s);
+                                  float* dWg, float* dbg, float* dx_r, void* ws, hipStream_t s, int beta = 0);
 // column sums in a fixed order; part: ceil(rows / 256) * cols floats of scratch
-moe_status_t launch_colsum_ws(const float* X, int rows, int cols, float* out, float* part, hipStream_t s);
+moe_status_t launch_colsum_ws(const float* X, int rows, int cols, float* out, float* part, hipStream_t s,
+                              int beta = 0);
 
 // ---------------------------------------------------------------- fp8 experts
 moe_status_t launch_quantize_fp8(int src_dtype, const void* src, int64_t rows, int cols, int block_rows, uint8_t* q,
@@ -113,6 +114,7 @@ struct GemmDesc {
   const float* bias;            // EPI_STORE_BIAS: [N]
   int F;                        // SwiGLU: offset of the up half (columns of H / rows of W13)
   Glu glu;                      // SwiGLU epilogues: the gated activation (zero: plain SwiGLU)
+  int beta;                     // EPI_STORE: 1 = add into C (accumulate), 0 = overwrite
   const int32_t* offsets;
   int G;
   int range_end;

@@ -402,12 +402,12 @@ __global__ __launch_bounds__(256) void shared_gate_wgrad_part_kernel(const void*
   part[static_cast<int64_t>(blockIdx.y) * d + c] = acc;
 }
 __global__ __launch_bounds__(256) void shared_gate_wgrad_final_kernel(const float* __restrict__ part, int nchunk,
-                                                                      int d, float* __restrict__ dWsg) {
+                                                                      int d, float* __restrict__ dWsg, int beta) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= d) return;
   float acc = 0.0f;
   for (int q = 0; q < nchunk; ++q) acc += part[static_cast<int64_t>(q) * d + c];
-  dWsg[c] = acc;
+  dWsg[c] = beta ? dWsg[c] + acc : acc;
 }
 
 }  // namespace
@@ -463,14 +463,14 @@ moe_status_t launch_shared_gate(const moe_config_t& c, const void* x, const floa
 }
 
 moe_status_t launch_shared_gate_bwd(const moe_config_t& c, const void* x, const float* dl_s, float* dWsg,
-                                    float* part, hipStream_t s) {
+                                    float* part, hipStream_t s, int beta) {
   const int nchunk = static_cast<int>(ceil_div(c.T, kGateChunk));
   const dim3 grid(static_cast<unsigned>(ceil_div(c.d, 256)), static_cast<unsigned>(nchunk));
   if (c.act_dtype == MOE_BF16)
     shared_gate_wgrad_part_kernel<uint16_t><<<grid, 256, 0, s>>>(x, dl_s, c.T, c.d, part);
   else
     shared_gate_wgrad_part_kernel<float><<<grid, 256, 0, s>>>(x, dl_s, c.T, c.d, part);
-  shared_gate_wgrad_final_kernel<<<static_cast<int>(ceil_div(c.d, 256)), 256, 0, s>>>(part, nchunk, c.d, dWsg);
+  shared_gate_wgrad_final_kernel<<<static_cast<int>(ceil_div(c.d, 256)), 256, 0, s>>>(part, nchunk, c.d, dWsg, beta);
   return check_launch("shared_gate_bwd");
 }
 
