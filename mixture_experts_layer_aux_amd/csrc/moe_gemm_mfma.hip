@@ -31,6 +31,8 @@
 //   * the epilogue stages the tile through LDS in two passes of 128 rows and then works on
 //     whole tile rows, so its global loads and stores are contiguous runs of a row (a 1 KB
 //     row of fp32 per store instruction) rather than 16 bytes of each of 32 rows;
+//   * in an expert's last row tile, the 32-row accumulator blocks past its end skip their
+//     fragment reads and MFMAs (a wave-uniform branch around a second copy of the loop);
 //   * a device-built tile list (per-expert prefix of row tiles) so the host never reads
 //     the expert counts; empty experts get no tiles (forward) or exact-zero gradients
 //     (weight gradient, zero-length reduction);
@@ -42,6 +44,8 @@
 //   * fused epilogues: SwiGLU (forward: H in fp32 and Act in bf16 from the same
 //     accumulators, the gate and up rows of W13 interleaved per 32-row block of the B
 //     tile) and the SwiGLU backward (reads the saved fp32 H, writes dH in bf16).
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -335,40 +339,57 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
     // the slot of stage it-1, which both groups finished reading one barrier earlier.
     constexpr int D = STAGES - 1;
     const bool late = wm == 1;
+    // This wave's 32-row accumulator blocks that hold rows of the group.  In a group's last
+    // row tile the blocks past its end are padding that the epilogue never stores: their
+    // fragment reads and MFMAs are skipped (the loads still run, every wave takes its part
+    // of each stage's DMA).  Wave-uniform, so the skip is a scalar branch.
+    const int vi = __builtin_amdgcn_readfirstlane(min(NI, max(0, (row_end - row_begin - wm * WTM + 31) / 32)));
 #pragma unroll
     for (int st = 0; st < D; ++st)
       if (st < nk) issue_stage(st);
     wait_vm(max(0, min(D, nk) - 1) * NDMA);
     block_barrier();
     if (late) block_barrier();
-    for (int it = 0; it < nk; ++it) {
-      const uint16_t* As = lds + (it % STAGES) * STAGE_ELEMS;
-      const uint16_t* Bs = As + TILE;
-      bf16x8_t fa[BK / 16][NI], fb[BK / 16][NJ];
+    // FULL: every block of the wave is live (all but the last row tile of a group); the
+    // partial copy of the loop differs only by the per-block guards.
+    auto main_loop = [&](auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      for (int it = 0; it < nk; ++it) {
+        const uint16_t* As = lds + (it % STAGES) * STAGE_ELEMS;
+        const uint16_t* Bs = As + TILE;
+        bf16x8_t fa[BK / 16][NI], fb[BK / 16][NJ];
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
+        for (int ks = 0; ks < BK / 16; ++ks) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) fa[ks][i] = frag(As, AMAJ, wm * WTM + i * 32, ks);
+          for (int i = 0; i < NI; ++i)
+            if (FULL || i < vi) fa[ks][i] = frag(As, AMAJ, wm * WTM + i * 32, ks);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) fb[ks][j] = frag(Bs, BMAJ, wn * WTN + j * 32, ks);
+          for (int j = 0; j < NJ; ++j) fb[ks][j] = frag(Bs, BMAJ, wn * WTN + j * 32, ks);
+        }
+        if (it + D < nk) issue_stage(it + D);
+        wait_lgkm0();  // fragments in registers before the slot may be refilled
+        wait_vm(max(0, min(it + D, nk - 1) - (it + 1)) * NDMA);  // own part of stage it+1 landed
+        __builtin_amdgcn_sched_barrier(0);
+        block_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+            if (FULL || i < vi) {
+#pragma unroll
+              for (int j = 0; j < NJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        block_barrier();
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (it + D < nk) issue_stage(it + D);
-      wait_lgkm0();  // fragments in registers before the slot may be refilled
-      wait_vm(max(0, min(it + D, nk - 1) - (it + 1)) * NDMA);  // own part of stage it+1 landed
-      __builtin_amdgcn_sched_barrier(0);
-      block_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks)
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      block_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    if (vi == NI)
+      main_loop(std::true_type{});
+    else
+      main_loop(std::false_type{});
     if (!late) block_barrier();
   } else {
     // prologue: stages 0 .. STAGES-2 in flight
