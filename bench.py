@@ -452,8 +452,8 @@ def main() -> int:
         L.grouped_wgrad(cfg, S["offsets"], E, A, dH, 2 * F, S["x_perm"], d, G["dW13"])
         mark()
         if Fs:
-            L.grouped_wgrad(cfg, None, 1, T, dH_s, 2 * Fs, x, d, G["dW13s"])
-            L.grouped_wgrad(cfg, None, 1, T, dY_s, d, S["Act_s"], Fs, G["dW2s"])
+            L.grouped_wgrad(cfg, None, 1, T, dH_s, 2 * Fs, x, d, G["dW13s"], ws=ws)
+            L.grouped_wgrad(cfg, None, 1, T, dY_s, d, S["Act_s"], Fs, G["dW2s"], ws=ws)
         mark()
         L.router_bwd(cfg, S["logits"], S["idx"], S["w"], dw, S["counts"], 1.0, dlogits)
         mark()

@@ -339,12 +339,20 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
  * The routed experts: (dH, x_perm) -> dW13 with N = 2F, K = d, and (dY_perm, Act) -> dW2
  * with N = d, K = F.  offsets NULL: one group over rows [0, rows) (the shared expert, on
  * all T tokens).  A group with no rows gets exact zeros.  offsets[groups] <= rows is the
- * caller's promise (device data is not read on the host).  One kernel launch.
+ * caller's promise (device data is not read on the host).  One kernel launch, except:
+ * ws (optional, 16-byte aligned) lets a one-group bf16 call whose dW has fewer than 128
+ * tiles of 256 x 256 (a shared expert's narrow projections) split its rows into up to 8
+ * chunks of at least 256 rows: fp32 partials in ws, then one kernel sums them in chunk order
+ * (so the result is deterministic, and bit-equal to moe_layer_bwd's and
+ * moe_grouped_gemm_swiglu_bwd's shared-expert gradients, which split the same way).  The
+ * split needs chunks * N * K * 4 bytes of ws (at most 32 N K); the backward workspace of
+ * moe_workspace_size covers the shared expert's two calls.  ws NULL: no split.
  * Errors: groups outside [1, 4096], groups != 1 without offsets, rows outside [0, 2^31),
- * N or K not a positive multiple of 64, accumulate not 0 or 1 -> MOE_ERR_INVALID_ARG. */
+ * N or K not a positive multiple of 64, accumulate not 0 or 1 -> MOE_ERR_INVALID_ARG; ws
+ * given but smaller than a split needs -> MOE_ERR_WORKSPACE. */
 moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, int32_t groups, int64_t rows,
                                const void* dY, int32_t N, const void* X, int32_t K, void* dW, int32_t accumulate,
-                               void* stream);
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- fp8 experts
  * e4m3 block quantiser (the fp8 recipe is a reading: the pages leave low-precision expert

@@ -311,9 +311,10 @@ def grouped_gemm_swiglu_bwd(cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, 
         _P(_stream(stream))))
 
 
-def grouped_wgrad(cfg, offsets, groups, rows, dY, N, X, K, dW, stream=None, accumulate=False):
+def grouped_wgrad(cfg, offsets, groups, rows, dY, N, X, K, dW, stream=None, accumulate=False, ws=None):
     """dW[g] = dY_g^T X_g per group of rows (offsets None: one group of `rows` rows);
-    accumulate: dW[g] += dY_g^T X_g."""
+    accumulate: dW[g] += dY_g^T X_g; ws: scratch that lets a one-group call split its rows."""
+    wp, wn = _ws(ws) if ws is not None else (None, 0)
     ad = act_dtype(cfg)
     if offsets is not None and offsets.numel() != groups + 1:
         raise ValueError(f"offsets: expected {groups + 1} entries, got {offsets.numel()}")
@@ -321,7 +322,7 @@ def grouped_wgrad(cfg, offsets, groups, rows, dY, N, X, K, dW, stream=None, accu
         ctypes.byref(cfg), _P(_ptr(offsets, torch.int32, groups + 1, "offsets")), ctypes.c_int32(groups),
         ctypes.c_int64(rows), _P(_ptr(dY, ad, rows * N, "dY")), ctypes.c_int32(N), _P(_ptr(X, ad, rows * K, "X")),
         ctypes.c_int32(K), _P(_ptr(dW, wgrad_dtype(cfg), groups * N * K, "dW")), ctypes.c_int32(int(accumulate)),
-        _P(_stream(stream))))
+        _P(wp), ctypes.c_size_t(wn), _P(_stream(stream))))
 
 
 def quantize_fp8(src, block_rows, q, scale, stream=None):

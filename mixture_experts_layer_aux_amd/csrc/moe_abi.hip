@@ -111,6 +111,7 @@ struct BwdWs {
   float* dl_s;     // [T]: the shared gate's logit gradient
   float* sg_part;  // shared_gate_part_bytes: partial sums of its weight gradient
   float* dact;     // fp32 path: [max(A, T), max(F, Fs)]
+  float* wsplit;   // bf16 shared expert: split-K partials of its weight gradients (or NULL)
   int32_t* sched;  // [E + 1]
   void* gate;      // router GEMM scratch (gate_bwd_ws_bytes)
   size_t bytes;
@@ -138,6 +139,10 @@ BwdWs carve_bwd(const moe_config_t& c, void* base) {
   w.dl_s = c.shared_gate ? reinterpret_cast<float*>(take(T * 4)) : nullptr;
   w.sg_part = c.shared_gate ? reinterpret_cast<float*>(take(shared_gate_part_bytes(c))) : nullptr;
   w.dact = c.act_dtype == MOE_F32 ? reinterpret_cast<float*>(take(std::max(A, T) * std::max(c.F, c.Fs) * 4)) : nullptr;
+  const size_t split = c.Fs && c.act_dtype == MOE_BF16
+                           ? std::max(wgrad_split_bytes(c.d, c.Fs, c.T), wgrad_split_bytes(2 * c.Fs, c.d, c.T))
+                           : 0;
+  w.wsplit = split ? reinterpret_cast<float*>(take(split)) : nullptr;
   w.sched = reinterpret_cast<int32_t*>(take(mfma_schedule_bytes(c.E)));
   w.gate = take(gate_bwd_ws_bytes(c));
   w.bytes = off;
@@ -334,9 +339,11 @@ moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const in
 }
 
 // dW[g] = dY_g^T X_g over the rows of each group (reduction-ragged); fp32 accumulation,
-// output in the weight-gradient dtype.
+// output in the weight-gradient dtype.  A one-group bf16 call with split_ws (at least
+// wgrad_split_bytes(N, K, rows)) is split over its rows when its output has too few tiles:
+// fp32 partials per row chunk, then their sum in chunk order.
 moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G, int64_t rows, const void* dY, int N,
-                       const void* X, int K, void* dW, hipStream_t s, int beta) {
+                       const void* X, int K, void* dW, hipStream_t s, int beta, float* split_ws = nullptr) {
   GemmDesc w{};
   w.a_major = MN_MAJOR; w.b_major = MN_MAJOR; w.ragged = RAGGED_K; w.epi = EPI_STORE;
   w.a_type = w.b_type = act_dtype;
@@ -346,6 +353,14 @@ moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G
   w.C = dW; w.ldc = K; w.c_gstride = int64_t{1} * N * K;
   w.offsets = off; w.G = G; w.range_end = static_cast<int>(rows);
   w.beta = beta;
+  if (act_dtype == MOE_BF16 && !off && split_ws) {
+    const WgradSplit sp = wgrad_split(N, K, rows);
+    if (sp.chunks > 1) {
+      w.c_type = MOE_F32; w.C = split_ws; w.G = sp.chunks; w.kchunk = sp.kchunk; w.beta = 0;
+      MOE_TRY(launch_gemm_mfma(w, nullptr, s));
+      return launch_splitk_reduce(split_ws, sp.chunks, int64_t{1} * N * K, dW, wgrad_dtype, beta, s);
+    }
+  }
   return act_dtype == MOE_BF16 ? launch_gemm_mfma(w, nullptr, s) : launch_gemm_fma(w, s);
 }
 
@@ -366,7 +381,7 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
                              const void* W2, const void* H, const void* Act, const void* dY_perm, void* dH,
                              void* dX_perm, void* dW13, void* dW2, const void* x, const void* W13s, const void* W2s,
                              const void* H_s, const void* Act_s, const void* dY_s, void* dH_s, void* dx_s,
-                             void* dW13s, void* dW2s, int32_t* sched, float* dact, hipStream_t s,
+                             void* dW13s, void* dW2s, int32_t* sched, float* dact, float* wsplit, hipStream_t s,
                              hipStream_t s2 = nullptr, hipEvent_t ev_dh = nullptr, int beta = 0) {
   // s2 (when given, with dY_perm and dX_perm distinct) runs the weight gradients; its
   // caller has made it wait for dY_perm and joins it back.
@@ -419,11 +434,12 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
                                             rows, F, s));
     }
     // (2) fc2 weight gradient dW2 = dY^T Act, queued before dX may overwrite an aliased dY
-    if (dw2) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dY, c.d, act, F, dw2, s2, beta));
+    float* sw = shared ? wsplit : nullptr;   // both shared weight gradients run on s2, one after the other
+    if (dw2) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dY, c.d, act, F, dw2, s2, beta, sw));
     MOE_TRY(fork(s, ev_dh, s2));  // dH ready for the fc1 weight gradient
     MOE_TRY(et == MOE_BF16 ? launch_gemm_mfma(d1, sched, s) : launch_gemm_fma(d1, s));
     // (4) fc1 weight gradient dW13 = dH^T X
-    if (dw13) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dh, 2 * F, X, c.d, dw13, s2, beta));
+    if (dw13) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dh, 2 * F, X, c.d, dw13, s2, beta, sw));
   }
   return MOE_OK;
 }
@@ -678,12 +694,12 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
   const BwdWs bw = carve_bwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, bw.bytes, __func__));
   return run_experts_bwd(*cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, dX_perm, dW13, dW2, x, W13s, W2s, H_s,
-                         Act_s, dY_s, dH_s, dx_s, dW13s, dW2s, bw.sched, bw.dact, S(stream));
+                         Act_s, dY_s, dH_s, dx_s, dW13s, dW2s, bw.sched, bw.dact, bw.wsplit, S(stream));
 }
 
 moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, int32_t groups, int64_t rows,
                                const void* dY, int32_t N, const void* X, int32_t K, void* dW, int32_t accumulate,
-                               void* stream) {
+                               void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED16(dY); MOE_NEED16(X); MOE_NEED16(dW);
   if (groups < 1 || groups > 4096) return fail(MOE_ERR_INVALID_ARG, "groups must be in [1, 4096]");
@@ -692,7 +708,17 @@ moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, 
   if (N < 64 || K < 64 || N % 64 || K % 64) return fail(MOE_ERR_INVALID_ARG, "N and K must be positive multiples of 64");
   if (static_cast<int64_t>(N) * K * 4 >= (int64_t{1} << 40)) return fail(MOE_ERR_INVALID_ARG, "dW group too large");
   if (accumulate != 0 && accumulate != 1) return fail(MOE_ERR_INVALID_ARG, "accumulate must be 0 or 1");
-  return run_wgrad(cfg->act_dtype, cfg->wgrad_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream), accumulate);
+  float* split = nullptr;
+  if (ws && !offsets && cfg->act_dtype == MOE_BF16) {
+    const size_t need = wgrad_split_bytes(N, K, rows);
+    if (need) {
+      MOE_TRY(need_ws(ws_bytes, need, __func__));
+      if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+      split = static_cast<float*>(ws);
+    }
+  }
+  return run_wgrad(cfg->act_dtype, cfg->wgrad_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream), accumulate,
+                   split);
 }
 
 moe_status_t moe_quantize_fp8(int32_t src_dtype, const void* src, int64_t rows, int32_t cols, int32_t block_rows,
@@ -815,7 +841,7 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_TRY(fork(s, ss->dy, ss->s));  // dY_perm (and the shared expert's dY) ready
   MOE_TRY(run_experts_bwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, sv->H, sv->Act, bw.dY, bw.dH, bw.dX, gr->dW13,
                           gr->dW2, x, W->W13s, W->W2s, sv->H_s, sv->Act_s, dY_s, bw.dH_s, bw.dx_s, gr->dW13s,
-                          gr->dW2s, bw.sched, bw.dact, s, ss->s, ss->dh, beta));
+                          gr->dW2s, bw.sched, bw.dact, bw.wsplit, s, ss->s, ss->dh, beta));
   MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, sv->seq_counts, daux, bw.dlogits, s));
   MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, bw.gate, s, beta));
   if (c.shared_gate) MOE_TRY(launch_shared_gate_bwd(c, x, bw.dl_s, gr->dWsg, bw.sg_part, s, beta));

@@ -105,7 +105,10 @@ size_t gate_fwd_ws_bytes(const moe_config_t& c) {
 size_t gate_bwd_ws_bytes(const moe_config_t& c) {
   const size_t T = c.T, E = c.E, d = c.d;
   size_t b = ceil_div(c.T, kColChunk) * E * 4 + 256;
-  if (gate_on_mfma(c)) b += T * 3 * E * 2 + 256 + T * 6 * E * 2 + 256 + 6 * E * d * 2 + 256 + 3 * E * d * 4 + 256;
+  if (gate_on_mfma(c)) {
+    b += T * 3 * E * 2 + 256 + T * 6 * E * 2 + 256 + 6 * E * d * 2 + 256 + 3 * E * d * 4 + 256;
+    b += wgrad_split_bytes(3 * c.E, c.d, c.T) + 256;   // split-K partials of dWg
+  }
   return b;
 }
 
@@ -148,7 +151,11 @@ moe_status_t launch_gate_bwd_mfma(const moe_config_t& c, const void* x, const fl
   uint16_t* A6 = reinterpret_cast<uint16_t*>(carve(p, T * 6 * E * 2));
   uint16_t* B6 = reinterpret_cast<uint16_t*>(carve(p, 6 * E * d * 2));
   float* C3 = reinterpret_cast<float*>(carve(p, 3 * E * d * 4));
-  // dWg = dlogits^T x: the three parts of dlogits side by side in each row
+  // dWg = dlogits^T x: the three parts of dlogits side by side in each row.  Its [3E, d]
+  // output has few tiles (48 at E = 512, d = 2048) for a reduction over all T tokens, so
+  // the tokens are split into chunks whose fp32 partials are summed in chunk order first.
+  const WgradSplit sp = wgrad_split(3 * c.E, c.d, c.T);
+  float* P = reinterpret_cast<float*>(carve(p, wgrad_split_bytes(3 * c.E, c.d, c.T)));
   MOE_TRY_INTERNAL(split(dlogits, T, c.E, D3, 3 * E, E, 3, kPat3, s));
   GemmDesc gw{};
   gw.a_major = MN_MAJOR; gw.b_major = MN_MAJOR; gw.ragged = RAGGED_K; gw.epi = EPI_STORE;
@@ -156,7 +163,13 @@ moe_status_t launch_gate_bwd_mfma(const moe_config_t& c, const void* x, const fl
   gw.M = 3 * c.E; gw.N = c.d;
   gw.A = D3; gw.lda = 3 * E; gw.B = x; gw.ldb = d; gw.C = C3; gw.ldc = d;
   gw.range_end = c.T; gw.G = 1;
-  MOE_TRY_INTERNAL(launch_gemm_mfma(gw, nullptr, s));
+  if (sp.chunks > 1) {
+    gw.C = P; gw.c_gstride = 3 * E * d; gw.G = sp.chunks; gw.kchunk = sp.kchunk;
+    MOE_TRY_INTERNAL(launch_gemm_mfma(gw, nullptr, s));
+    MOE_TRY_INTERNAL(launch_splitk_reduce(P, sp.chunks, 3 * E * d, C3, MOE_F32, 0, s));
+  } else {
+    MOE_TRY_INTERNAL(launch_gemm_mfma(gw, nullptr, s));
+  }
   MOE_TRY_INTERNAL(sum3(C3, E, c.d, d, E * d, dWg, d, nullptr, s, beta));
   if (dbg) MOE_TRY_INTERNAL(launch_colsum_ws(dlogits, c.T, c.E, dbg, part, s, beta));
   if (dx_r) {

@@ -44,6 +44,7 @@
 //   * fused epilogues: SwiGLU (forward: H in fp32 and Act in bf16 from the same
 //     accumulators, the gate and up rows of W13 interleaved per 32-row block of the B
 //     tile) and the SwiGLU backward (reads the saved fp32 H, writes dH in bf16).
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -90,6 +91,7 @@ struct MfmaArgs {
   int b_rows_bytes;  // K-major B: bytes of one group's weight matrix (bounds the DMA)
   Glu glu;           // SwiGLU epilogues: the gated activation
   int beta;          // EPI_STORE: 1 = add into C
+  int kchunk;        // RAGGED_K without offsets: reduction rows per group (0: one group)
 };
 
 // K-contiguous layout: element (r, k) of a stage tile at r * BK + ((k/8) ^ swk(r)) * 8 + k%8
@@ -208,8 +210,13 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
     mt = band * WG_BAND + (rem - nt * bh);
     row_begin = mt * BM;
     row_end = p.M;
-    k_begin = p.offsets ? p.offsets[grp] : 0;
-    k_end = p.offsets ? p.offsets[grp + 1] : p.range_end;
+    if (p.offsets) {
+      k_begin = p.offsets[grp];
+      k_end = p.offsets[grp + 1];
+    } else {   // split-K chunks of one group (kchunk 0: the whole range)
+      k_begin = grp * p.kchunk;
+      k_end = p.kchunk ? min(p.range_end, k_begin + p.kchunk) : p.range_end;
+    }
   }
   const int n0 = nt * BN;
   const uint16_t* Bg = p.B + (RAG == RAGGED_M ? static_cast<int64_t>(grp) * p.b_gstride : 0);
@@ -534,6 +541,36 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
 }
 
 
+// out[i] = sum over s of part[s][i], s in order (+ out[i] when beta), four elements a lane
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t elems,
+                                                            void* __restrict__ out, int out_bf16, int beta) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= elems) return;
+  float4 v = *reinterpret_cast<const float4*>(part + i);
+  for (int q = 1; q < splits; ++q) {
+    const float4 u = *reinterpret_cast<const float4*>(part + q * elems + i);
+    v = make_float4(v.x + u.x, v.y + u.y, v.z + u.z, v.w + u.w);
+  }
+  if (out_bf16) {
+    uint2* dst = reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + i);
+    if (beta) {   // one rounding of old + the fp32 sum
+      const uint2 o = *dst;
+      v.x += __uint_as_float(o.x << 16);
+      v.y += __uint_as_float(o.x & 0xFFFF0000u);
+      v.z += __uint_as_float(o.y << 16);
+      v.w += __uint_as_float(o.y & 0xFFFF0000u);
+    }
+    *dst = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  } else {
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + i);
+    if (beta) {
+      const float4 o = *dst;
+      v = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+    }
+    *dst = v;
+  }
+}
+
 template <int AMAJ, int BMAJ, int RAG, int EPI, bool OUT_F32>
 void launch_kernel(const MfmaArgs& a, int64_t grid, hipStream_t s) {
   gemm_mfma_kernel<AMAJ, BMAJ, RAG, EPI, OUT_F32><<<static_cast<unsigned>(grid), NTHR, 0, s>>>(a);
@@ -542,6 +579,31 @@ void launch_kernel(const MfmaArgs& a, int64_t grid, hipStream_t s) {
 }  // namespace
 
 size_t mfma_schedule_bytes(int G) { return static_cast<size_t>(G + 1) * sizeof(int32_t); }
+
+// A one-group weight gradient whose output has fewer than 128 tiles (a shared expert's
+// narrow projections: 32 or 16 tiles on a chip of 256 CUs) is split over its reduction
+// rows into up to 8 chunks of at least 256 rows, so that about 256 workgroups run.
+WgradSplit wgrad_split(int M, int N, int64_t rows) {
+  const int64_t tiles = ceil_div(static_cast<int64_t>(M), BM) * ceil_div(static_cast<int64_t>(N), BN);
+  const int64_t want = std::min<int64_t>({8, 256 / std::max<int64_t>(tiles, 1), rows / 256});
+  if (tiles >= 128 || want < 2) return WgradSplit{1, static_cast<int>(rows)};
+  const int64_t chunk = ceil_div(ceil_div(rows, want), 64) * 64;
+  return WgradSplit{static_cast<int>(ceil_div(rows, chunk)), static_cast<int>(chunk)};
+}
+
+size_t wgrad_split_bytes(int M, int N, int64_t rows) {
+  const WgradSplit sp = wgrad_split(M, N, rows);
+  return sp.chunks > 1 ? static_cast<size_t>(sp.chunks) * M * N * sizeof(float) : 0;
+}
+
+moe_status_t launch_splitk_reduce(const float* part, int splits, int64_t elems, void* out, int out_dtype, int beta,
+                                  hipStream_t s) {
+  if (elems % 4) return fail(MOE_ERR_UNSUPPORTED, "split-K reduce: elements must be a multiple of 4");
+  if (elems > 0)
+    splitk_reduce_kernel<<<static_cast<unsigned>(ceil_div(elems / 4, 256)), 256, 0, s>>>(
+        part, splits, elems, out, out_dtype == MOE_BF16, beta);
+  return check_launch("splitk_reduce");
+}
 
 moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) {
   if (g.a_type != MOE_BF16 || g.b_type != MOE_BF16)
@@ -571,6 +633,7 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
   a.range_end = g.range_end;
   a.glu = g.glu;
   a.beta = g.beta;
+  a.kchunk = g.kchunk;
   if (g.b_major == K_MAJOR) {
     const int64_t bytes = static_cast<int64_t>(g.epi == EPI_SWIGLU_FWD ? 2 * g.F : g.N) * g.ldb * 2;
     if (bytes >= (int64_t{1} << 31)) return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: weight matrix above 2 GB");
@@ -590,7 +653,8 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
   } else {
     a.nM = static_cast<int>(ceil_div(g.M, BM));
     a.nN = static_cast<int>(ceil_div(g.N, BN));
-    grid = 8 * static_cast<int64_t>(g.offsets ? g.G : 1) * ceil_div(static_cast<int64_t>(a.nM) * a.nN, 8);
+    // groups: the offsets' groups, or the split-K chunks of one group
+    grid = 8 * static_cast<int64_t>(g.offsets || g.kchunk ? g.G : 1) * ceil_div(static_cast<int64_t>(a.nM) * a.nN, 8);
   }
   if (grid == 0) return MOE_OK;
 #define MOE_MF(AM, BMJ, RG, EP, OF)                                                              \

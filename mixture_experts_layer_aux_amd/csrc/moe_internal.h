@@ -115,6 +115,8 @@ struct GemmDesc {
   int F;                        // SwiGLU: offset of the up half (columns of H / rows of W13)
   Glu glu;                      // SwiGLU epilogues: the gated activation (zero: plain SwiGLU)
   int beta;                     // EPI_STORE: 1 = add into C (accumulate), 0 = overwrite
+  int kchunk;                   // RAGGED_K without offsets: group g owns reduction rows
+                                // [g kchunk, min(range_end, (g + 1) kchunk)) (0: one group)
   const int32_t* offsets;
   int G;
   int range_end;
@@ -131,5 +133,15 @@ moe_status_t launch_swiglu_bwd_elementwise(Glu glu, const float* H, const float*
 // bf16 MFMA grouped GEMM (gfx950 v_mfma_f32_32x32x16_bf16), fused epilogues.
 size_t mfma_schedule_bytes(int G);
 moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched_ws, hipStream_t s);
+// Split-K of a one-group weight gradient dW [M, N] over `rows` reduction rows: the row
+// chunk (a multiple of 64) and the number of chunks, 1 when the output alone has enough
+// tiles to fill the chip (then kchunk = rows).  Partials: chunks * M * N fp32.
+struct WgradSplit { int chunks; int kchunk; };
+WgradSplit wgrad_split(int M, int N, int64_t rows);
+size_t wgrad_split_bytes(int M, int N, int64_t rows);
+// out = sum of the `splits` fp32 partials [splits, elems] in order (+ out when beta), in the
+// weight-gradient dtype (bf16: rounded once).
+moe_status_t launch_splitk_reduce(const float* part, int splits, int64_t elems, void* out, int out_dtype, int beta,
+                                  hipStream_t s);
 
 }  // namespace moe

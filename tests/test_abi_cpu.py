@@ -233,16 +233,20 @@ def test_entry_points_reject_bad_arguments_before_launching():
     assert st == L.MOE_ERR_INVALID_ARG and b"counts" in lib.moe_last_error()
     # grouped weight gradient: group count, offsets and sizes are checked on the host
     i32, i64 = ctypes.c_int32, ctypes.c_int64
-    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(0), i64(64), fake, i32(64), fake, i32(64), fake, i32(0), s)
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(0), i64(64), fake, i32(64), fake, i32(64), fake, i32(0), nul, ctypes.c_size_t(0), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"groups" in lib.moe_last_error()
-    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), nul, i32(2), i64(64), fake, i32(64), fake, i32(64), fake, i32(0), s)
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), nul, i32(2), i64(64), fake, i32(64), fake, i32(64), fake, i32(0), nul, ctypes.c_size_t(0), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"one group" in lib.moe_last_error()
-    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(64), fake, i32(96), fake, i32(64), fake, i32(0), s)
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(64), fake, i32(96), fake, i32(64), fake, i32(0), nul, ctypes.c_size_t(0), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"multiples of 64" in lib.moe_last_error()
-    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(-1), fake, i32(64), fake, i32(64), fake, i32(0), s)
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(-1), fake, i32(64), fake, i32(64), fake, i32(0), nul, ctypes.c_size_t(0), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"rows" in lib.moe_last_error()
-    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(64), fake, i32(64), fake, i32(64), fake, i32(2), s)
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(64), fake, i32(64), fake, i32(64), fake, i32(2), nul, ctypes.c_size_t(0), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"accumulate" in lib.moe_last_error()
+    # a one-group weight gradient that would split its rows needs room for the partials
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), nul, i32(1), i64(1000), fake, i32(192), fake, i32(320), fake, i32(0),
+                               fake, ctypes.c_size_t(16), s)
+    assert st == L.MOE_ERR_WORKSPACE and str(3 * 192 * 320 * 4).encode() in lib.moe_last_error()
     # layer backward: the gradient structure's accumulate flag is 0 or 1
     w = L.Weights(Wg=fake, W13=fake, W2=fake)
     sv = L.Saved(logits=fake, idx=fake, w=fake, counts=fake, offsets=fake, row_of=fake, Y_perm=fake)

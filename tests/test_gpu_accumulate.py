@@ -154,3 +154,43 @@ def test_grouped_wgrad_accumulate(wgrad):
         ref = dY64[off[g]:off[g + 1]].T @ X64[off[g]:off[g + 1]]
         err = np.abs(got[g] - ref).max() / max(1.0, np.sqrt(max(sizes[g], 1)))
         assert err < 1e-4, f"group {g}: {err:.2e}"
+
+
+def test_grouped_wgrad_split_k():
+    """A one-group weight gradient with too few output tiles is split over its rows when a
+    workspace is given: 1000 rows in three chunks of 384, 384 and 232.  The split sum is
+    held to fp64, and to the unsplit call within fp32 rounding.  The bf16 output is the
+    split fp32 sum rounded once, and accumulating adds to it in fp32 first, bit for bit.
+    A workspace smaller than the partials is refused."""
+    torch = torch_mod()
+    from mixture_experts_layer_aux_amd import _lib as L
+    print("grouped wgrad split-K", flush=True)
+    shape = W.SMALL[2]
+    c16, c32 = L.config_from_shape(shape, wgrad="bf16"), L.config_from_shape(shape, wgrad="f32")
+    rng = np.random.default_rng(21)
+    rows, N, K = 1000, 192, 320
+    dY = rng.standard_normal((rows, N)).astype(np.float32)
+    X = rng.standard_normal((rows, K)).astype(np.float32)
+    bits = lambda a: torch.from_numpy(W.f32_to_bf16_bits(a).view(np.int16)).view(torch.bfloat16)  # noqa: E731
+    dY_d, X_d = bits(dY).to(dev()), bits(X).to(dev())
+    ws = torch.empty(3 * N * K * 4, dtype=torch.uint8, device=dev())
+    whole = torch.empty(N, K, dtype=torch.float32, device=dev())
+    L.grouped_wgrad(c32, None, 1, rows, dY_d, N, X_d, K, whole)
+    split32 = torch.empty(N, K, dtype=torch.float32, device=dev())
+    L.grouped_wgrad(c32, None, 1, rows, dY_d, N, X_d, K, split32, ws=ws)
+    split16 = torch.empty(N, K, dtype=torch.bfloat16, device=dev())
+    L.grouped_wgrad(c16, None, 1, rows, dY_d, N, X_d, K, split16, ws=ws)
+    prior = _prior({"dW": split16}, seed=4)["dW"]
+    acc16 = prior.clone()
+    L.grouped_wgrad(c16, None, 1, rows, dY_d, N, X_d, K, acc16, ws=ws, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(split16, split32.to(torch.bfloat16)), "bf16 split output is the fp32 split sum rounded once"
+    assert torch.equal(acc16, _expected(prior, split32)), "split accumulation"
+    ref = (W.bf16_bits_to_f32(W.f32_to_bf16_bits(dY)).astype(np.float64).T
+           @ W.bf16_bits_to_f32(W.f32_to_bf16_bits(X)).astype(np.float64))
+    for got in (split32, whole):
+        err = np.abs(to_np(got) - ref).max() / np.sqrt(rows)
+        assert err < 1e-4, f"against fp64: {err:.2e}"
+    small = torch.empty(3 * N * K * 4 - 16, dtype=torch.uint8, device=dev())
+    with pytest.raises(L.MoeError, match="workspace"):
+        L.grouped_wgrad(c32, None, 1, rows, dY_d, N, X_d, K, split32, ws=small)

@@ -166,8 +166,8 @@ def check_grouped_experts(shape, cid):
     split = [(dH, dH2), (dXp, dXp2), (dW13, sW13), (dW2, sW2)]
     if Fs:
         sW13s, sW2s = ew(2 * Fs, d), ew(d, Fs)
-        L.grouped_wgrad(cfg, None, 1, T, dH2_s, 2 * Fs, x, d, sW13s)
-        L.grouped_wgrad(cfg, None, 1, T, dy, d, Act_s, Fs, sW2s)
+        L.grouped_wgrad(cfg, None, 1, T, dH2_s, 2 * Fs, x, d, sW13s, ws=ws)
+        L.grouped_wgrad(cfg, None, 1, T, dy, d, Act_s, Fs, sW2s, ws=ws)
         split += [(dH_s, dH2_s), (dx_s, dx2_s), (dW13s, sW13s), (dW2s, sW2s)]
     if cfg.wgrad_dtype == L.MOE_BF16:
         # the fp32-output weight gradients of the same kernel: the bf16 ones are exactly
@@ -179,8 +179,8 @@ def check_grouped_experts(shape, cid):
         split += [(dW13, fW13.to(torch.bfloat16)), (dW2, fW2.to(torch.bfloat16))]
         if Fs:
             fW13s, fW2s = e32(2 * Fs, d), e32(d, Fs)
-            L.grouped_wgrad(c32, None, 1, T, dH2_s, 2 * Fs, x, d, fW13s)
-            L.grouped_wgrad(c32, None, 1, T, dy, d, Act_s, Fs, fW2s)
+            L.grouped_wgrad(c32, None, 1, T, dH2_s, 2 * Fs, x, d, fW13s, ws=ws)
+            L.grouped_wgrad(c32, None, 1, T, dy, d, Act_s, Fs, fW2s, ws=ws)
             split += [(dW13s, fW13s.to(torch.bfloat16)), (dW2s, fW2s.to(torch.bfloat16))]
             fW13s_np, fW2s_np = to_np(fW13s), to_np(fW2s)
         fW13_np, fW2_np = to_np(fW13), to_np(fW2)
