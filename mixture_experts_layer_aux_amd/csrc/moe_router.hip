@@ -18,10 +18,14 @@ namespace moe {
 
 namespace {
 
-constexpr int kRouterWaves = 8;
-// 64 tokens per block (8 per wave): a block's expert histogram is also the permute's
-// chunk histogram, so this must equal the permute chunk.
+// 64 tokens per block: a block's expert histogram is also the permute's chunk histogram,
+// so this must equal the permute chunk.
 constexpr int kRouterTokensPerBlock = 64;
+// Waves per block, by keys per lane: a wave's top-k is a chain of dependent cross-lane
+// steps, so more waves per SIMD hide more of it; the count is the most whose registers
+// still fit without spilling (16 waves: 128 VGPRs each; 12: 168; 8: 256).
+template <int EPL>
+constexpr int router_waves() { return EPL <= 4 ? 16 : (EPL == 8 ? 12 : 8); }
 
 struct Best {
   double key;
@@ -59,7 +63,7 @@ __device__ __forceinline__ float score_deriv_f32(int score, float l) {
 // logsumexp^2 for the z-loss.  pnorm[t] = (m, 1/Z) so that q_te = exp(l_te - m) / Z
 // (softmax) or s(l_te) / Z (normalised scores) can be recomputed by the sequence pass.
 template <int EPL>
-__global__ __launch_bounds__(64 * kRouterWaves) void router_topk_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(64 * router_waves<EPL>()) void router_topk_kernel(const float* __restrict__ logits,
                                                           const float* __restrict__ expert_bias,
                                                           int T, int E, int k, int score, int pre_softmax,
                                                           float scaling, int ngroups, int gtopk,
@@ -70,8 +74,9 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_topk_kernel(const fl
                                                           float2* __restrict__ pnorm) {
   extern __shared__ int smem_i[];
   int* hist = smem_i;                                          // [E]
-  float* red = reinterpret_cast<float*>(smem_i + E);           // [kRouterWaves][E]
-  __shared__ float red_z[kRouterWaves];
+  constexpr int NW = router_waves<EPL>();
+  float* red = reinterpret_cast<float*>(smem_i + E);           // [NW][E]
+  __shared__ float red_z[NW];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
@@ -83,7 +88,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_topk_kernel(const fl
   float zacc = 0.0f;  // wave-uniform
 
   const int t0 = blockIdx.x * kRouterTokensPerBlock;
-  for (int s = wave; s < kRouterTokensPerBlock; s += kRouterWaves) {
+  for (int s = wave; s < kRouterTokensPerBlock; s += NW) {
     const int t = t0 + s;
     if (t >= T) break;
     const float* row = logits + static_cast<int64_t>(t) * E;
@@ -264,13 +269,13 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_topk_kernel(const fl
     cnt_part[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
     float s = 0.0f;
 #pragma unroll
-    for (int v = 0; v < kRouterWaves; ++v) s += red[v * E + e];
+    for (int v = 0; v < NW; ++v) s += red[v * E + e];
     prob_part[static_cast<int64_t>(blockIdx.x) * E + e] = s;
   }
   if (z_part && threadIdx.x == 0) {
     float s = 0.0f;
 #pragma unroll
-    for (int v = 0; v < kRouterWaves; ++v) s += red_z[v];
+    for (int v = 0; v < NW; ++v) s += red_z[v];
     z_part[blockIdx.x] = s;
   }
 }
@@ -624,22 +629,24 @@ moe_status_t launch_router_topk(const moe_config_t& c, const float* logits, cons
                                 int32_t* seq_counts, const RouterWs& rw, hipStream_t s) {
   const int nblk = static_cast<int>(router_num_blocks(c.T));
   if (nblk != permute_num_chunks(c.T)) return fail(MOE_ERR_UNSUPPORTED, "router blocks differ from permute chunks");
-  const size_t shm = static_cast<size_t>(c.E) * sizeof(int) + static_cast<size_t>(kRouterWaves) * c.E * sizeof(float);
   const int epl = router_epl(c.E);
   const bool seq_on = c.seq_aux_coeff != 0.0f;
   float* zp = c.z_coeff != 0.0f ? rw.z_part : nullptr;
   float2* pn = seq_on ? reinterpret_cast<float2*>(rw.pnorm) : nullptr;
 #define MOE_ROUTER_CASE(N)                                                                              \
-  case N:                                                                                               \
+  case N: {                                                                                             \
+    const size_t shm = static_cast<size_t>(c.E) * sizeof(int) +                                         \
+                       static_cast<size_t>(router_waves<N>()) * c.E * sizeof(float);                     \
     if (shm > 65536 &&                                                                                  \
         hipFuncSetAttribute(reinterpret_cast<const void*>(router_topk_kernel<N>),                       \
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)) != hipSuccess) \
       return fail(MOE_ERR_HIP, "router: cannot raise the LDS limit to %zu bytes", shm);                 \
-    router_topk_kernel<N><<<nblk, 64 * kRouterWaves, shm, s>>>(logits, expert_bias, c.T, c.E, c.k, c.score,          \
-                                                 c.pre_softmax, c.routed_scaling, c.num_groups,          \
+    router_topk_kernel<N><<<nblk, 64 * router_waves<N>(), shm, s>>>(logits, expert_bias, c.T, c.E, c.k,   \
+                                                 c.score, c.pre_softmax, c.routed_scaling, c.num_groups, \
                                                  c.group_topk, idx, w, rw.cnt_part,                      \
                                                  rw.prob_part, zp, pn);                                  \
-    break;
+    break;                                                                                              \
+  }
   switch (epl) {
     MOE_ROUTER_CASE(1)
     MOE_ROUTER_CASE(2)
