@@ -110,7 +110,19 @@ __global__ __launch_bounds__(256) void quantile_hist_kernel(const float* __restr
     const uint32_t mask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
     const uint32_t pre = prefix[e] & mask;
     const int t1 = min(T, t0 + kQTokens);
-    for (int t = t0 + wave; t < t1; t += 4) {
+    // eight rows' loads in flight before their histogram updates (the integer counts do
+    // not depend on the order)
+    constexpr int U = 8;
+    int t = t0 + wave;
+    for (; t + 4 * (U - 1) < t1; t += 4 * U) {
+      uint32_t u[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) u[j] = orderable(scores[static_cast<int64_t>(t + 4 * j) * E + e] - alpha[t + 4 * j]);
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+        if ((u[j] & mask) == pre) atomicAdd(&h[lane * kQPad + ((u[j] >> shift) & 255u)], 1);
+    }
+    for (; t < t1; t += 4) {
       const uint32_t u = orderable(scores[static_cast<int64_t>(t) * E + e] - alpha[t]);
       if ((u & mask) == pre) atomicAdd(&h[lane * kQPad + ((u >> shift) & 255u)], 1);
     }

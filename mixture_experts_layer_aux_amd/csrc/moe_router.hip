@@ -302,6 +302,8 @@ __global__ __launch_bounds__(256) void seq_stats_kernel(const float* __restrict_
   const int64_t out = (static_cast<int64_t>(b) * nsc + c) * E;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     float acc = 0.0f;
+    // unrolled so that several rows' loads are in flight; the sum keeps its order
+#pragma unroll 8
     for (int s = s0; s < s1; ++s) {
       const int64_t t = static_cast<int64_t>(s) * B + b;
       const float l = logits[t * E + e];
