@@ -106,7 +106,7 @@ def test_layer_fp32_weight_gradients():
     assert got["dW13"].dtype == torch_mod().float32
 
 
-@pytest.mark.parametrize("variant", ["scaling", "no_shared_sigmoid", "k_equals_E", "one_row_experts"])
+@pytest.mark.parametrize("variant", ["scaling", "no_shared_sigmoid", "k_equals_E", "one_row_experts", "ragged_split"])
 def test_layer_edge_cases(variant):
     from dataclasses import replace
     base = W.SMALL[3]
@@ -116,6 +116,10 @@ def test_layer_edge_cases(variant):
         shape = replace(base, Fs=0, T=257)
     elif variant == "k_equals_E":
         shape = replace(W.SMALL[2], E=4, k=4, T=130, aux_coeff=0.1)
+    elif variant == "ragged_split":
+        # the shared expert's weight gradients and the gate's split over the tokens with
+        # a short last chunk (384, 384 and 232 tokens)
+        shape = replace(base, T=1000)
     else:  # tiny T: every expert gets at most a handful of rows, many get none
         shape = replace(base, T=3, k=2, E=32)
     _check_layer(shape, seed=11)

@@ -5,6 +5,8 @@ results must be within the benchmark spec's tolerance (max |err| / rms(ref)): 1e-4 for
 activations, 2e-2 for bf16.  Inputs are the seeded generator's bytes; both sides consume
 the same bytes.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 
@@ -276,9 +278,20 @@ def test_combine_and_backward_pieces(cid):
 
 @pytest.mark.parametrize("cid", SMALL_IDS)
 def test_router_and_gate_backward(cid):
+    _router_and_gate(W.SMALL[cid], cid)
+
+
+@pytest.mark.parametrize("cid,T", [(2, 1000), (4, 2000)])
+def test_router_and_gate_backward_ragged_tokens(cid, T):
+    """Token counts that leave the last 64-token router block partial and, in the gate
+    weight gradient, a short last chunk of its split over the tokens (384, 384, 232 rows at
+    T = 1000; six of 320 and one of 80 at T = 2000)."""
+    _router_and_gate(replace(W.SMALL[cid], T=T), cid)
+
+
+def _router_and_gate(shape, cid):
     torch = torch_mod()
     L = _lib()
-    shape = W.SMALL[cid]
     cfg = L.config_from_shape(shape)
     ws = L.alloc_workspace(cfg, dev())
     inp = W.make_inputs(shape, seed=cid, with_experts=False)
