@@ -455,6 +455,37 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
   static_assert(STAGES * STAGE_ELEMS * 2 >= 128 * BN * 4, "epilogue staging needs 128 KB of LDS");
   auto pass_row = [&](int lr, int h) { return row_begin + (lr >> 6) * WTM + h * 64 + (lr & 63); };
   auto chunk = [&](int lr, int c) -> const float4& { return L4[lr * 64 + (c ^ (lr & 63))]; };
+  if (RAG == RAGGED_K && EPI == EPI_STORE && !OUT_F32) {
+    if (!p.beta) {
+      // bf16 weight gradient, overwritten: rounded in registers, so the whole 256 x 256
+      // tile fits the LDS in one pass (8-byte unit u of tile row r at r * 64 + (u ^ (r & 63)),
+      // four consecutive columns), then stored a 512-byte row per wave instruction.
+      uint2* U2 = reinterpret_cast<uint2*>(lds);
+      block_barrier();  // the main loop is done with the LDS
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int lr = wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int u = (wn * WTN + j * 32 + 8 * q + cbase) >> 2;
+            U2[lr * 64 + (u ^ (lr & 63))] = make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                                       pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+          }
+      }
+      block_barrier();
+      const int col = n0 + 4 * lane;
+#pragma unroll 4
+      for (int rr = 0; rr < BM / NWAVES; ++rr) {
+        const int lr = wave * (BM / NWAVES) + rr;
+        const int row = row_begin + lr;
+        if (row >= row_end || col >= p.N) continue;
+        *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * p.ldc + col) = U2[lr * 64 + (lane ^ (lr & 63))];
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     block_barrier();  // the previous use of LDS (main loop, or the previous pass) is over
