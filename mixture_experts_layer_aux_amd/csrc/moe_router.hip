@@ -179,20 +179,24 @@ __global__ __launch_bounds__(64 * router_waves<EPL>()) void router_topk_kernel(c
         if (!(taken & (1u << i)) && better(key[i], lane + 64 * i, b.key, b.e)) {
           b.key = key[i];
           b.e = lane + 64 * i;
-          b.l = l[i];
         }
       }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
         double ok = __shfl_xor(b.key, o, 64);
         int oe = __shfl_xor(b.e, o, 64);
-        float ol = __shfl_xor(b.l, o, 64);
         if (better(ok, oe, b.key, b.e)) {
           b.key = ok;
           b.e = oe;
-          b.l = ol;
         }
       }
+      // the winner (the same on every lane) is lane b.e % 64's key b.e / 64: its logit
+      // comes from that lane once, rather than riding along every exchange above
+      float wl = 0.0f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if ((b.e >> 6) == i) wl = l[i];
+      b.l = __shfl(wl, b.e & 63, 64);
       if ((b.e & 63) == lane) taken |= 1u << (b.e >> 6);
       if (lane == j) {
         my_e = b.e;
