@@ -30,7 +30,10 @@
 //     each lane owns four consecutive output columns of one row;
 //   * the epilogue stages the tile through LDS in two passes of 128 rows and then works on
 //     whole tile rows, so its global loads and stores are contiguous runs of a row (a 1 KB
-//     row of fp32 per store instruction) rather than 16 bytes of each of 32 rows;
+//     row of fp32 per store instruction) rather than 16 bytes of each of 32 rows; a bf16
+//     weight gradient that overwrites is rounded first and staged in one pass;
+//   * a one-group weight gradient can be split over its reduction rows (kchunk): each
+//     chunk is a group writing fp32 partials, summed in chunk order by splitk_reduce_kernel;
 //   * in an expert's last row tile, the 32-row accumulator blocks past its end skip their
 //     fragment reads and MFMAs (a wave-uniform branch around a second copy of the loop);
 //   * a device-built tile list (per-expert prefix of row tiles) so the host never reads
