@@ -27,8 +27,12 @@ constexpr int kRouterTokensPerBlock = 64;
 template <int EPL>
 constexpr int router_waves() { return EPL <= 4 ? 16 : (EPL == 8 ? 12 : 8); }
 
+// KT: the key type.  Softmax keys are the fp32 logits themselves, so they are compared as
+// floats (the same order as in fp64, and one exchange per step instead of two); the
+// elementwise scores are fp64.
+template <typename KT>
 struct Best {
-  double key;
+  KT key;
   int e;
   float l;
 };
@@ -36,6 +40,11 @@ struct Best {
 __device__ __forceinline__ bool better(double ka, int ea, double kb, int eb) {
   return ka > kb || (ka == kb && ea < eb);
 }
+__device__ __forceinline__ bool better(float ka, int ea, float kb, int eb) {
+  return ka > kb || (ka == kb && ea < eb);
+}
+template <typename KT>
+__device__ __forceinline__ KT lowest_key() { return sizeof(KT) == 8 ? static_cast<KT>(-DBL_MAX) : static_cast<KT>(-FLT_MAX); }
 
 // fp64 score of one logit for the elementwise gating functions (selection keys and
 // weights): sigmoid, or sqrt(softplus) with softplus(l) = max(l, 0) + log(1 + e^-|l|).
@@ -62,7 +71,7 @@ __device__ __forceinline__ float score_deriv_f32(int score, float l) {
 // aux probabilities q (full softmax, or the scores normalised over all E), and the sum of
 // logsumexp^2 for the z-loss.  pnorm[t] = (m, 1/Z) so that q_te = exp(l_te - m) / Z
 // (softmax) or s(l_te) / Z (normalised scores) can be recomputed by the sequence pass.
-template <int EPL>
+template <int EPL, typename KT>
 __global__ __launch_bounds__(64 * router_waves<EPL>()) void router_topk_kernel(const float* __restrict__ logits,
                                                           const float* __restrict__ expert_bias,
                                                           int T, int E, int k, int score, int pre_softmax,
@@ -93,7 +102,7 @@ __global__ __launch_bounds__(64 * router_waves<EPL>()) void router_topk_kernel(c
     if (t >= T) break;
     const float* row = logits + static_cast<int64_t>(t) * E;
     float l[EPL];
-    double key[EPL];
+    KT key[EPL];
     uint32_t taken = 0;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
@@ -101,15 +110,15 @@ __global__ __launch_bounds__(64 * router_waves<EPL>()) void router_topk_kernel(c
       if (e < E) {
         l[i] = row[e];
         if (score == MOE_SOFTMAX) {
-          key[i] = static_cast<double>(l[i]);
+          key[i] = static_cast<KT>(l[i]);
         } else {
           // s(l) (+ bias) in fp64 from the fp32 values
           const double sc = score_f64(score, l[i]);
-          key[i] = expert_bias ? sc + static_cast<double>(expert_bias[e]) : sc;
+          key[i] = static_cast<KT>(expert_bias ? sc + static_cast<double>(expert_bias[e]) : sc);
         }
       } else {
         l[i] = 0.0f;
-        key[i] = -DBL_MAX;
+        key[i] = lowest_key<KT>();
         taken |= 1u << i;
       }
     }
@@ -127,7 +136,7 @@ __global__ __launch_bounds__(64 * router_waves<EPL>()) void router_topk_kernel(c
 #pragma unroll
           for (int i = 0; i < EPL; ++i) {
             const int e = lane + 64 * i;
-            if (e < E && e / n == g && !(used & (1u << i)) && better(key[i], e, bk, be)) {
+            if (e < E && e / n == g && !(used & (1u << i)) && better(static_cast<double>(key[i]), e, bk, be)) {
               bk = key[i];
               be = e;
             }
@@ -173,7 +182,7 @@ __global__ __launch_bounds__(64 * router_waves<EPL>()) void router_topk_kernel(c
     float my_l = 0.0f;
     float top_l = 0.0f;
     for (int j = 0; j < k; ++j) {
-      Best b{-DBL_MAX, INT_MAX, 0.0f};
+      Best<KT> b{lowest_key<KT>(), INT_MAX, 0.0f};
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         if (!(taken & (1u << i)) && better(key[i], lane + 64 * i, b.key, b.e)) {
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(64 * router_waves<EPL>()) void router_topk_kernel(c
       }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
-        double ok = __shfl_xor(b.key, o, 64);
+        KT ok = __shfl_xor(b.key, o, 64);
         int oe = __shfl_xor(b.e, o, 64);
         if (better(ok, oe, b.key, b.e)) {
           b.key = ok;
@@ -630,6 +639,34 @@ int router_epl(int E) {
 
 int64_t router_num_blocks(int T) { return ceil_div(T, kRouterTokensPerBlock); }
 
+namespace {
+
+template <int EPL, typename KT>
+moe_status_t launch_topk_kt(const moe_config_t& c, int nblk, const float* logits, const float* expert_bias,
+                            int32_t* idx, float* w, const RouterWs& rw, float* zp, float2* pn, hipStream_t s) {
+  const size_t shm = static_cast<size_t>(c.E) * sizeof(int) + static_cast<size_t>(router_waves<EPL>()) * c.E * sizeof(float);
+  if (shm > 65536 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(router_topk_kernel<EPL, KT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)) != hipSuccess)
+    return fail(MOE_ERR_HIP, "router: cannot raise the LDS limit to %zu bytes", shm);
+  router_topk_kernel<EPL, KT><<<nblk, 64 * router_waves<EPL>(), shm, s>>>(
+      logits, expert_bias, c.T, c.E, c.k, c.score, c.pre_softmax, c.routed_scaling, c.num_groups, c.group_topk, idx,
+      w, rw.cnt_part, rw.prob_part, zp, pn);
+  return MOE_OK;
+}
+
+// softmax keys are the fp32 logits: compared as floats (above 1024 experts the fp64
+// instance, which spills less, serves them too); the elementwise scores in fp64
+template <int EPL>
+moe_status_t launch_topk(const moe_config_t& c, int nblk, const float* logits, const float* expert_bias,
+                         int32_t* idx, float* w, const RouterWs& rw, float* zp, float2* pn, hipStream_t s) {
+  return c.score == MOE_SOFTMAX && EPL <= 16
+             ? launch_topk_kt<EPL, float>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s)
+                                : launch_topk_kt<EPL, double>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s);
+}
+
+}  // namespace
+
 moe_status_t launch_router_topk(const moe_config_t& c, const float* logits, const float* expert_bias,
                                 int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* stats,
                                 int32_t* seq_counts, const RouterWs& rw, hipStream_t s) {
@@ -639,31 +676,18 @@ moe_status_t launch_router_topk(const moe_config_t& c, const float* logits, cons
   const bool seq_on = c.seq_aux_coeff != 0.0f;
   float* zp = c.z_coeff != 0.0f ? rw.z_part : nullptr;
   float2* pn = seq_on ? reinterpret_cast<float2*>(rw.pnorm) : nullptr;
-#define MOE_ROUTER_CASE(N)                                                                              \
-  case N: {                                                                                             \
-    const size_t shm = static_cast<size_t>(c.E) * sizeof(int) +                                         \
-                       static_cast<size_t>(router_waves<N>()) * c.E * sizeof(float);                     \
-    if (shm > 65536 &&                                                                                  \
-        hipFuncSetAttribute(reinterpret_cast<const void*>(router_topk_kernel<N>),                       \
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)) != hipSuccess) \
-      return fail(MOE_ERR_HIP, "router: cannot raise the LDS limit to %zu bytes", shm);                 \
-    router_topk_kernel<N><<<nblk, 64 * router_waves<N>(), shm, s>>>(logits, expert_bias, c.T, c.E, c.k,   \
-                                                 c.score, c.pre_softmax, c.routed_scaling, c.num_groups, \
-                                                 c.group_topk, idx, w, rw.cnt_part,                      \
-                                                 rw.prob_part, zp, pn);                                  \
-    break;                                                                                              \
-  }
+  moe_status_t st = MOE_OK;
   switch (epl) {
-    MOE_ROUTER_CASE(1)
-    MOE_ROUTER_CASE(2)
-    MOE_ROUTER_CASE(4)
-    MOE_ROUTER_CASE(8)
-    MOE_ROUTER_CASE(16)
-    MOE_ROUTER_CASE(32)
+    case 1: st = launch_topk<1>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
+    case 2: st = launch_topk<2>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
+    case 4: st = launch_topk<4>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
+    case 8: st = launch_topk<8>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
+    case 16: st = launch_topk<16>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
+    case 32: st = launch_topk<32>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
     default:
       return fail(MOE_ERR_UNSUPPORTED, "router: E=%d too large", c.E);
   }
-#undef MOE_ROUTER_CASE
+  MOE_TRY_INTERNAL(st);
   router_finalize_kernel<<<static_cast<int>(ceil_div(c.E, 64)), 1024, 0, s>>>(rw.cnt_part, rw.prob_part, nblk, c.E,
                                                                             counts, prob_sum);
   if (stats)
