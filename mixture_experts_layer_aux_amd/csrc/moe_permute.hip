@@ -210,9 +210,28 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    // slots four at a time: the four rows are loaded before any is added, so each lane
-    // has four loads in flight; the sum still runs in slot order
+    const int64_t gi = static_cast<int64_t>(t) * d;
+    // the addends are loaded first, so that their latency overlaps the gathered rows'
+    // (they are still added after the slots)
+    float fa1[8] = {}, fa2[8] = {};
+    if (on && add1) R8<TA1>::template load<true>(add1, gi, c0, c1, fa1);
+    if (on && add2) R8<float>::load<true>(add2, gi, c0, c1, fa2);
+    // slots eight, then four at a time: the rows are loaded before any is added, so each
+    // lane has that many loads in flight; the sum still runs in slot order
     int j = 0;
+    for (; j + 8 <= k; j += 8) {
+      float f[8][8] = {}, wj[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int r = __shfl(my_r, j + q, 64);
+        wj[q] = __shfl(my_w, j + q, 64);
+        if (on) R8<TY>::template load<true>(Y, static_cast<int64_t>(r) * d, c0, c1, f[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += wj[q] * f[q][i];
+    }
     for (; j + 4 <= k; j += 4) {
       float f[4][8] = {}, wj[4];
 #pragma unroll
@@ -235,24 +254,19 @@ __global__ __launch_bounds__(256) void gather_sum_kernel(const void* __restrict_
       for (int i = 0; i < 8; ++i) acc[i] += wj * f[i];
     }
     if (!on) continue;
-    const int64_t gi = static_cast<int64_t>(t) * d;
     if (add1) {
-      float f[8];
-      R8<TA1>::template load<true>(add1, gi, c0, c1, f);
       if (a1_scale) {
         const float sc = a1_scale[t];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += sc * f[i];
+        for (int i = 0; i < 8; ++i) acc[i] += sc * fa1[i];
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += f[i];
+        for (int i = 0; i < 8; ++i) acc[i] += fa1[i];
       }
     }
     if (add2) {
-      float f[8];
-      R8<float>::load<true>(add2, gi, c0, c1, f);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += f[i];
+      for (int i = 0; i < 8; ++i) acc[i] += fa2[i];
     }
     if (r1_coef) {
       float v[8];
