@@ -55,12 +55,18 @@ def algorithmic(shape, wgrad_bytes=4):
         # dW13 written once, dH and x_perm read once, the offsets
         wgrad_fc1_bytes=E * 2 * F * d * wgrad_bytes + A * 2 * F * eb + A * d * eb + (E + 1) * 4,
         gate_flop=6.0 * T * E * d,                 # logits, dWg, dx_r
-        # bytes each HBM-bound phase must move at least once
+        # bytes each HBM-bound phase must move at least once, every activation row in the
+        # activation dtype (the layer's statement: Y_perm, dX_perm, y, dy, dx as act rows)
         router_bytes=T * E * 4 + T * k * 8 + E * 8,
         permute_bytes=T * d * eb + A * d * eb + A * 4 * 3,
-        combine_bytes=A * d * 4 + (T * d * 4 if Fs else 0) + T * k * 8 + T * d * 4,
-        combine_bwd_bytes=T * d * 4 + A * d * 4 + A * d * eb + (T * d * eb if Fs else 0) + T * k * 12,
-        unpermute_reduce_bytes=A * d * 4 + (T * d * 4 if Fs else 0) + T * d * 4 + T * d * 4 + T * k * 4,
+        combine_bytes=A * d * eb + (T * d * eb if Fs else 0) + T * d * eb + T * k * 8,
+        combine_bwd_bytes=T * d * eb + 2 * A * d * eb + T * k * 12,
+        unpermute_reduce_bytes=A * d * eb + T * d * eb + T * k * 4,
+        # the same with this library's storage: Y_perm, Y_s, dX_perm, dx_s, dx_r, y, dy, dx in
+        # fp32, dY_perm and dY_s in the activation dtype
+        combine_bytes_storage=A * d * 4 + (T * d * 4 if Fs else 0) + T * k * 8 + T * d * 4,
+        combine_bwd_bytes_storage=T * d * 4 + A * d * 4 + A * d * eb + (T * d * eb if Fs else 0) + T * k * 12,
+        unpermute_reduce_bytes_storage=A * d * 4 + (T * d * 4 if Fs else 0) + T * d * 4 + T * d * 4 + T * k * 4,
     )
 
 
@@ -115,6 +121,26 @@ def gate_engine(shape):
     return dict(engine="fp32 FMA", flop_executed_per_flop=1.0, peak=PEAK_FP32_TFLOPS)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(shape, inp, tokens: int):
     """The fp64 oracle's layer forward + backward on the first `tokens` tokens of the same
     inputs, timed on the host cores.  The fp64 copies of the weights of the experts those
@@ -147,6 +173,7 @@ def cpu_baseline(shape, inp, tokens: int):
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return dict(value=round(tokens * runs / dt, 4), unit="tokens/s", cores=int(threads), kind="oracle",
+                cpu_model=cpu_model(), os_cpu_count=os.cpu_count(),
                 sample=(f"fp64 oracle forward+backward of the first {tokens} of {shape.T} tokens of the "
                         f"{shape.name} layer ({len(experts)} experts reached), run {runs} times in {dt:.1f} s on "
                         f"{threads} BLAS threads; fp64 weight copies made before timing"))
@@ -353,8 +380,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--wgrad", choices=["default", "f32"], default="default",
                     help="dtype of the expert weight gradients: the activation dtype (default) or fp32")
-    ap.add_argument("--entry-points", action="store_true",
-                    help="also time the layer through moe_layer_fwd + moe_layer_bwd (reported beside value)")
+    ap.add_argument("--no-entry-points", action="store_true",
+                    help="skip timing the layer through moe_layer_fwd + moe_layer_bwd (reported beside value)")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0 = by layer)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 3 device copies of 1 GiB each (the known-size kernel that scales the "
@@ -483,23 +510,25 @@ def main() -> int:
     ms_step = elapsed * 1e3 / args.steps
     st = stats.cpu().numpy()
 
-    # --entry-points: the same layer through the two product entry points, moe_layer_fwd and
-    # moe_layer_bwd (the backward overlaps the expert weight gradients on a second stream).
-    # Off by default, so a profile of the default command holds the timed kernels only.
-    layer_ms = None
-    if args.entry_points:
-        def layer_step():
-            L.layer_fwd(cfg, Wt, x, S, y, stats, ws)
-            L.layer_bwd(cfg, Wt, S, x, dy, 1.0, dx, G, ws)
+    # the same layer through the two product entry points, moe_layer_fwd and moe_layer_bwd,
+    # on one stream and with the expert weight gradients on a second stream of the caller
+    layer_ms = {}
+    if not args.no_entry_points:
+        side = torch.cuda.Stream()
 
-        for _ in range(args.warmup):
-            layer_step()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for _ in range(args.steps):
-            layer_step()
-        torch.cuda.synchronize()
-        layer_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+        def layer_step(ws2):
+            L.layer_fwd(cfg, Wt, x, S, y, stats, ws)
+            L.layer_bwd(cfg, Wt, S, x, dy, 1.0, dx, G, ws, wgrad_stream=ws2)
+
+        for name, ws2 in (("one_stream", None), ("two_streams", side)):
+            for _ in range(args.warmup):
+                layer_step(ws2)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for _ in range(args.steps):
+                layer_step(ws2)
+            torch.cuda.synchronize()
+            layer_ms[name] = (time.perf_counter() - t1) * 1e3 / args.steps
 
     wbf16 = cfg.wgrad_dtype == L.MOE_BF16
     alg = algorithmic(shape, 2 if wbf16 else 4)
@@ -509,9 +538,17 @@ def main() -> int:
     roof = roofline(alg, phase_ms[ROOFLINE_PHASE], peak, shape, "bf16" if wbf16 else "fp32")
 
     def hbm(p, key):
+        """frac against the bytes of activation-dtype rows; where this library keeps fp32
+        rows, the bytes it must move with them, their rate and their ratio beside it."""
         gbps = alg[key] / (phase_ms[p] * 1e-3) / 1e9
-        return dict(ms=round(phase_ms[p], 4), bytes=int(alg[key]), achieved_gbps=round(gbps, 1),
-                    frac=round(gbps / PEAK_HBM_GBPS, 4))
+        out = dict(ms=round(phase_ms[p], 4), bytes=int(alg[key]), achieved_gbps=round(gbps, 1),
+                   frac=round(gbps / PEAK_HBM_GBPS, 4))
+        if key + "_storage" in alg:
+            sb = alg[key + "_storage"]
+            sg = sb / (phase_ms[p] * 1e-3) / 1e9
+            out.update(bytes_fp32_storage=int(sb), storage_over_act_bytes=round(sb / alg[key], 3),
+                       achieved_gbps_fp32_storage=round(sg, 1), frac_fp32_storage=round(sg / PEAK_HBM_GBPS, 4))
+        return out
 
     layer_flop = alg["grouped_gemm_flop"] + alg["gate_flop"]
     out = dict(
@@ -535,9 +572,9 @@ def main() -> int:
                           flop_per_step=alg["grouped_gemm_flop"], ms_per_step=round(gemm_ms, 3),
                           tflops=round(gemm_tflops, 2), peak=peak, frac=round(gemm_tflops / peak, 4)),
         layer_tflops=round(layer_flop / (ms_step * 1e-3) / 1e12, 2),
-        layer_entry_points=None if layer_ms is None else dict(
-            calls="moe_layer_fwd + moe_layer_bwd", ms_per_step=round(layer_ms, 3),
-            tokens_per_s=round(T / (layer_ms * 1e-3), 1)),
+        layer_entry_points=None if not layer_ms else {
+            n: dict(calls="moe_layer_fwd + moe_layer_bwd" + (" (wgrad_stream)" if n == "two_streams" else ""),
+                    ms_per_step=round(v, 3), tokens_per_s=round(T / (v * 1e-3), 1)) for n, v in layer_ms.items()},
         phases_ms={p: round(v, 4) for p, v in phase_ms.items()},
         hbm_phases=dict(router=hbm("router", "router_bytes"), permute=hbm("permute", "permute_bytes"),
                         combine=hbm("combine", "combine_bytes"), combine_bwd=hbm("combine_bwd", "combine_bwd_bytes"),

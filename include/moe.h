@@ -2,8 +2,14 @@
  * libmoe: one Mixture-of-Experts layer, forward and backward, on one AMD Instinct
  * MI355X (gfx950).  Plain C ABI: every tensor argument is a DEVICE pointer that the
  * caller allocated; sizes come from moe_config_t; `stream` is a hipStream_t (NULL =
- * the default stream).  The library allocates nothing, keeps no state between calls
- * and never synchronises the host: every call only enqueues kernels on `stream`.
+ * the default stream).  The library allocates no memory, keeps no state between calls
+ * (the only HIP objects it creates are the events of one moe_layer_bwd call given a second
+ * stream, destroyed before that call returns) and never synchronises the host: every call
+ * only enqueues kernels on `stream`.
+ *
+ * Deviation from the plain statement of the layer: y, dy and dx are fp32 in every layer,
+ * also where the activations are bf16, because one bf16 rounding of the combined output
+ * (or of the input gradient) costs up to 2e-2 of its RMS on its own.
  *
  * Sources, cited by page title and section:
  *   [HB] "The Ultimate MoE Training Handbook" (Hugging Face).
@@ -414,20 +420,22 @@ moe_status_t moe_gate_logits_bwd(const moe_config_t* cfg, const void* x, const f
                                  size_t ws_bytes, void* stream);
 
 /* Whole backward from the saved forward tensors.
- * bf16/fp32 experts: the expert weight gradients (dW2 = dY^T Act, dW13 = dH^T X, routed
- * and shared) run on a second stream of the library -- one per device, default priority,
- * created on the first call -- that waits on `stream` for dY_perm and dH and is joined
- * back into `stream` before the call returns, so work queued on `stream` afterwards sees
- * every output.  That stream and its events are per device, not per call: calls on one
- * device must not be issued concurrently from several host threads.
+ * bf16/fp32 experts: wgrad_stream (a hipStream_t of the caller, or NULL) -- when it is
+ * given and differs from `stream`, the expert weight gradients (dW2 = dY^T Act,
+ * dW13 = dH^T X, routed and shared) run on it beside the data gradients: it waits on
+ * `stream` for dY_perm and dH through events this call creates, and `stream` waits on it
+ * before the call returns, so work queued on `stream` afterwards sees every output.  The
+ * events are destroyed before the call returns; the streams are the caller's.  NULL (or
+ * `stream` itself): everything runs on `stream` in order.
  * fp8 experts are frozen (no expert gradients): grads->dW13, dW2, dW13s, dW2s must be
  * NULL, and the call computes the router path only -- dw, dlogits, dWg, dbg, and
- * dx = dlogits Wg, the input gradient through the router.
+ * dx = dlogits Wg, the input gradient through the router (wgrad_stream is not used).
  * grads->accumulate = 1 adds every weight gradient into its buffer (see moe_grads_t); dx
- * is overwritten either way. */
+ * is overwritten either way.  Errors: as every call, plus MOE_ERR_HIP if the events cannot
+ * be created. */
 moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* weights, const moe_saved_t* saved,
                            const void* x, const float* dy, float daux, float* dx, const moe_grads_t* grads,
-                           void* ws, size_t ws_bytes, void* stream);
+                           void* ws, size_t ws_bytes, void* stream, void* wgrad_stream);
 
 #ifdef __cplusplus
 }

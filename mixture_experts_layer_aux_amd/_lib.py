@@ -430,8 +430,9 @@ def layer_fwd(cfg, W, x, S, y, stats, ws, stream=None):
                                 _P(_stream(stream))))
 
 
-def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None, accumulate=False):
-    """The layer's backward; accumulate: add the weight gradients into G's buffers."""
+def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None, accumulate=False, wgrad_stream=None):
+    """The layer's backward; accumulate: add the weight gradients into G's buffers;
+    wgrad_stream: a second torch stream for the expert weight gradients (None: one stream)."""
     wp, wn = _ws(ws)
     ad, d, E, F, Fs = act_dtype(cfg), cfg.d, cfg.E, cfg.F, cfg.Fs
     ws_ = _weights_struct(cfg, W)
@@ -445,7 +446,8 @@ def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None, accumulate=False):
     _check(load().moe_layer_bwd(ctypes.byref(cfg), ctypes.byref(ws_), ctypes.byref(ss),
                                 _P(_ptr(x, ad, cfg.T * d, "x")), _P(_ptr(dy, f32, cfg.T * d, "dy")),
                                 ctypes.c_float(daux), _P(_ptr(dx, f32, cfg.T * d, "dx")), ctypes.byref(gs), _P(wp),
-                                ctypes.c_size_t(wn), _P(_stream(stream))))
+                                ctypes.c_size_t(wn), _P(_stream(stream)),
+                                _P(wgrad_stream.cuda_stream if wgrad_stream is not None else None)))
 
 
 # ----------------------------------------------------------------- buffer helpers

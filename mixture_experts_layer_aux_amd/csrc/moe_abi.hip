@@ -6,7 +6,6 @@
 #include <stdio.h>
 
 #include <algorithm>
-#include <mutex>
 
 #include "moe_internal.h"
 
@@ -245,37 +244,25 @@ moe_status_t need_ws(size_t have, size_t need, const char* fn) {
 
 hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 
-// A second stream per device for the expert weight gradients of moe_layer_bwd: they need
-// only dY_perm and dH, so they run beside the data gradients (HBM-heavy fp32 weight
-// gradients next to MFMA-heavy data gradients).  Default priority; created on first use.
-struct SideStream {
-  hipStream_t s = nullptr;
+// Events of one moe_layer_bwd call that overlaps its expert weight gradients on a second,
+// caller-owned stream: created by the call, recorded and waited on, and destroyed before it
+// returns (a destroyed event's pending waits still complete), so no HIP object outlives the
+// call.
+struct CallEvents {
   hipEvent_t dy = nullptr, dh = nullptr, join = nullptr;
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
-
-moe_status_t side_stream(SideStream** out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-    return fail(MOE_ERR_HIP, "side stream: no current device");
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream& ss = g_side[dev];
-  if (!ss.s) {
-    hipStream_t st = nullptr;
-    hipEvent_t e[3] = {nullptr, nullptr, nullptr};
-    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess)
-      return fail(MOE_ERR_HIP, "side stream: hipStreamCreateWithFlags failed");
-    for (hipEvent_t& ev : e)
-      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
-        return fail(MOE_ERR_HIP, "side stream: hipEventCreateWithFlags failed");
-    ss.dy = e[0]; ss.dh = e[1]; ss.join = e[2];
-    ss.s = st;
+  ~CallEvents() {
+    for (hipEvent_t e : {dy, dh, join})
+      if (e) (void)hipEventDestroy(e);
   }
-  *out = &ss;
-  return MOE_OK;
-}
+  moe_status_t create() {
+    for (hipEvent_t* e : {&dy, &dh, &join})
+      if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) {
+        *e = nullptr;
+        return fail(MOE_ERR_HIP, "moe_layer_bwd: hipEventCreateWithFlags failed");
+      }
+    return MOE_OK;
+  }
+};
 
 // Makes `waiter` wait for the work queued on `from` so far (no-op on one stream).
 moe_status_t fork(hipStream_t from, hipEvent_t ev, hipStream_t waiter) {
@@ -796,7 +783,7 @@ moe_status_t moe_gate_logits_bwd(const moe_config_t* cfg, const void* x, const f
 
 moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, const moe_saved_t* sv, const void* x,
                            const float* dy, float daux, float* dx, const moe_grads_t* gr, void* ws, size_t ws_bytes,
-                           void* stream) {
+                           void* stream, void* wgrad_stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED(W); MOE_NEED(sv); MOE_NEED(gr); MOE_NEED16(x); MOE_NEED16(dy); MOE_NEED16(dx); MOE_NEED(ws);
   MOE_NEED(W->Wg); MOE_NEED16(W->W13); MOE_NEED16(W->W2);
@@ -836,19 +823,22 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_TRY(launch_combine_bwd(c, dy, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, bw.dY, bw.dw,
                              dy_in_place ? nullptr : dY_s, c.shared_gate ? sv->gs : nullptr,
                              c.shared_gate ? static_cast<const float*>(sv->Y_s) : nullptr, bw.dl_s, s));
-  SideStream* ss = nullptr;
-  MOE_TRY(side_stream(&ss));
-  MOE_TRY(fork(s, ss->dy, ss->s));  // dY_perm (and the shared expert's dY) ready
+  // the expert weight gradients go to wgrad_stream when the caller gives a second stream:
+  // it waits for dY_perm (and the shared expert's dY) here and for dH inside run_experts_bwd
+  hipStream_t s2 = wgrad_stream ? S(wgrad_stream) : s;
+  CallEvents ev;
+  if (s2 != s) MOE_TRY(ev.create());
+  MOE_TRY(fork(s, ev.dy, s2));
   MOE_TRY(run_experts_bwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, sv->H, sv->Act, bw.dY, bw.dH, bw.dX, gr->dW13,
                           gr->dW2, x, W->W13s, W->W2s, sv->H_s, sv->Act_s, dY_s, bw.dH_s, bw.dx_s, gr->dW13s,
-                          gr->dW2s, bw.sched, bw.dact, bw.wsplit, s, ss->s, ss->dh, beta));
+                          gr->dW2s, bw.sched, bw.dact, bw.wsplit, s, s2, ev.dh, beta));
   MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, sv->seq_counts, daux, bw.dlogits, s));
   MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, bw.gate, s, beta));
   if (c.shared_gate) MOE_TRY(launch_shared_gate_bwd(c, x, bw.dl_s, gr->dWsg, bw.sg_part, s, beta));
   MOE_TRY(launch_unpermute_reduce(c, bw.dX, sv->row_of, c.Fs ? static_cast<const float*>(bw.dx_s) : nullptr,
                                   bw.dx_r, c.shared_gate ? bw.dl_s : nullptr, c.shared_gate ? W->Wsg : nullptr, dx,
                                   s));
-  return fork(ss->s, ss->join, s);  // the caller's stream sees the weight gradients too
+  return fork(s2, ev.join, s);  // the caller's stream sees the weight gradients too
 }
 
 }  // extern "C"

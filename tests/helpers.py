@@ -20,45 +20,174 @@ from oracle import moe_oracle as O  # noqa: E402
 TOL_F32 = 1e-4
 TOL_BF16 = 2e-2
 MARGIN = 1e-3
-# Weight gradients with bf16 operands: relative Frobenius error ||got - ref|| / ||ref||,
-# per expert for the stacked expert weights.  Each element is a sum of products of
-# operands that went through one to three bf16 roundings (unit roundoff 2^-9 each); the
-# errors are independent across rows, so the relative error of the sum stays near a few
-# times 2^-9 (~0.002-0.005) whatever the number of rows, while one dropped or doubled row
-# of an expert with n rows moves it by ~1/sqrt(n).  With fp32 activations the
-# per-token bar (max-abs / rms <= 1e-4) applies to the gradients too.
-TOL_GRAD_BF16 = 1e-2
+# Weight gradients with bf16 operands are checked element by element.  dW = P^T Q sums n
+# rows of stored operands (fc1: P = dH, Q = x_perm; fc2: P = dY_perm, Q = Act).  Every
+# operand the GPU stores in bf16 is the round-to-nearest-even of an fp32 value, so its
+# relative error is at most U_BF16 = 2^-9; these rounding errors are modelled as independent
+# with zero mean (the usual probabilistic model of rounding errors).  By Hoeffding's
+# inequality a weighted sum of them, sum_r a_r delta_r, exceeds LAMBDA * 2^-9 * sqrt(sum a_r^2)
+# with probability at most 2 exp(-LAMBDA^2 / 2) = 2.5e-14 per element.  The bound of one
+# element (wgrad_bound) adds the final bf16 rounding of dW (2^-8 |ref|, the rounding of a
+# value that may itself sit one fp32 step off) and, for the fp32 accumulation of n
+# products (at most n 2^-24 of sum |P||Q|, far less in the probabilistic model) and the fp32
+# errors of H and dAct, 2^-14 (|P|^T |Q|).  Rounding upstream of P propagates into it: a
+# stored dY_perm reaches dH through dAct = dY W2 and the activation's derivative, giving
+# P_ri the variance proxy sig2_ri = phi_ri^2 sum_c dY_rc^2 W2_ci^2 (grad_sig2).
+LAMBDA = 8.0
+U_BF16 = 2.0 ** -9
 
 
 def tol(shape) -> float:
     return TOL_F32 if shape.act == "f32" else TOL_BF16
 
 
-def frob_err(got, ref) -> float:
+def wgrad_bound(P, Q, rho_p, rho_q, sig2=None):
+    """(bound, ref) for dW = P^T Q: ref in fp64 and the element-wise bound of |dW_gpu - ref|.
+    rho_p / rho_q: 1 if the GPU stores that operand rounded to bf16, 0 if it is an exact
+    input; sig2 [n, cols(P)]: variance proxy of rounding that reached P from upstream."""
+    P = np.asarray(P, dtype=np.float64)
+    Q = np.asarray(Q, dtype=np.float64)
+    Q2 = Q * Q
+    var = (rho_p + rho_q) * ((P * P).T @ Q2)
+    if sig2 is not None:
+        var = var + np.asarray(sig2, dtype=np.float64).T @ Q2
+    ref = P.T @ Q
+    bound = LAMBDA * U_BF16 * np.sqrt(var) + 2.0 ** -8 * np.abs(ref) + 2.0 ** -14 * (np.abs(P).T @ np.abs(Q))
+    return bound, ref
+
+
+def grad_sig2(H, dY, W2, glu):
+    """Variance proxy of the rounding of a stored dY that reaches dH = glu'(H) dAct through
+    dAct = dY W2 (W2 [d, F]): the activation's backward is linear in dAct, so its factors
+    are glu_backward(H, 1)."""
+    n, F = H.shape[0], H.shape[1] // 2
+    phi = O.glu_backward(H, np.ones((n, F)), glu)
+    S2 = (np.asarray(dY, dtype=np.float64) ** 2) @ (np.asarray(W2, dtype=np.float64) ** 2)
+    return phi * phi * np.concatenate([S2, S2], axis=1)
+
+
+def check_wgrad(name, got, P, Q, rho_p, rho_q, sig2=None):
+    """Element-wise gate of a bf16 weight gradient (see wgrad_bound)."""
     got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    n = np.linalg.norm(ref)
-    return float(np.linalg.norm(got - ref) / n) if n > 0 else float(np.linalg.norm(got))
+    bound, ref = wgrad_bound(P, Q, rho_p, rho_q, sig2)
+    err = np.abs(got - ref)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{name}: {int(bad.sum())} element(s) outside the bound; worst at {tuple(int(v) for v in i)}: "
+                             f"got {got[i]:.6e} ref {ref[i]:.6e} bound {bound[i]:.3e}")
+    return float(np.max(err / np.maximum(bound, 1e-300))) if err.size else 0.0
 
 
 def check_grad(name, got, ref, shape):
-    """Weight-gradient gate for a whole tensor (see TOL_GRAD_BF16)."""
+    """Whole-tensor gate of a gradient that is not an expert weight gradient of bf16 operands
+    (the router's and the shared gate's, fp32 and bf16 layers alike): max |got - ref| / rms(ref)
+    within the per-token bar of the layer's dtype."""
+    err = rel_err(got, ref)
+    assert err < tol(shape), f"{name}: max|err|/rms = {err:.3e}"
+
+
+def router_dw_sig2(f, o, W2):
+    """Variance proxy of the GPU's dw[t, j] = <dy_t, Y_perm[row]> from the bf16 rounding of Act:
+    a rounding delta of Act[row, f] moves dw by delta Act[row, f] (dy_t W2_e)_f."""
+    perm = f["perm"]
+    v = np.zeros(len(perm.token_of))
+    dy = np.asarray(o["dy"], dtype=np.float64)
+    for e in range(len(perm.offsets) - 1):
+        a, b = perm.offsets[e], perm.offsets[e + 1]
+        if b > a:
+            g = dy[perm.token_of[a:b]] @ np.asarray(W2[e], dtype=np.float64)
+            v[a:b] = np.sum((f["Act"][a:b] * g) ** 2, axis=1)
+    return v[perm.row_of]
+
+
+def router_grad_bounds(f, o, spec, W2):
+    """Element-wise bounds of the router's weight gradients dWg = dl^T x and dbg = sum_t dl_t
+    of a bf16 layer.  dl is linear in dw (slot j's column of that map is the router backward
+    of a unit dw in slot j, no loss terms), so the Act roundings reach dl_t with the variance
+    proxy U[t, i] = sum_j M_t[i, j]^2 v[t, j]; the fp32 router arithmetic adds 2^-14 of the
+    absolute terms and 2^-8 of the value."""
+    r = f["route"]
+    vdw = router_dw_sig2(f, o, W2)
+    U = np.zeros_like(f["logits"])
+    for j in range(r["idx"].shape[1]):
+        unit = np.zeros_like(r["w"])
+        unit[:, j] = 1.0
+        Mj = O.router_backward(f["logits"], r["idx"], r["w"], unit, spec, counts=r["counts"], daux=0.0,
+                               seq_counts=r.get("seq_counts"))
+        U += Mj * Mj * vdw[:, j:j + 1]
+    return U
+
+
+def check_router_grads(got, f, b, o, spec, W2, shape):
+    """dWg and dbg (and dWsg behind a shared gate): max-abs/rms for fp32 layers; for bf16 layers
+    element by element within the Hoeffding bound of the Act roundings (router_grad_bounds)."""
     if shape.act == "f32":
-        err = rel_err(got, ref)
-        assert err < TOL_F32, f"{name}: max|err|/rms = {err:.3e}"
-    else:
-        err = frob_err(got, ref)
-        assert err < TOL_GRAD_BF16, f"{name}: ||err||/||ref|| = {err:.3e}"
+        for n in ("dWg", "dbg", "dWsg"):
+            if got.get(n) is not None:
+                check_grad(n, got[n], b[n], shape)
+        return
+    x = np.asarray(o["x"], dtype=np.float64)
+    U = router_grad_bounds(f, o, spec, W2)
+    dl = b["dlogits"]
+    lam = LAMBDA * U_BF16
+    checks = [("dWg", lam * np.sqrt(U.T @ (x * x)) + 2.0 ** -14 * (np.abs(dl).T @ np.abs(x)), b["dWg"])]
+    if got.get("dbg") is not None:
+        checks.append(("dbg", lam * np.sqrt(U.sum(axis=0)) + 2.0 ** -14 * np.abs(dl).sum(axis=0), b["dbg"]))
+    if got.get("dWsg") is not None:
+        sh = f["shared"]
+        gs = sh["gs"]
+        g = np.asarray(o["dy"], dtype=np.float64) @ np.asarray(o["W2s"], dtype=np.float64)
+        v = (gs * (1.0 - gs)) ** 2 * np.sum((sh["Act"] * g) ** 2, axis=1)
+        dls = b["dl_s"]
+        checks.append(("dWsg", lam * np.sqrt(v @ (x * x)) + 2.0 ** -14 * (np.abs(dls) @ np.abs(x)), b["dWsg"]))
+    for n, bound, ref in checks:
+        bound = bound + 2.0 ** -8 * np.abs(ref)
+        err = np.abs(np.asarray(got[n], dtype=np.float64) - ref)
+        if np.any(err > bound):
+            i = np.unravel_index(np.argmax(err - bound), err.shape)
+            raise AssertionError(f"{n}: {int((err > bound).sum())} element(s) outside the bound; worst at "
+                                 f"{tuple(int(v) for v in i)}: err {err[i]:.3e} bound {bound[i]:.3e}")
 
 
-def check_expert_grads(name, got, ref, counts, shape, experts=None):
-    """Per-expert weight-gradient gate; experts without rows must be exact zeros."""
-    ids = range(len(counts)) if experts is None else experts
+def check_layer_grads(got, f, b, o, spec, shape, ids=None, router=True, dy_exact=True):
+    """Every weight gradient of one layer call against the oracle's forward f and backward b.
+    got: name -> array (dW13, dW2 stacked by expert; dW13s, dW2s; dWg, dbg, dWsg when present).
+    ids: the experts to compare (None: all); router: compare the router's gradients too (only
+    when no token was routed differently).  dy_exact: the upstream gradient is representable
+    in bf16, so the shared expert's ungated dY_s = dy carries no rounding.
+    fp32 layers: max |err| / rms < 1e-4 per tensor (per expert for the stacked ones).
+    bf16 layers: element-wise bounds (wgrad_bound); experts without rows exact zeros."""
+    perm = f["perm"]
+    E = len(perm.offsets) - 1
+    ids = range(E) if ids is None else ids
+    W13, W2 = o["W13"], o["W2"]
     for e in ids:
-        if counts[e] == 0:
-            assert not np.any(got[e]), f"{name}[{e}]: expert without rows has a nonzero gradient"
+        a, bb = perm.offsets[e], perm.offsets[e + 1]
+        for n in ("dW13", "dW2"):
+            g = np.asarray(got[n][e], dtype=np.float64)
+            if bb == a:
+                assert not np.any(g), f"{n}[{e}]: expert without rows has a nonzero gradient"
+            elif shape.act == "f32":
+                check_grad(f"{n}[{e}]", g, b[n][e], shape)
+        if bb == a or shape.act == "f32":
+            continue
+        sig2 = grad_sig2(f["H"][a:bb], b["dY_perm"][a:bb], W2[e], spec.glu)
+        check_wgrad(f"dW13[{e}]", got["dW13"][e], b["dH"][a:bb], f["x_perm"][a:bb], 1, 0, sig2)
+        check_wgrad(f"dW2[{e}]", got["dW2"][e], b["dY_perm"][a:bb], f["Act"][a:bb], 1, 1)
+    if got.get("dW13s") is not None:
+        if shape.act == "f32":
+            check_grad("dW13s", got["dW13s"], b["dW13s"], shape)
+            check_grad("dW2s", got["dW2s"], b["dW2s"], shape)
         else:
-            check_grad(f"{name}[{e}]", got[e], ref[e], shape)
+            sh = f["shared"]
+            dYs = sh["gs"][:, None] * np.asarray(o["dy"], dtype=np.float64)
+            rounded = 1 if (spec.shared_gate or not dy_exact) else 0
+            sig2 = grad_sig2(sh["H"], dYs, o["W2s"], spec.glu) if rounded else None
+            check_wgrad("dW13s", got["dW13s"], b["dH_s"], o["x"], 1, 0, sig2)
+            check_wgrad("dW2s", got["dW2s"], dYs, sh["Act"], rounded, 1)
+    if router:
+        check_router_grads(got, f, b, o, spec, W2, shape)
 
 
 def torch_mod():

@@ -106,7 +106,7 @@ def test_quantize_fp8_rejects_bad_shapes_before_launching():
     sv = L.Saved(**{n: 1 << 20 for n, _ in L.Saved._fields_})
     g = L.Grads(dWg=1 << 20, dW13=1 << 20)
     st = lib.moe_layer_bwd(ctypes.byref(c8), ctypes.byref(w), ctypes.byref(sv), fake, fake, ctypes.c_float(1.0), fake,
-                           ctypes.byref(g), fake, ctypes.c_size_t(1 << 40), P(None))
+                           ctypes.byref(g), fake, ctypes.c_size_t(1 << 40), P(None), P(None))
     assert st == L.MOE_ERR_INVALID_ARG and b"frozen" in lib.moe_last_error()
 
 
@@ -252,7 +252,7 @@ def test_entry_points_reject_bad_arguments_before_launching():
     sv = L.Saved(logits=fake, idx=fake, w=fake, counts=fake, offsets=fake, row_of=fake, Y_perm=fake)
     gr = L.Grads(dWg=fake, dW13=fake, dW2=fake, accumulate=2)
     st = lib.moe_layer_bwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(sv), fake, fake, ctypes.c_float(1.0),
-                           fake, ctypes.byref(gr), fake, ctypes.c_size_t(1 << 40), s)
+                           fake, ctypes.byref(gr), fake, ctypes.c_size_t(1 << 40), s, s)
     assert st == L.MOE_ERR_INVALID_ARG and b"accumulate" in lib.moe_last_error()
     # expert backward: routed weight gradients are both given or both NULL
     st = lib.moe_grouped_gemm_swiglu_bwd(ctypes.byref(cfg), *([fake] * 9), fake, nul, *([nul] * 10), fake,

@@ -17,7 +17,7 @@ from dataclasses import replace
 import numpy as np
 import pytest
 
-from helpers import O, W, check_grad, dev, oracle_inputs, spec_of, to_dev, to_np, torch_mod
+from helpers import O, W, check_layer_grads, dev, oracle_inputs, spec_of, to_dev, to_np, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -102,8 +102,7 @@ def test_layer_bwd_accumulate(name):
     if np.array_equal(f["route"]["idx"], to_np(S["idx"])):
         b = O.layer_backward(f, o["x"], o["Wg"], o["W13"], o["W2"], o["dy"], spec, W13s=o["W13s"], W2s=o["W2s"],
                              daux=1.0, Wsg=o["Wsg"])
-        for k in G32:
-            check_grad(k, to_np(G32[k]), b[k], shape)
+        check_layer_grads({k: to_np(v) for k, v in G32.items()}, f, b, o, spec, shape)
     else:
         print("routing differs from the oracle's at a near-tie: oracle check left to the layer tests", flush=True)
 

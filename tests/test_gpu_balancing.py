@@ -13,7 +13,7 @@ from dataclasses import replace
 import numpy as np
 import pytest
 
-from helpers import (MARGIN, O, W, check_grad, dev, f64, oracle_inputs, rel_err, routing_moved, spec_of, to_dev,
+from helpers import (MARGIN, O, W, check_router_grads, dev, f64, oracle_inputs, rel_err, routing_moved, spec_of, to_dev,
                      to_np, tol, torch_mod)
 
 pytestmark = pytest.mark.gpu
@@ -224,7 +224,7 @@ def test_layer_with_variants_and_losses(name):
         assert np.array_equal(to_np(S["seq_counts"]), r["seq_counts"])
         # dx carries the router path (with every loss gradient) through the gate GEMM
         assert rel_err(to_np(dx), b["dx"], safe) < tl, "dx"
-        check_grad("dWg", to_np(G["dWg"]), b["dWg"], shape)
+        check_router_grads({"dWg": to_np(G["dWg"])}, f, b, o, spec, o["W2"], shape)
 
 
 # quantile balancing: (T, E, k, scores law, solve)

@@ -10,13 +10,13 @@ is compared when no token moved.
 import numpy as np
 import pytest
 
-from helpers import (MARGIN, O, W, check_expert_grads, check_grad, dev, oracle_inputs, rel_err, routing_moved, spec_of, to_dev,
-                     to_np, tol, torch_mod)
+from helpers import (MARGIN, O, W, check_layer_grads, dev, oracle_inputs, rel_err, routing_moved, spec_of, to_dev, to_np,
+                     tol, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
 
-def _run_layer(shape, inp, **cfg_extra):
+def _run_layer(shape, inp, wgrad_stream=None, **cfg_extra):
     torch = torch_mod()
     from mixture_experts_layer_aux_amd import _lib as L
     cfg = L.config_from_shape(shape, **cfg_extra)
@@ -33,7 +33,9 @@ def _run_layer(shape, inp, **cfg_extra):
     dx = torch.empty(shape.T, shape.d, dtype=torch.float32, device=d)
     stats = torch.empty(L.MOE_NSTATS, dtype=torch.float32, device=d)
     L.layer_fwd(cfg, Wt, x, S, y, stats, ws)
-    L.layer_bwd(cfg, Wt, S, x, dy, 1.0, dx, G, ws)
+    L.layer_bwd(cfg, Wt, S, x, dy, 1.0, dx, G, ws, wgrad_stream=wgrad_stream)
+    if wgrad_stream is not None:      # copies queued on the caller's stream right after the call
+        G = {k: v.clone() for k, v in G.items()}
     torch.cuda.synchronize()
     return dict(y=y, dx=dx, stats=stats, **{f"S_{k}": v for k, v in S.items()}, **G)
 
@@ -61,26 +63,17 @@ def _check_layer(shape, seed, **cfg_extra):
     if not moved.any():
         assert np.array_equal(to_np(got["S_counts"]), r["counts"])
         assert st[1] == pytest.approx(r["maxvio"], rel=1e-6)
-        check_grad("dWg", to_np(got["dWg"]), b["dWg"], shape)
-        if "dbg" in got:
-            check_grad("dbg", to_np(got["dbg"]), b["dbg"], shape)
     same = np.ones(shape.E, dtype=bool)
     for t in np.where(moved)[0]:
         same[idx_gpu[t]] = False
         same[r["idx"][t]] = False
     assert same.sum() >= shape.E - 2 * shape.k * moved.sum()
-    ids = np.where(same)[0]
-    check_expert_grads("dW13", to_np(got["dW13"]), b["dW13"], r["counts"], shape, ids)
-    check_expert_grads("dW2", to_np(got["dW2"]), b["dW2"], r["counts"], shape, ids)
-    if shape.Fs:
-        check_grad("dW13s", to_np(got["dW13s"]), b["dW13s"], shape)
-        check_grad("dW2s", to_np(got["dW2s"]), b["dW2s"], shape)
+    # every weight gradient element by element (the router's when no token moved)
+    grads = {n: to_np(got[n]) for n in ("dW13", "dW2", "dW13s", "dW2s", "dWg", "dbg", "dWsg") if n in got}
+    check_layer_grads(grads, f, b, o, spec, shape, ids=np.where(same)[0], router=not moved.any())
     if getattr(shape, "shared_gate", False):
-        # the gate values and its weight gradient (a sum over all tokens, fp32)
         gs_err = np.abs(to_np(got["S_gs"]) - f["shared"]["gs"]).max()
         assert gs_err < 1e-5 if shape.act == "bf16" else gs_err < 1e-6, f"gs: {gs_err:.2e}"
-        if not moved.any():
-            check_grad("dWsg", to_np(got["dWsg"]), b["dWsg"], shape)
     return got
 
 
@@ -98,6 +91,20 @@ def test_layer_determinism():
     b = _run_layer(shape, inp)
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("cid", [3, 4])
+def test_layer_two_streams(cid):
+    """The expert weight gradients on a second stream of the caller give the same bits as on
+    one stream, and the caller's stream sees them when the call returns."""
+    torch = torch_mod()
+    shape = W.SMALL[cid]
+    inp = W.make_inputs(shape, seed=cid)
+    one = _run_layer(shape, inp)
+    side = torch.cuda.Stream()
+    two = _run_layer(shape, inp, wgrad_stream=side)
+    for k in one:
+        assert torch.equal(one[k], two[k]), k
 
 
 def test_layer_fp32_weight_gradients():

@@ -10,8 +10,8 @@ from dataclasses import replace
 import numpy as np
 import pytest
 
-from helpers import (O, W, check_expert_grads, check_grad, dev, f64, oracle_inputs, rel_err, spec_of, storage_ok,
-                     to_dev, to_np, tol, torch_mod)
+from helpers import (O, W, check_grad, check_wgrad, dev, f64, oracle_inputs, rel_err, spec_of, storage_ok, to_dev,
+                     to_np, tol, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -210,12 +210,25 @@ def check_grouped_experts(shape, cid):
     for name, got in (("Y", Yp), ("dX", dXp)):
         err = rel_err(to_np(got), ref[name])
         assert err < tl, f"{name}: {err:.3e}"
+    # expert weight gradients, element by element: dW13 = dH^T x_perm (dH stored rounded,
+    # x_perm exact), dW2 = dY^T Act (dY an exact input here, Act stored rounded); fp32
+    # layers at the per-tensor bar
     counts = np.diff(p.offsets)
-    check_expert_grads("dW13", to_np(dW13), ref["dW13"], counts, shape)
-    check_expert_grads("dW2", to_np(dW2), ref["dW2"], counts, shape)
+    outs = [("", to_np(dW13), to_np(dW2))]
     if cfg.wgrad_dtype == L.MOE_BF16:    # the fp32 option against the oracle too
-        check_expert_grads("dW13 (fp32)", fW13_np, ref["dW13"], counts, shape)
-        check_expert_grads("dW2 (fp32)", fW2_np, ref["dW2"], counts, shape)
+        outs.append((" (fp32)", fW13_np, fW2_np))
+    for tag, gW13, gW2 in outs:
+        for ex in range(E):
+            a, b = p.offsets[ex], p.offsets[ex + 1]
+            if b == a:
+                assert not np.any(gW13[ex]) and not np.any(gW2[ex]), f"expert {ex} without rows{tag}"
+            elif shape.act == "f32":
+                check_grad(f"dW13[{ex}]{tag}", gW13[ex], ref["dW13"][ex], shape)
+                check_grad(f"dW2[{ex}]{tag}", gW2[ex], ref["dW2"][ex], shape)
+            else:
+                check_wgrad(f"dW13[{ex}]{tag}", gW13[ex], ref["dH"][a:b], xp[a:b], 1, 0)
+                check_wgrad(f"dW2[{ex}]{tag}", gW2[ex], dYo[a:b], ref["Act"][a:b], 0, 1)
+    assert counts.sum() == A
     if Fs:
         hs, acts, ys = O.swiglu_forward(o["x"], o["W13s"], o["W2s"], glu)
         gs = O.swiglu_backward(o["x"], o["W13s"], o["W2s"], hs, o["dy"], glu)
@@ -226,11 +239,16 @@ def check_grouped_experts(shape, cid):
         for name, got, rf in (("Y_s", Y_s, ys), ("dx_s", dx_s, gs["dX"])):
             err = rel_err(to_np(got), rf)
             assert err < tl, f"{name}: {err:.3e}"
-        check_grad("dW13s", to_np(dW13s), gs["dW13"], shape)
-        check_grad("dW2s", to_np(dW2s), gs["dW2"], shape)
+        souts = [("", to_np(dW13s), to_np(dW2s))]
         if cfg.wgrad_dtype == L.MOE_BF16:
-            check_grad("dW13s (fp32)", fW13s_np, gs["dW13"], shape)
-            check_grad("dW2s (fp32)", fW2s_np, gs["dW2"], shape)
+            souts.append((" (fp32)", fW13s_np, fW2s_np))
+        for tag, g13, g2 in souts:
+            if shape.act == "f32":
+                check_grad(f"dW13s{tag}", g13, gs["dW13"], shape)
+                check_grad(f"dW2s{tag}", g2, gs["dW2"], shape)
+            else:   # the shared expert's dY is the bf16 input dy itself: exact
+                check_wgrad(f"dW13s{tag}", g13, gs["dH"], o["x"], 1, 0)
+                check_wgrad(f"dW2s{tag}", g2, o["dy"], acts, 0, 1)
 
 
 @pytest.mark.parametrize("cid", SMALL_IDS)

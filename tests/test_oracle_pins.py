@@ -757,3 +757,174 @@ def test_shared_gate_printed_form_and_limits():
     # a zero gate weight halves the shared output
     z = O.layer_forward(L["x"], L["Wg"], L["W13"], L["W2"], spec, W13s=L["W13s"], W2s=L["W2s"], Wsg=np.zeros(8))
     np.testing.assert_allclose(z["y"], plain["y"] - 0.5 * plain["shared"]["Y"], rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ routing margins
+
+def _brute_margin(row, k):
+    """Pure Python: the smallest selected key minus the largest unselected key, the
+    selected set taken from the brute-force top-k (inf when every expert is selected)."""
+    sel = set(O.brute_force_topk(row, k))
+    if len(sel) == len(row):
+        return math.inf
+    return min(float(row[e]) for e in sel) - max(float(row[e]) for e in range(len(row)) if e not in sel)
+
+
+def test_margins_match_brute_force_and_distance_to_a_flip():
+    rng = np.random.default_rng(81)
+    T, E = 30, 7
+    keys = rng.standard_normal((T, E))
+    for k in range(1, E + 1):
+        m = O.margins(keys, k)
+        assert m.shape == (T,)
+        for t in range(T):
+            assert m[t] == _brute_margin(keys[t], k)
+    assert np.all(O.margins(keys, E) == np.inf)
+    # an exact tie at the k-th place has margin 0; a tie inside the selection does not matter
+    row = np.array([[3.0, 1.0, 2.0, 1.0, 0.5]])
+    assert O.margins(row, 3)[0] == 0.0
+    assert O.margins(row, 2)[0] == 1.0
+    assert O.margins(row, 4)[0] == 0.5
+    # the margin is the distance to a flip: moving the k-th key down and the (k+1)-th up by
+    # just under half of it keeps the selected set, by just over half of it changes the set
+    k = 3
+    m = O.margins(keys, k)
+    for t in range(T):
+        order = np.argsort(-keys[t], kind="stable")
+        s_last, u_first = order[k - 1], order[k]
+        for frac, same in ((0.49, True), (0.51, False)):
+            p = keys[t].copy()
+            p[s_last] -= frac * m[t]
+            p[u_first] += frac * m[t]
+            moved = set(O.topk(p[None, :], k)[0].tolist()) != set(order[:k].tolist())
+            assert moved != same, (t, frac)
+
+
+def test_group_limited_route_margin_matches_brute_force():
+    """The margin of a group-limited token is the nearer of its two decisions: the gap between
+    the last kept and the first dropped group score, and the key gap inside the kept groups."""
+    from itertools import combinations
+    rng = np.random.default_rng(82)
+    T, E, G, gk, k = 40, 16, 4, 2, 4
+    n, mpick = E // G, k // gk
+    logits = rng.standard_normal((T, E))
+    spec = O.LayerSpec(E=E, k=k, score="sigmoid", num_groups=G, group_topk=gk)
+    r = O.route(logits, spec)
+    for t in range(T):
+        row = [float(v) for v in r["keys"][t]]
+        # group scores added from the largest key down, as the oracle states
+        score = []
+        for g in range(G):
+            acc = 0.0
+            for v in sorted(row[g * n:(g + 1) * n], reverse=True)[:mpick]:
+                acc += v
+            score.append(acc)
+        kept = max(combinations(range(G), gk), key=lambda S: sum(score[g] for g in S))
+        ranked = sorted(score, reverse=True)
+        gmargin = ranked[gk - 1] - ranked[gk]
+        pool = [e for g in sorted(kept) for e in range(g * n, (g + 1) * n)]
+        inner = sorted((row[e] for e in pool), reverse=True)
+        kmargin = inner[k - 1] - inner[k]
+        assert r["margin"][t] == min(gmargin, kmargin), t
+        assert r["margin"][t] > 0
+
+
+# ------------------------------------------------------------------ router-path backward
+
+_RP_CASES = [
+    dict(score="softmax", k=2, aux=0.7, bias="bg"),
+    dict(score="sigmoid", k=3, aux=0.0, bias="expert_bias", extra=dict(scaling=2.5)),
+    dict(score="softmax", k=2, aux=0.2, bias=None, extra=dict(z_coeff=0.05, seq_aux_coeff=0.3, seq_len=4)),
+    dict(score="softmax", k=1, aux=0.4, bias="bg", extra=dict(pre_softmax=True)),
+    dict(score="sqrtsoftplus", k=2, aux=0.3, bias="expert_bias"),
+]
+
+
+def _router_path_loss(x_router, x_expert, Wg, bg, eb, Yfull, dy, spec):
+    """L = sum(dy * y) + aux + z + seq_aux where the router sees x_router and every expert
+    output is frozen at Yfull [T, E, d] (computed from x_expert)."""
+    logits = O.gate_logits(x_router, Wg, bg)
+    r = O.route(logits, spec, eb)
+    T = x_expert.shape[0]
+    y = np.zeros_like(x_expert)
+    for t in range(T):
+        for j in range(spec.k):
+            y[t] += r["w"][t, j] * Yfull[t, r["idx"][t, j]]
+    return float(np.sum(dy * y) + r["aux"] + r["z"] + r["seq_aux"])
+
+
+@pytest.mark.parametrize("case", _RP_CASES)
+def test_router_path_backward_equals_layer_backward_and_differences(case):
+    rng = np.random.default_rng(83)
+    extra = dict(case.get("extra", {}))
+    scaling = extra.pop("scaling", 1.0)
+    L, spec = _rand_layer(rng, T=16, d=8, E=5, k=case["k"], F=6, score=case["score"], scaling=scaling,
+                          aux=case["aux"], bias=case["bias"], **extra)
+    keys = O.selection_keys(O.gate_logits(L["x"], L["Wg"], L["bg"]), spec.score, L["expert_bias"])
+    assert O.margins(keys, spec.k).min() > 1e-4
+    f = O.layer_forward(L["x"], L["Wg"], L["W13"], L["W2"], spec, bg=L["bg"], expert_bias=L["expert_bias"])
+    b = O.layer_backward(f, L["x"], L["Wg"], L["W13"], L["W2"], L["dy"], spec, daux=1.0)
+    rp = O.router_path_backward(f, L["x"], L["Wg"], L["dy"], spec, daux=1.0)
+    for name in ("dw", "dlogits", "dWg", "dbg", "dx_router"):
+        np.testing.assert_allclose(rp[name], b[name], rtol=1e-12, atol=1e-14, err_msg=name)
+    # central differences with the experts frozen: every token's output under every expert
+    Yfull = np.stack([np.stack([O.swiglu_forward(L["x"][t:t + 1], L["W13"][e], L["W2"][e])[2][0]
+                                for e in range(spec.E)]) for t in range(16)])
+    args = lambda xr, Wg, bg: _router_path_loss(xr, L["x"], Wg, bg, L["expert_bias"], Yfull, L["dy"], spec)  # noqa: E731
+    h = 1e-6
+    params = [("x", "dx_router"), ("Wg", "dWg")] + ([("bg", "dbg")] if L["bg"] is not None else [])
+    for pname, gname in params:
+        P = (L["x"] if pname == "x" else L[pname]).copy()
+        flat = P.reshape(-1)
+        for i in rng.choice(flat.size, size=min(flat.size, 30), replace=False):
+            old = flat[i]
+            vals = []
+            for step in (h, -h):
+                flat[i] = old + step
+                xr = P if pname == "x" else L["x"]
+                Wg = P if pname == "Wg" else L["Wg"]
+                bg = P if pname == "bg" else L["bg"]
+                vals.append(args(xr, Wg, bg))
+            flat[i] = old
+            fd = (vals[0] - vals[1]) / (2 * h)
+            an = rp[gname].reshape(-1)[i]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (pname, i, fd, an)
+
+
+def test_router_path_backward_of_the_fp8_layer_matches_differences():
+    """The e4m3 layer's experts do not depend on Wg or bg, so the loss's derivatives in those
+    are the router-path gradients the oracle returns for it."""
+    rng = np.random.default_rng(84)
+    T, d, E, k, F = 6, 128, 4, 2, 128
+    spec = O.LayerSpec(E=E, k=k, score="softmax", aux_coeff=0.5)
+    x = rng.standard_normal((T, d))
+    Wg = rng.standard_normal((E, d)) / np.sqrt(d)
+    bg = rng.standard_normal(E) * 0.3
+    dy = rng.standard_normal((T, d))
+    q13 = [O.quantize_blocks(rng.standard_normal((2 * F, d)).astype(np.float32) * 0.05, 128) for _ in range(E)]
+    q2 = [O.quantize_blocks(rng.standard_normal((d, F)).astype(np.float32) * 0.05, 128) for _ in range(E)]
+    W13q, W13s = np.stack([a for a, _ in q13]), np.stack([b for _, b in q13])
+    W2q, W2s = np.stack([a for a, _ in q2]), np.stack([b for _, b in q2])
+    assert O.margins(O.gate_logits(x, Wg, bg), k).min() > 1e-4
+
+    def loss(Wg_, bg_):
+        f = O.layer_forward_fp8(x, Wg_, W13q, W13s, W2q, W2s, spec, bg=bg_)
+        return float(np.sum(dy * f["y"]) + f["route"]["aux"])
+
+    f = O.layer_forward_fp8(x, Wg, W13q, W13s, W2q, W2s, spec, bg=bg)
+    rp = O.router_path_backward(f, x, Wg, dy, spec, daux=1.0)
+    h = 1e-6
+    for P, gname, pick in ((Wg, "dWg", 30), (bg, "dbg", E)):
+        flat = P.reshape(-1)
+        for i in rng.choice(flat.size, size=pick, replace=False):
+            old = flat[i]
+            flat[i] = old + h
+            lp = loss(Wg, bg)
+            flat[i] = old - h
+            lm = loss(Wg, bg)
+            flat[i] = old
+            fd = (lp - lm) / (2 * h)
+            an = rp[gname].reshape(-1)[i]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (gname, i, fd, an)
+    # dx_router is dlogits through the router's weight
+    np.testing.assert_allclose(rp["dx_router"], rp["dlogits"] @ Wg, rtol=1e-12, atol=1e-14)
