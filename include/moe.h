@@ -230,6 +230,21 @@ moe_status_t moe_router_topk(const moe_config_t* cfg, const float* logits, const
                              int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* stats,
                              int32_t* seq_counts, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_router_topk for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same call and kernels, with no
+ * workspace argument.  Its scratch (the router's block partials) lives in a static device
+ * array of 8 MiB inside the library -- one per GPU, held until the process ends -- whose
+ * device address is looked up once per device on the first call there.  The call allocates
+ * nothing.  Every kernel fully writes the scratch it reads, so no clearing is needed, but
+ * all calls on one GPU share that array: calls that overlap on one GPU (concurrent host
+ * threads, or different streams) race and must not be issued.  Errors: as moe_router_topk,
+ * plus MOE_ERR_WORKSPACE when the configuration needs more than the 8 MiB (the router's
+ * partials are about 8 * E * ceil(T / 64) bytes, more with the sequence-wise loss), and
+ * MOE_ERR_HIP when the array's address cannot be taken. */
+moe_status_t moe_router_topk_noalloc(const moe_config_t* cfg, const float* logits, const float* expert_bias,
+                                     int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* stats,
+                                     int32_t* seq_counts, void* stream);
+
 /* Loss-free balancing bias, one update ([HB] §3.3 Load balancing, Loss-free bias):
  *   direction_e = sign(sum(counts) - counts[e] * E)   (integers: exact),
  *   step_e = direction_e * rate;  centered != 0: step_e -= (rate * sum_e direction_e) / E;

@@ -31,7 +31,7 @@ EXPORTED = (
     "moe_unpermute_combine_bwd", "moe_grouped_gemm_swiglu_bwd", "moe_grouped_wgrad", "moe_permute_bwd", "moe_router_bwd",
     "moe_quantize_fp8", "moe_permute_fp8", "moe_grouped_gemm_swiglu_fp8",
     "moe_gate_logits_bwd", "moe_layer_bwd", "moe_expert_bias_update", "moe_router_quantile",
-    "moe_quantile_bias_update", "moe_shared_gate", "moe_shared_gate_bwd",
+    "moe_quantile_bias_update", "moe_shared_gate", "moe_shared_gate_bwd", "moe_router_topk_noalloc",
 )
 
 
@@ -202,6 +202,19 @@ def router_topk(cfg, logits, expert_bias, idx, w, counts, prob_sum, stats, ws, s
                                   _P(_ptr(stats, torch.float32, MOE_NSTATS, "stats")),
                                   _P(_ptr(seq_counts, torch.int32, nsc, "seq_counts")), _P(wp), ctypes.c_size_t(wn),
                                   _P(_stream(stream))))
+
+
+def router_topk_noalloc(cfg, logits, expert_bias, idx, w, counts, prob_sum, stats, stream=None, seq_counts=None):
+    """moe_router_topk with the library's static scratch instead of a workspace."""
+    TK = cfg.T * cfg.k
+    nsc = num_sequences(cfg) * cfg.E
+    _check(load().moe_router_topk_noalloc(ctypes.byref(cfg), _P(_ptr(logits, torch.float32, cfg.T * cfg.E, "logits")),
+                                          _P(_ptr(expert_bias, torch.float32, cfg.E, "expert_bias")),
+                                          _P(_ptr(idx, torch.int32, TK, "idx")), _P(_ptr(w, torch.float32, TK, "w")),
+                                          _P(_ptr(counts, torch.int32, cfg.E, "counts")),
+                                          _P(_ptr(prob_sum, torch.float32, cfg.E, "prob_sum")),
+                                          _P(_ptr(stats, torch.float32, MOE_NSTATS, "stats")),
+                                          _P(_ptr(seq_counts, torch.int32, nsc, "seq_counts")), _P(_stream(stream))))
 
 
 def expert_bias_update(cfg, counts, rate, centered, expert_bias, stream=None):

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -156,6 +157,37 @@ RouterWs router_ws(const FwdWs& f) {
   r.pnorm = f.pnorm;
   r.seq_cnt_part = f.seq_cnt_part;
   r.seq_prob_part = f.seq_prob_part;
+  return r;
+}
+
+// The router's own scratch (its block partials and, for the sequence-wise loss, the
+// per-token normalisers and per-sequence partials) plus a prob_sum buffer for callers that
+// pass none: the layout of moe_router_topk_noalloc's static scratch.
+struct RouterScratch {
+  RouterWs rw;
+  float* prob_sum;  // [E]
+  size_t bytes;
+};
+
+RouterScratch carve_router(const moe_config_t& c, void* base) {
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* q = p ? p + off : nullptr;
+    off += align_up(n);
+    return q;
+  };
+  const size_t nblk = static_cast<size_t>(router_num_blocks(c.T));
+  RouterScratch r{};
+  r.rw.cnt_part = reinterpret_cast<int32_t*>(take(nblk * c.E * 4));
+  r.rw.prob_part = reinterpret_cast<float*>(take(nblk * c.E * 4));
+  r.rw.z_part = reinterpret_cast<float*>(take(nblk * 4));
+  const size_t nseq = router_seq_part_elems(c);
+  r.rw.pnorm = nseq ? reinterpret_cast<float*>(take(static_cast<size_t>(c.T) * 8)) : nullptr;
+  r.rw.seq_cnt_part = nseq ? reinterpret_cast<int32_t*>(take(nseq * 4)) : nullptr;
+  r.rw.seq_prob_part = nseq ? reinterpret_cast<float*>(take(nseq * 4)) : nullptr;
+  r.prob_sum = reinterpret_cast<float*>(take(static_cast<size_t>(c.E) * 4));
+  r.bytes = off;
   return r;
 }
 
@@ -455,6 +487,34 @@ moe_status_t run_gate_bwd(const moe_config_t& c, const void* x, const float* Wg,
   return MOE_OK;
 }
 
+// ------------------------------------------------- scratch of the allocation-free router call
+// moe_router_topk_noalloc keeps its scratch in this file-scope device array instead of a
+// workspace.  Each GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: the device address is
+// taken once per device with hipGetSymbolAddress and only that address is used.
+constexpr size_t kNoallocScratchBytes = size_t{8} << 20;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status_t scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_HIP, "moe_router_topk_noalloc: no current device (or device id >= %d)", kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "moe_router_topk_noalloc: hipGetSymbolAddress failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -510,6 +570,25 @@ moe_status_t moe_router_topk(const moe_config_t* cfg, const float* logits, const
   float* ps = prob_sum ? prob_sum : fw.prob_sum;
   return launch_router_topk(*cfg, logits, expert_bias, idx, w, counts, ps, stats, seq_counts, router_ws(fw),
                             S(stream));
+}
+
+moe_status_t moe_router_topk_noalloc(const moe_config_t* cfg, const float* logits, const float* expert_bias,
+                                     int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* stats,
+                                     int32_t* seq_counts, void* stream) {
+  MOE_TRY(validate(cfg));
+  MOE_NEED(logits); MOE_NEED(idx); MOE_NEED(w); MOE_NEED(counts);
+  if (cfg->seq_aux_coeff != 0.0f) MOE_NEED(seq_counts);
+  if (expert_bias && cfg->score == MOE_SOFTMAX)
+    return fail(MOE_ERR_UNSUPPORTED, "the expert bias is provided for sigmoid and sqrt(softplus) scores only");
+  const size_t need = carve_router(*cfg, nullptr).bytes;
+  if (need > kNoallocScratchBytes)
+    return fail(MOE_ERR_WORKSPACE, "%s: this configuration needs %zu bytes of scratch, more than the %zu of the static "
+                "scratch (use moe_router_topk with a workspace)", __func__, need, kNoallocScratchBytes);
+  void* base = nullptr;
+  MOE_TRY(scratch_address(&base));
+  const RouterScratch rs = carve_router(*cfg, base);
+  return launch_router_topk(*cfg, logits, expert_bias, idx, w, counts, prob_sum ? prob_sum : rs.prob_sum, stats,
+                            seq_counts, rs.rw, S(stream));
 }
 
 moe_status_t moe_expert_bias_update(const moe_config_t* cfg, const int32_t* counts, float rate, int32_t centered,

@@ -23,10 +23,19 @@ def header_functions():
 def test_library_exports_every_declared_entry_point():
     lib = L.load()
     names = header_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     assert sorted(L.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_router_noalloc_refuses_configurations_beyond_its_scratch():
+    """The allocation-free router call checks the scratch it needs before touching the GPU."""
+    lib = L.load()
+    cfg = L.make_config(T=65536, d=64, E=2048, k=8, F=128, act="f32")   # 16 MiB of block partials
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib.moe_router_topk_noalloc(ctypes.byref(cfg), fake, None, fake, fake, fake, None, None, None, None)
+    assert st == L.MOE_ERR_WORKSPACE and b"static" in lib.moe_last_error()
 
 
 def _status(cfg):
