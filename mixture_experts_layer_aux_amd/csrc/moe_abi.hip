@@ -47,6 +47,7 @@ struct FwdWs {
   int32_t* cnt_part;   // [nchunk, E] router chunk histograms == permute chunk histograms
   float* prob_part;    // [nchunk, E]
   float* z_part;       // [nchunk]
+  int32_t* done;       // the router finaliser's block counter
   float* pnorm;        // [T, 2] (sequence-wise loss only)
   int32_t* seq_cnt_part;  // router_seq_part_elems
   float* seq_prob_part;   // router_seq_part_elems
@@ -75,6 +76,7 @@ FwdWs carve_fwd(const moe_config_t& c, void* base) {
   w.cnt_part = reinterpret_cast<int32_t*>(take(nch * c.E * 4));
   w.prob_part = reinterpret_cast<float*>(take(nch * c.E * 4));
   w.z_part = reinterpret_cast<float*>(take(nch * 4));
+  w.done = reinterpret_cast<int32_t*>(take(4));
   const size_t nseq = router_seq_part_elems(c);
   w.pnorm = nseq ? reinterpret_cast<float*>(take(static_cast<size_t>(c.T) * 8)) : nullptr;
   w.seq_cnt_part = nseq ? reinterpret_cast<int32_t*>(take(nseq * 4)) : nullptr;
@@ -154,6 +156,7 @@ RouterWs router_ws(const FwdWs& f) {
   r.cnt_part = f.cnt_part;
   r.prob_part = f.prob_part;
   r.z_part = f.z_part;
+  r.done = f.done;
   r.pnorm = f.pnorm;
   r.seq_cnt_part = f.seq_cnt_part;
   r.seq_prob_part = f.seq_prob_part;
@@ -182,6 +185,7 @@ RouterScratch carve_router(const moe_config_t& c, void* base) {
   r.rw.cnt_part = reinterpret_cast<int32_t*>(take(nblk * c.E * 4));
   r.rw.prob_part = reinterpret_cast<float*>(take(nblk * c.E * 4));
   r.rw.z_part = reinterpret_cast<float*>(take(nblk * 4));
+  r.rw.done = reinterpret_cast<int32_t*>(take(4));
   const size_t nseq = router_seq_part_elems(c);
   r.rw.pnorm = nseq ? reinterpret_cast<float*>(take(static_cast<size_t>(c.T) * 8)) : nullptr;
   r.rw.seq_cnt_part = nseq ? reinterpret_cast<int32_t*>(take(nseq * 4)) : nullptr;
@@ -567,9 +571,8 @@ moe_status_t moe_router_topk(const moe_config_t* cfg, const float* logits, const
     return fail(MOE_ERR_UNSUPPORTED, "the expert bias is provided for sigmoid and sqrt(softplus) scores only");
   const FwdWs fw = carve_fwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
-  float* ps = prob_sum ? prob_sum : fw.prob_sum;
-  return launch_router_topk(*cfg, logits, expert_bias, idx, w, counts, ps, stats, seq_counts, router_ws(fw),
-                            S(stream));
+  return launch_router_topk(*cfg, logits, expert_bias, idx, w, counts, prob_sum, fw.prob_sum, stats, seq_counts,
+                            router_ws(fw), S(stream));
 }
 
 moe_status_t moe_router_topk_noalloc(const moe_config_t* cfg, const float* logits, const float* expert_bias,
@@ -587,8 +590,8 @@ moe_status_t moe_router_topk_noalloc(const moe_config_t* cfg, const float* logit
   void* base = nullptr;
   MOE_TRY(scratch_address(&base));
   const RouterScratch rs = carve_router(*cfg, base);
-  return launch_router_topk(*cfg, logits, expert_bias, idx, w, counts, prob_sum ? prob_sum : rs.prob_sum, stats,
-                            seq_counts, rs.rw, S(stream));
+  return launch_router_topk(*cfg, logits, expert_bias, idx, w, counts, prob_sum, rs.prob_sum, stats, seq_counts,
+                            rs.rw, S(stream));
 }
 
 moe_status_t moe_expert_bias_update(const moe_config_t* cfg, const int32_t* counts, float rate, int32_t centered,
@@ -702,7 +705,7 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   hipStream_t s = S(stream);
   MOE_TRY(run_gate(c, x, W->Wg, W->bg, sv->logits, fw.gate, s));
   if (c.shared_gate) MOE_TRY(launch_shared_gate(c, x, W->Wsg, sv->gs, s));
-  MOE_TRY(launch_router_topk(c, sv->logits, W->expert_bias, sv->idx, sv->w, sv->counts, fw.prob_sum, stats,
+  MOE_TRY(launch_router_topk(c, sv->logits, W->expert_bias, sv->idx, sv->w, sv->counts, nullptr, fw.prob_sum, stats,
                              sv->seq_counts, router_ws(fw), s));
   if (fp8) {
     // x is quantised per token per 128 before the permute, so the permute moves e4m3 rows

@@ -18,12 +18,13 @@ struct RouterWs {
   float* pnorm;            // [T, 2]    per-token (m, 1/Z) of the aux probabilities
   int32_t* seq_cnt_part;   // [B, ceil(S/64), E]
   float* seq_prob_part;    // [B, ceil(S/64), E]
+  int32_t* done;           // one counter: blocks of the router's finaliser that are done
 };
 // elements of each per-sequence partial (0 when the sequence-wise loss is off)
 size_t router_seq_part_elems(const moe_config_t& c);
 moe_status_t launch_router_topk(const moe_config_t& c, const float* logits, const float* expert_bias,
-                                int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* stats,
-                                int32_t* seq_counts, const RouterWs& rw, hipStream_t s);
+                                int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* prob_scratch,
+                                float* stats, int32_t* seq_counts, const RouterWs& rw, hipStream_t s);
 moe_status_t launch_router_bwd(const moe_config_t& c, const float* logits, const int32_t* idx, const float* w,
                                const float* dw, const int32_t* counts, const int32_t* seq_counts, float daux,
                                float* dlogits, hipStream_t s);

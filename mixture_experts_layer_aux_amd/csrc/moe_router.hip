@@ -12,6 +12,8 @@
 #include <float.h>
 #include <limits.h>
 
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -482,6 +484,605 @@ __global__ __launch_bounds__(1024) void router_stats_kernel(const int32_t* __res
   }
 }
 
+// ======================================================================= row-group router
+// The router of layers without group-limited routing.  A token is handled by a group of
+// LPT lanes (16, 32 or 64): lane g of a group holds the experts e = i * LPT + g, i < KPL,
+// so a token's logits are read with coalesced loads and its keys stay in registers.  Each
+// lane keeps its three best keys in order (key descending, then index ascending); a
+// token's k winners come from k rounds of a group arg-max over the lanes' first entries --
+// DPP moves inside a 16-lane row and the gfx950 permlane swaps across rows, no LDS -- after
+// which the winning lane drops its first entry, and rescans its keys in the rare round
+// where all three are used.  Slot j's winner is kept by lane j of the group (LPT >= k).
+namespace rg {
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_v(float v) { return __int_as_float(dpp_i<CTRL>(__float_as_int(v))); }
+template <int CTRL>
+__device__ __forceinline__ double dpp_v(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = dpp_i<CTRL>(static_cast<int>(b));
+  const int hi = dpp_i<CTRL>(static_cast<int>(b >> 32));
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+// A permlane swap of v with itself: every lane gets its own value in one half of the pair
+// and its partner's (W = 16 or 32 lanes away) in the other.
+template <int W>
+__device__ __forceinline__ void swap_i(int v, int& a, int& b) {
+  if constexpr (W == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    a = static_cast<int>(r[0]);
+    b = static_cast<int>(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = static_cast<int>(r[0]);
+    b = static_cast<int>(r[1]);
+  }
+}
+template <int W>
+__device__ __forceinline__ void swap_v(float v, float& a, float& b) {
+  int ia, ib;
+  swap_i<W>(__float_as_int(v), ia, ib);
+  a = __int_as_float(ia);
+  b = __int_as_float(ib);
+}
+template <int W>
+__device__ __forceinline__ void swap_v(double v, double& a, double& b) {
+  const long long x = __double_as_longlong(v);
+  int la, lb, ha, hb;
+  swap_i<W>(static_cast<int>(x), la, lb);
+  swap_i<W>(static_cast<int>(x >> 32), ha, hb);
+  a = __longlong_as_double((static_cast<long long>(ha) << 32) | static_cast<unsigned int>(la));
+  b = __longlong_as_double((static_cast<long long>(hb) << 32) | static_cast<unsigned int>(lb));
+}
+
+// DPP controls: lane ^ 1 and lane ^ 2 (quad permutes), the other quad of each 8 lanes
+// (half-row mirror), the other 8 lanes of each 16 (row mirror).  After each step both lanes
+// of a pair hold the same value, so the mirrors pair whole reduced blocks.
+constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+
+template <int CTRL, typename KT>
+__device__ __forceinline__ void argmax_step(KT& k, int& e) {
+  const KT ok = dpp_v<CTRL>(k);
+  const int oe = dpp_i<CTRL>(e);
+  if (better(ok, oe, k, e)) {
+    k = ok;
+    e = oe;
+  }
+}
+template <int W, typename KT>
+__device__ __forceinline__ void argmax_swap(KT& k, int& e) {
+  KT ka, kb;
+  int ea, eb;
+  swap_v<W>(k, ka, kb);
+  swap_i<W>(e, ea, eb);
+  const bool b_wins = better(kb, eb, ka, ea);
+  k = b_wins ? kb : ka;
+  e = b_wins ? eb : ea;
+}
+// (key, index) arg-max over the LPT lanes of each group, the lower index winning ties; the
+// result is on every lane of the group.
+template <int LPT, typename KT>
+__device__ __forceinline__ void group_argmax(KT& k, int& e) {
+  argmax_step<kXor1>(k, e);
+  argmax_step<kXor2>(k, e);
+  argmax_step<kHalfMirror>(k, e);
+  argmax_step<kMirror>(k, e);
+  if constexpr (LPT >= 32) argmax_swap<16>(k, e);
+  if constexpr (LPT == 64) argmax_swap<32>(k, e);
+}
+// Sum over the LPT lanes of each group (fixed order, the same bits on every lane).
+template <int LPT, typename V>
+__device__ __forceinline__ V group_sum(V v) {
+  v += dpp_v<kXor1>(v);
+  v += dpp_v<kXor2>(v);
+  v += dpp_v<kHalfMirror>(v);
+  v += dpp_v<kMirror>(v);
+  V a, b;
+  if constexpr (LPT >= 32) {
+    swap_v<16>(v, a, b);
+    v = a + b;
+  }
+  if constexpr (LPT == 64) {
+    swap_v<32>(v, a, b);
+    v = a + b;
+  }
+  return v;
+}
+template <int LPT>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp_v<kXor1>(v));
+  v = fmaxf(v, dpp_v<kXor2>(v));
+  v = fmaxf(v, dpp_v<kHalfMirror>(v));
+  v = fmaxf(v, dpp_v<kMirror>(v));
+  float a, b;
+  if constexpr (LPT >= 32) {
+    swap_v<16>(v, a, b);
+    v = fmaxf(a, b);
+  }
+  if constexpr (LPT == 64) {
+    swap_v<32>(v, a, b);
+    v = fmaxf(a, b);
+  }
+  return v;
+}
+// Sum over the 64 / LPT groups of a wave, lane by lane (lane g of every group gets the sum
+// of lane g of all groups).
+template <int LPT>
+__device__ __forceinline__ float across_groups_sum(float v) {
+  float a, b;
+  if constexpr (LPT == 16) {
+    swap_v<16>(v, a, b);
+    v = a + b;
+  }
+  if constexpr (LPT <= 32) {
+    swap_v<32>(v, a, b);
+    v = a + b;
+  }
+  return v;
+}
+
+// A lane's three best (key, expert) pairs in order.  insert() takes keys in ascending expert
+// order, so a key equal to one already held ranks after it.
+template <typename KT>
+struct Top3 {
+  KT k0, k1, k2;
+  int e0, e1, e2;
+  __device__ __forceinline__ void clear() {
+    k0 = k1 = k2 = lowest_key<KT>();
+    e0 = e1 = e2 = INT_MAX;
+  }
+  __device__ __forceinline__ void insert(KT kv, int ev) {
+    const bool c0 = kv > k0, c1 = kv > k1, c2 = kv > k2;
+    if (c2) {
+      k2 = c1 ? k1 : kv;
+      e2 = c1 ? e1 : ev;
+    }
+    if (c1) {
+      k1 = c0 ? k0 : kv;
+      e1 = c0 ? e0 : ev;
+    }
+    if (c0) {
+      k0 = kv;
+      e0 = ev;
+    }
+  }
+  __device__ __forceinline__ void pop() {
+    k0 = k1;
+    e0 = e1;
+    k1 = k2;
+    e1 = e2;
+    k2 = lowest_key<KT>();
+    e2 = INT_MAX;
+  }
+};
+
+}  // namespace rg
+
+struct RouterRowArgs {
+  const float* logits;
+  const float* expert_bias;
+  int T, E, k, score, pre_softmax;
+  float scaling;
+  int32_t* idx;
+  float* w;
+  int32_t* cnt_part;   // [nblk, E]
+  float* prob_part;    // [nblk, E], NULL: the aux probabilities are not summed
+  float* z_part;       // [nblk], NULL: no z-loss
+  float2* pnorm;       // [T], NULL: no sequence-wise pass
+  int32_t* done;       // the finaliser's block counter, reset here
+};
+
+namespace rg {
+
+// k rounds of the group arg-max over the lanes' Top3 lists built from key[] (keys of the
+// experts i * LPT + g, lowest_key for experts the token does not have).  Lane j of the
+// group gets slot j's winner (my_e, my_key); every lane gets the first (top) and the last
+// (kth) winner.
+template <int LPT, int KPL, typename KT>
+__device__ __forceinline__ void select_topk(const KT (&key)[KPL], int g, int E, int k, bool live, int& my_e,
+                                            KT& my_key, KT& top_key, KT& kth_key, int& kth_e) {
+  // keys the token does not have are lowest_key, which insert() never takes
+  Top3<KT> top;
+  top.clear();
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) top.insert(key[i], i * LPT + g);
+  my_e = 0;
+  my_key = lowest_key<KT>();
+  for (int j = 0; j < k; ++j) {
+    KT bk = top.k0;
+    int be = top.e0;
+    group_argmax<LPT>(bk, be);
+    if (j == 0) top_key = bk;
+    kth_key = bk;
+    kth_e = be;
+    if (g == j) {
+      my_e = be;
+      my_key = bk;
+    }
+    if (top.e0 == be) {
+      const KT lk = top.k0;
+      const int le = top.e0;
+      top.pop();
+      if (top.e0 == INT_MAX && j + 1 < k) {
+        // all three used: the next three of this lane's keys after the last one taken
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+          const int e = i * LPT + g;
+          if (better(lk, le, key[i], e)) top.insert(key[i], e);
+        }
+      }
+    }
+  }
+}
+
+// DPP moves between neighbouring lanes of a 16-lane row: lane i gets lane i + 1's value
+// (row_shl:1) or lane i - 1's (row_shr:1).
+constexpr int kFromNext = 0x101, kFromPrev = 0x111;
+
+}  // namespace rg
+
+
+// KEYS: 0 = the fp32 logits (softmax); 1 = fp64 keys s(l) (+ bias); 2 = sigmoid keys chosen
+// on fp32 approximations and confirmed in fp64: the fp32 key of an expert is within
+// half of sig_band of its fp64 key, so when no expert outside the fp32 top-k lies within
+// sig_band of the k-th fp32 key, the fp32 top-k is the fp64 top-k as a set; the slots are
+// then put in fp64 order (a neighbour sort wherever two fp32 keys lie that close), and a
+// wave with any token not so separated routes all its tokens on fp64 keys instead.
+__device__ __forceinline__ float sig_band(float kth) { return 2.0f * (0x1p-19f + 0x1p-22f * fabsf(kth)); }
+__device__ __forceinline__ float sigmoid32(float l) { return __builtin_amdgcn_rcpf(1.0f + __expf(-l)); }
+
+// 64 tokens per block (the permute's chunk, whose histograms it reuses), NW waves; each
+// wave routes 64 / LPT tokens per pass.
+template <int LPT, int KPL, int NW, int KEYS>
+__global__ __launch_bounds__(64 * NW) void router_rows_kernel(const RouterRowArgs a) {
+  extern __shared__ int smem_r[];
+  const int E = a.E, k = a.k;
+  constexpr int TPW = 64 / LPT;
+  // LDS: hist [E] | (KEYS 2: each token's logits [NW * TPW][E]) | (KEYS 1, 2: the selection
+  // biases [E]) | red [NW][E] (prob sums only)
+  int* hist = smem_r;
+  float* stage = reinterpret_cast<float*>(smem_r + E);
+  float* bias_s = stage + (KEYS == 2 ? NW * TPW * E : 0);
+  float* red = bias_s + (KEYS != 0 ? E : 0);
+  __shared__ float red_z[NW];
+  constexpr int PASSES = kRouterTokensPerBlock / (NW * TPW);
+  static_assert(PASSES * NW * TPW == kRouterTokensPerBlock, "a block routes 64 tokens");
+  static_assert(KEYS != 2 || LPT == 16, "the fp32-first sigmoid keys sort slots inside one 16-lane row");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane % LPT, grp = lane / LPT;
+  const bool softmax = KEYS == 0;
+  const bool want_p = a.prob_part != nullptr;
+  // the full-E normaliser: aux probabilities, pre-softmax weights, the sequence pass
+  const bool want_norm = want_p || a.pnorm != nullptr || (softmax && (a.pre_softmax || a.z_part));
+  if (blockIdx.x == 0 && threadIdx.x == 0 && a.done) *a.done = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    hist[e] = 0;
+    if (KEYS != 0) bias_s[e] = a.expert_bias ? a.expert_bias[e] : 0.0f;
+  }
+  __syncthreads();
+
+  float acc[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) acc[i] = 0.0f;
+  float zacc = 0.0f;
+#pragma unroll 1
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int t = blockIdx.x * kRouterTokensPerBlock + (pass * NW + wave) * TPW + grp;
+    const bool live = t < a.T;
+    const float* row = a.logits + static_cast<int64_t>(live ? t : 0) * E;
+    // every load of the token's logits (and biases) is issued before any is used: the
+    // addresses are clamped into the row instead of being guarded by branches
+    float l[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) l[i] = row[min(i * LPT + g, E - 1)];
+    float* my_stage = stage + static_cast<int64_t>(wave * TPW + grp) * E;
+    if constexpr (KEYS == 2) {
+      // the token's logits stay in LDS for the slots' scores below
+#pragma unroll
+      for (int i = 0; i < KPL; ++i)
+        if (i * LPT + g < E) my_stage[i * LPT + g] = l[i];
+    }
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (!(live && i * LPT + g < E)) l[i] = 0.0f;
+    // winners: my_e for lane j < k of the group (slot j); for softmax, top_l is the top-1 logit
+    int my_e = 0;
+    float my_l = 0.0f, top_l = 0.0f;
+    double my_k64 = 0.0, my_s64 = 0.0;   // mode 1, and mode 2's fp64 paths
+    bool have_s64 = false;
+    if constexpr (KEYS == 1) {
+      double key[KPL];
+#pragma unroll
+      for (int i = 0; i < KPL; ++i)
+        key[i] = (live && i * LPT + g < E)
+                     ? score_f64(a.score, l[i]) + static_cast<double>(bias_s[min(i * LPT + g, E - 1)])
+                     : lowest_key<double>();
+      double tk, kk;
+      int ke;
+      rg::select_topk<LPT, KPL, double>(key, g, E, k, live, my_e, my_k64, tk, kk, ke);
+      my_e = (g < k && live) ? my_e : 0;
+    } else {
+      float key[KPL];
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const int e = i * LPT + g;
+        const float kv = KEYS == 0 ? l[i] : sigmoid32(l[i]) + bias_s[min(e, E - 1)];
+        key[i] = (live && e < E) ? kv : lowest_key<float>();
+      }
+      float my_key, top_key, kth_key;
+      int kth_e;
+      rg::select_topk<LPT, KPL, float>(key, g, E, k, live, my_e, my_key, top_key, kth_key, kth_e);
+      my_e = (g < k && live) ? my_e : 0;
+      if constexpr (KEYS == 0) {
+        my_l = my_key;
+        top_l = top_key;
+      } else {
+        const float band = sig_band(kth_key);
+        bool far = true;   // no unselected expert within the band of the k-th key
+#pragma unroll
+        for (int i = 0; i < KPL; ++i)
+          if (live && better(kth_key, kth_e, key[i], i * LPT + g) && key[i] >= kth_key - band) far = false;
+        if (__ballot(!far) != 0) {
+          // some token of this wave has an unselected expert that close: fp64 keys for all
+          double k64[KPL];
+#pragma unroll
+          for (int i = 0; i < KPL; ++i)
+            k64[i] = (live && i * LPT + g < E)
+                         ? score_f64(MOE_SIGMOID, my_stage[min(i * LPT + g, E - 1)]) +
+                               static_cast<double>(bias_s[min(i * LPT + g, E - 1)])
+                         : lowest_key<double>();
+          double tk, kk;
+          int ke;
+          rg::select_topk<LPT, KPL, double>(k64, g, E, k, live, my_e, my_k64, tk, kk, ke);
+          my_e = (g < k && live) ? my_e : 0;
+        } else {
+          // slots in fp64 order: a neighbour (odd-even) sort where two fp32 keys lie within
+          // the band of each other
+          const float next_key = __int_as_float(rg::dpp_i<rg::kFromNext>(__float_as_int(my_key)));
+          const bool near = g + 1 < k && live && my_key - next_key <= sig_band(my_key);
+          if (__ballot(near) != 0) {
+            const bool slot = g < k && live;
+            my_s64 = slot ? score_f64(MOE_SIGMOID, my_stage[my_e]) : 0.0;
+            my_k64 = slot ? my_s64 + static_cast<double>(bias_s[my_e]) : lowest_key<double>();
+            have_s64 = true;
+            for (int ph = 0; ph < k; ++ph) {
+              // both neighbours' values on every lane first: a DPP move reads its source
+              // lane only while that lane is active, so none may sit in a divergent branch
+              const double kn = rg::dpp_v<rg::kFromNext>(my_k64), kp = rg::dpp_v<rg::kFromPrev>(my_k64);
+              const double sn = rg::dpp_v<rg::kFromNext>(my_s64), sp = rg::dpp_v<rg::kFromPrev>(my_s64);
+              const int en = rg::dpp_i<rg::kFromNext>(my_e), ep = rg::dpp_i<rg::kFromPrev>(my_e);
+              const bool lower = (g & 1) == (ph & 1);
+              const double nk = lower ? kn : kp;
+              const double ns = lower ? sn : sp;
+              const int ne = lower ? en : ep;
+              const int partner = lower ? g + 1 : g - 1;
+              if (g < k && partner >= 0 && partner < k) {
+                const bool pb = better(nk, ne, my_k64, my_e);
+                if (lower == pb) {
+                  my_k64 = nk;
+                  my_s64 = ns;
+                  my_e = ne;
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+    // the full-E normaliser (softmax: exp(l - max), the max being the top-1 logit; other
+    // scores: s(l)), and the z-loss's logsumexp of the logits
+    float q[KPL];
+    float m = 0.0f, inv = 0.0f, lse = 0.0f;
+    if (want_norm || a.z_part) {
+      if (softmax) {
+        m = top_l;
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+          q[i] = (live && i * LPT + g < E) ? expf(l[i] - m) : 0.0f;
+          part += q[i];
+        }
+        const float z = rg::group_sum<LPT>(part);
+        inv = 1.0f / z;
+        lse = m + logf(z);
+      } else {
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+          if (KEYS == 2) l[i] = (live && i * LPT + g < E) ? my_stage[min(i * LPT + g, E - 1)] : 0.0f;
+          q[i] = (live && i * LPT + g < E) ? score_f32(a.score, l[i]) : 0.0f;
+          part += q[i];
+        }
+        inv = 1.0f / (rg::group_sum<LPT>(part) + 1e-20f);
+        if (a.z_part) {
+          float mx = -FLT_MAX;
+#pragma unroll
+          for (int i = 0; i < KPL; ++i)
+            if (i * LPT + g < E) mx = fmaxf(mx, l[i]);
+          mx = rg::group_max<LPT>(mx);
+          float pe = 0.0f;
+#pragma unroll
+          for (int i = 0; i < KPL; ++i) pe += (live && i * LPT + g < E) ? expf(l[i] - mx) : 0.0f;
+          lse = mx + logf(rg::group_sum<LPT>(pe));
+        }
+      }
+      if (want_p && live) {
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) acc[i] += q[i] * inv;
+      }
+      if (a.z_part && live && g == 0) zacc += lse * lse;
+      if (a.pnorm && live && g == 0) a.pnorm[t] = make_float2(m, inv);
+    }
+    // mixing weights: lane j < k of the group owns slot j
+    const bool slot = g < k && live;
+    float wv;
+    if constexpr (KEYS == 0) {
+      if (a.pre_softmax) {
+        wv = slot ? expf(my_l - top_l) * inv : 0.0f;
+      } else {
+        const float ex = slot ? expf(my_l - top_l) : 0.0f;
+        wv = ex / rg::group_sum<LPT>(ex);
+      }
+    } else if constexpr (KEYS == 1) {
+      const double sg = slot ? score_f64(a.score, row[slot ? my_e : 0]) : 0.0;
+      const double z = rg::group_sum<LPT>(sg);
+      wv = static_cast<float>(k > 1 ? sg / (z + 1e-20) : sg);
+    } else {
+      // sigmoid scores of the selected experts, renormalised over them (fp32)
+      const float sg = slot ? (have_s64 ? static_cast<float>(my_s64) : sigmoid32(my_stage[my_e])) : 0.0f;
+      const float z = rg::group_sum<LPT>(sg);
+      wv = k > 1 ? sg / (z + 1e-20f) : sg;
+    }
+    if (slot) {
+      a.idx[static_cast<int64_t>(t) * k + g] = my_e;
+      a.w[static_cast<int64_t>(t) * k + g] = wv * a.scaling;
+      atomicAdd(&hist[my_e], 1);   // integer: order-independent
+    }
+  }
+  if (want_p) {
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const float v = rg::across_groups_sum<LPT>(acc[i]);
+      const int e = i * LPT + g;
+      if (grp == 0 && e < E) red[wave * E + e] = v;
+    }
+  }
+  if (a.z_part) {
+    const float zw = rg::group_sum<64>(zacc);
+    if (lane == 0) red_z[wave] = zw;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    a.cnt_part[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
+    if (want_p) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) sum += red[v * E + e];
+      a.prob_part[static_cast<int64_t>(blockIdx.x) * E + e] = sum;
+    }
+  }
+  if (a.z_part && threadIdx.x == 0) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) sum += red_z[v];
+    a.z_part[blockIdx.x] = sum;
+  }
+}
+
+// Column sums of the router's block partials and then, in the last block to finish, the
+// statistics (aux, MaxVio, empty experts, max count, z-loss).  Block x sums the 32 experts
+// [32 x, 32 x + 32): thread (r, c) adds the partials of blocks b = r, r + 32, ... of expert
+// c in that order, 16 loads in flight, then the 32 subset sums are added by a fixed tree.
+// The last block (a counter that router_rows_kernel zeroed, this kernel running after it
+// on the stream) reduces the finished sums in a fixed order: no float atomics.
+__device__ __forceinline__ int coherent_load(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kFinCols = 32;
+
+__global__ __launch_bounds__(1024) void router_finalize_stats_kernel(
+    const int32_t* __restrict__ cnt_part, const float* __restrict__ prob_part, int nblk, int E, int T, int k,
+    float coeff, const float* __restrict__ z_part, float z_coeff, int seq_on, int32_t* __restrict__ counts,
+    float* __restrict__ prob_sum, float* __restrict__ stats, int32_t* __restrict__ done) {
+  constexpr int R = 1024 / kFinCols, U = 16;
+  __shared__ int sc[R][kFinCols];
+  __shared__ float sp[R][kFinCols];
+  __shared__ int s_last;
+  __shared__ double s_dot[16], s_z[16];
+  __shared__ int s_max[16], s_empty[16];
+  const int c = threadIdx.x % kFinCols, r = threadIdx.x / kFinCols;
+  const int e = blockIdx.x * kFinCols + c;
+  int ci = 0;
+  float pf = 0.0f;
+  if (e < E) {
+    for (int b0 = r; b0 < nblk; b0 += R * U) {
+      int v[U];
+      float pv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int b = b0 + u * R;
+        v[u] = b < nblk ? cnt_part[static_cast<int64_t>(b) * E + e] : 0;
+        pv[u] = (prob_part && b < nblk) ? prob_part[static_cast<int64_t>(b) * E + e] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        ci += v[u];
+        pf += pv[u];
+      }
+    }
+  }
+  sc[r][c] = ci;
+  sp[r][c] = pf;
+  __syncthreads();
+  for (int h = R / 2; h > 0; h >>= 1) {
+    if (r < h) {
+      sc[r][c] += sc[r + h][c];
+      sp[r][c] += sp[r + h][c];
+    }
+    __syncthreads();
+  }
+  if (r == 0 && e < E) {
+    counts[e] = sc[0][c];
+    if (prob_part) prob_sum[e] = sp[0][c];
+  }
+  if (!stats) return;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(done, 1) == static_cast<int>(gridDim.x) - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  double dot = 0.0, zs = 0.0;
+  int mx = 0, empty = 0;
+  for (int x = threadIdx.x; x < E; x += blockDim.x) {
+    const int cnt = coherent_load(counts + x);
+    if (prob_part) dot += static_cast<double>(coherent_load(prob_sum + x)) * cnt;
+    mx = max(mx, cnt);
+    empty += (cnt == 0);
+  }
+  if (z_part)
+    for (int b = threadIdx.x; b < nblk; b += blockDim.x) zs += z_part[b];
+  // wave sums (fixed butterfly), then the 16 wave results in order by thread 0
+  dot = wave_sum(dot);
+  zs = wave_sum(zs);
+  for (int o = 32; o >= 1; o >>= 1) {
+    mx = max(mx, __shfl_xor(mx, o, 64));
+    empty += __shfl_xor(empty, o, 64);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_dot[w] = dot;
+    s_z[w] = zs;
+    s_max[w] = mx;
+    s_empty[w] = empty;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double d = 0.0, z = 0.0;
+    int m = 0, em = 0;
+    for (int i = 0; i < static_cast<int>(blockDim.x >> 6); ++i) {
+      d += s_dot[i];
+      z += s_z[i];
+      m = max(m, s_max[i]);
+      em += s_empty[i];
+    }
+    const double Td = static_cast<double>(T);
+    const double mean = Td * k / E;
+    stats[0] = static_cast<float>(d * coeff * E / (k * Td * Td));
+    stats[1] = static_cast<float>((m - mean) / mean);
+    stats[2] = static_cast<float>(em);
+    stats[3] = static_cast<float>(m);
+    stats[4] = z_part ? static_cast<float>(z_coeff * z / Td) : 0.0f;
+    if (!seq_on) stats[5] = 0.0f;
+  }
+}
+
 // Router backward, one wave per token (see moe_router_bwd in moe.h for the formulas).
 struct RouterBwdArgs {
   const float* logits;
@@ -667,32 +1268,96 @@ moe_status_t launch_topk(const moe_config_t& c, int nblk, const float* logits, c
 
 }  // namespace
 
+namespace {
+
+template <int LPT, int KPL, int NW, int KEYS>
+moe_status_t launch_rows_inst(const moe_config_t& c, const RouterRowArgs& a, int nblk, hipStream_t s) {
+  const size_t shm = static_cast<size_t>(c.E) * sizeof(int) +
+                     (KEYS == 2 ? static_cast<size_t>(NW * (64 / LPT)) * c.E * 4 : 0) + (KEYS != 0 ? c.E * 4 : 0) +
+                     (a.prob_part ? static_cast<size_t>(NW) * c.E * 4 : 0);
+  if (shm > 65536 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(router_rows_kernel<LPT, KPL, NW, KEYS>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)) != hipSuccess)
+    return fail(MOE_ERR_HIP, "router: cannot raise the LDS limit to %zu bytes", shm);
+  router_rows_kernel<LPT, KPL, NW, KEYS><<<nblk, 64 * NW, shm, s>>>(a);
+  return MOE_OK;
+}
+
+// lanes per token: 16 while k <= 16 and E <= 512 (up to 32 keys per lane), else 32 (k > 16,
+// E <= 512) or 64 (a group's lane j keeps slot j, so LPT >= k).  Blocks whose lanes hold
+// more than 16 keys, or whose groups span rows, run 8 waves so that each may use up to 256
+// registers without spilling.
+template <int KEYS>
+moe_status_t launch_rows(const moe_config_t& c, const RouterRowArgs& a, int nblk, hipStream_t s) {
+  if (c.k <= 16 && c.E <= 512) {
+    if (c.E <= 16) return launch_rows_inst<16, 1, 16, KEYS>(c, a, nblk, s);
+    if (c.E <= 32) return launch_rows_inst<16, 2, 16, KEYS>(c, a, nblk, s);
+    if (c.E <= 64) return launch_rows_inst<16, 4, 16, KEYS>(c, a, nblk, s);
+    if (c.E <= 128) return launch_rows_inst<16, 8, 16, KEYS>(c, a, nblk, s);
+    if (c.E <= 256) return launch_rows_inst<16, 16, 16, KEYS>(c, a, nblk, s);
+    if constexpr (KEYS != 2) return launch_rows_inst<16, 32, 8, KEYS>(c, a, nblk, s);
+  }
+  if constexpr (KEYS == 2) {
+    return fail(MOE_ERR_UNSUPPORTED, "router: fp32-first sigmoid keys need k <= 16 and E <= 256");
+  } else {
+    if (c.E <= 512) return launch_rows_inst<32, 16, 8, KEYS>(c, a, nblk, s);
+    if (c.E <= 1024) return launch_rows_inst<64, 16, 8, KEYS>(c, a, nblk, s);
+    return launch_rows_inst<64, 32, 8, KEYS>(c, a, nblk, s);
+  }
+}
+
+}  // namespace
+
 moe_status_t launch_router_topk(const moe_config_t& c, const float* logits, const float* expert_bias,
-                                int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* stats,
-                                int32_t* seq_counts, const RouterWs& rw, hipStream_t s) {
+                                int32_t* idx, float* w, int32_t* counts, float* prob_sum, float* prob_scratch,
+                                float* stats, int32_t* seq_counts, const RouterWs& rw, hipStream_t s) {
   const int nblk = static_cast<int>(router_num_blocks(c.T));
   if (nblk != permute_num_chunks(c.T)) return fail(MOE_ERR_UNSUPPORTED, "router blocks differ from permute chunks");
-  const int epl = router_epl(c.E);
   const bool seq_on = c.seq_aux_coeff != 0.0f;
   float* zp = c.z_coeff != 0.0f ? rw.z_part : nullptr;
   float2* pn = seq_on ? reinterpret_cast<float2*>(rw.pnorm) : nullptr;
-  moe_status_t st = MOE_OK;
-  switch (epl) {
-    case 1: st = launch_topk<1>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
-    case 2: st = launch_topk<2>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
-    case 4: st = launch_topk<4>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
-    case 8: st = launch_topk<8>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
-    case 16: st = launch_topk<16>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
-    case 32: st = launch_topk<32>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
-    default:
-      return fail(MOE_ERR_UNSUPPORTED, "router: E=%d too large", c.E);
+  if (c.num_groups == 0) {
+    // the row-group kernel; the aux probabilities are summed only when asked for or when
+    // the aux loss needs them
+    const bool want_p = prob_sum != nullptr || c.aux_coeff != 0.0f;
+    float* ps = prob_sum ? prob_sum : (want_p ? prob_scratch : nullptr);
+    RouterRowArgs a{};
+    a.logits = logits; a.expert_bias = expert_bias;
+    a.T = c.T; a.E = c.E; a.k = c.k; a.score = c.score; a.pre_softmax = c.pre_softmax; a.scaling = c.routed_scaling;
+    a.idx = idx; a.w = w;
+    a.cnt_part = rw.cnt_part; a.prob_part = want_p ? rw.prob_part : nullptr; a.z_part = zp; a.pnorm = pn;
+    a.done = rw.done;
+    // sigmoid keys are chosen on fp32 approximations and confirmed in fp64 when 16 lanes
+    // route a token; other scores compare fp64 keys
+    const bool sig16 = c.score == MOE_SIGMOID && c.k <= 16 && c.E <= 256;
+    MOE_TRY_INTERNAL(c.score == MOE_SOFTMAX ? launch_rows<0>(c, a, nblk, s)
+                     : sig16                ? launch_rows<2>(c, a, nblk, s)
+                                            : launch_rows<1>(c, a, nblk, s));
+    router_finalize_stats_kernel<<<static_cast<int>(ceil_div(c.E, kFinCols)), 1024, 0, s>>>(
+        rw.cnt_part, a.prob_part, nblk, c.E, c.T, c.k, c.aux_coeff, zp, c.z_coeff, seq_on ? 1 : 0, counts, ps, stats,
+        rw.done);
+  } else {
+    // group-limited routing: one wave per token
+    float* ps = prob_sum ? prob_sum : prob_scratch;
+    const int epl = router_epl(c.E);
+    moe_status_t st = MOE_OK;
+    switch (epl) {
+      case 1: st = launch_topk<1>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
+      case 2: st = launch_topk<2>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
+      case 4: st = launch_topk<4>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
+      case 8: st = launch_topk<8>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
+      case 16: st = launch_topk<16>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
+      case 32: st = launch_topk<32>(c, nblk, logits, expert_bias, idx, w, rw, zp, pn, s); break;
+      default:
+        return fail(MOE_ERR_UNSUPPORTED, "router: E=%d too large", c.E);
+    }
+    MOE_TRY_INTERNAL(st);
+    router_finalize_kernel<<<static_cast<int>(ceil_div(c.E, 64)), 1024, 0, s>>>(rw.cnt_part, rw.prob_part, nblk,
+                                                                              c.E, counts, ps);
+    if (stats)
+      router_stats_kernel<<<1, 1024, 0, s>>>(counts, ps, c.E, c.T, c.k, c.aux_coeff, zp, nblk, c.z_coeff,
+                                             seq_on ? 1 : 0, stats);
   }
-  MOE_TRY_INTERNAL(st);
-  router_finalize_kernel<<<static_cast<int>(ceil_div(c.E, 64)), 1024, 0, s>>>(rw.cnt_part, rw.prob_part, nblk, c.E,
-                                                                            counts, prob_sum);
-  if (stats)
-    router_stats_kernel<<<1, 1024, 0, s>>>(counts, prob_sum, c.E, c.T, c.k, c.aux_coeff, zp, nblk, c.z_coeff,
-                                           seq_on ? 1 : 0, stats);
   if (seq_on) {
     const int S = c.seq_len, B = c.T / c.seq_len, nsc = static_cast<int>(ceil_div(S, 64));
     const size_t shm_s = static_cast<size_t>(c.E) * sizeof(int);
