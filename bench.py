@@ -44,21 +44,25 @@ GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_aux_amd", "csrc", "moe_g
 def algorithmic(shape, wgrad_bytes=4):
     """Algorithmic work per step: the bytes each HBM-bound kernel must move and the FLOP
     each GEMM must compute, at minimum.  wgrad_bytes: bytes per expert weight-gradient
-    element (2 for bf16, 4 for fp32)."""
+    element (2 for bf16, 4 for fp32).  bf16 layers keep no grouped copy of x: the permute
+    moves indices only and the fc1 GEMMs read the token rows through token_of."""
     T, d, E, k, F, Fs = shape.T, shape.d, shape.E, shape.k, shape.F, shape.Fs
     A = T * k
     eb = 2 if shape.act == "bf16" else 4
+    gather = shape.act == "bf16"
     gemm_fwd = 6.0 * d * (F * A + Fs * T)          # fc1 (2 x d x 2F) + fc2 (2 x F x d) per row
     return dict(
         grouped_gemm_flop=3.0 * gemm_fwd,          # forward + data gradient + weight gradient
-        wgrad_fc1_flop=2.0 * A * 2 * F * d,        # dW13 = dH^T x_perm over the routed rows
-        # dW13 written once, dH and x_perm read once, the offsets
-        wgrad_fc1_bytes=E * 2 * F * d * wgrad_bytes + A * 2 * F * eb + A * d * eb + (E + 1) * 4,
+        wgrad_fc1_flop=2.0 * A * 2 * F * d,        # dW13 = dH^T X over the routed rows
+        # dW13 written once, dH and the routed rows of x read once, the offsets (and the
+        # token index of each routed row)
+        wgrad_fc1_bytes=E * 2 * F * d * wgrad_bytes + A * 2 * F * eb + A * d * eb + (E + 1) * 4 + (A * 4 if gather else 0),
         gate_flop=6.0 * T * E * d,                 # logits, dWg, dx_r
         # bytes each HBM-bound phase must move at least once, every activation row in the
         # activation dtype (the layer's statement: Y_perm, dX_perm, y, dy, dx as act rows)
         router_bytes=T * E * 4 + T * k * 8 + E * 8,
-        permute_bytes=T * d * eb + A * d * eb + A * 4 * 3,
+        # idx read, row_of and token_of written (+ x read and x_perm written with the copy)
+        permute_bytes=A * 4 * 3 + (0 if gather else T * d * eb + A * d * eb),
         combine_bytes=A * d * eb + (T * d * eb if Fs else 0) + T * d * eb + T * k * 8,
         combine_bwd_bytes=T * d * eb + 2 * A * d * eb + T * k * 12,
         unpermute_reduce_bytes=A * d * eb + T * d * eb + T * k * 4,
@@ -98,8 +102,9 @@ def roofline(alg, ms, peak_tflops, shape, wgrad_name="fp32"):
     t_mfma = flop / (peak_tflops * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
     s = ms * 1e-3
-    common = dict(kernel="routed fc1 weight gradient dW13 = dH^T x_perm (one grouped-GEMM launch, bf16 MFMA, "
-                         f"{wgrad_name} output)", launch_ms=round(ms, 4), flop_per_launch=flop,
+    x_rows = "the token rows of x through token_of" if shape.act == "bf16" else "x_perm"
+    common = dict(kernel=f"routed fc1 weight gradient dW13 = dH^T X, X = {x_rows} (one grouped-GEMM launch, "
+                         f"bf16 MFMA, {wgrad_name} output)", launch_ms=round(ms, 4), flop_per_launch=flop,
                   bytes_per_launch=int(nbytes),
                   mfma_frac=round(flop / s / 1e12 / peak_tflops, 4), hbm_frac=round(nbytes / s / 1e9 / PEAK_HBM_GBPS, 4))
     if t_hbm >= t_mfma:
@@ -229,11 +234,10 @@ def bench_fp8(args, shape, cfg, inp, up, dev) -> int:
         mark()
         L.quantize_fp8(x, 1, xq, xs)
         mark()
-        L.permute_fp8(cfg, xq, xs, S["idx"], S["offsets"], S["row_of"], S["token_of"], S["x_perm"],
-                      S["x_perm_scale"], ws)
+        L.permute_fp8(cfg, None, None, S["idx"], S["offsets"], S["row_of"], S["token_of"], None, None, ws)
         mark()
-        L.grouped_gemm_swiglu_fp8(cfg, S["x_perm"], S["x_perm_scale"], S["offsets"], W13q, W13s.view(-1), W2q,
-                                  W2s.view(-1), None, S["Act"], S["Act_scale"], S["Y_perm"], ws)
+        L.grouped_gemm_swiglu_fp8(cfg, xq, xs, S["offsets"], W13q, W13s.view(-1), W2q, W2s.view(-1), None,
+                                  S["Act"], S["Act_scale"], S["Y_perm"], ws, token_of=S["token_of"])
         mark()
         L.unpermute_combine(cfg, S["Y_perm"], S["row_of"], S["w"], None, y)
         mark()
@@ -266,7 +270,8 @@ def bench_fp8(args, shape, cfg, inp, up, dev) -> int:
         scaling="weak", vs_baseline=None, dtype="fp8-e4m3 experts, bf16 activations",
         data="synthetic (seeded generator, random-init weights)",
         config=dict(workload=shape.name, T=T, d=d, E=E, k=k, F=F, Fs=0, score=shape.score, bias=shape.bias,
-                    passes="forward + router-path backward (frozen fp8 experts)", parallelism="single GPU"),
+                    passes="forward + router-path backward (frozen fp8 experts)",
+                    fc1_rows="token rows' e4m3 codes through token_of (no grouped copy)", parallelism="single GPU"),
         roofline=dict(kernel="grouped fp8 SwiGLU experts forward (fc1 GEMM + Act quantiser + fc2 GEMM)",
                       bound="mfma", achieved=round(tf, 2), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
                       frac=round(tf / PEAK_FP8_TFLOPS, 4), traffic=None, flop_per_step=flop, ms_per_step=round(ms, 4)),
@@ -277,7 +282,7 @@ def bench_fp8(args, shape, cfg, inp, up, dev) -> int:
     return 0
 
 
-def bench_wgrad_f32(args, shape, L, S, dY_perm, dH, dev, phase_ms):
+def bench_wgrad_f32(args, shape, L, S, x, dY_perm, dH, dev, phase_ms):
     """The two routed weight-gradient launches again with fp32 output (the other option of
     the weight-gradient dtype), timed with HIP events on the launch stream, beside the
     step's bf16 ones."""
@@ -289,7 +294,9 @@ def bench_wgrad_f32(args, shape, L, S, dY_perm, dH, dev, phase_ms):
     dW2 = torch.empty(E, d, F, dtype=torch.float32, device=dev)
     runs = max(args.steps // 2, 3)
     res = {}
-    for name, fn in (("wgrad_fc1", lambda: L.grouped_wgrad(c32, S["offsets"], E, A, dH, 2 * F, S["x_perm"], d, dW13)),
+    X, x_rows = (x, S["token_of"]) if "x_perm" not in S else (S["x_perm"], None)
+    for name, fn in (("wgrad_fc1", lambda: L.grouped_wgrad(c32, S["offsets"], E, A, dH, 2 * F, X, d, dW13,
+                                                           x_rows=x_rows)),
                      ("wgrad_fc2", lambda: L.grouped_wgrad(c32, S["offsets"], E, A, dY_perm, d, S["Act"], F, dW2))):
         fn()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(runs + 1)]
@@ -433,7 +440,10 @@ def main() -> int:
               W2=up(inp["W2"]), W13s=up(inp["W13s"]), W2s=up(inp["W2s"]))
     x = up(inp["x"])
     dy = up(W.to_f32(inp["dy"], shape.act))
-    S = L.alloc_saved(cfg, dev)
+    S = L.alloc_saved(cfg, dev)        # bf16: no grouped copy of x, the fc1 GEMMs read it through token_of
+    gather = "x_perm" not in S
+    tok = S["token_of"] if gather else None
+    X1 = x if gather else S["x_perm"]   # the fc1 weight gradient's X
     G = L.alloc_grads(cfg, dev, with_dbg=inp["bg"] is not None)
     ws = L.alloc_workspace(cfg, dev)
     f32, ad = torch.float32, L.act_dtype(cfg)
@@ -467,22 +477,23 @@ def main() -> int:
         mark()
         L.router_topk(cfg, S["logits"], Wt["expert_bias"], S["idx"], S["w"], S["counts"], None, stats, ws)
         mark()
-        L.permute(cfg, x, S["idx"], S["offsets"], S["row_of"], S["token_of"], S["x_perm"], ws)
+        L.permute(cfg, None if gather else x, S["idx"], S["offsets"], S["row_of"], S["token_of"], S.get("x_perm"), ws)
         mark()
-        L.grouped_gemm_swiglu(cfg, S["x_perm"], S["offsets"], Wt["W13"], Wt["W2"], x if Fs else None, Wt["W13s"],
-                              Wt["W2s"], S["H"], S["Act"], S["Y_perm"], S.get("H_s"), S.get("Act_s"), S.get("Y_s"), ws)
+        L.grouped_gemm_swiglu(cfg, S.get("x_perm"), S["offsets"], Wt["W13"], Wt["W2"], x if Fs or gather else None,
+                              Wt["W13s"], Wt["W2s"], S["H"], S["Act"], S["Y_perm"], S.get("H_s"), S.get("Act_s"),
+                              S.get("Y_s"), ws, token_of=tok)
         mark()
         L.unpermute_combine(cfg, S["Y_perm"], S["row_of"], S["w"], S.get("Y_s"), y)
         mark()
         L.unpermute_combine_bwd(cfg, dy, S["Y_perm"], S["row_of"], S["w"], dY_perm, dw, dY_s)
         mark()
-        L.grouped_gemm_swiglu_bwd(cfg, S["x_perm"], S["offsets"], Wt["W13"], Wt["W2"], S["H"], S["Act"], dY_perm,
+        L.grouped_gemm_swiglu_bwd(cfg, S.get("x_perm"), S["offsets"], Wt["W13"], Wt["W2"], S["H"], S["Act"], dY_perm,
                                   dH, dX_perm, None, None, x if Fs else None, Wt["W13s"], Wt["W2s"],
                                   S.get("H_s"), S.get("Act_s"), dY_s, dH_s, dx_s, None, None, ws)
         mark()
         L.grouped_wgrad(cfg, S["offsets"], E, A, dY_perm, d, S["Act"], F, G["dW2"])
         mark()
-        L.grouped_wgrad(cfg, S["offsets"], E, A, dH, 2 * F, S["x_perm"], d, G["dW13"])
+        L.grouped_wgrad(cfg, S["offsets"], E, A, dH, 2 * F, X1, d, G["dW13"], x_rows=tok)
         mark()
         if Fs:
             L.grouped_wgrad(cfg, None, 1, T, dH_s, 2 * Fs, x, d, G["dW13s"], ws=ws)
@@ -566,6 +577,7 @@ def main() -> int:
         data="synthetic (seeded generator, random-init weights)",
         config=dict(workload=shape.name, T=T, d=d, E=E, k=k, F=F, Fs=Fs, score=shape.score,
                     bias=shape.bias, aux_coeff=shape.aux_coeff, wgrad_dtype="bf16" if wbf16 else "f32",
+                    fc1_rows="token rows of x through token_of (no grouped copy)" if gather else "grouped copy x_perm",
                     parallelism="single GPU"),
         roofline=roof,
         grouped_gemm=dict(kernels="every expert projection of fwd + bwd (routed and shared)",
@@ -587,7 +599,7 @@ def main() -> int:
     )
     out["balancing"] = bench_balancing(args, shape, L, S, Wt["expert_bias"], dw, dlogits, dev)
     if wbf16:
-        out["wgrad_f32"] = bench_wgrad_f32(args, shape, L, S, dY_perm, dH, dev, phase_ms)
+        out["wgrad_f32"] = bench_wgrad_f32(args, shape, L, S, x, dY_perm, dH, dev, phase_ms)
     if not args.no_cpu_baseline:
         tokens = args.cpu_tokens or {1: 128, 2: 8192, 3: 48, 4: 1024, 5: 256}[args.config]
         out["cpu_baseline"] = cpu_baseline(shape, inp, min(tokens, T))

@@ -163,14 +163,18 @@ typedef struct moe_saved {
   int32_t* offsets;  /* [E+1] */
   int32_t* row_of;   /* [T, k] */
   int32_t* token_of; /* [A] */
-  void* x_perm;      /* [A, d] */
+  void* x_perm;      /* [A, d], or NULL (bf16 activations): the grouped fc1 and its weight
+                        gradient then read row token_of[r] of x in place of row r, and the
+                        grouped copy is never made */
   void* H;           /* [A, 2F] fp32 */
   void* Act;         /* [A, F] */
   void* Y_perm;      /* [A, d] fp32 */
   void* H_s;         /* [T, 2Fs] fp32, or NULL when Fs == 0 */
   void* Act_s;       /* [T, Fs]  or NULL */
   void* Y_s;         /* [T, d]   fp32, or NULL */
-  float* x_perm_scale; /* fp8 weights only: [A, d/128], the scales of x_perm's e4m3 rows */
+  float* x_perm_scale; /* fp8 weights only: [A, d/128], the scales of x_perm's e4m3 rows
+                          (NULL with x_perm: the fc1 then reads the token rows' codes and
+                          scales, kept in the forward workspace, through token_of) */
   float* Act_scale;    /* fp8 weights only: [A, F/128], the scales of Act's e4m3 rows */
   int32_t* seq_counts; /* [B, E] tokens of sequence b routed to e; needed when seq_aux_coeff > 0 */
   float* gs;           /* [T] the shared expert's gate values, when shared_gate */
@@ -278,7 +282,12 @@ moe_status_t moe_quantile_bias_update(const moe_config_t* cfg, const float* beta
 /* Dropless permutation ([LC] "Read the timeline before blaming the network": tokens are
  * grouped by expert before the expert matmuls): offsets = exclusive prefix of the
  * per-expert counts; row_of[t, j] = row of (t, j); token_of[row] = t;
- * x_perm[row_of[t, j]] = x[t]. */
+ * x_perm[row_of[t, j]] = x[t].  Rows inside an expert follow token order.
+ * x_perm NULL: only the grouping is computed (x may then be NULL too); the grouped GEMMs
+ * take token_of in place of the copy.
+ * idx must hold, for each token, k distinct expert ids in [0, E) (the router's output
+ * does).  Ids outside [0, E) are clamped into it and a repeated id leaves rows of token_of
+ * unwritten: the results are then unspecified, but no access leaves the buffers. */
 moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* idx, int32_t* offsets,
                          int32_t* row_of, int32_t* token_of, void* x_perm, void* ws, size_t ws_bytes,
                          void* stream);
@@ -286,11 +295,15 @@ moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* 
 /* Grouped SwiGLU experts ([HB] §3.4 Count and size, Activation): for each expert e, on its
  * rows [offsets[e], offsets[e+1]):  H = X W13[e]^T, Act = silu(H[:, :F]) * H[:, F:],
  * Y_perm = Act W2[e]^T (fp32).  When Fs > 0 the shared expert runs the same on x (all T
- * rows) into H_s, Act_s, Y_s ([HB] §3.4 Shared experts). */
-moe_status_t moe_grouped_gemm_swiglu(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
-                                     const void* W13, const void* W2, const void* x, const void* W13s,
-                                     const void* W2s, void* H, void* Act, void* Y_perm, void* H_s,
-                                     void* Act_s, void* Y_s, void* ws, size_t ws_bytes, void* stream);
+ * rows) into H_s, Act_s, Y_s ([HB] §3.4 Shared experts).
+ * X is x_perm [A, d] (token_of NULL), or, with token_of [A] given and x_perm NULL, row
+ * token_of[r] of x [T, d] for row r (bf16 activations only): the same products, bit for
+ * bit, without the grouped copy.  Errors: both or neither of x_perm and token_of ->
+ * MOE_ERR_INVALID_ARG; token_of with fp32 activations -> MOE_ERR_UNSUPPORTED. */
+moe_status_t moe_grouped_gemm_swiglu(const moe_config_t* cfg, const void* x_perm, const int32_t* token_of,
+                                     const int32_t* offsets, const void* W13, const void* W2, const void* x,
+                                     const void* W13s, const void* W2s, void* H, void* Act, void* Y_perm,
+                                     void* H_s, void* Act_s, void* Y_s, void* ws, size_t ws_bytes, void* stream);
 
 /* Weighted combine ([LC] "An expert transforms numbers inside the model": the weighted
  * sum of the selected outputs, coordinate by coordinate; [HB] §3.4 Shared experts: the
@@ -316,7 +329,11 @@ moe_status_t moe_shared_gate_bwd(const moe_config_t* cfg, const void* x, const f
  * receives the per-sequence counts when seq_aux_coeff > 0.
  * fp8 experts: x (bf16) is quantised per token per 128 before the permute, the weights
  * are e4m3 codes with weights->W13_scale / W2_scale, and saved->x_perm, saved->Act hold
- * codes with saved->x_perm_scale, saved->Act_scale. */
+ * codes with saved->x_perm_scale, saved->Act_scale.
+ * saved->x_perm NULL (bf16 activations, fp8 weights included): the permute only groups
+ * (offsets, row_of, token_of) and the grouped fc1 reads the token rows of x (or of its
+ * e4m3 codes) through saved->token_of; moe_layer_bwd then does the same for dW13.  The
+ * results are bit-equal to those with the grouped copy. */
 moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* weights, const void* x,
                            const moe_saved_t* saved, float* y, float* stats, void* ws, size_t ws_bytes,
                            void* stream);
@@ -343,13 +360,16 @@ moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const float* dy,
  * consumed before dX_perm is written).  dH [A, 2F] and dH_s [T, 2Fs] (act dtype) are
  * outputs too.  dx_s [T, d] fp32 receives the shared expert's input gradient.
  * dW13 and dW2 may both be NULL (then dW13s and dW2s must be NULL too): only the data
- * gradients are computed, and the weight gradients can follow from moe_grouped_wgrad. */
-moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
-                                         const void* W13, const void* W2, const void* H, const void* Act,
-                                         const void* dY_perm, void* dH, void* dX_perm, void* dW13, void* dW2,
-                                         const void* x, const void* W13s, const void* W2s, const void* H_s,
-                                         const void* Act_s, const void* dY_s, void* dH_s, void* dx_s,
-                                         void* dW13s, void* dW2s, void* ws, size_t ws_bytes, void* stream);
+ * gradients are computed, X is not read, and the weight gradients can follow from
+ * moe_grouped_wgrad.  X (for dW13) is x_perm, or the token rows of x through token_of,
+ * as in moe_grouped_gemm_swiglu. */
+moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_perm, const int32_t* token_of,
+                                         const int32_t* offsets, const void* W13, const void* W2, const void* H,
+                                         const void* Act, const void* dY_perm, void* dH, void* dX_perm, void* dW13,
+                                         void* dW2, const void* x, const void* W13s, const void* W2s,
+                                         const void* H_s, const void* Act_s, const void* dY_s, void* dH_s,
+                                         void* dx_s, void* dW13s, void* dW2s, void* ws, size_t ws_bytes,
+                                         void* stream);
 
 /* Grouped weight gradient (the expert weight gradients of [HB] §3.4's FFN, by the chain
  * rule): for each group g over its rows [offsets[g], offsets[g+1]),
@@ -368,12 +388,19 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
  * moe_grouped_gemm_swiglu_bwd's shared-expert gradients, which split the same way).  The
  * split needs chunks * N * K * 4 bytes of ws (at most 32 N K); the backward workspace of
  * moe_workspace_size covers the shared expert's two calls.  ws NULL: no split.
+ * x_rows (bf16 activations; NULL: none): reduction row r of X is row x_rows[r] of X, which
+ * then has x_src_rows rows [x_src_rows, K] (the routed dW13 straight from the token rows
+ * of x, with x_rows = token_of and x_src_rows = T: bit-equal to the call on x_perm).  An
+ * entry outside [0, x_src_rows) is the caller's error; the reads never leave X.  No split
+ * with x_rows.
  * Errors: groups outside [1, 4096], groups != 1 without offsets, rows outside [0, 2^31),
- * N or K not a positive multiple of 64, accumulate not 0 or 1 -> MOE_ERR_INVALID_ARG; ws
- * given but smaller than a split needs -> MOE_ERR_WORKSPACE. */
+ * N or K not a positive multiple of 64, accumulate not 0 or 1, x_rows with x_src_rows < 1
+ * -> MOE_ERR_INVALID_ARG; x_rows with fp32 activations -> MOE_ERR_UNSUPPORTED; ws given
+ * but smaller than a split needs -> MOE_ERR_WORKSPACE. */
 moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, int32_t groups, int64_t rows,
-                               const void* dY, int32_t N, const void* X, int32_t K, void* dW, int32_t accumulate,
-                               void* ws, size_t ws_bytes, void* stream);
+                               const void* dY, int32_t N, const void* X, int32_t K, const int32_t* x_rows,
+                               int32_t x_src_rows, void* dW, int32_t accumulate, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* ---------------------------------------------------------------- fp8 experts
  * e4m3 block quantiser (the fp8 recipe is a reading: the pages leave low-precision expert
@@ -392,7 +419,8 @@ moe_status_t moe_quantize_fp8(int32_t src_dtype, const void* src, int64_t rows, 
 
 /* moe_permute for e4m3 rows: the same grouping (offsets, row_of, token_of) of x_q [T, d]
  * uint8 codes into x_perm [A, d] uint8, with their scales x_scale [T, d/128] -> x_perm_scale
- * [A, d/128].  Needs cfg->w_dtype == MOE_FP8_E4M3. */
+ * [A, d/128].  Needs cfg->w_dtype == MOE_FP8_E4M3.  x_perm and x_perm_scale both NULL: the
+ * grouping only (x_q, x_scale may be NULL); one of them NULL -> MOE_ERR_INVALID_ARG. */
 moe_status_t moe_permute_fp8(const moe_config_t* cfg, const uint8_t* x_q, const float* x_scale, const int32_t* idx,
                              int32_t* offsets, int32_t* row_of, int32_t* token_of, uint8_t* x_perm,
                              float* x_perm_scale, void* ws, size_t ws_bytes, void* stream);
@@ -402,9 +430,12 @@ moe_status_t moe_permute_fp8(const moe_config_t* cfg, const uint8_t* x_q, const 
  * accumulate on the matrix cores per 128-wide K block, then the two block scales apply);
  * Act = silu(H[:, :F]) * H[:, F:] in fp32, quantised per row per 128 columns by the rule
  * of moe_quantize_fp8 into Act [A, F] uint8 + Act_scale [A, F/128];
- * Y_perm = deq(Act) deq(W2[e])^T (fp32).  H may be NULL (not written). */
+ * Y_perm = deq(Act) deq(W2[e])^T (fp32).  H may be NULL (not written).
+ * token_of [A] (NULL: none): x_perm and x_perm_scale are then the token rows x_q [T, d] and
+ * x_scale [T, d/128], and grouped row r reads token row token_of[r] (no grouped copy). */
 moe_status_t moe_grouped_gemm_swiglu_fp8(const moe_config_t* cfg, const uint8_t* x_perm, const float* x_perm_scale,
-                                         const int32_t* offsets, const uint8_t* W13, const float* W13_scale,
+                                         const int32_t* token_of, const int32_t* offsets, const uint8_t* W13,
+                                         const float* W13_scale,
                                          const uint8_t* W2, const float* W2_scale, float* H, uint8_t* Act,
                                          float* Act_scale, float* Y_perm, void* ws, size_t ws_bytes, void* stream);
 

@@ -243,6 +243,8 @@ def quantile_bias_update(cfg, beta_local, ema, beta, stream=None):
 
 
 def permute(cfg, x, idx, offsets, row_of, token_of, x_perm, ws, stream=None):
+    """The grouping (offsets, row_of, token_of) and, when x_perm is given, the grouped copy
+    of x; x_perm None: the grouping only (x may be None too)."""
     ad, TK = act_dtype(cfg), cfg.T * cfg.k
     wp, wn = _ws(ws)
     _check(load().moe_permute(ctypes.byref(cfg), _P(_ptr(x, ad, cfg.T * cfg.d, "x")),
@@ -253,11 +255,13 @@ def permute(cfg, x, idx, offsets, row_of, token_of, x_perm, ws, stream=None):
 
 
 def grouped_gemm_swiglu(cfg, x_perm, offsets, W13, W2, x, W13s, W2s, H, Act, Y_perm, H_s, Act_s, Y_s, ws,
-                        stream=None):
+                        stream=None, token_of=None):
+    """token_of given (x_perm None): the routed fc1 reads row token_of[r] of x."""
     ad, A, T, d, E, F, Fs = act_dtype(cfg), cfg.T * cfg.k, cfg.T, cfg.d, cfg.E, cfg.F, cfg.Fs
     wp, wn = _ws(ws)
     _check(load().moe_grouped_gemm_swiglu(
-        ctypes.byref(cfg), _P(_ptr(x_perm, ad, A * d, "x_perm")), _P(_ptr(offsets, torch.int32, E + 1, "offsets")),
+        ctypes.byref(cfg), _P(_ptr(x_perm, ad, A * d, "x_perm")), _P(_ptr(token_of, torch.int32, A, "token_of")),
+        _P(_ptr(offsets, torch.int32, E + 1, "offsets")),
         _P(_ptr(W13, ad, E * 2 * F * d, "W13")), _P(_ptr(W2, ad, E * d * F, "W2")),
         _P(_ptr(x, ad, T * d, "x")), _P(_ptr(W13s, ad, 2 * Fs * d, "W13s")), _P(_ptr(W2s, ad, d * Fs, "W2s")),
         _P(_ptr(H, torch.float32, A * 2 * F, "H")), _P(_ptr(Act, ad, A * F, "Act")),
@@ -304,11 +308,13 @@ def unpermute_combine_bwd(cfg, dy, Y_perm, row_of, w, dY_perm, dw, dY_s=None, st
 
 
 def grouped_gemm_swiglu_bwd(cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, dX_perm, dW13, dW2, x, W13s, W2s,
-                            H_s, Act_s, dY_s, dH_s, dx_s, dW13s, dW2s, ws, stream=None):
+                            H_s, Act_s, dY_s, dH_s, dx_s, dW13s, dW2s, ws, stream=None, token_of=None):
+    """token_of given (x_perm None): the routed dW13 reads row token_of[r] of x."""
     ad, A, T, d, E, F, Fs = act_dtype(cfg), cfg.T * cfg.k, cfg.T, cfg.d, cfg.E, cfg.F, cfg.Fs
     wp, wn = _ws(ws)
     _check(load().moe_grouped_gemm_swiglu_bwd(
-        ctypes.byref(cfg), _P(_ptr(x_perm, ad, A * d, "x_perm")), _P(_ptr(offsets, torch.int32, E + 1, "offsets")),
+        ctypes.byref(cfg), _P(_ptr(x_perm, ad, A * d, "x_perm")), _P(_ptr(token_of, torch.int32, A, "token_of")),
+        _P(_ptr(offsets, torch.int32, E + 1, "offsets")),
         _P(_ptr(W13, ad, E * 2 * F * d, "W13")), _P(_ptr(W2, ad, E * d * F, "W2")),
         _P(_ptr(H, torch.float32, A * 2 * F, "H")),
         _P(_ptr(Act, ad, A * F, "Act")), _P(_ptr(dY_perm, ad, A * d, "dY_perm")), _P(_ptr(dH, ad, A * 2 * F, "dH")),
@@ -324,17 +330,22 @@ def grouped_gemm_swiglu_bwd(cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, 
         _P(_stream(stream))))
 
 
-def grouped_wgrad(cfg, offsets, groups, rows, dY, N, X, K, dW, stream=None, accumulate=False, ws=None):
+def grouped_wgrad(cfg, offsets, groups, rows, dY, N, X, K, dW, stream=None, accumulate=False, ws=None, x_rows=None):
     """dW[g] = dY_g^T X_g per group of rows (offsets None: one group of `rows` rows);
-    accumulate: dW[g] += dY_g^T X_g; ws: scratch that lets a one-group call split its rows."""
+    accumulate: dW[g] += dY_g^T X_g; ws: scratch that lets a one-group call split its rows;
+    x_rows [rows] int32: reduction row r of X is row x_rows[r] of X (X then has any number
+    of rows)."""
     wp, wn = _ws(ws) if ws is not None else (None, 0)
     ad = act_dtype(cfg)
     if offsets is not None and offsets.numel() != groups + 1:
         raise ValueError(f"offsets: expected {groups + 1} entries, got {offsets.numel()}")
+    x_src = X.numel() // K if x_rows is not None else 0
     _check(load().moe_grouped_wgrad(
         ctypes.byref(cfg), _P(_ptr(offsets, torch.int32, groups + 1, "offsets")), ctypes.c_int32(groups),
-        ctypes.c_int64(rows), _P(_ptr(dY, ad, rows * N, "dY")), ctypes.c_int32(N), _P(_ptr(X, ad, rows * K, "X")),
-        ctypes.c_int32(K), _P(_ptr(dW, wgrad_dtype(cfg), groups * N * K, "dW")), ctypes.c_int32(int(accumulate)),
+        ctypes.c_int64(rows), _P(_ptr(dY, ad, rows * N, "dY")), ctypes.c_int32(N),
+        _P(_ptr(X, ad, (x_src if x_rows is not None else rows) * K, "X")), ctypes.c_int32(K),
+        _P(_ptr(x_rows, torch.int32, rows, "x_rows")), ctypes.c_int32(x_src),
+        _P(_ptr(dW, wgrad_dtype(cfg), groups * N * K, "dW")), ctypes.c_int32(int(accumulate)),
         _P(wp), ctypes.c_size_t(wn), _P(_stream(stream))))
 
 
@@ -352,6 +363,7 @@ def quantize_fp8(src, block_rows, q, scale, stream=None):
 
 
 def permute_fp8(cfg, x_q, x_scale, idx, offsets, row_of, token_of, x_perm, x_perm_scale, ws, stream=None):
+    """x_perm and x_perm_scale None: the grouping only."""
     A, T, d, E = cfg.T * cfg.k, cfg.T, cfg.d, cfg.E
     wp, wn = _ws(ws)
     _check(load().moe_permute_fp8(
@@ -363,13 +375,16 @@ def permute_fp8(cfg, x_q, x_scale, idx, offsets, row_of, token_of, x_perm, x_per
 
 
 def grouped_gemm_swiglu_fp8(cfg, x_perm, x_perm_scale, offsets, W13, W13_scale, W2, W2_scale, H, Act, Act_scale,
-                            Y_perm, ws, stream=None):
+                            Y_perm, ws, stream=None, token_of=None):
+    """token_of given: x_perm, x_perm_scale are the token rows x_q [T, d], x_scale [T, d/128],
+    read through token_of."""
     A, d, E, F = cfg.T * cfg.k, cfg.d, cfg.E, cfg.F
+    R = cfg.T if token_of is not None else A
     wp, wn = _ws(ws)
     u8, f32 = torch.uint8, torch.float32
     _check(load().moe_grouped_gemm_swiglu_fp8(
-        ctypes.byref(cfg), _P(_ptr(x_perm, u8, A * d, "x_perm")), _P(_ptr(x_perm_scale, f32, A * (d // 128), "x_perm_scale")),
-        _P(_ptr(offsets, torch.int32, E + 1, "offsets")), _P(_ptr(W13, u8, E * 2 * F * d, "W13")),
+        ctypes.byref(cfg), _P(_ptr(x_perm, u8, R * d, "x_perm")), _P(_ptr(x_perm_scale, f32, R * (d // 128), "x_perm_scale")),
+        _P(_ptr(token_of, torch.int32, A, "token_of")), _P(_ptr(offsets, torch.int32, E + 1, "offsets")), _P(_ptr(W13, u8, E * 2 * F * d, "W13")),
         _P(_ptr(W13_scale, f32, E * (2 * F // 128) * (d // 128), "W13_scale")), _P(_ptr(W2, u8, E * d * F, "W2")),
         _P(_ptr(W2_scale, f32, E * (d // 128) * (F // 128), "W2_scale")), _P(_ptr(H, f32, A * 2 * F, "H")),
         _P(_ptr(Act, u8, A * F, "Act")), _P(_ptr(Act_scale, f32, A * (F // 128), "Act_scale")),
@@ -465,16 +480,24 @@ def layer_bwd(cfg, W, S, x, dy, daux, dx, G, ws, stream=None, accumulate=False, 
 
 # ----------------------------------------------------------------- buffer helpers
 
-def alloc_saved(cfg: Config, device="cuda") -> Dict[str, torch.Tensor]:
+def alloc_saved(cfg: Config, device="cuda", x_perm=None) -> Dict[str, torch.Tensor]:
+    """Buffers of moe_saved_t.  x_perm: keep the grouped copy of x (default: only with fp32
+    activations; bf16 layers read the token rows of x through token_of instead)."""
     ad, T, d, E, F, Fs, A = act_dtype(cfg), cfg.T, cfg.d, cfg.E, cfg.F, cfg.Fs, cfg.T * cfg.k
     e = lambda *s, dt=ad: torch.empty(*s, dtype=dt, device=device)  # noqa: E731
     qd = torch.uint8 if is_fp8(cfg) else ad
+    if x_perm is None:
+        x_perm = ad != torch.bfloat16
     S = dict(logits=e(T, E, dt=torch.float32), idx=e(T, cfg.k, dt=torch.int32), w=e(T, cfg.k, dt=torch.float32),
              counts=e(E, dt=torch.int32), offsets=e(E + 1, dt=torch.int32), row_of=e(T, cfg.k, dt=torch.int32),
-             token_of=e(A, dt=torch.int32), x_perm=e(A, d, dt=qd), H=e(A, 2 * F, dt=torch.float32),
+             token_of=e(A, dt=torch.int32), H=e(A, 2 * F, dt=torch.float32),
              Act=e(A, F, dt=qd), Y_perm=e(A, d, dt=torch.float32))
+    if x_perm:
+        S["x_perm"] = e(A, d, dt=qd)
     if is_fp8(cfg):
-        S.update(x_perm_scale=e(A, d // 128, dt=torch.float32), Act_scale=e(A, F // 128, dt=torch.float32))
+        S["Act_scale"] = e(A, F // 128, dt=torch.float32)
+        if x_perm:
+            S["x_perm_scale"] = e(A, d // 128, dt=torch.float32)
     if Fs:
         S.update(H_s=e(T, 2 * Fs, dt=torch.float32), Act_s=e(T, Fs), Y_s=e(T, d, dt=torch.float32))
     if num_sequences(cfg):

@@ -308,6 +308,19 @@ moe_status_t fork(hipStream_t from, hipEvent_t ev, hipStream_t waiter) {
   return MOE_OK;
 }
 
+// The routed fc1 operand: the grouped rows x_perm, or (token_of given, x_perm NULL) the
+// token rows of x read through token_of, bf16 only.
+moe_status_t check_rows_source(const moe_config_t& c, const void* x_perm, const int32_t* token_of, const void* x) {
+  if (!token_of) {
+    MOE_NEED16(x_perm);
+    return MOE_OK;
+  }
+  if (x_perm) return fail(MOE_ERR_INVALID_ARG, "give x_perm or token_of, not both");
+  if (c.act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the token_of row gather needs bf16 activations");
+  MOE_NEED16(x);
+  return MOE_OK;
+}
+
 // ----------------------------------------------------------------- launch sequences
 moe_status_t run_gate(const moe_config_t& c, const void* x, const float* Wg, const float* bg, float* logits,
                       void* gate_ws, hipStream_t s) {
@@ -321,9 +334,11 @@ moe_status_t run_gate(const moe_config_t& c, const void* x, const float* Wg, con
   return launch_gemm_fma(g, s);
 }
 
-moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const int32_t* offsets, const void* W13,
-                             const void* W2, const void* x, const void* W13s, const void* W2s, void* H, void* Act,
-                             void* Y_perm, void* H_s, void* Act_s, void* Y_s, int32_t* sched, hipStream_t s) {
+// x_perm NULL: the routed fc1 reads the token rows of x through token_of (bf16 only).
+moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const int32_t* token_of,
+                             const int32_t* offsets, const void* W13, const void* W2, const void* x, const void* W13s,
+                             const void* W2s, void* H, void* Act, void* Y_perm, void* H_s, void* Act_s, void* Y_s,
+                             int32_t* sched, hipStream_t s) {
   const int64_t A = static_cast<int64_t>(c.T) * c.k;
   for (int shared = 0; shared < (c.Fs ? 2 : 1); ++shared) {
     const int F = shared ? c.Fs : c.F;
@@ -340,7 +355,13 @@ moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const in
     g1.C = h; g1.ldc = 2 * F; g1.C2 = act; g1.ldc2 = F;
     g1.offsets = shared ? nullptr : offsets; g1.G = shared ? 1 : c.E; g1.range_end = c.T; g1.rows_upper = A;
     g1.glu = glu_of(c);
+    if (!shared && !x_perm) {
+      g1.A = x;
+      g1.gather = token_of;
+      g1.gather_rows = c.T;
+    }
     GemmDesc g2 = g1;
+    g2.gather = nullptr;
     g2.c_type = MOE_F32;  // expert outputs are kept in fp32 for the combine
     g2.N = c.d; g2.K = F; g2.A = act; g2.lda = F;
     g2.B = shared ? W2s : W2; g2.ldb = F; g2.b_gstride = shared ? 0 : int64_t{1} * c.d * F;
@@ -365,8 +386,10 @@ moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const in
 // output in the weight-gradient dtype.  A one-group bf16 call with split_ws (at least
 // wgrad_split_bytes(N, K, rows)) is split over its rows when its output has too few tiles:
 // fp32 partials per row chunk, then their sum in chunk order.
+// x_rows (bf16 only): reduction row r of X is row x_rows[r] of X, which has x_src_rows rows.
 moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G, int64_t rows, const void* dY, int N,
-                       const void* X, int K, void* dW, hipStream_t s, int beta, float* split_ws = nullptr) {
+                       const void* X, int K, void* dW, hipStream_t s, int beta, float* split_ws = nullptr,
+                       const int32_t* x_rows = nullptr, int x_src_rows = 0) {
   GemmDesc w{};
   w.a_major = MN_MAJOR; w.b_major = MN_MAJOR; w.ragged = RAGGED_K; w.epi = EPI_STORE;
   w.a_type = w.b_type = act_dtype;
@@ -376,6 +399,12 @@ moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G
   w.C = dW; w.ldc = K; w.c_gstride = int64_t{1} * N * K;
   w.offsets = off; w.G = G; w.range_end = static_cast<int>(rows);
   w.beta = beta;
+  if (x_rows) {
+    if (act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "gathered weight gradients need bf16 activations");
+    w.gather = x_rows;
+    w.gather_rows = x_src_rows;
+    return launch_gemm_mfma(w, nullptr, s);
+  }
   if (act_dtype == MOE_BF16 && !off && split_ws) {
     const WgradSplit sp = wgrad_split(N, K, rows);
     if (sp.chunks > 1) {
@@ -388,13 +417,14 @@ moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G
 }
 
 // fp8 experts: fc1 (+ SwiGLU -> act32, H), Act quantised per row per 128, fc2 -> Y_perm.
+// token_of (or NULL): x_perm and xps are the token rows [T, ...], read through token_of.
 moe_status_t run_experts_fp8(const moe_config_t& c, const uint8_t* x_perm, const float* xps, const int32_t* offsets,
                              const uint8_t* W13, const float* W13_scale, const uint8_t* W2, const float* W2_scale,
                              float* H, uint8_t* Act, float* Act_scale, float* Y_perm, float* act32, int32_t* sched,
-                             hipStream_t s) {
+                             hipStream_t s, const int32_t* token_of = nullptr) {
   const int64_t A = static_cast<int64_t>(c.T) * c.k;
   MOE_TRY(launch_gemm_fp8(true, x_perm, xps, W13, W13_scale, act32, H, offsets, c.E, A, 2 * c.F, c.d, c.F, sched, s,
-                          glu_of(c)));
+                          glu_of(c), token_of, c.T));
   MOE_TRY(launch_quantize_fp8(MOE_F32, act32, A, c.F, 1, Act, Act_scale, s));
   return launch_gemm_fp8(false, Act, Act_scale, W2, W2_scale, Y_perm, nullptr, offsets, c.E, A, c.d, c.F, c.F, sched,
                          s);
@@ -405,7 +435,9 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
                              void* dX_perm, void* dW13, void* dW2, const void* x, const void* W13s, const void* W2s,
                              const void* H_s, const void* Act_s, const void* dY_s, void* dH_s, void* dx_s,
                              void* dW13s, void* dW2s, int32_t* sched, float* dact, float* wsplit, hipStream_t s,
-                             hipStream_t s2 = nullptr, hipEvent_t ev_dh = nullptr, int beta = 0) {
+                             hipStream_t s2 = nullptr, hipEvent_t ev_dh = nullptr, int beta = 0,
+                             const int32_t* token_of = nullptr) {
+  // x_perm NULL: the routed fc1 weight gradient reads the token rows of x through token_of
   // s2 (when given, with dY_perm and dX_perm distinct) runs the weight gradients; its
   // caller has made it wait for dY_perm and joins it back.
   if (!s2) s2 = s;
@@ -462,7 +494,10 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
     MOE_TRY(fork(s, ev_dh, s2));  // dH ready for the fc1 weight gradient
     MOE_TRY(et == MOE_BF16 ? launch_gemm_mfma(d1, sched, s) : launch_gemm_fma(d1, s));
     // (4) fc1 weight gradient dW13 = dH^T X
-    if (dw13) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dh, 2 * F, X, c.d, dw13, s2, beta, sw));
+    const bool gathered = !shared && !x_perm;
+    if (dw13)
+      MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dh, 2 * F, gathered ? x : X, c.d, dw13, s2, beta, sw,
+                        gathered ? token_of : nullptr, c.T));
   }
   return MOE_OK;
 }
@@ -627,28 +662,29 @@ moe_status_t moe_quantile_bias_update(const moe_config_t* cfg, const float* beta
 moe_status_t moe_permute(const moe_config_t* cfg, const void* x, const int32_t* idx, int32_t* offsets,
                          int32_t* row_of, int32_t* token_of, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate(cfg));
-  MOE_NEED16(x); MOE_NEED(idx); MOE_NEED(offsets); MOE_NEED(row_of); MOE_NEED(token_of); MOE_NEED16(x_perm);
-  MOE_NEED(ws);
+  MOE_NEED(idx); MOE_NEED(offsets); MOE_NEED(row_of); MOE_NEED(token_of); MOE_NEED(ws);
+  if (x_perm) { MOE_NEED16(x); MOE_NEED16(x_perm); }   // NULL x_perm: the grouping only
   const FwdWs fw = carve_fwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
   return launch_permute(*cfg, x, idx, offsets, row_of, token_of, x_perm, fw.cnt_part, fw.blk_base, fw.counts,
                         false, S(stream));
 }
 
-moe_status_t moe_grouped_gemm_swiglu(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
-                                     const void* W13, const void* W2, const void* x, const void* W13s,
-                                     const void* W2s, void* H, void* Act, void* Y_perm, void* H_s, void* Act_s,
-                                     void* Y_s, void* ws, size_t ws_bytes, void* stream) {
+moe_status_t moe_grouped_gemm_swiglu(const moe_config_t* cfg, const void* x_perm, const int32_t* token_of,
+                                     const int32_t* offsets, const void* W13, const void* W2, const void* x,
+                                     const void* W13s, const void* W2s, void* H, void* Act, void* Y_perm, void* H_s,
+                                     void* Act_s, void* Y_s, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate(cfg));
-  MOE_NEED16(x_perm); MOE_NEED(offsets); MOE_NEED16(W13); MOE_NEED16(W2); MOE_NEED16(H); MOE_NEED16(Act);
+  MOE_TRY(check_rows_source(*cfg, x_perm, token_of, x));
+  MOE_NEED(offsets); MOE_NEED16(W13); MOE_NEED16(W2); MOE_NEED16(H); MOE_NEED16(Act);
   MOE_NEED16(Y_perm); MOE_NEED(ws);
   if (cfg->Fs) {
     MOE_NEED16(x); MOE_NEED16(W13s); MOE_NEED16(W2s); MOE_NEED16(H_s); MOE_NEED16(Act_s); MOE_NEED16(Y_s);
   }
   const FwdWs fw = carve_fwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
-  return run_experts_fwd(*cfg, x_perm, offsets, W13, W2, x, W13s, W2s, H, Act, Y_perm, H_s, Act_s, Y_s, fw.sched,
-                         S(stream));
+  return run_experts_fwd(*cfg, x_perm, token_of, offsets, W13, W2, x, W13s, W2s, H, Act, Y_perm, H_s, Act_s, Y_s,
+                         fw.sched, S(stream));
 }
 
 moe_status_t moe_unpermute_combine(const moe_config_t* cfg, const float* Y_perm, const int32_t* row_of,
@@ -683,11 +719,17 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_NEED(W); MOE_NEED(sv); MOE_NEED16(x); MOE_NEED16(y); MOE_NEED(ws);
   MOE_NEED(W->Wg); MOE_NEED16(W->W13); MOE_NEED16(W->W2);
   MOE_NEED(sv->logits); MOE_NEED(sv->idx); MOE_NEED(sv->w); MOE_NEED(sv->counts); MOE_NEED(sv->offsets);
-  MOE_NEED(sv->row_of); MOE_NEED(sv->token_of); MOE_NEED16(sv->x_perm); MOE_NEED16(sv->Act);
+  MOE_NEED(sv->row_of); MOE_NEED(sv->token_of); MOE_NEED16(sv->Act);
   MOE_NEED16(sv->Y_perm);
+  // saved->x_perm NULL: the grouped fc1 reads the token rows of x through token_of
+  const bool gathered = sv->x_perm == nullptr;
+  if (gathered && cfg->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "saved->x_perm is needed with fp32 activations (the row gather is bf16 only)");
+  if (!gathered) MOE_NEED16(sv->x_perm);
   const bool fp8 = cfg->w_dtype == MOE_FP8_E4M3;
   if (fp8) {
-    MOE_NEED(W->W13_scale); MOE_NEED(W->W2_scale); MOE_NEED(sv->x_perm_scale); MOE_NEED(sv->Act_scale);
+    MOE_NEED(W->W13_scale); MOE_NEED(W->W2_scale); MOE_NEED(sv->Act_scale);
+    if (!gathered) MOE_NEED(sv->x_perm_scale);
     if (sv->H && !aligned16(sv->H)) return fail(MOE_ERR_INVALID_ARG, "H is not 16-byte aligned");
   } else {
     MOE_NEED16(sv->H);
@@ -713,18 +755,20 @@ moe_status_t moe_layer_fwd(const moe_config_t* cfg, const moe_weights_t* W, cons
     MOE_TRY(launch_quantize_fp8(MOE_BF16, x, c.T, c.d, 1, fw.xq, fw.xs, s));
     MOE_TRY(launch_permute(c, fw.xq, sv->idx, sv->offsets, sv->row_of, sv->token_of, sv->x_perm, fw.cnt_part,
                            fw.blk_base, fw.counts, true, s, 1));
-    MOE_TRY(launch_gather_scales(fw.xs, sv->token_of, A, c.d / 128, sv->x_perm_scale, s));
-    MOE_TRY(run_experts_fp8(c, static_cast<const uint8_t*>(sv->x_perm), sv->x_perm_scale, sv->offsets,
+    if (!gathered) MOE_TRY(launch_gather_scales(fw.xs, sv->token_of, A, c.d / 128, sv->x_perm_scale, s));
+    MOE_TRY(run_experts_fp8(c, gathered ? fw.xq : static_cast<const uint8_t*>(sv->x_perm),
+                            gathered ? fw.xs : sv->x_perm_scale, sv->offsets,
                             static_cast<const uint8_t*>(W->W13), W->W13_scale, static_cast<const uint8_t*>(W->W2),
                             W->W2_scale, static_cast<float*>(sv->H), static_cast<uint8_t*>(sv->Act), sv->Act_scale,
-                            static_cast<float*>(sv->Y_perm), fw.act32, fw.sched, s));
+                            static_cast<float*>(sv->Y_perm), fw.act32, fw.sched, s,
+                            gathered ? sv->token_of : nullptr));
     return launch_combine(c, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w, nullptr, nullptr,
                           static_cast<float*>(y), s);
   }
   MOE_TRY(launch_permute(c, x, sv->idx, sv->offsets, sv->row_of, sv->token_of, sv->x_perm, fw.cnt_part, fw.blk_base,
                          fw.counts, true, s));
-  MOE_TRY(run_experts_fwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, x, W->W13s, W->W2s, sv->H, sv->Act,
-                          sv->Y_perm, sv->H_s, sv->Act_s, sv->Y_s, fw.sched, s));
+  MOE_TRY(run_experts_fwd(c, sv->x_perm, sv->token_of, sv->offsets, W->W13, W->W2, x, W->W13s, W->W2s, sv->H,
+                          sv->Act, sv->Y_perm, sv->H_s, sv->Act_s, sv->Y_s, fw.sched, s));
   return launch_combine(c, static_cast<const float*>(sv->Y_perm), sv->row_of, sv->w,
                         c.Fs ? static_cast<const float*>(sv->Y_s) : nullptr, c.shared_gate ? sv->gs : nullptr,
                         static_cast<float*>(y), s);
@@ -743,16 +787,18 @@ moe_status_t moe_unpermute_combine_bwd(const moe_config_t* cfg, const float* dy,
   return launch_combine_bwd(*cfg, dy, Y_perm, row_of, w, dY_perm, dw, dY_s, gs, Y_s, dl_s, S(stream));
 }
 
-moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_perm, const int32_t* offsets,
-                                         const void* W13, const void* W2, const void* H, const void* Act,
-                                         const void* dY_perm, void* dH, void* dX_perm, void* dW13, void* dW2,
-                                         const void* x, const void* W13s, const void* W2s, const void* H_s,
-                                         const void* Act_s, const void* dY_s, void* dH_s, void* dx_s, void* dW13s,
-                                         void* dW2s, void* ws, size_t ws_bytes, void* stream) {
+moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_perm, const int32_t* token_of,
+                                         const int32_t* offsets, const void* W13, const void* W2, const void* H,
+                                         const void* Act, const void* dY_perm, void* dH, void* dX_perm, void* dW13,
+                                         void* dW2, const void* x, const void* W13s, const void* W2s,
+                                         const void* H_s, const void* Act_s, const void* dY_s, void* dH_s,
+                                         void* dx_s, void* dW13s, void* dW2s, void* ws, size_t ws_bytes,
+                                         void* stream) {
   MOE_TRY(validate(cfg));
-  MOE_NEED16(x_perm); MOE_NEED(offsets); MOE_NEED16(W13); MOE_NEED16(W2); MOE_NEED16(H); MOE_NEED16(Act);
+  MOE_NEED(offsets); MOE_NEED16(W13); MOE_NEED16(W2); MOE_NEED16(H); MOE_NEED16(Act);
   MOE_NEED16(dY_perm); MOE_NEED16(dH); MOE_NEED16(dX_perm); MOE_NEED(ws);
   const bool wgrad = dW13 || dW2;
+  if (wgrad) MOE_TRY(check_rows_source(*cfg, x_perm, token_of, x));
   if (wgrad) { MOE_NEED16(dW13); MOE_NEED16(dW2); }
   if (cfg->Fs) {
     MOE_NEED16(x); MOE_NEED16(W13s); MOE_NEED16(W2s); MOE_NEED16(H_s); MOE_NEED16(Act_s); MOE_NEED16(dY_s);
@@ -763,12 +809,14 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
   const BwdWs bw = carve_bwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, bw.bytes, __func__));
   return run_experts_bwd(*cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, dX_perm, dW13, dW2, x, W13s, W2s, H_s,
-                         Act_s, dY_s, dH_s, dx_s, dW13s, dW2s, bw.sched, bw.dact, bw.wsplit, S(stream));
+                         Act_s, dY_s, dH_s, dx_s, dW13s, dW2s, bw.sched, bw.dact, bw.wsplit, S(stream), nullptr,
+                         nullptr, 0, token_of);
 }
 
 moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, int32_t groups, int64_t rows,
-                               const void* dY, int32_t N, const void* X, int32_t K, void* dW, int32_t accumulate,
-                               void* ws, size_t ws_bytes, void* stream) {
+                               const void* dY, int32_t N, const void* X, int32_t K, const int32_t* x_rows,
+                               int32_t x_src_rows, void* dW, int32_t accumulate, void* ws, size_t ws_bytes,
+                               void* stream) {
   MOE_TRY(validate(cfg));
   MOE_NEED16(dY); MOE_NEED16(X); MOE_NEED16(dW);
   if (groups < 1 || groups > 4096) return fail(MOE_ERR_INVALID_ARG, "groups must be in [1, 4096]");
@@ -777,6 +825,13 @@ moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, 
   if (N < 64 || K < 64 || N % 64 || K % 64) return fail(MOE_ERR_INVALID_ARG, "N and K must be positive multiples of 64");
   if (static_cast<int64_t>(N) * K * 4 >= (int64_t{1} << 40)) return fail(MOE_ERR_INVALID_ARG, "dW group too large");
   if (accumulate != 0 && accumulate != 1) return fail(MOE_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  if (x_rows) {
+    if (cfg->act_dtype != MOE_BF16)
+      return fail(MOE_ERR_UNSUPPORTED, "x_rows (the row gather of X) needs bf16 activations");
+    if (x_src_rows < 1) return fail(MOE_ERR_INVALID_ARG, "x_src_rows must be >= 1 with x_rows");
+    return run_wgrad(cfg->act_dtype, cfg->wgrad_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream), accumulate,
+                     nullptr, x_rows, x_src_rows);
+  }
   float* split = nullptr;
   if (ws && !offsets && cfg->act_dtype == MOE_BF16) {
     const size_t need = wgrad_split_bytes(N, K, rows);
@@ -806,19 +861,23 @@ moe_status_t moe_permute_fp8(const moe_config_t* cfg, const uint8_t* x_q, const 
                              float* x_perm_scale, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate(cfg));
   if (cfg->w_dtype != MOE_FP8_E4M3) return fail(MOE_ERR_INVALID_ARG, "moe_permute_fp8 needs w_dtype fp8");
-  MOE_NEED16(x_q); MOE_NEED(x_scale); MOE_NEED(idx); MOE_NEED(offsets); MOE_NEED(row_of); MOE_NEED(token_of);
-  MOE_NEED16(x_perm); MOE_NEED(x_perm_scale); MOE_NEED(ws);
+  MOE_NEED(idx); MOE_NEED(offsets); MOE_NEED(row_of); MOE_NEED(token_of); MOE_NEED(ws);
+  if ((x_perm != nullptr) != (x_perm_scale != nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "x_perm and x_perm_scale go together (both NULL: the grouping only)");
+  if (x_perm) { MOE_NEED16(x_q); MOE_NEED(x_scale); MOE_NEED16(x_perm); }
   const FwdWs fw = carve_fwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
   hipStream_t s = S(stream);
   MOE_TRY(launch_permute(*cfg, x_q, idx, offsets, row_of, token_of, x_perm, fw.cnt_part, fw.blk_base, fw.counts,
                          false, s, 1));
+  if (!x_perm) return MOE_OK;
   return launch_gather_scales(x_scale, token_of, static_cast<int64_t>(cfg->T) * cfg->k, cfg->d / 128, x_perm_scale,
                               s);
 }
 
 moe_status_t moe_grouped_gemm_swiglu_fp8(const moe_config_t* cfg, const uint8_t* x_perm, const float* x_perm_scale,
-                                         const int32_t* offsets, const uint8_t* W13, const float* W13_scale,
+                                         const int32_t* token_of, const int32_t* offsets, const uint8_t* W13,
+                                         const float* W13_scale,
                                          const uint8_t* W2, const float* W2_scale, float* H, uint8_t* Act,
                                          float* Act_scale, float* Y_perm, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(validate(cfg));
@@ -829,7 +888,7 @@ moe_status_t moe_grouped_gemm_swiglu_fp8(const moe_config_t* cfg, const uint8_t*
   const FwdWs fw = carve_fwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, fw.bytes, __func__));
   return run_experts_fp8(*cfg, x_perm, x_perm_scale, offsets, W13, W13_scale, W2, W2_scale, H, Act, Act_scale, Y_perm,
-                         fw.act32, fw.sched, S(stream));
+                         fw.act32, fw.sched, S(stream), token_of);
 }
 
 moe_status_t moe_permute_bwd(const moe_config_t* cfg, const float* dX_perm, const int32_t* row_of, const float* dx_s,
@@ -888,7 +947,14 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
     MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, sv->seq_counts, daux, bw.dlogits, s));
     return run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, dx, bw.gate, s, beta);
   }
-  MOE_NEED16(sv->x_perm); MOE_NEED16(sv->H); MOE_NEED16(sv->Act); MOE_NEED16(gr->dW13); MOE_NEED16(gr->dW2);
+  if (sv->x_perm) {
+    MOE_NEED16(sv->x_perm);
+  } else {   // the fc1 weight gradient reads the token rows of x through token_of
+    if (cfg->act_dtype != MOE_BF16)
+      return fail(MOE_ERR_INVALID_ARG, "saved->x_perm is needed with fp32 activations (the row gather is bf16 only)");
+    MOE_NEED(sv->token_of);
+  }
+  MOE_NEED16(sv->H); MOE_NEED16(sv->Act); MOE_NEED16(gr->dW13); MOE_NEED16(gr->dW2);
   if (cfg->Fs) {
     MOE_NEED16(W->W13s); MOE_NEED16(W->W2s); MOE_NEED16(sv->H_s); MOE_NEED16(sv->Act_s);
     MOE_NEED16(gr->dW13s); MOE_NEED16(gr->dW2s);
@@ -913,7 +979,7 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_TRY(fork(s, ev.dy, s2));
   MOE_TRY(run_experts_bwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, sv->H, sv->Act, bw.dY, bw.dH, bw.dX, gr->dW13,
                           gr->dW2, x, W->W13s, W->W2s, sv->H_s, sv->Act_s, dY_s, bw.dH_s, bw.dx_s, gr->dW13s,
-                          gr->dW2s, bw.sched, bw.dact, bw.wsplit, s, s2, ev.dh, beta));
+                          gr->dW2s, bw.sched, bw.dact, bw.wsplit, s, s2, ev.dh, beta, sv->token_of));
   MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, sv->seq_counts, daux, bw.dlogits, s));
   MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, bw.gate, s, beta));
   if (c.shared_gate) MOE_TRY(launch_shared_gate_bwd(c, x, bw.dl_s, gr->dWsg, bw.sg_part, s, beta));

@@ -168,7 +168,12 @@ struct Fp8Args {
   const int32_t* tile_prefix;
   int G, N, K, F, nN;
   Glu glu;                // SWIGLU: the gated activation
+  const int32_t* gather;  // GATHER: row r of A (and of A_scale) is row gather[r] of the given ones
+  int gather_rows;        // rows of the gathered A
+  int gather_len;         // entries of gather
 };
+// Byte offset past the end of a gathered operand (bounded below 2^31 at launch).
+constexpr int kOob = 0x7FFFFFF0;
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
@@ -221,7 +226,9 @@ __global__ __launch_bounds__(1024) void fp8_tile_prefix_kernel(const int32_t* __
 
 constexpr int kMaxKB = 128;  // K <= 16384
 
-template <int EPI>
+// GATHER: the grouped rows of A and their scales are read from their token rows (the
+// permuted copy is never made).
+template <int EPI, bool GATHER>
 __global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE_BYTES];
   __shared__ float s_bs[NJ][kMaxKB];  // the tile's weight-block scales, one row per fragment j
@@ -262,21 +269,32 @@ __global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
 #pragma unroll
   for (int q = 0; q < A_DMA; ++q) {
     const int r = (wave * A_DMA + q) * 8 + (lane >> 3);
-    voffA[q] = r * p.K + (((lane & 7) ^ swz(r)) << 4);
+    if constexpr (GATHER) {
+      const int src = r < a_rows && row_begin + r < p.gather_len ? p.gather[row_begin + r] : -1;
+      voffA[q] = src >= 0 ? src * p.K + (((lane & 7) ^ swz(r)) << 4) : kOob;
+    } else {
+      voffA[q] = r * p.K + (((lane & 7) ^ swz(r)) << 4);
+    }
   }
 #pragma unroll
   for (int q = 0; q < B_DMA; ++q) {
     const int r = (wave * B_DMA + q) * 8 + (lane >> 3);
     voffB[q] = brow(r) * p.K + (((lane & 7) ^ swz(r)) << 4);
   }
-  const int voffS = (wave * 64 + lane) * KB * 4;  // waves 0-3 carry the 256 row scales
+  int voffS = (wave * 64 + lane) * KB * 4;  // waves 0-3 carry the 256 row scales
+  if constexpr (GATHER) {
+    const int r = wave * 64 + lane;
+    const int src = (wave < 4 && r < a_rows && row_begin + r < p.gather_len) ? p.gather[row_begin + r] : -1;
+    voffS = src >= 0 ? src * KB * 4 : kOob;
+  }
   const int ndma = A_DMA + B_DMA + (wave < 4 ? 1 : 0);
 
   auto issue = [&](int st) {
     uint8_t* dst = lds + (st % STAGES) * STAGE_BYTES;
     const int k0 = st * BKB;
     const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(p.A + static_cast<int64_t>(row_begin) * p.K + k0, (a_rows - 1) * p.K + BKB);
+        GATHER ? make_rsrc(p.A + k0, p.gather_rows * p.K - k0)
+               : make_rsrc(p.A + static_cast<int64_t>(row_begin) * p.K + k0, (a_rows - 1) * p.K + BKB);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg + k0, (p.N - 1) * p.K + BKB);
 #pragma unroll
     for (int q = 0; q < A_DMA; ++q)
@@ -287,7 +305,8 @@ __global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
                                                voffB[q], 0, 0, 0);
     if (wave < 4) {
       const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(p.A_scale + static_cast<int64_t>(row_begin) * KB + st, ((a_rows - 1) * KB + 1) * 4);
+          GATHER ? make_rsrc(p.A_scale + st, (p.gather_rows * KB - st) * 4)
+                 : make_rsrc(p.A_scale + static_cast<int64_t>(row_begin) * KB + st, ((a_rows - 1) * KB + 1) * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + A_BYTES + B_BYTES + wave * 256), 4, voffS, 0, 0,
                                                0);
     }
@@ -452,7 +471,8 @@ size_t fp8_schedule_bytes(int E) { return static_cast<size_t>(E + 1) * 4; }
 // fc1 (+ SwiGLU -> H, Act fp32) when act32 != NULL and C is NULL, else fc2 -> C.
 moe_status_t launch_gemm_fp8(bool swiglu, const uint8_t* A, const float* A_scale, const uint8_t* B,
                              const float* B_scale, float* C, float* H, const int32_t* offsets, int G, int64_t rows_upper,
-                             int N, int K, int F, int32_t* sched, hipStream_t s, Glu glu) {
+                             int N, int K, int F, int32_t* sched, hipStream_t s, Glu glu, const int32_t* gather,
+                             int gather_rows) {
   if (G > 4096) return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: more than 4096 experts");
   if (K > 128 * kMaxKB || K % 128 || N % 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: K must be a multiple of 128 up to 16384");
   if (static_cast<int64_t>(N) * K >= (int64_t{1} << 31) || rows_upper * K >= (int64_t{1} << 31))
@@ -461,14 +481,24 @@ moe_status_t launch_gemm_fp8(bool swiglu, const uint8_t* A, const float* A_scale
   a.A = A; a.A_scale = A_scale; a.B = B; a.B_scale = B_scale; a.C = C; a.H = H;
   a.offsets = offsets; a.tile_prefix = sched; a.G = G; a.N = N; a.K = K; a.F = F; a.glu = glu;
   a.nN = swiglu ? F / 64 : N / BN;
+  if (gather) {
+    if (!swiglu) return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: the row gather is for fc1");
+    if (static_cast<int64_t>(gather_rows) * K > kOob - 4096)
+      return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: gathered operand above 2 GB");
+    a.gather = gather;
+    a.gather_rows = gather_rows;
+    a.gather_len = static_cast<int>(rows_upper);
+  }
   fp8_tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, G, sched);
   const int64_t upper = (ceil_div(rows_upper, BM) + G) * a.nN;
   const int64_t grid = ceil_div(upper, 8) * 8;
   if (grid == 0) return MOE_OK;
-  if (swiglu)
-    fp8_gemm_kernel<FP8_SWIGLU><<<grid, NTHR, 0, s>>>(a);
+  if (swiglu && gather)
+    fp8_gemm_kernel<FP8_SWIGLU, true><<<grid, NTHR, 0, s>>>(a);
+  else if (swiglu)
+    fp8_gemm_kernel<FP8_SWIGLU, false><<<grid, NTHR, 0, s>>>(a);
   else
-    fp8_gemm_kernel<FP8_STORE><<<grid, NTHR, 0, s>>>(a);
+    fp8_gemm_kernel<FP8_STORE, false><<<grid, NTHR, 0, s>>>(a);
   return check_launch("gemm_fp8");
 }
 

@@ -87,7 +87,8 @@ size_t fp8_schedule_bytes(int E);
 // swiglu: fc1 of width N = 2F, Act (fp32) -> C [rows, F], H (optional); else C [rows, N]
 moe_status_t launch_gemm_fp8(bool swiglu, const uint8_t* A, const float* A_scale, const uint8_t* B,
                              const float* B_scale, float* C, float* H, const int32_t* offsets, int G, int64_t rows_upper,
-                             int N, int K, int F, int32_t* sched, hipStream_t s, Glu glu = Glu{0, 0.0f, 0.0f});
+                             int N, int K, int F, int32_t* sched, hipStream_t s, Glu glu = Glu{0, 0.0f, 0.0f},
+                             const int32_t* gather = nullptr, int gather_rows = 0);
 
 // ---------------------------------------------------------------- GEMMs
 // Storage of an operand: K_MAJOR = [rows][K] (K contiguous), MN_MAJOR = [K][rows].
@@ -122,6 +123,12 @@ struct GemmDesc {
   int G;
   int range_end;
   int64_t rows_upper;           // ragged M: upper bound of sum of rows (for grid sizing)
+  // Row gather of the permuted activation (the grouped rows are read from their token rows
+  // instead of a permuted copy): ragged M with a K-contiguous A reads row r of A from row
+  // gather[r] of A; ragged K with a row-contiguous B reads reduction row k of B from row
+  // gather[k] of B.  gather_rows: rows of the gathered operand (bounds every gathered read).
+  const int32_t* gather;
+  int gather_rows;
 };
 
 // fp32-accumulating FMA GEMM for fp32 (and mixed fp32/bf16) operands; SwiGLU epilogues are

@@ -22,6 +22,12 @@ namespace {
 
 constexpr int kChunk = 64;  // tokens per histogram chunk (one wave)
 
+// Expert id of a slot, clamped into [0, E): ids outside it break the caller's contract,
+// and clamping keeps every access that the id addresses inside its buffer.
+__device__ __forceinline__ int expert_of(const int32_t* __restrict__ idx, int64_t i, int E) {
+  return min(max(idx[i], 0), E - 1);
+}
+
 __global__ __launch_bounds__(64) void chunk_hist_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
                                                         int32_t* __restrict__ blk_hist) {
   extern __shared__ int hist[];
@@ -29,7 +35,7 @@ __global__ __launch_bounds__(64) void chunk_hist_kernel(const int32_t* __restric
   __syncthreads();
   const int t = blockIdx.x * kChunk + threadIdx.x;
   if (t < T)
-    for (int j = 0; j < k; ++j) atomicAdd(&hist[idx[static_cast<int64_t>(t) * k + j]], 1);
+    for (int j = 0; j < k; ++j) atomicAdd(&hist[expert_of(idx, static_cast<int64_t>(t) * k + j, E)], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 64) blk_hist[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
 }
@@ -90,14 +96,14 @@ __global__ __launch_bounds__(64) void permute_index_kernel(const int32_t* __rest
   const int lane = threadIdx.x;
   const int t = blockIdx.x * kChunk + lane;
   const bool ok = t < T;
-  for (int j = 0; j < k && ok; ++j) mask[idx[static_cast<int64_t>(t) * k + j]] = 0ull;
+  for (int j = 0; j < k && ok; ++j) mask[expert_of(idx, static_cast<int64_t>(t) * k + j, E)] = 0ull;
   __syncthreads();
-  for (int j = 0; j < k && ok; ++j) atomicOr(&mask[idx[static_cast<int64_t>(t) * k + j]], 1ull << lane);
+  for (int j = 0; j < k && ok; ++j) atomicOr(&mask[expert_of(idx, static_cast<int64_t>(t) * k + j, E)], 1ull << lane);
   __syncthreads();
   if (!ok) return;
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int j = 0; j < k; ++j) {
-    const int e = idx[static_cast<int64_t>(t) * k + j];
+    const int e = expert_of(idx, static_cast<int64_t>(t) * k + j, E);
     const int r = offsets[e] + blk_base[static_cast<int64_t>(blockIdx.x) * E + e] + __popcll(mask[e] & below);
     row_of[static_cast<int64_t>(t) * k + j] = r;
     token_of[r] = t;
@@ -439,9 +445,11 @@ moe_status_t launch_permute(const moe_config_t& c, const void* x, const int32_t*
   offsets_kernel<<<1, 1024, 0, s>>>(counts_ws, c.E, offsets);
   permute_index_kernel<<<nblk, 64, c.E * sizeof(unsigned long long), s>>>(idx, c.T, c.E, c.k, offsets, blk_base,
                                                                           row_of, token_of);
-  const int units = static_cast<int>(static_cast<int64_t>(c.d) * (elem_bytes ? elem_bytes : act_bytes(c)) / 16);
-  permute_copy_kernel<<<static_cast<int>(ceil_div(c.T, 4)), 256, 0, s>>>(
-      static_cast<const uint4*>(x), c.T, units, c.k, row_of, static_cast<uint4*>(x_perm));
+  if (x_perm) {   // NULL: the grouped GEMMs read the token rows of x through token_of instead
+    const int units = static_cast<int>(static_cast<int64_t>(c.d) * (elem_bytes ? elem_bytes : act_bytes(c)) / 16);
+    permute_copy_kernel<<<static_cast<int>(ceil_div(c.T, 4)), 256, 0, s>>>(
+        static_cast<const uint4*>(x), c.T, units, c.k, row_of, static_cast<uint4*>(x_perm));
+  }
   return check_launch("permute");
 }
 

@@ -242,18 +242,18 @@ def test_entry_points_reject_bad_arguments_before_launching():
     assert st == L.MOE_ERR_INVALID_ARG and b"counts" in lib.moe_last_error()
     # grouped weight gradient: group count, offsets and sizes are checked on the host
     i32, i64 = ctypes.c_int32, ctypes.c_int64
-    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(0), i64(64), fake, i32(64), fake, i32(64), fake, i32(0), nul, ctypes.c_size_t(0), s)
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(0), i64(64), fake, i32(64), fake, i32(64), nul, i32(0), fake, i32(0), nul, ctypes.c_size_t(0), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"groups" in lib.moe_last_error()
-    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), nul, i32(2), i64(64), fake, i32(64), fake, i32(64), fake, i32(0), nul, ctypes.c_size_t(0), s)
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), nul, i32(2), i64(64), fake, i32(64), fake, i32(64), nul, i32(0), fake, i32(0), nul, ctypes.c_size_t(0), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"one group" in lib.moe_last_error()
-    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(64), fake, i32(96), fake, i32(64), fake, i32(0), nul, ctypes.c_size_t(0), s)
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(64), fake, i32(96), fake, i32(64), nul, i32(0), fake, i32(0), nul, ctypes.c_size_t(0), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"multiples of 64" in lib.moe_last_error()
-    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(-1), fake, i32(64), fake, i32(64), fake, i32(0), nul, ctypes.c_size_t(0), s)
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(-1), fake, i32(64), fake, i32(64), nul, i32(0), fake, i32(0), nul, ctypes.c_size_t(0), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"rows" in lib.moe_last_error()
-    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(64), fake, i32(64), fake, i32(64), fake, i32(2), nul, ctypes.c_size_t(0), s)
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(64), fake, i32(64), fake, i32(64), nul, i32(0), fake, i32(2), nul, ctypes.c_size_t(0), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"accumulate" in lib.moe_last_error()
     # a one-group weight gradient that would split its rows needs room for the partials
-    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), nul, i32(1), i64(1000), fake, i32(192), fake, i32(320), fake, i32(0),
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), nul, i32(1), i64(1000), fake, i32(192), fake, i32(320), nul, i32(0), fake, i32(0),
                                fake, ctypes.c_size_t(16), s)
     assert st == L.MOE_ERR_WORKSPACE and str(3 * 192 * 320 * 4).encode() in lib.moe_last_error()
     # layer backward: the gradient structure's accumulate flag is 0 or 1
@@ -264,9 +264,48 @@ def test_entry_points_reject_bad_arguments_before_launching():
                            fake, ctypes.byref(gr), fake, ctypes.c_size_t(1 << 40), s, s)
     assert st == L.MOE_ERR_INVALID_ARG and b"accumulate" in lib.moe_last_error()
     # expert backward: routed weight gradients are both given or both NULL
-    st = lib.moe_grouped_gemm_swiglu_bwd(ctypes.byref(cfg), *([fake] * 9), fake, nul, *([nul] * 10), fake,
+    st = lib.moe_grouped_gemm_swiglu_bwd(ctypes.byref(cfg), fake, nul, *([fake] * 8), fake, nul, *([nul] * 10), fake,
                                          ctypes.c_size_t(1 << 40), s)
     assert st == L.MOE_ERR_INVALID_ARG and b"dW2" in lib.moe_last_error()
+
+
+def test_row_gather_arguments_are_checked_before_launching():
+    """The grouped calls read the token rows of x through token_of only for bf16
+    activations and only in place of x_perm; the layer refuses a NULL x_perm with fp32
+    activations; the fp8 permute takes its two outputs together or neither."""
+    lib = L.load()
+    fake, nul, s = P(1 << 20), P(None), P(None)
+    i32, i64, big = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t(1 << 40)
+    cfg = L.config_from_shape(W.LAYERS[2])                 # bf16
+    c32 = L.config_from_shape(W.LAYERS[1])                 # fp32 activations
+    assert c32.act_dtype == L.MOE_F32 and cfg.act_dtype == L.MOE_BF16
+    st = lib.moe_grouped_gemm_swiglu(ctypes.byref(cfg), fake, fake, *([fake] * 12), fake, big, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"not both" in lib.moe_last_error()
+    st = lib.moe_grouped_gemm_swiglu(ctypes.byref(cfg), nul, nul, *([fake] * 12), fake, big, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"x_perm" in lib.moe_last_error()
+    st = lib.moe_grouped_gemm_swiglu(ctypes.byref(c32), nul, fake, *([fake] * 12), fake, big, s)
+    assert st == L.MOE_ERR_UNSUPPORTED and b"bf16" in lib.moe_last_error()
+    st = lib.moe_grouped_gemm_swiglu_bwd(ctypes.byref(cfg), fake, fake, *([fake] * 8), fake, fake, *([fake] * 10),
+                                         fake, big, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"not both" in lib.moe_last_error()
+    st = lib.moe_grouped_wgrad(ctypes.byref(c32), fake, i32(4), i64(64), fake, i32(64), fake, i32(64), fake, i32(16),
+                               fake, i32(0), nul, ctypes.c_size_t(0), s)
+    assert st == L.MOE_ERR_UNSUPPORTED and b"x_rows" in lib.moe_last_error()
+    st = lib.moe_grouped_wgrad(ctypes.byref(cfg), fake, i32(4), i64(64), fake, i32(64), fake, i32(64), fake, i32(0),
+                               fake, i32(0), nul, ctypes.c_size_t(0), s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"x_src_rows" in lib.moe_last_error()
+    names = [n for n, _ in L.Saved._fields_]
+    w = L.Weights(Wg=1 << 20, W13=1 << 20, W2=1 << 20)
+    sv = L.Saved(**{n: (None if n == "x_perm" else 1 << 20) for n in names})
+    st = lib.moe_layer_fwd(ctypes.byref(c32), ctypes.byref(w), fake, ctypes.byref(sv), fake, nul, fake, big, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"x_perm is needed" in lib.moe_last_error()
+    g = L.Grads(dWg=1 << 20, dW13=1 << 20, dW2=1 << 20)
+    st = lib.moe_layer_bwd(ctypes.byref(c32), ctypes.byref(w), ctypes.byref(sv), fake, fake, ctypes.c_float(1.0), fake,
+                           ctypes.byref(g), fake, big, s, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"x_perm is needed" in lib.moe_last_error()
+    c8 = L.config_from_shape(W.LAYERS[5])
+    st = lib.moe_permute_fp8(ctypes.byref(c8), fake, fake, fake, fake, fake, fake, fake, nul, fake, big, s)
+    assert st == L.MOE_ERR_INVALID_ARG and b"together" in lib.moe_last_error()
 
 
 def test_status_strings():

@@ -204,6 +204,14 @@ def test_fp8_grouped_experts_forward():
                               None, Act, Act_scale, Y2, ws)
     torch.cuda.synchronize()
     assert torch.equal(Y, Y2)
+    # the token rows' codes and scales read through token_of: the same bits
+    gH, gY = e32(A, 2 * F), e32(A, d)
+    gAct, gAct_scale = torch.empty_like(Act), e32(A, F // 128)
+    L.grouped_gemm_swiglu_fp8(cfg, xq, xs, off, wg["W13"], wg["W13_scale"], wg["W2"], wg["W2_scale"], gH, gAct,
+                              gAct_scale, gY, ws, token_of=to_dev(p.token_of.astype(np.int32)))
+    torch.cuda.synchronize()
+    for name, a, b in (("H", H, gH), ("Act", Act, gAct), ("Act_scale", Act_scale, gAct_scale), ("Y", Y, gY)):
+        assert torch.equal(a, b), f"{name}: token_of gather differs from the grouped copy"
 
 
 def test_fp8_layer_forward_and_router_backward():
@@ -229,7 +237,42 @@ def test_fp8_layer_edge_cases(case):
     _check_fp8_layer(shape, seed)
 
 
-def _check_fp8_layer(shape, seed):
+def test_fp8_layer_with_the_grouped_copy():
+    _check_fp8_layer(replace(SHAPE, T=300), seed=7, copy=True)
+
+
+@pytest.mark.parametrize("case", ["reduced", "one_token", "ragged_chunk"])
+def test_fp8_layer_token_rows_match_the_grouped_copy(case):
+    """The e4m3 layer without saved->x_perm (its fc1 reads the token rows' codes through
+    token_of) gives the same bits as with the grouped copy."""
+    torch = torch_mod()
+    L = _lib()
+    shape, seed = (SHAPE, 5) if case == "reduced" else FP8_EDGE[case]
+    cfg = L.config_from_shape(shape)
+    inp = W.make_inputs(shape, seed=seed)
+    wg, _ = _expert_weights(L, inp, shape)
+    Wt = dict(Wg=to_dev(inp["Wg"]), bg=to_dev(inp["bg"]), **wg)
+    x = to_dev(inp["x"])
+    dy = to_dev(W.to_f32(inp["dy"], shape.act).copy())
+    out = []
+    for copy in (True, False):
+        S = L.alloc_saved(cfg, dev(), x_perm=copy)
+        G = L.alloc_grads(cfg, dev(), with_dbg=True)
+        ws = L.alloc_workspace(cfg, dev())
+        y = torch.empty(shape.T, shape.d, dtype=torch.float32, device=dev())
+        dx = torch.empty_like(y)
+        stats = torch.empty(L.MOE_NSTATS, dtype=torch.float32, device=dev())
+        L.layer_fwd(cfg, Wt, x, S, y, stats, ws)
+        L.layer_bwd(cfg, Wt, S, x, dy, 1.0, dx, G, ws)
+        torch.cuda.synchronize()
+        out.append(dict(y=y, dx=dx, stats=stats, **{f"S_{k}": v for k, v in S.items()}, **G))
+    a, b = out
+    assert "S_x_perm" in a and "S_x_perm" not in b
+    for k in b:
+        assert torch.equal(a[k], b[k]), k
+
+
+def _check_fp8_layer(shape, seed, copy=None):
     torch = torch_mod()
     L = _lib()
     cfg = L.config_from_shape(shape)
@@ -239,7 +282,7 @@ def _check_fp8_layer(shape, seed):
     Wt = dict(Wg=to_dev(inp["Wg"]), bg=to_dev(inp["bg"]), **wg)
     x = to_dev(inp["x"])
     dy = to_dev(W.to_f32(inp["dy"], shape.act).copy())
-    S = L.alloc_saved(cfg, dev())
+    S = L.alloc_saved(cfg, dev(), x_perm=copy)
     G = L.alloc_grads(cfg, dev(), with_dbg=True)
     assert "dW13" not in G
     ws = L.alloc_workspace(cfg, dev())
@@ -256,10 +299,16 @@ def _check_fp8_layer(shape, seed):
     r = f["route"]
     safe = r["margin"] > MARGIN
     moved = routing_moved(to_np(S["idx"]), r)
-    # the saved e4m3 rows are the oracle's bytes
+    # the e4m3 rows are the oracle's bytes (the saved grouped copy, or the token rows the
+    # layer quantises in its workspace, which the same quantiser call reproduces)
     tok = f["perm"].token_of
-    assert np.array_equal(S["x_perm"].cpu().numpy(), f["x_q"][tok])
-    assert np.array_equal(S["x_perm_scale"].cpu().numpy(), f["x_scale"][tok])
+    if "x_perm" in S:
+        assert np.array_equal(S["x_perm"].cpu().numpy(), f["x_q"][tok])
+        assert np.array_equal(S["x_perm_scale"].cpu().numpy(), f["x_scale"][tok])
+    else:
+        xq, xs = _quantise_gpu(L, x, 1)
+        assert np.array_equal(xq.cpu().numpy(), f["x_q"]) and np.array_equal(xs.cpu().numpy(), f["x_scale"])
+        assert np.array_equal(to_np(S["token_of"]), tok)
     # y: the combine of the per-row bound (routing equal on the compared tokens)
     ybound = np.einsum("tk,tkd->td", np.abs(r["w"]), _flip_bound(f, wo["W2q"], wo["W2s"], spec)[f["perm"].row_of])
     _check_within(to_np(y), f["y"], ybound, 2e-3, "y", safe)

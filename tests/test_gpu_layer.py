@@ -7,6 +7,8 @@ on both sides (a token can only move between experts when its margin is below th
 logit error, which is checked too); the router weight gradient, a sum over all tokens,
 is compared when no token moved.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 
@@ -16,7 +18,7 @@ from helpers import (MARGIN, O, W, check_layer_grads, dev, oracle_inputs, rel_er
 pytestmark = pytest.mark.gpu
 
 
-def _run_layer(shape, inp, wgrad_stream=None, **cfg_extra):
+def _run_layer(shape, inp, wgrad_stream=None, copy=None, **cfg_extra):
     torch = torch_mod()
     from mixture_experts_layer_aux_amd import _lib as L
     cfg = L.config_from_shape(shape, **cfg_extra)
@@ -26,7 +28,7 @@ def _run_layer(shape, inp, wgrad_stream=None, **cfg_extra):
               Wsg=to_dev(inp.get("Wsg")))
     x = to_dev(inp["x"])
     dy = to_dev(W.to_f32(inp["dy"], shape.act).copy())     # upstream gradient, fp32
-    S = L.alloc_saved(cfg, d)
+    S = L.alloc_saved(cfg, d, x_perm=copy)     # default: bf16 layers keep no grouped copy of x
     G = L.alloc_grads(cfg, d, with_dbg=inp["bg"] is not None)
     ws = L.alloc_workspace(cfg, d)
     y = torch.empty(shape.T, shape.d, dtype=torch.float32, device=d)
@@ -107,6 +109,31 @@ def test_layer_two_streams(cid):
         assert torch.equal(one[k], two[k]), k
 
 
+_GATHER_CASES = {
+    "small2": (W.SMALL[2], {}),
+    "small3": (W.SMALL[3], {}),
+    "small4": (W.SMALL[4], {}),
+    "small5": (W.SMALL[5], {}),
+    "ragged_t257": (replace(W.SMALL[3], T=257), {}),
+    "empty_experts": (replace(W.SMALL[3], T=3, k=2, E=32), {}),
+    "fp32_wgrad": (W.SMALL[3], {"wgrad": "f32"}),
+}
+
+
+@pytest.mark.parametrize("case", list(_GATHER_CASES))
+def test_layer_token_rows_match_the_grouped_copy(case):
+    """saved->x_perm NULL (the fc1 and its weight gradient read the token rows of x through
+    token_of) gives the same bits as the layer with the grouped copy of x."""
+    torch = torch_mod()
+    shape, extra = _GATHER_CASES[case]
+    inp = W.make_inputs(shape, seed=21)
+    a = _run_layer(shape, inp, copy=True, **extra)
+    b = _run_layer(shape, inp, copy=False, **extra)
+    assert "S_x_perm" in a and "S_x_perm" not in b
+    for k in b:
+        assert torch.equal(a[k], b[k]), k
+
+
 def test_layer_fp32_weight_gradients():
     """The fp32 weight-gradient option of a bf16 layer (the default is bf16)."""
     got = _check_layer(W.SMALL[3], seed=3, wgrad="f32")
@@ -115,7 +142,6 @@ def test_layer_fp32_weight_gradients():
 
 @pytest.mark.parametrize("variant", ["scaling", "no_shared_sigmoid", "k_equals_E", "one_row_experts", "ragged_split"])
 def test_layer_edge_cases(variant):
-    from dataclasses import replace
     base = W.SMALL[3]
     if variant == "scaling":
         shape = replace(W.SMALL[2], scaling=2.5, T=300)

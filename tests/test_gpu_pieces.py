@@ -108,6 +108,11 @@ def test_permute_bit_exact(cid):
     assert np.array_equal(to_np(token_of), p.token_of)
     # the moved rows are exact copies
     assert torch.equal(x_perm, x[torch.from_numpy(p.token_of).to(dev())])
+    # without x_perm: the same grouping, no copy
+    offsets2, row_of2, token_of2 = offsets.clone().fill_(-7), row_of.clone().fill_(-7), token_of.clone().fill_(-7)
+    L.permute(cfg, None, to_dev(idx.astype(np.int32)), offsets2, row_of2, token_of2, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(offsets2, offsets) and torch.equal(row_of2, row_of) and torch.equal(token_of2, token_of)
 
 
 def _expert_inputs(shape, cid):
@@ -186,9 +191,33 @@ def check_grouped_experts(shape, cid):
             split += [(dW13s, fW13s.to(torch.bfloat16)), (dW2s, fW2s.to(torch.bfloat16))]
             fW13s_np, fW2s_np = to_np(fW13s), to_np(fW2s)
         fW13_np, fW2_np = to_np(fW13), to_np(fW2)
+    if shape.act == "bf16":
+        # the same products with the token rows of x read through token_of instead of the
+        # grouped copy: the same bits
+        tok = to_dev(p.token_of.astype(np.int32))
+        gH, gAct, gYp = e32(A, 2 * F), e(A, F), e32(A, d)
+        gH_s, gAct_s, gY_s = (e32(T, 2 * Fs), e(T, Fs), e32(T, d)) if Fs else (None, None, None)
+        L.grouped_gemm_swiglu(cfg, None, off, W13, W2, x, W13s, W2s, gH, gAct, gYp, gH_s, gAct_s, gY_s, ws,
+                              token_of=tok)
+        split += [(H, gH), (Act, gAct), (Yp, gYp)]
+        gdH, gdXp, gW13, gW2 = e(A, 2 * F), e32(A, d), ew(E, 2 * F, d), ew(E, d, F)
+        gdH_s, gdx_s = (e(T, 2 * Fs), e32(T, d)) if Fs else (None, None)
+        gW13s, gW2s = (ew(2 * Fs, d), ew(d, Fs)) if Fs else (None, None)
+        L.grouped_gemm_swiglu_bwd(cfg, None, off, W13, W2, H, Act, dYp, gdH, gdXp, gW13, gW2, x, W13s, W2s, H_s,
+                                  Act_s, dy if Fs else None, gdH_s, gdx_s, gW13s, gW2s, ws, token_of=tok)
+        split += [(dH, gdH), (dXp, gdXp), (dW13, gW13), (dW2, gW2)]
+        if Fs:
+            split += [(dW13s, gW13s), (dW2s, gW2s), (dx_s, gdx_s)]
+        xW13 = ew(E, 2 * F, d)
+        L.grouped_wgrad(cfg, off, E, A, dH2, 2 * F, x, d, xW13, x_rows=tok)
+        split += [(dW13, xW13)]
+        if cfg.wgrad_dtype == L.MOE_BF16:
+            xW13f = e32(E, 2 * F, d)
+            L.grouped_wgrad(c32, off, E, A, dH2, 2 * F, x, d, xW13f, x_rows=tok)
+            split += [(fW13, xW13f)]
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(split):
-        assert torch.equal(a, b), f"split backward differs from the fused one (output {i})"
+        assert torch.equal(a, b), f"pair {i} differs (split vs fused backward, or token_of vs grouped copy)"
     tl = tol(shape)
     xp = o["x"][p.token_of]
     dYo = f64(dYp_np, shape.act)
