@@ -272,7 +272,8 @@ def bench_fp8(args, shape, cfg, inp, up, dev) -> int:
         config=dict(workload=shape.name, T=T, d=d, E=E, k=k, F=F, Fs=0, score=shape.score, bias=shape.bias,
                     passes="forward + router-path backward (frozen fp8 experts)",
                     fc1_rows="token rows' e4m3 codes through token_of (no grouped copy)", parallelism="single GPU"),
-        roofline=dict(kernel="grouped fp8 SwiGLU experts forward (fc1 GEMM + Act quantiser + fc2 GEMM)",
+        roofline=dict(kernel="grouped fp8 SwiGLU experts forward (fc1 GEMM, Act quantised in its epilogue with "
+                             "128-row tiles or by the quantiser after it, fc2 GEMM)",
                       bound="mfma", achieved=round(tf, 2), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
                       frac=round(tf / PEAK_FP8_TFLOPS, 4), traffic=None, flop_per_step=flop, ms_per_step=round(ms, 4)),
         phases_ms={p: round(v, 4) for p, v in phase_ms.items()},

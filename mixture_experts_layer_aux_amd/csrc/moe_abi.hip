@@ -423,11 +423,17 @@ moe_status_t run_experts_fp8(const moe_config_t& c, const uint8_t* x_perm, const
                              float* H, uint8_t* Act, float* Act_scale, float* Y_perm, float* act32, int32_t* sched,
                              hipStream_t s, const int32_t* token_of = nullptr) {
   const int64_t A = static_cast<int64_t>(c.T) * c.k;
-  MOE_TRY(launch_gemm_fp8(true, x_perm, xps, W13, W13_scale, act32, H, offsets, c.E, A, 2 * c.F, c.d, c.F, sched, s,
-                          glu_of(c), token_of, c.T));
-  MOE_TRY(launch_quantize_fp8(MOE_F32, act32, A, c.F, 1, Act, Act_scale, s));
+  // one tile shape for both GEMMs (they share the tile schedule); with 128-row tiles the
+  // fc1 epilogue quantises Act itself
+  const bool narrow = fp8_tile_rows(A, c.E, 2 * c.F, c.F, true) == 128 && fp8_tile_rows(A, c.E, c.d, c.F, false) == 128;
+  const int bm = narrow ? 128 : 256;
+  const bool fused = bm == 128;
+  MOE_TRY(launch_gemm_fp8(true, x_perm, xps, W13, W13_scale, fused ? nullptr : act32, H, offsets, c.E, A, 2 * c.F,
+                          c.d, c.F, sched, s, glu_of(c), token_of, c.T, bm, fused ? Act : nullptr,
+                          fused ? Act_scale : nullptr));
+  if (!fused) MOE_TRY(launch_quantize_fp8(MOE_F32, act32, A, c.F, 1, Act, Act_scale, s));
   return launch_gemm_fp8(false, Act, Act_scale, W2, W2_scale, Y_perm, nullptr, offsets, c.E, A, c.d, c.F, c.F, sched,
-                         s);
+                         s, Glu{0, 0.0f, 0.0f}, nullptr, 0, bm);
 }
 
 moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const int32_t* offsets, const void* W13,

@@ -7,12 +7,17 @@
 // fp32 quotient v / scale, ties to the even code, saturated to 448.  Weights use 128 x 128
 // blocks, activations 1 x 128 (per token per 128 columns).
 //
-// GEMM design (per workgroup: 512 threads = 8 waves in a 4 x 2 grid):
-//   * 256 x 128 output tile, each wave 64 x 64 as 2 x 2 accumulators of
-//     v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, fp32 out);
+// GEMM design (per workgroup: 512 threads = 8 waves):
+//   * two tile shapes of the same area: 256 x 128 (waves 4 x 2) and 128 x 256 (waves
+//     2 x 4), each wave 64 x 64 as 2 x 2 accumulators of v_mfma_f32_32x32x64_f8f6f4
+//     (e4m3 x e4m3, fp32 out).  Launches whose experts average fewer than 512 rows take
+//     128-row tiles: a 256-row tile of an expert with a few hundred rows is mostly
+//     padding.  The 128 x 256 fc1 tile holds 128 Act columns of each row, one whole
+//     quantisation block, so its epilogue writes the e4m3 codes and the block scale
+//     itself (no fp32 Act round trip through HBM);
 //   * one stage = one 128-wide K block = one scale block: both operands (128 bytes per row)
-//     and the 256 row scales of the A operand go from HBM into LDS by buffer_load ... lds,
-//     through a ring of 3 stages (147 KB);
+//     and the row scales of the A operand go from HBM into LDS by buffer_load ... lds,
+//     through a ring of 3 stages (147 / 146 KB);
 //   * per K block, each accumulator pair is formed from zero by two MFMAs and added to the
 //     fp32 accumulator times (row scale x weight-block scale): the block scales of both
 //     operands apply exactly once per block;
@@ -23,7 +28,7 @@
 //     columns per register quad (vector epilogue stores);
 //   * fc1's B tile interleaves 32 gate rows and 32 up rows, so the SwiGLU epilogue finds a
 //     gate value and its up value in the same lane; it writes H (fp32, optional) and Act
-//     (fp32) for the per-row quantiser.
+//     (fp32 for the per-row quantiser, or, with 128-row tiles, e4m3 codes and scales).
 #include "moe_internal.h"
 
 namespace moe {
@@ -146,14 +151,22 @@ __global__ __launch_bounds__(256) void gather_scales_kernel(const float* __restr
 
 // ------------------------------------------------------------------ grouped fp8 GEMM
 
-constexpr int BM = 256, BN = 128, BKB = 128, STAGES = 3;  // BKB: K bytes (= values) per stage
-constexpr int WAVES_M = 4, WAVES_N = 2, NWAVES = 8, NTHR = 512;
-constexpr int NI = 2, NJ = 2;                              // 32 x 32 blocks per wave
-constexpr int A_BYTES = BM * BKB, B_BYTES = BN * BKB;     // 32 KB, 16 KB
-constexpr int S_BYTES = BM * 4;                           // A row scales of one stage
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
-constexpr int A_DMA = A_BYTES / 1024 / NWAVES;            // 4 one-KB loads per wave
-constexpr int B_DMA = B_BYTES / 1024 / NWAVES;            // 2
+constexpr int BKB = 128, STAGES = 3;     // BKB: K bytes (= values) per stage
+constexpr int NWAVES = 8, NTHR = 512;
+constexpr int NI = 2, NJ = 2;            // 32 x 32 blocks per wave (64 x 64)
+constexpr int TILE_AREA = 256 * 128;     // BM x BN of both tile shapes
+// Tile shape of a launch: BM rows (256 or 128) by BN = TILE_AREA / BM columns.
+template <int BM> struct Fp8Tile {
+  static constexpr int BN = TILE_AREA / BM;
+  static constexpr int WAVES_M = BM / 64, WAVES_N = BN / 64;
+  static constexpr int A_BYTES = BM * BKB, B_BYTES = BN * BKB;   // 32 + 16 KB or 16 + 32 KB
+  static constexpr int S_BYTES = BM * 4;                        // A row scales of one stage
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int A_DMA = A_BYTES / 1024 / NWAVES;          // one-KB loads per wave
+  static constexpr int B_DMA = B_BYTES / 1024 / NWAVES;
+  static constexpr int S_WAVES = BM / 64;                        // waves that carry the row scales
+  static_assert(WAVES_M * WAVES_N == NWAVES, "8 waves of 64 x 64");
+};
 constexpr int kRsrcFlags = 0x00020000;
 enum { FP8_SWIGLU = 0, FP8_STORE = 1 };
 
@@ -162,8 +175,10 @@ struct Fp8Args {
   const float* A_scale;   // [rows, K/128]
   const uint8_t* B;       // [G, N, K] codes
   const float* B_scale;   // [G, N/128, K/128]
-  float* C;               // STORE: [rows, N]; SWIGLU: Act fp32 [rows, F]
+  float* C;               // STORE: [rows, N]; SWIGLU: Act fp32 [rows, F] (unless Cq)
   float* H;               // SWIGLU: [rows, 2F] or NULL
+  uint8_t* Cq;            // SWIGLU with 128-row tiles: Act e4m3 codes [rows, F] (C unused)
+  float* Cq_scale;        //   and their scales [rows, F/128]
   const int32_t* offsets;
   const int32_t* tile_prefix;
   int G, N, K, F, nN;
@@ -204,10 +219,10 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(1024) void fp8_tile_prefix_kernel(const int32_t* __restrict__ offsets, int G,
+__global__ __launch_bounds__(1024) void fp8_tile_prefix_kernel(const int32_t* __restrict__ offsets, int G, int bm,
                                                                int32_t* __restrict__ prefix) {
   __shared__ int s[4096];
-  for (int g = threadIdx.x; g < 4096; g += 1024) s[g] = g < G ? (offsets[g + 1] - offsets[g] + BM - 1) / BM : 0;
+  for (int g = threadIdx.x; g < 4096; g += 1024) s[g] = g < G ? (offsets[g + 1] - offsets[g] + bm - 1) / bm : 0;
   __syncthreads();
   for (int off = 1; off < 4096; off <<= 1) {
     int a[4];
@@ -228,10 +243,15 @@ constexpr int kMaxKB = 128;  // K <= 16384
 
 // GATHER: the grouped rows of A and their scales are read from their token rows (the
 // permuted copy is never made).
-template <int EPI, bool GATHER>
-__global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
+template <int EPI, bool GATHER, int BM>
+__device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
+  using Tl = Fp8Tile<BM>;
+  constexpr int BN = Tl::BN, WAVES_N = Tl::WAVES_N, A_BYTES = Tl::A_BYTES, B_BYTES = Tl::B_BYTES;
+  constexpr int STAGE_BYTES = Tl::STAGE_BYTES, A_DMA = Tl::A_DMA, B_DMA = Tl::B_DMA, S_WAVES = Tl::S_WAVES;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE_BYTES];
-  __shared__ float s_bs[NJ][kMaxKB];  // the tile's weight-block scales, one row per fragment j
+  // the tile's weight-block scales per K block: every wave's fragment j lies in one
+  // 128-row block of the weights, which depends on the wave's column slot wn
+  __shared__ float s_bs[WAVES_N][NJ][kMaxKB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -260,9 +280,10 @@ __global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
   const uint8_t* Bg = p.B + static_cast<int64_t>(g) * p.N * p.K;
   const float* Bsg = p.B_scale + static_cast<int64_t>(g) * (p.N / 128) * KB;
 
-  // B-tile row r -> weight row: fc1 interleaves 32 gate rows and 32 up rows
+  // B-tile row r -> weight row: fc1 interleaves 32 gate rows and 32 up rows (BN / 2 Act
+  // columns per tile)
   auto brow = [&](int r) -> int {
-    return EPI == FP8_SWIGLU ? (((r >> 5) & 1) ? p.F : 0) + nt * 64 + (r >> 6) * 32 + (r & 31) : nt * BN + r;
+    return EPI == FP8_SWIGLU ? (((r >> 5) & 1) ? p.F : 0) + nt * (BN / 2) + (r >> 6) * 32 + (r & 31) : nt * BN + r;
   };
   // per-lane DMA offsets (bytes from the stage's base)
   int voffA[A_DMA], voffB[B_DMA];
@@ -281,13 +302,13 @@ __global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
     const int r = (wave * B_DMA + q) * 8 + (lane >> 3);
     voffB[q] = brow(r) * p.K + (((lane & 7) ^ swz(r)) << 4);
   }
-  int voffS = (wave * 64 + lane) * KB * 4;  // waves 0-3 carry the 256 row scales
+  int voffS = (wave * 64 + lane) * KB * 4;  // waves 0 .. S_WAVES-1 carry the BM row scales
   if constexpr (GATHER) {
     const int r = wave * 64 + lane;
-    const int src = (wave < 4 && r < a_rows && row_begin + r < p.gather_len) ? p.gather[row_begin + r] : -1;
+    const int src = (wave < S_WAVES && r < a_rows && row_begin + r < p.gather_len) ? p.gather[row_begin + r] : -1;
     voffS = src >= 0 ? src * KB * 4 : kOob;
   }
-  const int ndma = A_DMA + B_DMA + (wave < 4 ? 1 : 0);
+  const int ndma = A_DMA + B_DMA + (wave < S_WAVES ? 1 : 0);
 
   auto issue = [&](int st) {
     uint8_t* dst = lds + (st % STAGES) * STAGE_BYTES;
@@ -303,7 +324,7 @@ __global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
     for (int q = 0; q < B_DMA; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dst + A_BYTES + (wave * B_DMA + q) * 1024), 16,
                                                voffB[q], 0, 0, 0);
-    if (wave < 4) {
+    if (wave < S_WAVES) {
       const __amdgpu_buffer_rsrc_t rs =
           GATHER ? make_rsrc(p.A_scale + st, (p.gather_rows * KB - st) * 4)
                  : make_rsrc(p.A_scale + static_cast<int64_t>(row_begin) * KB + st, ((a_rows - 1) * KB + 1) * 4);
@@ -325,9 +346,10 @@ __global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
   // The weight-block scales of this tile (every wave's fragment j falls in the same
   // 128-row block), staged in LDS once: loaded per K block in the loop they would be
   // vector loads whose waits would also wait for the stage DMA issued before them.
-  for (int t = tid; t < NJ * KB; t += NTHR) {
-    const int j = t / KB, kb = t - j * KB;
-    s_bs[j][kb] = Bsg[(brow(j * 32) / 128) * KB + kb];
+  for (int t = tid; t < WAVES_N * NJ * KB; t += NTHR) {
+    const int wj = t / KB, kb = t - wj * KB;
+    const int w = wj / NJ, j = wj - w * NJ;
+    s_bs[w][j][kb] = Bsg[(brow(w * 64 + j * 32) / 128) * KB + kb];
   }
   __syncthreads();
 
@@ -361,7 +383,7 @@ __global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
     for (int j = 0; j < NJ; ++j) {
       fb[j][0] = frag(Bs, wn * 64 + j * 32, 0);
       fb[j][1] = frag(Bs, wn * 64 + j * 32, 1);
-      sb[j] = s_bs[j][it];
+      sb[j] = s_bs[wn][j][it];
     }
     // the stage's reads go out before the next DMA is issued: the compiler would
     // otherwise wait for that DMA before any LDS read that follows it
@@ -382,9 +404,10 @@ __global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
   }
 
   // epilogue: acc[i][j][4q + c] is row wm*64 + i*32 + lane%32, column
-  // wn*64 + j*32 + 8q + 4(lane/32) + c of the B tile.  The 256 x 128 fp32 tile goes through
-  // LDS (row-major, 16-byte chunk c of row r at r * 32 + (c ^ (r & 31))), so that the global
-  // writes run along whole rows instead of 16-byte pieces of 32 rows.
+  // wn*64 + j*32 + 8q + 4(lane/32) + c of the B tile.  The BM x BN fp32 tile goes through
+  // LDS (row-major, 16-byte chunk c of row r at r * (BN / 4) + (c ^ (r & 31))), so that the
+  // global writes run along whole rows instead of 16-byte pieces of 32 rows.
+  constexpr int RC = BN / 4;   // 16-byte chunks per tile row
   float4* L4 = reinterpret_cast<float4*>(lds);
   static_assert(STAGES * STAGE_BYTES >= BM * BN * 4, "epilogue staging needs the tile in LDS");
   block_barrier();  // every wave is done with the last stage
@@ -397,45 +420,79 @@ __global__ __launch_bounds__(NTHR, 1) void fp8_gemm_kernel(const Fp8Args p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int c = (wn * 64 + j * 32 + 8 * q + cb) >> 2;
-        L4[r * 32 + (c ^ (r & 31))] =
+        L4[r * RC + (c ^ (r & 31))] =
             make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       }
   }
   block_barrier();
+  constexpr int RPW = BM / NWAVES;   // tile rows per wave in the write-out
   if (EPI == FP8_SWIGLU) {
-    // B-tile column blocks of 32 alternate gate and up; four rows per step, 16 lanes per
-    // row, lane l the output columns 4l .. 4l+3 of nt*64 ..
-    const int l = lane & 15;
-    const int cgate = (l >> 3) * 16 + (l & 7), col = nt * 64 + 4 * l;
+    // B-tile column blocks of 32 alternate gate and up.  LPR = BN / 8 lanes per row, lane
+    // l the output columns 4l .. 4l+3 of the tile's BN / 2 (from nt * BN / 2), 64 / LPR
+    // rows per step
+    constexpr int LPR = BN / 8, RPS = 64 / LPR;
+    const int l = lane % LPR;
+    const int cgate = (l >> 3) * 16 + (l & 7), col = nt * (BN / 2) + 4 * l;
 #pragma unroll 2
-    for (int rr = 0; rr < 8; ++rr) {
-      const int r = wave * 32 + rr * 4 + (lane >> 4);
+    for (int rr = 0; rr < RPW / RPS; ++rr) {
+      const int r = wave * RPW + rr * RPS + lane / LPR;
       const int row = row_begin + r;
-      if (row >= row_end) continue;
-      const float4 gt = L4[r * 32 + (cgate ^ (r & 31))], up = L4[r * 32 + ((cgate + 8) ^ (r & 31))];
+      const bool live = row < row_end;
+      const float4 gt = L4[r * RC + (cgate ^ (r & 31))], up = L4[r * RC + ((cgate + 8) ^ (r & 31))];
       float4 act;
       act.x = glu_f(p.glu, gt.x, up.x); act.y = glu_f(p.glu, gt.y, up.y);
       act.z = glu_f(p.glu, gt.z, up.z); act.w = glu_f(p.glu, gt.w, up.w);
-      if (p.H) {
+      if (live && p.H) {
         float* hrow = p.H + static_cast<int64_t>(row) * 2 * p.F;
         *reinterpret_cast<float4*>(hrow + col) = gt;
         *reinterpret_cast<float4*>(hrow + p.F + col) = up;
       }
-      *reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.F + col) = act;
+      if constexpr (BN / 2 == 128) {
+        if (p.Cq) {
+          // the row's 128 Act columns of this tile are one quantisation block, held by
+          // the 32 lanes of this half-wave: the block amax, its scale and the codes by
+          // the rule of the standalone quantiser (quant_rows_kernel)
+          float amax = fmaxf(fmaxf(fabsf(act.x), fabsf(act.y)), fmaxf(fabsf(act.z), fabsf(act.w)));
+#pragma unroll
+          for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+          const float sc = block_scale(amax);
+          if (live) {
+            const uint32_t code = e4m3_code(__fdiv_rn(act.x, sc)) | (e4m3_code(__fdiv_rn(act.y, sc)) << 8) |
+                                  (e4m3_code(__fdiv_rn(act.z, sc)) << 16) | (e4m3_code(__fdiv_rn(act.w, sc)) << 24);
+            *reinterpret_cast<uint32_t*>(p.Cq + static_cast<int64_t>(row) * p.F + col) = code;
+            if (l == 0) p.Cq_scale[static_cast<int64_t>(row) * (p.F / 128) + nt] = sc;
+          }
+          continue;
+        }
+      }
+      if (live) *reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.F + col) = act;
     }
   } else {
-    // two rows per step, 32 lanes per row, lane l the columns 4l .. 4l+3 of nt*BN ..
-    const int l = lane & 31, col = nt * BN + 4 * l;
+    // 64 / RC rows per step, RC lanes per row, lane l the columns 4l .. 4l+3 of nt*BN ..
+    constexpr int RPS = 64 / RC;
+    const int l = lane % RC, col = nt * BN + 4 * l;
 #pragma unroll 4
-    for (int rr = 0; rr < 16; ++rr) {
-      const int r = wave * 32 + rr * 2 + (lane >> 5);
+    for (int rr = 0; rr < RPW / RPS; ++rr) {
+      const int r = wave * RPW + rr * RPS + lane / RC;
       const int row = row_begin + r;
       if (row >= row_end) continue;
-      *reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.N + col) = L4[r * 32 + (l ^ (r & 31))];
+      *reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.N + col) = L4[r * RC + (l ^ (r & 31))];
     }
   }
 }
 
+
+// One plain kernel per launched variant around the device-function body (the host pass
+// emitted no launch stubs for the body as a kernel template).
+#define MOE_FP8_KERNEL(NAME, EP, GT, BMV) \
+  __global__ __launch_bounds__(NTHR, 1) void NAME(const Fp8Args p) { fp8_gemm_body<EP, GT, BMV>(p); }
+MOE_FP8_KERNEL(fp8_gemm_swiglu_gather_256, FP8_SWIGLU, true, 256)
+MOE_FP8_KERNEL(fp8_gemm_swiglu_256, FP8_SWIGLU, false, 256)
+MOE_FP8_KERNEL(fp8_gemm_store_256, FP8_STORE, false, 256)
+MOE_FP8_KERNEL(fp8_gemm_swiglu_gather_128, FP8_SWIGLU, true, 128)
+MOE_FP8_KERNEL(fp8_gemm_swiglu_128, FP8_SWIGLU, false, 128)
+MOE_FP8_KERNEL(fp8_gemm_store_128, FP8_STORE, false, 128)
+#undef MOE_FP8_KERNEL
 
 }  // namespace
 
@@ -469,18 +526,30 @@ moe_status_t launch_gather_scales(const float* xs, const int32_t* token_of, int6
 size_t fp8_schedule_bytes(int E) { return static_cast<size_t>(E + 1) * 4; }
 
 // fc1 (+ SwiGLU -> H, Act fp32) when act32 != NULL and C is NULL, else fc2 -> C.
+int fp8_tile_rows(int64_t rows_upper, int G, int N, int F, bool swiglu) {
+  // 128-row tiles when the experts average fewer than 512 rows and the 256-wide column
+  // tile divides the output (fc1: F / 128 Act columns blocks; fc2: N)
+  const bool narrow_ok = swiglu ? F % 128 == 0 : N % 256 == 0;
+  return rows_upper < int64_t{512} * G && narrow_ok ? 128 : 256;
+}
+
 moe_status_t launch_gemm_fp8(bool swiglu, const uint8_t* A, const float* A_scale, const uint8_t* B,
                              const float* B_scale, float* C, float* H, const int32_t* offsets, int G, int64_t rows_upper,
                              int N, int K, int F, int32_t* sched, hipStream_t s, Glu glu, const int32_t* gather,
-                             int gather_rows) {
+                             int gather_rows, int bm, uint8_t* act_q, float* act_scale) {
   if (G > 4096) return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: more than 4096 experts");
   if (K > 128 * kMaxKB || K % 128 || N % 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: K must be a multiple of 128 up to 16384");
   if (static_cast<int64_t>(N) * K >= (int64_t{1} << 31) || rows_upper * K >= (int64_t{1} << 31))
     return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: operand above 2 GB");
+  if (bm != 128 && bm != 256) return fail(MOE_ERR_INVALID_ARG, "fp8 gemm: tile rows must be 128 or 256");
+  const int bn = TILE_AREA / bm;
+  if (swiglu ? F % (bn / 2) : N % bn) return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: output not a multiple of the tile");
+  if (act_q && !(swiglu && bm == 128)) return fail(MOE_ERR_INVALID_ARG, "fp8 gemm: fused Act codes need fc1 with 128-row tiles");
   Fp8Args a{};
   a.A = A; a.A_scale = A_scale; a.B = B; a.B_scale = B_scale; a.C = C; a.H = H;
+  a.Cq = act_q; a.Cq_scale = act_scale;
   a.offsets = offsets; a.tile_prefix = sched; a.G = G; a.N = N; a.K = K; a.F = F; a.glu = glu;
-  a.nN = swiglu ? F / 64 : N / BN;
+  a.nN = swiglu ? F / (bn / 2) : N / bn;
   if (gather) {
     if (!swiglu) return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: the row gather is for fc1");
     if (static_cast<int64_t>(gather_rows) * K > kOob - 4096)
@@ -489,17 +558,23 @@ moe_status_t launch_gemm_fp8(bool swiglu, const uint8_t* A, const float* A_scale
     a.gather_rows = gather_rows;
     a.gather_len = static_cast<int>(rows_upper);
   }
-  fp8_tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, G, sched);
-  const int64_t upper = (ceil_div(rows_upper, BM) + G) * a.nN;
+  fp8_tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, G, bm, sched);
+  const int64_t upper = (ceil_div(rows_upper, bm) + G) * a.nN;
   const int64_t grid = ceil_div(upper, 8) * 8;
   if (grid == 0) return MOE_OK;
-  if (swiglu && gather)
-    fp8_gemm_kernel<FP8_SWIGLU, true><<<grid, NTHR, 0, s>>>(a);
-  else if (swiglu)
-    fp8_gemm_kernel<FP8_SWIGLU, false><<<grid, NTHR, 0, s>>>(a);
-  else
-    fp8_gemm_kernel<FP8_STORE, false><<<grid, NTHR, 0, s>>>(a);
-  return check_launch("gemm_fp8");
+#define MOE_FP8(NAME, SW, GT, BMV)                                   \
+  if (SW == swiglu && GT == (gather != nullptr) && bm == BMV) {       \
+    NAME<<<static_cast<unsigned>(grid), NTHR, 0, s>>>(a);            \
+    return check_launch("gemm_fp8");                                  \
+  }
+  MOE_FP8(fp8_gemm_swiglu_gather_256, true, true, 256)
+  MOE_FP8(fp8_gemm_swiglu_256, true, false, 256)
+  MOE_FP8(fp8_gemm_store_256, false, false, 256)
+  MOE_FP8(fp8_gemm_swiglu_gather_128, true, true, 128)
+  MOE_FP8(fp8_gemm_swiglu_128, true, false, 128)
+  MOE_FP8(fp8_gemm_store_128, false, false, 128)
+#undef MOE_FP8
+  return fail(MOE_ERR_UNSUPPORTED, "fp8 gemm: unsupported variant");
 }
 
 }  // namespace moe

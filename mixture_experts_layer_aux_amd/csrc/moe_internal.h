@@ -84,11 +84,15 @@ moe_status_t launch_quantize_fp8(int src_dtype, const void* src, int64_t rows, i
 moe_status_t launch_gather_scales(const float* xs, const int32_t* token_of, int64_t A, int nb, float* out,
                                   hipStream_t s);
 size_t fp8_schedule_bytes(int E);
-// swiglu: fc1 of width N = 2F, Act (fp32) -> C [rows, F], H (optional); else C [rows, N]
+// swiglu: fc1 of width N = 2F, Act (fp32) -> C [rows, F], H (optional); else C [rows, N].
+// bm: tile rows, 256 (256 x 128 tiles) or 128 (128 x 256); fp8_tile_rows picks it.  With
+// bm 128, fc1 can write Act as e4m3 codes act_q [rows, F] and scales act_scale [rows, F/128]
+// (the rule of launch_quantize_fp8 with block_rows 1) in place of C.
+int fp8_tile_rows(int64_t rows_upper, int G, int N, int F, bool swiglu);
 moe_status_t launch_gemm_fp8(bool swiglu, const uint8_t* A, const float* A_scale, const uint8_t* B,
                              const float* B_scale, float* C, float* H, const int32_t* offsets, int G, int64_t rows_upper,
-                             int N, int K, int F, int32_t* sched, hipStream_t s, Glu glu = Glu{0, 0.0f, 0.0f},
-                             const int32_t* gather = nullptr, int gather_rows = 0);
+                             int N, int K, int F, int32_t* sched, hipStream_t s, Glu glu, const int32_t* gather,
+                             int gather_rows, int bm, uint8_t* act_q = nullptr, float* act_scale = nullptr);
 
 // ---------------------------------------------------------------- GEMMs
 // Storage of an operand: K_MAJOR = [rows][K] (K contiguous), MN_MAJOR = [K][rows].

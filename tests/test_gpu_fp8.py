@@ -228,6 +228,9 @@ FP8_EDGE = {
     "one_hot_expert": (replace(SHAPE, name="fp8-one-hot", T=256, skew_beta=40.0), 11),
     # SiTU-GLU in the fp8 fc1 epilogue (The Ultimate MoE Training Handbook, §3.4 Activation)
     "situ_glu": (replace(SHAPE, name="fp8-situ", T=300, glu="situ", glu_c=0.3, glu_c_linear=0.5), 11),
+    # 512 rows per expert on average: the GEMMs take 256 x 128 tiles and the standalone
+    # Act quantiser (the other cases take 128 x 256 tiles with Act quantised in fc1)
+    "few_experts": (replace(SHAPE, name="fp8-few-experts", E=32, T=1024), 11),
 }
 
 
