@@ -213,6 +213,11 @@ __device__ __forceinline__ void wait_vm_upto8(int n) {
   }
   asm volatile("" ::: "memory");
 }
+// Waits until this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0; vmcnt (63) and expcnt (7) at their maxima
+  asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -361,13 +366,24 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // Main loop, two wave groups in alternation (waves 0-3 and 4-7; wave w and w+4 share a
+  // SIMD): every stage is a memory phase (read the stage's fragments and scales into
+  // registers, issue this wave's DMA part of stage it+D, wait for its part of stage it+1)
+  // and a compute phase (matrix and scale instructions from registers only), each ended
+  // by a workgroup barrier.  The second group runs one phase behind the first, so on every
+  // SIMD one wave computes while the other reads and issues.  Slot reuse: stage it+D
+  // overwrites the slot of stage it-1, which both groups finished reading one barrier
+  // earlier.
+  constexpr int D = STAGES - 1;
+  const bool late = wave >= 4;
   const int nk = KB;
 #pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
+  for (int st = 0; st < D; ++st)
     if (st < nk) issue(st);
+  wait_vm_upto8(max(0, min(D, nk) - 1) * ndma);   // own part of stage 0 landed
+  block_barrier();
+  if (late) block_barrier();
   for (int it = 0; it < nk; ++it) {
-    wait_vm_upto8(min(STAGES - 2, nk - 1 - it) * ndma);
-    block_barrier();  // stage it is in LDS; stage it-1 is consumed
     const uint8_t* As = lds + (it % STAGES) * STAGE_BYTES;
     const uint8_t* Bs = As + A_BYTES;
     const float* Ss = reinterpret_cast<const float*>(As + A_BYTES + B_BYTES);
@@ -388,7 +404,12 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
     // the stage's reads go out before the next DMA is issued: the compiler would
     // otherwise wait for that DMA before any LDS read that follows it
     __builtin_amdgcn_sched_barrier(0);
-    if (it + STAGES - 1 < nk) issue(it + STAGES - 1);
+    if (it + D < nk) issue(it + D);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkm0();  // fragments and scales in registers before the slot may be refilled
+    wait_vm_upto8(max(0, min(it + D, nk - 1) - (it + 1)) * ndma);  // own part of stage it+1 landed
+    __builtin_amdgcn_sched_barrier(0);
+    block_barrier();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
@@ -401,7 +422,11 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = fmaf(t[e], f, acc[i][j][e]);
       }
+    __builtin_amdgcn_sched_barrier(0);
+    block_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (!late) block_barrier();
 
   // epilogue: acc[i][j][4q + c] is row wm*64 + i*32 + lane%32, column
   // wn*64 + j*32 + 8q + 4(lane/32) + c of the B tile.  The BM x BN fp32 tile goes through
@@ -410,7 +435,7 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
   constexpr int RC = BN / 4;   // 16-byte chunks per tile row
   float4* L4 = reinterpret_cast<float4*>(lds);
   static_assert(STAGES * STAGE_BYTES >= BM * BN * 4, "epilogue staging needs the tile in LDS");
-  block_barrier();  // every wave is done with the last stage
+  block_barrier();  // every wave is done with the last stage (and its DMA, waited above)
   const int cb = 4 * (lane >> 5);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
