@@ -55,7 +55,7 @@ struct FwdWs {
   int32_t* blk_base;   // [nchunk, E]
   int32_t* counts;     // [E]
   float* prob_sum;     // [E]
-  int32_t* sched;      // [E + 1]
+  int32_t* sched;      // tile schedule of the grouped GEMMs: [E + 1] prefix + owner table
   uint8_t* xq;         // fp8 experts: [T, d] e4m3 codes of x
   float* xs;           // fp8 experts: [T, d/128] their scales
   float* act32;        // fp8 experts: [A, F] fp32 SwiGLU output before quantisation
@@ -85,7 +85,8 @@ FwdWs carve_fwd(const moe_config_t& c, void* base) {
   w.blk_base = reinterpret_cast<int32_t*>(take(nch * c.E * 4));
   w.counts = reinterpret_cast<int32_t*>(take(static_cast<size_t>(c.E) * 4));
   w.prob_sum = reinterpret_cast<float*>(take(static_cast<size_t>(c.E) * 4));
-  w.sched = reinterpret_cast<int32_t*>(take(std::max(mfma_schedule_bytes(c.E), fp8_schedule_bytes(c.E))));
+  const int64_t rows = static_cast<int64_t>(c.T) * c.k;
+  w.sched = reinterpret_cast<int32_t*>(take(std::max(mfma_schedule_bytes(c.E, rows), fp8_schedule_bytes(c.E, rows))));
   w.xq = nullptr;
   w.xs = w.act32 = nullptr;
   if (c.w_dtype == MOE_FP8_E4M3) {
@@ -114,7 +115,7 @@ struct BwdWs {
   float* sg_part;  // shared_gate_part_bytes: partial sums of its weight gradient
   float* dact;     // fp32 path: [max(A, T), max(F, Fs)]
   float* wsplit;   // bf16 shared expert: split-K partials of its weight gradients (or NULL)
-  int32_t* sched;  // [E + 1]
+  int32_t* sched;  // tile schedule of the grouped GEMMs: [E + 1] prefix + owner table
   void* gate;      // router GEMM scratch (gate_bwd_ws_bytes)
   size_t bytes;
 };
@@ -145,7 +146,7 @@ BwdWs carve_bwd(const moe_config_t& c, void* base) {
                            ? std::max(wgrad_split_bytes(c.d, c.Fs, c.T), wgrad_split_bytes(2 * c.Fs, c.d, c.T))
                            : 0;
   w.wsplit = split ? reinterpret_cast<float*>(take(split)) : nullptr;
-  w.sched = reinterpret_cast<int32_t*>(take(mfma_schedule_bytes(c.E)));
+  w.sched = reinterpret_cast<int32_t*>(take(mfma_schedule_bytes(c.E, A)));
   w.gate = take(gate_bwd_ws_bytes(c));
   w.bytes = off;
   return w;

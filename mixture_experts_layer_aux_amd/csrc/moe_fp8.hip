@@ -180,7 +180,8 @@ struct Fp8Args {
   uint8_t* Cq;            // SWIGLU with 128-row tiles: Act e4m3 codes [rows, F] (C unused)
   float* Cq_scale;        //   and their scales [rows, F/128]
   const int32_t* offsets;
-  const int32_t* tile_prefix;
+  const int32_t* tile_prefix;   // prefix [G + 1], then the owner of each row tile [tile_cap]
+  int tile_cap;
   int G, N, K, F, nN;
   Glu glu;                // SWIGLU: the gated activation
   const int32_t* gather;  // GATHER: row r of A (and of A_scale) is row gather[r] of the given ones
@@ -224,10 +225,14 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The tile schedule: prefix[g] = row tiles of the experts before g (G + 1 entries), then
+// owner[m] = the expert of row tile m (cap entries; a count past cap is the caller's
+// broken offsets, and the writes stop there).
 __global__ __launch_bounds__(1024) void fp8_tile_prefix_kernel(const int32_t* __restrict__ offsets, int G, int bm,
-                                                               int32_t* __restrict__ prefix) {
+                                                               int cap, int32_t* __restrict__ prefix) {
   __shared__ int s[4096];
-  for (int g = threadIdx.x; g < 4096; g += 1024) s[g] = g < G ? (offsets[g + 1] - offsets[g] + bm - 1) / bm : 0;
+  for (int g = threadIdx.x; g < 4096; g += 1024)
+    s[g] = g < G ? max(0, (offsets[g + 1] - offsets[g] + bm - 1) / bm) : 0;
   __syncthreads();
   for (int off = 1; off < 4096; off <<= 1) {
     int a[4];
@@ -242,6 +247,9 @@ __global__ __launch_bounds__(1024) void fp8_tile_prefix_kernel(const int32_t* __
     __syncthreads();
   }
   for (int g = threadIdx.x; g <= G; g += 1024) prefix[g] = g == 0 ? 0 : s[g - 1];
+  int32_t* owner = prefix + G + 1;
+  for (int g = threadIdx.x; g < G; g += 1024)
+    for (int m = g ? s[g - 1] : 0; m < s[g] && m < cap; ++m) owner[m] = g;
 }
 
 constexpr int kMaxKB = 128;  // K <= 16384
@@ -264,17 +272,14 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
   // tile: workgroup h runs on XCD h % 8; each XCD walks a contiguous run of
   // (expert, column tile, row tile)
   const int h = blockIdx.x;
-  const int total = p.tile_prefix[p.G] * p.nN;
+  const int total = min(p.tile_prefix[p.G], p.tile_cap) * p.nN;
   const int chunk = (total + 7) >> 3;
   const int qh = h >> 3;
   const int L = (h & 7) * chunk + qh;
   if (qh >= chunk || L >= total) return;
-  int lo = 0, hi = p.G - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.tile_prefix[mid] * p.nN <= L) lo = mid; else hi = mid - 1;
-  }
-  const int g = lo;
+  // expert g owns tiles [prefix[g] nN, prefix[g+1] nN), so tile L's row-tile index L / nN
+  // lies in its range: one lookup in the owner table
+  const int g = min(max(p.tile_prefix[p.G + 1 + L / p.nN], 0), p.G - 1);
   const int base = p.tile_prefix[g];
   const int mtiles = p.tile_prefix[g + 1] - base;
   const int local = L - base * p.nN;
@@ -290,6 +295,22 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
   auto brow = [&](int r) -> int {
     return EPI == FP8_SWIGLU ? (((r >> 5) & 1) ? p.F : 0) + nt * (BN / 2) + (r >> 6) * 32 + (r & 31) : nt * BN + r;
   };
+  // The weight-block scales of this tile per K block (every wave's fragment j lies in one
+  // 128-row block of the weights), staged in LDS once.  Their loads go out first, so that
+  // their latency overlaps the offsets' set-up and the first stages' DMA; they reach LDS
+  // with the wait for stage 0.
+  constexpr int NBS = (WAVES_N * NJ * kMaxKB + NTHR - 1) / NTHR;   // per thread, at most
+  float bsv[NBS];
+#pragma unroll
+  for (int u = 0; u < NBS; ++u) {
+    const int t = tid + u * NTHR;
+    bsv[u] = 0.0f;
+    if (t < WAVES_N * NJ * KB) {
+      const int wj = t / KB, kb = t - wj * KB;
+      const int w = wj / NJ, j = wj - w * NJ;
+      bsv[u] = Bsg[(brow(w * 64 + j * 32) / 128) * KB + kb];
+    }
+  }
   // per-lane DMA offsets (bytes from the stage's base)
   int voffA[A_DMA], voffB[B_DMA];
 #pragma unroll
@@ -348,15 +369,6 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
                        static_cast<int>(v1.x), static_cast<int>(v1.y), static_cast<int>(v1.z), static_cast<int>(v1.w)};
     return v;
   };
-  // The weight-block scales of this tile (every wave's fragment j falls in the same
-  // 128-row block), staged in LDS once: loaded per K block in the loop they would be
-  // vector loads whose waits would also wait for the stage DMA issued before them.
-  for (int t = tid; t < WAVES_N * NJ * KB; t += NTHR) {
-    const int wj = t / KB, kb = t - wj * KB;
-    const int w = wj / NJ, j = wj - w * NJ;
-    s_bs[w][j][kb] = Bsg[(brow(w * 64 + j * 32) / 128) * KB + kb];
-  }
-  __syncthreads();
 
   f32x16_t acc[NI][NJ];
 #pragma unroll
@@ -380,7 +392,16 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
 #pragma unroll
   for (int st = 0; st < D; ++st)
     if (st < nk) issue(st);
+#pragma unroll
+  for (int u = 0; u < NBS; ++u) {
+    const int t = tid + u * NTHR;
+    if (t < WAVES_N * NJ * KB) {
+      const int wj = t / KB, kb = t - wj * KB;
+      s_bs[wj / NJ][wj % NJ][kb] = bsv[u];
+    }
+  }
   wait_vm_upto8(max(0, min(D, nk) - 1) * ndma);   // own part of stage 0 landed
+  wait_lgkm0();                                   // the scales written
   block_barrier();
   if (late) block_barrier();
   for (int it = 0; it < nk; ++it) {
@@ -548,7 +569,10 @@ moe_status_t launch_gather_scales(const float* xs, const int32_t* token_of, int6
   return check_launch("gather_scales");
 }
 
-size_t fp8_schedule_bytes(int E) { return static_cast<size_t>(E + 1) * 4; }
+namespace {
+int64_t fp8_tile_cap(int E, int64_t rows) { return ceil_div(rows, int64_t{128}) + E; }
+}
+size_t fp8_schedule_bytes(int E, int64_t rows) { return static_cast<size_t>(E + 1 + fp8_tile_cap(E, rows)) * 4; }
 
 // fc1 (+ SwiGLU -> H, Act fp32) when act32 != NULL and C is NULL, else fc2 -> C.
 int fp8_tile_rows(int64_t rows_upper, int G, int N, int F, bool swiglu) {
@@ -583,7 +607,8 @@ moe_status_t launch_gemm_fp8(bool swiglu, const uint8_t* A, const float* A_scale
     a.gather_rows = gather_rows;
     a.gather_len = static_cast<int>(rows_upper);
   }
-  fp8_tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, G, bm, sched);
+  a.tile_cap = static_cast<int>(ceil_div(rows_upper, int64_t{bm}) + G);
+  fp8_tile_prefix_kernel<<<1, 1024, 0, s>>>(offsets, G, bm, a.tile_cap, sched);
   const int64_t upper = (ceil_div(rows_upper, bm) + G) * a.nN;
   const int64_t grid = ceil_div(upper, 8) * 8;
   if (grid == 0) return MOE_OK;

@@ -89,7 +89,8 @@ struct MfmaArgs {
   const float* H;
   int64_t ldh;
   const int32_t* offsets;
-  const int32_t* tile_prefix;
+  const int32_t* tile_prefix;   // prefix [G + 1], then the owner of each row tile [tile_cap]
+  int tile_cap;
   int G, M, N, K, F, range_end, nN, nM;
   int b_rows_bytes;  // K-major B: bytes of one group's weight matrix (bounds the DMA)
   Glu glu;           // SwiGLU epilogues: the gated activation
@@ -173,11 +174,13 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 // Tiles of a row-ragged launch: group g has ceil(rows_g / 256) row tiles.
-__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ offsets, int G,
+// prefix [G + 1] of the row tiles, then owner[m] = the group of row tile m (cap entries;
+// a count past cap is the caller's broken offsets, and the writes stop there).
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ offsets, int G, int cap,
                                                            int32_t* __restrict__ prefix) {
   __shared__ int s[2048];
   for (int g = threadIdx.x; g < 2048; g += 1024)
-    s[g] = g < G ? (offsets[g + 1] - offsets[g] + BM - 1) / BM : 0;
+    s[g] = g < G ? max(0, (offsets[g + 1] - offsets[g] + BM - 1) / BM) : 0;
   __syncthreads();
   for (int off = 1; off < 2048; off <<= 1) {
     const int i0 = threadIdx.x, i1 = threadIdx.x + 1024;
@@ -189,6 +192,9 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
     __syncthreads();
   }
   for (int g = threadIdx.x; g <= G; g += 1024) prefix[g] = g == 0 ? 0 : s[g - 1];
+  int32_t* owner = prefix + G + 1;
+  for (int g = threadIdx.x; g < G; g += 1024)
+    for (int m = g ? s[g - 1] : 0; m < s[g] && m < cap; ++m) owner[m] = g;
 }
 
 // Byte offset past the end of every gathered operand (bounded below 2^31 at launch): a
@@ -220,21 +226,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
   int k_begin, k_end;
   if (RAG == RAGGED_M) {
     const int h = blockIdx.x;
-    const int total_m = p.offsets ? p.tile_prefix[p.G] : (p.range_end + BM - 1) / BM;
+    const int total_m = p.offsets ? min(p.tile_prefix[p.G], p.tile_cap) : (p.range_end + BM - 1) / BM;
     const int total = total_m * p.nN;
     const int chunk = (total + 7) >> 3;
     const int q = h >> 3;
     const int L = (h & 7) * chunk + q;
     if (q >= chunk || L >= total) return;
-    int g = 0;
-    if (p.offsets) {
-      int lo = 0, hi = p.G - 1;  // largest g with prefix[g] * nN <= L
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (p.tile_prefix[mid] * p.nN <= L) lo = mid; else hi = mid - 1;
-      }
-      g = lo;
-    }
+    // group g owns tiles [prefix[g] nN, prefix[g+1] nN), so the row-tile index L / nN of
+    // tile L lies in its range: one lookup in the owner table
+    const int g = p.offsets ? min(max(p.tile_prefix[p.G + 1 + L / p.nN], 0), p.G - 1) : 0;
     const int base = p.offsets ? p.tile_prefix[g] : 0;
     const int mtiles = p.offsets ? p.tile_prefix[g + 1] - base : total_m;
     const int local = L - base * p.nN;
@@ -744,7 +744,9 @@ void launch_kernel(const MfmaArgs& a, int64_t grid, hipStream_t s) {
 
 }  // namespace
 
-size_t mfma_schedule_bytes(int G) { return static_cast<size_t>(G + 1) * sizeof(int32_t); }
+size_t mfma_schedule_bytes(int G, int64_t rows) {
+  return static_cast<size_t>(G + 1 + ceil_div(rows, int64_t{BM}) + G) * sizeof(int32_t);
+}
 
 // A one-group weight gradient whose output has fewer than 128 tiles (a shared expert's
 // narrow projections: 32 or 16 tiles on a chip of 256 CUs) is split over its reduction
@@ -823,7 +825,8 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
     a.nN = static_cast<int>(g.epi == EPI_SWIGLU_FWD ? ceil_div(g.N, 256) : ceil_div(g.N, BN));
     int64_t upper;
     if (g.offsets) {
-      tile_prefix_kernel<<<1, 1024, 0, s>>>(g.offsets, g.G, sched);
+      a.tile_cap = static_cast<int>(ceil_div(g.rows_upper, int64_t{BM}) + g.G);
+      tile_prefix_kernel<<<1, 1024, 0, s>>>(g.offsets, g.G, a.tile_cap, sched);
       upper = (ceil_div(g.rows_upper, BM) + g.G) * a.nN;
     } else {
       upper = ceil_div(g.range_end, BM) * a.nN;

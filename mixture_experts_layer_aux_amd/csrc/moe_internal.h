@@ -83,7 +83,7 @@ moe_status_t launch_quantize_fp8(int src_dtype, const void* src, int64_t rows, i
                                  float* scale, hipStream_t s);
 moe_status_t launch_gather_scales(const float* xs, const int32_t* token_of, int64_t A, int nb, float* out,
                                   hipStream_t s);
-size_t fp8_schedule_bytes(int E);
+size_t fp8_schedule_bytes(int E, int64_t rows);   // rows: the upper bound of the grouped rows
 // swiglu: fc1 of width N = 2F, Act (fp32) -> C [rows, F], H (optional); else C [rows, N].
 // bm: tile rows, 256 (256 x 128 tiles) or 128 (128 x 256); fp8_tile_rows picks it.  With
 // bm 128, fc1 can write Act as e4m3 codes act_q [rows, F] and scales act_scale [rows, F/128]
@@ -143,7 +143,7 @@ moe_status_t launch_swiglu_bwd_elementwise(Glu glu, const float* H, const float*
                                            hipStream_t s);
 
 // bf16 MFMA grouped GEMM (gfx950 v_mfma_f32_32x32x16_bf16), fused epilogues.
-size_t mfma_schedule_bytes(int G);
+size_t mfma_schedule_bytes(int G, int64_t rows);  // rows: the upper bound of the grouped rows
 moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched_ws, hipStream_t s);
 // Split-K of a one-group weight gradient dW [M, N] over `rows` reduction rows: the row
 // chunk (a multiple of 64) and the number of chunks, 1 when the output alone has enough
