@@ -15,14 +15,15 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
-// Round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+// Round to nearest, ties to even, in one v_cvt_pk_bf16_f32 per pair of values.
+typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_cvt_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2_cvt_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_cvt_t));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.0f));
 }
 
 // Element access for the two activation storage types.

@@ -225,6 +225,13 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// A barrier after LDS writes that other waves read next: s_barrier does not wait for this
+// wave's own LDS operations to complete.
+__device__ __forceinline__ void lds_barrier() {
+  wait_lgkm0();
+  block_barrier();
+}
+
 // The tile schedule: prefix[g] = row tiles of the experts before g (G + 1 entries), then
 // owner[m] = the expert of row tile m (cap entries; a count past cap is the caller's
 // broken offsets, and the writes stop there).
@@ -470,7 +477,7 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
             make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       }
   }
-  block_barrier();
+  lds_barrier();
   constexpr int RPW = BM / NWAVES;   // tile rows per wave in the write-out
   if (EPI == FP8_SWIGLU) {
     // B-tile column blocks of 32 alternate gate and up.  LPR = BN / 8 lanes per row, lane

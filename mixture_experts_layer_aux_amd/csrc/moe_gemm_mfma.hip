@@ -173,6 +173,13 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// A barrier after LDS writes that other waves read next: s_barrier does not wait for this
+// wave's own LDS operations to complete.
+__device__ __forceinline__ void lds_barrier() {
+  wait_lgkm0();
+  block_barrier();
+}
+
 // Tiles of a row-ragged launch: group g has ceil(rows_g / 256) row tiles.
 // prefix [G + 1] of the row tiles, then owner[m] = the group of row tile m (cap entries;
 // a count past cap is the caller's broken offsets, and the writes stop there).
@@ -609,7 +616,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
                                                        pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
           }
       }
-      block_barrier();
+      lds_barrier();
       const int col = n0 + 4 * lane;
 #pragma unroll 4
       for (int rr = 0; rr < BM / NWAVES; ++rr) {
@@ -637,7 +644,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
               make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         }
     }
-    block_barrier();
+    lds_barrier();
     if (EPI == EPI_SWIGLU_FWD) {
       // tile column blocks of 32 alternate gate and up (block 2b gate, 2b + 1 up, for
       // output columns nt*128 + 32b ..); two rows per step, 32 lanes per row, lane l the

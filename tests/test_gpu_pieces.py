@@ -280,6 +280,50 @@ def check_grouped_experts(shape, cid):
                 check_wgrad(f"dW2s{tag}", g2, o["dy"], acts, 0, 1)
 
 
+def test_grouped_gemms_repeat_bit_identical():
+    """Every grouped GEMM of the reduced DeepSeek-V3-shaped layer (the experts' forward,
+    data gradients, and weight gradients with the token rows read through token_of and from
+    the grouped copy) gives the same bits on every repeat.  The epilogues stage tiles through
+    the LDS; a barrier that does not wait for a wave's LDS writes lets another wave read a
+    stale value now and then."""
+    torch = torch_mod()
+    L = _lib()
+    shape = W.SMALL[3]
+    cfg = L.config_from_shape(shape)
+    inp, o, r, p = _expert_inputs(shape, 3)
+    T, E, d, F, Fs, A = shape.T, shape.E, shape.d, shape.F, shape.Fs, shape.A
+    x = to_dev(inp["x"])
+    tok = to_dev(p.token_of.astype(np.int32))
+    x_perm = x[tok.long()].contiguous()
+    off = to_dev(p.offsets.astype(np.int32))
+    W13, W2 = to_dev(inp["W13"]), to_dev(inp["W2"])
+    W13s, W2s = to_dev(inp["W13s"]), to_dev(inp["W2s"])
+    dy = to_dev(inp["dy"])
+    dYp = to_dev(W.random_rows(A, d, seed=103, act=shape.act))
+    ws = L.alloc_workspace(cfg, dev())
+    bf, f32 = torch.bfloat16, torch.float32
+    e = lambda *s_, dt=bf: torch.empty(*s_, dtype=dt, device=dev())  # noqa: E731
+
+    def run():
+        H, Act, Yp = e(A, 2 * F, dt=f32), e(A, F), e(A, d, dt=f32)
+        H_s, Act_s, Y_s = e(T, 2 * Fs, dt=f32), e(T, Fs), e(T, d, dt=f32)
+        L.grouped_gemm_swiglu(cfg, None, off, W13, W2, x, W13s, W2s, H, Act, Yp, H_s, Act_s, Y_s, ws, token_of=tok)
+        dH, dXp, dW13, dW2 = e(A, 2 * F), e(A, d, dt=f32), e(E, 2 * F, d), e(E, d, F)
+        dH_s, dx_s, dW13s, dW2s = e(T, 2 * Fs), e(T, d, dt=f32), e(2 * Fs, d), e(d, Fs)
+        L.grouped_gemm_swiglu_bwd(cfg, None, off, W13, W2, H, Act, dYp, dH, dXp, dW13, dW2, x, W13s, W2s, H_s, Act_s,
+                                  dy, dH_s, dx_s, dW13s, dW2s, ws, token_of=tok)
+        cW13 = e(E, 2 * F, d)
+        L.grouped_wgrad(cfg, off, E, A, dH, 2 * F, x_perm, d, cW13)
+        return [H, Act, Yp, Y_s, dH, dXp, dW13, dW2, dx_s, dW13s, dW2s, cW13]
+
+    ref = run()
+    for rep in range(12):
+        got = run()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(ref, got)):
+            assert torch.equal(a, b), f"repeat {rep}: output {i} changed"
+
+
 @pytest.mark.parametrize("cid", SMALL_IDS)
 def test_combine_and_backward_pieces(cid):
     torch = torch_mod()
