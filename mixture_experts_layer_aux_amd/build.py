@@ -17,8 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
-SOURCES = ["moe_abi.hip", "moe_router.hip", "moe_permute.hip", "moe_gemm_fma.hip", "moe_gemm_mfma.hip", "moe_fp8.hip", "moe_gate.hip",
-           "moe_quantile.hip"]
+SOURCES = ["moe_abi.hip", "moe_router.hip", "moe_permute.hip", "moe_gemm_fma.hip", "moe_gemm_mfma.hip",
+           "moe_wgrad.hip", "moe_fp8.hip", "moe_gate.hip", "moe_quantile.hip"]
 # Packed fp32 arithmetic is disabled for all device code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]

@@ -404,7 +404,7 @@ moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G
     if (act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "gathered weight gradients need bf16 activations");
     w.gather = x_rows;
     w.gather_rows = x_src_rows;
-    return launch_gemm_mfma(w, nullptr, s);
+    return wgrad2_supported(w) ? launch_wgrad2(w, s) : launch_gemm_mfma(w, nullptr, s);
   }
   if (act_dtype == MOE_BF16 && !off && split_ws) {
     const WgradSplit sp = wgrad_split(N, K, rows);

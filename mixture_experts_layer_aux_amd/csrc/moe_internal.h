@@ -145,6 +145,10 @@ moe_status_t launch_swiglu_bwd_elementwise(Glu glu, const float* H, const float*
 // bf16 MFMA grouped GEMM (gfx950 v_mfma_f32_32x32x16_bf16), fused epilogues.
 size_t mfma_schedule_bytes(int G, int64_t rows);  // rows: the upper bound of the grouped rows
 moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched_ws, hipStream_t s);
+// Reduction-ragged bf16 weight gradients (both operands row-contiguous, no split-K) on
+// 256 x 128 tiles of 4 waves, two workgroups per CU (moe_wgrad.hip).
+bool wgrad2_supported(const GemmDesc& g);
+moe_status_t launch_wgrad2(const GemmDesc& g, hipStream_t s);
 // Split-K of a one-group weight gradient dW [M, N] over `rows` reduction rows: the row
 // chunk (a multiple of 64) and the number of chunks, 1 when the output alone has enough
 // tiles to fill the chip (then kchunk = rows).  Partials: chunks * M * N fp32.
