@@ -406,6 +406,10 @@ moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G
     w.gather_rows = x_src_rows;
     return wgrad2_supported(w) ? launch_wgrad2(w, s) : launch_gemm_mfma(w, nullptr, s);
   }
+  // per-expert gradients: many short reductions, each tile's fixed cost hidden by a second
+  // workgroup on the CU.  Gradients with fewer than 1024 columns (fc2's at F = 512) are
+  // faster on the 256 x 256 tiles, which read dY half as often.
+  if (act_dtype == MOE_BF16 && off && K >= 1024 && wgrad2_supported(w)) return launch_wgrad2(w, s);
   if (act_dtype == MOE_BF16 && !off && split_ws) {
     const WgradSplit sp = wgrad_split(N, K, rows);
     if (sp.chunks > 1) {
