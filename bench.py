@@ -36,9 +36,9 @@ PHASES = ["gate", "router", "permute", "experts_fwd", "combine", "combine_bwd", 
           "wgrad_fc1", "wgrad_shared", "router_bwd", "gate_bwd", "unpermute_reduce"]
 GEMM_PHASES = ["experts_fwd", "experts_bwd_data", "wgrad_fc2", "wgrad_fc1", "wgrad_shared"]
 # The kernel the roofline object reports: the routed fc1 weight gradient, one launch of the
-# grouped GEMM with a ragged reduction, the longest single kernel of the step.
+# reduction-ragged weight-gradient kernel, the longest single kernel of the step.
 ROOFLINE_PHASE = "wgrad_fc1"
-GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_aux_amd", "csrc", "moe_gemm_mfma.hip")
+ROOFLINE_SOURCE = os.path.join(ROOT, "mixture_experts_layer_aux_amd", "csrc", "moe_wgrad.hip")
 
 
 def algorithmic(shape, wgrad_bytes=4):
@@ -76,8 +76,8 @@ def algorithmic(shape, wgrad_bytes=4):
 
 def measured_traffic(shape):
     """HBM bytes per launch of the roofline kernel from the committed rocprofv3 counter
-    summary, or None when there is none for this layer or the GEMM source has changed since
-    the counters were taken (the summary records the source's sha256)."""
+    summary, or None when there is none for this layer or the kernel's source has changed
+    since the counters were taken (the summary records the source's sha256)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"wgrad_fc1_{shape.name}.md")
     if not os.path.exists(path):
@@ -88,9 +88,9 @@ def measured_traffic(shape):
             if line.startswith("- ") and ": " in line:
                 key, val = line[2:].split(": ", 1)
                 fields[key.strip("` ")] = val.strip().strip("`")
-    with open(GEMM_SOURCE, "rb") as f:
+    with open(ROOFLINE_SOURCE, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
-    if fields.get("gemm_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -103,9 +103,9 @@ def roofline(alg, ms, peak_tflops, shape, wgrad_name="fp32"):
     t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
     s = ms * 1e-3
     x_rows = "the token rows of x through token_of" if shape.act == "bf16" else "x_perm"
-    common = dict(kernel=f"routed fc1 weight gradient dW13 = dH^T X, X = {x_rows} (one grouped-GEMM launch, "
-                         f"bf16 MFMA, {wgrad_name} output)", launch_ms=round(ms, 4), flop_per_launch=flop,
-                  bytes_per_launch=int(nbytes),
+    common = dict(kernel=f"routed fc1 weight gradient dW13 = dH^T X, X = {x_rows} (one launch of the "
+                         f"reduction-ragged weight-gradient kernel, bf16 MFMA, {wgrad_name} output)",
+                  launch_ms=round(ms, 4), flop_per_launch=flop, bytes_per_launch=int(nbytes),
                   mfma_frac=round(flop / s / 1e12 / peak_tflops, 4), hbm_frac=round(nbytes / s / 1e9 / PEAK_HBM_GBPS, 4))
     if t_hbm >= t_mfma:
         gbps = nbytes / s / 1e9
