@@ -404,7 +404,7 @@ moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G
     if (act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "gathered weight gradients need bf16 activations");
     w.gather = x_rows;
     w.gather_rows = x_src_rows;
-    return wgrad2_supported(w) ? launch_wgrad2(w, s) : launch_gemm_mfma(w, nullptr, s);
+    return launch_wgrad2(w, s);   // (fails with MOE_ERR_UNSUPPORTED on dimensions not multiples of 8)
   }
   // per-expert gradients: many short reductions, each tile's fixed cost hidden by a second
   // workgroup on the CU.  Gradients with fewer than 1024 columns (fc2's at F = 512) are

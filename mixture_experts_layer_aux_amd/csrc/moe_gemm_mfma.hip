@@ -126,32 +126,6 @@ __device__ __forceinline__ void wait_vm(int n) {
   else __builtin_amdgcn_s_waitcnt(0x0F70);
   asm volatile("" ::: "memory");
 }
-// Waits until at most n (0..15) of this wave's buffer loads are outstanding, exactly.
-template <int N>
-__device__ __forceinline__ void wait_vm_const() {
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void wait_vm_exact(int n) {
-  switch (n < 0 ? 0 : n) {
-    case 0: wait_vm_const<0>(); break;
-    case 1: wait_vm_const<1>(); break;
-    case 2: wait_vm_const<2>(); break;
-    case 3: wait_vm_const<3>(); break;
-    case 4: wait_vm_const<4>(); break;
-    case 5: wait_vm_const<5>(); break;
-    case 6: wait_vm_const<6>(); break;
-    case 7: wait_vm_const<7>(); break;
-    case 8: wait_vm_const<8>(); break;
-    case 9: wait_vm_const<9>(); break;
-    case 10: wait_vm_const<10>(); break;
-    case 11: wait_vm_const<11>(); break;
-    case 12: wait_vm_const<12>(); break;
-    case 13: wait_vm_const<13>(); break;
-    case 14: wait_vm_const<14>(); break;
-    default: wait_vm_const<15>(); break;
-  }
-}
 // Transposing LDS read of 4 bf16 (ds_read_b64_tr_b16).  The restrict parameter gives the
 // read alias-scope information; without it the compiler cannot tell the read apart from
 // the LDS-DMA writes still in flight and waits for all of them (vmcnt 0) before every
@@ -210,18 +184,11 @@ constexpr int kOob = 0x7FFFFFF0;
 
 // GA: 0 = operands as given; 1 = K-contiguous A of a row-ragged launch read through a row
 // gather (grouped row r of the tile from row gather[r] of A: the fc1 forward on the token
-// rows); 2 = row-contiguous B of a reduction-ragged launch read through a gather of its
-// reduction rows (row k from row gather[k] of B: the fc1 weight gradient on the token
-// rows).  With GA 2 each stage's gather indices come through the LDS like the operands:
-// the indices of stage x + D are DMA'd with stage x, so they have landed when stage x + D
-// is issued.
+// rows).  The fc1 weight gradient over the token rows runs on moe_wgrad.hip.
 template <int AMAJ, int BMAJ, int RAG, int EPI, bool OUT_F32, int GA>
 __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
-  static_assert(GA == 0 || (GA == 1 && AMAJ == K_MAJOR && RAG == RAGGED_M) ||
-                    (GA == 2 && BMAJ == MN_MAJOR && RAG == RAGGED_K && PING_PONG),
-                "unsupported gather");
+  static_assert(GA == 0 || (GA == 1 && AMAJ == K_MAJOR && RAG == RAGGED_M), "unsupported gather");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE_ELEMS];
-  __shared__ int32_t tok_lds[4][64];   // GA 2: gather indices of 4 stages (64 loaded, BK used)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -331,9 +298,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
                      (a_rows - 1) * static_cast<int>(p.lda) * 2 + BK * 2);
     else
       ra = make_rsrc(p.A + static_cast<int64_t>(k0) * p.lda, min(BK, k_end - k0) * static_cast<int>(p.lda) * 2);
-    if (GA == 2)
-      rb = make_rsrc(Bg, p.gather_rows * static_cast<int>(p.ldb) * 2);
-    else if (BMAJ == K_MAJOR)
+    if (BMAJ == K_MAJOR)
       rb = make_rsrc(Bg + k0, p.b_rows_bytes - k0 * 2);
     else
       rb = make_rsrc(Bg + static_cast<int64_t>(k0) * p.ldb, min(BK, k_end - k0) * static_cast<int>(p.ldb) * 2);
@@ -355,33 +320,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
     stage_rsrc(st, ra, rb);
 #pragma unroll
     for (int q = 0; q < NDMA; ++q) issue_one(st, q, ra, rb);
-  };
-  // GA 2: this wave's B rows of a stage (block q: stage row kr_of(q)), their byte offsets
-  // from the gathered source rows, and the DMA of a stage's gather indices into its slot.
-  auto kr_of = [&](int q) { return (wave * DMA_PER_WAVE + q) * 2 + (lane >> 5); };
-  auto gathered_voff = [&](int st, int q, int src) {
-    const int kr = kr_of(q);
-    const int c = (lane & 31) ^ swm(kr);
-    return (k_begin + st * BK + kr < k_end && src >= 0) ? src * static_cast<int>(p.ldb) * 2 + (n0 + c * 8) * 2
-                                                          : kOob;
-  };
-  auto issue_tok = [&](int st) {   // indices of stage st -> tok_lds[st % 4] (all waves alike)
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.gather, p.gather_len * 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void_t*)(&tok_lds[st & 3][0]), 4,
-                                             (k_begin + st * BK + lane) * 4, 0, 0, 0);
-  };
-  // GA 2: stage st issued: its indices were DMA'd with stage st - D (or loaded directly
-  // for the first D stages), the indices of stage st + D go out with it
-  auto issue_stage_gathered = [&](int st, const int (&src)[DMA_PER_WAVE]) {
-    __amdgpu_buffer_rsrc_t ra, rb;
-    stage_rsrc(st, ra, rb);
-    if (st + (STAGES - 1) < (k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0)) issue_tok(st + (STAGES - 1));
-#pragma unroll
-    for (int q = 0; q < DMA_PER_WAVE; ++q) issue_one(st, q, ra, rb);
-#pragma unroll
-    for (int q = 0; q < DMA_PER_WAVE; ++q) voffB[q] = gathered_voff(st, q, src[q]);
-#pragma unroll
-    for (int q = DMA_PER_WAVE; q < NDMA; ++q) issue_one(st, q, ra, rb);
   };
 
   // ------------------------------------------------------------ LDS -> fragments
@@ -451,41 +389,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
     // fragment reads and MFMAs are skipped (the loads still run, every wave takes its part
     // of each stage's DMA).  Wave-uniform, so the skip is a scalar branch.
     const int vi = __builtin_amdgcn_readfirstlane(min(NI, max(0, (row_end - row_begin - wm * WTM + 31) / 32)));
-    // GA 2: loads of this wave that follow stage x's DMA, from stage x + 1 up to stage last
-    auto after_stage = [&](int x, int last) {
-      int n = 0;
-      for (int y = x + 1; y <= last; ++y) n += NDMA + (y + D < nk ? 1 : 0);
-      return n;
-    };
-    // GA 2: gather indices of the next stage to issue, read from LDS one phase ahead (in
-    // the compute phase before the memory phase that issues it), so that the memory
-    // phase does not wait on the LDS.  The indices of stage x + D land with stage x.
-    int nsrc[DMA_PER_WAVE];
-    auto read_tok = [&](int st) {
 #pragma unroll
-      for (int q = 0; q < DMA_PER_WAVE; ++q) nsrc[q] = tok_lds[st & 3][kr_of(q)];
-    };
-    if constexpr (GA == 2) {
-      // the first D stages' indices straight from memory, then those stages
-      int src0[D][DMA_PER_WAVE];
-#pragma unroll
-      for (int st = 0; st < D; ++st)
-#pragma unroll
-        for (int q = 0; q < DMA_PER_WAVE; ++q) {
-          const int row = k_begin + st * BK + kr_of(q);
-          src0[st][q] = row < k_end && row < p.gather_len ? p.gather[row] : -1;
-        }
-#pragma unroll
-      for (int st = 0; st < D; ++st)
-        if (st < nk) issue_stage_gathered(st, src0[st]);
-      wait_vm_exact(after_stage(0, min(D, nk) - 1));
-      if (D < nk) read_tok(D);   // stage 0 (and the indices of stage D with it) landed
-    } else {
-#pragma unroll
-      for (int st = 0; st < D; ++st)
-        if (st < nk) issue_stage(st);
-      wait_vm(max(0, min(D, nk) - 1) * NDMA);
-    }
+    for (int st = 0; st < D; ++st)
+      if (st < nk) issue_stage(st);
+    wait_vm(max(0, min(D, nk) - 1) * NDMA);
     block_barrier();
     if (late) block_barrier();
     // FULL: every block of the wave is live (all but the last row tile of a group); the
@@ -504,22 +411,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
 #pragma unroll
           for (int j = 0; j < NJ; ++j) fb[ks][j] = frag(Bs, BMAJ, wn * WTN + j * 32, ks);
         }
-        if constexpr (GA == 2) {
-          if (it + D < nk) issue_stage_gathered(it + D, nsrc);
-          wait_lgkm0();
-          wait_vm_exact(after_stage(it + 1, min(it + D, nk - 1)));  // own part of stage it+1 landed
-        } else {
-          if (it + D < nk) issue_stage(it + D);
-          wait_lgkm0();  // fragments in registers before the slot may be refilled
-          wait_vm(max(0, min(it + D, nk - 1) - (it + 1)) * NDMA);  // own part of stage it+1 landed
-        }
+        if (it + D < nk) issue_stage(it + D);
+        wait_lgkm0();  // fragments in registers before the slot may be refilled
+        wait_vm(max(0, min(it + D, nk - 1) - (it + 1)) * NDMA);  // own part of stage it+1 landed
         __builtin_amdgcn_sched_barrier(0);
         block_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        // GA 2: stage it+1 (and the indices of stage it+1+D with it) landed at the wait
-        // above; their slot is next refilled two phases from now
-        if constexpr (GA == 2)
-          if (it + 1 + D < nk) read_tok(it + 1 + D);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
@@ -529,7 +426,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
               for (int j = 0; j < NJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
             }
-        if constexpr (GA == 2) wait_lgkm0();   // the index reads returned before the slot is refilled
         __builtin_amdgcn_sched_barrier(0);
         block_barrier();
         __builtin_amdgcn_sched_barrier(0);
@@ -811,12 +707,12 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
   a.kchunk = g.kchunk;
   int ga = 0;
   if (g.gather) {
-    ga = g.ragged == RAGGED_M ? 1 : 2;
-    if (ga == 1 && g.a_major != K_MAJOR) return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: gathered A must be K-contiguous");
-    if (ga == 2 && (g.b_major != MN_MAJOR || g.kchunk))
-      return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: gathered B must be row-contiguous, without split-K");
-    const int64_t ld = ga == 1 ? g.lda : g.ldb;
-    if (static_cast<int64_t>(g.gather_rows) * ld * 2 > kOob - 4096)
+    // the row gather is for the K-contiguous A of a row-ragged launch (the fc1 forward);
+    // a gathered weight gradient runs on moe_wgrad.hip
+    if (g.ragged != RAGGED_M || g.a_major != K_MAJOR)
+      return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: only a row-ragged launch's K-contiguous A can be gathered");
+    ga = 1;
+    if (static_cast<int64_t>(g.gather_rows) * g.lda * 2 > kOob - 4096)
       return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: gathered operand above 2 GB");
     a.gather = g.gather;
     a.gather_rows = g.gather_rows;
@@ -858,8 +754,6 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
   MOE_MF(K_MAJOR, MN_MAJOR, RAGGED_M, EPI_STORE, true, 0)        // fc1 data gradient -> dX (fp32)
   MOE_MF(MN_MAJOR, MN_MAJOR, RAGGED_K, EPI_STORE, true, 0)       // weight gradients (fp32)
   MOE_MF(MN_MAJOR, MN_MAJOR, RAGGED_K, EPI_STORE, false, 0)      // weight gradients (bf16, rounded once from fp32)
-  MOE_MF(MN_MAJOR, MN_MAJOR, RAGGED_K, EPI_STORE, true, 2)       // fc1 weight gradient on the token rows (fp32)
-  MOE_MF(MN_MAJOR, MN_MAJOR, RAGGED_K, EPI_STORE, false, 2)      // the same, bf16
 #undef MOE_MF
   return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: unsupported operand combination");
 }
