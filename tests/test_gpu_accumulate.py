@@ -107,19 +107,21 @@ def test_layer_bwd_accumulate(name):
         print("routing differs from the oracle's at a near-tie: oracle check left to the layer tests", flush=True)
 
 
-@pytest.mark.parametrize("wgrad", ["bf16", "f32"])
-def test_grouped_wgrad_accumulate(wgrad):
+@pytest.mark.parametrize("wgrad,K", [("bf16", 320), ("f32", 320), ("bf16", 1024), ("f32", 1024)])
+def test_grouped_wgrad_accumulate(wgrad, K):
     """The grouped weight gradient on ragged groups, some empty, three calls on one buffer:
-    overwrite, then accumulate twice."""
+    overwrite, then accumulate twice.  K = 1024 columns take the two-workgroup kernel
+    (narrower gradients the 8-wave GEMM); there the same calls with X read through a row
+    gather (x_rows) must give the same bits."""
     torch = torch_mod()
     from mixture_experts_layer_aux_amd import _lib as L
-    print(f"grouped wgrad accumulate {wgrad}", flush=True)
+    print(f"grouped wgrad accumulate {wgrad} K={K}", flush=True)
     shape = W.SMALL[2]
     cfg = L.config_from_shape(shape, wgrad=wgrad)
     cfg32 = L.config_from_shape(shape, wgrad="f32")
     rng = np.random.default_rng(7)
     sizes = np.array([300, 0, 257, 1, 0, 64, 511, 0], dtype=np.int64)
-    G, N, K = len(sizes), 192, 320
+    G, N = len(sizes), 192
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     rows = int(off[-1])
     dY = rng.standard_normal((rows, N)).astype(np.float32)
@@ -145,6 +147,21 @@ def test_grouped_wgrad_accumulate(wgrad):
     assert torch.equal(dW, _expected(once, ref32)), "second accumulation"
     for g in np.where(sizes == 0)[0]:
         assert torch.equal(dW[g], prior[g]), f"group {g} without rows keeps its gradient"
+    if K >= 1024:
+        # X's rows scattered over a larger source, read back through x_rows
+        src_rows = rows + 37
+        perm = rng.permutation(src_rows)[:rows].astype(np.int32)
+        Xsrc = torch.zeros(src_rows, K, dtype=X_d.dtype, device=dev())
+        Xsrc[torch.from_numpy(perm).long().to(dev())] = X_d
+        x_rows = torch.from_numpy(perm).to(dev())
+        gW = torch.full((G, N, K), 7.0, dtype=wd, device=dev())
+        L.grouped_wgrad(cfg, off_d, G, rows, dY_d, N, Xsrc, K, gW, x_rows=x_rows)
+        torch.cuda.synchronize()
+        assert torch.equal(gW, ref32.to(wd)), "overwrite through x_rows"
+        gW.copy_(prior)
+        L.grouped_wgrad(cfg, off_d, G, rows, dY_d, N, Xsrc, K, gW, x_rows=x_rows, accumulate=True)
+        torch.cuda.synchronize()
+        assert torch.equal(gW, once), "accumulation through x_rows"
     # the fp32 sums against fp64 dY_g^T X_g of the bf16 operands
     dY64 = W.bf16_bits_to_f32(W.f32_to_bf16_bits(dY)).astype(np.float64)
     X64 = W.bf16_bits_to_f32(W.f32_to_bf16_bits(X)).astype(np.float64)
