@@ -986,6 +986,48 @@ __device__ __forceinline__ float coherent_load(const float* p) {
 
 constexpr int kFinCols = 32;
 
+// Block reduction of the per-thread statistics parts of a 1024-thread block (fixed butterfly
+// per wave, then the 16 wave results in order by thread 0), and the statistics written by
+// thread 0: aux, MaxVio, empty experts, max count, z-loss (and a zero sequence-wise loss
+// when that loss is off).
+__device__ void router_block_stats(double dot, double zs, int mx, int empty, int E, int T, int k, float coeff,
+                                   bool has_z, float z_coeff, int seq_on, float* __restrict__ stats) {
+  __shared__ double s_dot[16], s_z[16];
+  __shared__ int s_max[16], s_empty[16];
+  dot = wave_sum(dot);
+  zs = wave_sum(zs);
+  for (int o = 32; o >= 1; o >>= 1) {
+    mx = max(mx, __shfl_xor(mx, o, 64));
+    empty += __shfl_xor(empty, o, 64);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_dot[w] = dot;
+    s_z[w] = zs;
+    s_max[w] = mx;
+    s_empty[w] = empty;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double d = 0.0, z = 0.0;
+    int m = 0, em = 0;
+    for (int i = 0; i < static_cast<int>(blockDim.x >> 6); ++i) {
+      d += s_dot[i];
+      z += s_z[i];
+      m = max(m, s_max[i]);
+      em += s_empty[i];
+    }
+    const double Td = static_cast<double>(T);
+    const double mean = Td * k / E;
+    stats[0] = static_cast<float>(d * coeff * E / (k * Td * Td));
+    stats[1] = static_cast<float>((m - mean) / mean);
+    stats[2] = static_cast<float>(em);
+    stats[3] = static_cast<float>(m);
+    stats[4] = has_z ? static_cast<float>(z_coeff * z / Td) : 0.0f;
+    if (!seq_on) stats[5] = 0.0f;
+  }
+}
+
 __global__ __launch_bounds__(1024) void router_finalize_stats_kernel(
     const int32_t* __restrict__ cnt_part, const float* __restrict__ prob_part, int nblk, int E, int T, int k,
     float coeff, const float* __restrict__ z_part, float z_coeff, int seq_on, int32_t* __restrict__ counts,
@@ -994,8 +1036,6 @@ __global__ __launch_bounds__(1024) void router_finalize_stats_kernel(
   __shared__ int sc[R][kFinCols];
   __shared__ float sp[R][kFinCols];
   __shared__ int s_last;
-  __shared__ double s_dot[16], s_z[16];
-  __shared__ int s_max[16], s_empty[16];
   const int c = threadIdx.x % kFinCols, r = threadIdx.x / kFinCols;
   const int e = blockIdx.x * kFinCols + c;
   int ci = 0;
@@ -1048,39 +1088,95 @@ __global__ __launch_bounds__(1024) void router_finalize_stats_kernel(
   }
   if (z_part)
     for (int b = threadIdx.x; b < nblk; b += blockDim.x) zs += z_part[b];
-  // wave sums (fixed butterfly), then the 16 wave results in order by thread 0
-  dot = wave_sum(dot);
-  zs = wave_sum(zs);
-  for (int o = 32; o >= 1; o >>= 1) {
-    mx = max(mx, __shfl_xor(mx, o, 64));
-    empty += __shfl_xor(empty, o, 64);
-  }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    s_dot[w] = dot;
-    s_z[w] = zs;
-    s_max[w] = mx;
-    s_empty[w] = empty;
+  router_block_stats(dot, zs, mx, empty, E, T, k, coeff, z_part != nullptr, z_coeff, seq_on, stats);
+}
+
+// Small partials (up to kFinOneBlockBytes): one block sums the columns and computes the
+// statistics itself, so no block waits for another (no counter, no device-wide fence).
+// VEC experts per thread (4: 16-byte loads).  Thread (r, c) adds rows b = r, r + R, ... of
+// column group c in that order, 8 loads in flight; expert e's R row sums are then added in
+// the order r = 0, 1, ..., R - 1.  The caller guarantees E % VEC == 0 and E / VEC <= 1024.
+constexpr size_t kFinOneBlockBytes = 512 * 1024;
+
+template <int VEC>
+__global__ __launch_bounds__(1024) void router_finalize_one_block_kernel(
+    const int32_t* __restrict__ cnt_part, const float* __restrict__ prob_part, int nblk, int E, int T, int k,
+    float coeff, const float* __restrict__ z_part, float z_coeff, int seq_on, int32_t* __restrict__ counts,
+    float* __restrict__ prob_sum, float* __restrict__ stats) {
+  extern __shared__ int smem_f[];
+  constexpr int U = 8;
+  const int ncol = E / VEC, R = 1024 / ncol;
+  int* sc = smem_f;                                          // [R][E]
+  float* sp = reinterpret_cast<float*>(smem_f + R * E);      // [R][E], with prob_part
+  const int c = threadIdx.x % ncol, r = threadIdx.x / ncol;
+  if (r < R) {
+    int ci[VEC];
+    float pf[VEC];
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) {
+      ci[q] = 0;
+      pf[q] = 0.0f;
+    }
+    for (int b0 = r; b0 < nblk; b0 += R * U) {
+      int v[U][VEC];
+      float pv[U][VEC];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int b = b0 + u * R;
+        const int64_t o = static_cast<int64_t>(b < nblk ? b : 0) * E + c * VEC;
+        if constexpr (VEC == 4) {
+          const int4 iv = *reinterpret_cast<const int4*>(cnt_part + o);
+          const float4 fv = prob_part ? *reinterpret_cast<const float4*>(prob_part + o) : make_float4(0, 0, 0, 0);
+          v[u][0] = iv.x; v[u][1] = iv.y; v[u][2] = iv.z; v[u][3] = iv.w;
+          pv[u][0] = fv.x; pv[u][1] = fv.y; pv[u][2] = fv.z; pv[u][3] = fv.w;
+        } else {
+          v[u][0] = cnt_part[o];
+          pv[u][0] = prob_part ? prob_part[o] : 0.0f;
+        }
+        if (b >= nblk) {
+#pragma unroll
+          for (int q = 0; q < VEC; ++q) {
+            v[u][q] = 0;
+            pv[u][q] = 0.0f;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) {
+          ci[q] += v[u][q];
+          pf[q] += pv[u][q];
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) {
+      sc[r * E + c * VEC + q] = ci[q];
+      if (prob_part) sp[r * E + c * VEC + q] = pf[q];
+    }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double d = 0.0, z = 0.0;
-    int m = 0, em = 0;
-    for (int i = 0; i < static_cast<int>(blockDim.x >> 6); ++i) {
-      d += s_dot[i];
-      z += s_z[i];
-      m = max(m, s_max[i]);
-      em += s_empty[i];
+  double dot = 0.0, zs = 0.0;
+  int mx = 0, empty = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int cnt = 0;
+    float p = 0.0f;
+    for (int rr = 0; rr < R; ++rr) {
+      cnt += sc[rr * E + e];
+      if (prob_part) p += sp[rr * E + e];
     }
-    const double Td = static_cast<double>(T);
-    const double mean = Td * k / E;
-    stats[0] = static_cast<float>(d * coeff * E / (k * Td * Td));
-    stats[1] = static_cast<float>((m - mean) / mean);
-    stats[2] = static_cast<float>(em);
-    stats[3] = static_cast<float>(m);
-    stats[4] = z_part ? static_cast<float>(z_coeff * z / Td) : 0.0f;
-    if (!seq_on) stats[5] = 0.0f;
+    counts[e] = cnt;
+    if (prob_part) {
+      prob_sum[e] = p;
+      dot += static_cast<double>(p) * cnt;
+    }
+    mx = max(mx, cnt);
+    empty += (cnt == 0);
   }
+  if (!stats) return;
+  if (z_part)
+    for (int b = threadIdx.x; b < nblk; b += blockDim.x) zs += z_part[b];
+  router_block_stats(dot, zs, mx, empty, E, T, k, coeff, z_part != nullptr, z_coeff, seq_on, stats);
 }
 
 // Router backward, one wave per token (see moe_router_bwd in moe.h for the formulas).
@@ -1333,9 +1429,24 @@ moe_status_t launch_router_topk(const moe_config_t& c, const float* logits, cons
     MOE_TRY_INTERNAL(c.score == MOE_SOFTMAX ? launch_rows<0>(c, a, nblk, s)
                      : sig16                ? launch_rows<2>(c, a, nblk, s)
                                             : launch_rows<1>(c, a, nblk, s));
-    router_finalize_stats_kernel<<<static_cast<int>(ceil_div(c.E, kFinCols)), 1024, 0, s>>>(
-        rw.cnt_part, a.prob_part, nblk, c.E, c.T, c.k, c.aux_coeff, zp, c.z_coeff, seq_on ? 1 : 0, counts, ps, stats,
-        rw.done);
+    const size_t part_bytes = static_cast<size_t>(nblk) * c.E * 4 * (a.prob_part ? 2 : 1);
+    const bool al16 = ((reinterpret_cast<uintptr_t>(rw.cnt_part) | reinterpret_cast<uintptr_t>(a.prob_part)) & 15u) == 0;
+    const int vec = (c.E % 4 == 0 && al16) ? 4 : 1;
+    if (part_bytes <= kFinOneBlockBytes && c.E / vec <= 1024) {
+      const size_t shm = static_cast<size_t>(1024 / (c.E / vec)) * c.E * 4 * (a.prob_part ? 2 : 1);
+      if (vec == 4)
+        router_finalize_one_block_kernel<4><<<1, 1024, shm, s>>>(rw.cnt_part, a.prob_part, nblk, c.E, c.T, c.k,
+                                                                 c.aux_coeff, zp, c.z_coeff, seq_on ? 1 : 0, counts,
+                                                                 ps, stats);
+      else
+        router_finalize_one_block_kernel<1><<<1, 1024, shm, s>>>(rw.cnt_part, a.prob_part, nblk, c.E, c.T, c.k,
+                                                                 c.aux_coeff, zp, c.z_coeff, seq_on ? 1 : 0, counts,
+                                                                 ps, stats);
+    } else {
+      router_finalize_stats_kernel<<<static_cast<int>(ceil_div(c.E, kFinCols)), 1024, 0, s>>>(
+          rw.cnt_part, a.prob_part, nblk, c.E, c.T, c.k, c.aux_coeff, zp, c.z_coeff, seq_on ? 1 : 0, counts, ps,
+          stats, rw.done);
+    }
   } else {
     // group-limited routing: one wave per token
     float* ps = prob_sum ? prob_sum : prob_scratch;

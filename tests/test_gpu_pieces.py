@@ -73,7 +73,8 @@ def test_router_full_size(cid):
 
 @pytest.mark.parametrize("score,k,E,scaling", [("softmax", 4, 16, 1.0), ("softmax", 8, 300, 2.5),
                                                ("sigmoid", 1, 8, 1.0), ("sigmoid", 6, 64, 2.5),
-                                               ("softmax", 32, 2048, 1.0), ("softmax", 2, 2, 1.0)])
+                                               ("softmax", 32, 2048, 1.0), ("softmax", 2, 2, 1.0),
+                                               ("softmax", 5, 77, 1.0)])
 def test_router_ties_and_variants(score, k, E, scaling):
     shape = W.LayerShape("router-edge", T=333, d=64, E=E, k=k, F=128, score=score, act="f32", scaling=scaling,
                          aux_coeff=0.01 if score == "softmax" else 0.0)
