@@ -735,7 +735,7 @@ __device__ __forceinline__ float sigmoid32(float l) { return __builtin_amdgcn_rc
 
 // 64 tokens per block (the permute's chunk, whose histograms it reuses), NW waves; each
 // wave routes 64 / LPT tokens per pass.
-template <int LPT, int KPL, int NW, int KEYS>
+template <int LPT, int KPL, int NW, int KEYS, bool FULL>
 __global__ __launch_bounds__(64 * NW) void router_rows_kernel(const RouterRowArgs a) {
   extern __shared__ int smem_r[];
   const int E = a.E, k = a.k;
@@ -752,10 +752,26 @@ __global__ __launch_bounds__(64 * NW) void router_rows_kernel(const RouterRowArg
   static_assert(KEYS != 2 || LPT == 16, "the fp32-first sigmoid keys sort slots inside one 16-lane row");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane % LPT, grp = lane / LPT;
+  // FULL: E == KPL * LPT, so every lane's every key is an expert (no bounds checks)
+  const auto inr = [&](int i) { return FULL || i * LPT + g < E; };
+  const auto col = [&](int i) { return FULL ? i * LPT + g : min(i * LPT + g, E - 1); };
   const bool softmax = KEYS == 0;
   const bool want_p = a.prob_part != nullptr;
   // the full-E normaliser: aux probabilities, pre-softmax weights, the sequence pass
   const bool want_norm = want_p || a.pnorm != nullptr || (softmax && (a.pre_softmax || a.z_part));
+  const auto token = [&](int pass) { return blockIdx.x * kRouterTokensPerBlock + (pass * NW + wave) * TPW + grp; };
+  const auto row_of_pass = [&](int pass) {
+    const int t = token(pass);
+    return a.logits + static_cast<int64_t>(t < a.T ? t : 0) * E;
+  };
+  // one pass per wave: its logits loads are issued before the LDS set-up and its barrier,
+  // so that their latency overlaps the expert biases' loads
+  float l0[PASSES == 1 ? KPL : 1];
+  if constexpr (PASSES == 1) {
+    const float* row = row_of_pass(0);
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) l0[i] = row[col(i)];
+  }
   if (blockIdx.x == 0 && threadIdx.x == 0 && a.done) *a.done = 0;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     hist[e] = 0;
@@ -769,24 +785,24 @@ __global__ __launch_bounds__(64 * NW) void router_rows_kernel(const RouterRowArg
   float zacc = 0.0f;
 #pragma unroll 1
   for (int pass = 0; pass < PASSES; ++pass) {
-    const int t = blockIdx.x * kRouterTokensPerBlock + (pass * NW + wave) * TPW + grp;
+    const int t = token(pass);
     const bool live = t < a.T;
-    const float* row = a.logits + static_cast<int64_t>(live ? t : 0) * E;
+    const float* row = row_of_pass(pass);
     // every load of the token's logits (and biases) is issued before any is used: the
     // addresses are clamped into the row instead of being guarded by branches
     float l[KPL];
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) l[i] = row[min(i * LPT + g, E - 1)];
+    for (int i = 0; i < KPL; ++i) l[i] = PASSES == 1 ? l0[i] : row[col(i)];
     float* my_stage = stage + static_cast<int64_t>(wave * TPW + grp) * E;
     if constexpr (KEYS == 2) {
       // the token's logits stay in LDS for the slots' scores below
 #pragma unroll
       for (int i = 0; i < KPL; ++i)
-        if (i * LPT + g < E) my_stage[i * LPT + g] = l[i];
+        if (inr(i)) my_stage[i * LPT + g] = l[i];
     }
 #pragma unroll
     for (int i = 0; i < KPL; ++i)
-      if (!(live && i * LPT + g < E)) l[i] = 0.0f;
+      if (!(live && inr(i))) l[i] = 0.0f;
     // winners: my_e for lane j < k of the group (slot j); for softmax, top_l is the top-1 logit
     int my_e = 0;
     float my_l = 0.0f, top_l = 0.0f;
@@ -796,8 +812,8 @@ __global__ __launch_bounds__(64 * NW) void router_rows_kernel(const RouterRowArg
       double key[KPL];
 #pragma unroll
       for (int i = 0; i < KPL; ++i)
-        key[i] = (live && i * LPT + g < E)
-                     ? score_f64(a.score, l[i]) + static_cast<double>(bias_s[min(i * LPT + g, E - 1)])
+        key[i] = (live && inr(i))
+                     ? score_f64(a.score, l[i]) + static_cast<double>(bias_s[col(i)])
                      : lowest_key<double>();
       double tk, kk;
       int ke;
@@ -808,8 +824,8 @@ __global__ __launch_bounds__(64 * NW) void router_rows_kernel(const RouterRowArg
 #pragma unroll
       for (int i = 0; i < KPL; ++i) {
         const int e = i * LPT + g;
-        const float kv = KEYS == 0 ? l[i] : sigmoid32(l[i]) + bias_s[min(e, E - 1)];
-        key[i] = (live && e < E) ? kv : lowest_key<float>();
+        const float kv = KEYS == 0 ? l[i] : sigmoid32(l[i]) + bias_s[col(i)];
+        key[i] = (live && inr(i)) ? kv : lowest_key<float>();
       }
       float my_key, top_key, kth_key;
       int kth_e;
@@ -829,9 +845,9 @@ __global__ __launch_bounds__(64 * NW) void router_rows_kernel(const RouterRowArg
           double k64[KPL];
 #pragma unroll
           for (int i = 0; i < KPL; ++i)
-            k64[i] = (live && i * LPT + g < E)
-                         ? score_f64(MOE_SIGMOID, my_stage[min(i * LPT + g, E - 1)]) +
-                               static_cast<double>(bias_s[min(i * LPT + g, E - 1)])
+            k64[i] = (live && inr(i))
+                         ? score_f64(MOE_SIGMOID, my_stage[col(i)]) +
+                               static_cast<double>(bias_s[col(i)])
                          : lowest_key<double>();
           double tk, kk;
           int ke;
@@ -881,7 +897,7 @@ __global__ __launch_bounds__(64 * NW) void router_rows_kernel(const RouterRowArg
         float part = 0.0f;
 #pragma unroll
         for (int i = 0; i < KPL; ++i) {
-          q[i] = (live && i * LPT + g < E) ? expf(l[i] - m) : 0.0f;
+          q[i] = (live && inr(i)) ? expf(l[i] - m) : 0.0f;
           part += q[i];
         }
         const float z = rg::group_sum<LPT>(part);
@@ -891,8 +907,8 @@ __global__ __launch_bounds__(64 * NW) void router_rows_kernel(const RouterRowArg
         float part = 0.0f;
 #pragma unroll
         for (int i = 0; i < KPL; ++i) {
-          if (KEYS == 2) l[i] = (live && i * LPT + g < E) ? my_stage[min(i * LPT + g, E - 1)] : 0.0f;
-          q[i] = (live && i * LPT + g < E) ? score_f32(a.score, l[i]) : 0.0f;
+          if (KEYS == 2) l[i] = (live && inr(i)) ? my_stage[col(i)] : 0.0f;
+          q[i] = (live && inr(i)) ? score_f32(a.score, l[i]) : 0.0f;
           part += q[i];
         }
         inv = 1.0f / (rg::group_sum<LPT>(part) + 1e-20f);
@@ -900,11 +916,11 @@ __global__ __launch_bounds__(64 * NW) void router_rows_kernel(const RouterRowArg
           float mx = -FLT_MAX;
 #pragma unroll
           for (int i = 0; i < KPL; ++i)
-            if (i * LPT + g < E) mx = fmaxf(mx, l[i]);
+            if (inr(i)) mx = fmaxf(mx, l[i]);
           mx = rg::group_max<LPT>(mx);
           float pe = 0.0f;
 #pragma unroll
-          for (int i = 0; i < KPL; ++i) pe += (live && i * LPT + g < E) ? expf(l[i] - mx) : 0.0f;
+          for (int i = 0; i < KPL; ++i) pe += (live && inr(i)) ? expf(l[i] - mx) : 0.0f;
           lse = mx + logf(rg::group_sum<LPT>(pe));
         }
       }
@@ -1371,11 +1387,19 @@ moe_status_t launch_rows_inst(const moe_config_t& c, const RouterRowArgs& a, int
   const size_t shm = static_cast<size_t>(c.E) * sizeof(int) +
                      (KEYS == 2 ? static_cast<size_t>(NW * (64 / LPT)) * c.E * 4 : 0) + (KEYS != 0 ? c.E * 4 : 0) +
                      (a.prob_part ? static_cast<size_t>(NW) * c.E * 4 : 0);
+  // the instance without bounds checks serves E == LPT * KPL, except for 32 fp64 keys per
+  // lane, where the compiler spills more without them
+  constexpr bool kFullOk = !(KEYS == 1 && KPL == 32);
+  const bool full = kFullOk && c.E == LPT * KPL;
+  const void* fn = full ? reinterpret_cast<const void*>(router_rows_kernel<LPT, KPL, NW, KEYS, kFullOk>)
+                        : reinterpret_cast<const void*>(router_rows_kernel<LPT, KPL, NW, KEYS, false>);
   if (shm > 65536 &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(router_rows_kernel<LPT, KPL, NW, KEYS>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)) != hipSuccess)
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)) != hipSuccess)
     return fail(MOE_ERR_HIP, "router: cannot raise the LDS limit to %zu bytes", shm);
-  router_rows_kernel<LPT, KPL, NW, KEYS><<<nblk, 64 * NW, shm, s>>>(a);
+  if (full)
+    router_rows_kernel<LPT, KPL, NW, KEYS, kFullOk><<<nblk, 64 * NW, shm, s>>>(a);
+  else
+    router_rows_kernel<LPT, KPL, NW, KEYS, false><<<nblk, 64 * NW, shm, s>>>(a);
   return MOE_OK;
 }
 
