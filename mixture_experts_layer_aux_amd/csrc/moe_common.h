@@ -37,6 +37,23 @@ template <> struct Elem<uint16_t> {
   __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+// ------------------------------------------------------------------ streaming stores
+// Non-temporal global stores for the GEMM outputs (each written once, and far larger than
+// the L2s, so no later tile of the same kernel reads them back): they do not displace the
+// operand lines that other tiles of the kernel still reuse.
+typedef unsigned int nt_u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int nt_u32x4_t __attribute__((ext_vector_type(4)));
+typedef float nt_f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
+  __builtin_nontemporal_store(nt_u32x2_t{v.x, v.y}, reinterpret_cast<nt_u32x2_t*>(p));
+}
+__device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
+  __builtin_nontemporal_store(nt_u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u32x4_t*>(p));
+}
+__device__ __forceinline__ void store_nt(float4* p, float4 v) {
+  __builtin_nontemporal_store(nt_f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_f32x4_t*>(p));
+}
+
 // ------------------------------------------------------------------ wave reductions
 // Fixed butterfly order: deterministic.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -459,7 +459,8 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
   // epilogue: acc[i][j][4q + c] is row wm*64 + i*32 + lane%32, column
   // wn*64 + j*32 + 8q + 4(lane/32) + c of the B tile.  The BM x BN fp32 tile goes through
   // LDS (row-major, 16-byte chunk c of row r at r * (BN / 4) + (c ^ (r & 31))), so that the
-  // global writes run along whole rows instead of 16-byte pieces of 32 rows.
+  // global writes run along whole rows instead of 16-byte pieces of 32 rows.  The fp32
+  // outputs go out as non-temporal stores (written once, larger than the L2s).
   constexpr int RC = BN / 4;   // 16-byte chunks per tile row
   float4* L4 = reinterpret_cast<float4*>(lds);
   static_assert(STAGES * STAGE_BYTES >= BM * BN * 4, "epilogue staging needs the tile in LDS");
@@ -497,8 +498,8 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
       act.z = glu_f(p.glu, gt.z, up.z); act.w = glu_f(p.glu, gt.w, up.w);
       if (live && p.H) {
         float* hrow = p.H + static_cast<int64_t>(row) * 2 * p.F;
-        *reinterpret_cast<float4*>(hrow + col) = gt;
-        *reinterpret_cast<float4*>(hrow + p.F + col) = up;
+        store_nt(reinterpret_cast<float4*>(hrow + col), gt);
+        store_nt(reinterpret_cast<float4*>(hrow + p.F + col), up);
       }
       if constexpr (BN / 2 == 128) {
         if (p.Cq) {
@@ -518,7 +519,7 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
           continue;
         }
       }
-      if (live) *reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.F + col) = act;
+      if (live) store_nt(reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.F + col), act);
     }
   } else {
     // 64 / RC rows per step, RC lanes per row, lane l the columns 4l .. 4l+3 of nt*BN ..
@@ -529,7 +530,7 @@ __device__ __forceinline__ void fp8_gemm_body(const Fp8Args& p) {
       const int r = wave * RPW + rr * RPS + lane / RC;
       const int row = row_begin + r;
       if (row >= row_end) continue;
-      *reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.N + col) = L4[r * RC + (l ^ (r & 31))];
+      store_nt(reinterpret_cast<float4*>(p.C + static_cast<int64_t>(row) * p.N + col), L4[r * RC + (l ^ (r & 31))]);
     }
   }
 }

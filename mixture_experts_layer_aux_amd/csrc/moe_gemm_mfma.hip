@@ -31,7 +31,8 @@
 //   * the epilogue stages the tile through LDS in two passes of 128 rows and then works on
 //     whole tile rows, so its global loads and stores are contiguous runs of a row (a 1 KB
 //     row of fp32 per store instruction) rather than 16 bytes of each of 32 rows; a bf16
-//     weight gradient that overwrites is rounded first and staged in one pass;
+//     weight gradient that overwrites is rounded first and staged in one pass.  The
+//     outputs go out as non-temporal stores, so they do not evict operand lines from L2;
 //   * a one-group weight gradient can be split over its reduction rows (kchunk): each
 //     chunk is a group writing fp32 partials, summed in chunk order by splitk_reduce_kernel;
 //   * in an expert's last row tile, the 32-row accumulator blocks past its end skip their
@@ -368,8 +369,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
     if (col < p.N) {
       char* base = static_cast<char*>(p.C) + static_cast<int64_t>(grp) * p.c_gstride * EB;
       for (int r = tid / TPR; r < BM && row_begin + r < row_end; r += RPI)
-        *reinterpret_cast<uint4*>(base + (static_cast<int64_t>(row_begin + r) * p.ldc + col) * EB) =
-            make_uint4(0u, 0u, 0u, 0u);
+        store_nt(reinterpret_cast<uint4*>(base + (static_cast<int64_t>(row_begin + r) * p.ldc + col) * EB),
+                 make_uint4(0u, 0u, 0u, 0u));
     }
     return;
   }
@@ -519,7 +520,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
         const int lr = wave * (BM / NWAVES) + rr;
         const int row = row_begin + lr;
         if (row >= row_end || col >= p.N) continue;
-        *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * p.ldc + col) = U2[lr * 64 + (lane ^ (lr & 63))];
+        store_nt(reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * p.ldc + col), U2[lr * 64 + (lane ^ (lr & 63))]);
       }
       return;
     }
@@ -554,12 +555,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
         if (row < row_end) {
           const float4 gt = chunk(lr, cgate), up = chunk(lr, cgate + 8);
           float* hrow = Cf + static_cast<int64_t>(row) * p.ldc;
-          *reinterpret_cast<float4*>(hrow + col) = gt;
-          *reinterpret_cast<float4*>(hrow + p.F + col) = up;
+          store_nt(reinterpret_cast<float4*>(hrow + col), gt);
+          store_nt(reinterpret_cast<float4*>(hrow + p.F + col), up);
           uint2 av;
           av.x = pack_bf16x2(glu_f(p.glu, gt.x, up.x), glu_f(p.glu, gt.y, up.y));
           av.y = pack_bf16x2(glu_f(p.glu, gt.z, up.z), glu_f(p.glu, gt.w, up.w));
-          *reinterpret_cast<uint2*>(p.C2 + static_cast<int64_t>(row) * p.ldc2 + col) = av;
+          store_nt(reinterpret_cast<uint2*>(p.C2 + static_cast<int64_t>(row) * p.ldc2 + col), av);
         }
       }
     } else {
@@ -582,15 +583,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) glu_grad_f(p.glu, g[c], u[c], dv[c], dg[c], du[c]);
           uint16_t* drow = C + static_cast<int64_t>(row) * p.ldc;
-          *reinterpret_cast<uint2*>(drow + col) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-          *reinterpret_cast<uint2*>(drow + p.F + col) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+          store_nt(reinterpret_cast<uint2*>(drow + col), make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])));
+          store_nt(reinterpret_cast<uint2*>(drow + p.F + col), make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])));
         } else if (OUT_F32) {
           float4* dst = reinterpret_cast<float4*>(Cf + static_cast<int64_t>(row) * p.ldc + col);
           if (p.beta) {
             const float4 o = *dst;
             *dst = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
           } else {
-            *dst = v;
+            store_nt(dst, v);
           }
         } else {
           uint2* dst = reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * p.ldc + col);
@@ -602,7 +603,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
             w.z += __uint_as_float(o.y << 16);
             w.w += __uint_as_float(o.y & 0xFFFF0000u);
           }
-          *dst = make_uint2(pack_bf16x2(w.x, w.y), pack_bf16x2(w.z, w.w));
+          store_nt(dst, make_uint2(pack_bf16x2(w.x, w.y), pack_bf16x2(w.z, w.w)));
         }
       }
     }

@@ -35,7 +35,9 @@
 //     read zeros, so the ragged tail needs no code;
 //   * the epilogue stages the tile through the LDS (bf16 overwritten: one pass of the
 //     rounded tile, 64 KB; otherwise two passes of 128 fp32 rows, 64 KB each) and stores
-//     whole tile rows; the bf16 overwrite, bf16 accumulate and fp32 outputs are separate
+//     whole tile rows, non-temporal (the gradient, and the zeros of a group without rows,
+//     are written once and would only evict operand lines from L2); the bf16 overwrite,
+//     bf16 accumulate and fp32 outputs are separate
 //     kernels (a run-time branch between the epilogues makes the register allocator spill
 //     the accumulators).
 #include <type_traits>
@@ -151,8 +153,8 @@ __device__ __forceinline__ void wgrad_body(const WgArgs& p) {
     if (col < p.N) {
       char* base = static_cast<char*>(p.C) + cg * EB;
       for (int r = tid / TPR; r < BM && row_begin + r < p.M; r += RPI)
-        *reinterpret_cast<uint4*>(base + (static_cast<int64_t>(row_begin + r) * p.ldc + col) * EB) =
-            make_uint4(0u, 0u, 0u, 0u);
+        store_nt(reinterpret_cast<uint4*>(base + (static_cast<int64_t>(row_begin + r) * p.ldc + col) * EB),
+                 make_uint4(0u, 0u, 0u, 0u));
     }
     return;
   }
@@ -344,7 +346,7 @@ __device__ __forceinline__ void wgrad_body(const WgArgs& p) {
 #pragma unroll
       for (int q = 0; q < CH; ++q) {
         const int row = row_begin + wave * (BM / 4) + (s0 + q) * RPI + lane / UPR;
-        if (row < p.M && col < p.N) *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * p.ldc + col) = v[q];
+        if (row < p.M && col < p.N) store_nt(reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * p.ldc + col), v[q]);
       }
     }
     return;
@@ -386,7 +388,7 @@ __device__ __forceinline__ void wgrad_body(const WgArgs& p) {
           const float4 o = *dst;
           *dst = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
         } else {
-          *dst = v;
+          store_nt(dst, v);
         }
       } else {
         uint2* dst = reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.C) + cg + static_cast<int64_t>(row) * p.ldc + col);
@@ -396,7 +398,7 @@ __device__ __forceinline__ void wgrad_body(const WgArgs& p) {
         w.y += __uint_as_float(o.x & 0xFFFF0000u);
         w.z += __uint_as_float(o.y << 16);
         w.w += __uint_as_float(o.y & 0xFFFF0000u);
-        *dst = make_uint2(pack_bf16x2(w.x, w.y), pack_bf16x2(w.z, w.w));
+        store_nt(dst, make_uint2(pack_bf16x2(w.x, w.y), pack_bf16x2(w.z, w.w)));
       }
     }
   };
