@@ -41,29 +41,35 @@ __global__ __launch_bounds__(64) void chunk_hist_kernel(const int32_t* __restric
 }
 
 // Per expert column: blk_base[b][e] = sum_{b' < b} blk_hist[b'][e]; counts[e] = total.
-// 256 threads = 64 experts x 4 contiguous quarters of the chunks.
+// 256 threads = 16 experts x 16 contiguous parts of the chunks, so that each thread walks
+// few chunks (their loads unrolled and in flight together) and the grid spans E / 16
+// blocks.
+constexpr int kScanParts = 16, kScanCols = 256 / kScanParts;
 __global__ __launch_bounds__(256) void chunk_scan_kernel(const int32_t* __restrict__ blk_hist, int nblk, int E,
                                                          int32_t* __restrict__ blk_base,
                                                          int32_t* __restrict__ counts) {
-  __shared__ int part[4][64];
-  const int c = threadIdx.x & 63, r = threadIdx.x >> 6;
-  const int e = blockIdx.x * 64 + c;
-  const int q = (nblk + 3) / 4;
-  const int b0 = r * q, b1 = min(nblk, b0 + q);
+  __shared__ int part[kScanParts][kScanCols];
+  const int c = threadIdx.x % kScanCols, r = threadIdx.x / kScanCols;
+  const int e = blockIdx.x * kScanCols + c;
+  const int q = (nblk + kScanParts - 1) / kScanParts;
+  const int b0 = min(nblk, r * q), b1 = min(nblk, b0 + q);
   int s = 0;
-  if (e < E)
+  if (e < E) {
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) s += blk_hist[static_cast<int64_t>(b) * E + e];
+  }
   part[r][c] = s;
   __syncthreads();
   int base = 0;
   for (int i = 0; i < r; ++i) base += part[i][c];
   if (e < E) {
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) {
       const int v = blk_hist[static_cast<int64_t>(b) * E + e];
       blk_base[static_cast<int64_t>(b) * E + e] = base;
       base += v;
     }
-    if (r == 3) counts[e] = base;
+    if (r == kScanParts - 1) counts[e] = base;
   }
 }
 
@@ -441,7 +447,7 @@ moe_status_t launch_permute(const moe_config_t& c, const void* x, const int32_t*
   const int nblk = static_cast<int>(permute_num_chunks(c.T));
   if (!hist_ready)
     chunk_hist_kernel<<<nblk, 64, c.E * sizeof(int), s>>>(idx, c.T, c.E, c.k, blk_hist);
-  chunk_scan_kernel<<<static_cast<int>(ceil_div(c.E, 64)), 256, 0, s>>>(blk_hist, nblk, c.E, blk_base, counts_ws);
+  chunk_scan_kernel<<<static_cast<int>(ceil_div(c.E, kScanCols)), 256, 0, s>>>(blk_hist, nblk, c.E, blk_base, counts_ws);
   offsets_kernel<<<1, 1024, 0, s>>>(counts_ws, c.E, offsets);
   permute_index_kernel<<<nblk, 64, c.E * sizeof(unsigned long long), s>>>(idx, c.T, c.E, c.k, offsets, blk_base,
                                                                           row_of, token_of);
