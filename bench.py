@@ -283,7 +283,7 @@ def bench_fp8(args, shape, cfg, inp, up, dev) -> int:
     return 0
 
 
-def bench_wgrad_f32(args, shape, L, S, x, dY_perm, dH, dev, phase_ms):
+def bench_wgrad_f32(args, shape, L, S, x, dY_perm, dH, dev, phase_ms, ws):
     """The two routed weight-gradient launches again with fp32 output (the other option of
     the weight-gradient dtype), timed with HIP events on the launch stream, beside the
     step's bf16 ones."""
@@ -297,8 +297,8 @@ def bench_wgrad_f32(args, shape, L, S, x, dY_perm, dH, dev, phase_ms):
     res = {}
     X, x_rows = (x, S["token_of"]) if "x_perm" not in S else (S["x_perm"], None)
     for name, fn in (("wgrad_fc1", lambda: L.grouped_wgrad(c32, S["offsets"], E, A, dH, 2 * F, X, d, dW13,
-                                                           x_rows=x_rows)),
-                     ("wgrad_fc2", lambda: L.grouped_wgrad(c32, S["offsets"], E, A, dY_perm, d, S["Act"], F, dW2))):
+                                                           x_rows=x_rows, ws=ws)),
+                     ("wgrad_fc2", lambda: L.grouped_wgrad(c32, S["offsets"], E, A, dY_perm, d, S["Act"], F, dW2, ws=ws))):
         fn()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(runs + 1)]
         ev[0].record()
@@ -492,9 +492,9 @@ def main() -> int:
                                   dH, dX_perm, None, None, x if Fs else None, Wt["W13s"], Wt["W2s"],
                                   S.get("H_s"), S.get("Act_s"), dY_s, dH_s, dx_s, None, None, ws)
         mark()
-        L.grouped_wgrad(cfg, S["offsets"], E, A, dY_perm, d, S["Act"], F, G["dW2"])
+        L.grouped_wgrad(cfg, S["offsets"], E, A, dY_perm, d, S["Act"], F, G["dW2"], ws=ws)
         mark()
-        L.grouped_wgrad(cfg, S["offsets"], E, A, dH, 2 * F, X1, d, G["dW13"], x_rows=tok)
+        L.grouped_wgrad(cfg, S["offsets"], E, A, dH, 2 * F, X1, d, G["dW13"], x_rows=tok, ws=ws)
         mark()
         if Fs:
             L.grouped_wgrad(cfg, None, 1, T, dH_s, 2 * Fs, x, d, G["dW13s"], ws=ws)
@@ -600,7 +600,7 @@ def main() -> int:
     )
     out["balancing"] = bench_balancing(args, shape, L, S, Wt["expert_bias"], dw, dlogits, dev)
     if wbf16:
-        out["wgrad_f32"] = bench_wgrad_f32(args, shape, L, S, x, dY_perm, dH, dev, phase_ms)
+        out["wgrad_f32"] = bench_wgrad_f32(args, shape, L, S, x, dY_perm, dH, dev, phase_ms, ws)
     if not args.no_cpu_baseline:
         tokens = args.cpu_tokens or {1: 128, 2: 8192, 3: 48, 4: 1024, 5: 256}[args.config]
         out["cpu_baseline"] = cpu_baseline(shape, inp, min(tokens, T))

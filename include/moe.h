@@ -388,11 +388,19 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
  * moe_grouped_gemm_swiglu_bwd's shared-expert gradients, which split the same way).  The
  * split needs chunks * N * K * 4 bytes of ws (at most 32 N K); the backward workspace of
  * moe_workspace_size covers the shared expert's two calls.  ws NULL: no split.
+ * With offsets (bf16), a ws of at least moe_workspace_size's backward bytes lets the call
+ * cut a group with far more rows than the others (a long-tailed routing, [HB] §3.3 Cost
+ * of imbalance) into row chunks.  Its tiles would otherwise run alone on a few CUs for the
+ * whole call.  The chunk is a quarter of the rows one of the kernel's tile slots holds in
+ * a balanced launch (rows x tiles / slots), at least 1024.  Each chunk is an fp32 partial
+ * in ws, and the partials are summed in chunk order; the other groups are computed as
+ * without ws.  The plan is built on the device from offsets (no host sync).  It is the one
+ * moe_layer_bwd and moe_grouped_gemm_swiglu_bwd use for the routed experts, so the call
+ * gives their bits.  A ws too small for the plan: no split.
  * x_rows (bf16 activations; NULL: none): reduction row r of X is row x_rows[r] of X, which
  * then has x_src_rows rows [x_src_rows, K] (the routed dW13 straight from the token rows
  * of x, with x_rows = token_of and x_src_rows = T: bit-equal to the call on x_perm).  An
- * entry outside [0, x_src_rows) is the caller's error; the reads never leave X.  No split
- * with x_rows.
+ * entry outside [0, x_src_rows) is the caller's error; the reads never leave X.
  * Errors: groups outside [1, 4096], groups != 1 without offsets, rows outside [0, 2^31),
  * N or K not a positive multiple of 64, accumulate not 0 or 1, x_rows with x_src_rows < 1
  * -> MOE_ERR_INVALID_ARG; x_rows with fp32 activations -> MOE_ERR_UNSUPPORTED; ws given

@@ -117,8 +117,25 @@ struct BwdWs {
   float* wsplit;   // bf16 shared expert: split-K partials of its weight gradients (or NULL)
   int32_t* sched;  // tile schedule of the grouped GEMMs: [E + 1] prefix + owner table
   void* gate;      // router GEMM scratch (gate_bwd_ws_bytes)
+  void* skew;      // skew split of the routed weight gradients: plan tables + fp32 partials
+  size_t skew_bytes;
   size_t bytes;
 };
+
+// Workspace of the skew split of a routed weight gradient dW [M, N] (bf16 layers): the
+// plan's tables and its fp32 partials, 0 when no expert can reach the split point.  The
+// plan does not depend on which weight-gradient kernel runs: that kernel's tiles and
+// slots change by the same factor.
+size_t routed_skew_bytes(const moe_config_t& c, int M, int N) {
+  const int64_t A = static_cast<int64_t>(c.T) * c.k;
+  const int tiles = static_cast<int>(ceil_div(M, 256) * ceil_div(N, 256));
+  const SkewPlan sp = skew_plan(c.E, A, c.T, M, N, tiles, 256);
+  return sp.chunk ? align_up(sp.plan_bytes) + sp.partial_bytes : 0;
+}
+size_t skew_ws_bytes(const moe_config_t& c) {
+  if (c.act_dtype != MOE_BF16) return 0;
+  return std::max(routed_skew_bytes(c, c.d, c.F), routed_skew_bytes(c, 2 * c.F, c.d));
+}
 
 BwdWs carve_bwd(const moe_config_t& c, void* base) {
   char* p = static_cast<char*>(base);
@@ -148,6 +165,8 @@ BwdWs carve_bwd(const moe_config_t& c, void* base) {
   w.wsplit = split ? reinterpret_cast<float*>(take(split)) : nullptr;
   w.sched = reinterpret_cast<int32_t*>(take(mfma_schedule_bytes(c.E, A)));
   w.gate = take(gate_bwd_ws_bytes(c));
+  w.skew_bytes = skew_ws_bytes(c);
+  w.skew = w.skew_bytes ? take(w.skew_bytes) : nullptr;
   w.bytes = off;
   return w;
 }
@@ -388,9 +407,13 @@ moe_status_t run_experts_fwd(const moe_config_t& c, const void* x_perm, const in
 // wgrad_split_bytes(N, K, rows)) is split over its rows when its output has too few tiles:
 // fp32 partials per row chunk, then their sum in chunk order.
 // x_rows (bf16 only): reduction row r of X is row x_rows[r] of X, which has x_src_rows rows.
+// skew (with off, bf16): workspace of the skew split (routed_skew_bytes); a group with more
+// rows than the plan's chunk is left to a second, fp32 launch over its row chunks, whose
+// partials are then summed in chunk order.  max_group_rows bounds any group's rows.
 moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G, int64_t rows, const void* dY, int N,
                        const void* X, int K, void* dW, hipStream_t s, int beta, float* split_ws = nullptr,
-                       const int32_t* x_rows = nullptr, int x_src_rows = 0) {
+                       const int32_t* x_rows = nullptr, int x_src_rows = 0, void* skew = nullptr,
+                       size_t skew_bytes = 0, int64_t max_group_rows = 0) {
   GemmDesc w{};
   w.a_major = MN_MAJOR; w.b_major = MN_MAJOR; w.ragged = RAGGED_K; w.epi = EPI_STORE;
   w.a_type = w.b_type = act_dtype;
@@ -404,12 +427,36 @@ moe_status_t run_wgrad(int act_dtype, int wgrad_dtype, const int32_t* off, int G
     if (act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "gathered weight gradients need bf16 activations");
     w.gather = x_rows;
     w.gather_rows = x_src_rows;
-    return launch_wgrad2(w, s);   // (fails with MOE_ERR_UNSUPPORTED on dimensions not multiples of 8)
   }
+  const bool two_wg = act_dtype == MOE_BF16 && off && (x_rows || (K >= 1024 && wgrad2_supported(w)));
+  if (act_dtype == MOE_BF16 && off && skew) {
+    const int tiles = static_cast<int>(ceil_div(N, 256) * ceil_div(K, 256));
+    const SkewPlan sp = skew_plan(G, rows, max_group_rows, N, K, tiles, 256);
+    GemmDesc pc = w;
+    pc.c_type = MOE_F32;
+    pc.beta = 0;
+    if (sp.chunk && align_up(sp.plan_bytes) + sp.partial_bytes <= skew_bytes && wgrad2_supported(pc)) {
+      int32_t* plan = static_cast<int32_t*>(skew);
+      float* part = reinterpret_cast<float*>(static_cast<char*>(skew) + align_up(sp.plan_bytes));
+      MOE_TRY(launch_skew_plan(off, G, sp, plan, s));
+      const SkewTables t = skew_tables(plan, G, sp);
+      w.skip = t.skip;   // the split groups are left to the chunks below
+      MOE_TRY(two_wg ? launch_wgrad2(w, s) : launch_gemm_mfma(w, nullptr, s));
+      pc.pairs = t.pairs;
+      pc.gcount = t.gcount;
+      pc.G = sp.max_vg;
+      pc.C = part;
+      pc.ldc = K;
+      pc.c_gstride = int64_t{1} * N * K;
+      MOE_TRY(launch_wgrad2(pc, s));
+      return launch_skew_reduce(part, t, sp, int64_t{1} * N * K, dW, w.c_gstride, wgrad_dtype, beta, s);
+    }
+  }
+  if (x_rows) return launch_wgrad2(w, s);   // (fails with MOE_ERR_UNSUPPORTED on dimensions not multiples of 8)
   // per-expert gradients: many short reductions, each tile's fixed cost hidden by a second
   // workgroup on the CU.  Gradients with fewer than 1024 columns (fc2's at F = 512) are
   // faster on the 256 x 256 tiles, which read dY half as often.
-  if (act_dtype == MOE_BF16 && off && K >= 1024 && wgrad2_supported(w)) return launch_wgrad2(w, s);
+  if (two_wg) return launch_wgrad2(w, s);
   if (act_dtype == MOE_BF16 && !off && split_ws) {
     const WgradSplit sp = wgrad_split(N, K, rows);
     if (sp.chunks > 1) {
@@ -445,9 +492,9 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
                              const void* W2, const void* H, const void* Act, const void* dY_perm, void* dH,
                              void* dX_perm, void* dW13, void* dW2, const void* x, const void* W13s, const void* W2s,
                              const void* H_s, const void* Act_s, const void* dY_s, void* dH_s, void* dx_s,
-                             void* dW13s, void* dW2s, int32_t* sched, float* dact, float* wsplit, hipStream_t s,
-                             hipStream_t s2 = nullptr, hipEvent_t ev_dh = nullptr, int beta = 0,
-                             const int32_t* token_of = nullptr) {
+                             void* dW13s, void* dW2s, int32_t* sched, float* dact, float* wsplit, void* skew,
+                             size_t skew_bytes, hipStream_t s, hipStream_t s2 = nullptr, hipEvent_t ev_dh = nullptr,
+                             int beta = 0, const int32_t* token_of = nullptr) {
   // x_perm NULL: the routed fc1 weight gradient reads the token rows of x through token_of
   // s2 (when given, with dY_perm and dX_perm distinct) runs the weight gradients; its
   // caller has made it wait for dY_perm and joins it back.
@@ -501,14 +548,16 @@ moe_status_t run_experts_bwd(const moe_config_t& c, const void* x_perm, const in
     }
     // (2) fc2 weight gradient dW2 = dY^T Act, queued before dX may overwrite an aliased dY
     float* sw = shared ? wsplit : nullptr;   // both shared weight gradients run on s2, one after the other
-    if (dw2) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dY, c.d, act, F, dw2, s2, beta, sw));
+    void* sk = shared ? nullptr : skew;   // the routed experts' (the two run on s2, one after the other)
+    if (dw2) MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dY, c.d, act, F, dw2, s2, beta, sw, nullptr, 0, sk,
+                               skew_bytes, c.T));
     MOE_TRY(fork(s, ev_dh, s2));  // dH ready for the fc1 weight gradient
     MOE_TRY(et == MOE_BF16 ? launch_gemm_mfma(d1, sched, s) : launch_gemm_fma(d1, s));
     // (4) fc1 weight gradient dW13 = dH^T X
     const bool gathered = !shared && !x_perm;
     if (dw13)
       MOE_TRY(run_wgrad(et, c.wgrad_dtype, off, G, rows, dh, 2 * F, gathered ? x : X, c.d, dw13, s2, beta, sw,
-                        gathered ? token_of : nullptr, c.T));
+                        gathered ? token_of : nullptr, c.T, sk, skew_bytes, c.T));
   }
   return MOE_OK;
 }
@@ -820,8 +869,8 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
   const BwdWs bw = carve_bwd(*cfg, ws);
   MOE_TRY(need_ws(ws_bytes, bw.bytes, __func__));
   return run_experts_bwd(*cfg, x_perm, offsets, W13, W2, H, Act, dY_perm, dH, dX_perm, dW13, dW2, x, W13s, W2s, H_s,
-                         Act_s, dY_s, dH_s, dx_s, dW13s, dW2s, bw.sched, bw.dact, bw.wsplit, S(stream), nullptr,
-                         nullptr, 0, token_of);
+                         Act_s, dY_s, dH_s, dx_s, dW13s, dW2s, bw.sched, bw.dact, bw.wsplit, bw.skew, bw.skew_bytes,
+                         S(stream), nullptr, nullptr, 0, token_of);
 }
 
 moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, int32_t groups, int64_t rows,
@@ -840,8 +889,9 @@ moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, 
     if (cfg->act_dtype != MOE_BF16)
       return fail(MOE_ERR_UNSUPPORTED, "x_rows (the row gather of X) needs bf16 activations");
     if (x_src_rows < 1) return fail(MOE_ERR_INVALID_ARG, "x_src_rows must be >= 1 with x_rows");
+    const bool skew = ws && offsets && aligned16(ws);
     return run_wgrad(cfg->act_dtype, cfg->wgrad_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream), accumulate,
-                     nullptr, x_rows, x_src_rows);
+                     nullptr, x_rows, x_src_rows, skew ? ws : nullptr, skew ? ws_bytes : 0, rows);
   }
   float* split = nullptr;
   if (ws && !offsets && cfg->act_dtype == MOE_BF16) {
@@ -852,8 +902,12 @@ moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, 
       split = static_cast<float*>(ws);
     }
   }
+  // with offsets: the skew split of the layer backward when ws holds its plan (a group's
+  // rows are bounded by rows here, so the split is enabled at least as often as in the
+  // layer, whose bound is T; a plan in which no group exceeds the chunk gives the unsplit bits)
+  const bool skew = ws && offsets && aligned16(ws);
   return run_wgrad(cfg->act_dtype, cfg->wgrad_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream), accumulate,
-                   split);
+                   split, nullptr, 0, skew ? ws : nullptr, skew ? ws_bytes : 0, rows);
 }
 
 moe_status_t moe_quantize_fp8(int32_t src_dtype, const void* src, int64_t rows, int32_t cols, int32_t block_rows,
@@ -990,7 +1044,8 @@ moe_status_t moe_layer_bwd(const moe_config_t* cfg, const moe_weights_t* W, cons
   MOE_TRY(fork(s, ev.dy, s2));
   MOE_TRY(run_experts_bwd(c, sv->x_perm, sv->offsets, W->W13, W->W2, sv->H, sv->Act, bw.dY, bw.dH, bw.dX, gr->dW13,
                           gr->dW2, x, W->W13s, W->W2s, sv->H_s, sv->Act_s, dY_s, bw.dH_s, bw.dx_s, gr->dW13s,
-                          gr->dW2s, bw.sched, bw.dact, bw.wsplit, s, s2, ev.dh, beta, sv->token_of));
+                          gr->dW2s, bw.sched, bw.dact, bw.wsplit, bw.skew, bw.skew_bytes, s, s2, ev.dh, beta,
+                          sv->token_of));
   MOE_TRY(launch_router_bwd(c, sv->logits, sv->idx, sv->w, bw.dw, sv->counts, sv->seq_counts, daux, bw.dlogits, s));
   MOE_TRY(run_gate_bwd(c, x, W->Wg, bw.dlogits, gr->dWg, gr->dbg, bw.dx_r, bw.gate, s, beta));
   if (c.shared_gate) MOE_TRY(launch_shared_gate_bwd(c, x, bw.dl_s, gr->dWsg, bw.sg_part, s, beta));

@@ -100,6 +100,7 @@ struct MfmaArgs {
   const int32_t* gather;  // GA: source row of each grouped row (see the kernel)
   int gather_rows;        // rows of the gathered operand
   int gather_len;         // entries of gather (bounds the index loads)
+  const int32_t* skip;    // reduction-ragged: groups left to the skew split path, or NULL
 };
 
 // K-contiguous layout: element (r, k) of a stage tile at r * BK + ((k/8) ^ swk(r)) * 8 + k%8
@@ -235,6 +236,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_mfma_kernel(const MfmaArgs p) {
     grp = q / run;
     const int local = (h & 7) * run + (q - grp * run);
     if (grp >= p.G || local >= per) return;
+    if (p.skip && p.skip[grp]) return;
     const int band = local / (WG_BAND * p.nN);
     const int rem = local - band * WG_BAND * p.nN;
     const int bh = min(WG_BAND, p.nM - band * WG_BAND);
@@ -706,6 +708,7 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
   a.glu = g.glu;
   a.beta = g.beta;
   a.kchunk = g.kchunk;
+  a.skip = g.ragged == RAGGED_K ? g.skip : nullptr;
   int ga = 0;
   if (g.gather) {
     // the row gather is for the K-contiguous A of a row-ragged launch (the fc1 forward);

@@ -133,6 +133,13 @@ struct GemmDesc {
   // gather[k] of B.  gather_rows: rows of the gathered operand (bounds every gathered read).
   const int32_t* gather;
   int gather_rows;
+  // Skew splitting of reduction-ragged weight gradients (device tables of a split plan):
+  // skip[g] != 0: group g is left alone (its chunks are reduced elsewhere); pairs: group g
+  // reduces rows [pairs[2g], pairs[2g + 1]) instead of the offsets' range; gcount: the
+  // number of groups that exist (groups g >= *gcount do nothing).
+  const int32_t* skip;
+  const int32_t* pairs;
+  const int32_t* gcount;
 };
 
 // fp32-accumulating FMA GEMM for fp32 (and mixed fp32/bf16) operands; SwiGLU epilogues are
@@ -153,6 +160,31 @@ moe_status_t launch_wgrad2(const GemmDesc& g, hipStream_t s);
 // chunk (a multiple of 64) and the number of chunks, 1 when the output alone has enough
 // tiles to fill the chip (then kchunk = rows).  Partials: chunks * M * N fp32.
 struct WgradSplit { int chunks; int kchunk; };
+// Skew splitting of a grouped weight gradient dW[g] [M, N] (g < G) over ragged reduction
+// rows (`rows` in all, at most `max_group_rows` in one group), `tiles` output tiles per
+// group on a kernel that holds `slots` tiles at once.  A group with more rows than `chunk`
+// is cut into row chunks of `chunk` rows; each chunk is an fp32 partial of its own, and
+// the partials are summed in chunk order.  chunk 0: no group can exceed the balance point,
+// nothing is split.
+struct SkewPlan {
+  int chunk;      // rows per chunk (0: no split)
+  int max_vg;     // capacity: chunks of all split groups together
+  int max_split;  // capacity: split groups
+  size_t plan_bytes, partial_bytes;
+};
+SkewPlan skew_plan(int G, int64_t rows, int64_t max_group_rows, int M, int N, int tiles, int slots);
+// Builds the plan's device tables (one block): skip [G], gcount, nsplit, pairs [2 max_vg],
+// split_e / split_first / split_n [max_split] in `plan` (plan_bytes).
+moe_status_t launch_skew_plan(const int32_t* offsets, int G, const SkewPlan& sp, int32_t* plan, hipStream_t s);
+// Device table views of a plan buffer.
+struct SkewTables {
+  const int32_t *skip, *gcount, *nsplit, *pairs, *split_e, *split_first, *split_n;
+};
+SkewTables skew_tables(const int32_t* plan, int G, const SkewPlan& sp);
+// dW[split_e[j]] = sum_{c < split_n[j]} part[split_first[j] + c] (+ dW when beta), in
+// the weight-gradient dtype (bf16: rounded once), for j < *nsplit.
+moe_status_t launch_skew_reduce(const float* part, const SkewTables& t, const SkewPlan& sp, int64_t elems,
+                                void* dW, int64_t c_gstride, int out_dtype, int beta, hipStream_t s);
 WgradSplit wgrad_split(int M, int N, int64_t rows);
 size_t wgrad_split_bytes(int M, int N, int64_t rows);
 // out = sum of the `splits` fp32 partials [splits, elems] in order (+ out when beta), in the

@@ -40,6 +40,7 @@
 //     bf16 accumulate and fp32 outputs are separate
 //     kernels (a run-time branch between the epilogues makes the register allocator spill
 //     the accumulators).
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -77,6 +78,9 @@ struct WgArgs {
   int gather_rows, gather_len;
   int G, M, N, range_end, nM, nN;
   int beta;            // 1: add into C
+  const int32_t* skip;    // skew plan: groups left to the split path, or NULL
+  const int32_t* pairs;   // skew plan: [2 G] row range of each group (instead of offsets), or NULL
+  const int32_t* gcount;  // skew plan: groups that exist, or NULL
 };
 
 __device__ __forceinline__ int swm(int k) { return (k & 3) << 2; }
@@ -132,14 +136,15 @@ __device__ __forceinline__ void wgrad_body(const WgArgs& p) {
   const int grp = q8 / run;
   const int local = (h & 7) * run + (q8 - grp * run);
   if (grp >= p.G || local >= per) return;
+  if ((p.gcount && grp >= *p.gcount) || (p.skip && p.skip[grp])) return;
   const int band = local / (WG_BAND * p.nN);
   const int rem = local - band * WG_BAND * p.nN;
   const int bh = min(WG_BAND, p.nM - band * WG_BAND);
   const int nt = rem / bh;
   const int mt = band * WG_BAND + (rem - nt * bh);
   const int row_begin = mt * BM, n0 = nt * BN;
-  const int k_begin = p.offsets ? p.offsets[grp] : 0;
-  const int k_end = p.offsets ? p.offsets[grp + 1] : p.range_end;
+  const int k_begin = p.pairs ? p.pairs[2 * grp] : (p.offsets ? p.offsets[grp] : 0);
+  const int k_end = p.pairs ? p.pairs[2 * grp + 1] : (p.offsets ? p.offsets[grp + 1] : p.range_end);
   const int nk = k_end > k_begin ? (k_end - k_begin + BK - 1) / BK : 0;
   const int64_t cg = static_cast<int64_t>(grp) * p.c_gstride;
 
@@ -417,6 +422,164 @@ __global__ __launch_bounds__(NTHR, 2) void wgrad_f32_gather(const WgArgs p) { wg
 
 }  // namespace
 
+// ---------------------------------------------------------------- skew splitting
+// A group's weight-gradient tiles each reduce over all of the group's rows.  When one group
+// holds a large share of the rows (a long-tailed routing), its few tiles run for the whole
+// launch on a few CUs while the others idle.  The plan cuts every group with more rows
+// than the chunk into row chunks; the main launch skips those groups, one fp32 launch
+// computes a partial per chunk, and the partials are summed in chunk order.
+namespace {
+
+// One block: per group its chunk count (0 when not split), then two inclusive scans (chunk
+// counts and split flags) in LDS, then the tables.
+__global__ __launch_bounds__(1024) void skew_plan_kernel(const int32_t* __restrict__ offsets, int G, int chunk,
+                                                         int max_vg, int max_split, int32_t* __restrict__ plan) {
+  constexpr int NMAX = 4096;
+  __shared__ int sn[NMAX], sf[NMAX];
+  int32_t* skip = plan;
+  int32_t* gcount = plan + G;
+  int32_t* nsplit = plan + G + 1;
+  int32_t* pairs = plan + G + 2;
+  int32_t* split_e = pairs + 2 * max_vg;
+  int32_t* split_first = split_e + max_split;
+  int32_t* split_n = split_first + max_split;
+  auto nchunks = [&](int e) {
+    const int r = offsets[e + 1] - offsets[e];
+    return r > chunk ? (r + chunk - 1) / chunk : 0;
+  };
+  for (int e = threadIdx.x; e < NMAX; e += 1024) {
+    const int n = e < G ? nchunks(e) : 0;
+    if (e < G) skip[e] = n > 0;
+    sn[e] = n;
+    sf[e] = n > 0;
+  }
+  __syncthreads();
+  for (int off = 1; off < NMAX; off <<= 1) {
+    int a[NMAX / 1024], b[NMAX / 1024];
+#pragma unroll
+    for (int u = 0; u < NMAX / 1024; ++u) {
+      const int i = threadIdx.x + 1024 * u;
+      a[u] = i >= off ? sn[i - off] : 0;
+      b[u] = i >= off ? sf[i - off] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NMAX / 1024; ++u) {
+      sn[threadIdx.x + 1024 * u] += a[u];
+      sf[threadIdx.x + 1024 * u] += b[u];
+    }
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < G; e += 1024) {
+    const int n = nchunks(e);
+    if (n == 0) continue;
+    const int vb = sn[e] - n, j = sf[e] - 1;
+    if (j < max_split) {
+      split_e[j] = e;
+      split_first[j] = vb;
+      split_n[j] = n;
+    }
+    const int lo = offsets[e], hi = offsets[e + 1];
+    for (int c = 0; c < n && vb + c < max_vg; ++c) {
+      pairs[2 * (vb + c)] = lo + c * chunk;
+      pairs[2 * (vb + c) + 1] = min(lo + (c + 1) * chunk, hi);
+    }
+  }
+  if (threadIdx.x == 0) {
+    *gcount = min(G > 0 ? sn[G - 1] : 0, max_vg);
+    *nsplit = min(G > 0 ? sf[G - 1] : 0, max_split);
+  }
+}
+
+// dW[e] = the split group's partials summed in chunk order (+ dW when beta), four
+// elements a thread; blockIdx.y = split group j (those past *nsplit do nothing).
+__global__ __launch_bounds__(256) void skew_reduce_kernel(const float* __restrict__ part, int64_t elems,
+                                                          const int32_t* __restrict__ nsplit,
+                                                          const int32_t* __restrict__ split_e,
+                                                          const int32_t* __restrict__ split_first,
+                                                          const int32_t* __restrict__ split_n, int max_vg,
+                                                          void* __restrict__ dW, int64_t c_gstride, int out_bf16,
+                                                          int beta) {
+  const int j = blockIdx.y;
+  if (j >= *nsplit) return;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= elems) return;
+  // (the clamp keeps every read inside the partials even for offsets that break their
+  // contract; for valid offsets the plan's capacity always holds every chunk)
+  const int e = split_e[j], first = split_first[j], n = min(split_n[j], max_vg - first);
+  if (n < 1) return;
+  float4 v = *reinterpret_cast<const float4*>(part + static_cast<int64_t>(first) * elems + i);
+  for (int c = 1; c < n; ++c) {
+    const float4 u = *reinterpret_cast<const float4*>(part + static_cast<int64_t>(first + c) * elems + i);
+    v = make_float4(v.x + u.x, v.y + u.y, v.z + u.z, v.w + u.w);
+  }
+  const int64_t o = static_cast<int64_t>(e) * c_gstride + i;
+  if (out_bf16) {
+    uint2* dst = reinterpret_cast<uint2*>(static_cast<uint16_t*>(dW) + o);
+    if (beta) {   // one rounding of old + the fp32 sum
+      const uint2 old = *dst;
+      v.x += __uint_as_float(old.x << 16);
+      v.y += __uint_as_float(old.x & 0xFFFF0000u);
+      v.z += __uint_as_float(old.y << 16);
+      v.w += __uint_as_float(old.y & 0xFFFF0000u);
+    }
+    store_nt(dst, make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)));
+  } else {
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(dW) + o);
+    if (beta) {
+      const float4 old = *dst;
+      v = make_float4(old.x + v.x, old.y + v.y, old.z + v.z, old.w + v.w);
+    }
+    store_nt(dst, v);
+  }
+}
+
+}  // namespace
+
+SkewPlan skew_plan(int G, int64_t rows, int64_t max_group_rows, int M, int N, int tiles, int slots) {
+  SkewPlan sp{};
+  if (G < 1 || G > 4096 || rows <= 0 || tiles <= 0 || slots <= 0) return sp;
+  // a balanced launch gives each slot rows * tiles / slots rows of work; a chunk is a
+  // quarter of that (at least 1024 rows), so the longest tile is a quarter of a slot's work
+  int64_t chunk = std::max<int64_t>(1024, ceil_div(ceil_div(rows * tiles, slots), 4));
+  chunk = ceil_div(chunk, 256) * 256;
+  if (chunk >= max_group_rows || chunk >= rows || chunk >= (int64_t{1} << 30)) return sp;
+  sp.chunk = static_cast<int>(chunk);
+  sp.max_split = static_cast<int>(rows / chunk);                       // each split group has > chunk rows
+  sp.max_vg = static_cast<int>(ceil_div(rows, chunk)) + sp.max_split;  // sum of ceil(r / chunk) over them
+  sp.plan_bytes = static_cast<size_t>(G + 2 + 2 * sp.max_vg + 3 * sp.max_split) * 4;
+  sp.partial_bytes = static_cast<size_t>(sp.max_vg) * M * N * 4;
+  return sp;
+}
+
+SkewTables skew_tables(const int32_t* plan, int G, const SkewPlan& sp) {
+  SkewTables t;
+  t.skip = plan;
+  t.gcount = plan + G;
+  t.nsplit = plan + G + 1;
+  t.pairs = plan + G + 2;
+  t.split_e = t.pairs + 2 * sp.max_vg;
+  t.split_first = t.split_e + sp.max_split;
+  t.split_n = t.split_first + sp.max_split;
+  return t;
+}
+
+moe_status_t launch_skew_plan(const int32_t* offsets, int G, const SkewPlan& sp, int32_t* plan, hipStream_t s) {
+  if (G < 1 || G > 4096) return fail(MOE_ERR_UNSUPPORTED, "skew plan: 1 to 4096 groups");
+  skew_plan_kernel<<<1, 1024, 0, s>>>(offsets, G, sp.chunk, sp.max_vg, sp.max_split, plan);
+  return check_launch("skew_plan");
+}
+
+moe_status_t launch_skew_reduce(const float* part, const SkewTables& t, const SkewPlan& sp, int64_t elems,
+                                void* dW, int64_t c_gstride, int out_dtype, int beta, hipStream_t s) {
+  if (elems % 4 || c_gstride % 4) return fail(MOE_ERR_UNSUPPORTED, "skew reduce: sizes must be multiples of 4");
+  if (sp.max_split < 1 || elems == 0) return MOE_OK;
+  const dim3 grid(static_cast<unsigned>(ceil_div(elems / 4, 256)), static_cast<unsigned>(sp.max_split));
+  skew_reduce_kernel<<<grid, 256, 0, s>>>(part, elems, t.nsplit, t.split_e, t.split_first, t.split_n, sp.max_vg, dW,
+                                          c_gstride, out_dtype == MOE_BF16, beta);
+  return check_launch("skew_reduce");
+}
+
 bool wgrad2_supported(const GemmDesc& g) {
   return g.ragged == RAGGED_K && g.epi == EPI_STORE && g.a_major == MN_MAJOR && g.b_major == MN_MAJOR &&
          g.a_type == MOE_BF16 && g.b_type == MOE_BF16 && g.kchunk == 0 && g.M % 8 == 0 && g.N % 8 == 0 &&
@@ -425,7 +588,7 @@ bool wgrad2_supported(const GemmDesc& g) {
 
 moe_status_t launch_wgrad2(const GemmDesc& g, hipStream_t s) {
   if (!wgrad2_supported(g)) return fail(MOE_ERR_UNSUPPORTED, "wgrad: unsupported operand combination");
-  const int groups = g.offsets ? g.G : 1;
+  const int groups = g.offsets || g.pairs ? g.G : 1;
   if (groups < 1) return MOE_OK;
   WgArgs a{};
   a.A = static_cast<const uint16_t*>(g.A);
@@ -441,6 +604,9 @@ moe_status_t launch_wgrad2(const GemmDesc& g, hipStream_t s) {
   a.N = g.N;
   a.range_end = g.range_end;
   a.beta = g.beta;
+  a.skip = g.skip;
+  a.pairs = g.pairs;
+  a.gcount = g.gcount;
   a.nM = static_cast<int>(ceil_div(g.M, BM));
   a.nN = static_cast<int>(ceil_div(g.N, BN));
   if (a.nM <= 0 || a.nN <= 0) return MOE_OK;

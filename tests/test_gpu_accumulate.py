@@ -210,3 +210,72 @@ def test_grouped_wgrad_split_k():
     small = torch.empty(3 * N * K * 4 - 16, dtype=torch.uint8, device=dev())
     with pytest.raises(L.MoeError, match="workspace"):
         L.grouped_wgrad(c32, None, 1, rows, dY_d, N, X_d, K, split32, ws=small)
+
+
+@pytest.mark.parametrize("K", [320, 1024])
+def test_grouped_wgrad_skew_split(K):
+    """Groups with more rows than the skew plan's chunk (1024 rows here) are cut into row
+    chunks when ws is given: 3000 rows in three chunks, 1025 and 2049 with a one-row last
+    chunk, 1024 left whole.  The unsplit groups give the bits of the call without ws, the
+    split ones the fp64 sum within fp32 rounding; the bf16 output is the fp32 split sum
+    rounded once, accumulation adds to it in fp32 first, groups without rows keep their
+    gradient, the row gather of X (K = 1024) gives the same bits, and a workspace too small
+    for the plan gives the unsplit call's bits."""
+    torch = torch_mod()
+    from mixture_experts_layer_aux_amd import _lib as L
+    print(f"grouped wgrad skew split K={K}", flush=True)
+    shape = W.SMALL[2]
+    c16, c32 = L.config_from_shape(shape, wgrad="bf16"), L.config_from_shape(shape, wgrad="f32")
+    rng = np.random.default_rng(33)
+    sizes = np.array([3000, 0, 37, 1025, 1024, 0, 1, 2049, 512], dtype=np.int64)
+    G, N = len(sizes), 192
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(off[-1])
+    dY = rng.standard_normal((rows, N)).astype(np.float32)
+    X = rng.standard_normal((rows, K)).astype(np.float32)
+    bits = lambda a: torch.from_numpy(W.f32_to_bf16_bits(a).view(np.int16)).view(torch.bfloat16)  # noqa: E731
+    dY_d, X_d = bits(dY).to(dev()), bits(X).to(dev())
+    off_d = torch.from_numpy(off).to(dev())
+    ws = torch.empty(20 * N * K * 4 + (1 << 16), dtype=torch.uint8, device=dev())
+    e32 = lambda: torch.full((G, N, K), 7.0, dtype=torch.float32, device=dev())  # noqa: E731
+    e16 = lambda: torch.full((G, N, K), 7.0, dtype=torch.bfloat16, device=dev())  # noqa: E731
+    whole, split32, split16 = e32(), e32(), e16()
+    L.grouped_wgrad(c32, off_d, G, rows, dY_d, N, X_d, K, whole)
+    L.grouped_wgrad(c32, off_d, G, rows, dY_d, N, X_d, K, split32, ws=ws)
+    L.grouped_wgrad(c16, off_d, G, rows, dY_d, N, X_d, K, split16, ws=ws)
+    prior16 = _prior({"dW": split16}, seed=5)["dW"]
+    prior32 = _prior({"dW": split32}, seed=6)["dW"]
+    acc16, acc32 = prior16.clone(), prior32.clone()
+    L.grouped_wgrad(c16, off_d, G, rows, dY_d, N, X_d, K, acc16, ws=ws, accumulate=True)
+    L.grouped_wgrad(c32, off_d, G, rows, dY_d, N, X_d, K, acc32, ws=ws, accumulate=True)
+    tiny = torch.empty(4096, dtype=torch.uint8, device=dev())
+    small32 = e32()
+    L.grouped_wgrad(c32, off_d, G, rows, dY_d, N, X_d, K, small32, ws=tiny)
+    torch.cuda.synchronize()
+    assert torch.equal(small32, whole), "a workspace too small for the plan: no split"
+    assert torch.equal(split16, split32.to(torch.bfloat16)), "bf16 split output is the fp32 split sum rounded once"
+    assert torch.equal(acc16, _expected(prior16, split32)), "bf16 split accumulation"
+    assert torch.equal(acc32, _expected(prior32, split32)), "fp32 split accumulation"
+    for g in np.where(sizes == 0)[0]:
+        assert torch.equal(acc16[g], prior16[g]) and torch.equal(acc32[g], prior32[g]), f"empty group {g}"
+    for g in np.where(sizes <= 1024)[0]:
+        assert torch.equal(split32[g], whole[g]), f"group {g} ({sizes[g]} rows) is not split"
+    dY64 = W.bf16_bits_to_f32(W.f32_to_bf16_bits(dY)).astype(np.float64)
+    X64 = W.bf16_bits_to_f32(W.f32_to_bf16_bits(X)).astype(np.float64)
+    got_s, got_w = to_np(split32), to_np(whole)
+    for g in range(G):
+        ref = dY64[off[g]:off[g + 1]].T @ X64[off[g]:off[g + 1]]
+        for name, got in (("split", got_s), ("whole", got_w)):
+            err = np.abs(got[g] - ref).max() / max(1.0, np.sqrt(max(sizes[g], 1)))
+            assert err < 1e-4, f"{name} group {g}: {err:.2e}"
+    assert not torch.equal(split32[0], whole[0]), "the 3000-row group was not split"
+    if K >= 1024:
+        src_rows = rows + 37
+        perm = rng.permutation(src_rows)[:rows].astype(np.int32)
+        Xsrc = torch.zeros(src_rows, K, dtype=X_d.dtype, device=dev())
+        Xsrc[torch.from_numpy(perm).long().to(dev())] = X_d
+        x_rows = torch.from_numpy(perm).to(dev())
+        g16 = e16()
+        L.grouped_wgrad(c16, off_d, G, rows, dY_d, N, Xsrc, K, g16, ws=ws, x_rows=x_rows)
+        torch.cuda.synchronize()
+        assert torch.equal(g16, split16), "split through x_rows"

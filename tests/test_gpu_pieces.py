@@ -163,14 +163,16 @@ def check_grouped_experts(shape, cid):
     L.grouped_gemm_swiglu_bwd(cfg, x_perm, off, W13, W2, H, Act, dYp, dH, dXp, dW13, dW2, x if Fs else None, W13s,
                               W2s, H_s, Act_s, dy if Fs else None, dH_s, dx_s, dW13s, dW2s, ws)
     # the same backward as data gradients only, then the four weight gradients through
-    # moe_grouped_wgrad: the same kernels on the same inputs, so the same bits
+    # moe_grouped_wgrad: the same kernels on the same inputs, so the same bits (the routed
+    # calls get the layer workspace, so a long-tailed load splits its busiest experts'
+    # rows the same way the layer backward does)
     dH2, dXp2 = e(A, 2 * F), e32(A, d)
     dH2_s, dx2_s = (e(T, 2 * Fs), e32(T, d)) if Fs else (None, None)
     L.grouped_gemm_swiglu_bwd(cfg, x_perm, off, W13, W2, H, Act, dYp, dH2, dXp2, None, None, x if Fs else None, W13s,
                               W2s, H_s, Act_s, dy if Fs else None, dH2_s, dx2_s, None, None, ws)
     sW13, sW2 = ew(E, 2 * F, d), ew(E, d, F)
-    L.grouped_wgrad(cfg, off, E, A, dH2, 2 * F, x_perm, d, sW13)
-    L.grouped_wgrad(cfg, off, E, A, dYp, d, Act, F, sW2)
+    L.grouped_wgrad(cfg, off, E, A, dH2, 2 * F, x_perm, d, sW13, ws=ws)
+    L.grouped_wgrad(cfg, off, E, A, dYp, d, Act, F, sW2, ws=ws)
     split = [(dH, dH2), (dXp, dXp2), (dW13, sW13), (dW2, sW2)]
     if Fs:
         sW13s, sW2s = ew(2 * Fs, d), ew(d, Fs)
@@ -182,8 +184,8 @@ def check_grouped_experts(shape, cid):
         # their round-to-nearest-even
         c32 = L.config_from_shape(shape, wgrad="f32")
         fW13, fW2 = e32(E, 2 * F, d), e32(E, d, F)
-        L.grouped_wgrad(c32, off, E, A, dH2, 2 * F, x_perm, d, fW13)
-        L.grouped_wgrad(c32, off, E, A, dYp, d, Act, F, fW2)
+        L.grouped_wgrad(c32, off, E, A, dH2, 2 * F, x_perm, d, fW13, ws=ws)
+        L.grouped_wgrad(c32, off, E, A, dYp, d, Act, F, fW2, ws=ws)
         split += [(dW13, fW13.to(torch.bfloat16)), (dW2, fW2.to(torch.bfloat16))]
         if Fs:
             fW13s, fW2s = e32(2 * Fs, d), e32(d, Fs)
@@ -210,11 +212,11 @@ def check_grouped_experts(shape, cid):
         if Fs:
             split += [(dW13s, gW13s), (dW2s, gW2s), (dx_s, gdx_s)]
         xW13 = ew(E, 2 * F, d)
-        L.grouped_wgrad(cfg, off, E, A, dH2, 2 * F, x, d, xW13, x_rows=tok)
+        L.grouped_wgrad(cfg, off, E, A, dH2, 2 * F, x, d, xW13, x_rows=tok, ws=ws)
         split += [(dW13, xW13)]
         if cfg.wgrad_dtype == L.MOE_BF16:
             xW13f = e32(E, 2 * F, d)
-            L.grouped_wgrad(c32, off, E, A, dH2, 2 * F, x, d, xW13f, x_rows=tok)
+            L.grouped_wgrad(c32, off, E, A, dH2, 2 * F, x, d, xW13f, x_rows=tok, ws=ws)
             split += [(fW13, xW13f)]
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(split):
