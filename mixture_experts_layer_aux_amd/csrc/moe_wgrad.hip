@@ -77,6 +77,7 @@ struct WgArgs {
   const int32_t* gather;    // NULL, or the source row of each reduction row
   int gather_rows, gather_len;
   int G, M, N, range_end, nM, nN;
+  int band;            // row tiles per band of an XCD's run of a group's tiles (wgrad_band)
   int beta;            // 1: add into C
   const int32_t* skip;    // skew plan: groups left to the split path, or NULL
   const int32_t* pairs;   // skew plan: [2 G] row range of each group (instead of offsets), or NULL
@@ -127,8 +128,9 @@ __device__ __forceinline__ void wgrad_body(const WgArgs& p) {
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---------------------------------------------------------------- tile
-  // each group's tiles in 8 runs, one per XCD, bands of 4 row tiles walked column by column
-  constexpr int WG_BAND = 4;
+  // each group's tiles in 8 runs, one per XCD, bands of p.band row tiles walked column by
+  // column
+  const int WG_BAND = p.band;
   const int per = p.nM * p.nN;
   const int run = (per + 7) >> 3;
   const int h = blockIdx.x;
@@ -536,12 +538,16 @@ __global__ __launch_bounds__(256) void skew_reduce_kernel(const float* __restric
 
 }  // namespace
 
+#ifndef MOE_SKEW_PARTS
+#define MOE_SKEW_PARTS 2
+#endif
 SkewPlan skew_plan(int G, int64_t rows, int64_t max_group_rows, int M, int N, int tiles, int slots) {
   SkewPlan sp{};
   if (G < 1 || G > 4096 || rows <= 0 || tiles <= 0 || slots <= 0) return sp;
-  // a balanced launch gives each slot rows * tiles / slots rows of work; a chunk is a
-  // quarter of that (at least 1024 rows), so the longest tile is a quarter of a slot's work
-  int64_t chunk = std::max<int64_t>(1024, ceil_div(ceil_div(rows * tiles, slots), 4));
+  // a balanced launch gives each slot rows * tiles / slots rows of work; a chunk is half
+  // of that (at least 1024 rows), so no tile is longer than half a slot's share (a quarter
+  // or an eighth left the fp32 partials and their sum costing more than the balance won)
+  int64_t chunk = std::max<int64_t>(1024, ceil_div(ceil_div(rows * tiles, slots), MOE_SKEW_PARTS));
   chunk = ceil_div(chunk, 256) * 256;
   if (chunk >= max_group_rows || chunk >= rows || chunk >= (int64_t{1} << 30)) return sp;
   sp.chunk = static_cast<int>(chunk);
@@ -586,6 +592,29 @@ bool wgrad2_supported(const GemmDesc& g) {
          g.lda % 8 == 0 && g.ldb % 8 == 0 && g.ldc % 8 == 0 && g.c_gstride % 8 == 0;
 }
 
+// Band height of the tile walk.  An XCD runs an eighth of a group's tiles, band after
+// band, each band's row tiles column by column, so in a run of r tiles it reads the dY
+// columns of about b row tiles and the X columns of r / b column tiles.  b minimises that
+// footprint, b BM + ceil(r / b) BN operand columns, over 1, 2 and 4 up to nM (the smaller
+// b on a tie).  The 112-tile runs of the DeepSeek-V3-shaped fc1 gradient would take b = 8,
+// which was slower there (9.19 against 9.06 ms) though its footprint is smaller.
+static int wgrad_band(int nM, int nN) {
+#ifdef MOE_WG_BAND_FIXED
+  return std::min(MOE_WG_BAND_FIXED, nM);
+#endif
+  const int64_t run = ceil_div(static_cast<int64_t>(nM) * nN, 8);
+  int best = 1;
+  int64_t best_cols = INT64_MAX;
+  for (int b = 1; b <= nM && b <= 4; b *= 2) {
+    const int64_t cols = static_cast<int64_t>(b) * BM + ceil_div(run, b) * BN;
+    if (cols < best_cols) {
+      best_cols = cols;
+      best = b;
+    }
+  }
+  return best;
+}
+
 moe_status_t launch_wgrad2(const GemmDesc& g, hipStream_t s) {
   if (!wgrad2_supported(g)) return fail(MOE_ERR_UNSUPPORTED, "wgrad: unsupported operand combination");
   const int groups = g.offsets || g.pairs ? g.G : 1;
@@ -610,6 +639,7 @@ moe_status_t launch_wgrad2(const GemmDesc& g, hipStream_t s) {
   a.nM = static_cast<int>(ceil_div(g.M, BM));
   a.nN = static_cast<int>(ceil_div(g.N, BN));
   if (a.nM <= 0 || a.nN <= 0) return MOE_OK;
+  a.band = wgrad_band(a.nM, a.nN);
   if (g.gather) {
     if (static_cast<int64_t>(g.gather_rows) * g.ldb * 2 > kOob - 4096)
       return fail(MOE_ERR_UNSUPPORTED, "wgrad: gathered operand above 2 GB");
