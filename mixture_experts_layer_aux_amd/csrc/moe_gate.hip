@@ -51,25 +51,54 @@ __global__ __launch_bounds__(256) void sum_parts_kernel(const float* __restrict_
   out[r * out_ld + c] = v;
 }
 
-// Column sums in a fixed order: partial sums over 256-row chunks (rows in order), then
-// the chunk sums in chunk order.
-constexpr int kColChunk = 256;
+// Column sums in a fixed order: partial sums over 64-row chunks (rows in order), then per
+// column 16 interleaved runs of chunks (run g: chunks g, g + 16, ..., in order), then the
+// 16 run sums in run order.  Each thread keeps 16 loads in flight, so neither pass waits on
+// one load at a time.
+constexpr int kColChunk = 64, kColRuns = 16, kColUnroll = 16;
 __global__ __launch_bounds__(256) void colsum_part_kernel(const float* __restrict__ X, int rows, int cols,
                                                           float* __restrict__ part) {
   const int col = blockIdx.x * 256 + threadIdx.x;
   if (col >= cols) return;
   const int r0 = blockIdx.y * kColChunk, r1 = min(rows, r0 + kColChunk);
   float s = 0.0f;
-  for (int r = r0; r < r1; ++r) s += X[static_cast<int64_t>(r) * cols + col];
+  int r = r0;
+  for (; r + kColUnroll <= r1; r += kColUnroll) {
+    float v[kColUnroll];
+#pragma unroll
+    for (int u = 0; u < kColUnroll; ++u) v[u] = X[static_cast<int64_t>(r + u) * cols + col];
+#pragma unroll
+    for (int u = 0; u < kColUnroll; ++u) s += v[u];
+  }
+  for (; r < r1; ++r) s += X[static_cast<int64_t>(r) * cols + col];
   part[static_cast<int64_t>(blockIdx.y) * cols + col] = s;
 }
-__global__ __launch_bounds__(256) void colsum_final_kernel(const float* __restrict__ part, int nchunk, int cols,
-                                                           float* __restrict__ out, int beta) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= cols) return;
+// block: 64 columns x kColRuns runs (1024 threads)
+__global__ __launch_bounds__(1024) void colsum_final_kernel(const float* __restrict__ part, int nchunk, int cols,
+                                                            float* __restrict__ out, int beta) {
+  __shared__ float srun[kColRuns][64];
+  const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + c;
   float s = 0.0f;
-  for (int q = 0; q < nchunk; ++q) s += part[static_cast<int64_t>(q) * cols + col];
-  out[col] = beta ? out[col] + s : s;
+  if (col < cols) {
+    int q = g;
+    for (; q + (kColUnroll - 1) * kColRuns < nchunk; q += kColUnroll * kColRuns) {
+      float v[kColUnroll];
+#pragma unroll
+      for (int u = 0; u < kColUnroll; ++u) v[u] = part[static_cast<int64_t>(q + u * kColRuns) * cols + col];
+#pragma unroll
+      for (int u = 0; u < kColUnroll; ++u) s += v[u];
+    }
+    for (; q < nchunk; q += kColRuns) s += part[static_cast<int64_t>(q) * cols + col];
+  }
+  srun[g][c] = s;
+  __syncthreads();
+  if (g == 0 && col < cols) {
+    float t = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kColRuns; ++h) t += srun[h][c];
+    out[col] = beta ? out[col] + t : t;
+  }
 }
 
 // slot patterns (2 bits per slot: part index 0 = hi, 1 = mid, 2 = lo)
@@ -137,8 +166,9 @@ moe_status_t launch_gate_fwd_mfma(const moe_config_t& c, const void* x, const fl
 moe_status_t launch_colsum_ws(const float* X, int rows, int cols, float* out, float* part, hipStream_t s, int beta) {
   const int nchunk = static_cast<int>(ceil_div(rows, kColChunk));
   if (nchunk == 0) return MOE_OK;
+  if (nchunk > 65535) return fail(MOE_ERR_UNSUPPORTED, "column sums: at most 65535 x 64 rows");
   colsum_part_kernel<<<dim3(static_cast<unsigned>(ceil_div(cols, 256)), nchunk), 256, 0, s>>>(X, rows, cols, part);
-  colsum_final_kernel<<<static_cast<unsigned>(ceil_div(cols, 256)), 256, 0, s>>>(part, nchunk, cols, out, beta);
+  colsum_final_kernel<<<static_cast<unsigned>(ceil_div(cols, 64)), 1024, 0, s>>>(part, nchunk, cols, out, beta);
   return check_launch("colsum");
 }
 
