@@ -344,10 +344,26 @@ __global__ __launch_bounds__(1024) void seq_finalize_kernel(const int32_t* __res
     const int b = pair / E, e = pair - b * E;
     int cnt = 0;
     float P = 0.0f;
-    for (int c = 0; c < nsc; ++c) {
-      const int64_t i = (static_cast<int64_t>(b) * nsc + c) * E + e;
-      cnt += cnt_part[i];
-      P += prob_part[i];
+    // the chunks in order, 8 of each part's loads in flight before they are added
+    const int64_t i0 = static_cast<int64_t>(b) * nsc * E + e;
+    int c = 0;
+    for (; c + 8 <= nsc; c += 8) {
+      int cv[8];
+      float pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        cv[u] = cnt_part[i0 + static_cast<int64_t>(c + u) * E];
+        pv[u] = prob_part[i0 + static_cast<int64_t>(c + u) * E];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        cnt += cv[u];
+        P += pv[u];
+      }
+    }
+    for (; c < nsc; ++c) {
+      cnt += cnt_part[i0 + static_cast<int64_t>(c) * E];
+      P += prob_part[i0 + static_cast<int64_t>(c) * E];
     }
     seq_counts[pair] = cnt;
     dot += static_cast<double>(P) * cnt;
