@@ -206,9 +206,8 @@ moe_status_t moe_validate(const moe_config_t* cfg);
 /* Workspace bytes the forward (router, permute, layer forward) and backward calls need.
  * Host only.  One workspace of max(fwd, bwd) bytes serves every call.  On bf16 layers
  * whose skew-split chunk (see moe_grouped_wgrad) is below T, the backward bytes include
- * the split's plan and (ceil(A / chunk) + floor(A / chunk)) fp32 partials of N x K for the
- * larger of the two routed
- * weight gradients (268 MB on the Qwen3-Next-shaped layer). */
+ * the split's plan and (ceil(A / chunk) + floor(A / chunk)) fp32 partials of N x K for
+ * the larger of the two routed weight gradients (268 MB on the Qwen3-Next-shaped layer). */
 moe_status_t moe_workspace_size(const moe_config_t* cfg, size_t* fwd_bytes, size_t* bwd_bytes);
 
 /* Router logits = x Wg^T (+ bg), fp32 ([HB] §3.1 Router scoring, Precision: the router's
