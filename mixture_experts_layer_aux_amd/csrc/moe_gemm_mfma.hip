@@ -158,26 +158,40 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Tiles of a row-ragged launch: group g has ceil(rows_g / 256) row tiles.
 // prefix [G + 1] of the row tiles, then owner[m] = the group of row tile m (cap entries;
-// a count past cap is the caller's broken offsets, and the writes stop there).
+// a count past cap is the caller's broken offsets, and the writes stop there).  G <= 2048:
+// thread i holds groups 2i and 2i + 1; a wave-level scan, then the 16 wave totals; each
+// owner entry is found by a binary search of the inclusive prefix.
 __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ offsets, int G, int cap,
                                                            int32_t* __restrict__ prefix) {
-  __shared__ int s[2048];
-  for (int g = threadIdx.x; g < 2048; g += 1024)
-    s[g] = g < G ? max(0, (offsets[g + 1] - offsets[g] + BM - 1) / BM) : 0;
-  __syncthreads();
-  for (int off = 1; off < 2048; off <<= 1) {
-    const int i0 = threadIdx.x, i1 = threadIdx.x + 1024;
-    const int a0 = i0 >= off ? s[i0 - off] : 0;
-    const int a1 = i1 >= off ? s[i1 - off] : 0;
-    __syncthreads();
-    s[i0] += a0;
-    s[i1] += a1;
-    __syncthreads();
+  __shared__ int s[2048];   // inclusive prefix of the row tiles
+  __shared__ int wtot[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g0 = 2 * tid, g1 = g0 + 1;
+  const int c0 = g0 < G ? max(0, (offsets[g0 + 1] - offsets[g0] + BM - 1) / BM) : 0;
+  const int c1 = g1 < G ? max(0, (offsets[g1 + 1] - offsets[g1] + BM - 1) / BM) : 0;
+  int v = c0 + c1;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
   }
-  for (int g = threadIdx.x; g <= G; g += 1024) prefix[g] = g == 0 ? 0 : s[g - 1];
+  if (lane == 63) wtot[w] = v;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) v += wtot[i];
+  s[g1] = v;
+  s[g0] = v - c1;
+  __syncthreads();
+  for (int g = tid; g <= G; g += 1024) prefix[g] = g == 0 ? 0 : s[g - 1];
   int32_t* owner = prefix + G + 1;
-  for (int g = threadIdx.x; g < G; g += 1024)
-    for (int m = g ? s[g - 1] : 0; m < s[g] && m < cap; ++m) owner[m] = g;
+  const int lim = G > 0 ? min(s[G - 1], cap) : 0;
+  for (int m = tid; m < lim; m += 1024) {
+    int lo = 0, hi = G - 1;   // the first group whose inclusive prefix exceeds m
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s[mid] > m) hi = mid;
+      else lo = mid + 1;
+    }
+    owner[m] = lo;
+  }
 }
 
 // Byte offset past the end of every gathered operand (bounded below 2^31 at launch): a
@@ -732,6 +746,7 @@ moe_status_t launch_gemm_mfma(const GemmDesc& g, int32_t* sched, hipStream_t s) 
     a.nN = static_cast<int>(g.epi == EPI_SWIGLU_FWD ? ceil_div(g.N, 256) : ceil_div(g.N, BN));
     int64_t upper;
     if (g.offsets) {
+      if (g.G > 2048) return fail(MOE_ERR_UNSUPPORTED, "mfma gemm: more than 2048 row-ragged groups");
       a.tile_cap = static_cast<int>(ceil_div(g.rows_upper, int64_t{BM}) + g.G);
       tile_prefix_kernel<<<1, 1024, 0, s>>>(g.offsets, g.G, a.tile_cap, sched);
       upper = (ceil_div(g.rows_upper, BM) + g.G) * a.nN;
