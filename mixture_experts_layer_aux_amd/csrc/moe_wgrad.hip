@@ -432,12 +432,12 @@ __global__ __launch_bounds__(NTHR, 2) void wgrad_f32_gather(const WgArgs p) { wg
 // computes a partial per chunk, and the partials are summed in chunk order.
 namespace {
 
-// One block: per group its chunk count (0 when not split), then two inclusive scans (chunk
-// counts and split flags) in LDS, then the tables.
+// One block, thread i holding groups 4i .. 4i + 3 (G <= 4096): per group its chunk count
+// (0 when not split) and split flag, their prefix sums by wave shuffles and the 16 wave
+// totals, then the tables.
 __global__ __launch_bounds__(1024) void skew_plan_kernel(const int32_t* __restrict__ offsets, int G, int chunk,
                                                          int max_vg, int max_split, int32_t* __restrict__ plan) {
-  constexpr int NMAX = 4096;
-  __shared__ int sn[NMAX], sf[NMAX];
+  __shared__ int wn[16], wf[16];
   int32_t* skip = plan;
   int32_t* gcount = plan + G;
   int32_t* nsplit = plan + G + 1;
@@ -445,51 +445,59 @@ __global__ __launch_bounds__(1024) void skew_plan_kernel(const int32_t* __restri
   int32_t* split_e = pairs + 2 * max_vg;
   int32_t* split_first = split_e + max_split;
   int32_t* split_n = split_first + max_split;
-  auto nchunks = [&](int e) {
-    const int r = offsets[e + 1] - offsets[e];
-    return r > chunk ? (r + chunk - 1) / chunk : 0;
-  };
-  for (int e = threadIdx.x; e < NMAX; e += 1024) {
-    const int n = e < G ? nchunks(e) : 0;
-    if (e < G) skip[e] = n > 0;
-    sn[e] = n;
-    sf[e] = n > 0;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int n[4], tn = 0, tf = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = 4 * tid + u;
+    n[u] = 0;
+    if (e < G) {
+      const int r = offsets[e + 1] - offsets[e];
+      n[u] = r > chunk ? (r + chunk - 1) / chunk : 0;
+      skip[e] = n[u] > 0;
+    }
+    tn += n[u];
+    tf += n[u] > 0;
+  }
+  int in = tn, inf = tf;   // inclusive prefixes at the thread's last group
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a = __shfl_up(in, o, 64), b = __shfl_up(inf, o, 64);
+    if (lane >= o) {
+      in += a;
+      inf += b;
+    }
+  }
+  if (lane == 63) {
+    wn[w] = in;
+    wf[w] = inf;
   }
   __syncthreads();
-  for (int off = 1; off < NMAX; off <<= 1) {
-    int a[NMAX / 1024], b[NMAX / 1024];
-#pragma unroll
-    for (int u = 0; u < NMAX / 1024; ++u) {
-      const int i = threadIdx.x + 1024 * u;
-      a[u] = i >= off ? sn[i - off] : 0;
-      b[u] = i >= off ? sf[i - off] : 0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < NMAX / 1024; ++u) {
-      sn[threadIdx.x + 1024 * u] += a[u];
-      sf[threadIdx.x + 1024 * u] += b[u];
-    }
-    __syncthreads();
+  for (int i = 0; i < w; ++i) {
+    in += wn[i];
+    inf += wf[i];
   }
-  for (int e = threadIdx.x; e < G; e += 1024) {
-    const int n = nchunks(e);
-    if (n == 0) continue;
-    const int vb = sn[e] - n, j = sf[e] - 1;
-    if (j < max_split) {
-      split_e[j] = e;
-      split_first[j] = vb;
-      split_n[j] = n;
+  int vb = in - tn, j = inf - tf;   // first chunk and split index of the thread's first group
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = 4 * tid + u;
+    if (n[u] > 0) {
+      if (j < max_split) {
+        split_e[j] = e;
+        split_first[j] = vb;
+        split_n[j] = n[u];
+      }
+      const int lo = offsets[e], hi = offsets[e + 1];
+      for (int c = 0; c < n[u] && vb + c < max_vg; ++c) {
+        pairs[2 * (vb + c)] = lo + c * chunk;
+        pairs[2 * (vb + c) + 1] = min(lo + (c + 1) * chunk, hi);
+      }
+      ++j;
     }
-    const int lo = offsets[e], hi = offsets[e + 1];
-    for (int c = 0; c < n && vb + c < max_vg; ++c) {
-      pairs[2 * (vb + c)] = lo + c * chunk;
-      pairs[2 * (vb + c) + 1] = min(lo + (c + 1) * chunk, hi);
-    }
+    vb += n[u];
   }
-  if (threadIdx.x == 0) {
-    *gcount = min(G > 0 ? sn[G - 1] : 0, max_vg);
-    *nsplit = min(G > 0 ? sf[G - 1] : 0, max_split);
+  if (tid == 1023) {   // its inclusive prefixes cover all 4096 slots
+    *gcount = min(in, max_vg);
+    *nsplit = min(inf, max_split);
   }
 }
 
