@@ -397,7 +397,8 @@ moe_status_t moe_grouped_gemm_swiglu_bwd(const moe_config_t* cfg, const void* x_
  * whole call.  The chunk is a quarter of the rows one of the kernel's tile slots holds in
  * a balanced launch (rows x tiles / slots), at least 1024.  Each chunk is an fp32 partial
  * in ws, and the partials are summed in chunk order; the other groups are computed as
- * without ws.  The plan is built on the device from offsets (no host sync).  It is the one
+ * without ws.  The split is enabled only when the chunk is below cfg->T (an expert holds
+ * at most T rows) and below rows.  The plan is built on the device from offsets (no host sync).  It is the one
  * moe_layer_bwd and moe_grouped_gemm_swiglu_bwd use for the routed experts, so the call
  * gives their bits.  A ws too small for the plan: no split.
  * x_rows (bf16 activations; NULL: none): reduction row r of X is row x_rows[r] of X, which

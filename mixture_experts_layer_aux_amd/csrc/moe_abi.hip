@@ -891,7 +891,7 @@ moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, 
     if (x_src_rows < 1) return fail(MOE_ERR_INVALID_ARG, "x_src_rows must be >= 1 with x_rows");
     const bool skew = ws && offsets && aligned16(ws);
     return run_wgrad(cfg->act_dtype, cfg->wgrad_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream), accumulate,
-                     nullptr, x_rows, x_src_rows, skew ? ws : nullptr, skew ? ws_bytes : 0, rows);
+                     nullptr, x_rows, x_src_rows, skew ? ws : nullptr, skew ? ws_bytes : 0, std::min<int64_t>(rows, cfg->T));
   }
   float* split = nullptr;
   if (ws && !offsets && cfg->act_dtype == MOE_BF16) {
@@ -902,12 +902,12 @@ moe_status_t moe_grouped_wgrad(const moe_config_t* cfg, const int32_t* offsets, 
       split = static_cast<float*>(ws);
     }
   }
-  // with offsets: the skew split of the layer backward when ws holds its plan (a group's
-  // rows are bounded by rows here, so the split is enabled at least as often as in the
-  // layer, whose bound is T; a plan in which no group exceeds the chunk gives the unsplit bits)
+  // with offsets: the skew split of the layer backward when ws holds its plan.  A group is
+  // an expert's rows, at most T of them, so the split is enabled exactly when the layer's
+  // is (chunk below T and below rows), and gives the layer's bits
   const bool skew = ws && offsets && aligned16(ws);
   return run_wgrad(cfg->act_dtype, cfg->wgrad_dtype, offsets, groups, rows, dY, N, X, K, dW, S(stream), accumulate,
-                   split, nullptr, 0, skew ? ws : nullptr, skew ? ws_bytes : 0, rows);
+                   split, nullptr, 0, skew ? ws : nullptr, skew ? ws_bytes : 0, std::min<int64_t>(rows, cfg->T));
 }
 
 moe_status_t moe_quantize_fp8(int32_t src_dtype, const void* src, int64_t rows, int32_t cols, int32_t block_rows,

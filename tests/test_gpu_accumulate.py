@@ -224,7 +224,7 @@ def test_grouped_wgrad_skew_split(K):
     torch = torch_mod()
     from mixture_experts_layer_aux_amd import _lib as L
     print(f"grouped wgrad skew split K={K}", flush=True)
-    shape = W.SMALL[2]
+    shape = replace(W.SMALL[2], T=8192)   # groups of up to T rows: the split is enabled
     c16, c32 = L.config_from_shape(shape, wgrad="bf16"), L.config_from_shape(shape, wgrad="f32")
     rng = np.random.default_rng(33)
     sizes = np.array([3000, 0, 37, 1025, 1024, 0, 1, 2049, 512], dtype=np.int64)
